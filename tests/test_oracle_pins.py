@@ -1,0 +1,407 @@
+"""Pins of the CPU oracle against facts the pages and the mathematics fix.
+
+None of these re-types an oracle formula: each compares the oracle with an
+independent construction (Sylvester recursion, numerical quadrature, published
+tables, brute-force search, hand-derived bit patterns, closed forms of tiny
+attention problems, the pages' own data-driven Lloyd algorithm).
+"""
+
+import math
+
+import numpy as np
+import pytest
+from scipy import integrate
+
+import oracle as O
+from tests.conftest import read_golden
+
+SIGMA = 1.0 / math.sqrt(128)
+
+
+# ----------------------------------------------------------------- Hadamard / rotation
+
+def test_hadamard_orthogonal_exact():
+    h = O.hadamard_matrix(128)
+    assert np.array_equal(h @ h.T, 128.0 * np.eye(128))
+
+
+def test_hadamard_equals_sylvester_recursion():
+    h = np.array([[1.0]])
+    while h.shape[0] < 128:
+        h = np.block([[h, h], [h, -h]])
+    assert np.array_equal(O.hadamard_matrix(128), h)
+
+
+def test_hadamard_special_vectors():
+    h = O.hadamard_matrix(128)
+    ones = np.ones(128)
+    e0 = np.zeros(128); e0[0] = 1
+    assert np.array_equal(h @ e0, ones)
+    assert np.array_equal(h @ ones, 128 * e0)
+
+
+def test_sign_vector_bit_order():
+    s = O.sign_vector([1, 0, 0, 0x80000000])
+    assert s[0] == -1 and s[127] == -1
+    assert np.all(s[1:127] == 1)
+    s = O.sign_vector([0, 0x10, 0, 0])
+    assert s[36] == -1 and np.sum(s == -1) == 1
+
+
+def test_rotation_applies_signs_before_hadamard():
+    """rotate(e_k) must be s_k * H[:, k] / sqrt(d) (D first, then H)."""
+    words = np.array([0x80000001, 0x1234, 0, 0xFFFFFFFF], np.uint32)
+    s = O.sign_vector(words)
+    h = O.hadamard_matrix()
+    for k in (0, 1, 5, 31, 44, 127):
+        e = np.zeros(128); e[k] = 1
+        np.testing.assert_allclose(O.rotate(e[None], s)[0], s[k] * h[:, k] / math.sqrt(128), atol=1e-15)
+
+
+def test_rotation_norm_and_inverse():
+    rng = np.random.default_rng(1)
+    u = rng.standard_normal((64, 128))
+    s = O.sign_vector(rng.integers(0, 2**32, 4, dtype=np.uint64).astype(np.uint32))
+    y = O.rotate(u, s)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(u, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(O.unrotate(y, s), u, atol=1e-12)
+
+
+def test_rotation_flattens_a_spike():
+    """A single-coordinate outlier spreads to magnitude 1/sqrt(d) on every coordinate."""
+    s = O.sign_vector([0xDEADBEEF, 0, 7, 9])
+    e = np.zeros(128); e[17] = 1
+    np.testing.assert_allclose(np.abs(O.rotate(e[None], s)[0]), np.full(128, 1 / math.sqrt(128)), rtol=1e-14)
+
+
+# ----------------------------------------------------------------- Lloyd-Max codebook
+
+def test_one_bit_closed_form():
+    c = O.gaussian_lloyd_max(2, SIGMA)
+    np.testing.assert_allclose(c, [-SIGMA * math.sqrt(2 / math.pi), SIGMA * math.sqrt(2 / math.pi)], rtol=1e-13)
+    # distortion of the sign quantizer: sigma^2 (1 - 2/pi)
+    assert abs(O.codebook_mse(c, np.array([0.0]), SIGMA) - SIGMA ** 2 * (1 - 2 / math.pi)) < 1e-15
+
+
+@pytest.mark.parametrize("row", read_golden("lloyd_max_gaussian.txt"), ids=lambda r: r[0])
+def test_published_gaussian_table(row):
+    levels = int(row[0])
+    outs = [float(v) for v in row[1].split()]
+    bnds = [float(v) for v in row[2].split()] if row[2] else []
+    mse = float(row[3]) if row[3] else None
+    c = O.gaussian_lloyd_max(levels, 1.0)
+    pos = c[levels // 2:]
+    # the 1960 table is printed to four significant digits; allow 1.5 units of
+    # the last printed digit (rounding plus a possible last-digit slip)
+    for got, want in zip(pos, outs):
+        assert abs(got - want) <= 1.5 * 10 ** (math.floor(math.log10(want)) - 3), (got, want)
+    b = 0.5 * (c[:-1] + c[1:])
+    for got, want in zip(b[levels // 2:], bnds):
+        assert abs(got - want) <= 1.5 * 10 ** (math.floor(math.log10(want)) - 3), (got, want)
+    if mse is None:
+        return
+    got_mse = O.codebook_mse(c, b, 1.0)
+    assert abs(got_mse - mse) <= 1.5 * 10 ** (math.floor(math.log10(mse)) - 3), (got_mse, mse)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_centroid_condition_by_quadrature(bits):
+    """Each centre is the conditional mean of its cell, by numerical integration."""
+    c = O.gaussian_lloyd_max(1 << bits, 1.0)
+    b = np.concatenate(([-np.inf], 0.5 * (c[:-1] + c[1:]), [np.inf]))
+    pdf = lambda x: math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi)
+    for j in range(len(c)):
+        lo, hi = max(b[j], -12.0), min(b[j + 1], 12.0)
+        m0 = integrate.quad(pdf, lo, hi, epsabs=0, epsrel=1e-13, limit=200)[0]
+        m1 = integrate.quad(lambda x: x * pdf(x), lo, hi, epsabs=0, epsrel=1e-13, limit=200)[0]
+        assert abs(m1 / m0 - c[j]) < 1e-9
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_mse_by_quadrature(bits):
+    cb = O.build_codebook(bits)
+    b = np.concatenate(([-np.inf], cb.boundaries, [np.inf]))
+    pdf = lambda x: math.exp(-0.5 * (x / SIGMA) ** 2) / (SIGMA * math.sqrt(2 * math.pi))
+    tot = 0.0
+    for j in range(cb.n_levels):
+        lo, hi = max(b[j], -12 * SIGMA), min(b[j + 1], 12 * SIGMA)
+        cj = cb.centroids[j]
+        tot += integrate.quad(lambda x: (x - cj) ** 2 * pdf(x), lo, hi, epsabs=0, epsrel=1e-12, limit=200)[0]
+    assert abs(tot - cb.mse) < 1e-10 * SIGMA ** 2 + 1e-9 * cb.mse
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_data_driven_lloyd_matches_density_form(bits):
+    """The pages' assign/mean/repeat loop on Gaussian samples lands on the analytic centres."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(400_000) * SIGMA
+    c_data = O.lloyd_max_from_samples(x, 1 << bits)
+    c_ana = O.gaussian_lloyd_max(1 << bits, SIGMA)
+    assert np.max(np.abs(c_data - c_ana)) < 0.01 * SIGMA
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_stored_codebook_format(bits):
+    cb = O.build_codebook(bits)
+    c = cb.centroids
+    assert np.all(np.diff(c) > 0)
+    assert np.array_equal(c, -c[::-1])
+    assert np.array_equal(c.astype(np.float16).astype(np.float64), c)            # float16-exact
+    assert np.array_equal(cb.boundaries.astype(np.float32).astype(np.float64), cb.boundaries)  # float32-exact
+    assert np.array_equal(cb.boundaries, (c[:-1] + c[1:]) / 2)
+    # rounding to float16 moves a centre by at most half a float16 ulp
+    ulp = np.spacing(np.abs(cb.centroids_f64).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(c - cb.centroids_f64) <= 0.5 * ulp)
+
+
+# ----------------------------------------------------------------- encode / pack
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_encode_is_nearest_centroid(bits):
+    cb = O.build_codebook(bits)
+    rng = np.random.default_rng(bits)
+    y = rng.standard_normal(200_000) * SIGMA * 1.5
+    got = O.encode(y, cb.boundaries)
+    brute = np.argmin(np.abs(y[:, None] - cb.centroids[None, :]), axis=1)
+    far = ~O.near_boundary_mask(y, cb.boundaries, 1e-12)
+    assert np.array_equal(got[far], brute[far])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_encode_ties_and_extremes(bits):
+    cb = O.build_codebook(bits)
+    L = cb.n_levels
+    b = cb.boundaries
+    assert list(O.encode(b, b)) == list(range(L - 1))                      # tie -> lower code
+    assert list(O.encode(np.nextafter(b, np.inf), b)) == list(range(1, L))
+    assert O.encode(np.array([0.0]), b)[0] == L // 2 - 1
+    assert O.encode(np.array([-1.0, 1.0]), b).tolist() == [0, L - 1]
+
+
+def test_zero_vector_quantizes_to_middle_code():
+    cb = O.build_codebook(3)
+    n, codes, y = O.quantize_vectors(np.zeros((1, 128), np.float16), np.ones(128), cb)
+    assert n[0] == 0 and np.all(y == 0) and np.all(codes == 3)
+
+
+@pytest.mark.parametrize("row", read_golden("pack_patterns.txt"), ids=lambda r: r[0] + ":" + r[1])
+def test_pack_hand_patterns(row):
+    bits = int(row[0])
+    prefix = [int(v) for v in row[1].split()]
+    want = bytes(int(v, 16) for v in row[2].split())
+    codes = np.array((prefix * (128 // len(prefix) + 1))[:128], np.uint8)
+    packed = O.pack_codes(codes, bits)
+    assert packed.shape == (16 * bits,)
+    assert bytes(packed[: len(want)]) == want
+    assert np.array_equal(O.unpack_codes(packed, bits), codes)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_pack_roundtrip_random(bits):
+    rng = np.random.default_rng(bits)
+    codes = rng.integers(0, 1 << bits, size=(50, 128)).astype(np.uint8)
+    assert np.array_equal(O.unpack_codes(O.pack_codes(codes, bits), bits), codes)
+
+
+@pytest.mark.parametrize("row", read_golden("bits_per_value.txt"), ids=lambda r: r[0])
+def test_bits_per_value_matches_pages(row):
+    bits, bpv, ratio = int(row[0]), float(row[1]), float(row[2])
+    assert O.bits_per_value(bits) == bpv
+    assert (16 * bits + 4) * 8 / 128 == bpv       # bytes stored per 128-block
+    assert round(16 / bpv, 1) == ratio
+
+
+# ----------------------------------------------------------------- dequantize
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_dequantize_error_matches_codebook_mse(bits):
+    """Relative error of Gaussian vectors ~ MSE_b / sigma^2 (rotated coordinates ~ N(0, 1/128))."""
+    cb = O.build_codebook(bits)
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((4000, 128)).astype(np.float16)
+    s = O.sign_vector([0x0F0F0F0F, 0x33333333, 0x55555555, 0x00FF00FF])
+    n, codes, _ = O.quantize_vectors(x, s, cb)
+    xh = O.dequantize_vectors(n, codes, s, cb)
+    xf = x.astype(np.float64)
+    rel = np.sum((xf - xh) ** 2) / np.sum(xf ** 2)
+    want = cb.mse / SIGMA ** 2
+    assert 0.9 * want < rel < 1.05 * want, (rel, want)
+
+
+def test_dequantize_recovers_sign_and_scale():
+    """Scaling the input scales the output; flipping it flips the output (antisymmetric codebook)."""
+    cb = O.build_codebook(4)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((8, 128)).astype(np.float16)
+    s = O.sign_vector([1, 2, 3, 4])
+    n, c, _ = O.quantize_vectors(x, s, cb)
+    n2, c2, _ = O.quantize_vectors((-x) * np.float16(4), s, cb)
+    far = ~O.near_boundary_mask(O.rotate(x.astype(np.float64) / np.linalg.norm(x.astype(np.float64), axis=1)[:, None], s), cb.boundaries)
+    assert np.array_equal(c2[far], (cb.n_levels - 1 - c)[far])
+    np.testing.assert_allclose(n2, 4 * n, rtol=1e-7)
+
+
+# ----------------------------------------------------------------- attention
+
+def _cache_from(xs, bits, signs, block_size=4, shuffle=None):
+    """Quantize xs [T, H, 128] into an oracle cache with the given page order."""
+    T, H, _ = xs.shape
+    nb = -(-T // block_size)
+    order = np.arange(nb) if shuffle is None else shuffle
+    cb = O.build_codebook(bits)
+    c = O.new_cache(bits, H, block_size, nb, signs, cb)
+    t = np.arange(T)
+    slots = order[t // block_size] * block_size + t % block_size
+    O.cache_write(c, xs, slots)
+    return c, order
+
+
+def test_score_in_rotated_domain_equals_plain_dot():
+    """[llama-tq]: Q.K can be computed against K codes in the Hadamard domain."""
+    cb = O.build_codebook(4)
+    rng = np.random.default_rng(5)
+    s = O.sign_vector([9, 8, 7, 6])
+    k = rng.standard_normal((32, 128)).astype(np.float16)
+    q = rng.standard_normal(128)
+    n, codes, _ = O.quantize_vectors(k, s, cb)
+    plain = O.dequantize_vectors(n, codes, s, cb) @ q
+    rotated = n.astype(np.float64) * (cb.centroids[codes] @ O.rotate(q[None], s)[0])
+    np.testing.assert_allclose(rotated, plain, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_single_token_returns_value():
+    rng = np.random.default_rng(2)
+    xs = rng.standard_normal((1, 1, 128)).astype(np.float16)
+    kc, _ = _cache_from(xs, 4, [[1, 2, 3, 4]])
+    vc, _ = _cache_from(xs[::-1] * np.float16(2), 3, [[5, 6, 7, 8]])
+    q = rng.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    out = O.decode_attention(q, kc, vc, [1], np.array([[0]]), 1)
+    np.testing.assert_allclose(out[0, 0, 0], O.cache_read(vc, np.array([0]), 0)[0], rtol=1e-14)
+
+
+def test_attention_two_tokens_closed_form():
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((2, 1, 128)).astype(np.float16)
+    v = rng.standard_normal((2, 1, 128)).astype(np.float16)
+    kc, _ = _cache_from(k, 4, [[3, 1, 4, 1]])
+    vc, _ = _cache_from(v, 4, [[5, 9, 2, 6]])
+    q = rng.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    kh = O.cache_read(kc, np.array([0, 1]), 0)
+    vh = O.cache_read(vc, np.array([0, 1]), 0)
+    qq = q[0, 0, 0].astype(np.float64)
+    s0, s1 = kh @ qq / math.sqrt(128)
+    p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    want = p0 * vh[0] + (1 - p0) * vh[1]
+    out = O.decode_attention(q, kc, vc, [2], np.array([[0]]), 1)          # scale 0 -> 1/sqrt(128)
+    np.testing.assert_allclose(out[0, 0, 0], want, rtol=1e-12, atol=1e-14)
+    out2 = O.decode_attention(q, kc, vc, [2], np.array([[0]]), 1, scale=0.5)
+    s0, s1 = kh @ qq * 0.5
+    p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    np.testing.assert_allclose(out2[0, 0, 0], p0 * vh[0] + (1 - p0) * vh[1], rtol=1e-12, atol=1e-14)
+
+
+def test_attention_uniform_cases_give_mean_value():
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((7, 1, 128)).astype(np.float16)
+    kc, _ = _cache_from(np.repeat(rng.standard_normal((1, 1, 128)), 7, 0).astype(np.float16), 4, [[1, 1, 1, 1]])
+    vc, _ = _cache_from(v, 3, [[2, 2, 2, 2]])
+    vh = O.cache_read(vc, np.arange(7), 0)
+    q = rng.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    out = O.decode_attention(q, kc, vc, [7], np.array([[0, 1]]), 1)
+    np.testing.assert_allclose(out[0, 0, 0], vh.mean(0), rtol=1e-12, atol=1e-14)
+    kc2, _ = _cache_from(rng.standard_normal((7, 1, 128)).astype(np.float16), 4, [[1, 1, 1, 1]])
+    out0 = O.decode_attention(np.zeros_like(q), kc2, vc, [7], np.array([[0, 1]]), 1)
+    np.testing.assert_allclose(out0[0, 0, 0], vh.mean(0), rtol=1e-12, atol=1e-14)
+
+
+def test_attention_weights_by_pairwise_form():
+    """Brute force: p_t = 1 / sum_u exp(s_u - s_t), a different route to the softmax."""
+    rng = np.random.default_rng(8)
+    T = 13
+    k = rng.standard_normal((T, 1, 128)).astype(np.float16)
+    v = rng.standard_normal((T, 1, 128)).astype(np.float16)
+    kc, order = _cache_from(k, 3, [[11, 22, 33, 44]], block_size=4, shuffle=np.array([2, 0, 3, 1]))
+    vc, _ = _cache_from(v, 2, [[55, 66, 77, 88]], block_size=4, shuffle=np.array([2, 0, 3, 1]))
+    q = rng.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    slots = O.slots_for_sequence(order, 4, T)
+    kh, vh = O.cache_read(kc, slots, 0), O.cache_read(vc, slots, 0)
+    s = kh @ q[0, 0, 0].astype(np.float64) / math.sqrt(128)
+    p = np.array([1.0 / sum(math.exp(su - st) for su in s) for st in s])
+    out = O.decode_attention(q, kc, vc, [T], order[None], 1)
+    np.testing.assert_allclose(out[0, 0, 0], p @ vh, rtol=1e-12, atol=1e-14)
+
+
+def test_page_order_does_not_change_result():
+    rng = np.random.default_rng(9)
+    T = 10
+    k = rng.standard_normal((T, 1, 128)).astype(np.float16)
+    v = rng.standard_normal((T, 1, 128)).astype(np.float16)
+    q = rng.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    outs = []
+    for perm in (np.arange(3), np.array([1, 2, 0])):
+        kc, order = _cache_from(k, 4, [[1, 2, 3, 4]], block_size=4, shuffle=perm)
+        vc, _ = _cache_from(v, 3, [[4, 3, 2, 1]], block_size=4, shuffle=perm)
+        outs.append(O.decode_attention(q, kc, vc, [T], order[None], 1))
+    np.testing.assert_allclose(outs[0], outs[1], rtol=1e-14)
+
+
+def test_causal_multi_token_equals_truncated_single_token():
+    rng = np.random.default_rng(10)
+    T, nq = 9, 3
+    k = rng.standard_normal((T, 1, 128)).astype(np.float16)
+    v = rng.standard_normal((T, 1, 128)).astype(np.float16)
+    kc, order = _cache_from(k, 4, [[1, 2, 3, 4]], block_size=4)
+    vc, _ = _cache_from(v, 4, [[4, 3, 2, 1]], block_size=4)
+    q = rng.standard_normal((1, nq, 1, 128)).astype(np.float16)
+    out = O.decode_attention(q, kc, vc, [T], order[None], nq)
+    for j in range(nq):
+        single = O.decode_attention(q[:, j:j + 1], kc, vc, [T - nq + j + 1], order[None], 1)
+        np.testing.assert_allclose(out[0, j, 0], single[0, 0, 0], rtol=1e-14)
+    # a row that sees no token outputs zeros
+    z = O.decode_attention(q, kc, vc, [1], order[None], nq)
+    assert np.all(z[0, :2] == 0) and np.any(z[0, 2] != 0)
+
+
+def test_gqa_maps_query_head_to_kv_head_by_division():
+    rng = np.random.default_rng(12)
+    T, hkv, g = 6, 2, 3
+    k = rng.standard_normal((T, hkv, 128)).astype(np.float16)
+    v = rng.standard_normal((T, hkv, 128)).astype(np.float16)
+    kc, order = _cache_from(k, 4, [[1, 2, 3, 4], [5, 6, 7, 8]], block_size=8)
+    vc, _ = _cache_from(v, 3, [[8, 7, 6, 5], [4, 3, 2, 1]], block_size=8)
+    q = rng.standard_normal((1, 1, hkv * g, 128)).astype(np.float16)
+    out = O.decode_attention(q, kc, vc, [T], order[None], 1)
+    slots = O.slots_for_sequence(order, 8, T)
+    for h in range(hkv * g):
+        kv = h // g
+        kh, vh = O.cache_read(kc, slots, kv), O.cache_read(vc, slots, kv)
+        s = kh @ q[0, 0, h].astype(np.float64) / math.sqrt(128)
+        p = np.exp(s - s.max()); p /= p.sum()
+        np.testing.assert_allclose(out[0, 0, h], p @ vh, rtol=1e-12, atol=1e-14)
+
+
+def test_sparse_v_semantics():
+    """[TQ+ article]: V of low-weight positions is skipped and treated as zero."""
+    rng = np.random.default_rng(13)
+    T = 40
+    k = rng.standard_normal((T, 1, 128)).astype(np.float16) * np.float16(3)
+    v = rng.standard_normal((T, 1, 128)).astype(np.float16)
+    kc, order = _cache_from(k, 4, [[1, 2, 3, 4]], block_size=8)
+    vc, _ = _cache_from(v, 2, [[4, 3, 2, 1]], block_size=8)
+    q = rng.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    tbl = order[None]
+    dense, w = O.decode_attention(q, kc, vc, [T], tbl, 1, return_weights=True)
+    p = w[(0, 0, 0)]
+    vh = O.cache_read(vc, O.slots_for_sequence(order, 8, T), 0)
+    assert np.array_equal(O.decode_attention(q, kc, vc, [T], tbl, 1, tau=0.0), dense)
+    assert np.all(O.decode_attention(q, kc, vc, [T], tbl, 1, tau=1.01) == 0)
+    tau = float(np.sort(p)[T // 2]) * 1.0000001
+    sp = O.decode_attention(q, kc, vc, [T], tbl, 1, tau=tau)
+    want = np.zeros(128)
+    for t in range(T):                       # enumeration, no renormalisation
+        if p[t] >= tau:
+            want += p[t] * vh[t]
+    np.testing.assert_allclose(sp[0, 0, 0], want, rtol=1e-12, atol=1e-14)
+    skipped = p < tau
+    bound = np.sum(p[skipped] * np.linalg.norm(vh[skipped], axis=1))
+    assert np.linalg.norm(sp[0, 0, 0] - dense[0, 0, 0]) <= bound * (1 + 1e-12)
