@@ -1,0 +1,322 @@
+"""Benchmark of the compressed-KV hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: quantize-on-append of
+the new tokens' K and V into the paged compressed cache (tq_quantize_kv) and
+decode attention of the new query tokens over the whole cache
+(tq_decode_attention).  The default workload is the Llama-3-8B-shaped decode:
+1 sequence of 32768 tokens, 32 query / 8 KV heads, d = 128, K 4-bit, V 3-bit.
+
+The cache is replicated R times (R x 31.5 MB > the 256 MB last-level cache)
+and step i works on replica i mod R, so every step streams its cache from HBM.
+`value` = algorithmic bytes of a step / time of a step (inputs resident in HBM).
+The second half of the metric, quantize throughput, is measured on the prefill
+workload (32 layers x 8192 tokens x 8 KV heads, K 3-bit, V 2-bit).
+
+python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload llama8b]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from compressed_kv_attention_tq_amd import tq as T  # noqa: E402
+from compressed_kv_attention_tq_amd import workloads as W  # noqa: E402
+
+METRIC = "compressed-KV decode attention HBM GB/s (% of peak) + quantize Mtok/s"
+HBM_PEAK_GBS = 8000.0
+LLC_BYTES = 256 << 20
+KERNEL_SOURCES = ["tq_decode.hip", "tq_device.h", "tq_quant.hip", "tq_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cache_bytes_per_token_head(bits):
+    return 16 * bits + 4
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "compressed_kv_attention_tq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(kernel_key):
+    """HBM bytes per launch from a committed PMC record of the same kernel sources, else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    r = rec.get(kernel_key)
+    if not r or r.get("source_hash") != source_hash():
+        return None
+    return r.get("bytes_per_launch")
+
+
+def decode_workload(name):
+    return {"llama8b": W.llama8b, "longctx": W.longctx, "ragged": W.ragged, "tiny": W.tiny}[name]()
+
+
+def gen_kv_device(wl, b, torch, gen):
+    """K/V of sequence b: the workload's own seeded numpy recipe, except the ragged
+    workload (2.2 M tokens), whose N(0,1) K/V come from a seeded device generator."""
+    if wl.kind == "normal":
+        n = int(wl.seq_lens[b])
+        k = torch.randn((n, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
+        v = torch.randn((n, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
+        return k, v
+    k, v = wl.kv_source(b)
+    return torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+
+
+def run_decode(args, torch):
+    wl = decode_workload(args.workload)
+    kb, vb = wl.k_bits, wl.v_bits
+    per_tok = cache_bytes_per_token_head(kb) + cache_bytes_per_token_head(vb)
+    cache_bytes = wl.total_tokens * wl.n_kv_heads * per_tok
+    reps = args.replicas or max(1, math.ceil(1.5 * LLC_BYTES / cache_bytes))
+    log(f"[bench] workload {wl.name}: {wl.n_seqs} seqs, {wl.total_tokens} tokens, cache {cache_bytes / 1e6:.1f} MB, "
+        f"{reps} replicas")
+
+    nb = wl.n_blocks
+    kc = T.Cache.allocate(kb, wl.n_kv_heads, wl.block_size, nb * reps, wl.signs_k)
+    vc = T.Cache.allocate(vb, wl.n_kv_heads, wl.block_size, nb * reps, wl.signs_v)
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    tables = []
+    for r in range(reps):
+        t = wl.block_table.copy()
+        t[t >= 0] += r * nb
+        tables.append(torch.from_numpy(t).cuda())
+    for b in range(wl.n_seqs):
+        if int(wl.seq_lens[b]) == 0:
+            continue
+        k, v = gen_kv_device(wl, b, torch, gen)
+        for r in range(reps):
+            slots = torch.from_numpy(wl.slots(b) + r * nb * wl.block_size).cuda()
+            T.tq_quantize_kv(kc, k, vc, v, slots)
+        del k, v
+    torch.cuda.synchronize()
+    log("[bench] caches filled")
+
+    # the new tokens of each step: the last n_qtok positions of every sequence
+    q = torch.from_numpy(wl.queries()).cuda()
+    n_new = wl.n_seqs * wl.n_qtok
+    k_new = torch.randn((n_new, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
+    v_new = torch.randn((n_new, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
+    new_slots = []
+    for r in range(reps):
+        s = []
+        for b in range(wl.n_seqs):
+            sl = wl.slots(b) + r * nb * wl.block_size
+            s.extend(sl[-wl.n_qtok:].tolist() if len(sl) >= wl.n_qtok else [-1] * wl.n_qtok)
+        new_slots.append(torch.tensor(s, dtype=torch.int64, device="cuda"))
+    lens = torch.from_numpy(wl.seq_lens).cuda()
+    out = torch.empty((wl.n_seqs, wl.n_qtok, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    ws_bytes = T.decode_workspace_bytes(kc, vc, wl.n_seqs, wl.n_qtok, wl.n_q_heads, wl.block_table.shape[1],
+                                        wl.tau)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+
+    def step(i, events=None):
+        r = i % reps
+        T.tq_quantize_kv(kc, k_new, vc, v_new, new_slots[r])
+        T.tq_decode_attention(kc, vc, q, lens, tables[r], 0.0, wl.tau, out=out, workspace=ws, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(args.warmup + i, events=evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    pass_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # algorithmic bytes
+    if wl.tau > 0:
+        kept = 64 * wl.n_seqs * wl.n_kv_heads          # planted positions kept per (seq, KV head)
+        cache_step = wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb) + \
+            kept * cache_bytes_per_token_head(vb)
+        pass_bytes = wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb)
+    else:
+        cache_step = cache_bytes
+        pass_bytes = cache_bytes
+    qo = wl.n_seqs * wl.n_qtok * wl.n_q_heads * 128 * (2 + 4)
+    meta = wl.n_seqs * 4 + wl.block_table.size * 4
+    append = n_new * wl.n_kv_heads * (2 * 256 + per_tok) + n_new * 8
+    step_bytes = cache_step + qo + meta + append
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
+    log(f"[bench] {ms_step * 1e3:.1f} us/step, pass kernel {pass_ms * 1e3:.1f} us, "
+        f"step {value:.0f} GB/s, pass {achieved:.0f} GB/s")
+    kernel_key = f"decode_pass_{wl.name}"
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(kernel_key),
+            "kernel": "tq_decode_pass_kernel", "bytes_per_launch": pass_bytes,
+            "avg_launch_us": round(pass_ms * 1e3, 2)}
+    cfg = {"workload": f"{wl.name}: {wl.n_seqs} seq x {int(wl.seq_lens.max())} tokens, "
+                       f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d=128, K{kb}/V{vb}, "
+                       f"{wl.n_qtok} query token(s), tau={wl.tau}, page {wl.block_size}",
+           "global_batch": wl.n_seqs, "seq_len": int(wl.seq_lens.max()), "replicas": reps,
+           "parallelism": "single GPU"}
+    return wl, value, ms_step, roof, cfg, step_bytes
+
+
+def run_quantize(args, torch):
+    """Prefill quantize: 32 layers x 8192 tokens x 8 KV heads, K3/V2, one call per layer."""
+    wl = W.prefill()
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    n = wl.n_tokens
+    srcs, caches = [], []
+    for layer in range(wl.n_layers):
+        xs = []
+        for _ in range(2):       # Laplace(0,1) = sign * Exp(1); 1% of entries x30
+            e = torch.empty((n, wl.n_kv_heads, 128), device="cuda").exponential_(generator=gen)
+            sgn = torch.randint(0, 2, e.shape, device="cuda", generator=gen) * 2 - 1
+            big = torch.rand(e.shape, device="cuda", generator=gen) < 0.01
+            xs.append((e * sgn * torch.where(big, 30.0, 1.0)).half())
+        srcs.append(xs)
+        sk, sv = wl.signs(layer)
+        caches.append((T.Cache.allocate(wl.k_bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, sk),
+                       T.Cache.allocate(wl.v_bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, sv)))
+    slots = torch.arange(n, dtype=torch.int64, device="cuda")
+
+    def one_pass(events=None):
+        for layer in range(wl.n_layers):
+            if events is not None:
+                events[layer][0].record()
+            T.tq_quantize_kv(caches[layer][0], srcs[layer][0], caches[layer][1], srcs[layer][1], slots)
+            if events is not None:
+                events[layer][1].record()
+
+    for _ in range(2):
+        one_pass()
+    torch.cuda.synchronize()
+    reps = max(1, args.quantize_reps)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(wl.n_layers)] for _ in range(reps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for r in range(reps):
+        one_pass(evs[r])
+    t1.record()
+    torch.cuda.synchronize()
+    pass_ms = t0.elapsed_time(t1) / reps
+    kern_ms = float(np.mean([a.elapsed_time(b) for er in evs for a, b in er]))
+    vec_per_call = 2 * n * wl.n_kv_heads
+    bytes_per_call = n * wl.n_kv_heads * (2 * 256 + cache_bytes_per_token_head(wl.k_bits)
+                                          + cache_bytes_per_token_head(wl.v_bits)) + n * 8
+    mtok = n * wl.n_layers / (pass_ms * 1e-3) / 1e6
+    achieved = bytes_per_call / (kern_ms * 1e-3) / 1e9
+    log(f"[bench] quantize: {pass_ms * 1e3:.1f} us / 32 layers, {kern_ms * 1e3:.2f} us/kernel, "
+        f"{mtok:.0f} M token-layers/s, {achieved:.0f} GB/s")
+    return {"workload": "prefill: 32 layers x 8192 tokens x 8 KV heads, d=128, K3/V2 (Laplace, 1% x30)",
+            "value": round(mtok, 1), "unit": "M token-layers/s",
+            "ms_per_32_layers": round(pass_ms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic("quantize_prefill"),
+                         "kernel": "tq_quantize_kernel", "bytes_per_launch": bytes_per_call,
+                         "vectors_per_launch": vec_per_call, "avg_launch_us": round(kern_ms * 1e3, 2)}}
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle (unchanged) on a bounded sample of the same decode step: for the KV
+    heads of sequence 0 in turn (cycling), quantize-append the new token and decode its
+    query rows over the whole context, until budget_s seconds are spent.  GB/s of
+    algorithmic bytes processed."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    b = 0
+    length = int(wl.seq_lens[b])
+    k, v = wl.kv_source(b)
+    slots = wl.slots(b)
+    q = wl.queries()
+    per_tok = cache_bytes_per_token_head(wl.k_bits) + cache_bytes_per_token_head(wl.v_bits)
+    lens1, table1 = wl.seq_lens[:1], wl.block_table[:1]
+    prepared = []
+    for kv in range(wl.n_kv_heads):   # the context before the new tokens (not timed)
+        kcache = O.new_cache(wl.k_bits, 1, wl.block_size, wl.n_blocks, wl.signs_k[kv:kv + 1],
+                             O.build_codebook(wl.k_bits))
+        vcache = O.new_cache(wl.v_bits, 1, wl.block_size, wl.n_blocks, wl.signs_v[kv:kv + 1],
+                             O.build_codebook(wl.v_bits))
+        O.cache_write(kcache, k[:-wl.n_qtok, kv:kv + 1], slots[:-wl.n_qtok])
+        O.cache_write(vcache, v[:-wl.n_qtok, kv:kv + 1], slots[:-wl.n_qtok])
+        prepared.append((kcache, vcache, q[:1, :, kv * wl.group:(kv + 1) * wl.group]))
+    done_bytes, spent, units = 0, 0.0, 0
+    while spent < budget_s:
+        kv = units % wl.n_kv_heads
+        kcache, vcache, qh = prepared[kv]
+        t0 = time.perf_counter()
+        O.cache_write(kcache, k[-wl.n_qtok:, kv:kv + 1], slots[-wl.n_qtok:])
+        O.cache_write(vcache, v[-wl.n_qtok:, kv:kv + 1], slots[-wl.n_qtok:])
+        O.decode_attention(qh, kcache, vcache, lens1, table1, wl.n_qtok, 0.0, wl.tau)
+        spent += time.perf_counter() - t0
+        units += 1
+        done_bytes += length * per_tok + wl.n_qtok * (2 * 256 + per_tok) + qh.size * 6
+    gbs = done_bytes / spent / 1e9
+    log(f"[bench] cpu oracle: {units} (KV head, step) units of seq 0 in {spent:.1f} s -> {gbs:.4f} GB/s, "
+        f"{cores} threads")
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{wl.name}: sequence 0, {units} single-KV-head steps (append + decode of "
+                      f"{wl.group * wl.n_qtok} query rows over {length} tokens each), {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "longctx", "ragged", "tiny"])
+    ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--quantize-reps", type=int, default=5)
+    ap.add_argument("--no-quantize", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the hot path does not shard across GPUs here)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    T.load_library()
+
+    wl, value, ms_step, roof, cfg, step_bytes = run_decode(args, torch)
+    quant = None if args.no_quantize else run_quantize(args, torch)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": cfg, "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "step_bytes": step_bytes, "roofline": roof, "cpu_baseline": cpu, "quantize": quant,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,348 @@
+// C ABI of libtq: argument validation, codebook construction, workspace sizing
+// and kernel dispatch.  Everything here runs on the host; nothing allocates.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "tq_internal.h"
+
+using namespace tq;
+
+namespace {
+
+bool is_aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Round a double to the nearest float16 value (ties to even), returned as double.
+double round_to_half(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    frexp(fabs(x), &e);               // |x| = m * 2^e, m in [0.5, 1)
+    int E = e - 1;                    // |x| in [2^E, 2^(E+1))
+    if (E < -14) E = -14;             // subnormal spacing 2^-24
+    const double ulp = ldexp(1.0, E - 10);
+    const double q = nearbyint(fabs(x) / ulp);
+    return copysign(q * ulp, x);
+}
+
+double std_normal_cdf(double z) {
+    if (isinf(z)) return z > 0 ? 1.0 : 0.0;
+    return 0.5 * erfc(-z / sqrt(2.0));
+}
+
+double std_normal_pdf(double z) {
+    if (isinf(z)) return 0.0;
+    return exp(-0.5 * z * z) / sqrt(2.0 * M_PI);
+}
+
+// Expected squared error of a scalar quantizer on N(0, sigma^2), cell by cell in
+// closed form: on a standardised cell [a, b] with centre c,
+//   int (x-c)^2 phi = (1 + c^2)(Phi(b) - Phi(a)) + (a - 2c) phi(a) - (b - 2c) phi(b).
+double gaussian_mse(const double *c, const double *bnd, int L, double sigma) {
+    double tot = 0.0;
+    for (int j = 0; j < L; ++j) {
+        const double a = j == 0 ? -INFINITY : bnd[j - 1] / sigma;
+        const double b = j == L - 1 ? INFINITY : bnd[j] / sigma;
+        const double cj = c[j] / sigma;
+        const double mass = std_normal_cdf(b) - std_normal_cdf(a);
+        const double ta = isinf(a) ? 0.0 : (a - 2.0 * cj) * std_normal_pdf(a);
+        const double tb = isinf(b) ? 0.0 : (b - 2.0 * cj) * std_normal_pdf(b);
+        tot += (1.0 + cj * cj) * mass + ta - tb;
+    }
+    return tot * sigma * sigma;
+}
+
+tq_status check_codebook(const tq_codebook &cb, int bits) {
+    if (cb.bits != bits || cb.n_levels != (1 << bits)) return TQ_ERR_INVALID_ARG;
+    for (int i = 0; i < cb.n_levels; ++i)
+        if (!isfinite(cb.centroids[i])) return TQ_ERR_INVALID_ARG;
+    for (int i = 0; i + 1 < cb.n_levels; ++i) {
+        if (!isfinite(cb.boundaries[i])) return TQ_ERR_INVALID_ARG;
+        if (i > 0 && !(cb.boundaries[i] > cb.boundaries[i - 1])) return TQ_ERR_INVALID_ARG;
+    }
+    return TQ_OK;
+}
+
+tq_status check_cache(const tq_cache *c) {
+    if (!c) return TQ_ERR_INVALID_ARG;
+    if (c->head_dim != TQ_HEAD_DIM) return TQ_ERR_UNSUPPORTED;
+    if (c->bits < 2 || c->bits > 4) return TQ_ERR_UNSUPPORTED;
+    if (c->n_kv_heads < 1 || c->block_size < 1 || c->n_blocks < 1) return TQ_ERR_INVALID_ARG;
+    if (!c->codes || !c->norms || !c->signs) return TQ_ERR_INVALID_ARG;
+    if (!is_aligned(c->codes, 16) || !is_aligned(c->norms, 4) || !is_aligned(c->signs, 4)) return TQ_ERR_INVALID_ARG;
+    // slots are handled as 32-bit values on the device
+    if ((double)c->n_blocks * c->block_size > 2147483647.0) return TQ_ERR_UNSUPPORTED;
+    return check_codebook(c->cb, c->bits);
+}
+
+// Encode grid for one codebook: cells of width 1/grid in y, at most one boundary
+// per (slightly widened) cell; the table covers y in [-1, 1] (|y| <= 1 because y
+// is a rotated unit vector).
+tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, int32_t n_tokens,
+                          QuantSide &q) {
+    double min_gap = INFINITY;
+    const int nb = c->cb.n_levels - 1;
+    for (int i = 0; i + 1 < nb; ++i) min_gap = std::min(min_gap, (double)c->cb.boundaries[i + 1] - c->cb.boundaries[i]);
+    int grid = 1;
+    if (nb > 1) {
+        const double g = ceil(1.25 / min_gap);
+        if (!(g <= (kLutMax - 5) / 2)) return TQ_ERR_UNSUPPORTED;
+        grid = std::max(1, (int)g);
+    }
+    q.src = static_cast<const uint16_t *>(src);
+    q.codes = c->codes;
+    q.norms = c->norms;
+    q.signs = c->signs;
+    q.src_stride = stride;
+    q.n_vec = (int64_t)n_tokens * c->n_kv_heads;
+    q.n_kv = c->n_kv_heads;
+    q.block_size = c->block_size;
+    q.bits = c->bits;
+    q.grid = (float)grid;
+    q.lut_half = grid + 2;
+    q.n_bnd = nb;
+    for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) q.bnd[i] = i < nb ? c->cb.boundaries[i] : 0.f;
+    return TQ_OK;
+}
+
+int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+// Blocks for one quantize side: 4 waves of 8 blocks each per thread block, at
+// most 8 thread blocks per CU, rounded so the grid stride is a multiple of n_kv.
+int quant_blocks(int64_t n_vec, int n_kv) {
+    if (n_vec == 0) return 0;
+    const int64_t need = (n_vec + 31) / 32;
+    int blocks = (int)std::min<int64_t>(need, 2048);
+    const int m = n_kv / gcd_int(n_kv, 32);
+    blocks = ((blocks + m - 1) / m) * m;
+    return blocks;
+}
+
+struct DecodePlan {
+    int rows, rows_pad, chunk, n_chunks, n_tiles;
+    size_t off_qrot, off_ml, off_acc, off_tile, off_stats, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DecodePlan plan_decode(int n_seqs, int n_kv, int rows, int max_blocks, int block_size, bool sparse) {
+    DecodePlan p{};
+    p.rows = rows;
+    p.rows_pad = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : rows <= 12 ? 12 : 16;
+    const int64_t cap = (int64_t)max_blocks * block_size;
+    const int64_t total = (int64_t)n_seqs * n_kv * cap;
+    int chunk = kSub;
+    while (chunk < 16384 && total / chunk > 2048) chunk *= 2;
+    p.chunk = chunk;
+    p.n_chunks = (int)((cap + chunk - 1) / chunk);
+    p.n_tiles = (int)((cap + kSub - 1) / kSub) * (kSub / kTile);
+    const size_t units = (size_t)n_seqs * n_kv;
+    size_t off = 0;
+    p.off_qrot = off;  off = align256(off + units * kD * p.rows_pad * sizeof(float));
+    p.off_ml = off;    off = align256(off + units * p.n_chunks * p.rows_pad * 2 * sizeof(float));
+    p.off_acc = off;   off = align256(off + units * p.n_chunks * p.rows_pad * kD * sizeof(float));
+    p.off_tile = off;  if (sparse) off = align256(off + units * p.n_tiles * p.rows_pad * sizeof(float));
+    p.off_stats = off; if (sparse) off = align256(off + units * p.rows_pad * 2 * sizeof(float));
+    p.total = off;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tq_status_string(tq_status s) {
+    switch (s) {
+        case TQ_OK: return "TQ_OK";
+        case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
+        case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+        case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE";
+        case TQ_ERR_HIP: return "TQ_ERR_HIP";
+    }
+    return "TQ_ERR_UNKNOWN";
+}
+
+tq_status tq_build_codebook(int32_t bits, double sigma, tq_codebook *out) {
+    if (!out) return TQ_ERR_INVALID_ARG;
+    if (!(sigma > 0.0) || !isfinite(sigma)) return TQ_ERR_INVALID_ARG;
+    if (bits < 1 || bits > 4) return TQ_ERR_UNSUPPORTED;
+    const int L = 1 << bits;
+    double c[TQ_MAX_LEVELS], cn[TQ_MAX_LEVELS], bnd[TQ_MAX_LEVELS];
+    // standardised units; uniform start on [-2, 2]
+    for (int j = 0; j < L; ++j) c[j] = -2.0 + 4.0 * j / (L - 1);
+    for (int it = 0; it < 20000; ++it) {
+        for (int j = 0; j + 1 < L; ++j) bnd[j] = 0.5 * (c[j] + c[j + 1]);
+        for (int j = 0; j < L; ++j) {
+            const double lo = j == 0 ? -INFINITY : bnd[j - 1];
+            const double hi = j == L - 1 ? INFINITY : bnd[j];
+            const double mass = std_normal_cdf(hi) - std_normal_cdf(lo);
+            cn[j] = (std_normal_pdf(lo) - std_normal_pdf(hi)) / mass;
+        }
+        double moved = 0.0;
+        for (int j = 0; j < L; ++j) {
+            const double v = 0.5 * (cn[j] - cn[L - 1 - j]);
+            moved = std::max(moved, fabs(v - c[j]));
+            bnd[j] = v;   // temporary
+        }
+        for (int j = 0; j < L; ++j) c[j] = bnd[j];
+        if (moved < 1e-14) break;
+    }
+    memset(out, 0, sizeof(*out));
+    out->bits = bits;
+    out->n_levels = L;
+    out->sigma = (float)sigma;
+    double cs[TQ_MAX_LEVELS], bs[TQ_MAX_LEVELS];
+    for (int j = 0; j < L; ++j) cs[j] = round_to_half(c[j] * sigma);
+    for (int j = 0; j < L; ++j) cs[j] = 0.5 * (cs[j] - cs[L - 1 - j]);
+    for (int j = 0; j + 1 < L; ++j) bs[j] = 0.5 * (cs[j] + cs[j + 1]);
+    for (int j = 0; j < L; ++j) out->centroids[j] = (float)cs[j];
+    for (int j = 0; j + 1 < L; ++j) out->boundaries[j] = (float)bs[j];
+    out->mse = gaussian_mse(cs, bs, L, sigma);
+    return TQ_OK;
+}
+
+tq_status tq_quantize_kv(const tq_cache *k, const void *k_src, const tq_cache *v, const void *v_src,
+                         int64_t src_token_stride, int32_t n_tokens, const int64_t *slot_mapping,
+                         void *stream) {
+    if (n_tokens < 0) return TQ_ERR_INVALID_ARG;
+    const tq_cache *sides[2] = {k, v};
+    const void *srcs[2] = {k_src, v_src};
+    QuantArgs a;
+    memset(&a, 0, sizeof(a));
+    int n_kv = -1;
+    for (int i = 0; i < 2; ++i) {
+        if (!sides[i]) continue;
+        tq_status st = check_cache(sides[i]);
+        if (st != TQ_OK) return st;
+        if (!srcs[i] || !is_aligned(srcs[i], 16)) return TQ_ERR_INVALID_ARG;
+        if (!is_aligned(sides[i]->codes, 8)) return TQ_ERR_INVALID_ARG;
+        if (n_kv >= 0 && n_kv != sides[i]->n_kv_heads) return TQ_ERR_INVALID_ARG;
+        n_kv = sides[i]->n_kv_heads;
+        if (src_token_stride < (int64_t)n_kv * kD || src_token_stride % 8 != 0) return TQ_ERR_INVALID_ARG;
+        st = fill_quant_side(sides[i], srcs[i], src_token_stride, n_tokens, a.side[i]);
+        if (st != TQ_OK) return st;
+    }
+    if (n_tokens == 0 || n_kv < 0) return TQ_OK;
+    if (!slot_mapping) return TQ_ERR_INVALID_ARG;
+    if ((int64_t)n_tokens * n_kv > (1LL << 31) - (1LL << 20)) return TQ_ERR_UNSUPPORTED;
+    const int bk = quant_blocks(a.side[0].n_vec, std::max(1, a.side[0].n_kv));
+    const int bv = quant_blocks(a.side[1].n_vec, std::max(1, a.side[1].n_kv));
+    a.slots = slot_mapping;
+    a.blocks_k = bk;
+    if (launch_quantize(a, bk + bv, static_cast<hipStream_t>(stream)) != hipSuccess) return TQ_ERR_HIP;
+    return TQ_OK;
+}
+
+tq_status tq_dequantize(const tq_cache *c, const int64_t *slots, int32_t n_tokens, void *dst,
+                        int32_t dst_is_fp16, void *stream) {
+    tq_status st = check_cache(c);
+    if (st != TQ_OK) return st;
+    if (n_tokens < 0) return TQ_ERR_INVALID_ARG;
+    if (n_tokens == 0) return TQ_OK;
+    if (!slots || !dst || !is_aligned(dst, 16) || !is_aligned(c->codes, 8)) return TQ_ERR_INVALID_ARG;
+    if ((int64_t)n_tokens * c->n_kv_heads > (1LL << 31) - (1LL << 20)) return TQ_ERR_UNSUPPORTED;
+    DequantArgs a;
+    memset(&a, 0, sizeof(a));
+    a.codes = c->codes;
+    a.norms = c->norms;
+    a.signs = c->signs;
+    a.slots = slots;
+    a.dst = dst;
+    a.n_vec = (int64_t)n_tokens * c->n_kv_heads;
+    a.n_kv = c->n_kv_heads;
+    a.block_size = c->block_size;
+    a.dst_fp16 = dst_is_fp16 ? 1 : 0;
+    for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = i < c->cb.n_levels ? c->cb.centroids[i] : 0.f;
+    if (launch_dequantize(a, c->bits, static_cast<hipStream_t>(stream)) != hipSuccess) return TQ_ERR_HIP;
+    return TQ_OK;
+}
+
+tq_status tq_decode_attention(const tq_cache *k, const tq_cache *v, const void *q, int32_t n_seqs,
+                              int32_t n_qtok, int32_t n_q_heads, const int32_t *seq_lens,
+                              const int32_t *block_table, int32_t max_blocks_per_seq,
+                              float softmax_scale, float sparse_v_tau, float *out, void *workspace,
+                              size_t *workspace_bytes, void *stream) {
+    return tq_decode_attention_timed(k, v, q, n_seqs, n_qtok, n_q_heads, seq_lens, block_table,
+                                     max_blocks_per_seq, softmax_scale, sparse_v_tau, out, workspace,
+                                     workspace_bytes, stream, nullptr);
+}
+
+tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const void *q, int32_t n_seqs,
+                                    int32_t n_qtok, int32_t n_q_heads, const int32_t *seq_lens,
+                                    const int32_t *block_table, int32_t max_blocks_per_seq,
+                                    float softmax_scale, float sparse_v_tau, float *out, void *workspace,
+                                    size_t *workspace_bytes, void *stream, void *const *events) {
+    if (!workspace_bytes) return TQ_ERR_INVALID_ARG;
+    tq_status st = check_cache(k);
+    if (st != TQ_OK) return st;
+    st = check_cache(v);
+    if (st != TQ_OK) return st;
+    if (k->n_kv_heads != v->n_kv_heads || k->block_size != v->block_size) return TQ_ERR_INVALID_ARG;
+    if (!is_aligned(v->codes, 4)) return TQ_ERR_INVALID_ARG;
+    if (n_seqs < 0 || n_qtok < 1 || n_q_heads < 1 || max_blocks_per_seq < 1) return TQ_ERR_INVALID_ARG;
+    if (n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+    if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale)) return TQ_ERR_INVALID_ARG;
+    if (!(sparse_v_tau >= 0.f) || !isfinite(sparse_v_tau)) return TQ_ERR_INVALID_ARG;
+    const int group = n_q_heads / k->n_kv_heads;
+    const int64_t rows = (int64_t)group * n_qtok;
+    if (rows > TQ_MAX_ROWS_PER_KV_HEAD) return TQ_ERR_UNSUPPORTED;
+    if ((int64_t)max_blocks_per_seq * k->block_size > (1LL << 30)) return TQ_ERR_UNSUPPORTED;
+    const bool sparse = sparse_v_tau > 0.f;
+    const DecodePlan p = plan_decode(n_seqs, k->n_kv_heads, (int)rows, max_blocks_per_seq, k->block_size, sparse);
+    if ((int64_t)n_seqs * k->n_kv_heads * p.n_chunks > 0x7FFFFFFFLL) return TQ_ERR_UNSUPPORTED;
+    if (!workspace) {
+        *workspace_bytes = n_seqs == 0 ? 0 : p.total;
+        return TQ_OK;
+    }
+    if (n_seqs == 0) return TQ_OK;
+    if (!q || !seq_lens || !block_table || !out) return TQ_ERR_INVALID_ARG;
+    if (!is_aligned(workspace, 256) || !is_aligned(out, 4) || !is_aligned(q, 2)) return TQ_ERR_INVALID_ARG;
+    if (*workspace_bytes < p.total) return TQ_ERR_WORKSPACE;
+
+    DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.k_codes = k->codes;
+    a.k_norms = k->norms;
+    a.v_codes = v->codes;
+    a.v_norms = v->norms;
+    a.k_signs = k->signs;
+    a.v_signs = v->signs;
+    a.q = static_cast<const uint16_t *>(q);
+    a.seq_lens = seq_lens;
+    a.block_table = block_table;
+    a.out = out;
+    char *ws = static_cast<char *>(workspace);
+    a.qrot = reinterpret_cast<float *>(ws + p.off_qrot);
+    a.part_ml = reinterpret_cast<float *>(ws + p.off_ml);
+    a.part_acc = reinterpret_cast<float *>(ws + p.off_acc);
+    a.tilemax = sparse ? reinterpret_cast<float *>(ws + p.off_tile) : nullptr;
+    a.stats = sparse ? reinterpret_cast<float *>(ws + p.off_stats) : nullptr;
+    a.n_seqs = n_seqs;
+    a.n_qtok = n_qtok;
+    a.n_q_heads = n_q_heads;
+    a.n_kv = k->n_kv_heads;
+    a.group = group;
+    a.rows = (int)rows;
+    a.rows_pad = p.rows_pad;
+    a.max_blocks = max_blocks_per_seq;
+    a.block_size = k->block_size;
+    a.chunk = p.chunk;
+    a.n_chunks = p.n_chunks;
+    a.n_tiles = p.n_tiles;
+    const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)kD);
+    a.qscale = (float)(scale * M_LOG2E / sqrt((double)kD));
+    a.tau = sparse_v_tau;
+    a.k_bits = k->bits;
+    a.v_bits = v->bits;
+    for (int i = 0; i < TQ_MAX_LEVELS; ++i) {
+        a.kc[i] = i < k->cb.n_levels ? k->cb.centroids[i] : 0.f;
+        a.vc[i] = i < v->cb.n_levels ? v->cb.centroids[i] : 0.f;
+    }
+    hipEvent_t ev0 = events ? static_cast<hipEvent_t>(events[0]) : nullptr;
+    hipEvent_t ev1 = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
+    if (launch_decode(a, static_cast<hipStream_t>(stream), ev0, ev1) != hipSuccess) return TQ_ERR_HIP;
+    return TQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,621 @@
+// Decode attention over the compressed cache (gfx950, vector ALU only).
+//
+//   qrot   : per (seq, KV head) rotate the G*n_qtok query rows once,
+//            q'' = scale * log2(e) * H (s_K * q) / sqrt(128)            ([llama-tq])
+//   pass   : per (seq, KV head, chunk): score every token against its K codes in
+//            the Hadamard domain (lane per token, q'' from scalar loads, centroid
+//            from an LDS table; K is never dequantized), online softmax in the
+//            log2 domain, and either
+//              DENSE - accumulate V in the rotated domain: acc += e * n_V * c[code]
+//              SCORE - keep only per-chunk (max, sum) and per-64-token tile maxima
+//              GATED - with the global (max, sum) known, skip tiles whose bound is
+//                      below tau, re-score the rest, and accumulate V only where
+//                      p = 2^(s - M) / L >= tau                 ([TQ+ README]
+//                      sparse V; [TQ+ article] skipped V treated as zero)
+//   stats  : global (max, sum) per row from the SCORE partials
+//   combine: merge chunk partials (log-sum-exp for DENSE, plain sum for GATED),
+//            inverse-rotate once: o = s_V * H acc / sqrt(128)
+#include <float.h>
+
+#include <utility>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+enum { MODE_DENSE = 0, MODE_SCORE = 1, MODE_GATED = 2 };
+
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp<kDppXor1>(x));
+    x = fmaxf(x, dpp<kDppXor2>(x));
+    x = fmaxf(x, dpp<kDppRor4>(x));
+    x = fmaxf(x, dpp<kDppRor8>(x));
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppRor4>(x);
+    x += dpp<kDppRor8>(x);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// 2^(a - b) with the -inf conventions of an online softmax (0 when a is -inf).
+__device__ __forceinline__ float exp2_diff(float a, float b) {
+    return a == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(a - b);
+}
+
+#ifndef TQ_DECODE_KB
+// --------------------------------------------------------------------------
+// q rotation: one wave per row, two elements per lane.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void tq_qrot_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int r = threadIdx.x >> 6;                     // row within (seq, kv)
+    const int b = blockIdx.x / a.n_kv, kv = blockIdx.x % a.n_kv;
+    float x0 = 0.f, x1 = 0.f;
+    if (r < a.rows) {
+        const int jq = r / a.group, h = kv * a.group + r % a.group;
+        const uint16_t *q = a.q + (((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * kD;
+        const uint32_t *sg = a.k_signs + kv * 4;
+        x0 = (float)__builtin_bit_cast(_Float16, q[lane]);
+        x1 = (float)__builtin_bit_cast(_Float16, q[lane + 64]);
+        if ((sg[lane >> 5] >> (lane & 31)) & 1u) x0 = -x0;
+        if ((sg[2 + (lane >> 5)] >> (lane & 31)) & 1u) x1 = -x1;
+    }
+    // element bit 6 in registers, bits 0..5 across lanes
+    float a0 = x0 + x1, a1 = x0 - x1;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float p0 = __shfl_xor(a0, m), p1 = __shfl_xor(a1, m);
+        const bool hi = lane & m;
+        a0 = hi ? p0 - a0 : a0 + p0;
+        a1 = hi ? p1 - a1 : a1 + p1;
+    }
+    float *dst = a.qrot + ((int64_t)b * a.n_kv + kv) * kD * a.rows_pad;
+    dst[lane * a.rows_pad + r] = a0 * a.qscale;
+    dst[(lane + 64) * a.rows_pad + r] = a1 * a.qscale;
+}
+
+#endif  // !TQ_DECODE_KB
+
+// --------------------------------------------------------------------------
+// K scoring of one token per lane.
+//
+// q'' of the (seq, KV head) is wave-uniform, so it is read with scalar loads
+// into SGPRs and used as the SGPR operand of v_fmac.  It is addressed through
+// the constant address space (it is read-only for the whole kernel), the base
+// pointer is laundered once per sub-chunk so the loads are not hoisted out of
+// the token loop, and the 128 positions are walked in groups of P: the loads of
+// group g+1 are issued before the FMAs of group g, with scheduling barriers
+// between groups so at most two groups of q'' are live in SGPRs.
+// --------------------------------------------------------------------------
+typedef const __attribute__((address_space(4))) float *cfloat_p;
+
+template <typename T>
+__device__ __forceinline__ T launder_sgpr(T p) {
+    asm volatile("" : "+s"(p));
+    return p;
+}
+
+// Positions per q'' group: 16 scalar values per buffer (two buffers live).
+template <int RP>
+constexpr int score_group() { return RP <= 1 ? 16 : RP <= 2 ? 8 : RP <= 4 ? 4 : RP <= 8 ? 2 : 1; }
+
+// Keep a wave-uniform value in a VGPR (SGPRs are reserved for q'').
+__device__ __forceinline__ float in_vgpr(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+template <int KB, int RP, int I>
+__device__ __forceinline__ void score_pos(const uint32_t *w, const float *q, const float *ktab,
+                                          float (&acc)[RP]) {
+    const float cv = ktab[stream_code<KB, I>(w)];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) acc[r] = __builtin_fmaf(q[r], cv, acc[r]);
+}
+
+template <int KB, int RP, int P, int G, int... Ps>
+__device__ __forceinline__ void score_grp(const uint32_t *w, const float *q, const float *ktab,
+                                          float (&acc)[RP], std::integer_sequence<int, Ps...>) {
+    (score_pos<KB, RP, G * P + Ps>(w, q + Ps * RP, ktab, acc), ...);
+}
+
+template <int RP, int P>
+__device__ __forceinline__ void load_q(cfloat_p qp, int g, float (&q)[P * RP]) {
+#pragma unroll
+    for (int k = 0; k < P * RP; ++k) q[k] = qp[g * P * RP + k];
+}
+
+template <int KB, int RP, int P, int G>
+__device__ __forceinline__ void score_step_g(const uint32_t *w, cfloat_p qp, float (&qa)[P * RP],
+                                             float (&qb)[P * RP], const float *ktab, float (&acc)[RP]) {
+    constexpr int NG = kD / P;
+    // qa holds group G; prefetch G+1 into qb, then compute G
+    if constexpr (G + 1 < NG) load_q<RP, P>(qp, G + 1, qb);
+    __builtin_amdgcn_sched_barrier(0);
+    score_grp<KB, RP, P, G>(w, qa, ktab, acc, std::make_integer_sequence<int, P>{});
+    // the empty volatile asm orders the group's FMAs before the next barrier
+#pragma unroll
+    for (int r = 0; r < RP; ++r) asm volatile("" : "+v"(acc[r]));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int KB, int RP, int P, int... Gs>
+__device__ __forceinline__ void score_groups(const uint32_t *w, cfloat_p qp, const float *ktab,
+                                             float (&acc)[RP], std::integer_sequence<int, Gs...>) {
+    float qa[P * RP], qb[P * RP];
+    load_q<RP, P>(qp, 0, qa);
+    // alternate the two buffers: even groups compute from qa, odd from qb
+    ((Gs % 2 == 0 ? score_step_g<KB, RP, P, Gs>(w, qp, qa, qb, ktab, acc)
+                  : score_step_g<KB, RP, P, Gs>(w, qp, qb, qa, ktab, acc)), ...);
+}
+
+template <int KB, int RP>
+__device__ __forceinline__ void score_token(const uint8_t *kcode, cfloat_p qp, const float *ktab,
+                                            float (&acc)[RP]) {
+    constexpr int P = score_group<RP>();
+    uint32_t w[4 * KB];
+    const uint4 *p = reinterpret_cast<const uint4 *>(kcode);
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+        const uint4 x = p[i];
+        w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+    }
+#pragma unroll
+    for (int r = 0; r < RP; ++r) acc[r] = 0.f;
+    score_groups<KB, RP, P>(w, qp, ktab, acc, std::make_integer_sequence<int, kD / P>{});
+}
+
+// V phase layout: LPT lanes per token, each owning PPL consecutive positions.
+template <int RP>
+constexpr int v_lanes_per_token() { return RP >= 8 ? 32 : 16; }
+
+// Code bits of lane li (positions PPL*li .. PPL*li+PPL-1) of one token's V row.
+template <int VB, int PPL>
+__device__ __forceinline__ uint32_t v_lane_bits(const uint8_t *row, int li) {
+    constexpr int nbits = VB * PPL;
+    if constexpr (nbits == 32) {
+        return *reinterpret_cast<const uint32_t *>(row + 4 * li);
+    } else if constexpr (nbits == 16) {
+        return *reinterpret_cast<const uint16_t *>(row + 2 * li);
+    } else if constexpr (nbits == 8) {
+        return row[li];
+    } else {  // 24 or 12 bits: funnel-shift from the two covering dwords of the row
+        constexpr int last = (16 * VB) / 4 - 1;
+        const int bit = nbits * li, d = bit >> 5, o = bit & 31;
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(row);
+        const uint32_t lo = w[d], hi = w[d + 1 <= last ? d + 1 : last];
+        return __builtin_amdgcn_alignbit(hi, lo, o);
+    }
+}
+
+template <int VB, int RP, int PPL>
+__device__ __forceinline__ void accum_token(uint32_t bits, const float (&wt)[RP], const float *vtab,
+                                            float (&acc)[RP][PPL]) {
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+        const float cv = vtab[(bits >> (VB * k)) & ((1u << VB) - 1u)];
+#pragma unroll
+        for (int r = 0; r < RP; ++r) acc[r][k] = __builtin_fmaf(wt[r], cv, acc[r][k]);
+    }
+}
+
+// --------------------------------------------------------------------------
+// Main pass.  Block = 256 threads = one (seq, KV head, chunk).
+// --------------------------------------------------------------------------
+// Pointers used inside the token loops are separate __restrict__ arguments so the
+// compiler may keep q'' on the scalar-load path even though the kernel stores.
+template <int RP>
+constexpr int pass_waves_per_eu() { return RP >= 8 ? 2 : 3; }
+
+template <int KB, int VB, int RP, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(pass_waves_per_eu<RP>(), 8)))
+void tq_decode_pass_kernel(DecodeArgs a,
+                           const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
+                           const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms,
+                           const float *__restrict__ qrot, const int32_t *__restrict__ block_table,
+                           const int32_t *__restrict__ seq_lens, const float *__restrict__ tile_in,
+                           const float *__restrict__ stats, float *__restrict__ part_ml,
+                           float *__restrict__ part_acc, float *__restrict__ tile_out) {
+    constexpr int RS = RP + 1;                        // padded LDS row stride
+    __shared__ float ktab[TQ_MAX_LEVELS], vtab[TQ_MAX_LEVELS];
+    __shared__ float sc[kSub * RS];                   // scores, then weights
+    __shared__ float red[4 * RP];
+    __shared__ float accbuf[(MODE == MODE_SCORE) ? 1 : RP * kD];
+    constexpr int LPT = v_lanes_per_token<RP>();      // V phase: lanes per token
+    constexpr int PPL = kD / LPT;                     // V phase: positions per lane
+    constexpr int NGRP = kSub / LPT;                  // V phase: tokens in flight per block
+    __shared__ int keep_idx[kSub];
+    __shared__ int keep_cnt[4];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = blockIdx.x % a.n_chunks;
+    const int bk = blockIdx.x / a.n_chunks;
+    const int kv = bk % a.n_kv, b = bk / a.n_kv;
+    const int len = seq_lens[b];
+    const int start = c * a.chunk;
+    if (start >= len) return;
+    const int end = min(start + a.chunk, len);
+
+    if (tid < TQ_MAX_LEVELS) {
+        ktab[tid] = a.kc[tid];
+        vtab[tid] = a.vc[tid];
+    }
+    const cfloat_p qr = reinterpret_cast<cfloat_p>(
+        reinterpret_cast<uintptr_t>(qrot + ((int64_t)b * a.n_kv + kv) * kD * RP));
+    const int32_t *__restrict__ btab = block_table + (int64_t)b * a.max_blocks;
+    const int bs = a.block_size;
+    const FastDiv bsdiv = make_fastdiv((uint32_t)bs);
+    const int last_vis = len - a.n_qtok;              // row r sees t <= last_vis + r / G
+    const int64_t part = ((int64_t)b * a.n_kv + kv) * a.n_chunks + c;
+
+    float m_run[RP], l_run[RP], gM[RP], gInvL[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; gM[r] = 0.f; gInvL[r] = 0.f; }
+    if constexpr (MODE == MODE_GATED) {
+        const float *st = stats + ((int64_t)b * a.n_kv + kv) * RP * 2;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            gM[r] = in_vgpr(st[2 * r]);
+            const float L = st[2 * r + 1];
+            gInvL[r] = in_vgpr(L > 0.f ? 1.f / L : 0.f);
+        }
+    }
+    float acc[RP][PPL];
+#pragma unroll
+    for (int r = 0; r < RP; ++r)
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) acc[r][k] = 0.f;
+    __syncthreads();
+
+    const int gi = tid / LPT, li = tid % LPT;         // V phase: token group, lane in group
+
+    for (int sub = start; sub < end; sub += kSub) {
+        // ---------------- K phase: one token per thread
+        const int t = sub + tid;
+        bool active = t < end;
+        bool score_needed = true;
+        if constexpr (MODE == MODE_GATED) {
+            // tile bound: skip the wave's 64 tokens if no row can reach tau
+            const float *tm = tile_in + (((int64_t)b * a.n_kv + kv) * a.n_tiles + (sub >> 6) + wave) * RP;
+            bool cand = false;
+#pragma unroll
+            for (int r = 0; r < RP; ++r)
+                if (r < a.rows) cand |= (exp2_diff(tm[r], gM[r]) * gInvL[r] >= a.tau);
+            score_needed = cand && (sub + wave * kTile < end);
+        }
+        float s[RP];
+        if (score_needed) {
+            int64_t row = 0;
+            if (active) {
+                const uint32_t pg = fdiv((uint32_t)t, bsdiv);
+                const int blk = btab[pg];
+                row = ((int64_t)blk * a.n_kv + kv) * bs + (t - (int)pg * bs);
+            }
+            score_token<KB, RP>(k_codes + row * (16 * KB), launder_sgpr(qr), ktab, s);
+            const float nk = active ? k_norms[row] : 0.f;
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+                const bool vis = active && (t <= last_vis + r / a.group);
+                s[r] = vis ? s[r] * nk : -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < RP; ++r) s[r] = -INFINITY;
+        }
+
+        if constexpr (MODE == MODE_GATED) {
+            bool kept = false;
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+                const float p = exp2_diff(s[r], gM[r]) * gInvL[r];
+                const bool k = (r < a.rows) && p >= a.tau && p > 0.f;
+                sc[tid * RS + r] = k ? p : 0.f;
+                kept |= k;
+            }
+            // deterministic compaction of kept tokens
+            const uint64_t bal = __ballot(kept);
+            const int before = __popcll(bal & ((1ull << lane) - 1ull));
+            if (lane == 0) keep_cnt[wave] = __popcll(bal);
+            __syncthreads();
+            int off = 0, total = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+                off += (w2 < wave) ? keep_cnt[w2] : 0;
+                total += keep_cnt[w2];
+            }
+            if (kept) keep_idx[off + before] = tid;
+            __syncthreads();
+            for (int q = gi; q < total; q += NGRP) {
+                const int tt = keep_idx[q];
+                const int tk = sub + tt;
+                const uint32_t pg = fdiv((uint32_t)tk, bsdiv);
+                const int blk = btab[pg];
+                const int64_t row = ((int64_t)blk * a.n_kv + kv) * bs + (tk - (int)pg * bs);
+                const uint32_t bits = v_lane_bits<VB, PPL>(v_codes + row * (16 * VB), li);
+                const float nv = v_norms[row];
+                float wt[RP];
+#pragma unroll
+                for (int r = 0; r < RP; ++r) wt[r] = sc[tt * RS + r] * nv;
+                accum_token<VB, RP, PPL>(bits, wt, vtab, acc);
+            }
+            __syncthreads();
+        } else {
+            // ---------------- online softmax statistics of the sub-chunk
+            float wm[RP];
+#pragma unroll
+            for (int r = 0; r < RP; ++r) wm[r] = wave_max(s[r]);
+            if constexpr (MODE == MODE_SCORE) {
+                if (lane < RP && sub + wave * kTile < end) {
+                    float v = wm[0];
+#pragma unroll
+                    for (int r = 1; r < RP; ++r) v = (lane == r) ? wm[r] : v;
+                    tile_out[(((int64_t)b * a.n_kv + kv) * a.n_tiles + (sub >> 6) + wave) * RP + lane] = v;
+                }
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int r = 0; r < RP; ++r) red[wave * RP + r] = wm[r];
+            }
+            __syncthreads();
+            float m_new[RP], alpha[RP];
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+                const float sm = fmaxf(fmaxf(red[r], red[RP + r]), fmaxf(red[2 * RP + r], red[3 * RP + r]));
+                m_new[r] = in_vgpr(fmaxf(m_run[r], sm));
+                alpha[r] = in_vgpr(exp2_diff(m_run[r], m_new[r]));
+            }
+            float e[RP];
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+                e[r] = exp2_diff(s[r], m_new[r]);
+                if constexpr (MODE == MODE_DENSE) sc[tid * RS + r] = e[r];
+            }
+            float ws[RP];
+#pragma unroll
+            for (int r = 0; r < RP; ++r) ws[r] = wave_sum(e[r]);
+            __syncthreads();                                   // everyone has read red
+            if (lane == 0) {
+#pragma unroll
+                for (int r = 0; r < RP; ++r) red[wave * RP + r] = ws[r];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+                const float ls = (red[r] + red[RP + r]) + (red[2 * RP + r] + red[3 * RP + r]);
+                l_run[r] = in_vgpr(l_run[r] * alpha[r] + ls);
+                m_run[r] = m_new[r];
+            }
+            if constexpr (MODE == MODE_DENSE) {
+#pragma unroll
+                for (int r = 0; r < RP; ++r)
+#pragma unroll
+                    for (int k = 0; k < PPL; ++k) acc[r][k] *= alpha[r];
+                // ---------------- V phase: NGRP tokens at a time, LPT lanes per token
+                const int n_sub = min(kSub, end - sub);
+                for (int tt = gi; tt < n_sub; tt += NGRP) {
+                    const int tk = sub + tt;
+                    const uint32_t pg = fdiv((uint32_t)tk, bsdiv);
+                    const int blk = btab[pg];
+                    const int64_t row = ((int64_t)blk * a.n_kv + kv) * bs + (tk - (int)pg * bs);
+                    const uint32_t bits = v_lane_bits<VB, PPL>(v_codes + row * (16 * VB), li);
+                    const float nv = v_norms[row];
+                    float wt[RP];
+#pragma unroll
+                    for (int r = 0; r < RP; ++r) wt[r] = sc[tt * RS + r] * nv;
+                    accum_token<VB, RP, PPL>(bits, wt, vtab, acc);
+                }
+            }
+            __syncthreads();                                   // sc / red reused next sub-chunk
+        }
+    }
+
+    // ---------------- write the chunk's partial results
+    if constexpr (MODE != MODE_GATED) {
+        if (tid < RP) {
+            float mv = m_run[0], lv = l_run[0];
+#pragma unroll
+            for (int r = 1; r < RP; ++r) {
+                mv = (tid == r) ? m_run[r] : mv;
+                lv = (tid == r) ? l_run[r] : lv;
+            }
+            part_ml[(part * RP + tid) * 2] = mv;
+            part_ml[(part * RP + tid) * 2 + 1] = lv;
+        }
+    }
+    if constexpr (MODE != MODE_SCORE) {
+        // sum the token groups of each wave, then the 4 waves through LDS
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+#pragma unroll
+            for (int k = 0; k < PPL; ++k) {
+                float x = acc[r][k];
+                if constexpr (LPT == 16) x += __shfl_xor(x, 16);
+                x += __shfl_xor(x, 32);
+                acc[r][k] = x;
+            }
+        for (int w2 = 0; w2 < 4; ++w2) {
+            if (wave == w2 && lane < LPT) {
+#pragma unroll
+                for (int r = 0; r < RP; ++r)
+#pragma unroll
+                    for (int k = 0; k < PPL; ++k) {
+                        float *d = &accbuf[r * kD + PPL * lane + k];
+                        *d = (w2 == 0) ? acc[r][k] : *d + acc[r][k];
+                    }
+            }
+            __syncthreads();
+        }
+        float *dst = part_acc + part * RP * kD;
+        for (int i = tid; i < RP * kD; i += kSub) dst[i] = accbuf[i];
+    }
+}
+
+#ifndef TQ_DECODE_KB
+// --------------------------------------------------------------------------
+// Global (max, sum) per row for the sparse path.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void tq_stats_kernel(DecodeArgs a) {
+    const int b = blockIdx.x / a.n_kv, kv = blockIdx.x % a.n_kv;
+    const int r = threadIdx.x;
+    if (r >= a.rows_pad) return;
+    const int len = a.seq_lens[b];
+    const int nc = (len + a.chunk - 1) / a.chunk;
+    const float *ml = a.part_ml + ((int64_t)b * a.n_kv + kv) * a.n_chunks * a.rows_pad * 2;
+    float M = -INFINITY;
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[(c * a.rows_pad + r) * 2]);
+    float L = 0.f;
+    for (int c = 0; c < nc; ++c) L += ml[(c * a.rows_pad + r) * 2 + 1] * exp2_diff(ml[(c * a.rows_pad + r) * 2], M);
+    float *st = a.stats + (((int64_t)b * a.n_kv + kv) * a.rows_pad + r) * 2;
+    st[0] = M;
+    st[1] = L;
+}
+
+// --------------------------------------------------------------------------
+// Combine chunk partials and inverse-rotate.  One wave per output row.
+// --------------------------------------------------------------------------
+template <bool SPARSE>
+__global__ __launch_bounds__(64) void tq_combine_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x;
+    const int h = blockIdx.x % a.n_q_heads;
+    const int jq = (blockIdx.x / a.n_q_heads) % a.n_qtok;
+    const int b = blockIdx.x / (a.n_q_heads * a.n_qtok);
+    const int kv = h / a.group;
+    const int r = jq * a.group + (h % a.group);
+    const int len = a.seq_lens[b];
+    const int nc = (len + a.chunk - 1) / a.chunk;
+    const int64_t base = ((int64_t)b * a.n_kv + kv) * a.n_chunks;
+    float x0 = 0.f, x1 = 0.f;
+    if (SPARSE) {
+        for (int c = 0; c < nc; ++c) {
+            const float *pa = a.part_acc + ((base + c) * a.rows_pad + r) * kD;
+            x0 += pa[lane];
+            x1 += pa[lane + 64];
+        }
+    } else {
+        float M = -INFINITY;
+        for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_ml[((base + c) * a.rows_pad + r) * 2]);
+        float L = 0.f;
+        for (int c = 0; c < nc; ++c) {
+            const float *ml = a.part_ml + ((base + c) * a.rows_pad + r) * 2;
+            const float f = exp2_diff(ml[0], M);
+            if (f == 0.f) continue;
+            const float *pa = a.part_acc + ((base + c) * a.rows_pad + r) * kD;
+            L += ml[1] * f;
+            x0 += pa[lane] * f;
+            x1 += pa[lane + 64] * f;
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        x0 *= inv;
+        x1 *= inv;
+    }
+    // o = s_V * H acc / sqrt(128)
+    float a0 = x0 + x1, a1 = x0 - x1;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float p0 = __shfl_xor(a0, m), p1 = __shfl_xor(a1, m);
+        const bool hi = lane & m;
+        a0 = hi ? p0 - a0 : a0 + p0;
+        a1 = hi ? p1 - a1 : a1 + p1;
+    }
+    const uint32_t *sg = a.v_signs + kv * 4;
+    const float k = 0.088388347648318440550f;
+    a0 *= ((sg[lane >> 5] >> (lane & 31)) & 1u) ? -k : k;
+    a1 *= ((sg[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -k : k;
+    float *o = a.out + (((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * kD;
+    o[lane] = a0;
+    o[lane + 64] = a1;
+}
+
+#endif  // !TQ_DECODE_KB
+
+// --------------------------------------------------------------------------
+// Dispatch.  The pass kernels are instantiated per K bit width in separate
+// translation units (this file compiled with TQ_DECODE_KB=2, 3, 4) so the
+// build runs in parallel; the unit without TQ_DECODE_KB holds the rest.
+// --------------------------------------------------------------------------
+void launch_pass_kb2(const DecodeArgs &a, int mode, hipStream_t s);
+void launch_pass_kb3(const DecodeArgs &a, int mode, hipStream_t s);
+void launch_pass_kb4(const DecodeArgs &a, int mode, hipStream_t s);
+
+#ifdef TQ_DECODE_KB
+template <int KB, int VB, int RP>
+static void launch_pass(const DecodeArgs &a, int mode, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_kv * a.n_chunks));
+#define TQ_PASS_ARGS a, a.k_codes, a.k_norms, a.v_codes, a.v_norms, a.qrot, a.block_table, a.seq_lens, \
+        a.tilemax, a.stats, a.part_ml, a.part_acc, a.tilemax
+    if (mode == MODE_DENSE)
+        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, VB, RP, MODE_DENSE>), grid, dim3(kSub), 0, s, TQ_PASS_ARGS);
+    else if (mode == MODE_SCORE)
+        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, 2, RP, MODE_SCORE>), grid, dim3(kSub), 0, s, TQ_PASS_ARGS);
+    else
+        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, VB, RP, MODE_GATED>), grid, dim3(kSub), 0, s, TQ_PASS_ARGS);
+#undef TQ_PASS_ARGS
+}
+
+template <int KB, int VB>
+static void launch_pass_rp(const DecodeArgs &a, int mode, hipStream_t s) {
+    switch (a.rows_pad) {
+        case 1: launch_pass<KB, VB, 1>(a, mode, s); break;
+        case 2: launch_pass<KB, VB, 2>(a, mode, s); break;
+        case 4: launch_pass<KB, VB, 4>(a, mode, s); break;
+        case 8: launch_pass<KB, VB, 8>(a, mode, s); break;
+        case 12: launch_pass<KB, VB, 12>(a, mode, s); break;
+        default: launch_pass<KB, VB, 16>(a, mode, s); break;
+    }
+}
+
+template <int KB>
+static void launch_pass_vb(const DecodeArgs &a, int mode, hipStream_t s) {
+    switch (a.v_bits) {
+        case 2: launch_pass_rp<KB, 2>(a, mode, s); break;
+        case 3: launch_pass_rp<KB, 3>(a, mode, s); break;
+        default: launch_pass_rp<KB, 4>(a, mode, s); break;
+    }
+}
+
+#define TQ_CAT2(a, b) a##b
+#define TQ_CAT(a, b) TQ_CAT2(a, b)
+void TQ_CAT(launch_pass_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStream_t s) {
+    launch_pass_vb<TQ_DECODE_KB>(a, mode, s);
+}
+
+#else
+
+static void launch_pass_any(const DecodeArgs &a, int mode, hipStream_t s) {
+    switch (a.k_bits) {
+        case 2: launch_pass_kb2(a, mode, s); break;
+        case 3: launch_pass_kb3(a, mode, s); break;
+        default: launch_pass_kb4(a, mode, s); break;
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
+    hipLaunchKernelGGL(tq_qrot_kernel, dim3(a.n_seqs * a.n_kv), dim3(64 * a.rows_pad), 0, s, a);
+    const dim3 rows_grid((unsigned)((int64_t)a.n_seqs * a.n_qtok * a.n_q_heads));
+    if (ev_before) (void)hipEventRecord(ev_before, s);
+    if (a.tau > 0.f) {
+        launch_pass_any(a, MODE_SCORE, s);
+        if (ev_after) (void)hipEventRecord(ev_after, s);
+        hipLaunchKernelGGL(tq_stats_kernel, dim3(a.n_seqs * a.n_kv), dim3(64), 0, s, a);
+        launch_pass_any(a, MODE_GATED, s);
+        hipLaunchKernelGGL(tq_combine_kernel<true>, rows_grid, dim3(64), 0, s, a);
+    } else {
+        launch_pass_any(a, MODE_DENSE, s);
+        if (ev_after) (void)hipEventRecord(ev_after, s);
+        hipLaunchKernelGGL(tq_combine_kernel<false>, rows_grid, dim3(64), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+#endif
+
+}  // namespace tq

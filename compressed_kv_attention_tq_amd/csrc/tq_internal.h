@@ -1,0 +1,90 @@
+// Internal interface between the C-ABI host layer (tq_api.cpp) and the HIP
+// kernels (tq_quant.hip, tq_decode.hip).  Kernel arguments are plain structs
+// passed by value; nothing here allocates.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kD = 128;            // elements per block
+constexpr int kSub = 256;          // decode: tokens per sub-chunk (= threads per block)
+constexpr int kTile = 64;          // decode: tokens per sparse-V gating tile (one wave)
+constexpr int kLutMax = 256;       // quantize: max entries of the encode lookup table
+
+// One side of a quantize launch.
+struct QuantSide {
+    const uint16_t *src;      // float16 bits [n_tokens][n_kv][128], token stride src_stride
+    uint8_t *codes;
+    float *norms;
+    const uint32_t *signs;    // [n_kv][4]
+    int64_t src_stride;       // elements between tokens
+    int64_t n_vec;            // n_tokens * n_kv
+    int32_t n_kv;
+    int32_t block_size;
+    int32_t bits;
+    int32_t lut_half;         // table index = floor(t) + lut_half
+    float grid;               // t = y * grid (cells of width 1/grid in y)
+    int32_t n_bnd;            // 2^bits - 1
+    float bnd[TQ_MAX_LEVELS - 1];
+};
+
+struct QuantArgs {
+    QuantSide side[2];        // [0] = K, [1] = V (a side with n_vec == 0 is skipped)
+    const int64_t *slots;
+    int32_t blocks_k;         // blocks [0, blocks_k) do side 0, the rest side 1
+};
+
+struct DequantArgs {
+    const uint8_t *codes;
+    const float *norms;
+    const uint32_t *signs;
+    const int64_t *slots;
+    void *dst;
+    int64_t n_vec;
+    int32_t n_kv;
+    int32_t block_size;
+    int32_t dst_fp16;
+    float cent[TQ_MAX_LEVELS];
+};
+
+// Decode attention.
+struct DecodeArgs {
+    const uint8_t *k_codes;
+    const float *k_norms;
+    const uint8_t *v_codes;
+    const float *v_norms;
+    const uint32_t *k_signs;
+    const uint32_t *v_signs;
+    const uint16_t *q;        // float16 [S][n_qtok][H_q][128]
+    const int32_t *seq_lens;
+    const int32_t *block_table;
+    float *out;
+    // workspace sections
+    float *qrot;              // [S][n_kv][128][RP]   rotated, scaled queries
+    float *part_ml;           // [S][n_kv][n_chunks][RP][2]  (max, sum) per chunk, log2 domain
+    float *part_acc;          // [S][n_kv][n_chunks][RP][128] rotated-domain V accumulators
+    float *tilemax;           // [S][n_kv][n_tiles][RP]  (sparse only)
+    float *stats;             // [S][n_kv][RP][2]  global (max, sum) (sparse only)
+    int32_t n_seqs, n_qtok, n_q_heads, n_kv, group, rows, rows_pad;
+    int32_t max_blocks, block_size;
+    int32_t chunk;            // tokens per chunk (multiple of kSub)
+    int32_t n_chunks;         // chunks per sequence capacity
+    int32_t n_tiles;          // tiles per sequence capacity
+    float qscale;             // softmax_scale * log2(e) / sqrt(128)
+    float tau;
+    int32_t k_bits, v_bits;
+    float kc[TQ_MAX_LEVELS];
+    float vc[TQ_MAX_LEVELS];
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_quantize(const QuantArgs &a, int blocks_total, hipStream_t s);
+hipError_t launch_dequantize(const DequantArgs &a, int bits, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_before = nullptr,
+                         hipEvent_t ev_after = nullptr);
+
+}  // namespace tq

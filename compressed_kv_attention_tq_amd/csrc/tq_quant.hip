@@ -1,0 +1,277 @@
+// Quantize-on-append and dequantize kernels (gfx950).
+//
+// Per 128-element block (see tq_device.h for the 8-lanes-per-block layout):
+//   load 16 float16 per lane, flip signs (s of the KV head) in the float16
+//   domain, sum of squares with v_dot2_f32_f16, 8-lane DPP reduction -> norm,
+//   Walsh-Hadamard transform (4 in-register stages + 3 DPP stages), scale to
+//   the encode grid, encode with a small LDS table, bit-pack, store.
+// Sources: [TQ blog] 3.2 (signs then Hadamard, fast transform), [TQ blog] 3.3
+// (Lloyd-Max codebook), [TQ+ README] quantization-types note (128-element
+// blocks) and backend table (SET_ROWS quantize-on-append).
+#include <float.h>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+struct LutEntry {
+    float thr;      // boundary * grid inside this cell, or FLT_MAX if none
+    int32_t base;   // number of boundaries entirely below the cell
+};
+
+// Encode table over cells [g, g+1) of t = y * grid, extended by a margin on both
+// sides.  The host picks grid so that no two boundaries fall in one extended
+// cell; then code(t) = base + (t > thr) for every t that floors to g.
+__device__ void build_lut(const QuantSide &p, LutEntry *lut) {
+    const int n = 2 * p.lut_half + 1;
+    for (int e = threadIdx.x; e < n; e += blockDim.x) {
+        const float g = (float)(e - p.lut_half);
+        const float lo = g - 1e-3f, hi = g + 1.0f + 1e-3f;
+        int base = 0;
+        float thr = FLT_MAX;
+        for (int b = 0; b < p.n_bnd; ++b) {
+            const float bt = p.bnd[b] * p.grid;
+            if (bt < lo) ++base;
+            else if (bt < hi) thr = bt;
+        }
+        lut[e].thr = thr;
+        lut[e].base = base;
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__restrict__ slots,
+                                           const LutEntry *lut, int blk, int nblk) {
+    const Lane8 L = lane8();
+    const int j = L.j;
+    const int wpb = blockDim.x >> 6;
+    const int wave_id = blk * wpb + (int)(threadIdx.x >> 6);
+    // The grid stride (in blocks) is a multiple of n_kv, so the head of this
+    // lane's block never changes and the token advances by a constant.
+    const int step = nblk * wpb * 8;
+    const int v0 = wave_id * 8 + L.vin;
+    const int head = v0 % p.n_kv;
+    const int tok_step = step / p.n_kv;
+    const FastDiv bsdiv = make_fastdiv((uint32_t)p.block_size);
+
+    // Sign flips of this lane's 16 elements as float16 sign-bit masks.
+    const uint32_t sb = (p.signs[head * 4 + (j >> 1)] >> ((j & 1) * 16)) & 0xFFFFu;
+    uint32_t smask[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        smask[k] = (((sb >> (2 * k)) & 1u) << 15) | (((sb >> (2 * k + 1)) & 1u) << 31);
+
+    const float kscale = lane_sign(j) * p.grid * 0.088388347648318440550f;   // grid / sqrt(128)
+    const uint16_t *src = p.src + (int64_t)head * kD + j * 16;
+    const LutEntry *lut0 = lut + p.lut_half;
+
+    int tok = v0 / p.n_kv;
+    for (int g0 = wave_id * 8; g0 < p.n_vec; g0 += step, tok += tok_step) {   // uniform per wave
+        const bool valid = g0 + L.vin < p.n_vec;
+        uint32_t w[8];
+        if (valid) {
+            const uint4 *sp = reinterpret_cast<const uint4 *>(src + (int64_t)tok * p.src_stride);
+            const uint4 a = sp[0], b = sp[1];
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) w[k] = 0;
+        }
+        const int64_t slot = valid ? slots[tok] : -1;
+
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            w[k] ^= smask[k];
+            const half2_t h = __builtin_bit_cast(half2_t, w[k]);
+            ss = __builtin_amdgcn_fdot2(h, h, ss, false);
+        }
+        ss = block8_sum(ss);
+        const bool finite = ss <= FLT_MAX;   // false for inf and NaN
+        if (!finite) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) w[k] = 0;
+        }
+        const float tscale = (finite && ss > 0.f) ? kscale * __frsqrt_rn(ss) : 0.f;
+
+        // first Hadamard stage straight from the float16 pairs, then the rest
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) half_pair_butterfly(w[k], v[2 * k], v[2 * k + 1]);
+        wht16<2>(v);
+        wht_cross(v, j);
+
+        uint32_t code[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const float t = v[k] * tscale;
+            const LutEntry e = lut0[cvt_floor(t)];
+            code[k] = (uint32_t)e.base + (t > e.thr ? 1u : 0u);
+        }
+
+        if (valid && slot >= 0) {
+            const uint32_t blk_id = fdiv((uint32_t)slot, bsdiv);
+            const uint32_t off = (uint32_t)slot - blk_id * (uint32_t)p.block_size;
+            const int64_t row = ((int64_t)blk_id * p.n_kv + head) * p.block_size + off;
+            uint8_t *dst = p.codes + row * (16 * BITS);
+            if constexpr (BITS == 4) {
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) lo |= code[k] << (4 * k);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) hi |= code[8 + k] << (4 * k);
+                *reinterpret_cast<uint2 *>(dst + 8 * j) = make_uint2(lo, hi);
+            } else if constexpr (BITS == 2) {
+                uint32_t x = 0;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) x |= code[k] << (2 * k);
+                *reinterpret_cast<uint32_t *>(dst + 4 * j) = x;
+            } else {  // 3 bits: 48 bits at byte 6j
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    if (3 * k + 3 <= 32) lo |= code[k] << (3 * k);
+                    else if (3 * k >= 32) hi |= code[k] << (3 * k - 32);
+                    else { lo |= code[k] << (3 * k); hi |= code[k] >> (32 - 3 * k); }
+                }
+                uint8_t *d = dst + 6 * j;
+                if ((j & 1) == 0) {
+                    *reinterpret_cast<uint32_t *>(d) = lo;
+                    *reinterpret_cast<uint16_t *>(d + 4) = (uint16_t)hi;
+                } else {
+                    *reinterpret_cast<uint16_t *>(d) = (uint16_t)lo;
+                    *reinterpret_cast<uint32_t *>(d + 2) = (lo >> 16) | (hi << 16);
+                }
+            }
+            if (j == 0) p.norms[row] = __fsqrt_rn(ss);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void tq_quantize_kernel(QuantArgs a) {
+    __shared__ LutEntry lut[kLutMax];
+    const bool second = (int)blockIdx.x >= a.blocks_k;
+    const QuantSide &p = second ? a.side[1] : a.side[0];
+    const int blk = second ? (int)blockIdx.x - a.blocks_k : (int)blockIdx.x;
+    const int nblk = second ? (int)gridDim.x - a.blocks_k : a.blocks_k;
+    build_lut(p, lut);
+    __syncthreads();
+    switch (p.bits) {
+        case 2: quant_side<2>(p, a.slots, lut, blk, nblk); break;
+        case 3: quant_side<3>(p, a.slots, lut, blk, nblk); break;
+        default: quant_side<4>(p, a.slots, lut, blk, nblk); break;
+    }
+}
+
+// --------------------------------------------------------------------------
+// Dequantize: x_hat = n * s * (H c[code]) / sqrt(128), same lane layout.
+// --------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(256) void tq_dequantize_kernel(DequantArgs a) {
+    __shared__ float ctab[TQ_MAX_LEVELS];
+    if (threadIdx.x < TQ_MAX_LEVELS) ctab[threadIdx.x] = a.cent[threadIdx.x];
+    __syncthreads();
+    const Lane8 L = lane8();
+    const int j = L.j;
+    const int wpb = blockDim.x >> 6;
+    const int wave_id = blockIdx.x * wpb + (int)(threadIdx.x >> 6);
+    const int step = gridDim.x * wpb * 8;
+    const float lsign = lane_sign(j) * 0.088388347648318440550f;
+    const FastDiv kvdiv = make_fastdiv((uint32_t)a.n_kv);
+    const FastDiv bsdiv = make_fastdiv((uint32_t)a.block_size);
+    for (int g0 = wave_id * 8; g0 < a.n_vec; g0 += step) {
+        const int vid = g0 + L.vin;
+        const bool valid = vid < a.n_vec;
+        const int tok = valid ? (int)fdiv((uint32_t)vid, kvdiv) : 0;
+        const int head = valid ? vid - tok * a.n_kv : 0;
+        int64_t row = 0;
+        uint32_t w[2] = {0, 0};
+        float n = 0.f;
+        if (valid) {
+            const uint32_t slot = (uint32_t)a.slots[tok];
+            const uint32_t blk_id = fdiv(slot, bsdiv);
+            const uint32_t off = slot - blk_id * (uint32_t)a.block_size;
+            row = ((int64_t)blk_id * a.n_kv + head) * a.block_size + off;
+            const uint8_t *src = a.codes + row * (16 * BITS) + 2 * BITS * j;
+            if constexpr (BITS == 4) {
+                const uint2 x = *reinterpret_cast<const uint2 *>(src);
+                w[0] = x.x; w[1] = x.y;
+            } else if constexpr (BITS == 2) {
+                w[0] = *reinterpret_cast<const uint32_t *>(src);
+            } else {
+                if ((j & 1) == 0) {
+                    w[0] = *reinterpret_cast<const uint32_t *>(src);
+                    w[1] = *reinterpret_cast<const uint16_t *>(src + 4);
+                } else {
+                    const uint32_t lo = *reinterpret_cast<const uint16_t *>(src);
+                    const uint32_t hi = *reinterpret_cast<const uint32_t *>(src + 2);
+                    w[0] = lo | (hi << 16);
+                    w[1] = hi >> 16;
+                }
+            }
+            n = a.norms[row];
+        }
+        float v[16];
+        v[0] = ctab[stream_code<BITS, 0>(w)];   v[1] = ctab[stream_code<BITS, 1>(w)];
+        v[2] = ctab[stream_code<BITS, 2>(w)];   v[3] = ctab[stream_code<BITS, 3>(w)];
+        v[4] = ctab[stream_code<BITS, 4>(w)];   v[5] = ctab[stream_code<BITS, 5>(w)];
+        v[6] = ctab[stream_code<BITS, 6>(w)];   v[7] = ctab[stream_code<BITS, 7>(w)];
+        v[8] = ctab[stream_code<BITS, 8>(w)];   v[9] = ctab[stream_code<BITS, 9>(w)];
+        v[10] = ctab[stream_code<BITS, 10>(w)]; v[11] = ctab[stream_code<BITS, 11>(w)];
+        v[12] = ctab[stream_code<BITS, 12>(w)]; v[13] = ctab[stream_code<BITS, 13>(w)];
+        v[14] = ctab[stream_code<BITS, 14>(w)]; v[15] = ctab[stream_code<BITS, 15>(w)];
+        wht16<1>(v);
+        wht_cross(v, j);
+        if (valid) {
+            const uint32_t sw = a.signs[head * 4 + (j >> 1)] >> ((j & 1) * 16);
+            const float sc = n * lsign;
+            float o[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) o[k] = ((sw >> k) & 1u) ? -v[k] * sc : v[k] * sc;
+            const int64_t dbase = ((int64_t)tok * a.n_kv + head) * kD + 16 * j;
+            if (a.dst_fp16) {
+                uint32_t h[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    half2_t x;
+                    x.x = (_Float16)o[2 * k];
+                    x.y = (_Float16)o[2 * k + 1];
+                    h[k] = __builtin_bit_cast(uint32_t, x);
+                }
+                uint4 *d = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.dst) + dbase);
+                d[0] = make_uint4(h[0], h[1], h[2], h[3]);
+                d[1] = make_uint4(h[4], h[5], h[6], h[7]);
+            } else {
+                float4 *d = reinterpret_cast<float4 *>(static_cast<float *>(a.dst) + dbase);
+                d[0] = make_float4(o[0], o[1], o[2], o[3]);
+                d[1] = make_float4(o[4], o[5], o[6], o[7]);
+                d[2] = make_float4(o[8], o[9], o[10], o[11]);
+                d[3] = make_float4(o[12], o[13], o[14], o[15]);
+            }
+        }
+    }
+}
+
+hipError_t launch_quantize(const QuantArgs &a, int blocks_total, hipStream_t s) {
+    hipLaunchKernelGGL(tq_quantize_kernel, dim3(blocks_total), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const DequantArgs &a, int bits, hipStream_t s) {
+    const int64_t waves = (a.n_vec + 7) / 8;
+    int blocks = (int)((waves + 3) / 4);
+    if (blocks > 65535) blocks = 65535;
+    if (blocks < 1) blocks = 1;
+    switch (bits) {
+        case 2: hipLaunchKernelGGL(tq_dequantize_kernel<2>, dim3(blocks), dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL(tq_dequantize_kernel<3>, dim3(blocks), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL(tq_dequantize_kernel<4>, dim3(blocks), dim3(256), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tq

@@ -1,0 +1,256 @@
+"""Python binding of libtq (include/tq.h): argument marshalling only.
+
+Every step of the hot path runs in the HIP kernels of libtq.so.  PyTorch is
+used for device memory and the current stream.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+
+Names follow the C ABI: tq_build_codebook, tq_quantize_kv,
+tq_decode_attention, tq_dequantize.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+HEAD_DIM = 128
+MAX_LEVELS = 16
+MAX_ROWS_PER_KV_HEAD = 16
+
+TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
+EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_quantize_kv", "tq_decode_attention",
+           "tq_decode_attention_timed", "tq_dequantize")
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {status_string(status)}")
+
+
+class TQCodebook(ctypes.Structure):
+    _fields_ = [
+        ("bits", ctypes.c_int32),
+        ("n_levels", ctypes.c_int32),
+        ("centroids", ctypes.c_float * MAX_LEVELS),
+        ("boundaries", ctypes.c_float * (MAX_LEVELS - 1)),
+        ("sigma", ctypes.c_float),
+        ("mse", ctypes.c_double),
+    ]
+
+    @property
+    def centroid_array(self) -> np.ndarray:
+        return np.array(self.centroids[: self.n_levels], dtype=np.float32)
+
+    @property
+    def boundary_array(self) -> np.ndarray:
+        return np.array(self.boundaries[: self.n_levels - 1], dtype=np.float32)
+
+
+class TQCache(ctypes.Structure):
+    _fields_ = [
+        ("bits", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int64),
+        ("codes", ctypes.c_void_p),
+        ("norms", ctypes.c_void_p),
+        ("signs", ctypes.c_void_p),
+        ("cb", TQCodebook),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libtq.so (raises if it is missing: there is no other implementation)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libtq.so not built at {path}; run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.tq_status_string.restype = ctypes.c_char_p
+    lib.tq_status_string.argtypes = [ctypes.c_int]
+    lib.tq_build_codebook.restype = ctypes.c_int
+    lib.tq_build_codebook.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.POINTER(TQCodebook)]
+    lib.tq_quantize_kv.restype = ctypes.c_int
+    lib.tq_quantize_kv.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.POINTER(TQCache),
+                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.tq_decode_attention.restype = ctypes.c_int
+    lib.tq_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
+                                        ctypes.c_void_p]
+    lib.tq_decode_attention_timed.restype = ctypes.c_int
+    lib.tq_decode_attention_timed.argtypes = lib.tq_decode_attention.argtypes + [ctypes.c_void_p]
+    lib.tq_dequantize.restype = ctypes.c_int
+    lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_int32, ctypes.c_void_p]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().tq_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != TQ_OK:
+        raise TQError(status, what)
+
+
+def tq_build_codebook(bits: int, sigma: float = 1.0 / math.sqrt(HEAD_DIM)) -> TQCodebook:
+    cb = TQCodebook()
+    _check(load_library().tq_build_codebook(bits, sigma, ctypes.byref(cb)), "tq_build_codebook")
+    return cb
+
+
+# ---------------------------------------------------------------------------- caches
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_ptr(t, what: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class Cache:
+    """One side (K or V) of a paged compressed cache, device memory owned by torch."""
+    bits: int
+    n_kv_heads: int
+    block_size: int
+    n_blocks: int
+    codes: object      # torch.uint8 [n_blocks, n_kv_heads, block_size, 16*bits]
+    norms: object      # torch.float32 [n_blocks, n_kv_heads, block_size]
+    signs: object      # torch.int32 (bit pattern of uint32) [n_kv_heads, 4]
+    cb: TQCodebook
+
+    @classmethod
+    def allocate(cls, bits, n_kv_heads, block_size, n_blocks, sign_words, device="cuda", cb=None):
+        torch = _torch()
+        codes = torch.zeros((n_blocks, n_kv_heads, block_size, 16 * bits), dtype=torch.uint8, device=device)
+        norms = torch.zeros((n_blocks, n_kv_heads, block_size), dtype=torch.float32, device=device)
+        sw = np.ascontiguousarray(np.asarray(sign_words, dtype=np.uint32).reshape(n_kv_heads, 4))
+        signs = torch.from_numpy(sw.view(np.int32)).to(device)
+        return cls(bits, n_kv_heads, block_size, n_blocks, codes, norms, signs,
+                   tq_build_codebook(bits) if cb is None else cb)
+
+    def desc(self) -> TQCache:
+        d = TQCache()
+        d.bits = self.bits
+        d.n_kv_heads = self.n_kv_heads
+        d.head_dim = HEAD_DIM
+        d.block_size = self.block_size
+        d.n_blocks = self.n_blocks
+        d.codes = _dev_ptr(self.codes, "codes").value
+        d.norms = _dev_ptr(self.norms, "norms").value
+        d.signs = _dev_ptr(self.signs, "signs").value
+        d.cb = self.cb
+        return d
+
+
+def tq_quantize_kv(k_cache: Cache | None, k_src, v_cache: Cache | None, v_src, slot_mapping, stream=None):
+    """Quantize-on-append: k_src / v_src float16 [n_tokens, n_kv_heads, 128] (token stride
+    taken from the tensor), slot_mapping int64 [n_tokens] (negative = skip)."""
+    torch = _torch()
+    src = k_src if k_src is not None else v_src
+    if src is None:
+        return
+    n_tokens = src.shape[0]
+    stride = src.stride(0)
+    for t, name in ((k_src, "k_src"), (v_src, "v_src")):
+        if t is None:
+            continue
+        if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 3 or t.shape[2] != HEAD_DIM:
+            raise ValueError(f"{name} must be a float16 device tensor [n_tokens, n_kv_heads, 128]")
+        if t.stride(2) != 1 or t.stride(1) != HEAD_DIM or t.stride(0) != stride or t.shape[0] != n_tokens:
+            raise ValueError(f"{name}: heads must be contiguous and both sides share one token stride")
+    kd = ctypes.byref(k_cache.desc()) if k_cache is not None else None
+    vd = ctypes.byref(v_cache.desc()) if v_cache is not None else None
+    st = load_library().tq_quantize_kv(
+        kd, ctypes.c_void_p(k_src.data_ptr()) if k_src is not None else None,
+        vd, ctypes.c_void_p(v_src.data_ptr()) if v_src is not None else None,
+        stride, n_tokens, _dev_ptr(slot_mapping, "slot_mapping", torch.int64), _stream_ptr(stream))
+    _check(st, "tq_quantize_kv")
+
+
+def decode_workspace_bytes(k_cache: Cache, v_cache: Cache, n_seqs, n_qtok, n_q_heads, max_blocks_per_seq,
+                           tau=0.0) -> int:
+    size = ctypes.c_size_t(0)
+    st = load_library().tq_decode_attention(ctypes.byref(k_cache.desc()), ctypes.byref(v_cache.desc()), None,
+                                            n_seqs, n_qtok, n_q_heads, None, None, max_blocks_per_seq,
+                                            0.0, float(tau), None, None, ctypes.byref(size), None)
+    _check(st, "tq_decode_attention (workspace query)")
+    return size.value
+
+
+def tq_decode_attention(k_cache: Cache, v_cache: Cache, q, seq_lens, block_table, softmax_scale=0.0,
+                        sparse_v_tau=0.0, out=None, workspace=None, stream=None, events=None):
+    """q float16 [n_seqs, n_qtok, n_q_heads, 128]; seq_lens int32 [n_seqs];
+    block_table int32 [n_seqs, max_blocks].  Returns float32 out like q.
+    events: optional pair of torch.cuda.Event (enable_timing) recorded around the
+    main pass kernel (tq_decode_attention_timed)."""
+    torch = _torch()
+    n_seqs, n_qtok, n_q_heads, hd = q.shape
+    if hd != HEAD_DIM:
+        raise ValueError("head_dim must be 128")
+    max_blocks = block_table.shape[1]
+    need = decode_workspace_bytes(k_cache, v_cache, n_seqs, n_qtok, n_q_heads, max_blocks, sparse_v_tau)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((n_seqs, n_qtok, n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    size = ctypes.c_size_t(workspace.numel())
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * 2)(events[0].cuda_event, events[1].cuda_event)
+    st = load_library().tq_decode_attention_timed(
+        ctypes.byref(k_cache.desc()), ctypes.byref(v_cache.desc()), _dev_ptr(q, "q", torch.float16),
+        n_seqs, n_qtok, n_q_heads, _dev_ptr(seq_lens, "seq_lens", torch.int32),
+        _dev_ptr(block_table, "block_table", torch.int32), max_blocks, float(softmax_scale),
+        float(sparse_v_tau), _dev_ptr(out, "out", torch.float32), _dev_ptr(workspace, "workspace"),
+        ctypes.byref(size), _stream_ptr(stream), ev)
+    _check(st, "tq_decode_attention")
+    return out
+
+
+def tq_dequantize(cache: Cache, slots, fp16=False, out=None, stream=None):
+    """Dequantized rows [n_tokens, n_kv_heads, 128] of the given slots (int64)."""
+    torch = _torch()
+    n = slots.shape[0]
+    if out is None:
+        out = torch.empty((n, cache.n_kv_heads, HEAD_DIM), dtype=torch.float16 if fp16 else torch.float32,
+                          device=slots.device)
+    st = load_library().tq_dequantize(ctypes.byref(cache.desc()), _dev_ptr(slots, "slots", torch.int64), n,
+                                      _dev_ptr(out, "out"), 1 if fp16 else 0, _stream_ptr(stream))
+    _check(st, "tq_dequantize")
+    return out

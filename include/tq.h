@@ -1,0 +1,187 @@
+/*
+ * tq.h - C ABI of libtq: TurboQuant-style KV-cache compression and the decode
+ * attention that reads the compressed cache, for AMD MI355X (gfx950).
+ *
+ * Sources, cited by key (page title, then the section / table used):
+ *   [llama-tq]    zingnex thread "llama-tq：让大模型在消费级显卡上跑起10万token长上下文的
+ *                 技术突破", section "KV缓存量化的技术困境与TurboQuant的解决方案": K is
+ *                 compressed with a randomized Hadamard transform plus a Lloyd-Max
+ *                 codebook, and Q.K is computed in the Hadamard domain so K is never
+ *                 dequantized during attention; K and V types are chosen separately.
+ *   [TQ+ README]  bittide repost of the "TheTom/llama-cpp-turboquant" README
+ *                 ("llama.cpp + TurboQuant+"): "量化类型" table and note (Walsh-Hadamard
+ *                 rotation then codebook quantization of 128-element blocks; turbo2 /
+ *                 turbo3 / turbo4); "压缩策略" (sparse V dequantization below a softmax
+ *                 weight threshold); "后端覆盖" table (SET_ROWS quantize-on-append for
+ *                 turbo types; VEC flash attention forced for quantized KV on HIP).
+ *   [TQ+ article] zingnex thread "TurboQuant+：面向生产环境的LLM KV缓存与权重量化技术",
+ *                 "注意力门控稀疏V解压" (skipped V positions are treated as zero).
+ *   [TQ blog]     intelliparadigm TurboQuant article: section 3.2 (H_random = D x H,
+ *                 D a random +-1 diagonal; fast Hadamard transform O(d log d)),
+ *                 section 3.3 (Lloyd-Max: nearest-centre assignment and mean update,
+ *                 separate quantizers for K and V), section 4.1 table (3.25 / 4.25 bits
+ *                 per value for turbo3 / turbo4).
+ *
+ * Format (fixed here where the pages are silent):
+ *   - Block = one 128-element K or V head vector x (float16).
+ *   - n = ||x||_2 stored as float32; u = x / n (u = 0 for a zero vector).
+ *   - y = H (s * u) / sqrt(128): s the +-1 signs of the KV head (signs first,
+ *     then the natural-order Sylvester Hadamard matrix H[i][j] = (-1)^popcount(i&j)).
+ *   - code_i = number of codebook boundaries strictly below y_i.
+ *   - 128 codes packed LSB-first: code i occupies bits [b*i, b*i+b) of the block's
+ *     16*b-byte bitstream, stream bit k being bit k%8 of byte k/8.
+ *   - Dequantized vector: x_hat = n * s * (H c[code]) / sqrt(128).
+ *   Storage is b + 0.25 bits per value (the [TQ blog] 4.1 figures for b = 3, 4).
+ *
+ * Conventions for every call:
+ *   - Pointers documented "device" are HIP device pointers; "host" are host memory.
+ *   - The library allocates no device memory and keeps no global state; every
+ *     buffer belongs to the caller.  Calls are asynchronous on `stream` (a
+ *     hipStream_t; NULL is the default stream) and may be captured in a HIP graph.
+ *   - All arguments are validated on the host before anything is launched; an
+ *     invalid call returns an error and launches nothing.  Contents of device
+ *     buffers (slots, block ids, lengths) cannot be checked on the host: values
+ *     outside the documented ranges are undefined behaviour.
+ *   - TQ_ERR_HIP is returned when a kernel launch fails; faults inside kernels
+ *     surface on the stream, as for any HIP kernel.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tq_status {
+    TQ_OK = 0,
+    TQ_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, inconsistent shape */
+    TQ_ERR_UNSUPPORTED = 2,   /* bits not in the supported set, head_dim != 128, too many rows */
+    TQ_ERR_WORKSPACE = 3,     /* workspace smaller than the size this call needs */
+    TQ_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} tq_status;
+
+#define TQ_HEAD_DIM 128
+#define TQ_MAX_LEVELS 16
+#define TQ_MAX_ROWS_PER_KV_HEAD 16   /* (n_q_heads / n_kv_heads) * n_qtok */
+
+/* Scalar codebook of one cache side ([TQ blog] 3.3).  Centroids are the Lloyd-Max
+ * quantizer of N(0, sigma^2) rounded to float16-exact values; boundaries are the
+ * exact midpoints of neighbouring centroids. */
+typedef struct tq_codebook {
+    int32_t bits;                          /* 1..4 (caches use 2..4) */
+    int32_t n_levels;                      /* 1 << bits */
+    float   centroids[TQ_MAX_LEVELS];      /* ascending, antisymmetric; unused tail is 0 */
+    float   boundaries[TQ_MAX_LEVELS - 1]; /* boundaries[j] = (c[j] + c[j+1]) / 2 */
+    float   sigma;                         /* the sigma the codebook was built for */
+    double  mse;                           /* expected squared error for N(0, sigma^2) */
+} tq_codebook;
+
+/* One side (K or V) of a paged compressed cache.  A contiguous cache is the case
+ * of an identity page table.  Descriptor lives in host memory; the arrays it
+ * points to are device memory owned by the caller. */
+typedef struct tq_cache {
+    int32_t  bits;          /* 2, 3 or 4; must equal cb.bits */
+    int32_t  n_kv_heads;    /* >= 1 */
+    int32_t  head_dim;      /* must be 128 */
+    int32_t  block_size;    /* tokens per page, >= 1 */
+    int64_t  n_blocks;      /* pages in the pool, >= 1 */
+    uint8_t *codes;         /* device uint8 [n_blocks][n_kv_heads][block_size][16*bits] */
+    float   *norms;         /* device float [n_blocks][n_kv_heads][block_size] */
+    const uint32_t *signs;  /* device uint32 [n_kv_heads][4]; bit i of word w set means
+                               element 32*w+i is multiplied by -1 before H */
+    tq_codebook cb;         /* by value */
+} tq_cache;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *tq_status_string(tq_status status);
+
+/* Lloyd-Max codebook for N(0, sigma^2) ([TQ blog] 3.3: centres and nearest-centre
+ * cells refined alternately until they stop moving; here with the Gaussian density
+ * in place of data points, which is the law of a rotated coordinate of a random
+ * unit 128-vector for sigma = 1/sqrt(128)).  Host only; deterministic.
+ *   bits  : 1..4            sigma : > 0 (caches use 1/sqrt(128))
+ *   out   : host, filled on success.
+ * Errors: TQ_ERR_INVALID_ARG (out NULL, sigma <= 0 or not finite),
+ *         TQ_ERR_UNSUPPORTED (bits outside 1..4). */
+tq_status tq_build_codebook(int32_t bits, double sigma, tq_codebook *out);
+
+/* Quantize-on-append ([TQ+ README] backend table, SET_ROWS for turbo types):
+ * compress n_tokens new K and V rows and write them into their cache slots.
+ *   k, v            : host descriptors; either may be NULL to skip that side.
+ *   k_src, v_src    : device float16 [n_tokens][n_kv_heads][128] of the side's cache;
+ *                     heads of one token are contiguous, tokens are
+ *                     src_token_stride elements apart (>= n_kv_heads * 128).
+ *   slot_mapping    : device int64 [n_tokens]; slot = block * block_size + offset,
+ *                     0 <= slot < n_blocks * block_size; a negative slot skips the token.
+ *   n_tokens        : >= 0 (0 is a no-op).
+ * For each (token, head): norm -> cache.norms, 16*bits code bytes -> cache.codes.
+ * Errors: TQ_ERR_INVALID_ARG (missing pointers for a side that is given, bad
+ *         stride or sizes, codebook inconsistent with bits), TQ_ERR_UNSUPPORTED
+ *         (bits not 2..4, head_dim != 128), TQ_ERR_HIP. */
+tq_status tq_quantize_kv(const tq_cache *k, const void *k_src,
+                         const tq_cache *v, const void *v_src,
+                         int64_t src_token_stride, int32_t n_tokens,
+                         const int64_t *slot_mapping, void *stream);
+
+/* Decode attention over the compressed cache ([llama-tq] Hadamard-domain Q.K;
+ * [TQ+ README] VEC flash attention for quantized KV and sparse V dequantization;
+ * [TQ+ article] skipped V treated as zero).
+ *   k, v               : host descriptors of the two sides (same n_kv_heads and
+ *                        block_size; bits may differ).
+ *   q                  : device float16 [n_seqs][n_qtok][n_q_heads][128].
+ *   n_seqs >= 0, n_qtok >= 1, n_q_heads a multiple of n_kv_heads with
+ *   (n_q_heads / n_kv_heads) * n_qtok <= TQ_MAX_ROWS_PER_KV_HEAD.
+ *   seq_lens           : device int32 [n_seqs], 0 <= len <= max_blocks_per_seq*block_size;
+ *                        each length includes the n_qtok new tokens.
+ *   block_table        : device int32 [n_seqs][max_blocks_per_seq]; entry p is the
+ *                        physical page holding positions [p*block_size, (p+1)*block_size).
+ *   softmax_scale      : > 0, or 0 for 1/sqrt(128).
+ *   sparse_v_tau       : >= 0.  With p the final normalised softmax weight, position t
+ *                        contributes p_t * v_hat_t iff p_t >= tau (no renormalisation);
+ *                        0 is dense attention.
+ *   out                : device float32 [n_seqs][n_qtok][n_q_heads][128].
+ *   workspace          : device scratch of *workspace_bytes bytes, 256-byte aligned;
+ *                        NULL queries the size: the required size is written to
+ *                        *workspace_bytes and nothing is launched.
+ * Query token j of a sequence of length len attends to positions t <= len - n_qtok + j;
+ * query head h reads KV head h / (n_q_heads / n_kv_heads).  A row that sees no
+ * position outputs zeros.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+tq_status tq_decode_attention(const tq_cache *k, const tq_cache *v, const void *q,
+                              int32_t n_seqs, int32_t n_qtok, int32_t n_q_heads,
+                              const int32_t *seq_lens, const int32_t *block_table,
+                              int32_t max_blocks_per_seq, float softmax_scale,
+                              float sparse_v_tau, float *out, void *workspace,
+                              size_t *workspace_bytes, void *stream);
+
+/* Same call as tq_decode_attention, for timing the dominant kernel: when `events`
+ * is not NULL, events[0] and events[1] (hipEvent_t handles created by the caller)
+ * are recorded on `stream` immediately before and after the main pass kernel (the
+ * one that streams every K code: the dense pass, or the scoring pass when
+ * sparse_v_tau > 0).  events == NULL behaves exactly like tq_decode_attention.
+ * Errors: as tq_decode_attention. */
+tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const void *q,
+                                    int32_t n_seqs, int32_t n_qtok, int32_t n_q_heads,
+                                    const int32_t *seq_lens, const int32_t *block_table,
+                                    int32_t max_blocks_per_seq, float softmax_scale,
+                                    float sparse_v_tau, float *out, void *workspace,
+                                    size_t *workspace_bytes, void *stream, void *const *events);
+
+/* Dequantize cache rows: dst[t][h][:] = x_hat of slot slots[t], head h
+ * ([llama-tq]: K needs no dequantization inside attention; this is the explicit
+ * inverse for everything else).
+ *   c           : host descriptor.
+ *   slots       : device int64 [n_tokens], each in [0, n_blocks*block_size).
+ *   dst         : device [n_tokens][n_kv_heads][128], float16 if dst_is_fp16 else float32.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
+tq_status tq_dequantize(const tq_cache *c, const int64_t *slots, int32_t n_tokens,
+                        void *dst, int32_t dst_is_fp16, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -243,16 +243,27 @@ def bits_per_value(bits: int) -> float:
 # Quantize one 128-vector  (R3, R5; [llama-tq]; [TQ+ README] types note)
 # ---------------------------------------------------------------------------
 
+_CHUNK = 1 << 20   # elements per step, only to bound temporary memory
+
+
 def encode(y: np.ndarray, boundaries: np.ndarray) -> np.ndarray:
     """code = #{j : y > boundary_j} (nearest centre with ties to the lower code, R5)."""
     y = np.asarray(y, dtype=np.float64)
-    return np.sum(y[..., None] > boundaries, axis=-1).astype(np.uint8)
+    flat = y.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i in range(0, flat.size, _CHUNK):
+        out[i:i + _CHUNK] = np.sum(flat[i:i + _CHUNK, None] > boundaries, axis=-1)
+    return out.reshape(y.shape)
 
 
 def near_boundary_mask(y: np.ndarray, boundaries: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     """Elements whose rotated value lies within eps of some decision boundary."""
     y = np.asarray(y, dtype=np.float64)
-    return np.any(np.abs(y[..., None] - boundaries) < eps, axis=-1)
+    flat = y.reshape(-1)
+    out = np.empty(flat.shape, dtype=bool)
+    for i in range(0, flat.size, _CHUNK):
+        out[i:i + _CHUNK] = np.any(np.abs(flat[i:i + _CHUNK, None] - boundaries) < eps, axis=-1)
+    return out.reshape(y.shape)
 
 
 def quantize_vectors(x: np.ndarray, s: np.ndarray, cb: Codebook):

@@ -1,0 +1,73 @@
+"""Helpers for the GPU parity tests: oracle caches, upload, comparisons.
+
+Every expected value comes from the oracle; GPU results are only compared.
+"""
+
+import numpy as np
+
+import oracle as O
+from compressed_kv_attention_tq_amd import tq as T
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def oracle_cache(wl, side, seqs=None, n_blocks=None):
+    """Quantize the workload's K (side 0) or V (side 1) with the oracle into pages."""
+    bits = wl.k_bits if side == 0 else wl.v_bits
+    signs = wl.signs_k if side == 0 else wl.signs_v
+    cb = O.build_codebook(bits)
+    c = O.new_cache(bits, wl.n_kv_heads, wl.block_size, n_blocks or wl.n_blocks, signs, cb)
+    for b in (range(wl.n_seqs) if seqs is None else seqs):
+        if int(wl.seq_lens[b]) == 0:
+            continue
+        k, v = wl.kv_source(b)
+        O.cache_write(c, k if side == 0 else v, wl.slots(b))
+    return c
+
+
+def gpu_cache_from(oc, device="cuda"):
+    """A device cache holding exactly the oracle cache's codes and norms."""
+    t = torch()
+    g = T.Cache.allocate(oc.bits, oc.n_kv_heads, oc.block_size, oc.n_blocks, oc.signs, device)
+    g.codes.copy_(t.from_numpy(oc.codes))
+    g.norms.copy_(t.from_numpy(oc.norms))
+    return g
+
+
+def upload_blocks(oc, g, blocks):
+    """Overwrite the given pages of a device cache with the oracle's pages."""
+    t = torch()
+    idx = t.as_tensor(np.asarray(blocks, np.int64), device=g.codes.device)
+    g.codes.index_copy_(0, idx, t.from_numpy(oc.codes[blocks]).to(g.codes.device))
+    g.norms.index_copy_(0, idx, t.from_numpy(oc.norms[blocks]).to(g.norms.device))
+
+
+def row_rel_err(got, want):
+    """Per-row ||got - want|| / ||want|| over the last axis (rows with ||want|| = 0 use 1)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    num = np.linalg.norm(got - want, axis=-1)
+    den = np.linalg.norm(want, axis=-1)
+    return num / np.where(den > 0, den, 1.0)
+
+
+def check_codes(gpu_packed, gpu_norms, x16, signs_words, bits, eps=1e-6):
+    """Compare GPU-written packed codes / norms of rows x16 [n, 128] against the oracle.
+
+    Returns the number of elements excluded as within eps of a decision boundary.
+    Codes must match bit-exactly elsewhere; norms within 1e-6 relative.
+    """
+    cb = O.build_codebook(bits)
+    s = O.sign_vector(signs_words)
+    n, codes, y = O.quantize_vectors(x16, s, cb)
+    got = O.unpack_codes(gpu_packed, bits)
+    near = O.near_boundary_mask(y, cb.boundaries, eps)
+    bad = (got != codes) & ~near
+    assert not bad.any(), f"{int(bad.sum())} code mismatches away from boundaries"
+    nf = n.astype(np.float64)
+    gn = np.asarray(gpu_norms, np.float64)
+    assert np.all(np.abs(gn - nf) <= 1e-6 * np.maximum(nf, 1e-30)), "norm mismatch"
+    return int(near.sum())

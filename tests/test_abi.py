@@ -1,0 +1,169 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+function include/tq.h declares, builds the same codebook as the oracle, and
+rejects invalid arguments on the host before launching anything."""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from compressed_kv_attention_tq_amd import tq as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(T.LIB_PATH), reason="libtq.so not built")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = T.load_library()
+    names = header_functions()
+    assert set(names) == set(T.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code, name in [(0, "TQ_OK"), (1, "TQ_ERR_INVALID_ARG"), (2, "TQ_ERR_UNSUPPORTED"),
+                       (3, "TQ_ERR_WORKSPACE"), (4, "TQ_ERR_HIP")]:
+        assert T.status_string(code) == name
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_matches_oracle_bit_exact(bits):
+    cb = T.tq_build_codebook(bits)
+    ref = O.build_codebook(bits)
+    assert cb.bits == bits and cb.n_levels == 1 << bits
+    assert np.array_equal(cb.centroid_array, ref.centroids.astype(np.float32))
+    assert np.array_equal(cb.boundary_array, ref.boundaries.astype(np.float32))
+    assert math.isclose(cb.mse, ref.mse, rel_tol=1e-9)
+    assert list(cb.centroids[cb.n_levels:]) == [0.0] * (16 - cb.n_levels)
+
+
+def test_codebook_other_sigma_scales():
+    a = T.tq_build_codebook(3, 1.0)
+    b = T.tq_build_codebook(3, 0.5)
+    ref = O.build_codebook(3, 0.5)
+    assert np.array_equal(b.centroid_array, ref.centroids.astype(np.float32))
+    assert np.allclose(a.centroid_array * 0.5, b.centroid_array, rtol=1e-3)
+
+
+def test_codebook_rejects_bad_arguments():
+    lib = T.load_library()
+    cb = T.TQCodebook()
+    assert lib.tq_build_codebook(0, 0.1, ctypes.byref(cb)) == T.TQ_ERR_UNSUPPORTED
+    assert lib.tq_build_codebook(5, 0.1, ctypes.byref(cb)) == T.TQ_ERR_UNSUPPORTED
+    assert lib.tq_build_codebook(2, 0.0, ctypes.byref(cb)) == T.TQ_ERR_INVALID_ARG
+    assert lib.tq_build_codebook(2, -1.0, ctypes.byref(cb)) == T.TQ_ERR_INVALID_ARG
+    assert lib.tq_build_codebook(2, float("nan"), ctypes.byref(cb)) == T.TQ_ERR_INVALID_ARG
+    assert lib.tq_build_codebook(2, 0.1, None) == T.TQ_ERR_INVALID_ARG
+
+
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced: every call below fails validation
+
+
+def fake_cache(bits=4, n_kv=2, block_size=256, n_blocks=4, head_dim=128):
+    d = T.TQCache()
+    d.bits, d.n_kv_heads, d.head_dim, d.block_size, d.n_blocks = bits, n_kv, head_dim, block_size, n_blocks
+    d.codes, d.norms, d.signs = FAKE, FAKE + 0x100000, FAKE + 0x200000
+    if 1 <= bits <= 4:
+        d.cb = T.tq_build_codebook(bits)
+    return d
+
+
+def decode_call(k=None, v=None, n_seqs=1, n_qtok=1, n_q_heads=2, max_blocks=4, scale=0.0, tau=0.0,
+                ws=None, ws_bytes=None, q=FAKE, out=FAKE):
+    lib = T.load_library()
+    k = fake_cache() if k is None else k
+    v = fake_cache(bits=3) if v is None else v
+    size = ctypes.c_size_t(0 if ws_bytes is None else ws_bytes)
+    st = lib.tq_decode_attention(ctypes.byref(k), ctypes.byref(v), q, n_seqs, n_qtok, n_q_heads, FAKE, FAKE,
+                                 max_blocks, scale, tau, out, ws, ctypes.byref(size), None)
+    return st, size.value
+
+
+def test_decode_workspace_query():
+    st, size = decode_call()
+    assert st == T.TQ_OK and size > 0 and size % 256 == 0
+    st, size_sparse = decode_call(tau=1e-4)
+    assert st == T.TQ_OK and size_sparse > size
+    st, size0 = decode_call(n_seqs=0)
+    assert st == T.TQ_OK and size0 == 0
+    st, big = decode_call(n_seqs=8, max_blocks=64)
+    assert big > size
+
+
+def test_decode_validation_errors():
+    assert decode_call(k=fake_cache(head_dim=64))[0] == T.TQ_ERR_UNSUPPORTED
+    assert decode_call(k=fake_cache(bits=5))[0] == T.TQ_ERR_UNSUPPORTED
+    assert decode_call(v=fake_cache(bits=3, n_kv=4))[0] == T.TQ_ERR_INVALID_ARG
+    assert decode_call(v=fake_cache(bits=3, block_size=128))[0] == T.TQ_ERR_INVALID_ARG
+    assert decode_call(n_q_heads=3)[0] == T.TQ_ERR_INVALID_ARG         # not a multiple of n_kv
+    assert decode_call(n_q_heads=2 * 17)[0] == T.TQ_ERR_UNSUPPORTED    # 17 rows per KV head
+    assert decode_call(n_q_heads=2 * 4, n_qtok=5)[0] == T.TQ_ERR_UNSUPPORTED
+    assert decode_call(n_qtok=0)[0] == T.TQ_ERR_INVALID_ARG
+    assert decode_call(n_seqs=-1)[0] == T.TQ_ERR_INVALID_ARG
+    assert decode_call(max_blocks=0)[0] == T.TQ_ERR_INVALID_ARG
+    assert decode_call(tau=-1.0)[0] == T.TQ_ERR_INVALID_ARG
+    assert decode_call(tau=float("nan"))[0] == T.TQ_ERR_INVALID_ARG
+    assert decode_call(scale=-0.1)[0] == T.TQ_ERR_INVALID_ARG
+    bad_cb = fake_cache()
+    bad_cb.cb.bits = 3
+    assert decode_call(k=bad_cb)[0] == T.TQ_ERR_INVALID_ARG
+    null_codes = fake_cache()
+    null_codes.codes = None
+    assert decode_call(k=null_codes)[0] == T.TQ_ERR_INVALID_ARG
+    misaligned = fake_cache()
+    misaligned.codes = FAKE + 4
+    assert decode_call(k=misaligned)[0] == T.TQ_ERR_INVALID_ARG
+    _, need = decode_call()
+    assert decode_call(ws=FAKE, ws_bytes=need - 1)[0] == T.TQ_ERR_WORKSPACE
+    assert decode_call(ws=FAKE + 16, ws_bytes=need)[0] == T.TQ_ERR_INVALID_ARG   # not 256-aligned
+    assert decode_call(ws=FAKE, ws_bytes=need, q=None)[0] == T.TQ_ERR_INVALID_ARG
+    assert decode_call(ws=FAKE, ws_bytes=need, out=None)[0] == T.TQ_ERR_INVALID_ARG
+    lib = T.load_library()
+    k, v = fake_cache(), fake_cache(bits=3)
+    assert lib.tq_decode_attention(ctypes.byref(k), ctypes.byref(v), FAKE, 1, 1, 2, FAKE, FAKE, 4, 0.0, 0.0,
+                                   FAKE, None, None, None) == T.TQ_ERR_INVALID_ARG
+
+
+def test_quantize_validation_errors():
+    lib = T.load_library()
+    k, v = fake_cache(), fake_cache(bits=3)
+    call = lambda kk, ks, vv, vs, stride=256, n=4, slots=FAKE: lib.tq_quantize_kv(
+        ctypes.byref(kk) if kk is not None else None, ks, ctypes.byref(vv) if vv is not None else None, vs,
+        stride, n, slots, None)
+    assert call(k, FAKE, v, FAKE, n=-1) == T.TQ_ERR_INVALID_ARG
+    assert call(k, None, v, FAKE) == T.TQ_ERR_INVALID_ARG
+    assert call(k, FAKE + 2, v, FAKE) == T.TQ_ERR_INVALID_ARG          # src not 16-byte aligned
+    assert call(k, FAKE, v, FAKE, stride=255) == T.TQ_ERR_INVALID_ARG   # < n_kv * 128
+    assert call(k, FAKE, v, FAKE, stride=260) == T.TQ_ERR_INVALID_ARG   # not a multiple of 8
+    assert call(k, FAKE, v, FAKE, slots=None) == T.TQ_ERR_INVALID_ARG
+    assert call(k, FAKE, fake_cache(bits=3, n_kv=4), FAKE, stride=512) == T.TQ_ERR_INVALID_ARG
+    assert call(fake_cache(head_dim=96), FAKE, None, None) == T.TQ_ERR_UNSUPPORTED
+    assert call(fake_cache(bits=1), FAKE, None, None) == T.TQ_ERR_UNSUPPORTED
+    assert call(fake_cache(block_size=1 << 20, n_blocks=1 << 12), FAKE, None, None) == T.TQ_ERR_UNSUPPORTED
+    # no-ops: nothing to do, nothing launched
+    assert call(k, FAKE, v, FAKE, n=0) == T.TQ_OK
+    assert call(None, None, None, None) == T.TQ_OK
+
+
+def test_dequantize_validation_errors():
+    lib = T.load_library()
+    c = fake_cache()
+    assert lib.tq_dequantize(ctypes.byref(c), FAKE, -1, FAKE, 0, None) == T.TQ_ERR_INVALID_ARG
+    assert lib.tq_dequantize(ctypes.byref(c), None, 4, FAKE, 0, None) == T.TQ_ERR_INVALID_ARG
+    assert lib.tq_dequantize(ctypes.byref(c), FAKE, 4, None, 0, None) == T.TQ_ERR_INVALID_ARG
+    assert lib.tq_dequantize(ctypes.byref(c), FAKE, 4, FAKE + 8, 0, None) == T.TQ_ERR_INVALID_ARG
+    assert lib.tq_dequantize(ctypes.byref(fake_cache(head_dim=256)), FAKE, 4, FAKE, 0, None) == T.TQ_ERR_UNSUPPORTED
+    assert lib.tq_dequantize(ctypes.byref(c), FAKE, 0, FAKE, 0, None) == T.TQ_OK
+    assert lib.tq_dequantize(None, FAKE, 4, FAKE, 0, None) == T.TQ_ERR_INVALID_ARG

@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path (called through the C ABI) against the CPU oracle.
+
+Codes must be bit-exact except elements whose rotated value lies within 1e-6 of
+a decision boundary (excluded, counted, printed).  Norms within 1e-6 relative.
+Attention rows within 1e-3 relative L2 of the float64 oracle computed on the
+same cache contents (the cache given to both sides is written by the oracle).
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from compressed_kv_attention_tq_amd import tq as T
+from compressed_kv_attention_tq_amd import workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+ATOL_ROW = 1e-3
+
+
+def _t():
+    import torch
+    return torch
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    torch = _t()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    T.load_library()
+    yield
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# --------------------------------------------------------------------------- quantize
+
+def quantize_and_compare(x16, signs, bits, block_size=16, slot_perm=None, token_pad=0):
+    """GPU-quantize x16 [n_tok, n_kv, 128] into a fresh cache and compare with the oracle."""
+    torch = _t()
+    n_tok, n_kv, _ = x16.shape
+    n_blocks = max(1, -(-n_tok // block_size)) + 1
+    slots = np.arange(n_tok, dtype=np.int64) if slot_perm is None else slot_perm
+    g = T.Cache.allocate(bits, n_kv, block_size, n_blocks, signs)
+    g.codes.fill_(0xAB)
+    src = np.zeros((n_tok, n_kv * 128 + token_pad), np.float16)
+    src[:, : n_kv * 128] = x16.reshape(n_tok, -1)
+    src_t = torch.from_numpy(src).cuda()
+    view = src_t[:, : n_kv * 128].view(n_tok, n_kv, 128) if token_pad == 0 else \
+        torch.as_strided(src_t, (n_tok, n_kv, 128), (n_kv * 128 + token_pad, 128, 1))
+    T.tq_quantize_kv(g, view, None, None, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    # [block][head][offset] -> [slot][head]
+    codes = g.codes.cpu().numpy().transpose(0, 2, 1, 3).reshape(-1, n_kv, 16 * bits)
+    norms = g.norms.cpu().numpy().transpose(0, 2, 1).reshape(-1, n_kv)
+    near = 0
+    for h in range(n_kv):
+        ok = slots >= 0
+        near += U.check_codes(codes[slots[ok], h], norms[slots[ok], h], x16[ok, h], signs[h], bits)
+    untouched = np.setdiff1d(np.arange(codes.shape[0]), slots[slots >= 0])
+    assert np.all(codes[untouched] == 0xAB), "a skipped or unused slot was written"
+    return near
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("n_kv,n_tok", [(1, 1), (3, 7), (8, 300), (5, 33)])
+def test_quantize_random(bits, n_kv, n_tok):
+    rng = np.random.default_rng(100 * bits + n_tok)
+    x = (rng.standard_normal((n_tok, n_kv, 128)) * rng.lognormal(0, 1, (1, n_kv, 128))).astype(np.float16)
+    signs = W.random_sign_words(rng, n_kv)
+    near = quantize_and_compare(x, signs, bits)
+    log(f"quantize bits={bits} n_kv={n_kv} n_tok={n_tok}: near-boundary {near}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_special_vectors_skips_and_strides(bits):
+    rng = np.random.default_rng(5)
+    n_tok, n_kv = 40, 2
+    x = rng.standard_normal((n_tok, n_kv, 128)).astype(np.float16)
+    x[0] = 0                                   # zero vectors
+    x[1, 0] = np.float16(65504.0)              # largest float16, all coordinates
+    x[2, 1, :] = np.float16(6e-8)              # float16 subnormals
+    x[3, 0, :] = 0; x[3, 0, 77] = 3.0          # a single spike
+    x[4, 1] = np.where(np.arange(128) % 2, 1.0, -1.0).astype(np.float16)
+    signs = W.random_sign_words(rng, n_kv)
+    perm = rng.permutation(n_tok + 24)[:n_tok].astype(np.int64)
+    perm[[5, 9, 17]] = -1                      # skipped tokens
+    near = quantize_and_compare(x, signs, bits, block_size=16, slot_perm=perm, token_pad=72)
+    log(f"quantize special bits={bits}: near-boundary {near}")
+
+
+def test_quantize_tiny_workload():
+    wl = W.tiny()
+    k, v = wl.kv_source(0)
+    nk = quantize_and_compare(k, wl.signs_k, wl.k_bits, block_size=256)
+    nv = quantize_and_compare(v, wl.signs_v, wl.v_bits, block_size=256)
+    log(f"tiny workload: near-boundary K {nk} / {k.size}, V {nv} / {v.size}")
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_quantize_prefill_layer_full(layer):
+    """Full 8192 x 8 heads K (3-bit) and V (2-bit) of one prefill layer, both sides in one call."""
+    torch = _t()
+    wl = W.prefill()
+    sk, sv = wl.signs(layer)
+    k, v = wl.kv_source(layer)
+    kc = T.Cache.allocate(wl.k_bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, sk)
+    vc = T.Cache.allocate(wl.v_bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, sv)
+    slots = torch.arange(wl.n_tokens, dtype=torch.int64, device="cuda")
+    T.tq_quantize_kv(kc, torch.from_numpy(k).cuda(), vc, torch.from_numpy(v).cuda(), slots)
+    torch.cuda.synchronize()
+    near = 0
+    for cache, x, sg in ((kc, k, sk), (vc, v, sv)):
+        codes = cache.codes.cpu().numpy().transpose(0, 2, 1, 3).reshape(wl.n_tokens, wl.n_kv_heads, -1)
+        norms = cache.norms.cpu().numpy().transpose(0, 2, 1).reshape(wl.n_tokens, wl.n_kv_heads)
+        for h in range(wl.n_kv_heads):
+            near += U.check_codes(codes[:, h], norms[:, h], x[:, h], sg[h], cache.bits)
+    log(f"prefill layer {layer}: near-boundary {near} of {2 * k.size}")
+
+
+# --------------------------------------------------------------------------- dequantize
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_dequantize_matches_oracle(bits):
+    torch = _t()
+    wl = W.small_decode(seed=bits, n_seqs=2, lens=[300, 77], n_qtok=1, n_q_heads=3, n_kv_heads=3,
+                        k_bits=bits, v_bits=bits, block_size=64)
+    oc = U.oracle_cache(wl, 0)
+    g = U.gpu_cache_from(oc)
+    slots = np.concatenate([wl.slots(0), wl.slots(1)])
+    out32 = T.tq_dequantize(g, torch.from_numpy(slots).cuda()).cpu().numpy()
+    out16 = T.tq_dequantize(g, torch.from_numpy(slots).cuda(), fp16=True).cpu().numpy()
+    for h in range(3):
+        want = O.cache_read(oc, slots, h)
+        assert np.max(U.row_rel_err(out32[:, h], want)) < 1e-5
+        np.testing.assert_allclose(out16[:, h].astype(np.float64), want, rtol=2e-3, atol=1e-4)
+
+
+# --------------------------------------------------------------------------- decode
+
+def decode_and_compare(wl, seqs=None, kv_heads=None, tau=None, scale=0.0, gpu_caches=None):
+    """Decode on the GPU with oracle-written caches; compare rows of the given seqs."""
+    torch = _t()
+    tau = wl.tau if tau is None else tau
+    if gpu_caches is None:
+        ok, ov = U.oracle_cache(wl, 0), U.oracle_cache(wl, 1)
+        gk, gv = U.gpu_cache_from(ok), U.gpu_cache_from(ov)
+    else:
+        ok, ov, gk, gv = gpu_caches
+    q = wl.queries()
+    out = T.tq_decode_attention(gk, gv, torch.from_numpy(q).cuda(),
+                                torch.from_numpy(wl.seq_lens).cuda(),
+                                torch.from_numpy(wl.block_table).cuda(), scale, tau).cpu().numpy()
+    want, weights = O.decode_attention(q, ok, ov, wl.seq_lens, wl.block_table, wl.n_qtok, scale, tau,
+                                       seqs=seqs, kv_heads=kv_heads, return_weights=True)
+    seqs = range(wl.n_seqs) if seqs is None else seqs
+    kv_heads = range(wl.n_kv_heads) if kv_heads is None else kv_heads
+    worst, ambiguous = 0.0, 0
+    for b in seqs:
+        for kv in kv_heads:
+            for j in range(wl.n_qtok):
+                for h in range(kv * wl.group, (kv + 1) * wl.group):
+                    g_row, w_row = out[b, j, h], want[b, j, h]
+                    den = max(np.linalg.norm(w_row), 1e-30)
+                    err = np.linalg.norm(g_row - w_row)
+                    slack = 0.0
+                    if tau > 0 and (b, j, h) in weights:
+                        p = weights[(b, j, h)]
+                        amb = np.abs(p / tau - 1.0) < 1e-4
+                        if amb.any():
+                            ambiguous += int(amb.sum())
+                            slots = O.slots_for_sequence(wl.block_table[b], wl.block_size, len(p))
+                            vh = O.cache_read(ov, slots[amb], kv)
+                            slack = float(np.sum(p[amb] * np.linalg.norm(vh, axis=1)))
+                    if np.linalg.norm(w_row) == 0:
+                        assert err <= 1e-6 + slack, (b, j, h, err)
+                        continue
+                    rel = err / den
+                    worst = max(worst, rel)
+                    assert err <= ATOL_ROW * den + slack, (b, j, h, rel)
+    log(f"decode {wl.name}: worst row rel err {worst:.2e}, ambiguous gate decisions {ambiguous}")
+    return out, want
+
+
+def test_decode_tiny_workload():
+    decode_and_compare(W.tiny())
+
+
+@pytest.mark.parametrize("case", [
+    # n_seqs, lens, n_qtok, n_q_heads, n_kv, kb, vb, block_size
+    (1, [1], 1, 1, 1, 4, 3, 256),
+    (3, [1000, 1, 257], 1, 8, 2, 4, 3, 256),
+    (2, [700, 1300], 1, 6, 3, 3, 2, 64),
+    (2, [255, 513], 2, 8, 4, 2, 4, 100),
+    (3, [40, 3, 2], 4, 4, 1, 4, 4, 16),
+    (2, [900, 600], 1, 20, 2, 3, 3, 128),
+    (2, [1500, 77], 4, 32, 8, 4, 4, 256),
+    (2, [333, 1024], 3, 4, 1, 2, 2, 32),
+    (1, [4097], 1, 16, 16, 4, 2, 256),
+], ids=lambda c: f"s{c[0]}-q{c[2]}-h{c[3]}/{c[4]}-b{c[5]}{c[6]}-bs{c[7]}")
+def test_decode_small_cases(case):
+    n_seqs, lens, n_qtok, hq, hkv, kb, vb, bs = case
+    wl = W.small_decode(seed=sum(lens), n_seqs=n_seqs, lens=lens, n_qtok=n_qtok, n_q_heads=hq,
+                        n_kv_heads=hkv, k_bits=kb, v_bits=vb, block_size=bs)
+    decode_and_compare(wl)
+
+
+def test_decode_rows_with_no_visible_token_are_zero():
+    wl = W.small_decode(seed=3, n_seqs=2, lens=[2, 0], n_qtok=4, n_q_heads=2, n_kv_heads=1, k_bits=4,
+                        v_bits=3, block_size=16)
+    out, want = decode_and_compare(wl)
+    assert np.all(out[0, :2] == 0) and np.all(out[1] == 0)
+
+
+def test_decode_custom_scale():
+    wl = W.small_decode(seed=8, n_seqs=1, lens=[800], n_qtok=1, n_q_heads=4, n_kv_heads=2, k_bits=4,
+                        v_bits=4, block_size=256)
+    decode_and_compare(wl, scale=0.3)
+
+
+@pytest.mark.parametrize("tau", [1e-4, 1e-3, 3e-2, 0.5, 1.5])
+def test_decode_sparse_small(tau):
+    wl = W.small_decode(seed=11, n_seqs=2, lens=[3000, 900], n_qtok=2, n_q_heads=8, n_kv_heads=2, k_bits=3,
+                        v_bits=2, tau=tau, block_size=256)
+    out, _ = decode_and_compare(wl)
+    if tau > 1:
+        assert np.all(out == 0)
+
+
+def test_decode_sparse_peaked_small():
+    wl = W.longctx(context=8192, batch=2)
+    decode_and_compare(wl)
+
+
+def test_decode_llama8b_full():
+    """Llama-3-8B-shaped decode (32 q / 8 KV heads, 32K context, K4/V3), every row."""
+    decode_and_compare(W.llama8b())
+
+
+def _mixed_caches(wl, sampled):
+    """Device caches whose sampled sequences hold oracle-written pages and whose
+    other sequences hold GPU-quantized N(0,1) data (torch RNG); only sampled rows
+    are compared, and they depend only on their own pages."""
+    torch = _t()
+    gk = T.Cache.allocate(wl.k_bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, wl.signs_k)
+    gv = T.Cache.allocate(wl.v_bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, wl.signs_v)
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    for b in range(wl.n_seqs):
+        if b in sampled:
+            continue
+        n = int(wl.seq_lens[b])
+        kx = torch.randn((n, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
+        vx = torch.randn((n, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
+        T.tq_quantize_kv(gk, kx, gv, vx, torch.from_numpy(wl.slots(b)).cuda())
+    ok, ov = U.oracle_cache(wl, 0, seqs=sampled), U.oracle_cache(wl, 1, seqs=sampled)
+    blocks = np.concatenate([wl.block_table[b][: -(-int(wl.seq_lens[b]) // wl.block_size)] for b in sampled])
+    U.upload_blocks(ok, gk, blocks)
+    U.upload_blocks(ov, gv, blocks)
+    torch.cuda.synchronize()
+    return ok, ov, gk, gv
+
+
+def test_decode_longctx_sampled():
+    """4 x 128K sparse decode (40 q / 4 KV heads, K3/V2, tau 1e-4): sequence 0 checked, all heads."""
+    wl = W.longctx()
+    caches = _mixed_caches(wl, [0])
+    decode_and_compare(wl, seqs=[0], gpu_caches=caches)
+
+
+def test_decode_ragged_sampled():
+    """64 ragged sequences 4K-64K, 4 query tokens, paged: shortest and longest sequence checked."""
+    wl = W.ragged()
+    sampled = [int(np.argmin(wl.seq_lens)), int(np.argmax(wl.seq_lens))]
+    caches = _mixed_caches(wl, sampled)
+    decode_and_compare(wl, seqs=sampled, gpu_caches=caches)
+
+
+def test_end_to_end_tiny_against_oracle_pipeline():
+    """GPU quantize + GPU decode vs oracle quantize + oracle decode (codes equal away from
+    boundaries, so the outputs agree to the attention tolerance unless a boundary code flipped)."""
+    torch = _t()
+    wl = W.tiny()
+    k, v = wl.kv_source(0)
+    gk = T.Cache.allocate(wl.k_bits, 1, wl.block_size, wl.n_blocks, wl.signs_k)
+    gv = T.Cache.allocate(wl.v_bits, 1, wl.block_size, wl.n_blocks, wl.signs_v)
+    T.tq_quantize_kv(gk, torch.from_numpy(k).cuda(), gv, torch.from_numpy(v).cuda(),
+                     torch.from_numpy(wl.slots(0)).cuda())
+    q = wl.queries()
+    out = T.tq_decode_attention(gk, gv, torch.from_numpy(q).cuda(), torch.from_numpy(wl.seq_lens).cuda(),
+                                torch.from_numpy(wl.block_table).cuda()).cpu().numpy()
+    ok, ov = U.oracle_cache(wl, 0), U.oracle_cache(wl, 1)
+    flips = int(np.sum(gk.codes.cpu().numpy() != ok.codes) + np.sum(gv.codes.cpu().numpy() != ov.codes))
+    want = O.decode_attention(q, ok, ov, wl.seq_lens, wl.block_table, 1)
+    rel = float(U.row_rel_err(out[0, 0, 0], want[0, 0, 0]))
+    log(f"end-to-end tiny: rel err {rel:.2e}, differing code bytes {flips}")
+    assert rel < (ATOL_ROW if flips == 0 else 1e-2)
