@@ -68,6 +68,35 @@ def pmc_traffic(kernel_key):
     return r.get("bytes_per_launch")
 
 
+class HipEvents:
+    """Raw hipEvent_t pairs (the library records them on the launch stream itself)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0 and self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a, b))
+
+    def handles(self, i):
+        return self.pairs[i]
+
+    def mean_ms(self):
+        out = []
+        for a, b in self.pairs:
+            ms = self.ct.c_float()
+            assert self.hip.hipEventSynchronize(b) == 0
+            assert self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) == 0
+            out.append(ms.value)
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+        return float(np.mean(out))
+
+
 def decode_workload(name):
     return {"llama8b": W.llama8b, "longctx": W.longctx, "ragged": W.ragged, "tiny": W.tiny}[name]()
 
@@ -139,16 +168,38 @@ def run_decode(args, torch):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # eager steps, with the dominant kernel bracketed by HIP events on the launch stream
+    evs = HipEvents(args.steps)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for i in range(args.steps):
-        step(args.warmup + i, events=evs[i])
+        step(args.warmup + i, events=evs.handles(i))
     t1.record()
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    pass_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_step_eager = t0.elapsed_time(t1) / args.steps
+    pass_ms = evs.mean_ms()
+    # the same steps replayed from a HIP graph (one graph = one step on every replica)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for r in range(reps):
+            step(r)
+    for _ in range(max(1, args.warmup // reps)):
+        graph.replay()
+    torch.cuda.synchronize()
+    n_replay = max(1, -(-args.steps // reps))
+    t0.record()
+    for _ in range(n_replay):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / (n_replay * reps)
 
     # algorithmic bytes
     if wl.tau > 0:
@@ -165,8 +216,8 @@ def run_decode(args, torch):
     step_bytes = cache_step + qo + meta + append
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
-    log(f"[bench] {ms_step * 1e3:.1f} us/step, pass kernel {pass_ms * 1e3:.1f} us, "
-        f"step {value:.0f} GB/s, pass {achieved:.0f} GB/s")
+    log(f"[bench] {ms_step * 1e3:.1f} us/step (graph), {ms_step_eager * 1e3:.1f} us/step (eager), "
+        f"pass kernel {pass_ms * 1e3:.1f} us, step {value:.0f} GB/s, pass {achieved:.0f} GB/s")
     kernel_key = f"decode_pass_{wl.name}"
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(kernel_key),
@@ -176,6 +227,7 @@ def run_decode(args, torch):
                        f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d=128, K{kb}/V{vb}, "
                        f"{wl.n_qtok} query token(s), tau={wl.tau}, page {wl.block_size}",
            "global_batch": wl.n_seqs, "seq_len": int(wl.seq_lens.max()), "replicas": reps,
+           "launch": "HIP graph replay", "ms_per_step_eager": round(ms_step_eager, 5),
            "parallelism": "single GPU"}
     return wl, value, ms_step, roof, cfg, step_bytes
 
@@ -293,6 +345,8 @@ def main():
     ap.add_argument("--quantize-reps", type=int, default=5)
     ap.add_argument("--no-quantize", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 device copies of 256 MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -304,6 +358,14 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     T.load_library()
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 256 << 20, "copies": 5}), flush=True)
+        return
 
     wl, value, ms_step, roof, cfg, step_bytes = run_decode(args, torch)
     quant = None if args.no_quantize else run_quantize(args, torch)

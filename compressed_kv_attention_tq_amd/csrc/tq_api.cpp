@@ -132,11 +132,13 @@ DecodePlan plan_decode(int n_seqs, int n_kv, int rows, int max_blocks, int block
     p.rows_pad = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : rows <= 12 ? 12 : 16;
     const int64_t cap = (int64_t)max_blocks * block_size;
     const int64_t total = (int64_t)n_seqs * n_kv * cap;
-    int chunk = kSub;
-    while (chunk < 16384 && total / chunk > 2048) chunk *= 2;
+    // Largest chunk (tokens per pass block, a multiple of kChunkUnit) that still
+    // leaves at least ~2 blocks per compute unit of the 256 on the chip.
+    int chunk = kChunkUnit;
+    while (chunk < 16384 && total / (2 * chunk) >= 512) chunk *= 2;
     p.chunk = chunk;
     p.n_chunks = (int)((cap + chunk - 1) / chunk);
-    p.n_tiles = (int)((cap + kSub - 1) / kSub) * (kSub / kTile);
+    p.n_tiles = p.n_chunks * (chunk / kSlice);
     const size_t units = (size_t)n_seqs * n_kv;
     size_t off = 0;
     p.off_qrot = off;  off = align256(off + units * kD * p.rows_pad * sizeof(float));

@@ -104,9 +104,26 @@ __device__ __forceinline__ T launder_sgpr(T p) {
     return p;
 }
 
-// Positions per q'' group: 16 scalar values per buffer (two buffers live).
+// Positions per q'' group: 32 scalar values per buffer (two buffers live).
 template <int RP>
-constexpr int score_group() { return RP <= 1 ? 16 : RP <= 2 ? 8 : RP <= 4 ? 4 : RP <= 8 ? 2 : 1; }
+constexpr int score_group() { return RP <= 1 ? 32 : RP <= 2 ? 16 : RP <= 4 ? 8 : RP <= 8 ? 4 : 2; }
+
+// Pull every 64-byte line of q'' into the scalar cache with one round trip, so
+// the grouped scalar loads of the scoring loop hit.  16 lines per batch; the
+// empty asm consumes the values so the loads are issued and waited here.
+template <int RP>
+__device__ __forceinline__ void warm_q(cfloat_p qp) {
+    constexpr int kLines = kD * RP / 16;          // 16 floats per line
+#pragma unroll
+    for (int l0 = 0; l0 < kLines; l0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = (l0 + j < kLines) ? qp[(l0 + j) * 16] : 0.f;
+        asm volatile("" ::"s"(v[0]), "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5]), "s"(v[6]),
+                     "s"(v[7]), "s"(v[8]), "s"(v[9]), "s"(v[10]), "s"(v[11]), "s"(v[12]), "s"(v[13]),
+                     "s"(v[14]), "s"(v[15]));
+    }
+}
 
 // Keep a wave-uniform value in a VGPR (SGPRs are reserved for q'').
 __device__ __forceinline__ float in_vgpr(float x) {
@@ -158,27 +175,12 @@ __device__ __forceinline__ void score_groups(const uint32_t *w, cfloat_p qp, con
                   : score_step_g<KB, RP, P, Gs>(w, qp, qb, qa, ktab, acc)), ...);
 }
 
-template <int KB, int RP>
-__device__ __forceinline__ void score_token(const uint8_t *kcode, cfloat_p qp, const float *ktab,
-                                            float (&acc)[RP]) {
-    constexpr int P = score_group<RP>();
-    uint32_t w[4 * KB];
-    const uint4 *p = reinterpret_cast<const uint4 *>(kcode);
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-        const uint4 x = p[i];
-        w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
-    }
-#pragma unroll
-    for (int r = 0; r < RP; ++r) acc[r] = 0.f;
-    score_groups<KB, RP, P>(w, qp, ktab, acc, std::make_integer_sequence<int, kD / P>{});
-}
-
 // V phase layout: LPT lanes per token, each owning PPL consecutive positions.
 template <int RP>
 constexpr int v_lanes_per_token() { return RP >= 8 ? 32 : 16; }
 
-// Code bits of lane li (positions PPL*li .. PPL*li+PPL-1) of one token's V row.
+// Code bits of lane li (positions PPL*li .. PPL*li+PPL-1) of one token's V row
+// (global or LDS; the row is 4-byte aligned and 16*VB bytes long).
 template <int VB, int PPL>
 __device__ __forceinline__ uint32_t v_lane_bits(const uint8_t *row, int li) {
     constexpr int nbits = VB * PPL;
@@ -208,16 +210,74 @@ __device__ __forceinline__ void accum_token(uint32_t bits, const float (&wt)[RP]
     }
 }
 
+// One token's cache rows, loaded by the lane that scores it.  The physical page
+// of a token is looked up one slice before its rows are loaded (page_of), so the
+// block-table load never stalls the row loads.
+__device__ __forceinline__ int page_of(const int32_t *__restrict__ btab, const FastDiv &bsdiv, int t, int end) {
+    return t < end ? btab[fdiv((uint32_t)t, bsdiv)] : 0;
+}
+
+template <int KB, int VB, bool WITH_V>
+struct TokenRows {
+    uint4 k[KB];
+    uint4 v[WITH_V ? VB : 1];
+    float kn, vn;
+    bool active;
+
+    __device__ __forceinline__ void load(const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
+                                         const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms,
+                                         const FastDiv &bsdiv, int bs, int n_kv, int kv, int t, int end,
+                                         int blk) {
+        active = t < end;
+        int64_t row = 0;
+        if (active) {
+            const uint32_t pg = fdiv((uint32_t)t, bsdiv);
+            row = ((int64_t)blk * n_kv + kv) * bs + (t - (int)pg * bs);
+        }
+        const uint4 *kp = reinterpret_cast<const uint4 *>(k_codes + row * (16 * KB));
+#pragma unroll
+        for (int i = 0; i < KB; ++i) k[i] = kp[i];
+        kn = active ? k_norms[row] : 0.f;
+        if constexpr (WITH_V) {
+            const uint4 *vp = reinterpret_cast<const uint4 *>(v_codes + row * (16 * VB));
+#pragma unroll
+            for (int i = 0; i < VB; ++i) v[i] = vp[i];
+            vn = active ? v_norms[row] : 0.f;
+        }
+    }
+};
+
+// Scores of the lane's token for all RP rows (log2 domain), -inf where masked.
+template <int KB, int RP>
+__device__ __forceinline__ void score_rows(const uint4 (&kw)[KB], float kn, bool active, int t, int last_vis,
+                                           int group, cfloat_p qr, const float *ktab, float (&s)[RP]) {
+    uint32_t w[4 * KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+        w[4 * i] = kw[i].x; w[4 * i + 1] = kw[i].y; w[4 * i + 2] = kw[i].z; w[4 * i + 3] = kw[i].w;
+    }
+#pragma unroll
+    for (int r = 0; r < RP; ++r) s[r] = 0.f;
+    score_groups<KB, RP, score_group<RP>()>(w, launder_sgpr(qr), ktab, s,
+                                            std::make_integer_sequence<int, kD / score_group<RP>()>{});
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+        const bool vis = active && (t <= last_vis + r / group);
+        s[r] = vis ? s[r] * kn : -INFINITY;
+    }
+}
+
 // --------------------------------------------------------------------------
-// Main pass.  Block = 256 threads = one (seq, KV head, chunk).
+// Main pass.  Block = kWaves waves = one (seq, KV head, chunk).  Each wave walks
+// its own 64-token slices of the chunk (slice w, w + kWaves, ...) with private
+// online-softmax state, private LDS, and the next slice's rows prefetched, so
+// no block barrier is needed until the final merge of the waves' partials.
 // --------------------------------------------------------------------------
-// Pointers used inside the token loops are separate __restrict__ arguments so the
-// compiler may keep q'' on the scalar-load path even though the kernel stores.
 template <int RP>
-constexpr int pass_waves_per_eu() { return RP >= 8 ? 2 : 3; }
+constexpr int pass_waves_per_eu() { return RP >= 8 ? 2 : 4; }
 
 template <int KB, int VB, int RP, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(pass_waves_per_eu<RP>(), 8)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(pass_waves_per_eu<RP>(), 8)))
 void tq_decode_pass_kernel(DecodeArgs a,
                            const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
                            const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms,
@@ -225,16 +285,18 @@ void tq_decode_pass_kernel(DecodeArgs a,
                            const int32_t *__restrict__ seq_lens, const float *__restrict__ tile_in,
                            const float *__restrict__ stats, float *__restrict__ part_ml,
                            float *__restrict__ part_acc, float *__restrict__ tile_out) {
-    constexpr int RS = RP + 1;                        // padded LDS row stride
-    __shared__ float ktab[TQ_MAX_LEVELS], vtab[TQ_MAX_LEVELS];
-    __shared__ float sc[kSub * RS];                   // scores, then weights
-    __shared__ float red[4 * RP];
-    __shared__ float accbuf[(MODE == MODE_SCORE) ? 1 : RP * kD];
+    constexpr bool DENSE = MODE == MODE_DENSE;
+    constexpr int RS = RP + 1;                        // padded LDS row stride of the weights
     constexpr int LPT = v_lanes_per_token<RP>();      // V phase: lanes per token
     constexpr int PPL = kD / LPT;                     // V phase: positions per lane
-    constexpr int NGRP = kSub / LPT;                  // V phase: tokens in flight per block
-    __shared__ int keep_idx[kSub];
-    __shared__ int keep_cnt[4];
+    constexpr int GW = kSlice / LPT;                  // V phase: tokens in flight per wave
+    constexpr int VROW = 16 * VB + 4;                 // padded LDS V row (bank spread)
+    __shared__ float ktab[TQ_MAX_LEVELS], vtab[TQ_MAX_LEVELS];
+    __shared__ float wts[kWaves][kSlice * RS];        // per wave: token weights
+    __shared__ __attribute__((aligned(16))) uint8_t vrows[kWaves][DENSE ? kSlice * VROW : 4];
+    __shared__ int keep_idx[kWaves][kSlice];
+    __shared__ float wstate[kWaves][RP][2];           // per wave: (max, sum) at the end
+    __shared__ float accbuf[(MODE == MODE_SCORE) ? 1 : RP * kD];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = blockIdx.x % a.n_chunks;
@@ -256,6 +318,7 @@ void tq_decode_pass_kernel(DecodeArgs a,
     const FastDiv bsdiv = make_fastdiv((uint32_t)bs);
     const int last_vis = len - a.n_qtok;              // row r sees t <= last_vis + r / G
     const int64_t part = ((int64_t)b * a.n_kv + kv) * a.n_chunks + c;
+    const int64_t tile0 = ((int64_t)b * a.n_kv + kv) * a.n_tiles;
 
     float m_run[RP], l_run[RP], gM[RP], gInvL[RP];
 #pragma unroll
@@ -274,69 +337,53 @@ void tq_decode_pass_kernel(DecodeArgs a,
     for (int r = 0; r < RP; ++r)
 #pragma unroll
         for (int k = 0; k < PPL; ++k) acc[r][k] = 0.f;
-    __syncthreads();
 
-    const int gi = tid / LPT, li = tid % LPT;         // V phase: token group, lane in group
+    const int gi = lane / LPT, li = lane % LPT;       // V phase: token group in wave, lane in group
+    float *my_w = wts[wave];
+    uint8_t *my_v = vrows[wave];
+    constexpr int kStride = kWaves * kSlice;           // distance between a wave's slices
+    const int first = start + wave * kSlice;
 
-    for (int sub = start; sub < end; sub += kSub) {
-        // ---------------- K phase: one token per thread
-        const int t = sub + tid;
-        bool active = t < end;
-        bool score_needed = true;
+    TokenRows<KB, VB, MODE != MODE_GATED && DENSE> cur;
+    int blk_next = 0;
+    if constexpr (MODE != MODE_GATED) {
+        cur.load(k_codes, k_norms, v_codes, v_norms, bsdiv, bs, a.n_kv, kv, first + lane, end,
+                 page_of(btab, bsdiv, first + lane, end));
+        blk_next = page_of(btab, bsdiv, first + kStride + lane, end);
+    }
+    warm_q<RP>(launder_sgpr(qr));
+    __syncthreads();                                   // ktab / vtab
+
+    for (int base = first; base < end; base += kStride) {   // uniform per wave
+        const int t = base + lane;
+        float s[RP];
         if constexpr (MODE == MODE_GATED) {
-            // tile bound: skip the wave's 64 tokens if no row can reach tau
-            const float *tm = tile_in + (((int64_t)b * a.n_kv + kv) * a.n_tiles + (sub >> 6) + wave) * RP;
+            // tile bound: skip the slice if no row can reach tau with its best score
+            const float *tm = tile_in + (tile0 + (base >> 6)) * RP;
             bool cand = false;
 #pragma unroll
             for (int r = 0; r < RP; ++r)
                 if (r < a.rows) cand |= (exp2_diff(tm[r], gM[r]) * gInvL[r] >= a.tau);
-            score_needed = cand && (sub + wave * kTile < end);
-        }
-        float s[RP];
-        if (score_needed) {
-            int64_t row = 0;
-            if (active) {
-                const uint32_t pg = fdiv((uint32_t)t, bsdiv);
-                const int blk = btab[pg];
-                row = ((int64_t)blk * a.n_kv + kv) * bs + (t - (int)pg * bs);
-            }
-            score_token<KB, RP>(k_codes + row * (16 * KB), launder_sgpr(qr), ktab, s);
-            const float nk = active ? k_norms[row] : 0.f;
-#pragma unroll
-            for (int r = 0; r < RP; ++r) {
-                const bool vis = active && (t <= last_vis + r / a.group);
-                s[r] = vis ? s[r] * nk : -INFINITY;
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < RP; ++r) s[r] = -INFINITY;
-        }
-
-        if constexpr (MODE == MODE_GATED) {
+            if (!cand) continue;
+            cur.load(k_codes, k_norms, v_codes, v_norms, bsdiv, bs, a.n_kv, kv, t, end,
+                     page_of(btab, bsdiv, t, end));
+            score_rows<KB, RP>(cur.k, cur.kn, cur.active, t, last_vis, a.group, qr, ktab, s);
             bool kept = false;
 #pragma unroll
             for (int r = 0; r < RP; ++r) {
                 const float p = exp2_diff(s[r], gM[r]) * gInvL[r];
                 const bool k = (r < a.rows) && p >= a.tau && p > 0.f;
-                sc[tid * RS + r] = k ? p : 0.f;
+                my_w[lane * RS + r] = k ? p : 0.f;
                 kept |= k;
             }
-            // deterministic compaction of kept tokens
             const uint64_t bal = __ballot(kept);
-            const int before = __popcll(bal & ((1ull << lane) - 1ull));
-            if (lane == 0) keep_cnt[wave] = __popcll(bal);
-            __syncthreads();
-            int off = 0, total = 0;
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-                off += (w2 < wave) ? keep_cnt[w2] : 0;
-                total += keep_cnt[w2];
-            }
-            if (kept) keep_idx[off + before] = tid;
-            __syncthreads();
-            for (int q = gi; q < total; q += NGRP) {
-                const int tt = keep_idx[q];
-                const int tk = sub + tt;
+            const int total = __popcll(bal);
+            if (kept) keep_idx[wave][__popcll(bal & ((1ull << lane) - 1ull))] = lane;
+            __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): this wave's LDS writes done
+            __builtin_amdgcn_wave_barrier();
+            for (int q = gi; q < total; q += GW) {
+                const int tt = keep_idx[wave][q];
+                const int tk = base + tt;
                 const uint32_t pg = fdiv((uint32_t)tk, bsdiv);
                 const int blk = btab[pg];
                 const int64_t row = ((int64_t)blk * a.n_kv + kv) * bs + (tk - (int)pg * bs);
@@ -344,105 +391,103 @@ void tq_decode_pass_kernel(DecodeArgs a,
                 const float nv = v_norms[row];
                 float wt[RP];
 #pragma unroll
-                for (int r = 0; r < RP; ++r) wt[r] = sc[tt * RS + r] * nv;
+                for (int r = 0; r < RP; ++r) wt[r] = my_w[tt * RS + r] * nv;
                 accum_token<VB, RP, PPL>(bits, wt, vtab, acc);
             }
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
         } else {
-            // ---------------- online softmax statistics of the sub-chunk
-            float wm[RP];
+            // ---------------- K phase: one token per lane, rows loaded one slice ahead
+            score_rows<KB, RP>(cur.k, cur.kn, cur.active, t, last_vis, a.group, qr, ktab, s);
+            const float vn = cur.vn;
+            if constexpr (DENSE) {
 #pragma unroll
-            for (int r = 0; r < RP; ++r) wm[r] = wave_max(s[r]);
-            if constexpr (MODE == MODE_SCORE) {
-                if (lane < RP && sub + wave * kTile < end) {
-                    float v = wm[0];
-#pragma unroll
-                    for (int r = 1; r < RP; ++r) v = (lane == r) ? wm[r] : v;
-                    tile_out[(((int64_t)b * a.n_kv + kv) * a.n_tiles + (sub >> 6) + wave) * RP + lane] = v;
+                for (int i = 0; i < VB; ++i) {
+                    uint32_t *d = reinterpret_cast<uint32_t *>(my_v + lane * VROW) + 4 * i;
+                    d[0] = cur.v[i].x; d[1] = cur.v[i].y; d[2] = cur.v[i].z; d[3] = cur.v[i].w;
                 }
             }
-            if (lane == 0) {
-#pragma unroll
-                for (int r = 0; r < RP; ++r) red[wave * RP + r] = wm[r];
+            if (base + kStride < end) {
+                cur.load(k_codes, k_norms, v_codes, v_norms, bsdiv, bs, a.n_kv, kv, t + kStride, end, blk_next);
+                blk_next = page_of(btab, bsdiv, t + 2 * kStride, end);
             }
-            __syncthreads();
-            float m_new[RP], alpha[RP];
-#pragma unroll
-            for (int r = 0; r < RP; ++r) {
-                const float sm = fmaxf(fmaxf(red[r], red[RP + r]), fmaxf(red[2 * RP + r], red[3 * RP + r]));
-                m_new[r] = in_vgpr(fmaxf(m_run[r], sm));
-                alpha[r] = in_vgpr(exp2_diff(m_run[r], m_new[r]));
-            }
+            // ---------------- online softmax over the wave's slice
             float e[RP];
 #pragma unroll
             for (int r = 0; r < RP; ++r) {
-                e[r] = exp2_diff(s[r], m_new[r]);
-                if constexpr (MODE == MODE_DENSE) sc[tid * RS + r] = e[r];
-            }
-            float ws[RP];
+                const float wm = wave_max(s[r]);
+                if constexpr (MODE == MODE_SCORE) {
+                    if (lane == r) tile_out[(tile0 + (base >> 6)) * RP + r] = wm;
+                }
+                const float m_new = in_vgpr(fmaxf(m_run[r], wm));
+                const float alpha = exp2_diff(m_run[r], m_new);
+                e[r] = exp2_diff(s[r], m_new);
+                l_run[r] = in_vgpr(l_run[r] * alpha + wave_sum(e[r]));
+                m_run[r] = m_new;
+                if constexpr (DENSE) {
+                    my_w[lane * RS + r] = e[r] * vn;   // V norm folded into the weight
 #pragma unroll
-            for (int r = 0; r < RP; ++r) ws[r] = wave_sum(e[r]);
-            __syncthreads();                                   // everyone has read red
-            if (lane == 0) {
-#pragma unroll
-                for (int r = 0; r < RP; ++r) red[wave * RP + r] = ws[r];
-            }
-            __syncthreads();
-#pragma unroll
-            for (int r = 0; r < RP; ++r) {
-                const float ls = (red[r] + red[RP + r]) + (red[2 * RP + r] + red[3 * RP + r]);
-                l_run[r] = in_vgpr(l_run[r] * alpha[r] + ls);
-                m_run[r] = m_new[r];
-            }
-            if constexpr (MODE == MODE_DENSE) {
-#pragma unroll
-                for (int r = 0; r < RP; ++r)
-#pragma unroll
-                    for (int k = 0; k < PPL; ++k) acc[r][k] *= alpha[r];
-                // ---------------- V phase: NGRP tokens at a time, LPT lanes per token
-                const int n_sub = min(kSub, end - sub);
-                for (int tt = gi; tt < n_sub; tt += NGRP) {
-                    const int tk = sub + tt;
-                    const uint32_t pg = fdiv((uint32_t)tk, bsdiv);
-                    const int blk = btab[pg];
-                    const int64_t row = ((int64_t)blk * a.n_kv + kv) * bs + (tk - (int)pg * bs);
-                    const uint32_t bits = v_lane_bits<VB, PPL>(v_codes + row * (16 * VB), li);
-                    const float nv = v_norms[row];
-                    float wt[RP];
-#pragma unroll
-                    for (int r = 0; r < RP; ++r) wt[r] = sc[tt * RS + r] * nv;
-                    accum_token<VB, RP, PPL>(bits, wt, vtab, acc);
+                    for (int k = 0; k < PPL; ++k) acc[r][k] *= alpha;
                 }
             }
-            __syncthreads();                                   // sc / red reused next sub-chunk
+            if constexpr (DENSE) {
+                __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): weights and V rows in LDS
+                __builtin_amdgcn_wave_barrier();
+                // ---------------- V phase from LDS: GW tokens at a time, LPT lanes per token
+                const int n_tok = min(kSlice, end - base);
+#pragma unroll 2
+                for (int tt = gi; tt < n_tok; tt += GW) {
+                    const uint32_t bits = v_lane_bits<VB, PPL>(my_v + tt * VROW, li);
+                    float wt[RP];
+#pragma unroll
+                    for (int r = 0; r < RP; ++r) wt[r] = my_w[tt * RS + r];
+                    accum_token<VB, RP, PPL>(bits, wt, vtab, acc);
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
         }
     }
 
-    // ---------------- write the chunk's partial results
+    // ---------------- merge the waves' partials and write the chunk's result
     if constexpr (MODE != MODE_GATED) {
-        if (tid < RP) {
-            float mv = m_run[0], lv = l_run[0];
+        if (lane == 0) {
 #pragma unroll
-            for (int r = 1; r < RP; ++r) {
-                mv = (tid == r) ? m_run[r] : mv;
-                lv = (tid == r) ? l_run[r] : lv;
+            for (int r = 0; r < RP; ++r) {
+                wstate[wave][r][0] = m_run[r];
+                wstate[wave][r][1] = l_run[r];
             }
-            part_ml[(part * RP + tid) * 2] = mv;
-            part_ml[(part * RP + tid) * 2 + 1] = lv;
+        }
+    }
+    __syncthreads();
+    float scale[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+        scale[r] = 1.f;
+        if constexpr (MODE != MODE_GATED) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, wstate[w2][r][0]);
+            scale[r] = exp2_diff(m_run[r], M);
+            if (tid == 0) {
+                float L = 0.f;
+#pragma unroll
+                for (int w2 = 0; w2 < kWaves; ++w2) L += wstate[w2][r][1] * exp2_diff(wstate[w2][r][0], M);
+                part_ml[(part * RP + r) * 2] = M;
+                part_ml[(part * RP + r) * 2 + 1] = L;
+            }
         }
     }
     if constexpr (MODE != MODE_SCORE) {
-        // sum the token groups of each wave, then the 4 waves through LDS
+        // sum the token groups of each wave, then the waves in order through LDS
 #pragma unroll
         for (int r = 0; r < RP; ++r)
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
-                float x = acc[r][k];
+                float x = acc[r][k] * scale[r];
                 if constexpr (LPT == 16) x += __shfl_xor(x, 16);
                 x += __shfl_xor(x, 32);
                 acc[r][k] = x;
             }
-        for (int w2 = 0; w2 < 4; ++w2) {
+        for (int w2 = 0; w2 < kWaves; ++w2) {
             if (wave == w2 && lane < LPT) {
 #pragma unroll
                 for (int r = 0; r < RP; ++r)
@@ -455,36 +500,50 @@ void tq_decode_pass_kernel(DecodeArgs a,
             __syncthreads();
         }
         float *dst = part_acc + part * RP * kD;
-        for (int i = tid; i < RP * kD; i += kSub) dst[i] = accbuf[i];
+        for (int i = tid; i < RP * kD; i += kBlock) dst[i] = accbuf[i];
     }
 }
 
 #ifndef TQ_DECODE_KB
 // --------------------------------------------------------------------------
-// Global (max, sum) per row for the sparse path.
+// Global (max, sum) per row for the sparse path.  One block per (seq, KV head);
+// each wave reduces rows wave, wave+4, ... with its lanes striding the chunks.
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void tq_stats_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void tq_stats_kernel(DecodeArgs a) {
     const int b = blockIdx.x / a.n_kv, kv = blockIdx.x % a.n_kv;
-    const int r = threadIdx.x;
-    if (r >= a.rows_pad) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int len = a.seq_lens[b];
     const int nc = (len + a.chunk - 1) / a.chunk;
     const float *ml = a.part_ml + ((int64_t)b * a.n_kv + kv) * a.n_chunks * a.rows_pad * 2;
-    float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[(c * a.rows_pad + r) * 2]);
-    float L = 0.f;
-    for (int c = 0; c < nc; ++c) L += ml[(c * a.rows_pad + r) * 2 + 1] * exp2_diff(ml[(c * a.rows_pad + r) * 2], M);
-    float *st = a.stats + (((int64_t)b * a.n_kv + kv) * a.rows_pad + r) * 2;
-    st[0] = M;
-    st[1] = L;
+    for (int r = wave; r < a.rows_pad; r += 4) {
+        float m = -INFINITY;
+        for (int c = lane; c < nc; c += 64) m = fmaxf(m, ml[(c * a.rows_pad + r) * 2]);
+        const float M = wave_max(m);
+        float l = 0.f;
+        for (int c = lane; c < nc; c += 64)
+            l += ml[(c * a.rows_pad + r) * 2 + 1] * exp2_diff(ml[(c * a.rows_pad + r) * 2], M);
+        const float L = wave_sum(l);
+        if (lane == 0) {
+            float *st = a.stats + (((int64_t)b * a.n_kv + kv) * a.rows_pad + r) * 2;
+            st[0] = M;
+            st[1] = L;
+        }
+    }
 }
 
 // --------------------------------------------------------------------------
-// Combine chunk partials and inverse-rotate.  One wave per output row.
+// Combine chunk partials and inverse-rotate.  One block of 256 threads per
+// output row: the two halves of the block sum alternate chunks for all 128
+// elements, then wave 0 applies o = s_V * H acc / sqrt(128).
 // --------------------------------------------------------------------------
+constexpr int kCombineF = 1024;   // chunk weights kept in LDS (more chunks recompute theirs)
+
 template <bool SPARSE>
-__global__ __launch_bounds__(64) void tq_combine_kernel(DecodeArgs a) {
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void tq_combine_kernel(DecodeArgs a) {
+    __shared__ float red[4];
+    __shared__ float half_acc[2][kD];
+    __shared__ float fw[kCombineF];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.x % a.n_q_heads;
     const int jq = (blockIdx.x / a.n_q_heads) % a.n_qtok;
     const int b = blockIdx.x / (a.n_q_heads * a.n_qtok);
@@ -493,32 +552,58 @@ __global__ __launch_bounds__(64) void tq_combine_kernel(DecodeArgs a) {
     const int len = a.seq_lens[b];
     const int nc = (len + a.chunk - 1) / a.chunk;
     const int64_t base = ((int64_t)b * a.n_kv + kv) * a.n_chunks;
-    float x0 = 0.f, x1 = 0.f;
-    if (SPARSE) {
-        for (int c = 0; c < nc; ++c) {
-            const float *pa = a.part_acc + ((base + c) * a.rows_pad + r) * kD;
-            x0 += pa[lane];
-            x1 += pa[lane + 64];
+    const float *ml = a.part_ml + (base * a.rows_pad + r) * 2;        // chunk c at ml[c * rows_pad * 2]
+    const float *pa = a.part_acc + (base * a.rows_pad + r) * kD;      // chunk c at pa[c * rows_pad * kD]
+    const int mstride = a.rows_pad * 2, astride = a.rows_pad * kD;
+
+    // chunk weights f_c = 2^(m_c - M) (dense) in LDS, and L = sum f_c l_c
+    float L = 0.f, M = 0.f;
+    if (!SPARSE) {
+        float m = -INFINITY;
+        for (int c = tid; c < nc; c += 256) m = fmaxf(m, ml[c * mstride]);
+        m = wave_max(m);
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        float lp = 0.f;
+        for (int c = tid; c < nc; c += 256) {
+            const float f = exp2_diff(ml[c * mstride], M);
+            if (c < kCombineF) fw[c] = f;
+            lp += f * ml[c * mstride + 1];
         }
-    } else {
-        float M = -INFINITY;
-        for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_ml[((base + c) * a.rows_pad + r) * 2]);
-        float L = 0.f;
-        for (int c = 0; c < nc; ++c) {
-            const float *ml = a.part_ml + ((base + c) * a.rows_pad + r) * 2;
-            const float f = exp2_diff(ml[0], M);
-            if (f == 0.f) continue;
-            const float *pa = a.part_acc + ((base + c) * a.rows_pad + r) * kD;
-            L += ml[1] * f;
-            x0 += pa[lane] * f;
-            x1 += pa[lane + 64] * f;
-        }
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        x0 *= inv;
-        x1 *= inv;
+        lp = wave_sum(lp);
+        __syncthreads();
+        if (lane == 0) red[wave] = lp;
+        __syncthreads();
+        L = (red[0] + red[1]) + (red[2] + red[3]);
     }
-    // o = s_V * H acc / sqrt(128)
-    float a0 = x0 + x1, a1 = x0 - x1;
+    const int i = tid & (kD - 1), hf = tid >> 7;
+    // the two halves of the block take alternate chunks; loads are issued in
+    // batches of 16 independent chunks per thread
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = 0.f;
+    for (int c0 = hf; c0 < nc; c0 += 32) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int cj = c0 + 2 * j;
+            if (cj < nc) {
+                const float f = SPARSE ? 1.f : (cj < kCombineF ? fw[cj] : exp2_diff(ml[cj * mstride], M));
+                x[j] += f * pa[(int64_t)cj * astride + i];
+            }
+        }
+    }
+    const float x0 = (((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]))) +
+                     (((x[8] + x[9]) + (x[10] + x[11])) + ((x[12] + x[13]) + (x[14] + x[15])));
+    const float x1 = 0.f;
+    half_acc[hf][i] = x0 + x1;
+    __syncthreads();
+    if (wave != 0) return;
+    const float inv = SPARSE ? 1.f : (L > 0.f ? 1.f / L : 0.f);
+    const float y0 = (half_acc[0][lane] + half_acc[1][lane]) * inv;
+    const float y1 = (half_acc[0][lane + 64] + half_acc[1][lane + 64]) * inv;
+    // o = s_V * H acc / sqrt(128): element bit 6 in registers, bits 0..5 across lanes
+    float a0 = y0 + y1, a1 = y0 - y1;
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
         const float p0 = __shfl_xor(a0, m), p1 = __shfl_xor(a1, m);
@@ -553,11 +638,11 @@ static void launch_pass(const DecodeArgs &a, int mode, hipStream_t s) {
 #define TQ_PASS_ARGS a, a.k_codes, a.k_norms, a.v_codes, a.v_norms, a.qrot, a.block_table, a.seq_lens, \
         a.tilemax, a.stats, a.part_ml, a.part_acc, a.tilemax
     if (mode == MODE_DENSE)
-        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, VB, RP, MODE_DENSE>), grid, dim3(kSub), 0, s, TQ_PASS_ARGS);
+        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, VB, RP, MODE_DENSE>), grid, dim3(kBlock), 0, s, TQ_PASS_ARGS);
     else if (mode == MODE_SCORE)
-        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, 2, RP, MODE_SCORE>), grid, dim3(kSub), 0, s, TQ_PASS_ARGS);
+        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, 2, RP, MODE_SCORE>), grid, dim3(kBlock), 0, s, TQ_PASS_ARGS);
     else
-        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, VB, RP, MODE_GATED>), grid, dim3(kSub), 0, s, TQ_PASS_ARGS);
+        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, VB, RP, MODE_GATED>), grid, dim3(kBlock), 0, s, TQ_PASS_ARGS);
 #undef TQ_PASS_ARGS
 }
 
@@ -605,13 +690,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_befor
     if (a.tau > 0.f) {
         launch_pass_any(a, MODE_SCORE, s);
         if (ev_after) (void)hipEventRecord(ev_after, s);
-        hipLaunchKernelGGL(tq_stats_kernel, dim3(a.n_seqs * a.n_kv), dim3(64), 0, s, a);
+        hipLaunchKernelGGL(tq_stats_kernel, dim3(a.n_seqs * a.n_kv), dim3(256), 0, s, a);
         launch_pass_any(a, MODE_GATED, s);
-        hipLaunchKernelGGL(tq_combine_kernel<true>, rows_grid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL(tq_combine_kernel<true>, rows_grid, dim3(256), 0, s, a);
     } else {
         launch_pass_any(a, MODE_DENSE, s);
         if (ev_after) (void)hipEventRecord(ev_after, s);
-        hipLaunchKernelGGL(tq_combine_kernel<false>, rows_grid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL(tq_combine_kernel<false>, rows_grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

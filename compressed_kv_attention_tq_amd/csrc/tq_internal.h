@@ -11,8 +11,11 @@
 namespace tq {
 
 constexpr int kD = 128;            // elements per block
-constexpr int kSub = 256;          // decode: tokens per sub-chunk (= threads per block)
-constexpr int kTile = 64;          // decode: tokens per sparse-V gating tile (one wave)
+constexpr int kWaves = 8;          // decode: waves per pass block
+constexpr int kBlock = 64 * kWaves;// decode: threads per pass block
+constexpr int kSlice = 64;         // decode: tokens a wave scores at once (one per lane);
+                                   //         also the sparse-V gating tile
+constexpr int kChunkUnit = kBlock; // decode: chunks are multiples of this many tokens
 constexpr int kLutMax = 256;       // quantize: max entries of the encode lookup table
 
 // One side of a quantize launch.
@@ -71,7 +74,7 @@ struct DecodeArgs {
     float *stats;             // [S][n_kv][RP][2]  global (max, sum) (sparse only)
     int32_t n_seqs, n_qtok, n_q_heads, n_kv, group, rows, rows_pad;
     int32_t max_blocks, block_size;
-    int32_t chunk;            // tokens per chunk (multiple of kSub)
+    int32_t chunk;            // tokens per chunk (multiple of kChunkUnit)
     int32_t n_chunks;         // chunks per sequence capacity
     int32_t n_tiles;          // tiles per sequence capacity
     float qscale;             // softmax_scale * log2(e) / sqrt(128)

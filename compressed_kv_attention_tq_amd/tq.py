@@ -217,8 +217,8 @@ def tq_decode_attention(k_cache: Cache, v_cache: Cache, q, seq_lens, block_table
                         sparse_v_tau=0.0, out=None, workspace=None, stream=None, events=None):
     """q float16 [n_seqs, n_qtok, n_q_heads, 128]; seq_lens int32 [n_seqs];
     block_table int32 [n_seqs, max_blocks].  Returns float32 out like q.
-    events: optional pair of torch.cuda.Event (enable_timing) recorded around the
-    main pass kernel (tq_decode_attention_timed)."""
+    events: optional pair of raw hipEvent_t handles (ctypes.c_void_p or int) recorded
+    around the main pass kernel (tq_decode_attention_timed)."""
     torch = _torch()
     n_seqs, n_qtok, n_q_heads, hd = q.shape
     if hd != HEAD_DIM:
@@ -232,7 +232,7 @@ def tq_decode_attention(k_cache: Cache, v_cache: Cache, q, seq_lens, block_table
     size = ctypes.c_size_t(workspace.numel())
     ev = None
     if events is not None:
-        ev = (ctypes.c_void_p * 2)(events[0].cuda_event, events[1].cuda_event)
+        ev = (ctypes.c_void_p * 2)(*[e.value if isinstance(e, ctypes.c_void_p) else e for e in events])
     st = load_library().tq_decode_attention_timed(
         ctypes.byref(k_cache.desc()), ctypes.byref(v_cache.desc()), _dev_ptr(q, "q", torch.float16),
         n_seqs, n_qtok, n_q_heads, _dev_ptr(seq_lens, "seq_lens", torch.int32),

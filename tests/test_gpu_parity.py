@@ -302,3 +302,46 @@ def test_end_to_end_tiny_against_oracle_pipeline():
     rel = float(U.row_rel_err(out[0, 0, 0], want[0, 0, 0]))
     log(f"end-to-end tiny: rel err {rel:.2e}, differing code bytes {flips}")
     assert rel < (ATOL_ROW if flips == 0 else 1e-2)
+
+
+def test_graph_replay_matches_eager():
+    """Quantize-append + decode captured in a HIP graph: every replay equals the eager result."""
+    torch = _t()
+    wl = W.small_decode(seed=21, n_seqs=2, lens=[1500, 700], n_qtok=2, n_q_heads=8, n_kv_heads=2, k_bits=4,
+                        v_bits=3, block_size=64)
+    ok, ov = U.oracle_cache(wl, 0), U.oracle_cache(wl, 1)
+    gk, gv = U.gpu_cache_from(ok), U.gpu_cache_from(ov)
+    q = torch.from_numpy(wl.queries()).cuda()
+    lens = torch.from_numpy(wl.seq_lens).cuda()
+    table = torch.from_numpy(wl.block_table).cuda()
+    new_slots = torch.from_numpy(np.concatenate([wl.slots(b)[-2:] for b in range(2)])).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    knew = torch.randn((4, 2, 128), generator=gen, device="cuda").half()
+    vnew = torch.randn((4, 2, 128), generator=gen, device="cuda").half()
+    out = torch.zeros((2, 2, 8, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(T.decode_workspace_bytes(gk, gv, 2, 2, 8, wl.block_table.shape[1]), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        T.tq_quantize_kv(gk, knew, gv, vnew, new_slots)
+        T.tq_decode_attention(gk, gv, q, lens, table, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    codes_eager = gk.codes.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from eager"
+        assert torch.equal(gk.codes, codes_eager)
