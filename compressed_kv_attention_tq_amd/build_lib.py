@@ -29,6 +29,9 @@ SOURCES = [
     ("tq_decode.hip", "tq_decode_kb2", ["-DTQ_DECODE_KB=2"]),
     ("tq_decode.hip", "tq_decode_kb3", ["-DTQ_DECODE_KB=3"]),
     ("tq_decode.hip", "tq_decode_kb4", ["-DTQ_DECODE_KB=4"]),
+    ("tq_decode_mfma.hip", "tq_decode_mfma_kb2", ["-DTQ_DECODE_KB=2"]),
+    ("tq_decode_mfma.hip", "tq_decode_mfma_kb3", ["-DTQ_DECODE_KB=3"]),
+    ("tq_decode_mfma.hip", "tq_decode_mfma_kb4", ["-DTQ_DECODE_KB=4"]),
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -2,6 +2,7 @@
 // and kernel dispatch.  Everything here runs on the host; nothing allocates.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -126,26 +127,41 @@ struct DecodePlan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-DecodePlan plan_decode(int n_seqs, int n_kv, int rows, int max_blocks, int block_size, bool sparse) {
+// Decode kernels: the matrix-core pass (default) or the vector-ALU pass, chosen
+// by the environment variable TQ_DECODE_KERNEL ("mfma" / "valu").
+bool use_mfma_decode() {
+    const char *e = getenv("TQ_DECODE_KERNEL");
+    return !(e && strcmp(e, "valu") == 0);
+}
+
+// Tokens per pass block: a multiple of the unit (one 64-token slice per wave),
+// doubled while at least kTargetBlocks blocks remain and at most 16384 tokens;
+// TQ_DECODE_CHUNK (a multiple of the unit) overrides it.
+DecodePlan plan_decode(int n_seqs, int n_kv, int rows, int max_blocks, int block_size, bool sparse, bool mfma) {
     DecodePlan p{};
     p.rows = rows;
-    p.rows_pad = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : rows <= 12 ? 12 : 16;
+    if (mfma) p.rows_pad = rows <= 8 ? 8 : 16;
+    else p.rows_pad = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : rows <= 12 ? 12 : 16;
     const int64_t cap = (int64_t)max_blocks * block_size;
     const int64_t total = (int64_t)n_seqs * n_kv * cap;
-    // Largest chunk (tokens per pass block, a multiple of kChunkUnit) that still
-    // leaves at least ~2 blocks per compute unit of the 256 on the chip.
-    int chunk = kChunkUnit;
-    while (chunk < 16384 && total / (2 * chunk) >= 512) chunk *= 2;
+    const int unit = mfma ? kMBlock : kChunkUnit;
+    const int64_t target = mfma ? 1024 : 512;
+    int chunk = unit;
+    while (chunk < 16384 && total / (2 * chunk) >= target) chunk *= 2;
+    if (const char *e = getenv("TQ_DECODE_CHUNK")) {
+        const long v = strtol(e, nullptr, 10);
+        if (v >= unit && v <= (1 << 20) && v % unit == 0) chunk = (int)v;
+    }
     p.chunk = chunk;
     p.n_chunks = (int)((cap + chunk - 1) / chunk);
     p.n_tiles = p.n_chunks * (chunk / kSlice);
     const size_t units = (size_t)n_seqs * n_kv;
     size_t off = 0;
-    p.off_qrot = off;  off = align256(off + units * kD * p.rows_pad * sizeof(float));
+    p.off_qrot = off;  if (!mfma) off = align256(off + units * kD * p.rows_pad * sizeof(float));
     p.off_ml = off;    off = align256(off + units * p.n_chunks * p.rows_pad * 2 * sizeof(float));
     p.off_acc = off;   off = align256(off + units * p.n_chunks * p.rows_pad * kD * sizeof(float));
     p.off_tile = off;  if (sparse) off = align256(off + units * p.n_tiles * p.rows_pad * sizeof(float));
-    p.off_stats = off; if (sparse) off = align256(off + units * p.rows_pad * 2 * sizeof(float));
+    p.off_stats = off; if (sparse && !mfma) off = align256(off + units * p.rows_pad * 2 * sizeof(float));
     p.total = off;
     return p;
 }
@@ -290,8 +306,14 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     const int64_t rows = (int64_t)group * n_qtok;
     if (rows > TQ_MAX_ROWS_PER_KV_HEAD) return TQ_ERR_UNSUPPORTED;
     if ((int64_t)max_blocks_per_seq * k->block_size > (1LL << 30)) return TQ_ERR_UNSUPPORTED;
+    // cache rows are indexed with 32-bit integers on the device
+    if ((double)k->n_blocks * k->n_kv_heads * k->block_size > 2147483647.0 ||
+        (double)v->n_blocks * v->n_kv_heads * v->block_size > 2147483647.0)
+        return TQ_ERR_UNSUPPORTED;
     const bool sparse = sparse_v_tau > 0.f;
-    const DecodePlan p = plan_decode(n_seqs, k->n_kv_heads, (int)rows, max_blocks_per_seq, k->block_size, sparse);
+    const bool mfma = use_mfma_decode();
+    const DecodePlan p = plan_decode(n_seqs, k->n_kv_heads, (int)rows, max_blocks_per_seq, k->block_size, sparse,
+                                     mfma);
     if ((int64_t)n_seqs * k->n_kv_heads * p.n_chunks > 0x7FFFFFFFLL) return TQ_ERR_UNSUPPORTED;
     if (!workspace) {
         *workspace_bytes = n_seqs == 0 ? 0 : p.total;
@@ -315,11 +337,11 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     a.block_table = block_table;
     a.out = out;
     char *ws = static_cast<char *>(workspace);
-    a.qrot = reinterpret_cast<float *>(ws + p.off_qrot);
+    a.qrot = mfma ? nullptr : reinterpret_cast<float *>(ws + p.off_qrot);
     a.part_ml = reinterpret_cast<float *>(ws + p.off_ml);
     a.part_acc = reinterpret_cast<float *>(ws + p.off_acc);
     a.tilemax = sparse ? reinterpret_cast<float *>(ws + p.off_tile) : nullptr;
-    a.stats = sparse ? reinterpret_cast<float *>(ws + p.off_stats) : nullptr;
+    a.stats = (sparse && !mfma) ? reinterpret_cast<float *>(ws + p.off_stats) : nullptr;
     a.n_seqs = n_seqs;
     a.n_qtok = n_qtok;
     a.n_q_heads = n_q_heads;
@@ -337,6 +359,8 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     a.tau = sparse_v_tau;
     a.k_bits = k->bits;
     a.v_bits = v->bits;
+    a.mfma = mfma ? 1 : 0;
+    a.contig = (k->block_size % kSlice == 0 && is_aligned(k->norms, 16) && is_aligned(v->norms, 16)) ? 1 : 0;
     for (int i = 0; i < TQ_MAX_LEVELS; ++i) {
         a.kc[i] = i < k->cb.n_levels ? k->cb.centroids[i] : 0.f;
         a.vc[i] = i < v->cb.n_levels ? v->cb.centroids[i] : 0.f;

@@ -13,43 +13,15 @@
 //                      p = 2^(s - M) / L >= tau                 ([TQ+ README]
 //                      sparse V; [TQ+ article] skipped V treated as zero)
 //   stats  : global (max, sum) per row from the SCORE partials
-//   combine: merge chunk partials (log-sum-exp for DENSE, plain sum for GATED),
+//   merge  : merge chunk partials (log-sum-exp for DENSE, plain sum for GATED),
 //            inverse-rotate once: o = s_V * H acc / sqrt(128)
 #include <float.h>
 
 #include <utility>
 
-#include "tq_device.h"
-#include "tq_internal.h"
+#include "tq_decode_common.h"
 
 namespace tq {
-
-enum { MODE_DENSE = 0, MODE_SCORE = 1, MODE_GATED = 2 };
-
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, dpp<kDppXor1>(x));
-    x = fmaxf(x, dpp<kDppXor2>(x));
-    x = fmaxf(x, dpp<kDppRor4>(x));
-    x = fmaxf(x, dpp<kDppRor8>(x));
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-    x += dpp<kDppXor1>(x);
-    x += dpp<kDppXor2>(x);
-    x += dpp<kDppRor4>(x);
-    x += dpp<kDppRor8>(x);
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
-}
-
-// 2^(a - b) with the -inf conventions of an online softmax (0 when a is -inf).
-__device__ __forceinline__ float exp2_diff(float a, float b) {
-    return a == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(a - b);
-}
 
 #ifndef TQ_DECODE_KB
 // --------------------------------------------------------------------------
@@ -69,15 +41,8 @@ __global__ __launch_bounds__(1024) void tq_qrot_kernel(DecodeArgs a) {
         if ((sg[lane >> 5] >> (lane & 31)) & 1u) x0 = -x0;
         if ((sg[2 + (lane >> 5)] >> (lane & 31)) & 1u) x1 = -x1;
     }
-    // element bit 6 in registers, bits 0..5 across lanes
-    float a0 = x0 + x1, a1 = x0 - x1;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const float p0 = __shfl_xor(a0, m), p1 = __shfl_xor(a1, m);
-        const bool hi = lane & m;
-        a0 = hi ? p0 - a0 : a0 + p0;
-        a1 = hi ? p1 - a1 : a1 + p1;
-    }
+    hadamard128(x0, x1, lane);
+    const float a0 = x0, a1 = x1;
     float *dst = a.qrot + ((int64_t)b * a.n_kv + kv) * kD * a.rows_pad;
     dst[lane * a.rows_pad + r] = a0 * a.qscale;
     dst[(lane + 64) * a.rows_pad + r] = a1 * a.qscale;
@@ -123,12 +88,6 @@ __device__ __forceinline__ void warm_q(cfloat_p qp) {
                      "s"(v[7]), "s"(v[8]), "s"(v[9]), "s"(v[10]), "s"(v[11]), "s"(v[12]), "s"(v[13]),
                      "s"(v[14]), "s"(v[15]));
     }
-}
-
-// Keep a wave-uniform value in a VGPR (SGPRs are reserved for q'').
-__device__ __forceinline__ float in_vgpr(float x) {
-    asm volatile("" : "+v"(x));
-    return x;
 }
 
 template <int KB, int RP, int I>
@@ -209,43 +168,6 @@ __device__ __forceinline__ void accum_token(uint32_t bits, const float (&wt)[RP]
         for (int r = 0; r < RP; ++r) acc[r][k] = __builtin_fmaf(wt[r], cv, acc[r][k]);
     }
 }
-
-// One token's cache rows, loaded by the lane that scores it.  The physical page
-// of a token is looked up one slice before its rows are loaded (page_of), so the
-// block-table load never stalls the row loads.
-__device__ __forceinline__ int page_of(const int32_t *__restrict__ btab, const FastDiv &bsdiv, int t, int end) {
-    return t < end ? btab[fdiv((uint32_t)t, bsdiv)] : 0;
-}
-
-template <int KB, int VB, bool WITH_V>
-struct TokenRows {
-    uint4 k[KB];
-    uint4 v[WITH_V ? VB : 1];
-    float kn, vn;
-    bool active;
-
-    __device__ __forceinline__ void load(const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
-                                         const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms,
-                                         const FastDiv &bsdiv, int bs, int n_kv, int kv, int t, int end,
-                                         int blk) {
-        active = t < end;
-        int64_t row = 0;
-        if (active) {
-            const uint32_t pg = fdiv((uint32_t)t, bsdiv);
-            row = ((int64_t)blk * n_kv + kv) * bs + (t - (int)pg * bs);
-        }
-        const uint4 *kp = reinterpret_cast<const uint4 *>(k_codes + row * (16 * KB));
-#pragma unroll
-        for (int i = 0; i < KB; ++i) k[i] = kp[i];
-        kn = active ? k_norms[row] : 0.f;
-        if constexpr (WITH_V) {
-            const uint4 *vp = reinterpret_cast<const uint4 *>(v_codes + row * (16 * VB));
-#pragma unroll
-            for (int i = 0; i < VB; ++i) v[i] = vp[i];
-            vn = active ? v_norms[row] : 0.f;
-        }
-    }
-};
 
 // Scores of the lane's token for all RP rows (log2 domain), -inf where masked.
 template <int KB, int RP>
@@ -532,85 +454,88 @@ __global__ __launch_bounds__(256) void tq_stats_kernel(DecodeArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// Combine chunk partials and inverse-rotate.  One block of 256 threads per
-// output row: the two halves of the block sum alternate chunks for all 128
-// elements, then wave 0 applies o = s_V * H acc / sqrt(128).
+// Merge the chunk partials of one output row and inverse-rotate it (both pass
+// kernels write the same partial layout).  One block per row: 8 chunk groups x
+// 32 float4 columns.  Dense: each thread merges its chunks (c = group,
+// group + 8, ...) with the log-sum-exp rule in batches of 8 loads, then the
+// groups are merged through LDS and o = s_V * H (acc / L) / sqrt(128).  Gated:
+// the partials are already normalised and are summed.
 // --------------------------------------------------------------------------
-constexpr int kCombineF = 1024;   // chunk weights kept in LDS (more chunks recompute theirs)
-
 template <bool SPARSE>
-__global__ __launch_bounds__(256) void tq_combine_kernel(DecodeArgs a) {
-    __shared__ float red[4];
-    __shared__ float half_acc[2][kD];
-    __shared__ float fw[kCombineF];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
+    typedef float f4_t __attribute__((ext_vector_type(4)));
+    __shared__ float gm[8], gl[8];
+    __shared__ __attribute__((aligned(16))) float gx[8][kD];
+    __shared__ float y[kD];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int cg = tid >> 5, q4 = tid & 31;
     const int h = blockIdx.x % a.n_q_heads;
     const int jq = (blockIdx.x / a.n_q_heads) % a.n_qtok;
     const int b = blockIdx.x / (a.n_q_heads * a.n_qtok);
     const int kv = h / a.group;
     const int r = jq * a.group + (h % a.group);
     const int len = a.seq_lens[b];
-    const int nc = (len + a.chunk - 1) / a.chunk;
+    const int nc = len > 0 ? (len + a.chunk - 1) / a.chunk : 0;
     const int64_t base = ((int64_t)b * a.n_kv + kv) * a.n_chunks;
-    const float *ml = a.part_ml + (base * a.rows_pad + r) * 2;        // chunk c at ml[c * rows_pad * 2]
-    const float *pa = a.part_acc + (base * a.rows_pad + r) * kD;      // chunk c at pa[c * rows_pad * kD]
-    const int mstride = a.rows_pad * 2, astride = a.rows_pad * kD;
-
-    // chunk weights f_c = 2^(m_c - M) (dense) in LDS, and L = sum f_c l_c
-    float L = 0.f, M = 0.f;
-    if (!SPARSE) {
-        float m = -INFINITY;
-        for (int c = tid; c < nc; c += 256) m = fmaxf(m, ml[c * mstride]);
-        m = wave_max(m);
-        if (lane == 0) red[wave] = m;
-        __syncthreads();
-        M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        float lp = 0.f;
-        for (int c = tid; c < nc; c += 256) {
-            const float f = exp2_diff(ml[c * mstride], M);
-            if (c < kCombineF) fw[c] = f;
-            lp += f * ml[c * mstride + 1];
+    const int64_t mstride = (int64_t)a.rows_pad * 2, astride = (int64_t)a.rows_pad * kD;
+    const float *ml = a.part_ml + (base * a.rows_pad + r) * 2;          // chunk c at ml[c * mstride]
+    const float *pa = a.part_acc + (base * a.rows_pad + r) * kD + 4 * q4;  // chunk c at pa[c * astride]
+    float M = -INFINITY, L = 0.f;
+    f4_t x = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = cg; c0 < nc; c0 += 64) {
+        float m[8], l[8];
+        f4_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int cc = c0 + 8 * i;
+            const bool ok = cc < nc;
+            m[i] = (!SPARSE && ok) ? ml[cc * mstride] : -INFINITY;
+            l[i] = (!SPARSE && ok) ? ml[cc * mstride + 1] : 0.f;
+            v[i] = ok ? *reinterpret_cast<const f4_t *>(pa + cc * astride) : f4_t{0.f, 0.f, 0.f, 0.f};
         }
-        lp = wave_sum(lp);
-        __syncthreads();
-        if (lane == 0) red[wave] = lp;
-        __syncthreads();
-        L = (red[0] + red[1]) + (red[2] + red[3]);
-    }
-    const int i = tid & (kD - 1), hf = tid >> 7;
-    // the two halves of the block take alternate chunks; loads are issued in
-    // batches of 16 independent chunks per thread
-    float x[16];
+        if (SPARSE) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = 0.f;
-    for (int c0 = hf; c0 < nc; c0 += 32) {
+            for (int i = 0; i < 8; ++i) x += v[i];
+        } else {
+            float mb = M;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int cj = c0 + 2 * j;
-            if (cj < nc) {
-                const float f = SPARSE ? 1.f : (cj < kCombineF ? fw[cj] : exp2_diff(ml[cj * mstride], M));
-                x[j] += f * pa[(int64_t)cj * astride + i];
+            for (int i = 0; i < 8; ++i) mb = fmaxf(mb, m[i]);
+            const float sc = exp2_diff(M, mb);
+            x *= sc;
+            L *= sc;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float f = exp2_diff(m[i], mb);
+                x += f * v[i];
+                L += f * l[i];
             }
+            M = mb;
         }
     }
-    const float x0 = (((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]))) +
-                     (((x[8] + x[9]) + (x[10] + x[11])) + ((x[12] + x[13]) + (x[14] + x[15])));
-    const float x1 = 0.f;
-    half_acc[hf][i] = x0 + x1;
-    __syncthreads();
-    if (wave != 0) return;
-    const float inv = SPARSE ? 1.f : (L > 0.f ? 1.f / L : 0.f);
-    const float y0 = (half_acc[0][lane] + half_acc[1][lane]) * inv;
-    const float y1 = (half_acc[0][lane + 64] + half_acc[1][lane + 64]) * inv;
-    // o = s_V * H acc / sqrt(128): element bit 6 in registers, bits 0..5 across lanes
-    float a0 = y0 + y1, a1 = y0 - y1;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const float p0 = __shfl_xor(a0, m), p1 = __shfl_xor(a1, m);
-        const bool hi = lane & m;
-        a0 = hi ? p0 - a0 : a0 + p0;
-        a1 = hi ? p1 - a1 : a1 + p1;
+    if (q4 == 0) {
+        gm[cg] = M;
+        gl[cg] = L;
     }
+    *reinterpret_cast<f4_t *>(&gx[cg][4 * q4]) = x;
+    __syncthreads();
+    if (tid < kD) {
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) Mx = fmaxf(Mx, gm[k]);
+        float ys = 0.f, Ls = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float f = SPARSE ? 1.f : exp2_diff(gm[k], Mx);
+            ys += f * gx[k][tid];
+            Ls += f * gl[k];
+        }
+        y[tid] = SPARSE ? ys : (Ls > 0.f ? ys / Ls : 0.f);
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    // o = s_V * H acc / sqrt(128)
+    float a0 = y[lane], a1 = y[lane + 64];
+    hadamard128(a0, a1, lane);
     const uint32_t *sg = a.v_signs + kv * 4;
     const float k = 0.088388347648318440550f;
     a0 *= ((sg[lane >> 5] >> (lane & 31)) & 1u) ? -k : k;
@@ -675,6 +600,18 @@ void TQ_CAT(launch_pass_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStre
 
 #else
 
+void launch_mfma_kb2(const DecodeArgs &a, int mode, hipStream_t s);
+void launch_mfma_kb3(const DecodeArgs &a, int mode, hipStream_t s);
+void launch_mfma_kb4(const DecodeArgs &a, int mode, hipStream_t s);
+
+static void launch_mfma_any(const DecodeArgs &a, int mode, hipStream_t s) {
+    switch (a.k_bits) {
+        case 2: launch_mfma_kb2(a, mode, s); break;
+        case 3: launch_mfma_kb3(a, mode, s); break;
+        default: launch_mfma_kb4(a, mode, s); break;
+    }
+}
+
 static void launch_pass_any(const DecodeArgs &a, int mode, hipStream_t s) {
     switch (a.k_bits) {
         case 2: launch_pass_kb2(a, mode, s); break;
@@ -684,19 +621,33 @@ static void launch_pass_any(const DecodeArgs &a, int mode, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
-    hipLaunchKernelGGL(tq_qrot_kernel, dim3(a.n_seqs * a.n_kv), dim3(64 * a.rows_pad), 0, s, a);
     const dim3 rows_grid((unsigned)((int64_t)a.n_seqs * a.n_qtok * a.n_q_heads));
+    if (a.mfma) {   // q rotation runs inside the pass kernels
+        if (ev_before) (void)hipEventRecord(ev_before, s);
+        if (a.tau > 0.f) {
+            launch_mfma_any(a, MODE_SCORE, s);
+            if (ev_after) (void)hipEventRecord(ev_after, s);
+            launch_mfma_any(a, MODE_GATED, s);
+            hipLaunchKernelGGL(tq_merge_kernel<true>, rows_grid, dim3(256), 0, s, a);
+        } else {
+            launch_mfma_any(a, MODE_DENSE, s);
+            if (ev_after) (void)hipEventRecord(ev_after, s);
+            hipLaunchKernelGGL(tq_merge_kernel<false>, rows_grid, dim3(256), 0, s, a);
+        }
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(tq_qrot_kernel, dim3(a.n_seqs * a.n_kv), dim3(64 * a.rows_pad), 0, s, a);
     if (ev_before) (void)hipEventRecord(ev_before, s);
     if (a.tau > 0.f) {
         launch_pass_any(a, MODE_SCORE, s);
         if (ev_after) (void)hipEventRecord(ev_after, s);
         hipLaunchKernelGGL(tq_stats_kernel, dim3(a.n_seqs * a.n_kv), dim3(256), 0, s, a);
         launch_pass_any(a, MODE_GATED, s);
-        hipLaunchKernelGGL(tq_combine_kernel<true>, rows_grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(tq_merge_kernel<true>, rows_grid, dim3(256), 0, s, a);
     } else {
         launch_pass_any(a, MODE_DENSE, s);
         if (ev_after) (void)hipEventRecord(ev_after, s);
-        hipLaunchKernelGGL(tq_combine_kernel<false>, rows_grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(tq_merge_kernel<false>, rows_grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

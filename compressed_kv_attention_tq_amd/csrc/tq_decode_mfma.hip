@@ -1,0 +1,689 @@
+// Decode attention over the compressed cache on the gfx950 matrix cores.
+//
+// Computes what the vector-ALU kernels compute (scores against K codes in the
+// Hadamard domain without dequantizing K, online softmax in the log2 domain, V
+// accumulated in the rotated domain and inverse-rotated once per row;
+// [llama-tq] rotated-domain Q.K, [TQ+ README] sparse V, [TQ+ article] skipped V
+// is zero), with the two contractions of each 64-token slice as 16x16x32 fp16
+// MFMAs.  All query rows of one KV head (GQA group x query tokens, at most 16)
+// share the slice's codes, so per slice:
+//   scores  S[token][col] = sum_pos cK[token][pos] * Q[pos][col]     (K: 16 MFMAs)
+//   values  A[pos][col]  += sum_tok cV[pos][tok] * P[tok][col]       (V: 16 MFMAs)
+// Centroids are fp16-exact, so the code operands are exact.  The fp32 operands
+// (q'' and the softmax weights) are split into fp16 hi + lo parts (w = hi + lo to
+// ~2^-20 relative): with at most 8 rows the hi parts sit in columns 0-7 and the
+// lo parts in columns 8-15 of one MFMA and the two column halves are summed
+// afterwards; with 9-16 rows each part gets its own MFMA.
+//
+// Lane roles (lane l, g = l / 16, n = l % 16; checked on the hardware):
+//   A operand: row m = n, k = 8g + e (e = 0..7, fp16 pairs per dword)
+//   B operand: k = 8g + e, column n;   D: row 4g + e (e = 0..3), column n.
+// K: A row = token 16tm + n of tile tm, k = position 32g + 8ks + e, so each lane
+//    reads 4*KB contiguous code bytes of one token per tile and expands byte
+//    pairs of codes with an LDS table of fp16 centroid pairs.
+// V: k = token 32ks + 16(e/4) + 4g + (e%4), which is exactly the set of tokens
+//    whose scores lane (g, n) holds in the K output (tiles 2ks, 2ks+1), so the
+//    softmax weights feed the V MFMA's B operand without any data movement.
+//    A row m = n is position 8n + j of tile j, so each lane reads the 8-position
+//    unit n of 16 tokens and pairs two tokens' codes per table lookup.
+//
+// A block (4 waves) owns one chunk of one (sequence, KV head); each wave walks
+// its own 64-token slices with private softmax state, loading the next slice's
+// codes while it computes, and the block's partial goes to the workspace for the
+// merge kernel.
+#include "tq_decode_common.h"
+
+namespace tq {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kQS = 132;   // padded row stride (floats) of the q'' / merge buffer
+
+__device__ __forceinline__ f4_t mfma_f16(u4_t a, u4_t b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), c,
+                                                  0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ float half_lo(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> 16));
+}
+
+// One half of the fp16 split w = hi + lo of an fp32 pair: the hi pair when
+// lo_sel == 0, the lo pair when lo_sel == 1.  hi is w truncated to fp16, so
+// w - hi is exact in fp32 and lo holds it to fp16 precision.
+__device__ __forceinline__ uint32_t split_pair(float w0, float w1, float lo_sel) {
+    const uint32_t h = pk_rtz(w0, w1);
+    return pk_rtz(__builtin_fmaf(-lo_sel, half_lo(h), w0), __builtin_fmaf(-lo_sel, half_hi(h), w1));
+}
+
+__host__ __device__ inline uint32_t half2_bits(float lo, float hi) {
+    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Reductions over the four lane groups g (lanes n, n+16, n+32, n+48 hold one
+// column): swap rows of 16 lanes, then halves of the wave.
+__device__ __forceinline__ float xg_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xg_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// NW contiguous dwords (16, 12 or 8 bytes) of code bytes.
+template <int NW>
+__device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[NW]) {
+    if constexpr (NW == 4) {
+        const uint4 t = *reinterpret_cast<const uint4 *>(p);
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+    } else if constexpr (NW == 3) {
+        struct alignas(4) U3 { uint32_t x, y, z; };
+        const U3 t = *reinterpret_cast<const U3 *>(p);
+        w[0] = t.x; w[1] = t.y; w[2] = t.z;
+    } else {
+        const uint2 t = *reinterpret_cast<const uint2 *>(p);
+        w[0] = t.x; w[1] = t.y;
+    }
+}
+
+// A operand of the score MFMA for k-step ks from the lane's 32 positions of one
+// token (positions 32g + 8ks .. +7): 4 lookups of a code pair -> fp16 pair.
+template <int KB>
+__device__ __forceinline__ u4_t k_frag(const uint32_t (&w)[KB], int ks, const uint32_t *tab) {
+    constexpr int FB = 2 * KB;
+    uint32_t u;
+    if constexpr (KB == 4) {
+        u = w[ks];
+    } else if constexpr (KB == 3) {
+        u = ks == 0 ? w[0]
+            : ks == 1 ? __builtin_amdgcn_alignbit(w[1], w[0], 24)
+            : ks == 2 ? __builtin_amdgcn_alignbit(w[2], w[1], 16)
+                      : (w[2] >> 8);
+    } else {
+        u = (ks & 1) ? (w[ks >> 1] >> 16) : w[ks >> 1];
+    }
+    u4_t f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = tab[(u >> (FB * k)) & ((1u << FB) - 1u)];
+    return f;
+}
+
+// Raw word of the 8-position unit n of one V row: one dword (4-bit), one ushort
+// (2-bit).  3-bit units (bits [24n, 24n + 24)) come four to three dwords: lane
+// n = 4a + b of a quad loads dword 3a + min(b, 2), and vunit_bits takes the
+// low part of units 1 and 2 from the quad neighbour below.
+template <int VB>
+struct VUnit {
+    uint32_t d;
+};
+
+template <int VB>
+__device__ __forceinline__ void load_vunit(const uint8_t *row, int widx, VUnit<VB> &u) {
+    if constexpr (VB == 2) u.d = reinterpret_cast<const uint16_t *>(row)[widx];
+    else u.d = reinterpret_cast<const uint32_t *>(row)[widx];
+}
+
+// The unit's bits at bit 0 (bits above the unit are garbage); called by all lanes.
+template <int VB>
+__device__ __forceinline__ uint32_t vunit_bits(const VUnit<VB> &u, int o) {
+    if constexpr (VB == 3) {
+        constexpr int kQuadPerm0013 = 0xD0;   // quad_perm [0, 0, 1, 3]
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)u.d, kQuadPerm0013, 0xF, 0xF, false);
+        return __builtin_amdgcn_alignbit(u.d, lo, o);
+    } else {
+        return u.d;
+    }
+}
+
+// Pair the codes of tokens (2k, 2k+1) position by position: field f of x[k]
+// holds position 2f of both tokens, field f of y[k] position 2f+1 (the even
+// token in the low VB bits).  Bits above the unit are never read.
+template <int VB>
+__device__ __forceinline__ void v_pairs(const uint32_t (&u)[8], uint32_t (&x)[4], uint32_t (&y)[4]) {
+    constexpr uint32_t M = VB == 4 ? 0x0F0F0F0Fu : VB == 3 ? 0x001C71C7u : 0x00003333u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        x[k] = (u[2 * k] & M) | ((u[2 * k + 1] << VB) & ~M);
+        y[k] = ((u[2 * k] >> VB) & M) | (u[2 * k + 1] & ~M);
+    }
+}
+
+// A operand of the value MFMA for position tile j (position 8n + j of 8 tokens).
+template <int VB>
+__device__ __forceinline__ u4_t v_frag(const uint32_t (&x)[4], const uint32_t (&y)[4], int j, const uint32_t *tab) {
+    constexpr int FB = 2 * VB;
+    const int sh = FB * (j >> 1);
+    u4_t f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = tab[(((j & 1) ? y[k] : x[k]) >> sh) & ((1u << FB) - 1u)];
+    return f;
+}
+
+// --------------------------------------------------------------------------
+// The pass kernel.  MODE_DENSE: attention partials (max, sum, V accumulator) per
+// chunk.  MODE_SCORE: per-chunk (max, sum) and per-slice maxima only.
+// MODE_GATED: from the scoring partials, the global (max, sum) per row; then
+// re-score the candidate slices and accumulate V where p = 2^(s - M) / L >= tau.
+// PK: at most 8 rows (hi / lo parts packed in one MFMA's columns).
+// CONTIG: block_size is a multiple of 64, so a slice lies in one page.
+// --------------------------------------------------------------------------
+// Waves per SIMD the register allocation aims for (without spilling): the
+// packed-column variants fit three, the 9-16 row ones two.
+template <bool PK, int VB, int MODE>
+constexpr int mfma_waves_per_eu() { return PK ? 3 : 2; }
+
+template <int KB, int VB, bool PK, int MODE, bool CONTIG>
+__global__ __launch_bounds__(kMBlock) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<PK, VB, MODE>(), 8)))
+void tq_decode_mfma_kernel(
+    DecodeArgs a, const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
+    const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms, const uint16_t *__restrict__ qin,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens, float *__restrict__ part_ml,
+    float *__restrict__ part_acc, float *__restrict__ tilemax) {
+    constexpr bool DENSE = MODE == MODE_DENSE, SCORE = MODE == MODE_SCORE, GATED = MODE == MODE_GATED;
+    constexpr bool WV = !SCORE;
+    constexpr int NKT = 1 << (2 * KB), NVT = 1 << (2 * VB);
+    constexpr int LK = 1 << KB, LV = 1 << VB;
+    constexpr int KROW = 16 * KB, VROW = 16 * VB;   // bytes per code row
+    constexpr int NQB = PK ? 4 : 8;                 // q'' B fragments
+    constexpr int NPB = PK ? 2 : 4;                 // weight B fragments
+    __shared__ uint32_t ktab[NKT];
+    __shared__ uint32_t vtab[WV ? NVT : 1];
+    __shared__ __attribute__((aligned(16))) float buf[16 * kQS];       // q'', then per-row partials
+    __shared__ __attribute__((aligned(16))) float nrm[kMW][2][64];     // per wave: K, V norms of the slice
+    __shared__ float wst[kMW][16][2];
+    __shared__ float red[kMW];
+    __shared__ float gstat[16][2];
+    __shared__ __attribute__((aligned(16))) int32_t rowtab[CONTIG ? 1 : kMW][64];
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = blockIdx.x % a.n_chunks;
+    const int unit = blockIdx.x / a.n_chunks;
+    const int kv = unit % a.n_kv, b = unit / a.n_kv;
+    const int len = seq_lens[b];
+    const int R = a.rows, rp = a.rows_pad;
+    const int start = c * a.chunk;
+    if (start >= len) return;
+    const int end = min(start + a.chunk, len);
+    const int64_t part = (int64_t)unit * a.n_chunks + c;
+    const int64_t tile0 = (int64_t)unit * a.n_tiles;
+
+    const int bs = a.block_size, n_kv = a.n_kv;
+    const FastDiv bsdiv = make_fastdiv((uint32_t)bs);
+    const int32_t *__restrict__ btab = block_table + (int64_t)b * a.max_blocks;
+    constexpr int kStride = kMW * 64;
+    const int first = start + wave * 64;
+
+    // word of a V row this lane loads, and (3-bit) the unit's offset in it
+    int vwi = n, vo = 0;
+    if constexpr (VB == 3) {
+        vwi = 3 * (n >> 2) + min(n & 3, 2);
+        vo = (24 * n) & 31;
+    }
+
+    // ---- slice state: code words per lane, one K and one V norm per lane (token = lane)
+    uint32_t kw[4][KB];
+    VUnit<VB> vw[2][8];
+    float knl = 0.f, vnl = 0.f;
+    int myrow = 0;   // row of token base + lane (general page layout)
+
+    auto row0_of = [&](int base, int blk) -> int64_t {
+        const int pg = (int)fdiv((uint32_t)base, bsdiv);
+        return ((int64_t)blk * n_kv + kv) * bs + (base - pg * bs);
+    };
+    // general layout: the row of every token of the slice into the wave's table
+    auto fill_rows = [&](int base, int blk_lane) {
+        const int t = base + lane;
+        myrow = 0;
+        if (t < end) {
+            const int pg = (int)fdiv((uint32_t)t, bsdiv);
+            myrow = (blk_lane * n_kv + kv) * bs + (t - pg * bs);
+        }
+        rowtab[CONTIG ? 0 : wave][lane] = myrow;
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's row table is written
+        __builtin_amdgcn_wave_barrier();
+    };
+    auto load_k = [&](int64_t row0) {
+        if constexpr (CONTIG) {
+            const uint8_t *p = k_codes + (row0 + n) * KROW + g * (4 * KB);
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) load_words<KB>(p + tm * 16 * KROW, kw[tm]);
+            knl = k_norms[row0 + lane];
+        } else {
+            const int32_t *rt = rowtab[wave];
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+                load_words<KB>(k_codes + (int64_t)rt[16 * tm + n] * KROW + g * (4 * KB), kw[tm]);
+            knl = k_norms[myrow];
+        }
+    };
+    // V units of the slice's tokens; token (tile tm, e) of lane group g is loaded
+    // only where keep(tm, e) holds (every token for the dense pass)
+    auto load_v = [&](int64_t row0, auto keep) {
+        if constexpr (CONTIG) {
+            const uint8_t *p = v_codes + (row0 + 4 * g) * VROW;
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    VUnit<VB> &u = vw[tm >> 1][4 * (tm & 1) + e];
+                    if (keep(tm, e)) load_vunit<VB>(p + (16 * tm + e) * VROW, vwi, u);
+                    else u = VUnit<VB>{};
+                }
+            vnl = v_norms[row0 + lane];
+        } else {
+            const int32_t *rt = rowtab[wave];
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) {
+                const i4_t rr = *reinterpret_cast<const i4_t *>(rt + 16 * tm + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    VUnit<VB> &u = vw[tm >> 1][4 * (tm & 1) + e];
+                    if (keep(tm, e)) load_vunit<VB>(v_codes + (int64_t)rr[e] * VROW, vwi, u);
+                    else u = VUnit<VB>{};
+                }
+            }
+            vnl = v_norms[myrow];
+        }
+    };
+    auto all_tokens = [](int, int) { return true; };
+
+    // ---- the first slice's loads go out before the set-up below
+    int blk_next = 0;
+    int64_t r0n = 0;
+    if constexpr (!GATED) {
+        if (first < end) {
+            if constexpr (CONTIG) {
+                r0n = row0_of(first, btab[fdiv((uint32_t)first, bsdiv)]);
+                blk_next = first + kStride < end ? btab[fdiv((uint32_t)(first + kStride), bsdiv)] : 0;
+            } else {
+                fill_rows(first, page_of(btab, bsdiv, first + lane, end));
+                blk_next = page_of(btab, bsdiv, first + kStride + lane, end);
+            }
+            load_k(r0n);
+            if constexpr (DENSE) load_v(r0n, all_tokens);
+        }
+    }
+
+    for (int i = tid; i < NKT; i += kMBlock) ktab[i] = half2_bits(a.kc[i & (LK - 1)], a.kc[i >> KB]);
+    if constexpr (WV)
+        for (int i = tid; i < NVT; i += kMBlock) vtab[i] = half2_bits(a.vc[i & (LV - 1)], a.vc[i >> VB]);
+
+    // ---- q'' = qscale * H (s_K * q) of this KV head's rows, into buf
+    {
+        float qm = 0.f;
+        for (int r = wave; r < 16; r += kMW) {
+            float x0 = 0.f, x1 = 0.f;
+            if (r < R) {
+                const int jq = r / a.group, h = kv * a.group + r % a.group;
+                const uint16_t *qp = qin + (((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * kD;
+                const uint32_t *sg = a.k_signs + kv * 4;
+                x0 = (float)__builtin_bit_cast(_Float16, qp[lane]);
+                x1 = (float)__builtin_bit_cast(_Float16, qp[lane + 64]);
+                if ((sg[lane >> 5] >> (lane & 31)) & 1u) x0 = -x0;
+                if ((sg[2 + (lane >> 5)] >> (lane & 31)) & 1u) x1 = -x1;
+            }
+            hadamard128(x0, x1, lane);
+            x0 *= a.qscale;
+            x1 *= a.qscale;
+            buf[r * kQS + lane] = x0;
+            buf[r * kQS + lane + 64] = x1;
+            qm = fmaxf(qm, fmaxf(fabsf(x0), fabsf(x1)));
+        }
+        qm = wave_max(qm);
+        if (lane == 0) red[wave] = qm;
+    }
+    // sparse: global (max, sum) of each row from the scoring pass's chunk partials
+    if constexpr (GATED) {
+        const int nc = (len + a.chunk - 1) / a.chunk;
+        const float *ml = part_ml + (int64_t)unit * a.n_chunks * rp * 2;
+        for (int r = wave; r < R; r += kMW) {
+            float m = -INFINITY;
+            for (int cc = lane; cc < nc; cc += 64) m = fmaxf(m, ml[(cc * rp + r) * 2]);
+            const float M = wave_max(m);
+            float l = 0.f;
+            for (int cc = lane; cc < nc; cc += 64)
+                l += ml[(cc * rp + r) * 2 + 1] * exp2_diff(ml[(cc * rp + r) * 2], M);
+            const float L = wave_sum(l);
+            if (lane == 0) {
+                gstat[r][0] = M;
+                gstat[r][1] = L;
+            }
+        }
+    }
+    __syncthreads();
+
+    // q'' is scaled by a power of two so its largest element is in [2^13, 2^14)
+    // (fp16 range and precision for both parts); scores are scaled back by kscale.
+    const float qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int qex = qmax > 0.f ? max((int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127, -100) : 0;
+    const float sq = __builtin_ldexpf(1.f, 13 - qex), kscale = __builtin_ldexpf(1.f, qex - 13);
+
+    const int col_row = PK ? (n & 7) : n;             // query row of this lane's column
+    const float losel = (PK && n >= 8) ? 1.f : 0.f;   // column holds lo parts
+    u4_t qb[NQB];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float *qr = &buf[col_row * kQS + 32 * g + 8 * ks + 2 * k];
+            const float q0 = qr[0] * sq, q1 = qr[1] * sq;
+            if constexpr (PK) {
+                qb[ks][k] = split_pair(q0, q1, losel);
+            } else {
+                qb[ks][k] = pk_rtz(q0, q1);
+                qb[4 + ks][k] = split_pair(q0, q1, 1.f);
+            }
+        }
+
+    const bool row_ok = col_row < R;
+    // last position each row sees in this chunk (row r sees t <= len - n_qtok + r / G)
+    const int lim = row_ok ? min(end - 1, len - a.n_qtok + col_row / a.group) : -1;
+    const int lim_all = min(end - 1, len - a.n_qtok);   // seen by every row
+
+    // sparse: keep iff s >= sthr (p >= tau); weights 2^(s - mlog) = p
+    float sthr = INFINITY, mlog = 0.f;
+    if constexpr (GATED) {
+        if (row_ok) {
+            const float M = gstat[col_row][0], L = gstat[col_row][1];
+            if (L > 0.f && M > -INFINITY) {
+                mlog = M + log2f(L);
+                sthr = mlog + log2f(a.tau);
+            }
+        }
+    }
+
+    // ---- score MFMAs of the loaded slice
+    auto score_mfma = [&](f4_t (&S)[4]) {
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            S[tm] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const u4_t af = k_frag<KB>(kw[tm], ks, ktab);
+                S[tm] = mfma_f16(af, qb[ks], S[tm]);
+                if constexpr (!PK) S[tm] = mfma_f16(af, qb[4 + ks], S[tm]);
+            }
+        }
+    };
+    // the slice's norms to the wave's LDS rows (V norms past the chunk's end are
+    // not data and become 0); returns the V exponent E: max V norm < 2^E, so the
+    // weights e * vn * 2^-E stay below 1
+    float *my_kn = nrm[wave][0], *my_vn = nrm[wave][1];
+    auto stage_norms = [&](int base) -> float {
+        my_kn[lane] = knl;
+        float v = 0.f;
+        if constexpr (WV) {
+            v = base + lane < end ? vnl : 0.f;
+            my_vn[lane] = v;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        if constexpr (!WV) return 0.f;
+        const float vm = wave_max(v);
+        const int ex = vm > 0.f ? (int)((__float_as_uint(vm) >> 23) & 0xFF) - 126 : -40;
+        return (float)min(max(ex, -40), 40);
+    };
+    // scores in the log2 domain, -inf where the row does not see the token
+    auto scores = [&](const f4_t (&S)[4], int base, bool full, float (&s)[4][4]) {
+        const int dl = lim - base - 4 * g;   // element (tm, e) visible iff 16 tm + e <= dl
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            const f4_t kn = *reinterpret_cast<const f4_t *>(my_kn + 16 * tm + 4 * g) * kscale;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x = S[tm][e];
+                if constexpr (PK) x += dpp<kDppRor8>(x);
+                x *= kn[e];
+                s[tm][e] = (full || 16 * tm + e <= dl) ? x : -INFINITY;
+            }
+        }
+    };
+    // value MFMAs of the loaded slice with weights w (score layout)
+    f4_t acc[WV ? 8 : 1];
+#pragma unroll
+    for (int j = 0; j < (WV ? 8 : 1); ++j) acc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+    auto value_mfma = [&](const float (&w)[4][4]) {
+        u4_t pb[NPB];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int tm = 2 * ks + (k >> 1), e0 = 2 * (k & 1);
+                if constexpr (PK) {
+                    pb[ks][k] = split_pair(w[tm][e0], w[tm][e0 + 1], losel);
+                } else {
+                    pb[ks][k] = pk_rtz(w[tm][e0], w[tm][e0 + 1]);
+                    pb[2 + ks][k] = split_pair(w[tm][e0], w[tm][e0 + 1], 1.f);
+                }
+            }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint32_t u[8], x[4], y[4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = vunit_bits<VB>(vw[ks][e], vo);
+            v_pairs<VB>(u, x, y);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const u4_t af = v_frag<VB>(x, y, j, vtab);
+                acc[j] = mfma_f16(af, pb[ks], acc[j]);
+                if constexpr (!PK) acc[j] = mfma_f16(af, pb[2 + ks], acc[j]);
+            }
+        }
+    };
+
+    float m_raw = -INFINITY, m_state = -INFINITY, l_run = 0.f, E_run = -INFINITY;
+
+    if constexpr (!GATED) {
+        // ---------------- dense / scoring pass: loads run one slice ahead
+        for (int base = first; base < end; base += kStride) {
+            const int nb = base + kStride;
+            const bool has_next = nb < end;
+            const float E_s = stage_norms(base);
+            f4_t S[4];
+            score_mfma(S);
+            if (has_next) {   // next slice's K while this one is scored
+                if constexpr (CONTIG) {
+                    r0n = row0_of(nb, blk_next);
+                    blk_next = nb + kStride < end ? btab[fdiv((uint32_t)(nb + kStride), bsdiv)] : 0;
+                } else {
+                    fill_rows(nb, blk_next);
+                    blk_next = page_of(btab, bsdiv, nb + kStride + lane, end);
+                }
+                load_k(r0n);
+            }
+            const bool full = base + 63 <= lim_all;
+            float s[4][4];
+            scores(S, base, full, s);
+            float wm = -INFINITY;
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wm = fmaxf(wm, s[tm][e]);
+            wm = xg_max(wm);
+            if constexpr (SCORE) {
+                if (g == 0 && row_ok && (!PK || n < 8)) tilemax[(tile0 + (base >> 6)) * rp + col_row] = wm;
+            }
+            const float m_new = fmaxf(m_raw, wm);
+            const float E_new = DENSE ? fmaxf(E_run, E_s) : 0.f;
+            const float mu = (m_new == -INFINITY ? 0.f : m_new) + E_new;
+            const float alpha = exp2_diff(m_state, mu);
+            float lsum = 0.f, w[4][4];
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) {
+                const f4_t vn = DENSE ? *reinterpret_cast<const f4_t *>(my_vn + 16 * tm + 4 * g) : f4_t{};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ex = __builtin_amdgcn_exp2f(s[tm][e] - mu);
+                    lsum += ex;
+                    if constexpr (DENSE) w[tm][e] = ex * vn[e];
+                }
+            }
+            lsum = xg_sum(lsum);
+            l_run = l_run * alpha + lsum;
+            m_raw = m_new;
+            m_state = m_new == -INFINITY ? -INFINITY : mu;
+            E_run = E_new;
+            if constexpr (DENSE) {
+                if (__ballot(alpha != 1.f)) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+                }
+                value_mfma(w);
+                if (has_next) load_v(r0n, all_tokens);
+            }
+        }
+    } else {
+        // ---------------- gated pass: candidate slices only
+        for (int base = first; base < end; base += kStride) {
+            const float tmx = row_ok ? tilemax[(tile0 + (base >> 6)) * rp + col_row] : -INFINITY;
+            if (!__ballot(tmx >= sthr)) continue;
+            int64_t r0 = 0;
+            if constexpr (CONTIG) r0 = row0_of(base, btab[fdiv((uint32_t)base, bsdiv)]);
+            else fill_rows(base, page_of(btab, bsdiv, base + lane, end));
+            load_k(r0);
+            if constexpr (CONTIG) vnl = v_norms[r0 + lane];
+            else vnl = v_norms[myrow];
+            const float E_s = stage_norms(base);
+            f4_t S[4];
+            score_mfma(S);
+            const bool full = base + 63 <= lim_all;
+            float s[4][4];
+            scores(S, base, full, s);
+            // tokens kept by at least one row
+            bool kept[4][4];
+            uint64_t any = 0;
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint64_t bal = __ballot(s[tm][e] >= sthr);
+                    any |= bal;
+                    kept[tm][e] = ((bal >> (16 * g)) & 0xFFFFull) != 0ull;
+                }
+            if (!any) continue;
+            load_v(r0, [&](int tm, int e) { return kept[tm][e]; });
+            const float E_new = fmaxf(E_run, E_s);
+            if (E_run != -INFINITY && E_new != E_run) {
+                const float f = __builtin_amdgcn_exp2f(E_run - E_new);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[j] *= f;
+            }
+            E_run = E_new;
+            const float mu = mlog + E_new;
+            float w[4][4];
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) {
+                const f4_t vn = *reinterpret_cast<const f4_t *>(my_vn + 16 * tm + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[tm][e] = s[tm][e] >= sthr ? __builtin_amdgcn_exp2f(s[tm][e] - mu) * vn[e] : 0.f;
+            }
+            value_mfma(w);
+        }
+    }
+
+    // ---------------- merge the waves' partials into the chunk's partial
+    if constexpr (WV && PK) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][e] += dpp<kDppRor8>(acc[j][e]);
+    }
+    if constexpr (!GATED) {
+        if (g == 0) {
+            wst[wave][n][0] = m_state;
+            wst[wave][n][1] = l_run;
+        }
+    }
+    __syncthreads();   // also: every wave has read its q'' fragments from buf
+    const bool writer = row_ok && (!PK || n < 8);
+    float scale = 1.f;
+    if constexpr (!GATED) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w2 = 0; w2 < kMW; ++w2) M = fmaxf(M, wst[w2][n][0]);
+        scale = exp2_diff(m_state, M);
+        if (wave == 0 && g == 0 && writer) {
+            float L = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < kMW; ++w2) L += wst[w2][n][1] * exp2_diff(wst[w2][n][0], M);
+            part_ml[(part * rp + col_row) * 2] = M;
+            part_ml[(part * rp + col_row) * 2 + 1] = L;
+        }
+    } else {
+        scale = E_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(E_run);
+    }
+    if constexpr (WV) {
+        for (int w2 = 0; w2 < kMW; ++w2) {
+            if (wave == w2 && writer) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float *d = &buf[col_row * kQS + 8 * (4 * g + e) + j];
+                        *d = (w2 == 0 ? 0.f : *d) + acc[j][e] * scale;
+                    }
+            }
+            __syncthreads();
+        }
+        for (int i = tid; i < R * kD; i += kMBlock)
+            part_acc[(part * rp + i / kD) * kD + i % kD] = buf[(i / kD) * kQS + i % kD];
+    }
+}
+
+// --------------------------------------------------------------------------
+// Dispatch, one translation unit per K bit width (TQ_DECODE_KB = 2, 3, 4).
+// --------------------------------------------------------------------------
+template <int KB, int VB, bool PK, bool CONTIG>
+static void launch_mfma_mode(const DecodeArgs &a, int mode, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_kv * a.n_chunks)), block(kMBlock);
+#define TQ_MFMA_ARGS a, a.k_codes, a.k_norms, a.v_codes, a.v_norms, a.q, a.block_table, a.seq_lens, a.part_ml, \
+        a.part_acc, a.tilemax
+    if (mode == MODE_DENSE)
+        hipLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG>), grid, block, 0, s, TQ_MFMA_ARGS);
+    else if (mode == MODE_SCORE)
+        hipLaunchKernelGGL((tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG>), grid, block, 0, s, TQ_MFMA_ARGS);
+    else
+        hipLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG>), grid, block, 0, s, TQ_MFMA_ARGS);
+#undef TQ_MFMA_ARGS
+}
+
+template <int KB, int VB>
+static void launch_mfma_vb(const DecodeArgs &a, int mode, hipStream_t s) {
+    const bool pk = a.rows <= 8;
+    if (a.contig) {
+        if (pk) launch_mfma_mode<KB, VB, true, true>(a, mode, s);
+        else launch_mfma_mode<KB, VB, false, true>(a, mode, s);
+    } else {
+        if (pk) launch_mfma_mode<KB, VB, true, false>(a, mode, s);
+        else launch_mfma_mode<KB, VB, false, false>(a, mode, s);
+    }
+}
+
+#define TQ_CAT2(a, b) a##b
+#define TQ_CAT(a, b) TQ_CAT2(a, b)
+void TQ_CAT(launch_mfma_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStream_t s) {
+    switch (a.v_bits) {
+        case 2: launch_mfma_vb<TQ_DECODE_KB, 2>(a, mode, s); break;
+        case 3: launch_mfma_vb<TQ_DECODE_KB, 3>(a, mode, s); break;
+        default: launch_mfma_vb<TQ_DECODE_KB, 4>(a, mode, s); break;
+    }
+}
+
+}  // namespace tq

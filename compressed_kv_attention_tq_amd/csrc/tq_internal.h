@@ -16,6 +16,8 @@ constexpr int kBlock = 64 * kWaves;// decode: threads per pass block
 constexpr int kSlice = 64;         // decode: tokens a wave scores at once (one per lane);
                                    //         also the sparse-V gating tile
 constexpr int kChunkUnit = kBlock; // decode: chunks are multiples of this many tokens
+constexpr int kMW = 4;             // decode, matrix-core path: waves per block
+constexpr int kMBlock = 64 * kMW;  //   threads per block; chunks are multiples of kMBlock tokens
 constexpr int kLutMax = 256;       // quantize: max entries of the encode lookup table
 
 // One side of a quantize launch.
@@ -80,6 +82,8 @@ struct DecodeArgs {
     float qscale;             // softmax_scale * log2(e) / sqrt(128)
     float tau;
     int32_t k_bits, v_bits;
+    int32_t mfma;             // 1: matrix-core pass kernels, 0: vector-ALU kernels
+    int32_t contig;           // matrix-core path: every 64-token slice lies in one page
     float kc[TQ_MAX_LEVELS];
     float vc[TQ_MAX_LEVELS];
 };

@@ -41,6 +41,43 @@ def log(*a):
     sys.stdout.flush()
 
 
+# Decode kernels under test: the matrix-core pass with the default chunking, the
+# same with 1024-token chunks (several slices per wave, so the next-slice loads
+# run), and the vector-ALU pass.
+DECODE_KERNELS = {
+    "mfma": {"TQ_DECODE_KERNEL": "mfma"},
+    "mfma-c1024": {"TQ_DECODE_KERNEL": "mfma", "TQ_DECODE_CHUNK": "1024"},
+    "valu": {"TQ_DECODE_KERNEL": "valu"},
+}
+
+
+@pytest.fixture(params=list(DECODE_KERNELS))
+def kernel(request, monkeypatch):
+    monkeypatch.delenv("TQ_DECODE_CHUNK", raising=False)
+    for k, v in DECODE_KERNELS[request.param].items():
+        monkeypatch.setenv(k, v)
+    log(f"[decode kernel {request.param}]")
+    return request.param
+
+
+# Oracle results reused across the kernels of one case (keyed by the workload's
+# defining parameters; only the last few are kept).
+_ORACLE_MEMO = {}
+
+
+def _wl_key(wl):
+    return (wl.name, wl.kind, wl.seed, wl.n_seqs, tuple(int(x) for x in wl.seq_lens), wl.n_qtok, wl.n_q_heads,
+            wl.n_kv_heads, wl.k_bits, wl.v_bits, wl.block_size, wl.n_blocks)
+
+
+def _memo(key, fn):
+    if key not in _ORACLE_MEMO:
+        while len(_ORACLE_MEMO) >= 4:
+            _ORACLE_MEMO.pop(next(iter(_ORACLE_MEMO)))
+        _ORACLE_MEMO[key] = fn()
+    return _ORACLE_MEMO[key]
+
+
 # --------------------------------------------------------------------------- quantize
 
 def quantize_and_compare(x16, signs, bits, block_size=16, slot_perm=None, token_pad=0):
@@ -146,21 +183,29 @@ def test_dequantize_matches_oracle(bits):
 
 # --------------------------------------------------------------------------- decode
 
-def decode_and_compare(wl, seqs=None, kv_heads=None, tau=None, scale=0.0, gpu_caches=None):
+def oracle_caches(wl):
+    return _memo(("caches",) + _wl_key(wl), lambda: (U.oracle_cache(wl, 0), U.oracle_cache(wl, 1)))
+
+
+def decode_and_compare(wl, seqs=None, kv_heads=None, tau=None, scale=0.0, gpu_caches=None, q=None,
+                       oracle_key=None):
     """Decode on the GPU with oracle-written caches; compare rows of the given seqs."""
     torch = _t()
     tau = wl.tau if tau is None else tau
     if gpu_caches is None:
-        ok, ov = U.oracle_cache(wl, 0), U.oracle_cache(wl, 1)
+        ok, ov = oracle_caches(wl)
         gk, gv = U.gpu_cache_from(ok), U.gpu_cache_from(ov)
     else:
         ok, ov, gk, gv = gpu_caches
-    q = wl.queries()
+    q = wl.queries() if q is None else q
     out = T.tq_decode_attention(gk, gv, torch.from_numpy(q).cuda(),
                                 torch.from_numpy(wl.seq_lens).cuda(),
                                 torch.from_numpy(wl.block_table).cuda(), scale, tau).cpu().numpy()
-    want, weights = O.decode_attention(q, ok, ov, wl.seq_lens, wl.block_table, wl.n_qtok, scale, tau,
-                                       seqs=seqs, kv_heads=kv_heads, return_weights=True)
+    key = ("decode",) + _wl_key(wl) + (tau, scale, None if seqs is None else tuple(seqs),
+                                       None if kv_heads is None else tuple(kv_heads), oracle_key)
+    want, weights = _memo(key, lambda: O.decode_attention(q, ok, ov, wl.seq_lens, wl.block_table, wl.n_qtok,
+                                                          scale, tau, seqs=seqs, kv_heads=kv_heads,
+                                                          return_weights=True))
     seqs = range(wl.n_seqs) if seqs is None else seqs
     kv_heads = range(wl.n_kv_heads) if kv_heads is None else kv_heads
     worst, ambiguous = 0.0, 0
@@ -190,7 +235,7 @@ def decode_and_compare(wl, seqs=None, kv_heads=None, tau=None, scale=0.0, gpu_ca
     return out, want
 
 
-def test_decode_tiny_workload():
+def test_decode_tiny_workload(kernel):
     decode_and_compare(W.tiny())
 
 
@@ -206,28 +251,28 @@ def test_decode_tiny_workload():
     (2, [333, 1024], 3, 4, 1, 2, 2, 32),
     (1, [4097], 1, 16, 16, 4, 2, 256),
 ], ids=lambda c: f"s{c[0]}-q{c[2]}-h{c[3]}/{c[4]}-b{c[5]}{c[6]}-bs{c[7]}")
-def test_decode_small_cases(case):
+def test_decode_small_cases(case, kernel):
     n_seqs, lens, n_qtok, hq, hkv, kb, vb, bs = case
     wl = W.small_decode(seed=sum(lens), n_seqs=n_seqs, lens=lens, n_qtok=n_qtok, n_q_heads=hq,
                         n_kv_heads=hkv, k_bits=kb, v_bits=vb, block_size=bs)
     decode_and_compare(wl)
 
 
-def test_decode_rows_with_no_visible_token_are_zero():
+def test_decode_rows_with_no_visible_token_are_zero(kernel):
     wl = W.small_decode(seed=3, n_seqs=2, lens=[2, 0], n_qtok=4, n_q_heads=2, n_kv_heads=1, k_bits=4,
                         v_bits=3, block_size=16)
     out, want = decode_and_compare(wl)
     assert np.all(out[0, :2] == 0) and np.all(out[1] == 0)
 
 
-def test_decode_custom_scale():
+def test_decode_custom_scale(kernel):
     wl = W.small_decode(seed=8, n_seqs=1, lens=[800], n_qtok=1, n_q_heads=4, n_kv_heads=2, k_bits=4,
                         v_bits=4, block_size=256)
     decode_and_compare(wl, scale=0.3)
 
 
 @pytest.mark.parametrize("tau", [1e-4, 1e-3, 3e-2, 0.5, 1.5])
-def test_decode_sparse_small(tau):
+def test_decode_sparse_small(tau, kernel):
     wl = W.small_decode(seed=11, n_seqs=2, lens=[3000, 900], n_qtok=2, n_q_heads=8, n_kv_heads=2, k_bits=3,
                         v_bits=2, tau=tau, block_size=256)
     out, _ = decode_and_compare(wl)
@@ -235,12 +280,34 @@ def test_decode_sparse_small(tau):
         assert np.all(out == 0)
 
 
-def test_decode_sparse_peaked_small():
+@pytest.mark.parametrize("variant", ["large-q", "small-q"])
+def test_decode_extreme_magnitudes(variant, kernel):
+    """Queries scaled far from unit size (K norms scaled back for large ones, so the
+    scores keep their spread) and V norms spread over eight decades."""
+    wl = W.small_decode(seed=17, n_seqs=2, lens=[1200, 333], n_qtok=2, n_q_heads=8, n_kv_heads=2, k_bits=4,
+                        v_bits=3, block_size=64)
+    qs = 300.0 if variant == "large-q" else 1e-3
+
+    def build():
+        ok, ov = U.oracle_cache(wl, 0), U.oracle_cache(wl, 1)
+        f = np.random.default_rng(99).choice([3e4, 1.0, 1e-3], size=ov.norms.shape, p=[0.05, 0.5, 0.45])
+        ov.norms = (ov.norms * f).astype(np.float32)
+        if variant == "large-q":
+            ok.norms = (ok.norms / qs).astype(np.float32)
+        return ok, ov
+
+    ok, ov = _memo(("extreme", variant) + _wl_key(wl), build)
+    q = (wl.queries().astype(np.float64) * qs).astype(np.float16)
+    decode_and_compare(wl, gpu_caches=(ok, ov, U.gpu_cache_from(ok), U.gpu_cache_from(ov)), q=q,
+                       oracle_key=variant)
+
+
+def test_decode_sparse_peaked_small(kernel):
     wl = W.longctx(context=8192, batch=2)
     decode_and_compare(wl)
 
 
-def test_decode_llama8b_full():
+def test_decode_llama8b_full(kernel):
     """Llama-3-8B-shaped decode (32 q / 8 KV heads, 32K context, K4/V3), every row."""
     decode_and_compare(W.llama8b())
 
@@ -260,7 +327,8 @@ def _mixed_caches(wl, sampled):
         kx = torch.randn((n, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
         vx = torch.randn((n, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
         T.tq_quantize_kv(gk, kx, gv, vx, torch.from_numpy(wl.slots(b)).cuda())
-    ok, ov = U.oracle_cache(wl, 0, seqs=sampled), U.oracle_cache(wl, 1, seqs=sampled)
+    ok, ov = _memo(("mixed", tuple(sampled)) + _wl_key(wl),
+                   lambda: (U.oracle_cache(wl, 0, seqs=sampled), U.oracle_cache(wl, 1, seqs=sampled)))
     blocks = np.concatenate([wl.block_table[b][: -(-int(wl.seq_lens[b]) // wl.block_size)] for b in sampled])
     U.upload_blocks(ok, gk, blocks)
     U.upload_blocks(ov, gv, blocks)
@@ -268,14 +336,14 @@ def _mixed_caches(wl, sampled):
     return ok, ov, gk, gv
 
 
-def test_decode_longctx_sampled():
+def test_decode_longctx_sampled(kernel):
     """4 x 128K sparse decode (40 q / 4 KV heads, K3/V2, tau 1e-4): sequence 0 checked, all heads."""
     wl = W.longctx()
     caches = _mixed_caches(wl, [0])
     decode_and_compare(wl, seqs=[0], gpu_caches=caches)
 
 
-def test_decode_ragged_sampled():
+def test_decode_ragged_sampled(kernel):
     """64 ragged sequences 4K-64K, 4 query tokens, paged: shortest and longest sequence checked."""
     wl = W.ragged()
     sampled = [int(np.argmin(wl.seq_lens)), int(np.argmax(wl.seq_lens))]
@@ -283,7 +351,7 @@ def test_decode_ragged_sampled():
     decode_and_compare(wl, seqs=sampled, gpu_caches=caches)
 
 
-def test_end_to_end_tiny_against_oracle_pipeline():
+def test_end_to_end_tiny_against_oracle_pipeline(kernel):
     """GPU quantize + GPU decode vs oracle quantize + oracle decode (codes equal away from
     boundaries, so the outputs agree to the attention tolerance unless a boundary code flipped)."""
     torch = _t()
@@ -304,7 +372,7 @@ def test_end_to_end_tiny_against_oracle_pipeline():
     assert rel < (ATOL_ROW if flips == 0 else 1e-2)
 
 
-def test_graph_replay_matches_eager():
+def test_graph_replay_matches_eager(kernel):
     """Quantize-append + decode captured in a HIP graph: every replay equals the eager result."""
     torch = _t()
     wl = W.small_decode(seed=21, n_seqs=2, lens=[1500, 700], n_qtok=2, n_q_heads=8, n_kv_heads=2, k_bits=4,
