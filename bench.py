@@ -36,7 +36,8 @@ from compressed_kv_attention_tq_amd import workloads as W  # noqa: E402
 METRIC = "compressed-KV decode attention HBM GB/s (% of peak) + quantize Mtok/s"
 HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
-KERNEL_SOURCES = ["tq_decode.hip", "tq_device.h", "tq_quant.hip", "tq_internal.h"]
+KERNEL_SOURCES = ["tq_decode.hip", "tq_decode_mfma.hip", "tq_decode_common.h", "tq_device.h", "tq_quant.hip",
+                  "tq_internal.h", "tq_api.cpp"]
 
 
 def log(*a):
@@ -118,7 +119,7 @@ def run_decode(args, torch):
     kb, vb = wl.k_bits, wl.v_bits
     per_tok = cache_bytes_per_token_head(kb) + cache_bytes_per_token_head(vb)
     cache_bytes = wl.total_tokens * wl.n_kv_heads * per_tok
-    reps = args.replicas or max(1, math.ceil(1.5 * LLC_BYTES / cache_bytes))
+    reps = args.replicas or min(64, max(1, math.ceil(1.5 * LLC_BYTES / cache_bytes)))
     log(f"[bench] workload {wl.name}: {wl.n_seqs} seqs, {wl.total_tokens} tokens, cache {cache_bytes / 1e6:.1f} MB, "
         f"{reps} replicas")
 
@@ -168,7 +169,8 @@ def run_decode(args, torch):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # eager steps, with the dominant kernel bracketed by HIP events on the launch stream
+    # eager steps; the library launches the dominant kernel with start / stop events
+    # (hipExtLaunchKernelGGL), which time that kernel's execution
     evs = HipEvents(args.steps)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -217,17 +219,22 @@ def run_decode(args, torch):
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
     log(f"[bench] {ms_step * 1e3:.1f} us/step (graph), {ms_step_eager * 1e3:.1f} us/step (eager), "
-        f"pass kernel {pass_ms * 1e3:.1f} us, step {value:.0f} GB/s, pass {achieved:.0f} GB/s")
-    kernel_key = f"decode_pass_{wl.name}"
+        f"pass kernel {pass_ms * 1e3:.1f} us, "
+        f"step {value:.0f} GB/s, pass {achieved:.0f} GB/s")
+    mfma = os.environ.get("TQ_DECODE_KERNEL", "mfma") != "valu"
+    kernel = "tq_decode_mfma_kernel" if mfma else "tq_decode_pass_kernel"
+    kernel_key = f"{kernel}:{wl.name}"
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(kernel_key),
-            "kernel": "tq_decode_pass_kernel", "bytes_per_launch": pass_bytes,
+            "kernel": kernel + (" (scoring pass)" if wl.tau > 0 else ""), "bytes_per_launch": pass_bytes,
             "avg_launch_us": round(pass_ms * 1e3, 2)}
     cfg = {"workload": f"{wl.name}: {wl.n_seqs} seq x {int(wl.seq_lens.max())} tokens, "
                        f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d=128, K{kb}/V{vb}, "
                        f"{wl.n_qtok} query token(s), tau={wl.tau}, page {wl.block_size}",
            "global_batch": wl.n_seqs, "seq_len": int(wl.seq_lens.max()), "replicas": reps,
            "launch": "HIP graph replay", "ms_per_step_eager": round(ms_step_eager, 5),
+           "decode_kernel": ("matrix-core pass (fp16 MFMA, hi/lo-split fp32 operands, fp32 accumulate)"
+                             if mfma else "vector-ALU pass (fp32)"),
            "parallelism": "single GPU"}
     return wl, value, ms_step, roof, cfg, step_bytes
 
@@ -284,7 +291,8 @@ def run_quantize(args, torch):
             "value": round(mtok, 1), "unit": "M token-layers/s",
             "ms_per_32_layers": round(pass_ms, 4),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic("quantize_prefill"),
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": pmc_traffic("tq_quantize_kernel:prefill"),
                          "kernel": "tq_quantize_kernel", "bytes_per_launch": bytes_per_call,
                          "vectors_per_launch": vec_per_call, "avg_launch_us": round(kern_ms * 1e3, 2)}}
 
@@ -344,6 +352,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--quantize-reps", type=int, default=5)
     ap.add_argument("--no-quantize", action="store_true")
+    ap.add_argument("--quantize-only", action="store_true", help="only the prefill quantize measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 256 MiB (reference for HBM byte counters)")
@@ -367,6 +376,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": 256 << 20, "copies": 5}), flush=True)
         return
 
+    if args.quantize_only:
+        print(json.dumps({"quantize": run_quantize(args, torch)}), flush=True)
+        return
     wl, value, ms_step, roof, cfg, step_bytes = run_decode(args, torch)
     quant = None if args.no_quantize else run_quantize(args, torch)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)

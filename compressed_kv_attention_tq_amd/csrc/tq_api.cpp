@@ -145,7 +145,7 @@ DecodePlan plan_decode(int n_seqs, int n_kv, int rows, int max_blocks, int block
     const int64_t cap = (int64_t)max_blocks * block_size;
     const int64_t total = (int64_t)n_seqs * n_kv * cap;
     const int unit = mfma ? kMBlock : kChunkUnit;
-    const int64_t target = mfma ? 1024 : 512;
+    const int64_t target = 512;
     int chunk = unit;
     while (chunk < 16384 && total / (2 * chunk) >= target) chunk *= 2;
     if (const char *e = getenv("TQ_DECODE_CHUNK")) {

@@ -457,7 +457,7 @@ __global__ __launch_bounds__(256) void tq_stats_kernel(DecodeArgs a) {
 // Merge the chunk partials of one output row and inverse-rotate it (both pass
 // kernels write the same partial layout).  One block per row: 8 chunk groups x
 // 32 float4 columns.  Dense: each thread merges its chunks (c = group,
-// group + 8, ...) with the log-sum-exp rule in batches of 8 loads, then the
+// group + 8, ...) with the log-sum-exp rule in batches of 16 loads, then the
 // groups are merged through LDS and o = s_V * H (acc / L) / sqrt(128).  Gated:
 // the partials are already normalised and are summed.
 // --------------------------------------------------------------------------
@@ -482,11 +482,12 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     const float *pa = a.part_acc + (base * a.rows_pad + r) * kD + 4 * q4;  // chunk c at pa[c * astride]
     float M = -INFINITY, L = 0.f;
     f4_t x = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = cg; c0 < nc; c0 += 64) {
-        float m[8], l[8];
-        f4_t v[8];
+    constexpr int kB = 16;   // chunks per thread per batch (one round of loads)
+    for (int c0 = cg; c0 < nc; c0 += 8 * kB) {
+        float m[kB], l[kB];
+        f4_t v[kB];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kB; ++i) {
             const int cc = c0 + 8 * i;
             const bool ok = cc < nc;
             m[i] = (!SPARSE && ok) ? ml[cc * mstride] : -INFINITY;
@@ -495,16 +496,16 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
         }
         if (SPARSE) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x += v[i];
+            for (int i = 0; i < kB; ++i) x += v[i];
         } else {
             float mb = M;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) mb = fmaxf(mb, m[i]);
+            for (int i = 0; i < kB; ++i) mb = fmaxf(mb, m[i]);
             const float sc = exp2_diff(M, mb);
             x *= sc;
             L *= sc;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kB; ++i) {
                 const float f = exp2_diff(m[i], mb);
                 x += f * v[i];
                 L += f * l[i];
@@ -552,101 +553,103 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
 // translation units (this file compiled with TQ_DECODE_KB=2, 3, 4) so the
 // build runs in parallel; the unit without TQ_DECODE_KB holds the rest.
 // --------------------------------------------------------------------------
-void launch_pass_kb2(const DecodeArgs &a, int mode, hipStream_t s);
-void launch_pass_kb3(const DecodeArgs &a, int mode, hipStream_t s);
-void launch_pass_kb4(const DecodeArgs &a, int mode, hipStream_t s);
+// ev0 / ev1 (may be null): recorded at the start and the end of the pass kernel's
+// execution (hipExtLaunchKernelGGL), for timing.
+void launch_pass_kb2(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+void launch_pass_kb3(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+void launch_pass_kb4(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 #ifdef TQ_DECODE_KB
 template <int KB, int VB, int RP>
-static void launch_pass(const DecodeArgs &a, int mode, hipStream_t s) {
+static void launch_pass(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_kv * a.n_chunks));
 #define TQ_PASS_ARGS a, a.k_codes, a.k_norms, a.v_codes, a.v_norms, a.qrot, a.block_table, a.seq_lens, \
         a.tilemax, a.stats, a.part_ml, a.part_acc, a.tilemax
     if (mode == MODE_DENSE)
-        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, VB, RP, MODE_DENSE>), grid, dim3(kBlock), 0, s, TQ_PASS_ARGS);
+        hipExtLaunchKernelGGL((tq_decode_pass_kernel<KB, VB, RP, MODE_DENSE>), grid, dim3(kBlock), 0, s, ev0, ev1, 0,
+                              TQ_PASS_ARGS);
     else if (mode == MODE_SCORE)
-        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, 2, RP, MODE_SCORE>), grid, dim3(kBlock), 0, s, TQ_PASS_ARGS);
+        hipExtLaunchKernelGGL((tq_decode_pass_kernel<KB, 2, RP, MODE_SCORE>), grid, dim3(kBlock), 0, s, ev0, ev1, 0,
+                              TQ_PASS_ARGS);
     else
-        hipLaunchKernelGGL((tq_decode_pass_kernel<KB, VB, RP, MODE_GATED>), grid, dim3(kBlock), 0, s, TQ_PASS_ARGS);
+        hipExtLaunchKernelGGL((tq_decode_pass_kernel<KB, VB, RP, MODE_GATED>), grid, dim3(kBlock), 0, s, ev0, ev1, 0,
+                              TQ_PASS_ARGS);
 #undef TQ_PASS_ARGS
 }
 
 template <int KB, int VB>
-static void launch_pass_rp(const DecodeArgs &a, int mode, hipStream_t s) {
+static void launch_pass_rp(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     switch (a.rows_pad) {
-        case 1: launch_pass<KB, VB, 1>(a, mode, s); break;
-        case 2: launch_pass<KB, VB, 2>(a, mode, s); break;
-        case 4: launch_pass<KB, VB, 4>(a, mode, s); break;
-        case 8: launch_pass<KB, VB, 8>(a, mode, s); break;
-        case 12: launch_pass<KB, VB, 12>(a, mode, s); break;
-        default: launch_pass<KB, VB, 16>(a, mode, s); break;
+        case 1: launch_pass<KB, VB, 1>(a, mode, s, ev0, ev1); break;
+        case 2: launch_pass<KB, VB, 2>(a, mode, s, ev0, ev1); break;
+        case 4: launch_pass<KB, VB, 4>(a, mode, s, ev0, ev1); break;
+        case 8: launch_pass<KB, VB, 8>(a, mode, s, ev0, ev1); break;
+        case 12: launch_pass<KB, VB, 12>(a, mode, s, ev0, ev1); break;
+        default: launch_pass<KB, VB, 16>(a, mode, s, ev0, ev1); break;
     }
 }
 
 template <int KB>
-static void launch_pass_vb(const DecodeArgs &a, int mode, hipStream_t s) {
+static void launch_pass_vb(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     switch (a.v_bits) {
-        case 2: launch_pass_rp<KB, 2>(a, mode, s); break;
-        case 3: launch_pass_rp<KB, 3>(a, mode, s); break;
-        default: launch_pass_rp<KB, 4>(a, mode, s); break;
+        case 2: launch_pass_rp<KB, 2>(a, mode, s, ev0, ev1); break;
+        case 3: launch_pass_rp<KB, 3>(a, mode, s, ev0, ev1); break;
+        default: launch_pass_rp<KB, 4>(a, mode, s, ev0, ev1); break;
     }
 }
 
 #define TQ_CAT2(a, b) a##b
 #define TQ_CAT(a, b) TQ_CAT2(a, b)
-void TQ_CAT(launch_pass_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStream_t s) {
-    launch_pass_vb<TQ_DECODE_KB>(a, mode, s);
+void TQ_CAT(launch_pass_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0,
+                                          hipEvent_t ev1) {
+    launch_pass_vb<TQ_DECODE_KB>(a, mode, s, ev0, ev1);
 }
 
 #else
 
-void launch_mfma_kb2(const DecodeArgs &a, int mode, hipStream_t s);
-void launch_mfma_kb3(const DecodeArgs &a, int mode, hipStream_t s);
-void launch_mfma_kb4(const DecodeArgs &a, int mode, hipStream_t s);
+void launch_mfma_kb2(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+void launch_mfma_kb3(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+void launch_mfma_kb4(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
-static void launch_mfma_any(const DecodeArgs &a, int mode, hipStream_t s) {
+static void launch_mfma_any(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0 = nullptr,
+                            hipEvent_t ev1 = nullptr) {
     switch (a.k_bits) {
-        case 2: launch_mfma_kb2(a, mode, s); break;
-        case 3: launch_mfma_kb3(a, mode, s); break;
-        default: launch_mfma_kb4(a, mode, s); break;
+        case 2: launch_mfma_kb2(a, mode, s, ev0, ev1); break;
+        case 3: launch_mfma_kb3(a, mode, s, ev0, ev1); break;
+        default: launch_mfma_kb4(a, mode, s, ev0, ev1); break;
     }
 }
 
-static void launch_pass_any(const DecodeArgs &a, int mode, hipStream_t s) {
+static void launch_pass_any(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0 = nullptr,
+                            hipEvent_t ev1 = nullptr) {
     switch (a.k_bits) {
-        case 2: launch_pass_kb2(a, mode, s); break;
-        case 3: launch_pass_kb3(a, mode, s); break;
-        default: launch_pass_kb4(a, mode, s); break;
+        case 2: launch_pass_kb2(a, mode, s, ev0, ev1); break;
+        case 3: launch_pass_kb3(a, mode, s, ev0, ev1); break;
+        default: launch_pass_kb4(a, mode, s, ev0, ev1); break;
     }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
     const dim3 rows_grid((unsigned)((int64_t)a.n_seqs * a.n_qtok * a.n_q_heads));
     if (a.mfma) {   // q rotation runs inside the pass kernels
-        if (ev_before) (void)hipEventRecord(ev_before, s);
         if (a.tau > 0.f) {
-            launch_mfma_any(a, MODE_SCORE, s);
-            if (ev_after) (void)hipEventRecord(ev_after, s);
+            launch_mfma_any(a, MODE_SCORE, s, ev_before, ev_after);
             launch_mfma_any(a, MODE_GATED, s);
             hipLaunchKernelGGL(tq_merge_kernel<true>, rows_grid, dim3(256), 0, s, a);
         } else {
-            launch_mfma_any(a, MODE_DENSE, s);
-            if (ev_after) (void)hipEventRecord(ev_after, s);
+            launch_mfma_any(a, MODE_DENSE, s, ev_before, ev_after);
             hipLaunchKernelGGL(tq_merge_kernel<false>, rows_grid, dim3(256), 0, s, a);
         }
         return hipGetLastError();
     }
     hipLaunchKernelGGL(tq_qrot_kernel, dim3(a.n_seqs * a.n_kv), dim3(64 * a.rows_pad), 0, s, a);
-    if (ev_before) (void)hipEventRecord(ev_before, s);
     if (a.tau > 0.f) {
-        launch_pass_any(a, MODE_SCORE, s);
-        if (ev_after) (void)hipEventRecord(ev_after, s);
+        launch_pass_any(a, MODE_SCORE, s, ev_before, ev_after);
         hipLaunchKernelGGL(tq_stats_kernel, dim3(a.n_seqs * a.n_kv), dim3(256), 0, s, a);
         launch_pass_any(a, MODE_GATED, s);
         hipLaunchKernelGGL(tq_merge_kernel<true>, rows_grid, dim3(256), 0, s, a);
     } else {
-        launch_pass_any(a, MODE_DENSE, s);
-        if (ev_after) (void)hipEventRecord(ev_after, s);
+        launch_pass_any(a, MODE_DENSE, s, ev_before, ev_after);
         hipLaunchKernelGGL(tq_merge_kernel<false>, rows_grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();

@@ -103,8 +103,19 @@ __device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[NW]) 
 
 // A operand of the score MFMA for k-step ks from the lane's 32 positions of one
 // token (positions 32g + 8ks .. +7): 4 lookups of a code pair -> fp16 pair.
+// Centroid-pair tables are replicated 32 times, entry-major: copy c of entry e
+// is dword 32 e + c, and lane l reads copy l % 32, so the lanes of a half-wave
+// never meet in an LDS bank whatever their indices.
+template <int B>
+constexpr int tab_copies() { return 32; }
+
+template <int B>
+__device__ __forceinline__ uint32_t tab_read(const uint32_t *tab, uint32_t idx, uint32_t lane_off) {
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(tab) + ((idx << 7) | lane_off));
+}
+
 template <int KB>
-__device__ __forceinline__ u4_t k_frag(const uint32_t (&w)[KB], int ks, const uint32_t *tab) {
+__device__ __forceinline__ u4_t k_frag(const uint32_t (&w)[KB], int ks, const uint32_t *tab, uint32_t lane_off) {
     constexpr int FB = 2 * KB;
     uint32_t u;
     if constexpr (KB == 4) {
@@ -119,7 +130,7 @@ __device__ __forceinline__ u4_t k_frag(const uint32_t (&w)[KB], int ks, const ui
     }
     u4_t f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) f[k] = tab[(u >> (FB * k)) & ((1u << FB) - 1u)];
+    for (int k = 0; k < 4; ++k) f[k] = tab_read<KB>(tab, (u >> (FB * k)) & ((1u << FB) - 1u), lane_off);
     return f;
 }
 
@@ -165,12 +176,14 @@ __device__ __forceinline__ void v_pairs(const uint32_t (&u)[8], uint32_t (&x)[4]
 
 // A operand of the value MFMA for position tile j (position 8n + j of 8 tokens).
 template <int VB>
-__device__ __forceinline__ u4_t v_frag(const uint32_t (&x)[4], const uint32_t (&y)[4], int j, const uint32_t *tab) {
+__device__ __forceinline__ u4_t v_frag(const uint32_t (&x)[4], const uint32_t (&y)[4], int j, const uint32_t *tab,
+                                       uint32_t lane_off) {
     constexpr int FB = 2 * VB;
     const int sh = FB * (j >> 1);
     u4_t f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) f[k] = tab[(((j & 1) ? y[k] : x[k]) >> sh) & ((1u << FB) - 1u)];
+    for (int k = 0; k < 4; ++k)
+        f[k] = tab_read<VB>(tab, (((j & 1) ? y[k] : x[k]) >> sh) & ((1u << FB) - 1u), lane_off);
     return f;
 }
 
@@ -201,9 +214,18 @@ void tq_decode_mfma_kernel(
     constexpr int KROW = 16 * KB, VROW = 16 * VB;   // bytes per code row
     constexpr int NQB = PK ? 4 : 8;                 // q'' B fragments
     constexpr int NPB = PK ? 2 : 4;                 // weight B fragments
-    __shared__ uint32_t ktab[NKT];
-    __shared__ uint32_t vtab[WV ? NVT : 1];
-    __shared__ __attribute__((aligned(16))) float buf[16 * kQS];       // q'', then per-row partials
+    // the replicated K and V pair tables while slices are processed; afterwards the
+    // waves' partials ([wave][row][128] for at most 8 rows, one [row][kQS]
+    // accumulator otherwise)
+    constexpr int KCOP = tab_copies<KB>(), VCOP = tab_copies<VB>();
+    constexpr int kTabWords = NKT * KCOP + (WV ? NVT * VCOP : 0);
+    constexpr int kMerge = PK ? kMW * 8 * kD : 16 * kQS;
+    constexpr int kArea = kTabWords > kMerge ? kTabWords : kMerge;
+    __shared__ __attribute__((aligned(16))) uint32_t area[kArea];
+    uint32_t *const ktab = area;
+    uint32_t *const vtab = area + NKT * KCOP;
+    float *const mbuf = reinterpret_cast<float *>(area);
+    __shared__ __attribute__((aligned(16))) float buf[16 * kQS];      // q'' during set-up
     __shared__ __attribute__((aligned(16))) float nrm[kMW][2][64];     // per wave: K, V norms of the slice
     __shared__ float wst[kMW][16][2];
     __shared__ float red[kMW];
@@ -215,19 +237,27 @@ void tq_decode_mfma_kernel(
     const int c = blockIdx.x % a.n_chunks;
     const int unit = blockIdx.x / a.n_chunks;
     const int kv = unit % a.n_kv, b = unit / a.n_kv;
-    const int len = seq_lens[b];
     const int R = a.rows, rp = a.rows_pad;
     const int start = c * a.chunk;
-    if (start >= len) return;
-    const int end = min(start + a.chunk, len);
-    const int64_t part = (int64_t)unit * a.n_chunks + c;
-    const int64_t tile0 = (int64_t)unit * a.n_tiles;
-
     const int bs = a.block_size, n_kv = a.n_kv;
     const FastDiv bsdiv = make_fastdiv((uint32_t)bs);
     const int32_t *__restrict__ btab = block_table + (int64_t)b * a.max_blocks;
     constexpr int kStride = kMW * 64;
     const int first = start + wave * 64;
+    // page-table entries of the wave's first two slices are read together with the
+    // sequence length (indices clamped to the table; an entry is used only for
+    // positions below the length, where it is valid)
+    int blk0 = 0, blk1 = 0;
+    if constexpr (CONTIG && !GATED) {
+        const int last_page = a.max_blocks - 1;
+        blk0 = btab[min((int)fdiv((uint32_t)first, bsdiv), last_page)];
+        blk1 = btab[min((int)fdiv((uint32_t)(first + kStride), bsdiv), last_page)];
+    }
+    const int len = seq_lens[b];
+    if (start >= len) return;
+    const int end = min(start + a.chunk, len);
+    const int64_t part = (int64_t)unit * a.n_chunks + c;
+    const int64_t tile0 = (int64_t)unit * a.n_tiles;
 
     // word of a V row this lane loads, and (3-bit) the unit's offset in it
     int vwi = n, vo = 0;
@@ -309,8 +339,8 @@ void tq_decode_mfma_kernel(
     if constexpr (!GATED) {
         if (first < end) {
             if constexpr (CONTIG) {
-                r0n = row0_of(first, btab[fdiv((uint32_t)first, bsdiv)]);
-                blk_next = first + kStride < end ? btab[fdiv((uint32_t)(first + kStride), bsdiv)] : 0;
+                r0n = row0_of(first, blk0);
+                blk_next = blk1;
             } else {
                 fill_rows(first, page_of(btab, bsdiv, first + lane, end));
                 blk_next = page_of(btab, bsdiv, first + kStride + lane, end);
@@ -320,16 +350,27 @@ void tq_decode_mfma_kernel(
         }
     }
 
-    for (int i = tid; i < NKT; i += kMBlock) ktab[i] = half2_bits(a.kc[i & (LK - 1)], a.kc[i >> KB]);
-    if constexpr (WV)
-        for (int i = tid; i < NVT; i += kMBlock) vtab[i] = half2_bits(a.vc[i & (LV - 1)], a.vc[i >> VB]);
+    // pair tables: an entry is formed once and stored to all its copies
+    auto fill_table = [&](uint32_t *tab, const float *cb, int bits, int n_entries, int copies) {
+        const int lmask = (1 << bits) - 1;
+        for (int i = tid; i < n_entries * 4; i += kMBlock) {   // 4 threads per entry, 8 copies each
+            const int e = i >> 2;
+            const uint32_t v = half2_bits(cb[e & lmask], cb[e >> bits]);
+            u4_t *d = reinterpret_cast<u4_t *>(tab + e * copies + (i & 3) * 8);
+            d[0] = u4_t{v, v, v, v};
+            d[1] = u4_t{v, v, v, v};
+        }
+    };
+    fill_table(ktab, a.kc, KB, NKT, KCOP);
+    if constexpr (WV) fill_table(vtab, a.vc, VB, NVT, VCOP);
+    const uint32_t lane_off = (uint32_t)(lane & 31) << 2;
 
     // ---- q'' = qscale * H (s_K * q) of this KV head's rows, into buf
     {
         float qm = 0.f;
-        for (int r = wave; r < 16; r += kMW) {
-            float x0 = 0.f, x1 = 0.f;
-            if (r < R) {
+        for (int r = wave; r < R; r += kMW) {
+            float x0, x1;
+            {
                 const int jq = r / a.group, h = kv * a.group + r % a.group;
                 const uint16_t *qp = qin + (((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * kD;
                 const uint32_t *sg = a.k_signs + kv * 4;
@@ -382,7 +423,7 @@ void tq_decode_mfma_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const float *qr = &buf[col_row * kQS + 32 * g + 8 * ks + 2 * k];
-            const float q0 = qr[0] * sq, q1 = qr[1] * sq;
+            const float q0 = col_row < R ? qr[0] * sq : 0.f, q1 = col_row < R ? qr[1] * sq : 0.f;
             if constexpr (PK) {
                 qb[ks][k] = split_pair(q0, q1, losel);
             } else {
@@ -415,7 +456,7 @@ void tq_decode_mfma_kernel(
             S[tm] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const u4_t af = k_frag<KB>(kw[tm], ks, ktab);
+                const u4_t af = k_frag<KB>(kw[tm], ks, ktab, lane_off);
                 S[tm] = mfma_f16(af, qb[ks], S[tm]);
                 if constexpr (!PK) S[tm] = mfma_f16(af, qb[4 + ks], S[tm]);
             }
@@ -426,7 +467,7 @@ void tq_decode_mfma_kernel(
     // weights e * vn * 2^-E stay below 1
     float *my_kn = nrm[wave][0], *my_vn = nrm[wave][1];
     auto stage_norms = [&](int base) -> float {
-        my_kn[lane] = knl;
+        my_kn[lane] = knl * kscale;
         float v = 0.f;
         if constexpr (WV) {
             v = base + lane < end ? vnl : 0.f;
@@ -440,18 +481,25 @@ void tq_decode_mfma_kernel(
         return (float)min(max(ex, -40), 40);
     };
     // scores in the log2 domain, -inf where the row does not see the token
+    // (full: every row sees every token of the slice)
     auto scores = [&](const f4_t (&S)[4], int base, bool full, float (&s)[4][4]) {
-        const int dl = lim - base - 4 * g;   // element (tm, e) visible iff 16 tm + e <= dl
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) {
-            const f4_t kn = *reinterpret_cast<const f4_t *>(my_kn + 16 * tm + 4 * g) * kscale;
+            const f4_t kn = *reinterpret_cast<const f4_t *>(my_kn + 16 * tm + 4 * g);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float x = S[tm][e];
                 if constexpr (PK) x += dpp<kDppRor8>(x);
-                x *= kn[e];
-                s[tm][e] = (full || 16 * tm + e <= dl) ? x : -INFINITY;
+                s[tm][e] = x * kn[e];
             }
+        }
+        if (!full) {
+            const int dl = lim - base - 4 * g;   // element (tm, e) visible iff 16 tm + e <= dl
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (16 * tm + e > dl) s[tm][e] = -INFINITY;
         }
     };
     // value MFMAs of the loaded slice with weights w (score layout)
@@ -480,7 +528,7 @@ void tq_decode_mfma_kernel(
             v_pairs<VB>(u, x, y);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const u4_t af = v_frag<VB>(x, y, j, vtab);
+                const u4_t af = v_frag<VB>(x, y, j, vtab, lane_off);
                 acc[j] = mfma_f16(af, pb[ks], acc[j]);
                 if constexpr (!PK) acc[j] = mfma_f16(af, pb[2 + ks], acc[j]);
             }
@@ -540,7 +588,7 @@ void tq_decode_mfma_kernel(
             m_state = m_new == -INFINITY ? -INFINITY : mu;
             E_run = E_new;
             if constexpr (DENSE) {
-                if (__ballot(alpha != 1.f)) {
+                if (base != first && __ballot(alpha != 1.f)) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) acc[j] *= alpha;
                 }
@@ -611,7 +659,7 @@ void tq_decode_mfma_kernel(
             wst[wave][n][1] = l_run;
         }
     }
-    __syncthreads();   // also: every wave has read its q'' fragments from buf
+    __syncthreads();   // also: every wave is done with the pair tables
     const bool writer = row_ok && (!PK || n < 8);
     float scale = 1.f;
     if constexpr (!GATED) {
@@ -629,60 +677,81 @@ void tq_decode_mfma_kernel(
     } else {
         scale = E_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(E_run);
     }
-    if constexpr (WV) {
+    if constexpr (WV && PK) {
+        if (writer) {
+            float *d = &mbuf[(wave * 8 + col_row) * kD];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[8 * (4 * g + e) + j] = acc[j][e] * scale;
+        }
+        __syncthreads();
+        for (int i = tid; i < R * kD; i += kMBlock) {
+            float x = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < kMW; ++w2) x += mbuf[w2 * 8 * kD + i];
+            part_acc[(part * rp + i / kD) * kD + i % kD] = x;
+        }
+    } else if constexpr (WV) {
         for (int w2 = 0; w2 < kMW; ++w2) {
             if (wave == w2 && writer) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float *d = &buf[col_row * kQS + 8 * (4 * g + e) + j];
+                        float *d = &mbuf[col_row * kQS + 8 * (4 * g + e) + j];
                         *d = (w2 == 0 ? 0.f : *d) + acc[j][e] * scale;
                     }
             }
             __syncthreads();
         }
         for (int i = tid; i < R * kD; i += kMBlock)
-            part_acc[(part * rp + i / kD) * kD + i % kD] = buf[(i / kD) * kQS + i % kD];
+            part_acc[(part * rp + i / kD) * kD + i % kD] = mbuf[(i / kD) * kQS + i % kD];
     }
 }
 
 // --------------------------------------------------------------------------
 // Dispatch, one translation unit per K bit width (TQ_DECODE_KB = 2, 3, 4).
 // --------------------------------------------------------------------------
+// ev0 / ev1 (may be null): recorded at the start and the end of the kernel's
+// execution (hipExtLaunchKernelGGL), for timing.
 template <int KB, int VB, bool PK, bool CONTIG>
-static void launch_mfma_mode(const DecodeArgs &a, int mode, hipStream_t s) {
+static void launch_mfma_mode(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_kv * a.n_chunks)), block(kMBlock);
 #define TQ_MFMA_ARGS a, a.k_codes, a.k_norms, a.v_codes, a.v_norms, a.q, a.block_table, a.seq_lens, a.part_ml, \
         a.part_acc, a.tilemax
     if (mode == MODE_DENSE)
-        hipLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG>), grid, block, 0, s, TQ_MFMA_ARGS);
+        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG>), grid, block, 0, s, ev0, ev1, 0,
+                              TQ_MFMA_ARGS);
     else if (mode == MODE_SCORE)
-        hipLaunchKernelGGL((tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG>), grid, block, 0, s, TQ_MFMA_ARGS);
+        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG>), grid, block, 0, s, ev0, ev1, 0,
+                              TQ_MFMA_ARGS);
     else
-        hipLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG>), grid, block, 0, s, TQ_MFMA_ARGS);
+        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG>), grid, block, 0, s, ev0, ev1, 0,
+                              TQ_MFMA_ARGS);
 #undef TQ_MFMA_ARGS
 }
 
 template <int KB, int VB>
-static void launch_mfma_vb(const DecodeArgs &a, int mode, hipStream_t s) {
+static void launch_mfma_vb(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const bool pk = a.rows <= 8;
     if (a.contig) {
-        if (pk) launch_mfma_mode<KB, VB, true, true>(a, mode, s);
-        else launch_mfma_mode<KB, VB, false, true>(a, mode, s);
+        if (pk) launch_mfma_mode<KB, VB, true, true>(a, mode, s, ev0, ev1);
+        else launch_mfma_mode<KB, VB, false, true>(a, mode, s, ev0, ev1);
     } else {
-        if (pk) launch_mfma_mode<KB, VB, true, false>(a, mode, s);
-        else launch_mfma_mode<KB, VB, false, false>(a, mode, s);
+        if (pk) launch_mfma_mode<KB, VB, true, false>(a, mode, s, ev0, ev1);
+        else launch_mfma_mode<KB, VB, false, false>(a, mode, s, ev0, ev1);
     }
 }
 
 #define TQ_CAT2(a, b) a##b
 #define TQ_CAT(a, b) TQ_CAT2(a, b)
-void TQ_CAT(launch_mfma_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStream_t s) {
+void TQ_CAT(launch_mfma_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0,
+                                          hipEvent_t ev1) {
     switch (a.v_bits) {
-        case 2: launch_mfma_vb<TQ_DECODE_KB, 2>(a, mode, s); break;
-        case 3: launch_mfma_vb<TQ_DECODE_KB, 3>(a, mode, s); break;
-        default: launch_mfma_vb<TQ_DECODE_KB, 4>(a, mode, s); break;
+        case 2: launch_mfma_vb<TQ_DECODE_KB, 2>(a, mode, s, ev0, ev1); break;
+        case 3: launch_mfma_vb<TQ_DECODE_KB, 3>(a, mode, s, ev0, ev1); break;
+        default: launch_mfma_vb<TQ_DECODE_KB, 4>(a, mode, s, ev0, ev1); break;
     }
 }
 

@@ -149,6 +149,11 @@ tq_status tq_quantize_kv(const tq_cache *k, const void *k_src,
  * Query token j of a sequence of length len attends to positions t <= len - n_qtok + j;
  * query head h reads KV head h / (n_q_heads / n_kv_heads).  A row that sees no
  * position outputs zeros.
+ * Kernels: the pass runs on the matrix cores by default; the environment variable
+ * TQ_DECODE_KERNEL=valu selects the vector-ALU pass, and TQ_DECODE_CHUNK=<tokens>
+ * (a multiple of 256 for the matrix-core pass, 512 for the vector-ALU pass)
+ * overrides the tokens per pass block.  Both are read at every call and change
+ * the workspace size.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 tq_status tq_decode_attention(const tq_cache *k, const tq_cache *v, const void *q,
                               int32_t n_seqs, int32_t n_qtok, int32_t n_q_heads,
@@ -159,9 +164,10 @@ tq_status tq_decode_attention(const tq_cache *k, const tq_cache *v, const void *
 
 /* Same call as tq_decode_attention, for timing the dominant kernel: when `events`
  * is not NULL, events[0] and events[1] (hipEvent_t handles created by the caller)
- * are recorded on `stream` immediately before and after the main pass kernel (the
- * one that streams every K code: the dense pass, or the scoring pass when
- * sparse_v_tau > 0).  events == NULL behaves exactly like tq_decode_attention.
+ * mark the start and the end of the execution of the main pass kernel (the one
+ * that streams every K code: the dense pass, or the scoring pass when
+ * sparse_v_tau > 0), as hipExtLaunchKernelGGL records them.  events == NULL
+ * behaves exactly like tq_decode_attention.
  * Errors: as tq_decode_attention. */
 tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const void *q,
                                     int32_t n_seqs, int32_t n_qtok, int32_t n_q_heads,
