@@ -102,6 +102,8 @@ tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, in
     q.bits = c->bits;
     q.grid = (float)grid;
     q.lut_half = grid + 2;
+    q.bs_div = make_fastdiv((uint32_t)c->block_size);
+    q.kv_div = make_fastdiv((uint32_t)c->n_kv_heads);
     q.n_bnd = nb;
     for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) q.bnd[i] = i < nb ? c->cb.boundaries[i] : 0.f;
     return TQ_OK;
@@ -271,6 +273,8 @@ tq_status tq_dequantize(const tq_cache *c, const int64_t *slots, int32_t n_token
     a.n_kv = c->n_kv_heads;
     a.block_size = c->block_size;
     a.dst_fp16 = dst_is_fp16 ? 1 : 0;
+    a.kv_div = make_fastdiv((uint32_t)c->n_kv_heads);
+    a.bs_div = make_fastdiv((uint32_t)c->block_size);
     for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = i < c->cb.n_levels ? c->cb.centroids[i] : 0.f;
     if (launch_dequantize(a, c->bits, static_cast<hipStream_t>(stream)) != hipSuccess) return TQ_ERR_HIP;
     return TQ_OK;
@@ -356,6 +360,14 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     a.n_tiles = p.n_tiles;
     const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)kD);
     a.qscale = (float)(scale * M_LOG2E / sqrt((double)kD));
+    a.max_page = (int32_t)(std::min(k->n_blocks, v->n_blocks) - 1);
+    a.bs_div = make_fastdiv((uint32_t)a.block_size);
+    a.chunk_div = make_fastdiv((uint32_t)a.chunk);
+    a.chunk_div_n = make_fastdiv((uint32_t)a.n_chunks);
+    a.kv_div = make_fastdiv((uint32_t)a.n_kv);
+    a.grp_div = make_fastdiv((uint32_t)a.group);
+    a.qh_div = make_fastdiv((uint32_t)a.n_q_heads);
+    a.qt_div = make_fastdiv((uint32_t)a.n_qtok);
     a.tau = sparse_v_tau;
     a.k_bits = k->bits;
     a.v_bits = v->bits;
@@ -365,9 +377,15 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
         a.kc[i] = i < k->cb.n_levels ? k->cb.centroids[i] : 0.f;
         a.vc[i] = i < v->cb.n_levels ? v->cb.centroids[i] : 0.f;
     }
+    PairTables pt;
+    memset(&pt, 0, sizeof(pt));
+    for (int e = 0; e < (1 << (2 * k->bits)); ++e)
+        pt.k[e] = half2_bits(a.kc[e & ((1 << k->bits) - 1)], a.kc[e >> k->bits]);
+    for (int e = 0; e < (1 << (2 * v->bits)); ++e)
+        pt.v[e] = half2_bits(a.vc[e & ((1 << v->bits) - 1)], a.vc[e >> v->bits]);
     hipEvent_t ev0 = events ? static_cast<hipEvent_t>(events[0]) : nullptr;
     hipEvent_t ev1 = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
-    if (launch_decode(a, static_cast<hipStream_t>(stream), ev0, ev1) != hipSuccess) return TQ_ERR_HIP;
+    if (launch_decode(a, pt, static_cast<hipStream_t>(stream), ev0, ev1) != hipSuccess) return TQ_ERR_HIP;
     return TQ_OK;
 }
 

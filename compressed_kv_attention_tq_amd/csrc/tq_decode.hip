@@ -30,10 +30,10 @@ namespace tq {
 __global__ __launch_bounds__(1024) void tq_qrot_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63;
     const int r = threadIdx.x >> 6;                     // row within (seq, kv)
-    const int b = blockIdx.x / a.n_kv, kv = blockIdx.x % a.n_kv;
+    const int b = (int)fdiv(blockIdx.x, a.kv_div), kv = blockIdx.x - b * a.n_kv;
     float x0 = 0.f, x1 = 0.f;
     if (r < a.rows) {
-        const int jq = r / a.group, h = kv * a.group + r % a.group;
+        const int jq = (int)fdiv((uint32_t)r, a.grp_div), h = kv * a.group + (r - jq * a.group);
         const uint16_t *q = a.q + (((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * kD;
         const uint32_t *sg = a.k_signs + kv * 4;
         x0 = (float)__builtin_bit_cast(_Float16, q[lane]);
@@ -172,7 +172,7 @@ __device__ __forceinline__ void accum_token(uint32_t bits, const float (&wt)[RP]
 // Scores of the lane's token for all RP rows (log2 domain), -inf where masked.
 template <int KB, int RP>
 __device__ __forceinline__ void score_rows(const uint4 (&kw)[KB], float kn, bool active, int t, int last_vis,
-                                           int group, cfloat_p qr, const float *ktab, float (&s)[RP]) {
+                                           const FastDiv &gdiv, cfloat_p qr, const float *ktab, float (&s)[RP]) {
     uint32_t w[4 * KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
@@ -184,7 +184,7 @@ __device__ __forceinline__ void score_rows(const uint4 (&kw)[KB], float kn, bool
                                             std::make_integer_sequence<int, kD / score_group<RP>()>{});
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-        const bool vis = active && (t <= last_vis + r / group);
+        const bool vis = active && (t <= last_vis + (int)fdiv((uint32_t)r, gdiv));
         s[r] = vis ? s[r] * kn : -INFINITY;
     }
 }
@@ -221,9 +221,9 @@ void tq_decode_pass_kernel(DecodeArgs a,
     __shared__ float accbuf[(MODE == MODE_SCORE) ? 1 : RP * kD];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = blockIdx.x % a.n_chunks;
-    const int bk = blockIdx.x / a.n_chunks;
-    const int kv = bk % a.n_kv, b = bk / a.n_kv;
+    const int bk = (int)fdiv(blockIdx.x, a.chunk_div_n);
+    const int c = blockIdx.x - bk * a.n_chunks;
+    const int b = (int)fdiv((uint32_t)bk, a.kv_div), kv = bk - b * a.n_kv;
     const int len = seq_lens[b];
     const int start = c * a.chunk;
     if (start >= len) return;
@@ -237,7 +237,7 @@ void tq_decode_pass_kernel(DecodeArgs a,
         reinterpret_cast<uintptr_t>(qrot + ((int64_t)b * a.n_kv + kv) * kD * RP));
     const int32_t *__restrict__ btab = block_table + (int64_t)b * a.max_blocks;
     const int bs = a.block_size;
-    const FastDiv bsdiv = make_fastdiv((uint32_t)bs);
+    const FastDiv bsdiv = a.bs_div;
     const int last_vis = len - a.n_qtok;              // row r sees t <= last_vis + r / G
     const int64_t part = ((int64_t)b * a.n_kv + kv) * a.n_chunks + c;
     const int64_t tile0 = ((int64_t)b * a.n_kv + kv) * a.n_tiles;
@@ -289,7 +289,7 @@ void tq_decode_pass_kernel(DecodeArgs a,
             if (!cand) continue;
             cur.load(k_codes, k_norms, v_codes, v_norms, bsdiv, bs, a.n_kv, kv, t, end,
                      page_of(btab, bsdiv, t, end));
-            score_rows<KB, RP>(cur.k, cur.kn, cur.active, t, last_vis, a.group, qr, ktab, s);
+            score_rows<KB, RP>(cur.k, cur.kn, cur.active, t, last_vis, a.grp_div, qr, ktab, s);
             bool kept = false;
 #pragma unroll
             for (int r = 0; r < RP; ++r) {
@@ -319,7 +319,7 @@ void tq_decode_pass_kernel(DecodeArgs a,
             __builtin_amdgcn_wave_barrier();
         } else {
             // ---------------- K phase: one token per lane, rows loaded one slice ahead
-            score_rows<KB, RP>(cur.k, cur.kn, cur.active, t, last_vis, a.group, qr, ktab, s);
+            score_rows<KB, RP>(cur.k, cur.kn, cur.active, t, last_vis, a.grp_div, qr, ktab, s);
             const float vn = cur.vn;
             if constexpr (DENSE) {
 #pragma unroll
@@ -432,10 +432,10 @@ void tq_decode_pass_kernel(DecodeArgs a,
 // each wave reduces rows wave, wave+4, ... with its lanes striding the chunks.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void tq_stats_kernel(DecodeArgs a) {
-    const int b = blockIdx.x / a.n_kv, kv = blockIdx.x % a.n_kv;
+    const int b = (int)fdiv(blockIdx.x, a.kv_div), kv = blockIdx.x - b * a.n_kv;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int len = a.seq_lens[b];
-    const int nc = (len + a.chunk - 1) / a.chunk;
+    const int nc = (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div);
     const float *ml = a.part_ml + ((int64_t)b * a.n_kv + kv) * a.n_chunks * a.rows_pad * 2;
     for (int r = wave; r < a.rows_pad; r += 4) {
         float m = -INFINITY;
@@ -469,13 +469,14 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     __shared__ float y[kD];
     const int tid = threadIdx.x, lane = tid & 63;
     const int cg = tid >> 5, q4 = tid & 31;
-    const int h = blockIdx.x % a.n_q_heads;
-    const int jq = (blockIdx.x / a.n_q_heads) % a.n_qtok;
-    const int b = blockIdx.x / (a.n_q_heads * a.n_qtok);
-    const int kv = h / a.group;
-    const int r = jq * a.group + (h % a.group);
+    const int bj = (int)fdiv(blockIdx.x, a.qh_div);        // b * n_qtok + jq
+    const int h = blockIdx.x - bj * a.n_q_heads;
+    const int b = (int)fdiv((uint32_t)bj, a.qt_div);
+    const int jq = bj - b * a.n_qtok;
+    const int kv = (int)fdiv((uint32_t)h, a.grp_div);
+    const int r = jq * a.group + (h - kv * a.group);
     const int len = a.seq_lens[b];
-    const int nc = len > 0 ? (len + a.chunk - 1) / a.chunk : 0;
+    const int nc = len > 0 ? (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div) : 0;
     const int64_t base = ((int64_t)b * a.n_kv + kv) * a.n_chunks;
     const int64_t mstride = (int64_t)a.rows_pad * 2, astride = (int64_t)a.rows_pad * kD;
     const float *ml = a.part_ml + (base * a.rows_pad + r) * 2;          // chunk c at ml[c * mstride]
@@ -607,16 +608,19 @@ void TQ_CAT(launch_pass_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStre
 
 #else
 
-void launch_mfma_kb2(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
-void launch_mfma_kb3(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
-void launch_mfma_kb4(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+void launch_mfma_kb2(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
+                     hipEvent_t ev1);
+void launch_mfma_kb3(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
+                     hipEvent_t ev1);
+void launch_mfma_kb4(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
+                     hipEvent_t ev1);
 
-static void launch_mfma_any(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0 = nullptr,
-                            hipEvent_t ev1 = nullptr) {
+static void launch_mfma_any(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s,
+                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
     switch (a.k_bits) {
-        case 2: launch_mfma_kb2(a, mode, s, ev0, ev1); break;
-        case 3: launch_mfma_kb3(a, mode, s, ev0, ev1); break;
-        default: launch_mfma_kb4(a, mode, s, ev0, ev1); break;
+        case 2: launch_mfma_kb2(a, pt, mode, s, ev0, ev1); break;
+        case 3: launch_mfma_kb3(a, pt, mode, s, ev0, ev1); break;
+        default: launch_mfma_kb4(a, pt, mode, s, ev0, ev1); break;
     }
 }
 
@@ -629,15 +633,16 @@ static void launch_pass_any(const DecodeArgs &a, int mode, hipStream_t s, hipEve
     }
 }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
+hipError_t launch_decode(const DecodeArgs &a, const PairTables &pt, hipStream_t s, hipEvent_t ev_before,
+                         hipEvent_t ev_after) {
     const dim3 rows_grid((unsigned)((int64_t)a.n_seqs * a.n_qtok * a.n_q_heads));
     if (a.mfma) {   // q rotation runs inside the pass kernels
         if (a.tau > 0.f) {
-            launch_mfma_any(a, MODE_SCORE, s, ev_before, ev_after);
-            launch_mfma_any(a, MODE_GATED, s);
+            launch_mfma_any(a, pt, MODE_SCORE, s, ev_before, ev_after);
+            launch_mfma_any(a, pt, MODE_GATED, s);
             hipLaunchKernelGGL(tq_merge_kernel<true>, rows_grid, dim3(256), 0, s, a);
         } else {
-            launch_mfma_any(a, MODE_DENSE, s, ev_before, ev_after);
+            launch_mfma_any(a, pt, MODE_DENSE, s, ev_before, ev_after);
             hipLaunchKernelGGL(tq_merge_kernel<false>, rows_grid, dim3(256), 0, s, a);
         }
         return hipGetLastError();

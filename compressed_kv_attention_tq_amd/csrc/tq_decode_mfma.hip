@@ -65,11 +65,6 @@ __device__ __forceinline__ uint32_t split_pair(float w0, float w1, float lo_sel)
     return pk_rtz(__builtin_fmaf(-lo_sel, half_lo(h), w0), __builtin_fmaf(-lo_sel, half_hi(h), w1));
 }
 
-__host__ __device__ inline uint32_t half2_bits(float lo, float hi) {
-    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
 // Reductions over the four lane groups g (lanes n, n+16, n+32, n+48 hold one
 // column): swap rows of 16 lanes, then halves of the wave.
 __device__ __forceinline__ float xg_max(float x) {
@@ -195,22 +190,22 @@ __device__ __forceinline__ u4_t v_frag(const uint32_t (&x)[4], const uint32_t (&
 // PK: at most 8 rows (hi / lo parts packed in one MFMA's columns).
 // CONTIG: block_size is a multiple of 64, so a slice lies in one page.
 // --------------------------------------------------------------------------
-// Waves per SIMD the register allocation aims for (without spilling): the
-// packed-column variants fit three, the 9-16 row ones two.
+// Waves per SIMD the register allocation aims for (without spilling): the dense
+// pass holds two slices' loads and fits two; the scoring and gated passes with
+// at most 8 rows fit three.
 template <bool PK, int VB, int MODE>
-constexpr int mfma_waves_per_eu() { return PK ? 3 : 2; }
+constexpr int mfma_waves_per_eu() { return (PK && MODE != MODE_DENSE) ? 3 : 2; }
 
 template <int KB, int VB, bool PK, int MODE, bool CONTIG>
 __global__ __launch_bounds__(kMBlock) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<PK, VB, MODE>(), 8)))
 void tq_decode_mfma_kernel(
-    DecodeArgs a, const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
+    DecodeArgs a, PairTables pt, const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
     const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms, const uint16_t *__restrict__ qin,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens, float *__restrict__ part_ml,
     float *__restrict__ part_acc, float *__restrict__ tilemax) {
     constexpr bool DENSE = MODE == MODE_DENSE, SCORE = MODE == MODE_SCORE, GATED = MODE == MODE_GATED;
     constexpr bool WV = !SCORE;
     constexpr int NKT = 1 << (2 * KB), NVT = 1 << (2 * VB);
-    constexpr int LK = 1 << KB, LV = 1 << VB;
     constexpr int KROW = 16 * KB, VROW = 16 * VB;   // bytes per code row
     constexpr int NQB = PK ? 4 : 8;                 // q'' B fragments
     constexpr int NPB = PK ? 2 : 4;                 // weight B fragments
@@ -234,28 +229,72 @@ void tq_decode_mfma_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c = blockIdx.x % a.n_chunks;
-    const int unit = blockIdx.x / a.n_chunks;
-    const int kv = unit % a.n_kv, b = unit / a.n_kv;
+    const int unit = (int)fdiv(blockIdx.x, a.chunk_div_n);
+    const int c = blockIdx.x - unit * a.n_chunks;
+    const int b = (int)fdiv((uint32_t)unit, a.kv_div);
+    const int kv = unit - b * a.n_kv;
     const int R = a.rows, rp = a.rows_pad;
     const int start = c * a.chunk;
     const int bs = a.block_size, n_kv = a.n_kv;
-    const FastDiv bsdiv = make_fastdiv((uint32_t)bs);
+    const FastDiv bsdiv = a.bs_div;
     const int32_t *__restrict__ btab = block_table + (int64_t)b * a.max_blocks;
     constexpr int kStride = kMW * 64;
     const int first = start + wave * 64;
-    // page-table entries of the wave's first two slices are read together with the
-    // sequence length (indices clamped to the table; an entry is used only for
-    // positions below the length, where it is valid)
-    int blk0 = 0, blk1 = 0;
-    if constexpr (CONTIG && !GATED) {
-        const int last_page = a.max_blocks - 1;
-        blk0 = btab[min((int)fdiv((uint32_t)first, bsdiv), last_page)];
-        blk1 = btab[min((int)fdiv((uint32_t)(first + kStride), bsdiv), last_page)];
+
+    // Small loads go out first.  Vector loads complete in issue order, so loads
+    // issued after the slice codes could only be used once those had arrived:
+    // the pair-table entries this thread replicates, this wave's query rows and
+    // the K sign bits.
+    constexpr int KIT = (NKT * 4 + kMBlock - 1) / kMBlock, VIT = (NVT * 4 + kMBlock - 1) / kMBlock;
+    uint32_t kent[KIT], vent[WV ? VIT : 1];
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+        const int i = it * kMBlock + tid;
+        kent[it] = i < NKT * 4 ? pt.k[i >> 2] : 0u;
     }
-    const int len = seq_lens[b];
-    if (start >= len) return;
-    const int end = min(start + a.chunk, len);
+    if constexpr (WV) {
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int i = it * kMBlock + tid;
+            vent[it] = i < NVT * 4 ? pt.v[i >> 2] : 0u;
+        }
+    }
+    // (unconditional, from a row clamped into range: a load under a branch has its
+    // conversion folded into the branch, which then waits for the load)
+    constexpr int kRowsPerWave = 16 / kMW;
+    uint32_t qh0[kRowsPerWave], qh1[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+        const int r = min(wave + kMW * i, a.rows - 1);
+        const int jq = (int)fdiv((uint32_t)r, a.grp_div), h = kv * a.group + (r - jq * a.group);
+        const uint16_t *qp = qin + (((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * kD;
+        qh0[i] = qp[lane];
+        qh1[i] = qp[lane + 64];
+    }
+    const uint32_t ksg0 = a.k_signs[kv * 4 + (lane >> 5)], ksg1 = a.k_signs[kv * 4 + 2 + (lane >> 5)];
+    // the sequence length, through the vector path as well: a scalar load would
+    // either hold up the loads above (scalar loads are waited for together) or,
+    // issued later, queue behind the slice loads
+    int len_v;
+    {
+        int bi = b;
+        asm volatile("" : "+v"(bi));
+        len_v = seq_lens[bi];
+    }
+
+    // Page-table entries of the wave's first two slices (CONTIG: the slice's page;
+    // else the page of the lane's token), through the vector path too.  Indices
+    // are clamped to the table; entries past the sequence are never used.
+    const int last_entry = a.max_blocks - 1;
+    int vb0 = 0, vb1 = 0;
+    if constexpr (!GATED) {
+        int i0 = min((int)fdiv((uint32_t)(first + (CONTIG ? 0 : lane)), bsdiv), last_entry);
+        int i1 = min((int)fdiv((uint32_t)(first + kStride + (CONTIG ? 0 : lane)), bsdiv), last_entry);
+        asm volatile("" : "+v"(i0), "+v"(i1));
+        vb0 = btab[i0];
+        vb1 = btab[i1];
+    }
+    int len = 0, end = 0;
     const int64_t part = (int64_t)unit * a.n_chunks + c;
     const int64_t tile0 = (int64_t)unit * a.n_tiles;
 
@@ -266,18 +305,23 @@ void tq_decode_mfma_kernel(
         vo = (24 * n) & 31;
     }
 
-    // ---- slice state: code words per lane, one K and one V norm per lane (token = lane)
-    uint32_t kw[4][KB];
-    VUnit<VB> vw[2][8];
-    float knl = 0.f, vnl = 0.f;
+    // ---- one slice's loads: code words per lane, one K and one V norm per lane
+    // (token = lane).  The dense and scoring passes keep two slots, so the next
+    // slice's loads are in flight while a slice is computed.
+    struct Slot {
+        uint32_t kw[4][KB];
+        VUnit<VB> vw[2][8];
+        float knl, vnl;
+    };
+    Slot sa, sb;
     int myrow = 0;   // row of token base + lane (general page layout)
 
-    auto row0_of = [&](int base, int blk) -> int64_t {
+    auto row0_of = [&](int base, int blk) __attribute__((always_inline)) -> int64_t {
         const int pg = (int)fdiv((uint32_t)base, bsdiv);
         return ((int64_t)blk * n_kv + kv) * bs + (base - pg * bs);
     };
     // general layout: the row of every token of the slice into the wave's table
-    auto fill_rows = [&](int base, int blk_lane) {
+    auto fill_rows = [&](int base, int blk_lane) __attribute__((always_inline)) {
         const int t = base + lane;
         myrow = 0;
         if (t < end) {
@@ -288,34 +332,34 @@ void tq_decode_mfma_kernel(
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's row table is written
         __builtin_amdgcn_wave_barrier();
     };
-    auto load_k = [&](int64_t row0) {
+    auto load_k = [&](Slot &sl, int64_t row0) __attribute__((always_inline)) {
         if constexpr (CONTIG) {
             const uint8_t *p = k_codes + (row0 + n) * KROW + g * (4 * KB);
 #pragma unroll
-            for (int tm = 0; tm < 4; ++tm) load_words<KB>(p + tm * 16 * KROW, kw[tm]);
-            knl = k_norms[row0 + lane];
+            for (int tm = 0; tm < 4; ++tm) load_words<KB>(p + tm * 16 * KROW, sl.kw[tm]);
+            sl.knl = k_norms[row0 + lane];
         } else {
             const int32_t *rt = rowtab[wave];
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
-                load_words<KB>(k_codes + (int64_t)rt[16 * tm + n] * KROW + g * (4 * KB), kw[tm]);
-            knl = k_norms[myrow];
+                load_words<KB>(k_codes + (int64_t)rt[16 * tm + n] * KROW + g * (4 * KB), sl.kw[tm]);
+            sl.knl = k_norms[myrow];
         }
     };
     // V units of the slice's tokens; token (tile tm, e) of lane group g is loaded
     // only where keep(tm, e) holds (every token for the dense pass)
-    auto load_v = [&](int64_t row0, auto keep) {
+    auto load_v = [&](Slot &sl, int64_t row0, auto keep) __attribute__((always_inline)) {
         if constexpr (CONTIG) {
             const uint8_t *p = v_codes + (row0 + 4 * g) * VROW;
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    VUnit<VB> &u = vw[tm >> 1][4 * (tm & 1) + e];
+                    VUnit<VB> &u = sl.vw[tm >> 1][4 * (tm & 1) + e];
                     if (keep(tm, e)) load_vunit<VB>(p + (16 * tm + e) * VROW, vwi, u);
                     else u = VUnit<VB>{};
                 }
-            vnl = v_norms[row0 + lane];
+            sl.vnl = v_norms[row0 + lane];
         } else {
             const int32_t *rt = rowtab[wave];
 #pragma unroll
@@ -323,62 +367,81 @@ void tq_decode_mfma_kernel(
                 const i4_t rr = *reinterpret_cast<const i4_t *>(rt + 16 * tm + 4 * g);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    VUnit<VB> &u = vw[tm >> 1][4 * (tm & 1) + e];
+                    VUnit<VB> &u = sl.vw[tm >> 1][4 * (tm & 1) + e];
                     if (keep(tm, e)) load_vunit<VB>(v_codes + (int64_t)rr[e] * VROW, vwi, u);
                     else u = VUnit<VB>{};
                 }
             }
-            vnl = v_norms[myrow];
+            sl.vnl = v_norms[myrow];
         }
     };
     auto all_tokens = [](int, int) { return true; };
 
-    // ---- the first slice's loads go out before the set-up below
+    len = __builtin_amdgcn_readfirstlane(len_v);
+    if (start >= len) {
+        // the small loads are consumed on this path too, so they stay ahead of
+        // the length test instead of being moved below it
+        uint32_t x = ksg0 ^ ksg1 ^ (uint32_t)len_v ^ (uint32_t)vb0 ^ (uint32_t)vb1;
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) x ^= qh0[i] ^ qh1[i];
+#pragma unroll
+        for (int it = 0; it < KIT; ++it) x ^= kent[it];
+        if constexpr (WV) {
+#pragma unroll
+            for (int it = 0; it < VIT; ++it) x ^= vent[it];
+        }
+        asm volatile("" ::"v"(x));
+        return;
+    }
+    end = min(start + a.chunk, len);
+
+    // ---- the first slice's loads (r0_prev: its first row; blk_next: page of the
+    // second slice)
+    int64_t r0_prev = 0;
     int blk_next = 0;
-    int64_t r0n = 0;
     if constexpr (!GATED) {
-        if (first < end) {
-            if constexpr (CONTIG) {
-                r0n = row0_of(first, blk0);
-                blk_next = blk1;
-            } else {
-                fill_rows(first, page_of(btab, bsdiv, first + lane, end));
-                blk_next = page_of(btab, bsdiv, first + kStride + lane, end);
-            }
-            load_k(r0n);
-            if constexpr (DENSE) load_v(r0n, all_tokens);
+        if constexpr (CONTIG) {
+            const int blk0 = __builtin_amdgcn_readfirstlane(vb0);
+            const int pg = (int)fdiv((uint32_t)first, bsdiv);
+            r0_prev = ((int64_t)min(max(blk0, 0), a.max_page) * n_kv + kv) * bs + (first - pg * bs);
+            load_k(sa, r0_prev);
+            if constexpr (DENSE) load_v(sa, r0_prev, all_tokens);
+            blk_next = vb1;
+        } else {
+            fill_rows(first, first + lane < end ? vb0 : 0);
+            load_k(sa, 0);
+            if constexpr (DENSE) load_v(sa, 0, all_tokens);
+            blk_next = first + kStride + lane < end ? vb1 : 0;
         }
     }
 
-    // pair tables: an entry is formed once and stored to all its copies
-    auto fill_table = [&](uint32_t *tab, const float *cb, int bits, int n_entries, int copies) {
-        const int lmask = (1 << bits) - 1;
-        for (int i = tid; i < n_entries * 4; i += kMBlock) {   // 4 threads per entry, 8 copies each
-            const int e = i >> 2;
-            const uint32_t v = half2_bits(cb[e & lmask], cb[e >> bits]);
-            u4_t *d = reinterpret_cast<u4_t *>(tab + e * copies + (i & 3) * 8);
-            d[0] = u4_t{v, v, v, v};
-            d[1] = u4_t{v, v, v, v};
-        }
+    // replicate the pair tables: 4 threads per entry (i = 4 e + quarter), 8 copies each
+    auto fill_entry = [&](uint32_t *tab, uint32_t v, int i, int copies) __attribute__((always_inline)) {
+        u4_t *d = reinterpret_cast<u4_t *>(tab + (i >> 2) * copies + (i & 3) * 8);
+        d[0] = u4_t{v, v, v, v};
+        d[1] = u4_t{v, v, v, v};
     };
-    fill_table(ktab, a.kc, KB, NKT, KCOP);
-    if constexpr (WV) fill_table(vtab, a.vc, VB, NVT, VCOP);
+#pragma unroll
+    for (int it = 0; it < KIT; ++it)
+        if (it * kMBlock + tid < NKT * 4) fill_entry(ktab, kent[it], it * kMBlock + tid, KCOP);
+    if constexpr (WV) {
+#pragma unroll
+        for (int it = 0; it < VIT; ++it)
+            if (it * kMBlock + tid < NVT * 4) fill_entry(vtab, vent[it], it * kMBlock + tid, VCOP);
+    }
     const uint32_t lane_off = (uint32_t)(lane & 31) << 2;
 
     // ---- q'' = qscale * H (s_K * q) of this KV head's rows, into buf
     {
         float qm = 0.f;
-        for (int r = wave; r < R; r += kMW) {
-            float x0, x1;
-            {
-                const int jq = r / a.group, h = kv * a.group + r % a.group;
-                const uint16_t *qp = qin + (((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * kD;
-                const uint32_t *sg = a.k_signs + kv * 4;
-                x0 = (float)__builtin_bit_cast(_Float16, qp[lane]);
-                x1 = (float)__builtin_bit_cast(_Float16, qp[lane + 64]);
-                if ((sg[lane >> 5] >> (lane & 31)) & 1u) x0 = -x0;
-                if ((sg[2 + (lane >> 5)] >> (lane & 31)) & 1u) x1 = -x1;
-            }
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            const int r = wave + kMW * i;
+            if (r >= R) break;
+            float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)qh0[i]);
+            float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)qh1[i]);
+            if ((ksg0 >> (lane & 31)) & 1u) x0 = -x0;
+            if ((ksg1 >> (lane & 31)) & 1u) x1 = -x1;
             hadamard128(x0, x1, lane);
             x0 *= a.qscale;
             x1 *= a.qscale;
@@ -391,7 +454,7 @@ void tq_decode_mfma_kernel(
     }
     // sparse: global (max, sum) of each row from the scoring pass's chunk partials
     if constexpr (GATED) {
-        const int nc = (len + a.chunk - 1) / a.chunk;
+        const int nc = (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div);
         const float *ml = part_ml + (int64_t)unit * a.n_chunks * rp * 2;
         for (int r = wave; r < R; r += kMW) {
             float m = -INFINITY;
@@ -434,7 +497,7 @@ void tq_decode_mfma_kernel(
 
     const bool row_ok = col_row < R;
     // last position each row sees in this chunk (row r sees t <= len - n_qtok + r / G)
-    const int lim = row_ok ? min(end - 1, len - a.n_qtok + col_row / a.group) : -1;
+    const int lim = row_ok ? min(end - 1, len - a.n_qtok + (int)fdiv((uint32_t)col_row, a.grp_div)) : -1;
     const int lim_all = min(end - 1, len - a.n_qtok);   // seen by every row
 
     // sparse: keep iff s >= sthr (p >= tau); weights 2^(s - mlog) = p
@@ -449,14 +512,47 @@ void tq_decode_mfma_kernel(
         }
     }
 
+    // ---- the second slice's loads, once the set-up above is done: the first
+    // slice's went out before it, both would fill the memory pipeline and hold
+    // the set-up up.  Every issue loads, whether or not its slice lies below the end: one past the
+    // end re-reads the rows of the last slice issued (cached, and never used), so
+    // the loads of both slots are the same instructions on every path and each
+    // wait covers only the slot it needs, never the one in flight behind it.
+    // blk_next: page of the next slice (CONTIG, the same in every lane), or of the
+    // lane's token of it; page-table reads are clamped to the table.
+    auto page_clamped = [&](int t) __attribute__((always_inline)) -> int {
+        const int pg = btab[min((int)fdiv((uint32_t)t, bsdiv), last_entry)];
+        return t < end ? pg : 0;
+    };
+    auto issue = [&](Slot &sl, int base) __attribute__((always_inline)) {
+        int64_t r0 = 0;
+        if constexpr (CONTIG) {
+            r0 = base < end ? row0_of(base, __builtin_amdgcn_readfirstlane(blk_next)) : r0_prev;
+            r0_prev = r0;
+            int i = min((int)fdiv((uint32_t)(base + kStride), bsdiv), last_entry);
+            asm volatile("" : "+v"(i));
+            blk_next = btab[i];
+        } else {
+            fill_rows(base, blk_next);
+            blk_next = page_clamped(base + kStride + lane);
+        }
+        load_k(sl, r0);
+        if constexpr (DENSE) load_v(sl, r0, all_tokens);
+    };
+    if constexpr (!GATED) {
+        // slot b's loads strictly after slot a's, so waiting for a never waits for b
+        __builtin_amdgcn_sched_barrier(0);
+        issue(sb, first + kStride);
+    }
+
     // ---- score MFMAs of the loaded slice
-    auto score_mfma = [&](f4_t (&S)[4]) {
+    auto score_mfma = [&](const Slot &sl, f4_t (&S)[4]) {
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) {
             S[tm] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const u4_t af = k_frag<KB>(kw[tm], ks, ktab, lane_off);
+                const u4_t af = k_frag<KB>(sl.kw[tm], ks, ktab, lane_off);
                 S[tm] = mfma_f16(af, qb[ks], S[tm]);
                 if constexpr (!PK) S[tm] = mfma_f16(af, qb[4 + ks], S[tm]);
             }
@@ -466,11 +562,11 @@ void tq_decode_mfma_kernel(
     // not data and become 0); returns the V exponent E: max V norm < 2^E, so the
     // weights e * vn * 2^-E stay below 1
     float *my_kn = nrm[wave][0], *my_vn = nrm[wave][1];
-    auto stage_norms = [&](int base) -> float {
-        my_kn[lane] = knl * kscale;
+    auto stage_norms = [&](const Slot &sl, int base) __attribute__((always_inline)) -> float {
+        my_kn[lane] = sl.knl * kscale;
         float v = 0.f;
         if constexpr (WV) {
-            v = base + lane < end ? vnl : 0.f;
+            v = base + lane < end ? sl.vnl : 0.f;
             my_vn[lane] = v;
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -506,7 +602,7 @@ void tq_decode_mfma_kernel(
     f4_t acc[WV ? 8 : 1];
 #pragma unroll
     for (int j = 0; j < (WV ? 8 : 1); ++j) acc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
-    auto value_mfma = [&](const float (&w)[4][4]) {
+    auto value_mfma = [&](const Slot &sl, const float (&w)[4][4]) {
         u4_t pb[NPB];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -524,7 +620,7 @@ void tq_decode_mfma_kernel(
         for (int ks = 0; ks < 2; ++ks) {
             uint32_t u[8], x[4], y[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) u[e] = vunit_bits<VB>(vw[ks][e], vo);
+            for (int e = 0; e < 8; ++e) u[e] = vunit_bits<VB>(sl.vw[ks][e], vo);
             v_pairs<VB>(u, x, y);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -538,23 +634,12 @@ void tq_decode_mfma_kernel(
     float m_raw = -INFINITY, m_state = -INFINITY, l_run = 0.f, E_run = -INFINITY;
 
     if constexpr (!GATED) {
-        // ---------------- dense / scoring pass: loads run one slice ahead
-        for (int base = first; base < end; base += kStride) {
-            const int nb = base + kStride;
-            const bool has_next = nb < end;
-            const float E_s = stage_norms(base);
+        // ---------------- dense / scoring pass: a two-slot ring, the next slice's
+        // loads in flight while a slice is computed
+        auto compute = [&](const Slot &sl, int base) __attribute__((always_inline)) {
+            const float E_s = stage_norms(sl, base);
             f4_t S[4];
-            score_mfma(S);
-            if (has_next) {   // next slice's K while this one is scored
-                if constexpr (CONTIG) {
-                    r0n = row0_of(nb, blk_next);
-                    blk_next = nb + kStride < end ? btab[fdiv((uint32_t)(nb + kStride), bsdiv)] : 0;
-                } else {
-                    fill_rows(nb, blk_next);
-                    blk_next = page_of(btab, bsdiv, nb + kStride + lane, end);
-                }
-                load_k(r0n);
-            }
+            score_mfma(sl, S);
             const bool full = base + 63 <= lim_all;
             float s[4][4];
             scores(S, base, full, s);
@@ -592,9 +677,21 @@ void tq_decode_mfma_kernel(
 #pragma unroll
                     for (int j = 0; j < 8; ++j) acc[j] *= alpha;
                 }
-                value_mfma(w);
-                if (has_next) load_v(r0n, all_tokens);
+                value_mfma(sl, w);
             }
+        };
+        // one exit, at the top: a branch inside the loop would merge paths with
+        // different loads outstanding, and every wait after it would then cover both
+        // slots; skipping a compute (which issues no loads) does not
+        // (the scheduling barriers keep each compute below the loads issued
+        // before it in the source, which it must not wait for)
+        for (int base = first; base < end; base += 2 * kStride) {
+            __builtin_amdgcn_sched_barrier(0);
+            compute(sa, base);   // slot b holds base + kStride (in flight)
+            issue(sa, base + 2 * kStride);
+            __builtin_amdgcn_sched_barrier(0);
+            if (base + kStride < end) compute(sb, base + kStride);
+            issue(sb, base + 3 * kStride);
         }
     } else {
         // ---------------- gated pass: candidate slices only
@@ -604,12 +701,12 @@ void tq_decode_mfma_kernel(
             int64_t r0 = 0;
             if constexpr (CONTIG) r0 = row0_of(base, btab[fdiv((uint32_t)base, bsdiv)]);
             else fill_rows(base, page_of(btab, bsdiv, base + lane, end));
-            load_k(r0);
-            if constexpr (CONTIG) vnl = v_norms[r0 + lane];
-            else vnl = v_norms[myrow];
-            const float E_s = stage_norms(base);
+            load_k(sa, r0);
+            if constexpr (CONTIG) sa.vnl = v_norms[r0 + lane];
+            else sa.vnl = v_norms[myrow];
+            const float E_s = stage_norms(sa, base);
             f4_t S[4];
-            score_mfma(S);
+            score_mfma(sa, S);
             const bool full = base + 63 <= lim_all;
             float s[4][4];
             scores(S, base, full, s);
@@ -625,7 +722,7 @@ void tq_decode_mfma_kernel(
                     kept[tm][e] = ((bal >> (16 * g)) & 0xFFFFull) != 0ull;
                 }
             if (!any) continue;
-            load_v(r0, [&](int tm, int e) { return kept[tm][e]; });
+            load_v(sa, r0, [&](int tm, int e) { return kept[tm][e]; });
             const float E_new = fmaxf(E_run, E_s);
             if (E_run != -INFINITY && E_new != E_run) {
                 const float f = __builtin_amdgcn_exp2f(E_run - E_new);
@@ -642,7 +739,7 @@ void tq_decode_mfma_kernel(
                 for (int e = 0; e < 4; ++e)
                     w[tm][e] = s[tm][e] >= sthr ? __builtin_amdgcn_exp2f(s[tm][e] - mu) * vn[e] : 0.f;
             }
-            value_mfma(w);
+            value_mfma(sa, w);
         }
     }
 
@@ -716,9 +813,10 @@ void tq_decode_mfma_kernel(
 // ev0 / ev1 (may be null): recorded at the start and the end of the kernel's
 // execution (hipExtLaunchKernelGGL), for timing.
 template <int KB, int VB, bool PK, bool CONTIG>
-static void launch_mfma_mode(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+static void launch_mfma_mode(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
+                             hipEvent_t ev1) {
     const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_kv * a.n_chunks)), block(kMBlock);
-#define TQ_MFMA_ARGS a, a.k_codes, a.k_norms, a.v_codes, a.v_norms, a.q, a.block_table, a.seq_lens, a.part_ml, \
+#define TQ_MFMA_ARGS a, pt, a.k_codes, a.k_norms, a.v_codes, a.v_norms, a.q, a.block_table, a.seq_lens, a.part_ml, \
         a.part_acc, a.tilemax
     if (mode == MODE_DENSE)
         hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG>), grid, block, 0, s, ev0, ev1, 0,
@@ -733,25 +831,26 @@ static void launch_mfma_mode(const DecodeArgs &a, int mode, hipStream_t s, hipEv
 }
 
 template <int KB, int VB>
-static void launch_mfma_vb(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+static void launch_mfma_vb(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
+                           hipEvent_t ev1) {
     const bool pk = a.rows <= 8;
     if (a.contig) {
-        if (pk) launch_mfma_mode<KB, VB, true, true>(a, mode, s, ev0, ev1);
-        else launch_mfma_mode<KB, VB, false, true>(a, mode, s, ev0, ev1);
+        if (pk) launch_mfma_mode<KB, VB, true, true>(a, pt, mode, s, ev0, ev1);
+        else launch_mfma_mode<KB, VB, false, true>(a, pt, mode, s, ev0, ev1);
     } else {
-        if (pk) launch_mfma_mode<KB, VB, true, false>(a, mode, s, ev0, ev1);
-        else launch_mfma_mode<KB, VB, false, false>(a, mode, s, ev0, ev1);
+        if (pk) launch_mfma_mode<KB, VB, true, false>(a, pt, mode, s, ev0, ev1);
+        else launch_mfma_mode<KB, VB, false, false>(a, pt, mode, s, ev0, ev1);
     }
 }
 
 #define TQ_CAT2(a, b) a##b
 #define TQ_CAT(a, b) TQ_CAT2(a, b)
-void TQ_CAT(launch_mfma_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0,
-                                          hipEvent_t ev1) {
+void TQ_CAT(launch_mfma_kb, TQ_DECODE_KB)(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s,
+                                          hipEvent_t ev0, hipEvent_t ev1) {
     switch (a.v_bits) {
-        case 2: launch_mfma_vb<TQ_DECODE_KB, 2>(a, mode, s, ev0, ev1); break;
-        case 3: launch_mfma_vb<TQ_DECODE_KB, 3>(a, mode, s, ev0, ev1); break;
-        default: launch_mfma_vb<TQ_DECODE_KB, 4>(a, mode, s, ev0, ev1); break;
+        case 2: launch_mfma_vb<TQ_DECODE_KB, 2>(a, pt, mode, s, ev0, ev1); break;
+        case 3: launch_mfma_vb<TQ_DECODE_KB, 3>(a, pt, mode, s, ev0, ev1); break;
+        default: launch_mfma_vb<TQ_DECODE_KB, 4>(a, pt, mode, s, ev0, ev1); break;
     }
 }
 

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tq_internal.h"
+
 namespace tq {
 
 // DPP control words (gfx9 encoding).
@@ -112,30 +114,6 @@ __device__ __forceinline__ void half_pair_butterfly(uint32_t w, float &sum, floa
         "v_fma_mix_f32 %1, %2, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
         : "=&v"(sum), "=v"(diff)
         : "v"(w));
-}
-
-// Division by a runtime divisor d <= 2^31 for dividends n < 2^31:
-// q = umulhi(n, m) >> s with m = ceil(2^(31+l) / d), s = l - 1, 2^(l-1) < d <= 2^l
-// (the error term n*e / (d 2^(31+l)) stays below 1/d, so the floor is exact).
-struct FastDiv {
-    uint32_t d, m, s;
-};
-__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
-    FastDiv f;
-    f.d = d;
-    if (d <= 1) {
-        f.m = 0;
-        f.s = 0;
-        return f;
-    }
-    uint32_t l = 0;
-    while ((1ull << l) < d) ++l;
-    f.m = (uint32_t)(((1ull << (31 + l)) + d - 1) / d);
-    f.s = l - 1;
-    return f;
-}
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
-    return f.d <= 1 ? n : (__umulhi(n, f.m) >> f.s);
 }
 
 __device__ __forceinline__ float lane_sign(int j) { return (__popc(j) & 1) ? -1.f : 1.f; }

@@ -11,6 +11,33 @@
 
 namespace tq {
 
+// n / d for 32-bit n by one multiply-high and shift: m = ceil(2^(31 + l) / d),
+// l = ceil(log2 d), q = umulhi(n, m) >> (l - 1).  Exact for n, d < 2^31: the
+// rounding of m adds less than 1/d to n / d.  d = 1 uses m = 0, s = 0 and adds n
+// back (one = all ones), so the device code has no branch.  The magic numbers
+// are formed on the host and travel in the kernel arguments.
+struct FastDiv {
+    uint32_t m, s, one;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    if (d <= 1) {
+        f.m = 0;
+        f.s = 0;
+        f.one = 0xFFFFFFFFu;
+        return f;
+    }
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    f.m = (uint32_t)(((1ull << (31 + l)) + d - 1) / d);
+    f.s = l - 1;
+    f.one = 0;
+    return f;
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+    return (__umulhi(n, f.m) + (n & f.one)) >> f.s;
+}
+
 constexpr int kD = 128;            // elements per block
 constexpr int kWaves = 8;          // decode: waves per pass block
 constexpr int kBlock = 64 * kWaves;// decode: threads per pass block
@@ -32,6 +59,8 @@ struct QuantSide {
     int32_t n_kv;
     int32_t block_size;
     int32_t bits;
+    FastDiv bs_div;           // division by block_size
+    FastDiv kv_div;           // division by n_kv
     int32_t lut_half;         // table index = floor(t) + lut_half
     float grid;               // t = y * grid (cells of width 1/grid in y)
     int32_t n_bnd;            // 2^bits - 1
@@ -54,6 +83,7 @@ struct DequantArgs {
     int32_t n_kv;
     int32_t block_size;
     int32_t dst_fp16;
+    FastDiv kv_div, bs_div;   // division by n_kv, block_size
     float cent[TQ_MAX_LEVELS];
 };
 
@@ -77,10 +107,13 @@ struct DecodeArgs {
     float *stats;             // [S][n_kv][RP][2]  global (max, sum) (sparse only)
     int32_t n_seqs, n_qtok, n_q_heads, n_kv, group, rows, rows_pad;
     int32_t max_blocks, block_size;
+    int32_t max_page;         // largest physical page of the smaller cache (n_blocks - 1)
     int32_t chunk;            // tokens per chunk (multiple of kChunkUnit)
     int32_t n_chunks;         // chunks per sequence capacity
     int32_t n_tiles;          // tiles per sequence capacity
     float qscale;             // softmax_scale * log2(e) / sqrt(128)
+    FastDiv bs_div, chunk_div, chunk_div_n, kv_div, grp_div, qh_div, qt_div;
+                              // by block_size, chunk, n_chunks, n_kv, group, n_q_heads, n_qtok
     float tau;
     int32_t k_bits, v_bits;
     int32_t mfma;             // 1: matrix-core pass kernels, 0: vector-ALU kernels
@@ -89,10 +122,23 @@ struct DecodeArgs {
     float vc[TQ_MAX_LEVELS];
 };
 
+// Centroid-pair tables of the matrix-core decode pass, formed on the host:
+// entry e = (c[e mod 2^b] | c[e div 2^b] << 16) as fp16 bits (codes of two
+// consecutive positions, or of two tokens at one position).
+struct PairTables {
+    uint32_t k[1 << (2 * 4)];
+    uint32_t v[1 << (2 * 4)];
+};
+
+__host__ __device__ inline uint32_t half2_bits(float lo, float hi) {
+    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_quantize(const QuantArgs &a, int blocks_total, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, int bits, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_before = nullptr,
+hipError_t launch_decode(const DecodeArgs &a, const PairTables &pt, hipStream_t s, hipEvent_t ev_before = nullptr,
                          hipEvent_t ev_after = nullptr);
 
 }  // namespace tq

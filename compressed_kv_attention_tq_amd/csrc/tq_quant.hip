@@ -53,9 +53,10 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
     // lane's block never changes and the token advances by a constant.
     const int step = nblk * wpb * 8;
     const int v0 = wave_id * 8 + L.vin;
-    const int head = v0 % p.n_kv;
-    const int tok_step = step / p.n_kv;
-    const FastDiv bsdiv = make_fastdiv((uint32_t)p.block_size);
+    const int tok0 = (int)fdiv((uint32_t)v0, p.kv_div);
+    const int head = v0 - tok0 * p.n_kv;
+    const int tok_step = (int)fdiv((uint32_t)step, p.kv_div);
+    const FastDiv bsdiv = p.bs_div;
 
     // Sign flips of this lane's 16 elements as float16 sign-bit masks.
     const uint32_t sb = (p.signs[head * 4 + (j >> 1)] >> ((j & 1) * 16)) & 0xFFFFu;
@@ -68,7 +69,7 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
     const uint16_t *src = p.src + (int64_t)head * kD + j * 16;
     const LutEntry *lut0 = lut + p.lut_half;
 
-    int tok = v0 / p.n_kv;
+    int tok = tok0;
     for (int g0 = wave_id * 8; g0 < p.n_vec; g0 += step, tok += tok_step) {   // uniform per wave
         const bool valid = g0 + L.vin < p.n_vec;
         uint32_t w[8];
@@ -181,8 +182,8 @@ __global__ __launch_bounds__(256) void tq_dequantize_kernel(DequantArgs a) {
     const int wave_id = blockIdx.x * wpb + (int)(threadIdx.x >> 6);
     const int step = gridDim.x * wpb * 8;
     const float lsign = lane_sign(j) * 0.088388347648318440550f;
-    const FastDiv kvdiv = make_fastdiv((uint32_t)a.n_kv);
-    const FastDiv bsdiv = make_fastdiv((uint32_t)a.block_size);
+    const FastDiv kvdiv = a.kv_div;
+    const FastDiv bsdiv = a.bs_div;
     for (int g0 = wave_id * 8; g0 < a.n_vec; g0 += step) {
         const int vid = g0 + L.vin;
         const bool valid = vid < a.n_vec;
