@@ -98,18 +98,34 @@ __device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[NW]) 
 
 // A operand of the score MFMA for k-step ks from the lane's 32 positions of one
 // token (positions 32g + 8ks .. +7): 4 lookups of a code pair -> fp16 pair.
-// Centroid-pair tables are replicated 32 times, entry-major: copy c of entry e
-// is dword 32 e + c, and lane l reads copy l % 32, so the lanes of a half-wave
-// never meet in an LDS bank whatever their indices.
+// Centroid-pair tables are replicated 32 times, entry-major, and lane l reads
+// copy l % 32, so the lanes of a half-wave never meet in an LDS bank whatever
+// their indices.  Row e of the table area is RB bytes: copies 0..31 of K entry e,
+// then (RB = 256, when the pass has V tables) copies 0..31 of V entry e.  With
+// 256-byte rows, a pair index that fills a byte of a code word becomes its
+// address in one byte permute: (index << 8) | lane_off.
 template <int B>
 constexpr int tab_copies() { return 32; }
 
-template <int B>
-__device__ __forceinline__ uint32_t tab_read(const uint32_t *tab, uint32_t idx, uint32_t lane_off) {
-    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(tab) + ((idx << 7) | lane_off));
+// dword at byte offset `off` of the table area
+__device__ __forceinline__ uint32_t tab_at(const uint32_t *tab, uint32_t off) {
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(tab) + off);
 }
 
-template <int KB>
+// table offset of a pair index: the FB-bit field at bit `sh` of u (its byte k
+// when FB = 8, RB = 256 and sh = 8 k)
+template <int FB, int RB>
+__device__ __forceinline__ uint32_t tab_off(uint32_t u, int sh, uint32_t lane_off) {
+    if constexpr (FB == 8 && RB == 256) {
+        // v_perm_b32 bytes: 0 <- byte 0 of lane_off, 1 <- byte sh/8 of u, 2, 3 <- 0
+        return __builtin_amdgcn_perm(u, lane_off, 0x0C0C0000u | ((4u + (uint32_t)(sh >> 3)) << 8));
+    } else {
+        constexpr int RS = RB == 256 ? 8 : 7;
+        return (((u >> sh) & ((1u << FB) - 1u)) << RS) | lane_off;
+    }
+}
+
+template <int KB, int RB>
 __device__ __forceinline__ u4_t k_frag(const uint32_t (&w)[KB], int ks, const uint32_t *tab, uint32_t lane_off) {
     constexpr int FB = 2 * KB;
     uint32_t u;
@@ -125,7 +141,7 @@ __device__ __forceinline__ u4_t k_frag(const uint32_t (&w)[KB], int ks, const ui
     }
     u4_t f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) f[k] = tab_read<KB>(tab, (u >> (FB * k)) & ((1u << FB) - 1u), lane_off);
+    for (int k = 0; k < 4; ++k) f[k] = tab_at(tab, tab_off<FB, RB>(u, FB * k, lane_off));
     return f;
 }
 
@@ -169,7 +185,8 @@ __device__ __forceinline__ void v_pairs(const uint32_t (&u)[8], uint32_t (&x)[4]
     }
 }
 
-// A operand of the value MFMA for position tile j (position 8n + j of 8 tokens).
+// A operand of the value MFMA for position tile j (position 8n + j of 8 tokens);
+// `tab` points at the V half of the 256-byte table rows.
 template <int VB>
 __device__ __forceinline__ u4_t v_frag(const uint32_t (&x)[4], const uint32_t (&y)[4], int j, const uint32_t *tab,
                                        uint32_t lane_off) {
@@ -177,8 +194,7 @@ __device__ __forceinline__ u4_t v_frag(const uint32_t (&x)[4], const uint32_t (&
     const int sh = FB * (j >> 1);
     u4_t f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        f[k] = tab_read<VB>(tab, (((j & 1) ? y[k] : x[k]) >> sh) & ((1u << FB) - 1u), lane_off);
+    for (int k = 0; k < 4; ++k) f[k] = tab_at(tab, tab_off<FB, 256>((j & 1) ? y[k] : x[k], sh, lane_off));
     return f;
 }
 
@@ -213,12 +229,14 @@ void tq_decode_mfma_kernel(
     // waves' partials ([wave][row][128] for at most 8 rows, one [row][kQS]
     // accumulator otherwise)
     constexpr int KCOP = tab_copies<KB>(), VCOP = tab_copies<VB>();
-    constexpr int kTabWords = NKT * KCOP + (WV ? NVT * VCOP : 0);
+    static_assert(KCOP == 32 && VCOP == 32, "32 copies of an entry fill half of a 256-byte row");
+    constexpr int RB = WV ? 256 : 128;   // bytes per table row
+    constexpr int kTabWords = (WV ? (NKT > NVT ? NKT : NVT) : NKT) * (RB / 4);
     constexpr int kMerge = PK ? kMW * 8 * kD : 16 * kQS;
     constexpr int kArea = kTabWords > kMerge ? kTabWords : kMerge;
     __shared__ __attribute__((aligned(16))) uint32_t area[kArea];
     uint32_t *const ktab = area;
-    uint32_t *const vtab = area + NKT * KCOP;
+    uint32_t *const vtab = area + 32;   // V half of each row (RB = 256)
     float *const mbuf = reinterpret_cast<float *>(area);
     __shared__ __attribute__((aligned(16))) float buf[16 * kQS];      // q'' during set-up
     __shared__ __attribute__((aligned(16))) float nrm[kMW][2][64];     // per wave: K, V norms of the slice
@@ -416,18 +434,18 @@ void tq_decode_mfma_kernel(
     }
 
     // replicate the pair tables: 4 threads per entry (i = 4 e + quarter), 8 copies each
-    auto fill_entry = [&](uint32_t *tab, uint32_t v, int i, int copies) __attribute__((always_inline)) {
-        u4_t *d = reinterpret_cast<u4_t *>(tab + (i >> 2) * copies + (i & 3) * 8);
+    auto fill_entry = [&](uint32_t *tab, uint32_t v, int i) __attribute__((always_inline)) {
+        u4_t *d = reinterpret_cast<u4_t *>(tab + (i >> 2) * (RB / 4) + (i & 3) * 8);
         d[0] = u4_t{v, v, v, v};
         d[1] = u4_t{v, v, v, v};
     };
 #pragma unroll
     for (int it = 0; it < KIT; ++it)
-        if (it * kMBlock + tid < NKT * 4) fill_entry(ktab, kent[it], it * kMBlock + tid, KCOP);
+        if (it * kMBlock + tid < NKT * 4) fill_entry(ktab, kent[it], it * kMBlock + tid);
     if constexpr (WV) {
 #pragma unroll
         for (int it = 0; it < VIT; ++it)
-            if (it * kMBlock + tid < NVT * 4) fill_entry(vtab, vent[it], it * kMBlock + tid, VCOP);
+            if (it * kMBlock + tid < NVT * 4) fill_entry(vtab, vent[it], it * kMBlock + tid);
     }
     const uint32_t lane_off = (uint32_t)(lane & 31) << 2;
 
@@ -552,7 +570,7 @@ void tq_decode_mfma_kernel(
             S[tm] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const u4_t af = k_frag<KB>(sl.kw[tm], ks, ktab, lane_off);
+                const u4_t af = k_frag<KB, RB>(sl.kw[tm], ks, ktab, lane_off);
                 S[tm] = mfma_f16(af, qb[ks], S[tm]);
                 if constexpr (!PK) S[tm] = mfma_f16(af, qb[4 + ks], S[tm]);
             }

@@ -23,9 +23,12 @@ constexpr int kDppXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppRor4 = 0x124;   // row_ror:4
 constexpr int kDppRor8 = 0x128;   // row_ror:8 (= xor 8 inside a 16-lane row)
 
+// Every control above reads a valid lane of the same row, so bound_ctrl (zero for
+// an out-of-range source) never applies; setting it lets the compiler fold the
+// move into the add or max that uses it (one DPP instruction instead of two).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over the eight lanes of one block (virtual-lane bits <-> xor 1, 2, 8).
