@@ -77,6 +77,10 @@ tq_status check_cache(const tq_cache *c) {
     return check_codebook(c->cb, c->bits);
 }
 
+// Groups of 8 vectors each quantize wave takes in a row (when n_kv divides 8).
+constexpr int kQuantGroups = 4;
+int quant_gpw(int n_kv) { return (n_kv > 0 && 8 % n_kv == 0) ? kQuantGroups : 0; }
+
 // Encode grid for one codebook: cells of width 1/grid in y, at most one boundary
 // per (slightly widened) cell; the table covers y in [-1, 1] (|y| <= 1 because y
 // is a rotated unit vector).
@@ -97,6 +101,8 @@ tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, in
     q.signs = c->signs;
     q.src_stride = stride;
     q.n_vec = (int64_t)n_tokens * c->n_kv_heads;
+    q.n_tokens = n_tokens;
+    q.gpw = quant_gpw(c->n_kv_heads);
     q.n_kv = c->n_kv_heads;
     q.block_size = c->block_size;
     q.bits = c->bits;
@@ -111,14 +117,17 @@ tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, in
 
 int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 
-// Blocks for one quantize side: 4 waves of 8 blocks each per thread block, at
-// most 8 thread blocks per CU, rounded so the grid stride is a multiple of n_kv.
+// Blocks for one quantize side (4 waves per block).  When n_kv divides 8, every
+// wave takes kQuantGroups consecutive groups of 8 vectors; otherwise at most 512
+// blocks (with both sides, about 4 waves per SIMD, each pipelining several
+// groups), rounded so the grid stride is a multiple of n_kv.
 int quant_blocks(int64_t n_vec, int n_kv) {
     if (n_vec == 0) return 0;
+    if (quant_gpw(n_kv) > 0) return (int)((n_vec + 32 * kQuantGroups - 1) / (32 * kQuantGroups));
     const int64_t need = (n_vec + 31) / 32;
-    int blocks = (int)std::min<int64_t>(need, 2048);
+    int blocks = (int)std::min<int64_t>(need, 512);
     const int m = n_kv / gcd_int(n_kv, 32);
-    blocks = ((blocks + m - 1) / m) * m;
+    blocks = std::max(m, (blocks / m) * m);
     return blocks;
 }
 

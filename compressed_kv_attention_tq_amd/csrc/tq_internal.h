@@ -56,6 +56,8 @@ struct QuantSide {
     const uint32_t *signs;    // [n_kv][4]
     int64_t src_stride;       // elements between tokens
     int64_t n_vec;            // n_tokens * n_kv
+    int32_t n_tokens;
+    int32_t gpw;              // groups of 8 vectors per wave (consecutive), or 0: grid stride
     int32_t n_kv;
     int32_t block_size;
     int32_t bits;

@@ -44,15 +44,29 @@ __device__ void build_lut(const QuantSide &p, LutEntry *lut) {
 
 template <int BITS>
 __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__restrict__ slots,
-                                           const LutEntry *lut, int blk, int nblk) {
+                                           LutEntry *lut, int blk, int nblk) {
     const Lane8 L = lane8();
     const int j = L.j;
     const int wpb = blockDim.x >> 6;
-    const int wave_id = blk * wpb + (int)(threadIdx.x >> 6);
-    // The grid stride (in blocks) is a multiple of n_kv, so the head of this
-    // lane's block never changes and the token advances by a constant.
-    const int step = nblk * wpb * 8;
-    const int v0 = wave_id * 8 + L.vin;
+    const int wave_id = __builtin_amdgcn_readfirstlane(blk * wpb + (int)(threadIdx.x >> 6));   // uniform
+    // Groups of 8 vectors: with gpw > 0 (n_kv divides 8) the wave takes gpw
+    // consecutive groups, so a block writes whole, line-aligned runs of every
+    // head's code rows and no cache line of codes is shared with another block;
+    // otherwise the grid stride (in blocks) is a multiple of n_kv.  Either way
+    // the head of this lane's vector never changes and the token advances by a
+    // constant per group.
+    int first, step, n_groups;
+    if (p.gpw > 0) {
+        first = wave_id * p.gpw * 8;
+        step = 8;
+        n_groups = first < p.n_vec ? (int)min<int64_t>(p.gpw, (p.n_vec - first + 7) / 8) : 0;
+    } else {
+        first = wave_id * 8;
+        step = nblk * wpb * 8;
+        n_groups = first < p.n_vec ? (int)((p.n_vec - first + step - 1) / step) : 0;
+    }
+    n_groups = __builtin_amdgcn_readfirstlane(n_groups);   // uniform: the loop is scalar control flow
+    const int v0 = first + L.vin;
     const int tok0 = (int)fdiv((uint32_t)v0, p.kv_div);
     const int head = v0 - tok0 * p.n_kv;
     const int tok_step = (int)fdiv((uint32_t)step, p.kv_div);
@@ -69,25 +83,29 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
     const uint16_t *src = p.src + (int64_t)head * kD + j * 16;
     const LutEntry *lut0 = lut + p.lut_half;
 
-    int tok = tok0;
-    for (int g0 = wave_id * 8; g0 < p.n_vec; g0 += step, tok += tok_step) {   // uniform per wave
+    // One group = 8 vectors (one per 8-lane block of the wave).  Two groups'
+    // loads are in flight while one is encoded: every load is issued (past the
+    // end, from the last token's row: cached and never stored), and the loop
+    // exits only at the top, so a wait never covers the group loading behind it.
+    struct Group {
+        uint32_t w[8];
+        int64_t slot;
+    };
+    auto load = [&](Group &gr, int tk) __attribute__((always_inline)) {
+        const int t = min(tk, p.n_tokens - 1);
+        const uint4 *sp = reinterpret_cast<const uint4 *>(src + (int64_t)t * p.src_stride);
+        const uint4 a = sp[0], b = sp[1];
+        gr.w[0] = a.x; gr.w[1] = a.y; gr.w[2] = a.z; gr.w[3] = a.w;
+        gr.w[4] = b.x; gr.w[5] = b.y; gr.w[6] = b.z; gr.w[7] = b.w;
+        gr.slot = slots[t];
+    };
+    auto encode = [&](const Group &gr, int g0) __attribute__((always_inline)) {
         const bool valid = g0 + L.vin < p.n_vec;
         uint32_t w[8];
-        if (valid) {
-            const uint4 *sp = reinterpret_cast<const uint4 *>(src + (int64_t)tok * p.src_stride);
-            const uint4 a = sp[0], b = sp[1];
-            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) w[k] = 0;
-        }
-        const int64_t slot = valid ? slots[tok] : -1;
-
         float ss = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            w[k] ^= smask[k];
+            w[k] = gr.w[k] ^ smask[k];
             const half2_t h = __builtin_bit_cast(half2_t, w[k]);
             ss = __builtin_amdgcn_fdot2(h, h, ss, false);
         }
@@ -114,6 +132,7 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
             code[k] = (uint32_t)e.base + (t > e.thr ? 1u : 0u);
         }
 
+        const int64_t slot = gr.slot;
         if (valid && slot >= 0) {
             const uint32_t blk_id = fdiv((uint32_t)slot, bsdiv);
             const uint32_t off = (uint32_t)slot - blk_id * (uint32_t)p.block_size;
@@ -139,28 +158,45 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
                     else if (3 * k >= 32) hi |= code[k] << (3 * k - 32);
                     else { lo |= code[k] << (3 * k); hi |= code[k] >> (32 - 3 * k); }
                 }
+                // (even j: dword then ushort; odd j: ushort then dword, both 2-aligned)
                 uint8_t *d = dst + 6 * j;
-                if ((j & 1) == 0) {
-                    *reinterpret_cast<uint32_t *>(d) = lo;
-                    *reinterpret_cast<uint16_t *>(d + 4) = (uint16_t)hi;
-                } else {
-                    *reinterpret_cast<uint16_t *>(d) = (uint16_t)lo;
-                    *reinterpret_cast<uint32_t *>(d + 2) = (lo >> 16) | (hi << 16);
-                }
+                const bool odd = j & 1;
+                *reinterpret_cast<uint16_t *>(d + (odd ? 0 : 4)) = (uint16_t)(odd ? lo : hi);
+                *reinterpret_cast<uint32_t *>(d + (odd ? 2 : 0)) = odd ? ((lo >> 16) | (hi << 16)) : lo;
             }
             if (j == 0) p.norms[row] = __fsqrt_rn(ss);
+        }
+    };
+
+    // kDepth groups in flight: each encode is followed by the load of the group
+    // kDepth ahead
+    constexpr int kDepth = 2;
+    Group gr[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+        __builtin_amdgcn_sched_barrier(0);
+        load(gr[d], tok0 + d * tok_step);
+    }
+    // the encode table is built while the first groups load
+    build_lut(p, lut);
+    __syncthreads();
+    int tok = tok0;
+    for (int i = 0; i < n_groups; i += kDepth, tok += kDepth * tok_step) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            __builtin_amdgcn_sched_barrier(0);
+            encode(gr[d], first + (i + d) * step);   // (past the end: no lane stores)
+            load(gr[d], tok + (kDepth + d) * tok_step);
         }
     }
 }
 
 __global__ __launch_bounds__(256) void tq_quantize_kernel(QuantArgs a) {
-    __shared__ LutEntry lut[kLutMax];
+    __shared__ LutEntry lut[kLutMax];   // built inside quant_side, once its first loads are out
     const bool second = (int)blockIdx.x >= a.blocks_k;
     const QuantSide &p = second ? a.side[1] : a.side[0];
     const int blk = second ? (int)blockIdx.x - a.blocks_k : (int)blockIdx.x;
     const int nblk = second ? (int)gridDim.x - a.blocks_k : a.blocks_k;
-    build_lut(p, lut);
-    __syncthreads();
     switch (p.bits) {
         case 2: quant_side<2>(p, a.slots, lut, blk, nblk); break;
         case 3: quant_side<3>(p, a.slots, lut, blk, nblk); break;
