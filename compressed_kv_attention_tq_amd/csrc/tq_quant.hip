@@ -85,14 +85,16 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
 
     // One group = 8 vectors (one per 8-lane block of the wave).  Two groups'
     // loads are in flight while one is encoded: every load is issued (past the
-    // end, from the last token's row: cached and never stored), and the loop
-    // exits only at the top, so a wait never covers the group loading behind it.
+    // wave's groups, from its last group's rows: cached and never stored), and the
+    // loop exits only at the top, so a wait never covers the group loading behind it.
     struct Group {
         uint32_t w[8];
         int64_t slot;
     };
+    // past the wave's last group a load re-reads that group's rows (cached)
+    const int tok_last = tok0 + max(n_groups - 1, 0) * tok_step;
     auto load = [&](Group &gr, int tk) __attribute__((always_inline)) {
-        const int t = min(tk, p.n_tokens - 1);
+        const int t = min(min(tk, tok_last), p.n_tokens - 1);
         const uint4 *sp = reinterpret_cast<const uint4 *>(src + (int64_t)t * p.src_stride);
         const uint4 a = sp[0], b = sp[1];
         gr.w[0] = a.x; gr.w[1] = a.y; gr.w[2] = a.z; gr.w[3] = a.w;
