@@ -320,6 +320,41 @@ def run_quantize(args, torch):
                          "avg_launch_us_events": round(kern_ms * 1e3, 2)}}
 
 
+def run_codebook_fit(torch):
+    """Data-fitted codebooks (tq_fit_codebook) on the prefill data: fitted on the first
+    1024 tokens of layer 0, measured on the other 7168 through the GPU quantize and
+    dequantize kernels (relative MSE of the reconstruction), against the Gaussian
+    codebooks; plus the host fit time and the quantize kernel time with each."""
+    wl = W.prefill()
+    sk, sv = wl.signs(0)
+    k, v = wl.kv_source(0)
+    warm, n = 1024, wl.n_tokens
+    res = {"warmup_tokens": warm, "held_out_tokens": n - warm, "fit_ms": {}, "rel_mse": {}, "quantize_us": {}}
+    for side, x, sg, bits in (("k", k, sk, wl.k_bits), ("v", v, sv, wl.v_bits)):
+        t = time.perf_counter()
+        fitted = T.tq_fit_codebook(bits, x[:warm], sg)
+        res["fit_ms"][side] = round((time.perf_counter() - t) * 1e3, 1)
+        xs = torch.from_numpy(x[warm:]).cuda()
+        slots = torch.arange(n - warm, dtype=torch.int64, device="cuda")
+        ref = xs.float()
+        res["rel_mse"][side], res["quantize_us"][side] = {}, {}
+        for name, cb in (("gaussian", None), ("fitted", fitted)):
+            c = T.Cache.allocate(bits, wl.n_kv_heads, wl.block_size, -(-(n - warm) // wl.block_size), sg, cb=cb)
+            T.tq_quantize_kv(c, xs, None, None, slots)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                T.tq_quantize_kv(c, xs, None, None, slots)
+            e1.record()
+            torch.cuda.synchronize()
+            xh = T.tq_dequantize(c, slots)
+            err = float(((xh - ref) ** 2).sum() / (ref ** 2).sum())
+            res["rel_mse"][side][name] = round(err, 6)
+            res["quantize_us"][side][name] = round(e0.elapsed_time(e1) * 100.0, 2)
+    log(f"[bench] fitted codebooks: {res}")
+    return res
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The oracle (unchanged) on a bounded sample of the same decode step: for the KV
     heads of sequence 0 in turn (cycling), quantize-append the new token and decode its
@@ -400,10 +435,12 @@ def main():
         return
 
     if args.quantize_only:
-        print(json.dumps({"quantize": run_quantize(args, torch)}), flush=True)
+        print(json.dumps({"quantize": run_quantize(args, torch), "codebook_fit": run_codebook_fit(torch)}),
+              flush=True)
         return
     wl, value, ms_step, roof, cfg, step_bytes = run_decode(args, torch)
     quant = None if args.no_quantize else run_quantize(args, torch)
+    fitted = None if args.no_quantize else run_codebook_fit(torch)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -411,6 +448,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": cfg, "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_bytes": step_bytes, "roofline": roof, "cpu_baseline": cpu, "quantize": quant,
+        "codebook_fit": fitted,
     }
     print(json.dumps(rec), flush=True)
 

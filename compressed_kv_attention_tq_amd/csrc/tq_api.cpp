@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "tq_internal.h"
 
@@ -177,6 +178,27 @@ DecodePlan plan_decode(int n_seqs, int n_kv, int rows, int max_blocks, int block
     return p;
 }
 
+// float16 bits -> double (exact)
+double half_to_double(uint16_t h) {
+    const int e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp((double)(m | 1024), e - 25);
+    return (h >> 15) ? -v : v;
+}
+
+// In-place unnormalised Walsh-Hadamard transform of 128 values, natural order.
+void fwht128(double *x) {
+    for (int h = 1; h < 128; h <<= 1)
+        for (int i = 0; i < 128; i += 2 * h)
+            for (int k = i; k < i + h; ++k) {
+                const double a = x[k], b = x[k + h];
+                x[k] = a + b;
+                x[k + h] = a - b;
+            }
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,6 +250,79 @@ tq_status tq_build_codebook(int32_t bits, double sigma, tq_codebook *out) {
     for (int j = 0; j < L; ++j) out->centroids[j] = (float)cs[j];
     for (int j = 0; j + 1 < L; ++j) out->boundaries[j] = (float)bs[j];
     out->mse = gaussian_mse(cs, bs, L, sigma);
+    return TQ_OK;
+}
+
+tq_status tq_fit_codebook(int32_t bits, const uint16_t *vectors, int64_t n_vectors, int32_t n_heads,
+                          const uint32_t *signs, int32_t max_iter, tq_codebook *out) {
+    if (!out || !vectors || !signs || n_vectors < 1 || n_heads < 1 || max_iter < 1) return TQ_ERR_INVALID_ARG;
+    if (bits < 1 || bits > 4) return TQ_ERR_UNSUPPORTED;
+    const int L = 1 << bits;
+    const double sigma = 1.0 / sqrt(128.0);
+    // samples: the rotated coordinates of every nonzero, finite vector
+    std::vector<double> ys;
+    ys.reserve((size_t)n_vectors * 128);
+    double x[128];
+    for (int64_t i = 0; i < n_vectors; ++i) {
+        const uint16_t *v = vectors + i * 128;
+        const uint32_t *sw = signs + (i % n_heads) * 4;
+        double ss = 0.0;
+        bool finite = true;
+        for (int k = 0; k < 128; ++k) {
+            x[k] = half_to_double(v[k]);
+            finite = finite && isfinite(x[k]);
+            ss += x[k] * x[k];
+        }
+        if (!finite || !(ss > 0.0)) continue;
+        const double inv = 1.0 / sqrt(ss);
+        for (int k = 0; k < 128; ++k) x[k] = (((sw[k >> 5] >> (k & 31)) & 1u) ? -x[k] : x[k]) * inv;
+        fwht128(x);
+        for (int k = 0; k < 128; ++k) ys.push_back(x[k] * sigma);
+    }
+    if (ys.empty()) return TQ_ERR_INVALID_ARG;
+    // cells are runs of the sorted samples: each round is a search per boundary
+    std::sort(ys.begin(), ys.end());
+    const size_t n = ys.size();
+    std::vector<double> s1(n + 1, 0.0), s2(n + 1, 0.0);
+    for (size_t k = 0; k < n; ++k) {
+        s1[k + 1] = s1[k] + ys[k];
+        s2[k + 1] = s2[k] + ys[k] * ys[k];
+    }
+    tq_codebook init;
+    tq_build_codebook(bits, sigma, &init);
+    double c[TQ_MAX_LEVELS];
+    for (int j = 0; j < L; ++j) c[j] = init.centroids[j];
+    size_t idx[TQ_MAX_LEVELS + 1], prev[TQ_MAX_LEVELS + 1];
+    for (int it = 0; it < max_iter; ++it) {
+        // assignment: a sample above the midpoint of two centres goes to the upper
+        idx[0] = 0;
+        idx[L] = n;
+        for (int j = 0; j + 1 < L; ++j)
+            idx[j + 1] = (size_t)(std::upper_bound(ys.begin(), ys.end(), 0.5 * (c[j] + c[j + 1])) - ys.begin());
+        if (it > 0 && std::equal(idx, idx + L + 1, prev)) break;   // stable: done
+        std::copy(idx, idx + L + 1, prev);
+        // update: each centre moves to the mean of its samples (an empty cell keeps its centre)
+        for (int j = 0; j < L; ++j)
+            if (idx[j + 1] > idx[j]) c[j] = (s1[idx[j + 1]] - s1[idx[j]]) / (double)(idx[j + 1] - idx[j]);
+    }
+    memset(out, 0, sizeof(*out));
+    out->bits = bits;
+    out->n_levels = L;
+    out->sigma = (float)sigma;
+    double cs[TQ_MAX_LEVELS], bs[TQ_MAX_LEVELS];
+    for (int j = 0; j < L; ++j) cs[j] = round_to_half(c[j]);
+    for (int j = 0; j + 1 < L; ++j) bs[j] = 0.5 * (cs[j] + cs[j + 1]);
+    for (int j = 0; j < L; ++j) out->centroids[j] = (float)cs[j];
+    for (int j = 0; j + 1 < L; ++j) out->boundaries[j] = (float)bs[j];
+    // mean squared error of the samples under the stored codebook
+    double err = 0.0;
+    size_t lo = 0;
+    for (int j = 0; j < L; ++j) {
+        const size_t hi = j + 1 < L ? (size_t)(std::upper_bound(ys.begin(), ys.end(), bs[j]) - ys.begin()) : n;
+        err += (s2[hi] - s2[lo]) - 2.0 * cs[j] * (s1[hi] - s1[lo]) + (double)(hi - lo) * cs[j] * cs[j];
+        lo = hi;
+    }
+    out->mse = err / (double)n;
     return TQ_OK;
 }
 

@@ -25,7 +25,7 @@ MAX_LEVELS = 16
 MAX_ROWS_PER_KV_HEAD = 16
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
-EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_quantize_kv", "tq_decode_attention",
+EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_fit_codebook", "tq_quantize_kv", "tq_decode_attention",
            "tq_decode_attention_timed", "tq_dequantize")
 
 
@@ -83,6 +83,9 @@ def load_library(path: str = LIB_PATH):
     lib.tq_status_string.argtypes = [ctypes.c_int]
     lib.tq_build_codebook.restype = ctypes.c_int
     lib.tq_build_codebook.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.POINTER(TQCodebook)]
+    lib.tq_fit_codebook.restype = ctypes.c_int
+    lib.tq_fit_codebook.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(TQCodebook)]
     lib.tq_quantize_kv.restype = ctypes.c_int
     lib.tq_quantize_kv.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.POINTER(TQCache),
                                    ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
@@ -114,6 +117,22 @@ def _check(status: int, what: str):
 def tq_build_codebook(bits: int, sigma: float = 1.0 / math.sqrt(HEAD_DIM)) -> TQCodebook:
     cb = TQCodebook()
     _check(load_library().tq_build_codebook(bits, sigma, ctypes.byref(cb)), "tq_build_codebook")
+    return cb
+
+
+def tq_fit_codebook(bits: int, vectors, sign_words, max_iter: int = 200) -> TQCodebook:
+    """Data-fitted codebook of one side from host float16 vectors [..., n_heads, 128]
+    (the last-but-one axis is the head, whose signs are sign_words[head])."""
+    v = np.ascontiguousarray(np.asarray(vectors, dtype=np.float16))
+    if v.ndim < 2 or v.shape[-1] != HEAD_DIM:
+        raise ValueError("vectors must be [..., 128] float16")
+    sw = np.ascontiguousarray(np.asarray(sign_words, dtype=np.uint32).reshape(-1, 4))
+    n_heads = sw.shape[0]
+    if v.ndim >= 3 and v.shape[-2] != n_heads:
+        raise ValueError("vectors [..., n_heads, 128] must match sign_words [n_heads, 4]")
+    cb = TQCodebook()
+    _check(load_library().tq_fit_codebook(bits, v.ctypes.data, v.size // HEAD_DIM, n_heads, sw.ctypes.data,
+                                          max_iter, ctypes.byref(cb)), "tq_fit_codebook")
     return cb
 
 

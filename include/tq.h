@@ -108,6 +108,29 @@ const char *tq_status_string(tq_status status);
  *         TQ_ERR_UNSUPPORTED (bits outside 1..4). */
 tq_status tq_build_codebook(int32_t bits, double sigma, tq_codebook *out);
 
+/* Data-fitted Lloyd-Max codebook for one cache side ([TQ blog] 3.3, the steps as
+ * the article lists them: assign every sample to its nearest centre, move every
+ * centre to the mean of its samples, repeat until the assignment stops changing,
+ * with K and V fitted separately; [TQ blog] 5.3 advises a warm-up on typical
+ * inputs so the quantizer adapts to the task's data).  The samples
+ * are the 128 rotated coordinates y = H (s o x / |x|) / sqrt(128) of each of
+ * n_vectors float16 vectors (host memory, [n_vectors][128]; vector i belongs to
+ * head i % n_heads, so a token-major [n_tokens][n_heads][128] array works as
+ * is, with that head's signs signs[head][4], host memory, bit i of word w
+ * meaning element 32*w+i is negated).  Zero and non-finite vectors are skipped.
+ * It starts from tq_build_codebook(bits, 1/sqrt(128)) and runs at most max_iter
+ * rounds.  The stored codebook follows the same format: float16-exact centroids
+ * (ascending; not forced antisymmetric), exact midpoints as boundaries,
+ * sigma = 1/sqrt(128), and mse = the mean squared error over the samples.
+ * Host only; deterministic; allocates host memory for the samples only.
+ * A cache built with it is quantized and decoded by the same kernels; its
+ * boundaries must be at least 0.01 apart (tq_quantize_kv returns
+ * TQ_ERR_UNSUPPORTED otherwise).
+ * Errors: TQ_ERR_INVALID_ARG (NULL pointer, n_vectors, n_heads or max_iter < 1,
+ *         no nonzero finite vector), TQ_ERR_UNSUPPORTED (bits outside 1..4). */
+tq_status tq_fit_codebook(int32_t bits, const uint16_t *vectors, int64_t n_vectors, int32_t n_heads,
+                          const uint32_t *signs, int32_t max_iter, tq_codebook *out);
+
 /* Quantize-on-append ([TQ+ README] backend table, SET_ROWS for turbo types):
  * compress n_tokens new K and V rows and write them into their cache slots.
  *   k, v            : host descriptors; either may be NULL to skip that side.

@@ -50,6 +50,11 @@ Readings taken where the pages are silent (each one also listed in the design doc):
       then each centroid rounded to the nearest float16 value.  Decision
       boundaries are the exact midpoints of neighbouring stored centroids
       (exactly representable in float32).
+  R4a Data-fitted codebook (the [TQ blog] 3.3 steps on data, with the 5.3
+      warm-up advice): the samples are the rotated coordinates of the given
+      nonzero vectors; the centres start at the stored Gaussian codebook of R4
+      and stop when no sample changes cell; not made antisymmetric; stored like
+      R4 (float16 centres, exact midpoints).
   R5  Encoding: code = number of boundaries strictly below y, comparing the
       float64 y with the stored boundaries; a tie goes to the lower code.
   R6  Packing: LSB-first bitstream per 128-block; code i occupies stream bits
@@ -74,7 +79,7 @@ D = 128  # elements per block ([TQ+ README] note under the quantization types ta
 
 __all__ = [
     "D", "hadamard_matrix", "sign_vector", "rotate", "unrotate",
-    "gaussian_lloyd_max", "lloyd_max_from_samples", "Codebook", "build_codebook",
+    "gaussian_lloyd_max", "lloyd_max_from_samples", "Codebook", "build_codebook", "fit_codebook",
     "codebook_mse", "encode", "near_boundary_mask", "quantize_vectors",
     "pack_codes", "unpack_codes", "dequantize_vectors", "OracleCache",
     "new_cache", "cache_write", "cache_read", "slots_for_sequence",
@@ -232,6 +237,41 @@ def build_codebook(bits: int, sigma: float = 1.0 / math.sqrt(D)) -> Codebook:
     b = 0.5 * (c16[:-1] + c16[1:])
     return Codebook(bits=bits, centroids=c16, boundaries=b,
                     mse=codebook_mse(c16, b, sigma), sigma=sigma, centroids_f64=c64)
+
+
+def fit_codebook(bits: int, vectors: np.ndarray, sign_words, max_iter: int = 200):
+    """Data-fitted stored codebook of one side ([TQ blog] 3.3 steps; 5.3 warm-up; R4a).
+
+    Samples: for every nonzero, finite vector x (float16 values, rows of
+    [..., n_heads, 128]; the head is the last-but-one index), the 128 rotated
+    coordinates y = H (s_head * x / ||x||) / sqrt(128).  Centres start at the
+    stored Gaussian codebook of build_codebook(bits) and follow
+    lloyd_max_from_samples (nearest centre, then means, until the assignment is
+    stable).  Stored as build_codebook stores: centres rounded to float16,
+    boundaries the exact midpoints; mse is the mean squared error of the samples.
+
+    Returns (Codebook, centres before rounding, samples).
+    """
+    sw = np.asarray(sign_words, dtype=np.uint32).reshape(-1, 4)
+    x = np.asarray(vectors).astype(np.float64).reshape(-1, sw.shape[0], D)
+    ys = []
+    for h in range(sw.shape[0]):
+        xh = x[:, h, :]
+        n = np.sqrt(np.sum(xh * xh, axis=-1))
+        ok = np.isfinite(xh).all(axis=-1) & (n > 0)
+        u = xh[ok] / n[ok, None]
+        ys.append(rotate(u, sign_vector(sw[h])).ravel())
+    y = np.concatenate(ys)
+    if y.size == 0:
+        raise ValueError("no nonzero finite vector")
+    init = build_codebook(bits).centroids
+    c64 = lloyd_max_from_samples(y, 1 << bits, max_iter=max_iter, init=init)
+    c16 = c64.astype(np.float16).astype(np.float64)
+    b = 0.5 * (c16[:-1] + c16[1:])
+    code = encode(y, b)
+    mse = float(np.mean((y - c16[code]) ** 2))
+    cb = Codebook(bits=bits, centroids=c16, boundaries=b, mse=mse, sigma=1.0 / math.sqrt(D), centroids_f64=c64)
+    return cb, c64, y
 
 
 def bits_per_value(bits: int) -> float:

@@ -14,11 +14,26 @@ def torch():
     return _t
 
 
-def oracle_cache(wl, side, seqs=None, n_blocks=None):
-    """Quantize the workload's K (side 0) or V (side 1) with the oracle into pages."""
+def tq_codebook_from(ocb):
+    """The library's codebook struct holding an oracle codebook's stored values."""
+    cb = T.TQCodebook()
+    cb.bits = ocb.bits
+    cb.n_levels = 1 << ocb.bits
+    for j, c in enumerate(ocb.centroids):
+        cb.centroids[j] = float(c)
+    for j, b in enumerate(ocb.boundaries):
+        cb.boundaries[j] = float(b)
+    cb.sigma = float(ocb.sigma)
+    cb.mse = float(ocb.mse)
+    return cb
+
+
+def oracle_cache(wl, side, seqs=None, n_blocks=None, cb=None):
+    """Quantize the workload's K (side 0) or V (side 1) with the oracle into pages
+    (with codebook cb, by default the Gaussian one)."""
     bits = wl.k_bits if side == 0 else wl.v_bits
     signs = wl.signs_k if side == 0 else wl.signs_v
-    cb = O.build_codebook(bits)
+    cb = O.build_codebook(bits) if cb is None else cb
     c = O.new_cache(bits, wl.n_kv_heads, wl.block_size, n_blocks or wl.n_blocks, signs, cb)
     for b in (range(wl.n_seqs) if seqs is None else seqs):
         if int(wl.seq_lens[b]) == 0:
@@ -29,9 +44,10 @@ def oracle_cache(wl, side, seqs=None, n_blocks=None):
 
 
 def gpu_cache_from(oc, device="cuda"):
-    """A device cache holding exactly the oracle cache's codes and norms."""
+    """A device cache holding exactly the oracle cache's codes, norms and codebook."""
     t = torch()
-    g = T.Cache.allocate(oc.bits, oc.n_kv_heads, oc.block_size, oc.n_blocks, oc.signs, device)
+    g = T.Cache.allocate(oc.bits, oc.n_kv_heads, oc.block_size, oc.n_blocks, oc.signs, device,
+                         cb=tq_codebook_from(oc.cb))
     g.codes.copy_(t.from_numpy(oc.codes))
     g.norms.copy_(t.from_numpy(oc.norms))
     return g
@@ -54,13 +70,14 @@ def row_rel_err(got, want):
     return num / np.where(den > 0, den, 1.0)
 
 
-def check_codes(gpu_packed, gpu_norms, x16, signs_words, bits, eps=1e-6):
-    """Compare GPU-written packed codes / norms of rows x16 [n, 128] against the oracle.
+def check_codes(gpu_packed, gpu_norms, x16, signs_words, bits, eps=1e-6, cb=None):
+    """Compare GPU-written packed codes / norms of rows x16 [n, 128] against the oracle
+    (codebook cb, by default the Gaussian one).
 
     Returns the number of elements excluded as within eps of a decision boundary.
     Codes must match bit-exactly elsewhere; norms within 1e-6 relative.
     """
-    cb = O.build_codebook(bits)
+    cb = O.build_codebook(bits) if cb is None else cb
     s = O.sign_vector(signs_words)
     n, codes, y = O.quantize_vectors(x16, s, cb)
     got = O.unpack_codes(gpu_packed, bits)

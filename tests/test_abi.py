@@ -167,3 +167,57 @@ def test_dequantize_validation_errors():
     assert lib.tq_dequantize(ctypes.byref(fake_cache(head_dim=256)), FAKE, 4, FAKE, 0, None) == T.TQ_ERR_UNSUPPORTED
     assert lib.tq_dequantize(ctypes.byref(c), FAKE, 0, FAKE, 0, None) == T.TQ_OK
     assert lib.tq_dequantize(None, FAKE, 4, FAKE, 0, None) == T.TQ_ERR_INVALID_ARG
+
+
+def _fit_inputs(kind, bits, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "gauss":
+        x = rng.standard_normal((96, 4, 128))
+    elif kind == "laplace":
+        x = rng.laplace(size=(96, 4, 128)) * np.where(rng.random((96, 4, 128)) < 0.01, 30.0, 1.0)
+    else:  # channel scales, fixed across tokens (the K recipe of the 8B-shaped workload)
+        x = rng.standard_normal((96, 4, 128)) * np.exp(rng.standard_normal((1, 4, 128)))
+    x[3, 1] = 0.0   # a zero vector (skipped)
+    sw = rng.integers(0, 2 ** 32, size=(4, 4), dtype=np.uint64).astype(np.uint32)
+    return x.astype(np.float16), sw
+
+
+@pytest.mark.parametrize("kind", ["gauss", "laplace", "channels"])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_fit_codebook_matches_oracle(bits, kind):
+    """Library fit (host) = oracle fit; a stored centre may differ by one float16 ulp
+    only where the unrounded centre sits at a rounding midpoint."""
+    x, sw = _fit_inputs(kind, bits, 100 + bits)
+    cb = T.tq_fit_codebook(bits, x, sw)
+    ref, c64, _ = O.fit_codebook(bits, x, sw)
+    got = cb.centroid_array.astype(np.float64)
+    diff = got != ref.centroids
+    if diff.any():
+        ulp = np.spacing(np.abs(ref.centroids).astype(np.float16)).astype(np.float64)
+        frac = np.abs(c64 - ref.centroids) / ulp
+        assert np.all(np.abs(frac[diff] - 0.5) < 1e-6)
+    else:
+        assert np.array_equal(cb.boundary_array.astype(np.float64), ref.boundaries)
+    assert cb.n_levels == 1 << bits and cb.bits == bits
+    assert math.isclose(cb.sigma, 1.0 / math.sqrt(128), rel_tol=1e-7)
+    assert math.isclose(cb.mse, ref.mse, rel_tol=1e-6)
+
+
+def test_fit_codebook_rejects_bad_arguments():
+    lib = T.load_library()
+    cb = T.TQCodebook()
+    x = np.ones((4, 128), np.float16)
+    sw = np.zeros((1, 4), np.uint32)
+    ok = lambda bits, n, h, it, v=x, s=sw, out=ctypes.byref(cb): lib.tq_fit_codebook(
+        bits, v.ctypes.data if v is not None else None, n, h, s.ctypes.data if s is not None else None, it, out)
+    assert ok(3, 4, 1, 10) == T.TQ_OK
+    assert ok(0, 4, 1, 10) == T.TQ_ERR_UNSUPPORTED
+    assert ok(5, 4, 1, 10) == T.TQ_ERR_UNSUPPORTED
+    assert ok(3, 0, 1, 10) == T.TQ_ERR_INVALID_ARG
+    assert ok(3, 4, 0, 10) == T.TQ_ERR_INVALID_ARG
+    assert ok(3, 4, 1, 0) == T.TQ_ERR_INVALID_ARG
+    assert ok(3, 4, 1, 10, v=None) == T.TQ_ERR_INVALID_ARG
+    assert ok(3, 4, 1, 10, s=None) == T.TQ_ERR_INVALID_ARG
+    assert ok(3, 4, 1, 10, out=None) == T.TQ_ERR_INVALID_ARG
+    z = np.zeros((4, 128), np.float16)
+    assert ok(3, 4, 1, 10, v=z) == T.TQ_ERR_INVALID_ARG     # no nonzero vector

@@ -80,13 +80,15 @@ def _memo(key, fn):
 
 # --------------------------------------------------------------------------- quantize
 
-def quantize_and_compare(x16, signs, bits, block_size=16, slot_perm=None, token_pad=0):
-    """GPU-quantize x16 [n_tok, n_kv, 128] into a fresh cache and compare with the oracle."""
+def quantize_and_compare(x16, signs, bits, block_size=16, slot_perm=None, token_pad=0, ocb=None):
+    """GPU-quantize x16 [n_tok, n_kv, 128] into a fresh cache and compare with the oracle
+    (codebook ocb, an oracle codebook, by default the Gaussian one)."""
     torch = _t()
     n_tok, n_kv, _ = x16.shape
     n_blocks = max(1, -(-n_tok // block_size)) + 1
     slots = np.arange(n_tok, dtype=np.int64) if slot_perm is None else slot_perm
-    g = T.Cache.allocate(bits, n_kv, block_size, n_blocks, signs)
+    g = T.Cache.allocate(bits, n_kv, block_size, n_blocks, signs,
+                         cb=None if ocb is None else U.tq_codebook_from(ocb))
     g.codes.fill_(0xAB)
     src = np.zeros((n_tok, n_kv * 128 + token_pad), np.float16)
     src[:, : n_kv * 128] = x16.reshape(n_tok, -1)
@@ -101,7 +103,7 @@ def quantize_and_compare(x16, signs, bits, block_size=16, slot_perm=None, token_
     near = 0
     for h in range(n_kv):
         ok = slots >= 0
-        near += U.check_codes(codes[slots[ok], h], norms[slots[ok], h], x16[ok, h], signs[h], bits)
+        near += U.check_codes(codes[slots[ok], h], norms[slots[ok], h], x16[ok, h], signs[h], bits, cb=ocb)
     untouched = np.setdiff1d(np.arange(codes.shape[0]), slots[slots >= 0])
     assert np.all(codes[untouched] == 0xAB), "a skipped or unused slot was written"
     return near
@@ -161,6 +163,19 @@ def test_quantize_prefill_layer_full(layer):
         for h in range(wl.n_kv_heads):
             near += U.check_codes(codes[:, h], norms[:, h], x[:, h], sg[h], cache.bits)
     log(f"prefill layer {layer}: near-boundary {near} of {2 * k.size}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_with_fitted_codebook(bits):
+    """Codebook fitted (by the oracle) on warm-up tokens of a prefill layer; the GPU
+    quantizes the next tokens with it, the oracle with the same stored values."""
+    wl = W.prefill()
+    sk, _ = wl.signs(3)
+    k, _ = wl.kv_source(3)
+    ocb, _, _ = O.fit_codebook(bits, k[:256], sk)
+    assert not np.array_equal(ocb.centroids, O.build_codebook(bits).centroids)
+    near = quantize_and_compare(k[256:768], sk, bits, block_size=64, ocb=ocb)
+    log(f"fitted {bits}-bit: near-boundary {near}")
 
 
 # --------------------------------------------------------------------------- dequantize
@@ -263,6 +278,21 @@ def test_decode_rows_with_no_visible_token_are_zero(kernel):
                         v_bits=3, block_size=16)
     out, want = decode_and_compare(wl)
     assert np.all(out[0, :2] == 0) and np.all(out[1] == 0)
+
+
+def test_decode_with_fitted_codebooks(kernel):
+    """K and V codebooks fitted (oracle) on the first 512 positions of sequence 0."""
+    wl = W.small_decode(seed=31, n_seqs=2, lens=[1800, 640], n_qtok=2, n_q_heads=8, n_kv_heads=2, k_bits=4,
+                        v_bits=3, block_size=256)
+    k0, v0 = wl.kv_source(0)
+
+    def build():
+        ckb, _, _ = O.fit_codebook(wl.k_bits, k0[:512], wl.signs_k)
+        cvb, _, _ = O.fit_codebook(wl.v_bits, v0[:512], wl.signs_v)
+        return U.oracle_cache(wl, 0, cb=ckb), U.oracle_cache(wl, 1, cb=cvb)
+
+    ok, ov = _memo(("fitted",) + _wl_key(wl), build)
+    decode_and_compare(wl, gpu_caches=(ok, ov, U.gpu_cache_from(ok), U.gpu_cache_from(ov)), oracle_key="fitted")
 
 
 def test_decode_custom_scale(kernel):

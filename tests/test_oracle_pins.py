@@ -405,3 +405,66 @@ def test_sparse_v_semantics():
     skipped = p < tau
     bound = np.sum(p[skipped] * np.linalg.norm(vh[skipped], axis=1))
     assert np.linalg.norm(sp[0, 0, 0] - dense[0, 0, 0]) <= bound * (1 + 1e-12)
+
+
+# ----------------------------------------------------------- data-fitted codebook
+
+def _cluster_vectors(n_vec, levels, rng, jitter=0.01):
+    """Float16 vectors whose rotated coordinates fall in len(levels) well separated
+    clusters, 128 / len(levels) coordinates per cluster; also the cluster label of
+    each coordinate."""
+    k = len(levels)
+    base = np.repeat(np.asarray(levels, dtype=np.float64), 128 // k)
+    s = O.sign_vector([0x12345678, 0x9ABCDEF0, 0x0F1E2D3C, 0x4B5A6978])
+    xs, labels = [], []
+    for _ in range(n_vec):
+        perm = rng.permutation(128)
+        y = base[perm] * (1.0 + jitter * rng.standard_normal(128))
+        y /= np.linalg.norm(y)
+        xs.append(O.unrotate(y[None, :], s)[0] * 3.0)
+        labels.append(np.repeat(np.arange(k), 128 // k)[perm])
+    x16 = np.asarray(xs).astype(np.float16)
+    return x16, np.asarray(labels), s
+
+
+def test_fit_codebook_lands_on_cluster_means():
+    """Well separated clusters: the fixed point of assign/mean is the clusters' means."""
+    rng = np.random.default_rng(11)
+    x16, labels, s = _cluster_vectors(64, [-3.0, -1.0, 1.0, 3.0], rng)
+    sw = [0x12345678, 0x9ABCDEF0, 0x0F1E2D3C, 0x4B5A6978]
+    cb, c64, _ = O.fit_codebook(2, x16[:, None, :], [sw])
+    # the same samples, grouped by the cluster they were drawn from
+    x = x16.astype(np.float64)
+    y = O.rotate(x / np.linalg.norm(x, axis=1, keepdims=True), s)
+    means = np.array([y[labels == j].mean() for j in range(4)])
+    assert np.allclose(c64, means, rtol=0, atol=1e-12)
+    assert np.array_equal(cb.centroids, means.astype(np.float16).astype(np.float64))
+    assert np.array_equal(cb.boundaries, (cb.centroids[:-1] + cb.centroids[1:]) / 2)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_fit_codebook_lloyd_conditions_and_descent(bits):
+    """On heavy-tailed data: every centre is the mean of its cell, and the fit is no
+    worse on its samples than the Gaussian codebook it starts from."""
+    rng = np.random.default_rng(20 + bits)
+    x = rng.laplace(size=(256, 2, 128)) * np.where(rng.random((256, 2, 128)) < 0.01, 30.0, 1.0)
+    sw = rng.integers(0, 2 ** 32, size=(2, 4), dtype=np.uint64).astype(np.uint32)
+    cb, c64, y = O.fit_codebook(bits, x.astype(np.float16), sw)
+    b64 = (c64[:-1] + c64[1:]) / 2
+    cell = O.encode(y, b64)
+    for j in range(1 << bits):
+        assert abs(c64[j] - y[cell == j].mean()) < 1e-15
+    init = O.build_codebook(bits)
+    mse_init = np.mean((y - init.centroids[O.encode(y, init.boundaries)]) ** 2)
+    mse_fit = np.mean((y - c64[cell]) ** 2)
+    assert mse_fit <= mse_init * (1 + 1e-12)
+    assert cb.mse == pytest.approx(np.mean((y - cb.centroids[O.encode(y, cb.boundaries)]) ** 2), rel=1e-12)
+
+
+def test_fit_codebook_skips_zero_vectors():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 1, 128)).astype(np.float16)
+    sw = [[1, 2, 3, 4]]
+    a, _, _ = O.fit_codebook(3, x, sw)
+    b, _, _ = O.fit_codebook(3, np.concatenate([x, np.zeros((9, 1, 128), np.float16)]), sw)
+    assert np.array_equal(a.centroids, b.centroids)
