@@ -47,7 +47,7 @@ def log(*a):
 
 
 def cache_bytes_per_token_head(bits):
-    return 16 * bits + 4
+    return 256 if bits == 16 else 16 * bits + 4   # a float16 side: the row, no norm
 
 
 def source_hash():
@@ -101,7 +101,8 @@ class HipEvents:
 
 
 def decode_workload(name):
-    return {"llama8b": W.llama8b, "longctx": W.longctx, "ragged": W.ragged, "tiny": W.tiny}[name]()
+    return {"llama8b": W.llama8b, "llama8b_k16": W.llama8b_k16, "longctx": W.longctx, "ragged": W.ragged,
+            "tiny": W.tiny}[name]()
 
 
 def gen_kv_device(wl, b, torch, gen):
@@ -406,7 +407,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "longctx", "ragged", "tiny"])
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "llama8b_k16", "longctx", "ragged", "tiny"])
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--quantize-reps", type=int, default=5)
     ap.add_argument("--no-quantize", action="store_true")

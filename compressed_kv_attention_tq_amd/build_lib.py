@@ -32,6 +32,7 @@ SOURCES = [
     ("tq_decode_mfma.hip", "tq_decode_mfma_kb2", ["-DTQ_DECODE_KB=2"]),
     ("tq_decode_mfma.hip", "tq_decode_mfma_kb3", ["-DTQ_DECODE_KB=3"]),
     ("tq_decode_mfma.hip", "tq_decode_mfma_kb4", ["-DTQ_DECODE_KB=4"]),
+    ("tq_decode_mfma.hip", "tq_decode_mfma_kb16", ["-DTQ_DECODE_KB=16"]),   # K float16
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

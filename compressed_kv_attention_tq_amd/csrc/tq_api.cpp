@@ -69,12 +69,14 @@ tq_status check_codebook(const tq_codebook &cb, int bits) {
 tq_status check_cache(const tq_cache *c) {
     if (!c) return TQ_ERR_INVALID_ARG;
     if (c->head_dim != TQ_HEAD_DIM) return TQ_ERR_UNSUPPORTED;
-    if (c->bits < 2 || c->bits > 4) return TQ_ERR_UNSUPPORTED;
+    const bool fp16 = c->bits == TQ_BITS_FP16;
+    if (!fp16 && (c->bits < 2 || c->bits > 4)) return TQ_ERR_UNSUPPORTED;
     if (c->n_kv_heads < 1 || c->block_size < 1 || c->n_blocks < 1) return TQ_ERR_INVALID_ARG;
-    if (!c->codes || !c->norms || !c->signs) return TQ_ERR_INVALID_ARG;
-    if (!is_aligned(c->codes, 16) || !is_aligned(c->norms, 4) || !is_aligned(c->signs, 4)) return TQ_ERR_INVALID_ARG;
+    if (!c->codes || !is_aligned(c->codes, 16)) return TQ_ERR_INVALID_ARG;
     // slots are handled as 32-bit values on the device
     if ((double)c->n_blocks * c->block_size > 2147483647.0) return TQ_ERR_UNSUPPORTED;
+    if (fp16) return TQ_OK;   // rows of float16: no norms, signs or codebook
+    if (!c->norms || !c->signs || !is_aligned(c->norms, 4) || !is_aligned(c->signs, 4)) return TQ_ERR_INVALID_ARG;
     return check_codebook(c->cb, c->bits);
 }
 
@@ -87,6 +89,20 @@ int quant_gpw(int n_kv) { return (n_kv > 0 && 8 % n_kv == 0) ? kQuantGroups : 0;
 // is a rotated unit vector).
 tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, int32_t n_tokens,
                           QuantSide &q) {
+    if (c->bits == TQ_BITS_FP16) {   // the rows are stored as they come
+        q.src = static_cast<const uint16_t *>(src);
+        q.codes = c->codes;
+        q.src_stride = stride;
+        q.n_vec = (int64_t)n_tokens * c->n_kv_heads;
+        q.n_tokens = n_tokens;
+        q.gpw = quant_gpw(c->n_kv_heads);
+        q.n_kv = c->n_kv_heads;
+        q.block_size = c->block_size;
+        q.bits = c->bits;
+        q.bs_div = make_fastdiv((uint32_t)c->block_size);
+        q.kv_div = make_fastdiv((uint32_t)c->n_kv_heads);
+        return TQ_OK;
+    }
     double min_gap = INFINITY;
     const int nb = c->cb.n_levels - 1;
     for (int i = 0; i + 1 < nb; ++i) min_gap = std::min(min_gap, (double)c->cb.boundaries[i + 1] - c->cb.boundaries[i]);
@@ -379,7 +395,8 @@ tq_status tq_dequantize(const tq_cache *c, const int64_t *slots, int32_t n_token
     a.dst_fp16 = dst_is_fp16 ? 1 : 0;
     a.kv_div = make_fastdiv((uint32_t)c->n_kv_heads);
     a.bs_div = make_fastdiv((uint32_t)c->block_size);
-    for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = i < c->cb.n_levels ? c->cb.centroids[i] : 0.f;
+    if (c->bits != TQ_BITS_FP16)
+        for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = i < c->cb.n_levels ? c->cb.centroids[i] : 0.f;
     if (launch_dequantize(a, c->bits, static_cast<hipStream_t>(stream)) != hipSuccess) return TQ_ERR_HIP;
     return TQ_OK;
 }
@@ -405,6 +422,9 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     st = check_cache(v);
     if (st != TQ_OK) return st;
     if (k->n_kv_heads != v->n_kv_heads || k->block_size != v->block_size) return TQ_ERR_INVALID_ARG;
+    // float16 K needs the matrix-core pass; V is always a compressed side
+    const bool k_fp16 = k->bits == TQ_BITS_FP16;
+    if (v->bits == TQ_BITS_FP16 || (k_fp16 && !use_mfma_decode())) return TQ_ERR_UNSUPPORTED;
     if (!is_aligned(v->codes, 4)) return TQ_ERR_INVALID_ARG;
     if (n_seqs < 0 || n_qtok < 1 || n_q_heads < 1 || max_blocks_per_seq < 1) return TQ_ERR_INVALID_ARG;
     if (n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
@@ -463,7 +483,8 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     a.n_chunks = p.n_chunks;
     a.n_tiles = p.n_tiles;
     const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)kD);
-    a.qscale = (float)(scale * M_LOG2E / sqrt((double)kD));
+    // q'' = scale log2(e) H (s q) / sqrt(128); float16 K scores q itself
+    a.qscale = (float)(scale * M_LOG2E / (k_fp16 ? 1.0 : sqrt((double)kD)));
     a.max_page = (int32_t)(std::min(k->n_blocks, v->n_blocks) - 1);
     a.bs_div = make_fastdiv((uint32_t)a.block_size);
     a.chunk_div = make_fastdiv((uint32_t)a.chunk);
@@ -478,13 +499,14 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     a.mfma = mfma ? 1 : 0;
     a.contig = (k->block_size % kSlice == 0 && is_aligned(k->norms, 16) && is_aligned(v->norms, 16)) ? 1 : 0;
     for (int i = 0; i < TQ_MAX_LEVELS; ++i) {
-        a.kc[i] = i < k->cb.n_levels ? k->cb.centroids[i] : 0.f;
+        a.kc[i] = !k_fp16 && i < k->cb.n_levels ? k->cb.centroids[i] : 0.f;
         a.vc[i] = i < v->cb.n_levels ? v->cb.centroids[i] : 0.f;
     }
     PairTables pt;
     memset(&pt, 0, sizeof(pt));
-    for (int e = 0; e < (1 << (2 * k->bits)); ++e)
-        pt.k[e] = half2_bits(a.kc[e & ((1 << k->bits) - 1)], a.kc[e >> k->bits]);
+    if (!k_fp16)
+        for (int e = 0; e < (1 << (2 * k->bits)); ++e)
+            pt.k[e] = half2_bits(a.kc[e & ((1 << k->bits) - 1)], a.kc[e >> k->bits]);
     for (int e = 0; e < (1 << (2 * v->bits)); ++e)
         pt.v[e] = half2_bits(a.vc[e & ((1 << v->bits) - 1)], a.vc[e >> v->bits]);
     hipEvent_t ev0 = events ? static_cast<hipEvent_t>(events[0]) : nullptr;

@@ -614,12 +614,15 @@ void launch_mfma_kb3(const DecodeArgs &a, const PairTables &pt, int mode, hipStr
                      hipEvent_t ev1);
 void launch_mfma_kb4(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
                      hipEvent_t ev1);
+void launch_mfma_kb16(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
+                      hipEvent_t ev1);
 
 static void launch_mfma_any(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s,
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
     switch (a.k_bits) {
         case 2: launch_mfma_kb2(a, pt, mode, s, ev0, ev1); break;
         case 3: launch_mfma_kb3(a, pt, mode, s, ev0, ev1); break;
+        case 16: launch_mfma_kb16(a, pt, mode, s, ev0, ev1); break;   // K float16
         default: launch_mfma_kb4(a, pt, mode, s, ev0, ev1); break;
     }
 }

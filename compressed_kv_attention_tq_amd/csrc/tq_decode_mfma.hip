@@ -221,8 +221,12 @@ void tq_decode_mfma_kernel(
     float *__restrict__ part_acc, float *__restrict__ tilemax) {
     constexpr bool DENSE = MODE == MODE_DENSE, SCORE = MODE == MODE_SCORE, GATED = MODE == MODE_GATED;
     constexpr bool WV = !SCORE;
-    constexpr int NKT = 1 << (2 * KB), NVT = 1 << (2 * VB);
-    constexpr int KROW = 16 * KB, VROW = 16 * VB;   // bytes per code row
+    // KF: the K side is plain float16 (KB = 16): its rows are the score MFMA's A
+    // operand as loaded, with no pair table, norm, signs or rotation of q
+    constexpr bool KF = KB == 16;
+    constexpr int NKT = KF ? 1 : 1 << (2 * KB), NVT = 1 << (2 * VB);
+    constexpr int KROW = 16 * KB, VROW = 16 * VB;   // bytes per code row (K float16: 256)
+    constexpr int KW = KF ? 16 : KB;                // K words per lane and 16-token tile
     constexpr int NQB = PK ? 4 : 8;                 // q'' B fragments
     constexpr int NPB = PK ? 2 : 4;                 // weight B fragments
     // the replicated K and V pair tables while slices are processed; afterwards the
@@ -231,7 +235,7 @@ void tq_decode_mfma_kernel(
     constexpr int KCOP = tab_copies<KB>(), VCOP = tab_copies<VB>();
     static_assert(KCOP == 32 && VCOP == 32, "32 copies of an entry fill half of a 256-byte row");
     constexpr int RB = WV ? 256 : 128;   // bytes per table row
-    constexpr int kTabWords = (WV ? (NKT > NVT ? NKT : NVT) : NKT) * (RB / 4);
+    constexpr int kTabWords = (WV ? (NKT > NVT ? NKT : NVT) : NKT) * (RB / 4);   // (KF: the V halves only)
     constexpr int kMerge = PK ? kMW * 8 * kD : 16 * kQS;
     constexpr int kArea = kTabWords > kMerge ? kTabWords : kMerge;
     __shared__ __attribute__((aligned(16))) uint32_t area[kArea];
@@ -268,7 +272,7 @@ void tq_decode_mfma_kernel(
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
         const int i = it * kMBlock + tid;
-        kent[it] = i < NKT * 4 ? pt.k[i >> 2] : 0u;
+        kent[it] = !KF && i < NKT * 4 ? pt.k[i >> 2] : 0u;
     }
     if constexpr (WV) {
 #pragma unroll
@@ -289,7 +293,8 @@ void tq_decode_mfma_kernel(
         qh0[i] = qp[lane];
         qh1[i] = qp[lane + 64];
     }
-    const uint32_t ksg0 = a.k_signs[kv * 4 + (lane >> 5)], ksg1 = a.k_signs[kv * 4 + 2 + (lane >> 5)];
+    const uint32_t ksg0 = KF ? 0u : a.k_signs[kv * 4 + (lane >> 5)];
+    const uint32_t ksg1 = KF ? 0u : a.k_signs[kv * 4 + 2 + (lane >> 5)];
     // the sequence length, through the vector path as well: a scalar load would
     // either hold up the loads above (scalar loads are waited for together) or,
     // issued later, queue behind the slice loads
@@ -327,7 +332,7 @@ void tq_decode_mfma_kernel(
     // (token = lane).  The dense and scoring passes keep two slots, so the next
     // slice's loads are in flight while a slice is computed.
     struct Slot {
-        uint32_t kw[4][KB];
+        uint32_t kw[4][KW];
         VUnit<VB> vw[2][8];
         float knl, vnl;
     };
@@ -350,18 +355,34 @@ void tq_decode_mfma_kernel(
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's row table is written
         __builtin_amdgcn_wave_barrier();
     };
+    // this lane's K words of one token for one 16-token tile: 4 KB code bytes, or
+    // (K float16) the 64 bytes of positions 32g .. 32g+31
+    auto load_kwords = [&](const uint8_t *p, uint32_t (&w)[KW]) __attribute__((always_inline)) {
+        if constexpr (KF) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 t = reinterpret_cast<const uint4 *>(p)[i];
+                w[4 * i] = t.x;
+                w[4 * i + 1] = t.y;
+                w[4 * i + 2] = t.z;
+                w[4 * i + 3] = t.w;
+            }
+        } else {
+            load_words<KB>(p, w);
+        }
+    };
     auto load_k = [&](Slot &sl, int64_t row0) __attribute__((always_inline)) {
         if constexpr (CONTIG) {
-            const uint8_t *p = k_codes + (row0 + n) * KROW + g * (4 * KB);
+            const uint8_t *p = k_codes + (row0 + n) * KROW + g * (4 * KW);
 #pragma unroll
-            for (int tm = 0; tm < 4; ++tm) load_words<KB>(p + tm * 16 * KROW, sl.kw[tm]);
-            sl.knl = k_norms[row0 + lane];
+            for (int tm = 0; tm < 4; ++tm) load_kwords(p + tm * 16 * KROW, sl.kw[tm]);
+            sl.knl = KF ? 1.f : k_norms[row0 + lane];
         } else {
             const int32_t *rt = rowtab[wave];
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
-                load_words<KB>(k_codes + (int64_t)rt[16 * tm + n] * KROW + g * (4 * KB), sl.kw[tm]);
-            sl.knl = k_norms[myrow];
+                load_kwords(k_codes + (int64_t)rt[16 * tm + n] * KROW + g * (4 * KW), sl.kw[tm]);
+            sl.knl = KF ? 1.f : k_norms[myrow];
         }
     };
     // V units of the slice's tokens; token (tile tm, e) of lane group g is loaded
@@ -439,9 +460,11 @@ void tq_decode_mfma_kernel(
         d[0] = u4_t{v, v, v, v};
         d[1] = u4_t{v, v, v, v};
     };
+    if constexpr (!KF) {
 #pragma unroll
-    for (int it = 0; it < KIT; ++it)
-        if (it * kMBlock + tid < NKT * 4) fill_entry(ktab, kent[it], it * kMBlock + tid);
+        for (int it = 0; it < KIT; ++it)
+            if (it * kMBlock + tid < NKT * 4) fill_entry(ktab, kent[it], it * kMBlock + tid);
+    }
     if constexpr (WV) {
 #pragma unroll
         for (int it = 0; it < VIT; ++it)
@@ -449,7 +472,7 @@ void tq_decode_mfma_kernel(
     }
     const uint32_t lane_off = (uint32_t)(lane & 31) << 2;
 
-    // ---- q'' = qscale * H (s_K * q) of this KV head's rows, into buf
+    // ---- q'' = qscale * H (s_K * q) of this KV head's rows (K float16: qscale * q), into buf
     {
         float qm = 0.f;
 #pragma unroll
@@ -460,7 +483,7 @@ void tq_decode_mfma_kernel(
             float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)qh1[i]);
             if ((ksg0 >> (lane & 31)) & 1u) x0 = -x0;
             if ((ksg1 >> (lane & 31)) & 1u) x1 = -x1;
-            hadamard128(x0, x1, lane);
+            if constexpr (!KF) hadamard128(x0, x1, lane);   // (K float16: q is not rotated)
             x0 *= a.qscale;
             x1 *= a.qscale;
             buf[r * kQS + lane] = x0;
@@ -570,7 +593,10 @@ void tq_decode_mfma_kernel(
             S[tm] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const u4_t af = k_frag<KB, RB>(sl.kw[tm], ks, ktab, lane_off);
+                u4_t af;
+                if constexpr (KF) af = u4_t{sl.kw[tm][4 * ks], sl.kw[tm][4 * ks + 1], sl.kw[tm][4 * ks + 2],
+                                            sl.kw[tm][4 * ks + 3]};
+                else af = k_frag<KB, RB>(sl.kw[tm], ks, ktab, lane_off);
                 S[tm] = mfma_f16(af, qb[ks], S[tm]);
                 if constexpr (!PK) S[tm] = mfma_f16(af, qb[4 + ks], S[tm]);
             }

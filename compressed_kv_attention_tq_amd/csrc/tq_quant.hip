@@ -72,8 +72,9 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
     const int tok_step = (int)fdiv((uint32_t)step, p.kv_div);
     const FastDiv bsdiv = p.bs_div;
 
-    // Sign flips of this lane's 16 elements as float16 sign-bit masks.
-    const uint32_t sb = (p.signs[head * 4 + (j >> 1)] >> ((j & 1) * 16)) & 0xFFFFu;
+    // Sign flips of this lane's 16 elements as float16 sign-bit masks (a float16
+    // side, BITS = 16, has no signs: its rows are stored as they come).
+    const uint32_t sb = BITS == 16 ? 0u : (p.signs[head * 4 + (j >> 1)] >> ((j & 1) * 16)) & 0xFFFFu;
     uint32_t smask[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
@@ -103,6 +104,18 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
     };
     auto encode = [&](const Group &gr, int g0) __attribute__((always_inline)) {
         const bool valid = g0 + L.vin < p.n_vec;
+        if constexpr (BITS == 16) {
+            const int64_t slot = gr.slot;
+            if (valid && slot >= 0) {
+                const uint32_t blk_id = fdiv((uint32_t)slot, bsdiv);
+                const uint32_t off = (uint32_t)slot - blk_id * (uint32_t)p.block_size;
+                const int64_t row = ((int64_t)blk_id * p.n_kv + head) * p.block_size + off;
+                uint4 *d = reinterpret_cast<uint4 *>(p.codes + row * 256 + 32 * j);
+                d[0] = make_uint4(gr.w[0], gr.w[1], gr.w[2], gr.w[3]);
+                d[1] = make_uint4(gr.w[4], gr.w[5], gr.w[6], gr.w[7]);
+            }
+            return;
+        }
         uint32_t w[8];
         float ss = 0.f;
 #pragma unroll
@@ -180,8 +193,10 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
         load(gr[d], tok0 + d * tok_step);
     }
     // the encode table is built while the first groups load
-    build_lut(p, lut);
-    __syncthreads();
+    if constexpr (BITS != 16) {
+        build_lut(p, lut);
+        __syncthreads();
+    }
     int tok = tok0;
     for (int i = 0; i < n_groups; i += kDepth, tok += kDepth * tok_step) {
 #pragma unroll
@@ -202,6 +217,7 @@ __global__ __launch_bounds__(256) void tq_quantize_kernel(QuantArgs a) {
     switch (p.bits) {
         case 2: quant_side<2>(p, a.slots, lut, blk, nblk); break;
         case 3: quant_side<3>(p, a.slots, lut, blk, nblk); break;
+        case 16: quant_side<16>(p, a.slots, lut, blk, nblk); break;   // float16 side
         default: quant_side<4>(p, a.slots, lut, blk, nblk); break;
     }
 }
@@ -209,6 +225,47 @@ __global__ __launch_bounds__(256) void tq_quantize_kernel(QuantArgs a) {
 // --------------------------------------------------------------------------
 // Dequantize: x_hat = n * s * (H c[code]) / sqrt(128), same lane layout.
 // --------------------------------------------------------------------------
+// A float16 side: the rows as stored (float16 or widened to float32).
+__global__ __launch_bounds__(256) void tq_dequantize_fp16_kernel(DequantArgs a) {
+    const Lane8 L = lane8();
+    const int j = L.j;
+    const int wpb = blockDim.x >> 6;
+    const int wave_id = blockIdx.x * wpb + (int)(threadIdx.x >> 6);
+    const int step = gridDim.x * wpb * 8;
+    for (int g0 = wave_id * 8; g0 < a.n_vec; g0 += step) {
+        const int vid = g0 + L.vin;
+        if (vid >= a.n_vec) continue;
+        const int tok = (int)fdiv((uint32_t)vid, a.kv_div);
+        const int head = vid - tok * a.n_kv;
+        const uint32_t slot = (uint32_t)a.slots[tok];
+        const uint32_t blk_id = fdiv(slot, a.bs_div);
+        const uint32_t off = slot - blk_id * (uint32_t)a.block_size;
+        const int64_t row = ((int64_t)blk_id * a.n_kv + head) * a.block_size + off;
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.codes + row * 256 + 32 * j);
+        const uint4 x0 = src[0], x1 = src[1];
+        const int64_t dbase = ((int64_t)tok * a.n_kv + head) * kD + 16 * j;
+        if (a.dst_fp16) {
+            uint4 *d = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.dst) + dbase);
+            d[0] = x0;
+            d[1] = x1;
+        } else {
+            const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            float o[16];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const half2_t h = __builtin_bit_cast(half2_t, w[k]);
+                o[2 * k] = (float)h.x;
+                o[2 * k + 1] = (float)h.y;
+            }
+            float4 *d = reinterpret_cast<float4 *>(static_cast<float *>(a.dst) + dbase);
+            d[0] = make_float4(o[0], o[1], o[2], o[3]);
+            d[1] = make_float4(o[4], o[5], o[6], o[7]);
+            d[2] = make_float4(o[8], o[9], o[10], o[11]);
+            d[3] = make_float4(o[12], o[13], o[14], o[15]);
+        }
+    }
+}
+
 template <int BITS>
 __global__ __launch_bounds__(256) void tq_dequantize_kernel(DequantArgs a) {
     __shared__ float ctab[TQ_MAX_LEVELS];
@@ -308,6 +365,7 @@ hipError_t launch_dequantize(const DequantArgs &a, int bits, hipStream_t s) {
     switch (bits) {
         case 2: hipLaunchKernelGGL(tq_dequantize_kernel<2>, dim3(blocks), dim3(256), 0, s, a); break;
         case 3: hipLaunchKernelGGL(tq_dequantize_kernel<3>, dim3(blocks), dim3(256), 0, s, a); break;
+        case 16: hipLaunchKernelGGL(tq_dequantize_fp16_kernel, dim3(blocks), dim3(256), 0, s, a); break;
         default: hipLaunchKernelGGL(tq_dequantize_kernel<4>, dim3(blocks), dim3(256), 0, s, a); break;
     }
     return hipGetLastError();

@@ -21,6 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtq.so")
 
 HEAD_DIM = 128
+BITS_FP16 = 16   # a cache side kept in float16 (TQ_BITS_FP16)
 MAX_LEVELS = 16
 MAX_ROWS_PER_KV_HEAD = 16
 
@@ -180,6 +181,8 @@ class Cache:
         norms = torch.zeros((n_blocks, n_kv_heads, block_size), dtype=torch.float32, device=device)
         sw = np.ascontiguousarray(np.asarray(sign_words, dtype=np.uint32).reshape(n_kv_heads, 4))
         signs = torch.from_numpy(sw.view(np.int32)).to(device)
+        if bits == BITS_FP16:
+            cb = TQCodebook()   # a float16 side has no codebook
         return cls(bits, n_kv_heads, block_size, n_blocks, codes, norms, signs,
                    tq_build_codebook(bits) if cb is None else cb)
 

@@ -157,6 +157,13 @@ def llama8b(seed: int = 0, context: int = 32768) -> DecodeWorkload:
                           np.array([context], np.int32), table, nb, "llama8b", seed)
 
 
+def llama8b_k16(seed: int = 0, context: int = 32768) -> DecodeWorkload:
+    """The Llama-3-8B-shaped decode with K kept in float16 and V at 3 bits."""
+    table, nb = _identity_table(1, context, 256)
+    return DecodeWorkload("llama8b_k16", 1, 1, 32, 8, 16, 3, 0.0, 256,
+                          np.array([context], np.int32), table, nb, "llama8b", seed)
+
+
 def longctx(seed: int = 0, context: int = 131072, batch: int = 4) -> DecodeWorkload:
     table, nb = _identity_table(batch, context, 256)
     return DecodeWorkload("longctx", batch, 1, 40, 4, 3, 2, 1e-4, 256,

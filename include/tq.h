@@ -65,6 +65,7 @@ typedef enum tq_status {
 
 #define TQ_HEAD_DIM 128
 #define TQ_MAX_LEVELS 16
+#define TQ_BITS_FP16 16   /* a cache side kept in float16: see tq_cache */
 #define TQ_MAX_ROWS_PER_KV_HEAD 16   /* (n_q_heads / n_kv_heads) * n_qtok */
 
 /* Scalar codebook of one cache side ([TQ blog] 3.3).  Centroids are the Lloyd-Max
@@ -83,7 +84,14 @@ typedef struct tq_codebook {
  * of an identity page table.  Descriptor lives in host memory; the arrays it
  * points to are device memory owned by the caller. */
 typedef struct tq_cache {
-    int32_t  bits;          /* 2, 3 or 4; must equal cb.bits */
+    int32_t  bits;          /* 2, 3 or 4; must equal cb.bits.  Or TQ_BITS_FP16: the side
+                               keeps its rows as float16 (the "f16 K, turbo V" start of
+                               the [TQ+ README] usage steps; [TQ+ article] deployment
+                               advice): codes holds [n_blocks][n_kv_heads][block_size][128]
+                               float16 (256 bytes a row, 16*bits as for the others), and
+                               norms, signs and cb are not used (norms and signs may be
+                               NULL).  Only a K side may be float16 in tq_decode_attention,
+                               which then scores q . k directly (no rotation of q). */
     int32_t  n_kv_heads;    /* >= 1 */
     int32_t  head_dim;      /* must be 128 */
     int32_t  block_size;    /* tokens per page, >= 1 */

@@ -65,6 +65,10 @@ Readings taken where the pages are silent (each one also listed in the design doc):
   R8  Sparse V: with p the exact, final, normalised softmax weight, position t
       contributes p_t * v_hat_t iff p_t >= tau; skipped positions count as zero
       and the kept weights are not renormalised.  tau = 0 is dense attention.
+  R11 A side kept in float16 (the [TQ+ README] usage steps start from f16 K
+      with turbo V; the [TQ+ article] deployment advice starts from a light
+      asymmetric setting): the row is stored as its 128 float16 values and read
+      back exactly; attention scores it as scale * q . k with no rotation.
 """
 
 from __future__ import annotations
@@ -82,7 +86,7 @@ __all__ = [
     "gaussian_lloyd_max", "lloyd_max_from_samples", "Codebook", "build_codebook", "fit_codebook",
     "codebook_mse", "encode", "near_boundary_mask", "quantize_vectors",
     "pack_codes", "unpack_codes", "dequantize_vectors", "OracleCache",
-    "new_cache", "cache_write", "cache_read", "slots_for_sequence",
+    "new_cache", "cache_write", "cache_read", "slots_for_sequence", "FP16",
     "decode_attention_rows", "decode_attention", "bits_per_value",
 ]
 
@@ -376,7 +380,11 @@ class OracleCache:
     cb: Codebook
 
 
+FP16 = 16  # bits of a side kept in float16 (R11): rows of 128 float16, no norm, no codebook
+
+
 def new_cache(bits, n_kv_heads, block_size, n_blocks, signs, cb) -> OracleCache:
+    """A zeroed paged cache side; bits = FP16 keeps float16 rows (256 bytes each)."""
     return OracleCache(bits, n_kv_heads, block_size, n_blocks,
                        np.zeros((n_blocks, n_kv_heads, block_size, 16 * bits), np.uint8),
                        np.zeros((n_blocks, n_kv_heads, block_size), np.float32),
@@ -392,6 +400,13 @@ def cache_write(cache: OracleCache, src: np.ndarray, slots: np.ndarray):
     src = np.asarray(src)
     slots = np.asarray(slots, dtype=np.int64)
     n_tok = src.shape[0]
+    if cache.bits == FP16:   # R11: the row itself, byte for byte
+        rows = np.ascontiguousarray(src.astype(np.float16)).view(np.uint8).reshape(n_tok, cache.n_kv_heads, 2 * D)
+        for t in range(n_tok):
+            if slots[t] >= 0:
+                blk, off = divmod(int(slots[t]), cache.block_size)
+                cache.codes[blk, :, off, :] = rows[t]
+        return None
     norms = np.zeros((n_tok, cache.n_kv_heads), np.float32)
     codes = np.zeros((n_tok, cache.n_kv_heads, D), np.uint8)
     ys = np.zeros((n_tok, cache.n_kv_heads, D), np.float64)
@@ -419,6 +434,8 @@ def cache_read(cache: OracleCache, slots: np.ndarray, head: int) -> np.ndarray:
     """Dequantized float64 vectors [len(slots), 128] of one KV head."""
     slots = np.asarray(slots, dtype=np.int64)
     blk, off = slots // cache.block_size, slots % cache.block_size
+    if cache.bits == FP16:   # R11
+        return np.ascontiguousarray(cache.codes[blk, head, off, :]).view(np.float16).astype(np.float64)
     packed = cache.codes[blk, head, off, :]
     norms = cache.norms[blk, head, off]
     codes = unpack_codes(packed, cache.bits)

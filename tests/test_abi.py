@@ -221,3 +221,27 @@ def test_fit_codebook_rejects_bad_arguments():
     assert ok(3, 4, 1, 10, out=None) == T.TQ_ERR_INVALID_ARG
     z = np.zeros((4, 128), np.float16)
     assert ok(3, 4, 1, 10, v=z) == T.TQ_ERR_INVALID_ARG     # no nonzero vector
+
+
+def test_float16_side_validation(monkeypatch):
+    """A float16 side needs no norms, signs or codebook; only K may be float16 in
+    decode, and only with the matrix-core pass."""
+    monkeypatch.delenv("TQ_DECODE_KERNEL", raising=False)
+    k16 = fake_cache(bits=T.BITS_FP16)
+    k16.norms, k16.signs = None, None
+    st, need = decode_call(k=k16)
+    assert st == T.TQ_OK and need > 0
+    assert decode_call(k=k16, tau=1e-3)[0] == T.TQ_OK
+    assert decode_call(v=fake_cache(bits=T.BITS_FP16))[0] == T.TQ_ERR_UNSUPPORTED
+    assert decode_call(k=fake_cache(bits=8))[0] == T.TQ_ERR_UNSUPPORTED
+    monkeypatch.setenv("TQ_DECODE_KERNEL", "valu")
+    assert decode_call(k=k16)[0] == T.TQ_ERR_UNSUPPORTED
+    monkeypatch.delenv("TQ_DECODE_KERNEL")
+    # a compressed side still needs its norms, signs and codebook
+    k4 = fake_cache()
+    k4.norms = None
+    assert decode_call(k=k4)[0] == T.TQ_ERR_INVALID_ARG
+    # quantize / dequantize accept a float16 side with no norms or signs
+    lib = T.load_library()
+    assert lib.tq_quantize_kv(ctypes.byref(k16), FAKE, None, None, 2 * 128, 0, None, None) == T.TQ_OK
+    assert lib.tq_dequantize(ctypes.byref(k16), FAKE, 0, FAKE, 0, None) == T.TQ_OK

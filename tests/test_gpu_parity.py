@@ -178,6 +178,30 @@ def test_quantize_with_fitted_codebook(bits):
     log(f"fitted {bits}-bit: near-boundary {near}")
 
 
+@pytest.mark.parametrize("n_kv,n_tok", [(1, 5), (8, 300), (3, 77)])
+def test_float16_side_store_and_read(n_kv, n_tok):
+    """A float16 side stores each row's bytes in its slot and reads them back exactly."""
+    torch = _t()
+    rng = np.random.default_rng(n_kv * 1000 + n_tok)
+    x = (rng.standard_normal((n_tok, n_kv, 128)) * 8).astype(np.float16)
+    bs = 16
+    n_blocks = -(-n_tok // bs) + 2
+    slots = rng.permutation(n_blocks * bs)[:n_tok].astype(np.int64)
+    slots[1::9] = -1
+    g = T.Cache.allocate(T.BITS_FP16, n_kv, bs, n_blocks, np.zeros((n_kv, 4), np.uint32))
+    g.codes.fill_(0xAB)
+    T.tq_quantize_kv(g, torch.from_numpy(x).cuda(), None, None, torch.from_numpy(slots).cuda())
+    rows = g.codes.cpu().numpy().transpose(0, 2, 1, 3).reshape(-1, n_kv, 256)
+    ok = slots >= 0
+    want = np.ascontiguousarray(x).view(np.uint8).reshape(n_tok, n_kv, 256)
+    assert np.array_equal(rows[slots[ok]], want[ok])
+    untouched = np.setdiff1d(np.arange(rows.shape[0]), slots[ok])
+    assert np.all(rows[untouched] == 0xAB)
+    rd = torch.from_numpy(slots[ok]).cuda()
+    assert np.array_equal(T.tq_dequantize(g, rd, fp16=True).cpu().numpy(), x[ok])
+    assert np.array_equal(T.tq_dequantize(g, rd).cpu().numpy(), x[ok].astype(np.float32))
+
+
 # --------------------------------------------------------------------------- dequantize
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
@@ -293,6 +317,43 @@ def test_decode_with_fitted_codebooks(kernel):
 
     ok, ov = _memo(("fitted",) + _wl_key(wl), build)
     decode_and_compare(wl, gpu_caches=(ok, ov, U.gpu_cache_from(ok), U.gpu_cache_from(ov)), oracle_key="fitted")
+
+
+def _skip_valu_for_fp16_k(kernel):
+    if kernel == "valu":
+        pytest.skip("float16 K runs on the matrix-core pass only (the vector-ALU pass rejects it)")
+
+
+@pytest.mark.parametrize("case", [
+    # (n_seqs, lens, n_qtok, n_q_heads, n_kv_heads, v_bits, block_size)
+    (1, [700], 1, 4, 1, 3, 256),
+    (2, [1000, 33], 1, 32, 8, 2, 256),
+    (2, [300, 129], 4, 16, 4, 4, 64),
+    (3, [77, 5, 260], 2, 8, 1, 3, 16),
+])
+def test_decode_float16_k(case, kernel):
+    """K kept in float16, V compressed ([TQ+ README] f16 K with turbo V)."""
+    _skip_valu_for_fp16_k(kernel)
+    n_seqs, lens, n_qtok, hq, hkv, vb, bs = case
+    wl = W.small_decode(seed=sum(lens) + vb, n_seqs=n_seqs, lens=lens, n_qtok=n_qtok, n_q_heads=hq,
+                        n_kv_heads=hkv, k_bits=T.BITS_FP16, v_bits=vb, block_size=bs)
+    decode_and_compare(wl)
+
+
+@pytest.mark.parametrize("tau", [1e-4, 3e-2, 1.5])
+def test_decode_float16_k_sparse(tau, kernel):
+    _skip_valu_for_fp16_k(kernel)
+    wl = W.small_decode(seed=41, n_seqs=2, lens=[2500, 700], n_qtok=2, n_q_heads=8, n_kv_heads=2,
+                        k_bits=T.BITS_FP16, v_bits=2, tau=tau, block_size=256)
+    out, _ = decode_and_compare(wl)
+    if tau > 1:
+        assert np.all(out == 0)
+
+
+def test_decode_float16_k_llama8b_full(kernel):
+    """The Llama-3-8B-shaped decode (32768 tokens, 32 / 8 heads) with float16 K and 3-bit V."""
+    _skip_valu_for_fp16_k(kernel)
+    decode_and_compare(W.llama8b_k16())
 
 
 def test_decode_custom_scale(kernel):

@@ -468,3 +468,35 @@ def test_fit_codebook_skips_zero_vectors():
     a, _, _ = O.fit_codebook(3, x, sw)
     b, _, _ = O.fit_codebook(3, np.concatenate([x, np.zeros((9, 1, 128), np.float16)]), sw)
     assert np.array_equal(a.centroids, b.centroids)
+
+
+# --------------------------------------------------------------- float16 K side
+
+def test_float16_side_roundtrip_and_attention():
+    """R11: a float16 side stores the row's bytes and reads them back exactly; with a
+    float16 K side, attention is softmax(scale q . k) over the visible positions
+    against the dequantized V, written out here directly."""
+    rng = np.random.default_rng(3)
+    n_kv, bs, n_tok, G = 2, 16, 37, 3
+    k = (rng.standard_normal((n_tok, n_kv, 128)) * 4).astype(np.float16)
+    v = rng.standard_normal((n_tok, n_kv, 128)).astype(np.float16)
+    sv = rng.integers(0, 2 ** 32, size=(n_kv, 4), dtype=np.uint64).astype(np.uint32)
+    kc = O.new_cache(O.FP16, n_kv, bs, 4, np.zeros((n_kv, 4), np.uint32), None)
+    vc = O.new_cache(3, n_kv, bs, 4, sv, O.build_codebook(3))
+    table = np.array([[2, 0, 3]], np.int32)
+    slots = O.slots_for_sequence(table[0], bs, n_tok)
+    O.cache_write(kc, k, slots)
+    O.cache_write(vc, v, slots)
+    for h in range(n_kv):
+        assert np.array_equal(O.cache_read(kc, slots, h), k[:, h].astype(np.float64))
+    q = rng.standard_normal((1, 2, n_kv * G, 128)).astype(np.float16)
+    out = O.decode_attention(q, kc, vc, np.array([n_tok], np.int32), table, 2, 0.0, 0.0)
+    for j in range(2):
+        for h in range(n_kv * G):
+            kv = h // G
+            t_vis = n_tok - 2 + j + 1
+            s = (q[0, j, h].astype(np.float64) @ k[:t_vis, kv].astype(np.float64).T) / math.sqrt(128)
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            v_hat = O.cache_read(vc, slots[:t_vis], kv)
+            assert np.allclose(out[0, j, h], p @ v_hat, rtol=1e-12, atol=1e-12)
