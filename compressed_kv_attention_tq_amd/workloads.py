@@ -27,6 +27,9 @@ model here, so these synthetic tensors stand in for real K/V activations):
   ragged    64 sequences, lengths uniform in [4096, 65536], 32 q / 8 KV heads,
             4 query tokens per sequence (speculative verify); K 4-bit, V 4-bit;
             256-token pages in a seeded random physical order, table padded -1.
+  llama8b_d256, llama8b_d512
+            the llama8b decode with heads of 256 / 512 elements (two / four
+            128-element blocks, each with its own sign words).
 """
 
 from __future__ import annotations
@@ -67,6 +70,11 @@ class DecodeWorkload:
     n_blocks: int
     kind: str                   # value recipe: tiny | llama8b | normal | longctx
     seed: int = 0
+    head_dim: int = HEAD_DIM    # a multiple of 128: head_dim / 128 blocks per head
+
+    @property
+    def blocks_per_head(self) -> int:
+        return self.head_dim // HEAD_DIM
 
     @property
     def group(self) -> int:
@@ -74,35 +82,36 @@ class DecodeWorkload:
 
     @cached_property
     def signs_k(self) -> np.ndarray:
-        return random_sign_words(_rng(self.seed, _KEY_SIGNS_K), self.n_kv_heads)
+        """uint32 [n_kv_heads * blocks_per_head, 4]: the words of block i of head j in row nb j + i."""
+        return random_sign_words(_rng(self.seed, _KEY_SIGNS_K), self.n_kv_heads * self.blocks_per_head)
 
     @cached_property
     def signs_v(self) -> np.ndarray:
-        return random_sign_words(_rng(self.seed, _KEY_SIGNS_V), self.n_kv_heads)
+        return random_sign_words(_rng(self.seed, _KEY_SIGNS_V), self.n_kv_heads * self.blocks_per_head)
 
     @cached_property
     def _k_channel_scales(self) -> np.ndarray:
         # llama8b: sigma_c ~ lognormal(0, 1) per (KV head, channel), fixed across tokens
-        return _rng(self.seed, _KEY_SCALES).lognormal(0.0, 1.0, size=(self.n_kv_heads, HEAD_DIM))
+        return _rng(self.seed, _KEY_SCALES).lognormal(0.0, 1.0, size=(self.n_kv_heads, self.head_dim))
 
     @cached_property
     def _outlier_channels(self):
         r = _rng(self.seed, _KEY_OUTL)
-        return (r.choice(HEAD_DIM, size=4, replace=False), r.choice(HEAD_DIM, size=4, replace=False))
+        return (r.choice(self.head_dim, size=4, replace=False), r.choice(self.head_dim, size=4, replace=False))
 
     def _anchor_plan(self, seq: int):
         """longctx: per KV head an anchor, 64 planted positions and their noise."""
         r = _rng(self.seed, _KEY_KV, seq, 1)
         length = int(self.seq_lens[seq])
-        anchors = r.standard_normal((self.n_kv_heads, HEAD_DIM))
+        anchors = r.standard_normal((self.n_kv_heads, self.head_dim))
         pos = np.stack([r.choice(length, size=64, replace=False) for _ in range(self.n_kv_heads)])
         return anchors, pos, r
 
     def kv_source(self, seq: int):
-        """float16 K and V of one sequence: [seq_len, n_kv_heads, 128] each."""
+        """float16 K and V of one sequence: [seq_len, n_kv_heads, head_dim] each."""
         length = int(self.seq_lens[seq])
         r = _rng(self.seed, _KEY_KV, seq, 0)
-        shape = (length, self.n_kv_heads, HEAD_DIM)
+        shape = (length, self.n_kv_heads, self.head_dim)
         k = r.standard_normal(shape)
         v = r.standard_normal(shape)
         if self.kind == "tiny":
@@ -114,13 +123,13 @@ class DecodeWorkload:
         elif self.kind == "longctx":
             anchors, pos, ra = self._anchor_plan(seq)
             for h in range(self.n_kv_heads):
-                k[pos[h], h, :] = anchors[h] + 0.1 * ra.standard_normal((64, HEAD_DIM))
+                k[pos[h], h, :] = anchors[h] + 0.1 * ra.standard_normal((64, self.head_dim))
         return k.astype(np.float16), v.astype(np.float16)
 
     def queries(self) -> np.ndarray:
-        """float16 [n_seqs, n_qtok, n_q_heads, 128]."""
+        """float16 [n_seqs, n_qtok, n_q_heads, head_dim]."""
         r = _rng(self.seed, _KEY_Q)
-        q = r.standard_normal((self.n_seqs, self.n_qtok, self.n_q_heads, HEAD_DIM))
+        q = r.standard_normal((self.n_seqs, self.n_qtok, self.n_q_heads, self.head_dim))
         if self.kind == "longctx":
             for b in range(self.n_seqs):
                 anchors, _, _ = self._anchor_plan(b)
@@ -162,6 +171,14 @@ def llama8b_k16(seed: int = 0, context: int = 32768) -> DecodeWorkload:
     table, nb = _identity_table(1, context, 256)
     return DecodeWorkload("llama8b_k16", 1, 1, 32, 8, 16, 3, 0.0, 256,
                           np.array([context], np.int32), table, nb, "llama8b", seed)
+
+
+def llama8b_wide(head_dim: int, seed: int = 0, context: int = 32768) -> DecodeWorkload:
+    """The Llama-3-8B-shaped decode (heads, context, value recipe, K 4-bit / V 3-bit)
+    with heads of head_dim = 256 or 512 elements."""
+    table, nb = _identity_table(1, context, 256)
+    return DecodeWorkload(f"llama8b_d{head_dim}", 1, 1, 32, 8, 4, 3, 0.0, 256,
+                          np.array([context], np.int32), table, nb, "llama8b", seed, head_dim)
 
 
 def longctx(seed: int = 0, context: int = 131072, batch: int = 4) -> DecodeWorkload:
@@ -221,7 +238,7 @@ def prefill(seed: int = 0) -> PrefillWorkload:
 
 def small_decode(seed: int, n_seqs: int, lens, n_qtok: int, n_q_heads: int, n_kv_heads: int,
                  k_bits: int, v_bits: int, tau: float = 0.0, block_size: int = 256,
-                 shuffle_pages: bool = True) -> DecodeWorkload:
+                 shuffle_pages: bool = True, head_dim: int = HEAD_DIM) -> DecodeWorkload:
     """A small ragged, paged workload with N(0,1) K/V/q for parity tests."""
     lens = np.asarray(lens, np.int32)
     max_blocks = max(1, int(-(-int(np.max(lens)) // block_size))) if n_seqs else 1
@@ -235,4 +252,4 @@ def small_decode(seed: int, n_seqs: int, lens, n_qtok: int, n_q_heads: int, n_kv
         table[b, : need[b]] = perm[at: at + need[b]]
         at += need[b]
     return DecodeWorkload("small", n_seqs, n_qtok, n_q_heads, n_kv_heads, k_bits, v_bits, tau,
-                          block_size, lens, table, n_blocks, "normal", seed)
+                          block_size, lens, table, n_blocks, "normal", seed, head_dim)

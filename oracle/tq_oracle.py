@@ -59,7 +59,7 @@ Readings taken where the pages are silent (each one also listed in the design doc):
       float64 y with the stored boundaries; a tie goes to the lower code.
   R6  Packing: LSB-first bitstream per 128-block; code i occupies stream bits
       [b*i, b*i + b); stream bit k is bit (k mod 8) of byte k // 8; 16*b bytes.
-  R7  Attention: scores scale * q . k_hat with scale 1/sqrt(128) unless given;
+  R7  Attention: scores scale * q . k_hat with scale 1/sqrt(head_dim) unless given;
       GQA maps query head h to KV head h // (H_q / H_kv); with n_qtok query
       tokens per sequence, query token j sees positions t <= len - n_qtok + j.
   R8  Sparse V: with p the exact, final, normalised softmax weight, position t
@@ -69,6 +69,13 @@ Readings taken where the pages are silent (each one also listed in the design doc):
       with turbo V; the [TQ+ article] deployment advice starts from a light
       asymmetric setting): the row is stored as its 128 float16 values and read
       back exactly; attention scores it as scale * q . k with no rotation.
+  R12 Heads wider than one block (the [TQ+ README] types note puts every turbo
+      format on 128-element blocks; its Metal row has flash attention for a
+      512-wide head): a head of head_dim = 128 * nb elements is nb consecutive
+      blocks, elements [128 i, 128 i + 128) forming block i, each quantized on
+      its own as in R1-R6 with its own norm and its own sign vector.  The cache
+      keeps block i of head j as sub-head nb * j + i; the dequantized head is the
+      concatenation of its blocks, and attention is R7 over the whole head.
 """
 
 from __future__ import annotations
@@ -374,43 +381,61 @@ class OracleCache:
     n_kv_heads: int
     block_size: int
     n_blocks: int
-    codes: np.ndarray   # uint8 [n_blocks, n_kv_heads, block_size, 16*bits]
-    norms: np.ndarray   # float32 [n_blocks, n_kv_heads, block_size]
-    signs: np.ndarray   # uint32 [n_kv_heads, 4]
+    codes: np.ndarray   # uint8 [n_blocks, n_sub, block_size, 16*bits]
+    norms: np.ndarray   # float32 [n_blocks, n_sub, block_size]
+    signs: np.ndarray   # uint32 [n_sub, 4]
     cb: Codebook
+    head_dim: int = D   # elements per head; n_sub = n_kv_heads * head_dim / 128 sub-heads (R12)
+
+    @property
+    def blocks_per_head(self) -> int:
+        return self.head_dim // D
+
+    @property
+    def n_sub(self) -> int:
+        return self.n_kv_heads * self.blocks_per_head
 
 
 FP16 = 16  # bits of a side kept in float16 (R11): rows of 128 float16, no norm, no codebook
 
 
-def new_cache(bits, n_kv_heads, block_size, n_blocks, signs, cb) -> OracleCache:
-    """A zeroed paged cache side; bits = FP16 keeps float16 rows (256 bytes each)."""
+def new_cache(bits, n_kv_heads, block_size, n_blocks, signs, cb, head_dim: int = D) -> OracleCache:
+    """A zeroed paged cache side; bits = FP16 keeps float16 rows (256 bytes each).
+
+    head_dim is a multiple of 128 (R12); signs hold one word quadruple per
+    sub-head, [n_kv_heads, head_dim / 128, 4] in any shape of that size.
+    """
+    if head_dim % D != 0 or head_dim < D:
+        raise ValueError("head_dim must be a positive multiple of 128")
+    n_sub = n_kv_heads * (head_dim // D)
     return OracleCache(bits, n_kv_heads, block_size, n_blocks,
-                       np.zeros((n_blocks, n_kv_heads, block_size, 16 * bits), np.uint8),
-                       np.zeros((n_blocks, n_kv_heads, block_size), np.float32),
-                       np.asarray(signs, np.uint32).reshape(n_kv_heads, 4), cb)
+                       np.zeros((n_blocks, n_sub, block_size, 16 * bits), np.uint8),
+                       np.zeros((n_blocks, n_sub, block_size), np.float32),
+                       np.asarray(signs, np.uint32).reshape(n_sub, 4), cb, head_dim)
 
 
 def cache_write(cache: OracleCache, src: np.ndarray, slots: np.ndarray):
-    """Quantize src [n_tokens, n_kv_heads, 128] (float16) into the cache slots.
+    """Quantize src [n_tokens, n_kv_heads, head_dim] (float16) into the cache slots.
 
     slot = block * block_size + offset; a negative slot skips that token.
-    Returns (norms, codes, y) of all rows for the caller's diagnostics.
+    Returns (norms, codes, y) of all rows, per sub-head, for the caller's diagnostics.
     """
     src = np.asarray(src)
     slots = np.asarray(slots, dtype=np.int64)
     n_tok = src.shape[0]
+    # R12: element 128 i + e of head j is element e of sub-head nb j + i
+    src = src.reshape(n_tok, cache.n_kv_heads, cache.blocks_per_head, D).reshape(n_tok, cache.n_sub, D)
     if cache.bits == FP16:   # R11: the row itself, byte for byte
-        rows = np.ascontiguousarray(src.astype(np.float16)).view(np.uint8).reshape(n_tok, cache.n_kv_heads, 2 * D)
+        rows = np.ascontiguousarray(src.astype(np.float16)).view(np.uint8).reshape(n_tok, cache.n_sub, 2 * D)
         for t in range(n_tok):
             if slots[t] >= 0:
                 blk, off = divmod(int(slots[t]), cache.block_size)
                 cache.codes[blk, :, off, :] = rows[t]
         return None
-    norms = np.zeros((n_tok, cache.n_kv_heads), np.float32)
-    codes = np.zeros((n_tok, cache.n_kv_heads, D), np.uint8)
-    ys = np.zeros((n_tok, cache.n_kv_heads, D), np.float64)
-    for h in range(cache.n_kv_heads):
+    norms = np.zeros((n_tok, cache.n_sub), np.float32)
+    codes = np.zeros((n_tok, cache.n_sub, D), np.uint8)
+    ys = np.zeros((n_tok, cache.n_sub, D), np.float64)
+    for h in range(cache.n_sub):
         s = sign_vector(cache.signs[h])
         nh, ch, yh = quantize_vectors(src[:, h, :], s, cache.cb)
         norms[:, h], codes[:, h], ys[:, h] = nh, ch, yh
@@ -430,16 +455,23 @@ def slots_for_sequence(block_table_row: np.ndarray, block_size: int, n_tokens: i
     return np.asarray(block_table_row, np.int64)[t // block_size] * block_size + t % block_size
 
 
+def _read_sub(cache: OracleCache, blk: np.ndarray, off: np.ndarray, sub: int) -> np.ndarray:
+    """Dequantized float64 128-vectors of one sub-head at the given (page, offset)s."""
+    if cache.bits == FP16:   # R11
+        return np.ascontiguousarray(cache.codes[blk, sub, off, :]).view(np.float16).astype(np.float64)
+    packed = cache.codes[blk, sub, off, :]
+    norms = cache.norms[blk, sub, off]
+    codes = unpack_codes(packed, cache.bits)
+    return dequantize_vectors(norms, codes, sign_vector(cache.signs[sub]), cache.cb)
+
+
 def cache_read(cache: OracleCache, slots: np.ndarray, head: int) -> np.ndarray:
-    """Dequantized float64 vectors [len(slots), 128] of one KV head."""
+    """Dequantized float64 vectors [len(slots), head_dim] of one KV head: the
+    concatenation of its blocks (R12)."""
     slots = np.asarray(slots, dtype=np.int64)
     blk, off = slots // cache.block_size, slots % cache.block_size
-    if cache.bits == FP16:   # R11
-        return np.ascontiguousarray(cache.codes[blk, head, off, :]).view(np.float16).astype(np.float64)
-    packed = cache.codes[blk, head, off, :]
-    norms = cache.norms[blk, head, off]
-    codes = unpack_codes(packed, cache.bits)
-    return dequantize_vectors(norms, codes, sign_vector(cache.signs[head]), cache.cb)
+    nb = cache.blocks_per_head
+    return np.concatenate([_read_sub(cache, blk, off, nb * head + i) for i in range(nb)], axis=1)
 
 
 # ---------------------------------------------------------------------------
@@ -451,13 +483,13 @@ def decode_attention_rows(q_rows: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarr
                           n_visible: np.ndarray, scale: float, tau: float):
     """Attention of several query rows over one KV head's dequantized tokens.
 
-    q_rows [R, 128] float64, k_hat / v_hat [T, 128] float64, row r sees the first
-    n_visible[r] tokens.  Returns (out [R, 128], list of weight vectors p_r).
+    q_rows [R, d] float64, k_hat / v_hat [T, d] float64, row r sees the first
+    n_visible[r] tokens.  Returns (out [R, d], list of weight vectors p_r).
       s_t = scale * q . k_hat_t ;  p = exp(s - max s) / sum exp(s - max s)
       out = sum_{t : p_t >= tau} p_t v_hat_t     (tau = 0: every t)
     Rows that see no token return zeros.
     """
-    out = np.zeros((q_rows.shape[0], D), dtype=np.float64)
+    out = np.zeros((q_rows.shape[0], v_hat.shape[1]), dtype=np.float64)
     ps = []
     for r in range(q_rows.shape[0]):
         n = int(n_visible[r])
@@ -478,16 +510,18 @@ def decode_attention(q: np.ndarray, kc: OracleCache, vc: OracleCache, seq_lens,
                      seqs=None, kv_heads=None, return_weights: bool = False):
     """Decode attention over the paged caches, float64.
 
-    q [n_seqs, n_qtok, H_q, 128] (float16 values); seq_lens include the n_qtok
+    q [n_seqs, n_qtok, H_q, head_dim] (float16 values); seq_lens include the n_qtok
     new tokens; block_table [n_seqs, max_blocks].  Returns out with the shape of
     q (float64); only the requested sequences / KV heads are filled (others 0).
     """
     q = np.asarray(q).astype(np.float64)
-    n_seqs, _, hq, _ = q.shape
+    n_seqs, _, hq, hd = q.shape
+    if hd != kc.head_dim or hd != vc.head_dim:
+        raise ValueError("q, K and V must share head_dim")
     hkv = kc.n_kv_heads
     g = hq // hkv
     if scale == 0.0:
-        scale = 1.0 / math.sqrt(D)
+        scale = 1.0 / math.sqrt(hd)
     out = np.zeros_like(q)
     weights = {}
     seqs = range(n_seqs) if seqs is None else seqs

@@ -35,7 +35,7 @@ def oracle_cache(wl, side, seqs=None, n_blocks=None, cb=None):
     signs = wl.signs_k if side == 0 else wl.signs_v
     if bits != O.FP16:
         cb = O.build_codebook(bits) if cb is None else cb
-    c = O.new_cache(bits, wl.n_kv_heads, wl.block_size, n_blocks or wl.n_blocks, signs, cb)
+    c = O.new_cache(bits, wl.n_kv_heads, wl.block_size, n_blocks or wl.n_blocks, signs, cb, head_dim=wl.head_dim)
     for b in (range(wl.n_seqs) if seqs is None else seqs):
         if int(wl.seq_lens[b]) == 0:
             continue
@@ -48,7 +48,7 @@ def gpu_cache_from(oc, device="cuda"):
     """A device cache holding exactly the oracle cache's codes, norms and codebook."""
     t = torch()
     g = T.Cache.allocate(oc.bits, oc.n_kv_heads, oc.block_size, oc.n_blocks, oc.signs, device,
-                         cb=None if oc.bits == O.FP16 else tq_codebook_from(oc.cb))
+                         cb=None if oc.bits == O.FP16 else tq_codebook_from(oc.cb), head_dim=oc.head_dim)
     g.codes.copy_(t.from_numpy(oc.codes))
     g.norms.copy_(t.from_numpy(oc.norms))
     return g

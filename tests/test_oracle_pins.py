@@ -500,3 +500,93 @@ def test_float16_side_roundtrip_and_attention():
             p /= p.sum()
             v_hat = O.cache_read(vc, slots[:t_vis], kv)
             assert np.allclose(out[0, j, h], p @ v_hat, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------- heads of several blocks (R12)
+
+@pytest.mark.parametrize("head_dim", [256, 512])
+def test_wide_head_is_independent_blocks(head_dim):
+    """R12: block i of head j is the 128-slice [128 i, 128 i + 128) quantized on its
+    own with sign words signs[j, i]; changing one slice changes only its block."""
+    rng = np.random.default_rng(11)
+    nb, n_kv, bs, n_tok = head_dim // 128, 3, 8, 13
+    x = (rng.standard_normal((n_tok, n_kv, head_dim)) * 3).astype(np.float16)
+    sw = rng.integers(0, 2 ** 32, size=(n_kv, nb, 4), dtype=np.uint64).astype(np.uint32)
+    cb = O.build_codebook(3)
+    c = O.new_cache(3, n_kv, bs, 2, sw, cb, head_dim=head_dim)
+    slots = O.slots_for_sequence(np.array([1, 0]), bs, n_tok)
+    O.cache_write(c, x, slots)
+    for j in range(n_kv):
+        got = O.cache_read(c, slots, j)
+        assert got.shape == (n_tok, head_dim)
+        for i in range(nb):
+            s = O.sign_vector(sw[j, i])
+            n, codes, _ = O.quantize_vectors(x[:, j, 128 * i:128 * (i + 1)], s, cb)
+            want = O.dequantize_vectors(n, codes, s, cb)
+            np.testing.assert_array_equal(got[:, 128 * i:128 * (i + 1)], want)
+    # locality: a new last block leaves every other block as it was
+    x2 = x.copy()
+    x2[:, :, head_dim - 128:] = (rng.standard_normal((n_tok, n_kv, 128)) * 7).astype(np.float16)
+    c2 = O.new_cache(3, n_kv, bs, 2, sw, cb, head_dim=head_dim)
+    O.cache_write(c2, x2, slots)
+    for j in range(n_kv):
+        a, b = O.cache_read(c, slots, j), O.cache_read(c2, slots, j)
+        np.testing.assert_array_equal(a[:, :head_dim - 128], b[:, :head_dim - 128])
+        assert not np.array_equal(a[:, head_dim - 128:], b[:, head_dim - 128:])
+
+
+def test_wide_head_attention_reduces_to_one_block():
+    """With q zero outside block 0, 256-wide attention scores equal the 128-wide
+    scores of block 0 (same explicit scale); output block 0 is then the 128-wide
+    attention over the V block-0 cache and output block 1 the same weights applied
+    to the V block-1 cache."""
+    rng = np.random.default_rng(12)
+    n_kv, G, bs, n_tok = 2, 2, 16, 41
+    k = rng.standard_normal((n_tok, n_kv, 256)).astype(np.float16)
+    v = rng.standard_normal((n_tok, n_kv, 256)).astype(np.float16)
+    sk = rng.integers(0, 2 ** 32, size=(n_kv, 2, 4), dtype=np.uint64).astype(np.uint32)
+    sv = rng.integers(0, 2 ** 32, size=(n_kv, 2, 4), dtype=np.uint64).astype(np.uint32)
+    cbk, cbv = O.build_codebook(4), O.build_codebook(2)
+    table = np.array([[2, 0, 1]], np.int32)
+    slots = O.slots_for_sequence(table[0], bs, n_tok)
+
+    def cache(bits, cb, src, sw, hd):
+        c = O.new_cache(bits, n_kv, bs, 3, sw, cb, head_dim=hd)
+        O.cache_write(c, src, slots)
+        return c
+
+    kc, vc = cache(4, cbk, k, sk, 256), cache(2, cbv, v, sv, 256)
+    k0 = cache(4, cbk, k[:, :, :128], sk[:, 0], 128)
+    v0 = cache(2, cbv, v[:, :, :128], sv[:, 0], 128)
+    v1 = cache(2, cbv, v[:, :, 128:], sv[:, 1], 128)
+    q = np.zeros((1, 1, n_kv * G, 256), np.float16)
+    q[..., :128] = rng.standard_normal((1, 1, n_kv * G, 128)).astype(np.float16)
+    lens = np.array([n_tok], np.int32)
+    wide = O.decode_attention(q, kc, vc, lens, table, 1, scale=0.3)
+    narrow0 = O.decode_attention(q[..., :128], k0, v0, lens, table, 1, scale=0.3)
+    narrow1 = O.decode_attention(q[..., :128], k0, v1, lens, table, 1, scale=0.3)
+    np.testing.assert_allclose(wide[..., :128], narrow0, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(wide[..., 128:], narrow1, rtol=1e-12, atol=1e-13)
+
+
+def test_wide_head_two_tokens_closed_form_default_scale():
+    """Two tokens, head_dim 512: p0 = 1 / (1 + e^(s1 - s0)) with s = q . k_hat / sqrt(512)
+    (the default scale is 1/sqrt(head_dim)); the wide float16 side reads back exactly."""
+    rng = np.random.default_rng(13)
+    k = rng.standard_normal((2, 1, 512)).astype(np.float16)
+    v = rng.standard_normal((2, 1, 512)).astype(np.float16)
+    kc = O.new_cache(O.FP16, 1, 4, 1, np.zeros((1, 4, 4), np.uint32), None, head_dim=512)
+    vc = O.new_cache(4, 1, 4, 1, rng.integers(0, 2 ** 32, size=(4, 4), dtype=np.uint64).astype(np.uint32),
+                     O.build_codebook(4), head_dim=512)
+    slots = np.array([0, 1])
+    O.cache_write(kc, k, slots)
+    O.cache_write(vc, v, slots)
+    kh = O.cache_read(kc, slots, 0)
+    np.testing.assert_array_equal(kh, k[:, 0].astype(np.float64))
+    vh = O.cache_read(vc, slots, 0)
+    q = rng.standard_normal((1, 1, 1, 512)).astype(np.float16)
+    qq = q[0, 0, 0].astype(np.float64)
+    s0, s1 = kh @ qq / math.sqrt(512)
+    p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    out = O.decode_attention(q, kc, vc, [2], np.array([[0]]), 1)
+    np.testing.assert_allclose(out[0, 0, 0], p0 * vh[0] + (1 - p0) * vh[1], rtol=1e-12, atol=1e-14)
