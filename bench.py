@@ -102,7 +102,8 @@ class HipEvents:
 
 def decode_workload(name):
     return {"llama8b": W.llama8b, "llama8b_k16": W.llama8b_k16, "longctx": W.longctx, "ragged": W.ragged,
-            "tiny": W.tiny}[name]()
+            "tiny": W.tiny, "llama8b_d256": lambda: W.llama8b_wide(256),
+            "llama8b_d512": lambda: W.llama8b_wide(512)}[name]()
 
 
 def gen_kv_device(wl, b, torch, gen):
@@ -110,8 +111,8 @@ def gen_kv_device(wl, b, torch, gen):
     workload (2.2 M tokens), whose N(0,1) K/V come from a seeded device generator."""
     if wl.kind == "normal":
         n = int(wl.seq_lens[b])
-        k = torch.randn((n, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
-        v = torch.randn((n, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
+        k = torch.randn((n, wl.n_kv_heads, wl.head_dim), generator=gen, device="cuda").half()
+        v = torch.randn((n, wl.n_kv_heads, wl.head_dim), generator=gen, device="cuda").half()
         return k, v
     k, v = wl.kv_source(b)
     return torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
@@ -119,16 +120,16 @@ def gen_kv_device(wl, b, torch, gen):
 
 def run_decode(args, torch):
     wl = decode_workload(args.workload)
-    kb, vb = wl.k_bits, wl.v_bits
-    per_tok = cache_bytes_per_token_head(kb) + cache_bytes_per_token_head(vb)
+    kb, vb, hd, hb = wl.k_bits, wl.v_bits, wl.head_dim, wl.blocks_per_head
+    per_tok = hb * (cache_bytes_per_token_head(kb) + cache_bytes_per_token_head(vb))   # one token of one head
     cache_bytes = wl.total_tokens * wl.n_kv_heads * per_tok
     reps = args.replicas or min(64, max(1, math.ceil(1.5 * LLC_BYTES / cache_bytes)))
     log(f"[bench] workload {wl.name}: {wl.n_seqs} seqs, {wl.total_tokens} tokens, cache {cache_bytes / 1e6:.1f} MB, "
         f"{reps} replicas")
 
     nb = wl.n_blocks
-    kc = T.Cache.allocate(kb, wl.n_kv_heads, wl.block_size, nb * reps, wl.signs_k)
-    vc = T.Cache.allocate(vb, wl.n_kv_heads, wl.block_size, nb * reps, wl.signs_v)
+    kc = T.Cache.allocate(kb, wl.n_kv_heads, wl.block_size, nb * reps, wl.signs_k, head_dim=hd)
+    vc = T.Cache.allocate(vb, wl.n_kv_heads, wl.block_size, nb * reps, wl.signs_v, head_dim=hd)
     gen = torch.Generator(device="cuda").manual_seed(0)
     tables = []
     for r in range(reps):
@@ -149,8 +150,8 @@ def run_decode(args, torch):
     # the new tokens of each step: the last n_qtok positions of every sequence
     q = torch.from_numpy(wl.queries()).cuda()
     n_new = wl.n_seqs * wl.n_qtok
-    k_new = torch.randn((n_new, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
-    v_new = torch.randn((n_new, wl.n_kv_heads, 128), generator=gen, device="cuda").half()
+    k_new = torch.randn((n_new, wl.n_kv_heads, hd), generator=gen, device="cuda").half()
+    v_new = torch.randn((n_new, wl.n_kv_heads, hd), generator=gen, device="cuda").half()
     new_slots = []
     for r in range(reps):
         s = []
@@ -159,7 +160,7 @@ def run_decode(args, torch):
             s.extend(sl[-wl.n_qtok:].tolist() if len(sl) >= wl.n_qtok else [-1] * wl.n_qtok)
         new_slots.append(torch.tensor(s, dtype=torch.int64, device="cuda"))
     lens = torch.from_numpy(wl.seq_lens).cuda()
-    out = torch.empty((wl.n_seqs, wl.n_qtok, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    out = torch.empty((wl.n_seqs, wl.n_qtok, wl.n_q_heads, hd), dtype=torch.float32, device="cuda")
     ws_bytes = T.decode_workspace_bytes(kc, vc, wl.n_seqs, wl.n_qtok, wl.n_q_heads, wl.block_table.shape[1],
                                         wl.tau)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
@@ -209,15 +210,15 @@ def run_decode(args, torch):
     # algorithmic bytes
     if wl.tau > 0:
         kept = 64 * wl.n_seqs * wl.n_kv_heads          # planted positions kept per (seq, KV head)
-        cache_step = wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb) + \
-            kept * cache_bytes_per_token_head(vb)
-        pass_bytes = wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb)
+        cache_step = hb * (wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb) +
+                           kept * cache_bytes_per_token_head(vb))
+        pass_bytes = hb * wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb)
     else:
         cache_step = cache_bytes
         pass_bytes = cache_bytes
-    qo = wl.n_seqs * wl.n_qtok * wl.n_q_heads * 128 * (2 + 4)
+    qo = wl.n_seqs * wl.n_qtok * wl.n_q_heads * hd * (2 + 4)
     meta = wl.n_seqs * 4 + wl.block_table.size * 4
-    append = n_new * wl.n_kv_heads * (2 * 256 + per_tok) + n_new * 8
+    append = n_new * wl.n_kv_heads * (2 * 2 * hd + per_tok) + n_new * 8
     step_bytes = cache_step + qo + meta + append
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
@@ -232,7 +233,7 @@ def run_decode(args, torch):
             "kernel": kernel + (" (scoring pass)" if wl.tau > 0 else ""), "bytes_per_launch": pass_bytes,
             "avg_launch_us": round(pass_ms * 1e3, 2)}
     cfg = {"workload": f"{wl.name}: {wl.n_seqs} seq x {int(wl.seq_lens.max())} tokens, "
-                       f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d=128, K{kb}/V{vb}, "
+                       f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d={hd}, K{kb}/V{vb}, "
                        f"{wl.n_qtok} query token(s), tau={wl.tau}, page {wl.block_size}",
            "global_batch": wl.n_seqs, "seq_len": int(wl.seq_lens.max()), "replicas": reps,
            "launch": "HIP graph replay", "ms_per_step_eager": round(ms_step_eager, 5),
@@ -372,14 +373,15 @@ def cpu_baseline(wl, budget_s=12.0):
     k, v = wl.kv_source(b)
     slots = wl.slots(b)
     q = wl.queries()
-    per_tok = cache_bytes_per_token_head(wl.k_bits) + cache_bytes_per_token_head(wl.v_bits)
+    hb = wl.blocks_per_head
+    per_tok = hb * (cache_bytes_per_token_head(wl.k_bits) + cache_bytes_per_token_head(wl.v_bits))
     lens1, table1 = wl.seq_lens[:1], wl.block_table[:1]
     prepared = []
     for kv in range(wl.n_kv_heads):   # the context before the new tokens (not timed)
-        kcache = O.new_cache(wl.k_bits, 1, wl.block_size, wl.n_blocks, wl.signs_k[kv:kv + 1],
-                             O.build_codebook(wl.k_bits))
-        vcache = O.new_cache(wl.v_bits, 1, wl.block_size, wl.n_blocks, wl.signs_v[kv:kv + 1],
-                             O.build_codebook(wl.v_bits))
+        kcache = O.new_cache(wl.k_bits, 1, wl.block_size, wl.n_blocks, wl.signs_k[kv * hb:(kv + 1) * hb],
+                             None if wl.k_bits == 16 else O.build_codebook(wl.k_bits), head_dim=wl.head_dim)
+        vcache = O.new_cache(wl.v_bits, 1, wl.block_size, wl.n_blocks, wl.signs_v[kv * hb:(kv + 1) * hb],
+                             O.build_codebook(wl.v_bits), head_dim=wl.head_dim)
         O.cache_write(kcache, k[:-wl.n_qtok, kv:kv + 1], slots[:-wl.n_qtok])
         O.cache_write(vcache, v[:-wl.n_qtok, kv:kv + 1], slots[:-wl.n_qtok])
         prepared.append((kcache, vcache, q[:1, :, kv * wl.group:(kv + 1) * wl.group]))
@@ -393,7 +395,7 @@ def cpu_baseline(wl, budget_s=12.0):
         O.decode_attention(qh, kcache, vcache, lens1, table1, wl.n_qtok, 0.0, wl.tau)
         spent += time.perf_counter() - t0
         units += 1
-        done_bytes += length * per_tok + wl.n_qtok * (2 * 256 + per_tok) + qh.size * 6
+        done_bytes += length * per_tok + wl.n_qtok * (2 * 2 * wl.head_dim + per_tok) + qh.size * 6
     gbs = done_bytes / spent / 1e9
     log(f"[bench] cpu oracle: {units} (KV head, step) units of seq 0 in {spent:.1f} s -> {gbs:.4f} GB/s, "
         f"{cores} threads")
@@ -407,7 +409,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "llama8b_k16", "longctx", "ragged", "tiny"])
+    ap.add_argument("--workload", default="llama8b",
+                    choices=["llama8b", "llama8b_k16", "llama8b_d256", "llama8b_d512", "longctx", "ragged", "tiny"])
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--quantize-reps", type=int, default=5)
     ap.add_argument("--no-quantize", action="store_true")

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
 # (source, object name, extra flags): the decode pass kernels are built once per
-# K bit width so the slow unit compiles in parallel.
+# K bit width (and blocks per head) so the slow units compile in parallel.
 SOURCES = [
     ("tq_api.cpp", "tq_api", []),
     ("tq_quant.hip", "tq_quant", []),
@@ -29,10 +29,10 @@ SOURCES = [
     ("tq_decode.hip", "tq_decode_kb2", ["-DTQ_DECODE_KB=2"]),
     ("tq_decode.hip", "tq_decode_kb3", ["-DTQ_DECODE_KB=3"]),
     ("tq_decode.hip", "tq_decode_kb4", ["-DTQ_DECODE_KB=4"]),
-    ("tq_decode_mfma.hip", "tq_decode_mfma_kb2", ["-DTQ_DECODE_KB=2"]),
-    ("tq_decode_mfma.hip", "tq_decode_mfma_kb3", ["-DTQ_DECODE_KB=3"]),
-    ("tq_decode_mfma.hip", "tq_decode_mfma_kb4", ["-DTQ_DECODE_KB=4"]),
-    ("tq_decode_mfma.hip", "tq_decode_mfma_kb16", ["-DTQ_DECODE_KB=16"]),   # K float16
+] + [
+    # matrix-core pass: K bits (16 = K float16) x 128-element blocks per head
+    ("tq_decode_mfma.hip", f"tq_decode_mfma_kb{kb}_nb{nb}", [f"-DTQ_DECODE_KB={kb}", f"-DTQ_DECODE_NB={nb}"])
+    for kb in (4, 3, 2, 16) for nb in (1, 2, 4)
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

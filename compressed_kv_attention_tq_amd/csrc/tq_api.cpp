@@ -66,9 +66,16 @@ tq_status check_codebook(const tq_codebook &cb, int bits) {
     return TQ_OK;
 }
 
+// 128-element blocks per head; heads of 128, 256 or 512 elements are supported
+int blocks_per_head(const tq_cache *c) { return c->head_dim / TQ_HEAD_DIM; }
+
+// cache sub-heads: block i of head j is sub-head nb j + i
+int sub_heads(const tq_cache *c) { return c->n_kv_heads * blocks_per_head(c); }
+
 tq_status check_cache(const tq_cache *c) {
     if (!c) return TQ_ERR_INVALID_ARG;
-    if (c->head_dim != TQ_HEAD_DIM) return TQ_ERR_UNSUPPORTED;
+    if (c->head_dim != TQ_HEAD_DIM && c->head_dim != 2 * TQ_HEAD_DIM && c->head_dim != 4 * TQ_HEAD_DIM)
+        return TQ_ERR_UNSUPPORTED;
     const bool fp16 = c->bits == TQ_BITS_FP16;
     if (!fp16 && (c->bits < 2 || c->bits > 4)) return TQ_ERR_UNSUPPORTED;
     if (c->n_kv_heads < 1 || c->block_size < 1 || c->n_blocks < 1) return TQ_ERR_INVALID_ARG;
@@ -89,18 +96,19 @@ int quant_gpw(int n_kv) { return (n_kv > 0 && 8 % n_kv == 0) ? kQuantGroups : 0;
 // is a rotated unit vector).
 tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, int32_t n_tokens,
                           QuantSide &q) {
+    // (a head of several blocks is quantized as that many sub-heads of 128)
     if (c->bits == TQ_BITS_FP16) {   // the rows are stored as they come
         q.src = static_cast<const uint16_t *>(src);
         q.codes = c->codes;
         q.src_stride = stride;
-        q.n_vec = (int64_t)n_tokens * c->n_kv_heads;
+        q.n_vec = (int64_t)n_tokens * sub_heads(c);
         q.n_tokens = n_tokens;
-        q.gpw = quant_gpw(c->n_kv_heads);
-        q.n_kv = c->n_kv_heads;
+        q.gpw = quant_gpw(sub_heads(c));
+        q.n_kv = sub_heads(c);
         q.block_size = c->block_size;
         q.bits = c->bits;
         q.bs_div = make_fastdiv((uint32_t)c->block_size);
-        q.kv_div = make_fastdiv((uint32_t)c->n_kv_heads);
+        q.kv_div = make_fastdiv((uint32_t)sub_heads(c));
         return TQ_OK;
     }
     double min_gap = INFINITY;
@@ -117,16 +125,16 @@ tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, in
     q.norms = c->norms;
     q.signs = c->signs;
     q.src_stride = stride;
-    q.n_vec = (int64_t)n_tokens * c->n_kv_heads;
+    q.n_vec = (int64_t)n_tokens * sub_heads(c);
     q.n_tokens = n_tokens;
-    q.gpw = quant_gpw(c->n_kv_heads);
-    q.n_kv = c->n_kv_heads;
+    q.gpw = quant_gpw(sub_heads(c));
+    q.n_kv = sub_heads(c);
     q.block_size = c->block_size;
     q.bits = c->bits;
     q.grid = (float)grid;
     q.lut_half = grid + 2;
     q.bs_div = make_fastdiv((uint32_t)c->block_size);
-    q.kv_div = make_fastdiv((uint32_t)c->n_kv_heads);
+    q.kv_div = make_fastdiv((uint32_t)sub_heads(c));
     q.n_bnd = nb;
     for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) q.bnd[i] = i < nb ? c->cb.boundaries[i] : 0.f;
     return TQ_OK;
@@ -165,7 +173,8 @@ bool use_mfma_decode() {
 // Tokens per pass block: a multiple of the unit (one 64-token slice per wave),
 // doubled while at least kTargetBlocks blocks remain and at most 16384 tokens;
 // TQ_DECODE_CHUNK (a multiple of the unit) overrides it.
-DecodePlan plan_decode(int n_seqs, int n_kv, int rows, int max_blocks, int block_size, bool sparse, bool mfma) {
+DecodePlan plan_decode(int n_seqs, int n_kv, int nb, int rows, int max_blocks, int block_size, bool sparse,
+                       bool mfma) {
     DecodePlan p{};
     p.rows = rows;
     if (mfma) p.rows_pad = rows <= 8 ? 8 : 16;
@@ -186,8 +195,8 @@ DecodePlan plan_decode(int n_seqs, int n_kv, int rows, int max_blocks, int block
     const size_t units = (size_t)n_seqs * n_kv;
     size_t off = 0;
     p.off_qrot = off;  if (!mfma) off = align256(off + units * kD * p.rows_pad * sizeof(float));
-    p.off_ml = off;    off = align256(off + units * p.n_chunks * p.rows_pad * 2 * sizeof(float));
-    p.off_acc = off;   off = align256(off + units * p.n_chunks * p.rows_pad * kD * sizeof(float));
+    p.off_ml = off;    off = align256(off + units * p.n_chunks * p.rows_pad * nb * 2 * sizeof(float));
+    p.off_acc = off;   off = align256(off + units * p.n_chunks * p.rows_pad * nb * kD * sizeof(float));
     p.off_tile = off;  if (sparse) off = align256(off + units * p.n_tiles * p.rows_pad * sizeof(float));
     p.off_stats = off; if (sparse && !mfma) off = align256(off + units * p.rows_pad * 2 * sizeof(float));
     p.total = off;
@@ -350,22 +359,23 @@ tq_status tq_quantize_kv(const tq_cache *k, const void *k_src, const tq_cache *v
     const void *srcs[2] = {k_src, v_src};
     QuantArgs a;
     memset(&a, 0, sizeof(a));
-    int n_kv = -1;
+    int n_kv = -1, head_dim = -1;
     for (int i = 0; i < 2; ++i) {
         if (!sides[i]) continue;
         tq_status st = check_cache(sides[i]);
         if (st != TQ_OK) return st;
         if (!srcs[i] || !is_aligned(srcs[i], 16)) return TQ_ERR_INVALID_ARG;
         if (!is_aligned(sides[i]->codes, 8)) return TQ_ERR_INVALID_ARG;
-        if (n_kv >= 0 && n_kv != sides[i]->n_kv_heads) return TQ_ERR_INVALID_ARG;
+        if (n_kv >= 0 && (n_kv != sides[i]->n_kv_heads || head_dim != sides[i]->head_dim)) return TQ_ERR_INVALID_ARG;
         n_kv = sides[i]->n_kv_heads;
-        if (src_token_stride < (int64_t)n_kv * kD || src_token_stride % 8 != 0) return TQ_ERR_INVALID_ARG;
+        head_dim = sides[i]->head_dim;
+        if (src_token_stride < (int64_t)n_kv * head_dim || src_token_stride % 8 != 0) return TQ_ERR_INVALID_ARG;
         st = fill_quant_side(sides[i], srcs[i], src_token_stride, n_tokens, a.side[i]);
         if (st != TQ_OK) return st;
     }
     if (n_tokens == 0 || n_kv < 0) return TQ_OK;
     if (!slot_mapping) return TQ_ERR_INVALID_ARG;
-    if ((int64_t)n_tokens * n_kv > (1LL << 31) - (1LL << 20)) return TQ_ERR_UNSUPPORTED;
+    if ((int64_t)n_tokens * n_kv * (head_dim / kD) > (1LL << 31) - (1LL << 20)) return TQ_ERR_UNSUPPORTED;
     const int bk = quant_blocks(a.side[0].n_vec, std::max(1, a.side[0].n_kv));
     const int bv = quant_blocks(a.side[1].n_vec, std::max(1, a.side[1].n_kv));
     a.slots = slot_mapping;
@@ -381,7 +391,8 @@ tq_status tq_dequantize(const tq_cache *c, const int64_t *slots, int32_t n_token
     if (n_tokens < 0) return TQ_ERR_INVALID_ARG;
     if (n_tokens == 0) return TQ_OK;
     if (!slots || !dst || !is_aligned(dst, 16) || !is_aligned(c->codes, 8)) return TQ_ERR_INVALID_ARG;
-    if ((int64_t)n_tokens * c->n_kv_heads > (1LL << 31) - (1LL << 20)) return TQ_ERR_UNSUPPORTED;
+    if ((int64_t)n_tokens * sub_heads(c) > (1LL << 31) - (1LL << 20)) return TQ_ERR_UNSUPPORTED;
+    // a head of several blocks is that many sub-heads of 128: dst [n_tokens][n_kv][nb][128]
     DequantArgs a;
     memset(&a, 0, sizeof(a));
     a.codes = c->codes;
@@ -389,11 +400,11 @@ tq_status tq_dequantize(const tq_cache *c, const int64_t *slots, int32_t n_token
     a.signs = c->signs;
     a.slots = slots;
     a.dst = dst;
-    a.n_vec = (int64_t)n_tokens * c->n_kv_heads;
-    a.n_kv = c->n_kv_heads;
+    a.n_vec = (int64_t)n_tokens * sub_heads(c);
+    a.n_kv = sub_heads(c);
     a.block_size = c->block_size;
     a.dst_fp16 = dst_is_fp16 ? 1 : 0;
-    a.kv_div = make_fastdiv((uint32_t)c->n_kv_heads);
+    a.kv_div = make_fastdiv((uint32_t)sub_heads(c));
     a.bs_div = make_fastdiv((uint32_t)c->block_size);
     if (c->bits != TQ_BITS_FP16)
         for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = i < c->cb.n_levels ? c->cb.centroids[i] : 0.f;
@@ -421,10 +432,13 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     if (st != TQ_OK) return st;
     st = check_cache(v);
     if (st != TQ_OK) return st;
-    if (k->n_kv_heads != v->n_kv_heads || k->block_size != v->block_size) return TQ_ERR_INVALID_ARG;
-    // float16 K needs the matrix-core pass; V is always a compressed side
+    if (k->n_kv_heads != v->n_kv_heads || k->block_size != v->block_size || k->head_dim != v->head_dim)
+        return TQ_ERR_INVALID_ARG;
+    // float16 K and heads of several blocks need the matrix-core pass; V is always
+    // a compressed side
     const bool k_fp16 = k->bits == TQ_BITS_FP16;
-    if (v->bits == TQ_BITS_FP16 || (k_fp16 && !use_mfma_decode())) return TQ_ERR_UNSUPPORTED;
+    const int nb = blocks_per_head(k);
+    if (v->bits == TQ_BITS_FP16 || ((k_fp16 || nb > 1) && !use_mfma_decode())) return TQ_ERR_UNSUPPORTED;
     if (!is_aligned(v->codes, 4)) return TQ_ERR_INVALID_ARG;
     if (n_seqs < 0 || n_qtok < 1 || n_q_heads < 1 || max_blocks_per_seq < 1) return TQ_ERR_INVALID_ARG;
     if (n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
@@ -435,13 +449,13 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     if (rows > TQ_MAX_ROWS_PER_KV_HEAD) return TQ_ERR_UNSUPPORTED;
     if ((int64_t)max_blocks_per_seq * k->block_size > (1LL << 30)) return TQ_ERR_UNSUPPORTED;
     // cache rows are indexed with 32-bit integers on the device
-    if ((double)k->n_blocks * k->n_kv_heads * k->block_size > 2147483647.0 ||
-        (double)v->n_blocks * v->n_kv_heads * v->block_size > 2147483647.0)
+    if ((double)k->n_blocks * sub_heads(k) * k->block_size > 2147483647.0 ||
+        (double)v->n_blocks * sub_heads(v) * v->block_size > 2147483647.0)
         return TQ_ERR_UNSUPPORTED;
     const bool sparse = sparse_v_tau > 0.f;
     const bool mfma = use_mfma_decode();
-    const DecodePlan p = plan_decode(n_seqs, k->n_kv_heads, (int)rows, max_blocks_per_seq, k->block_size, sparse,
-                                     mfma);
+    const DecodePlan p = plan_decode(n_seqs, k->n_kv_heads, nb, (int)rows, max_blocks_per_seq, k->block_size,
+                                     sparse, mfma);
     if ((int64_t)n_seqs * k->n_kv_heads * p.n_chunks > 0x7FFFFFFFLL) return TQ_ERR_UNSUPPORTED;
     if (!workspace) {
         *workspace_bytes = n_seqs == 0 ? 0 : p.total;
@@ -482,7 +496,7 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     a.chunk = p.chunk;
     a.n_chunks = p.n_chunks;
     a.n_tiles = p.n_tiles;
-    const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)kD);
+    const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)k->head_dim);
     // q'' = scale log2(e) H (s q) / sqrt(128); float16 K scores q itself
     a.qscale = (float)(scale * M_LOG2E / (k_fp16 ? 1.0 : sqrt((double)kD)));
     a.max_page = (int32_t)(std::min(k->n_blocks, v->n_blocks) - 1);
@@ -496,6 +510,8 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     a.tau = sparse_v_tau;
     a.k_bits = k->bits;
     a.v_bits = v->bits;
+    a.nb = nb;
+    a.nb_log2 = nb == 4 ? 2 : nb == 2 ? 1 : 0;
     a.mfma = mfma ? 1 : 0;
     a.contig = (k->block_size % kSlice == 0 && is_aligned(k->norms, 16) && is_aligned(v->norms, 16)) ? 1 : 0;
     for (int i = 0; i < TQ_MAX_LEVELS; ++i) {

@@ -454,9 +454,10 @@ __global__ __launch_bounds__(256) void tq_stats_kernel(DecodeArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// Merge the chunk partials of one output row and inverse-rotate it (both pass
-// kernels write the same partial layout).  One block per row: 8 chunk groups x
-// 32 float4 columns.  Dense: each thread merges its chunks (c = group,
+// Merge the chunk partials of one 128-element block of one output row and
+// inverse-rotate it (both pass kernels write the same partial layout: per chunk
+// and row, (max, sum) per head block and the accumulator [block][128]).  One
+// block per (row, head block): 8 chunk groups x 32 float4 columns.  Dense: each thread merges its chunks (c = group,
 // group + 8, ...) with the log-sum-exp rule in batches of 16 loads, then the
 // groups are merged through LDS and o = s_V * H (acc / L) / sqrt(128).  Gated:
 // the partials are already normalised and are summed.
@@ -469,8 +470,10 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     __shared__ float y[kD];
     const int tid = threadIdx.x, lane = tid & 63;
     const int cg = tid >> 5, q4 = tid & 31;
-    const int bj = (int)fdiv(blockIdx.x, a.qh_div);        // b * n_qtok + jq
-    const int h = blockIdx.x - bj * a.n_q_heads;
+    const int nb = a.nb, hb = blockIdx.x & (nb - 1);      // head block (nb a power of two)
+    const uint32_t row_id = blockIdx.x >> a.nb_log2;
+    const int bj = (int)fdiv(row_id, a.qh_div);            // b * n_qtok + jq
+    const int h = (int)row_id - bj * a.n_q_heads;
     const int b = (int)fdiv((uint32_t)bj, a.qt_div);
     const int jq = bj - b * a.n_qtok;
     const int kv = (int)fdiv((uint32_t)h, a.grp_div);
@@ -478,9 +481,9 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     const int len = a.seq_lens[b];
     const int nc = len > 0 ? (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div) : 0;
     const int64_t base = ((int64_t)b * a.n_kv + kv) * a.n_chunks;
-    const int64_t mstride = (int64_t)a.rows_pad * 2, astride = (int64_t)a.rows_pad * kD;
-    const float *ml = a.part_ml + (base * a.rows_pad + r) * 2;          // chunk c at ml[c * mstride]
-    const float *pa = a.part_acc + (base * a.rows_pad + r) * kD + 4 * q4;  // chunk c at pa[c * astride]
+    const int64_t mstride = (int64_t)a.rows_pad * nb * 2, astride = (int64_t)a.rows_pad * nb * kD;
+    const float *ml = a.part_ml + ((base * a.rows_pad + r) * nb + hb) * 2;                // chunk c at ml[c * mstride]
+    const float *pa = a.part_acc + ((base * a.rows_pad + r) * nb + hb) * kD + 4 * q4;     // chunk c at pa[c * astride]
     float M = -INFINITY, L = 0.f;
     f4_t x = {0.f, 0.f, 0.f, 0.f};
     constexpr int kB = 16;   // chunks per thread per batch (one round of loads)
@@ -538,11 +541,11 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     // o = s_V * H acc / sqrt(128)
     float a0 = y[lane], a1 = y[lane + 64];
     hadamard128(a0, a1, lane);
-    const uint32_t *sg = a.v_signs + kv * 4;
+    const uint32_t *sg = a.v_signs + (kv * nb + hb) * 4;
     const float k = 0.088388347648318440550f;
     a0 *= ((sg[lane >> 5] >> (lane & 31)) & 1u) ? -k : k;
     a1 *= ((sg[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -k : k;
-    float *o = a.out + (((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * kD;
+    float *o = a.out + ((((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * nb + hb) * kD;
     o[lane] = a0;
     o[lane + 64] = a1;
 }
@@ -608,23 +611,32 @@ void TQ_CAT(launch_pass_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStre
 
 #else
 
-void launch_mfma_kb2(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
-                     hipEvent_t ev1);
-void launch_mfma_kb3(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
-                     hipEvent_t ev1);
-void launch_mfma_kb4(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
-                     hipEvent_t ev1);
-void launch_mfma_kb16(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
-                      hipEvent_t ev1);
+#define TQ_DECL_MFMA(KB, NB)                                                                                  \
+    void launch_mfma_kb##KB##_nb##NB(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s,        \
+                                     hipEvent_t ev0, hipEvent_t ev1);
+#define TQ_DECL_MFMA_KB(KB) TQ_DECL_MFMA(KB, 1) TQ_DECL_MFMA(KB, 2) TQ_DECL_MFMA(KB, 4)
+TQ_DECL_MFMA_KB(2)
+TQ_DECL_MFMA_KB(3)
+TQ_DECL_MFMA_KB(4)
+TQ_DECL_MFMA_KB(16)   // K float16
+#undef TQ_DECL_MFMA_KB
+#undef TQ_DECL_MFMA
 
 static void launch_mfma_any(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s,
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
-    switch (a.k_bits) {
-        case 2: launch_mfma_kb2(a, pt, mode, s, ev0, ev1); break;
-        case 3: launch_mfma_kb3(a, pt, mode, s, ev0, ev1); break;
-        case 16: launch_mfma_kb16(a, pt, mode, s, ev0, ev1); break;   // K float16
-        default: launch_mfma_kb4(a, pt, mode, s, ev0, ev1); break;
+#define TQ_CASE_NB(KB)                                                                  \
+    switch (a.nb) {                                                                     \
+        case 2: launch_mfma_kb##KB##_nb2(a, pt, mode, s, ev0, ev1); break;              \
+        case 4: launch_mfma_kb##KB##_nb4(a, pt, mode, s, ev0, ev1); break;              \
+        default: launch_mfma_kb##KB##_nb1(a, pt, mode, s, ev0, ev1); break;             \
     }
+    switch (a.k_bits) {
+        case 2: TQ_CASE_NB(2) break;
+        case 3: TQ_CASE_NB(3) break;
+        case 16: TQ_CASE_NB(16) break;
+        default: TQ_CASE_NB(4) break;
+    }
+#undef TQ_CASE_NB
 }
 
 static void launch_pass_any(const DecodeArgs &a, int mode, hipStream_t s, hipEvent_t ev0 = nullptr,
@@ -638,7 +650,7 @@ static void launch_pass_any(const DecodeArgs &a, int mode, hipStream_t s, hipEve
 
 hipError_t launch_decode(const DecodeArgs &a, const PairTables &pt, hipStream_t s, hipEvent_t ev_before,
                          hipEvent_t ev_after) {
-    const dim3 rows_grid((unsigned)((int64_t)a.n_seqs * a.n_qtok * a.n_q_heads));
+    const dim3 rows_grid((unsigned)((int64_t)a.n_seqs * a.n_qtok * a.n_q_heads * a.nb));   // x head blocks
     if (a.mfma) {   // q rotation runs inside the pass kernels
         if (a.tau > 0.f) {
             launch_mfma_any(a, pt, MODE_SCORE, s, ev_before, ev_after);

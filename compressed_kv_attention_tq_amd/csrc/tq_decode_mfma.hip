@@ -31,6 +31,16 @@
 // its own 64-token slices with private softmax state, loading the next slice's
 // codes while it computes, and the block's partial goes to the workspace for the
 // merge kernel.
+//
+// Heads of NB = head_dim / 128 > 1 blocks ([TQ+ README] types note: every format
+// works on 128-element blocks) are stored as NB sub-heads, block i of head j
+// being sub-head NB j + i with its own norms and sign words.  Wave w then takes
+// block w % NB of the slices of its group w / NB: the NB waves of a group load
+// the same tokens' codes of different blocks, each adds its block's partial scores
+// (q''_i . c_i times the block's norm) to an LDS exchange, and all of them read
+// back the sum in the same order, so they hold bitwise equal scores and softmax
+// state; each keeps the V accumulator of its own block.  Register use is that
+// of one block; the block's waves meet at two LDS barriers per slice.
 #include "tq_decode_common.h"
 
 namespace tq {
@@ -212,7 +222,15 @@ __device__ __forceinline__ u4_t v_frag(const uint32_t (&x)[4], const uint32_t (&
 template <bool PK, int VB, int MODE>
 constexpr int mfma_waves_per_eu() { return (PK && MODE != MODE_DENSE) ? 3 : 2; }
 
-template <int KB, int VB, bool PK, int MODE, bool CONTIG>
+// Barrier of the block's waves that orders their LDS accesses only: the global
+// loads in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int KB, int VB, bool PK, int MODE, bool CONTIG, int NB>
 __global__ __launch_bounds__(kMBlock) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<PK, VB, MODE>(), 8)))
 void tq_decode_mfma_kernel(
     DecodeArgs a, PairTables pt, const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
@@ -229,6 +247,9 @@ void tq_decode_mfma_kernel(
     constexpr int KW = KF ? 16 : KB;                // K words per lane and 16-token tile
     constexpr int NQB = PK ? 4 : 8;                 // q'' B fragments
     constexpr int NPB = PK ? 2 : 4;                 // weight B fragments
+    constexpr int NG = kMW / NB;                    // wave groups: slices the block has in flight
+    constexpr int NS = PK ? 32 : 64;                // exchange slots per tile and wave (lanes
+                                                    // holding distinct score columns)
     // the replicated K and V pair tables while slices are processed; afterwards the
     // waves' partials ([wave][row][128] for at most 8 rows, one [row][kQS]
     // accumulator otherwise)
@@ -236,13 +257,19 @@ void tq_decode_mfma_kernel(
     static_assert(KCOP == 32 && VCOP == 32, "32 copies of an entry fill half of a 256-byte row");
     constexpr int RB = WV ? 256 : 128;   // bytes per table row
     constexpr int kTabWords = (WV ? (NKT > NVT ? NKT : NVT) : NKT) * (RB / 4);   // (KF: the V halves only)
-    constexpr int kMerge = PK ? kMW * 8 * kD : 16 * kQS;
-    constexpr int kArea = kTabWords > kMerge ? kTabWords : kMerge;
+    // (NB > 1: q'' of every block, [block][row][kQS], passes through the area before
+    // the tables are written)
+    constexpr int kMerge = PK ? kMW * 8 * kD : NB * 16 * kQS;
+    constexpr int kQArea = NB > 1 ? NB * 16 * kQS : 0;
+    constexpr int kArea0 = kTabWords > kMerge ? kTabWords : kMerge;
+    constexpr int kArea = kArea0 > kQArea ? kArea0 : kQArea;
     __shared__ __attribute__((aligned(16))) uint32_t area[kArea];
     uint32_t *const ktab = area;
     uint32_t *const vtab = area + 32;   // V half of each row (RB = 256)
     float *const mbuf = reinterpret_cast<float *>(area);
-    __shared__ __attribute__((aligned(16))) float buf[16 * kQS];      // q'' during set-up
+    __shared__ __attribute__((aligned(16))) float buf[NB == 1 ? 16 * kQS : 4];   // q'' during set-up
+    // NB > 1: partial scores, [wave][tile][slot][4]
+    __shared__ __attribute__((aligned(16))) float xch[NB == 1 ? 4 : kMW * 4 * NS * 4];
     __shared__ __attribute__((aligned(16))) float nrm[kMW][2][64];     // per wave: K, V norms of the slice
     __shared__ float wst[kMW][16][2];
     __shared__ float red[kMW];
@@ -251,17 +278,19 @@ void tq_decode_mfma_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int blk = wave % NB, grp = wave / NB;   // head block and group of this wave
     const int unit = (int)fdiv(blockIdx.x, a.chunk_div_n);
     const int c = blockIdx.x - unit * a.n_chunks;
     const int b = (int)fdiv((uint32_t)unit, a.kv_div);
     const int kv = unit - b * a.n_kv;
     const int R = a.rows, rp = a.rows_pad;
     const int start = c * a.chunk;
-    const int bs = a.block_size, n_kv = a.n_kv;
+    const int bs = a.block_size;
+    const int n_sub = a.n_kv * NB, kvs = kv * NB + blk;   // cache sub-heads; this wave's
     const FastDiv bsdiv = a.bs_div;
     const int32_t *__restrict__ btab = block_table + (int64_t)b * a.max_blocks;
-    constexpr int kStride = kMW * 64;
-    const int first = start + wave * 64;
+    constexpr int kStride = NG * 64;
+    const int first = start + grp * 64;
 
     // Small loads go out first.  Vector loads complete in issue order, so loads
     // issued after the slice codes could only be used once those had arrived:
@@ -283,18 +312,19 @@ void tq_decode_mfma_kernel(
     }
     // (unconditional, from a row clamped into range: a load under a branch has its
     // conversion folded into the branch, which then waits for the load)
-    constexpr int kRowsPerWave = 16 / kMW;
+    // (the rows of this wave's block: rows grp, grp + NG, ...)
+    constexpr int kRowsPerWave = 16 / NG;
     uint32_t qh0[kRowsPerWave], qh1[kRowsPerWave];
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
-        const int r = min(wave + kMW * i, a.rows - 1);
+        const int r = min(grp + NG * i, a.rows - 1);
         const int jq = (int)fdiv((uint32_t)r, a.grp_div), h = kv * a.group + (r - jq * a.group);
-        const uint16_t *qp = qin + (((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * kD;
+        const uint16_t *qp = qin + (((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * (NB * kD) + blk * kD;
         qh0[i] = qp[lane];
         qh1[i] = qp[lane + 64];
     }
-    const uint32_t ksg0 = KF ? 0u : a.k_signs[kv * 4 + (lane >> 5)];
-    const uint32_t ksg1 = KF ? 0u : a.k_signs[kv * 4 + 2 + (lane >> 5)];
+    const uint32_t ksg0 = KF ? 0u : a.k_signs[kvs * 4 + (lane >> 5)];
+    const uint32_t ksg1 = KF ? 0u : a.k_signs[kvs * 4 + 2 + (lane >> 5)];
     // the sequence length, through the vector path as well: a scalar load would
     // either hold up the loads above (scalar loads are waited for together) or,
     // issued later, queue behind the slice loads
@@ -339,9 +369,9 @@ void tq_decode_mfma_kernel(
     Slot sa, sb;
     int myrow = 0;   // row of token base + lane (general page layout)
 
-    auto row0_of = [&](int base, int blk) __attribute__((always_inline)) -> int64_t {
+    auto row0_of = [&](int base, int page) __attribute__((always_inline)) -> int64_t {
         const int pg = (int)fdiv((uint32_t)base, bsdiv);
-        return ((int64_t)blk * n_kv + kv) * bs + (base - pg * bs);
+        return ((int64_t)page * n_sub + kvs) * bs + (base - pg * bs);
     };
     // general layout: the row of every token of the slice into the wave's table
     auto fill_rows = [&](int base, int blk_lane) __attribute__((always_inline)) {
@@ -349,7 +379,7 @@ void tq_decode_mfma_kernel(
         myrow = 0;
         if (t < end) {
             const int pg = (int)fdiv((uint32_t)t, bsdiv);
-            myrow = (blk_lane * n_kv + kv) * bs + (t - pg * bs);
+            myrow = (blk_lane * n_sub + kvs) * bs + (t - pg * bs);
         }
         rowtab[CONTIG ? 0 : wave][lane] = myrow;
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's row table is written
@@ -442,7 +472,7 @@ void tq_decode_mfma_kernel(
         if constexpr (CONTIG) {
             const int blk0 = __builtin_amdgcn_readfirstlane(vb0);
             const int pg = (int)fdiv((uint32_t)first, bsdiv);
-            r0_prev = ((int64_t)min(max(blk0, 0), a.max_page) * n_kv + kv) * bs + (first - pg * bs);
+            r0_prev = ((int64_t)min(max(blk0, 0), a.max_page) * n_sub + kvs) * bs + (first - pg * bs);
             load_k(sa, r0_prev);
             if constexpr (DENSE) load_v(sa, r0_prev, all_tokens);
             blk_next = vb1;
@@ -460,24 +490,29 @@ void tq_decode_mfma_kernel(
         d[0] = u4_t{v, v, v, v};
         d[1] = u4_t{v, v, v, v};
     };
-    if constexpr (!KF) {
+    auto fill_tables = [&]() __attribute__((always_inline)) {
+        if constexpr (!KF) {
 #pragma unroll
-        for (int it = 0; it < KIT; ++it)
-            if (it * kMBlock + tid < NKT * 4) fill_entry(ktab, kent[it], it * kMBlock + tid);
-    }
-    if constexpr (WV) {
+            for (int it = 0; it < KIT; ++it)
+                if (it * kMBlock + tid < NKT * 4) fill_entry(ktab, kent[it], it * kMBlock + tid);
+        }
+        if constexpr (WV) {
 #pragma unroll
-        for (int it = 0; it < VIT; ++it)
-            if (it * kMBlock + tid < NVT * 4) fill_entry(vtab, vent[it], it * kMBlock + tid);
-    }
+            for (int it = 0; it < VIT; ++it)
+                if (it * kMBlock + tid < NVT * 4) fill_entry(vtab, vent[it], it * kMBlock + tid);
+        }
+    };
+    if constexpr (NB == 1) fill_tables();   // (NB > 1: once q'' has left the area)
     const uint32_t lane_off = (uint32_t)(lane & 31) << 2;
 
-    // ---- q'' = qscale * H (s_K * q) of this KV head's rows (K float16: qscale * q), into buf
+    // ---- q'' = qscale * H (s_K * q) of this KV head's rows (K float16: qscale * q) for
+    // this wave's block, into qbuf
+    float *const qbuf = NB == 1 ? buf : reinterpret_cast<float *>(area) + blk * 16 * kQS;
     {
         float qm = 0.f;
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
-            const int r = wave + kMW * i;
+            const int r = grp + NG * i;
             if (r >= R) break;
             float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)qh0[i]);
             float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)qh1[i]);
@@ -486,24 +521,25 @@ void tq_decode_mfma_kernel(
             if constexpr (!KF) hadamard128(x0, x1, lane);   // (K float16: q is not rotated)
             x0 *= a.qscale;
             x1 *= a.qscale;
-            buf[r * kQS + lane] = x0;
-            buf[r * kQS + lane + 64] = x1;
+            qbuf[r * kQS + lane] = x0;
+            qbuf[r * kQS + lane + 64] = x1;
             qm = fmaxf(qm, fmaxf(fabsf(x0), fabsf(x1)));
         }
         qm = wave_max(qm);
         if (lane == 0) red[wave] = qm;
     }
     // sparse: global (max, sum) of each row from the scoring pass's chunk partials
+    // (part_ml is [chunk][row][block][2]; the blocks' entries are equal, block 0's is read)
     if constexpr (GATED) {
         const int nc = (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div);
-        const float *ml = part_ml + (int64_t)unit * a.n_chunks * rp * 2;
+        const float *ml = part_ml + (int64_t)unit * a.n_chunks * rp * NB * 2;
         for (int r = wave; r < R; r += kMW) {
             float m = -INFINITY;
-            for (int cc = lane; cc < nc; cc += 64) m = fmaxf(m, ml[(cc * rp + r) * 2]);
+            for (int cc = lane; cc < nc; cc += 64) m = fmaxf(m, ml[(cc * rp + r) * NB * 2]);
             const float M = wave_max(m);
             float l = 0.f;
             for (int cc = lane; cc < nc; cc += 64)
-                l += ml[(cc * rp + r) * 2 + 1] * exp2_diff(ml[(cc * rp + r) * 2], M);
+                l += ml[(cc * rp + r) * NB * 2 + 1] * exp2_diff(ml[(cc * rp + r) * NB * 2], M);
             const float L = wave_sum(l);
             if (lane == 0) {
                 gstat[r][0] = M;
@@ -515,7 +551,9 @@ void tq_decode_mfma_kernel(
 
     // q'' is scaled by a power of two so its largest element is in [2^13, 2^14)
     // (fp16 range and precision for both parts); scores are scaled back by kscale.
-    const float qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float qmax = red[blk];
+#pragma unroll
+    for (int g2 = 1; g2 < NG; ++g2) qmax = fmaxf(qmax, red[blk + NB * g2]);
     const int qex = qmax > 0.f ? max((int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127, -100) : 0;
     const float sq = __builtin_ldexpf(1.f, 13 - qex), kscale = __builtin_ldexpf(1.f, qex - 13);
 
@@ -526,7 +564,7 @@ void tq_decode_mfma_kernel(
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float *qr = &buf[col_row * kQS + 32 * g + 8 * ks + 2 * k];
+            const float *qr = &qbuf[col_row * kQS + 32 * g + 8 * ks + 2 * k];
             const float q0 = col_row < R ? qr[0] * sq : 0.f, q1 = col_row < R ? qr[1] * sq : 0.f;
             if constexpr (PK) {
                 qb[ks][k] = split_pair(q0, q1, losel);
@@ -535,6 +573,11 @@ void tq_decode_mfma_kernel(
                 qb[4 + ks][k] = split_pair(q0, q1, 1.f);
             }
         }
+    if constexpr (NB > 1) {
+        __syncthreads();   // every wave has its q'' fragments: the area takes the tables
+        fill_tables();
+        __syncthreads();
+    }
 
     const bool row_ok = col_row < R;
     // last position each row sees in this chunk (row r sees t <= len - n_qtok + r / G)
@@ -620,6 +663,32 @@ void tq_decode_mfma_kernel(
         const int ex = vm > 0.f ? (int)((__float_as_uint(vm) >> 23) & 0xFF) - 126 : -40;
         return (float)min(max(ex, -40), 40);
     };
+    // NB > 1: replace each partial score by the sum of the group's partials, blocks
+    // in ascending order (called by every wave of the block, the same number of
+    // times: it holds the block's barriers).  The first barrier keeps the previous
+    // exchange's reads ahead of this one's writes.  Lane (g, n) holds the scores of
+    // tokens 16 tm + 4 g + e for column n; with PK, columns n and n + 8 are equal
+    // and lanes n < 8 write.
+    const int xslot = PK ? 8 * g + (n & 7) : lane;
+    auto exchange = [&](float (&s)[4][4]) __attribute__((always_inline)) {
+        lds_barrier();
+        if (!PK || n < 8) {
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+                *reinterpret_cast<f4_t *>(&xch[((wave * 4 + tm) * NS + xslot) * 4]) =
+                    f4_t{s[tm][0], s[tm][1], s[tm][2], s[tm][3]};
+        }
+        lds_barrier();
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            f4_t t = *reinterpret_cast<const f4_t *>(&xch[(((grp * NB) * 4 + tm) * NS + xslot) * 4]);
+#pragma unroll
+            for (int j = 1; j < NB; ++j)
+                t += *reinterpret_cast<const f4_t *>(&xch[(((grp * NB + j) * 4 + tm) * NS + xslot) * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[tm][e] = t[e];
+        }
+    };
     // scores in the log2 domain, -inf where the row does not see the token
     // (full: every row sees every token of the slice)
     auto scores = [&](const f4_t (&S)[4], int base, bool full, float (&s)[4][4]) {
@@ -633,6 +702,7 @@ void tq_decode_mfma_kernel(
                 s[tm][e] = x * kn[e];
             }
         }
+        if constexpr (NB > 1) exchange(s);
         if (!full) {
             const int dl = lim - base - 4 * g;   // element (tm, e) visible iff 16 tm + e <= dl
 #pragma unroll
@@ -694,7 +764,8 @@ void tq_decode_mfma_kernel(
                 for (int e = 0; e < 4; ++e) wm = fmaxf(wm, s[tm][e]);
             wm = xg_max(wm);
             if constexpr (SCORE) {
-                if (g == 0 && row_ok && (!PK || n < 8)) tilemax[(tile0 + (base >> 6)) * rp + col_row] = wm;
+                if (g == 0 && row_ok && (!PK || n < 8) && blk == 0)
+                    tilemax[(tile0 + (base >> 6)) * rp + col_row] = wm;
             }
             const float m_new = fmaxf(m_raw, wm);
             const float E_new = DENSE ? fmaxf(E_run, E_s) : 0.f;
@@ -728,32 +799,50 @@ void tq_decode_mfma_kernel(
         // different loads outstanding, and every wait after it would then cover both
         // slots; skipping a compute (which issues no loads) does not
         // (the scheduling barriers keep each compute below the loads issued
-        // before it in the source, which it must not wait for)
-        for (int base = first; base < end; base += 2 * kStride) {
+        // before it in the source, which it must not wait for).
+        // NB > 1: the steps are the block's (b0 from the chunk start, the same in
+        // every wave, as the exchange's barriers need), each group's slice `lead`
+        // tokens in; a slice past the end has every score masked and changes nothing.
+        const int lead = first - start;
+        for (int b0 = NB == 1 ? first : start; b0 < end; b0 += 2 * kStride) {
+            const int base = NB == 1 ? b0 : b0 + lead;
             __builtin_amdgcn_sched_barrier(0);
             compute(sa, base);   // slot b holds base + kStride (in flight)
             issue(sa, base + 2 * kStride);
             __builtin_amdgcn_sched_barrier(0);
-            if (base + kStride < end) compute(sb, base + kStride);
+            if (b0 + kStride < end) compute(sb, base + kStride);
             issue(sb, base + 3 * kStride);
         }
     } else {
-        // ---------------- gated pass: candidate slices only
-        for (int base = first; base < end; base += kStride) {
-            const float tmx = row_ok ? tilemax[(tile0 + (base >> 6)) * rp + col_row] : -INFINITY;
-            if (!__ballot(tmx >= sthr)) continue;
+        // ---------------- gated pass: candidate slices only (a group's decision is
+        // the same in its NB waves; NB > 1: every wave takes part in each step's
+        // exchange, as in the dense loop)
+        const int lead = first - start;
+        for (int b0 = NB == 1 ? first : start; b0 < end; b0 += kStride) {
+            const int base = NB == 1 ? b0 : b0 + lead;
+            const float tmx = row_ok && base < end ? tilemax[(tile0 + (base >> 6)) * rp + col_row] : -INFINITY;
+            const bool cand = __ballot(tmx >= sthr) != 0ull;
+            if constexpr (NB == 1) {
+                if (!cand) continue;
+            }
             int64_t r0 = 0;
-            if constexpr (CONTIG) r0 = row0_of(base, btab[fdiv((uint32_t)base, bsdiv)]);
-            else fill_rows(base, page_of(btab, bsdiv, base + lane, end));
-            load_k(sa, r0);
-            if constexpr (CONTIG) sa.vnl = v_norms[r0 + lane];
-            else sa.vnl = v_norms[myrow];
-            const float E_s = stage_norms(sa, base);
-            f4_t S[4];
-            score_mfma(sa, S);
+            float E_s = 0.f;
+            f4_t S[4] = {};
+            if (cand) {
+                if constexpr (CONTIG) r0 = row0_of(base, btab[fdiv((uint32_t)base, bsdiv)]);
+                else fill_rows(base, page_of(btab, bsdiv, base + lane, end));
+                load_k(sa, r0);
+                if constexpr (CONTIG) sa.vnl = v_norms[r0 + lane];
+                else sa.vnl = v_norms[myrow];
+                E_s = stage_norms(sa, base);
+                score_mfma(sa, S);
+            }
             const bool full = base + 63 <= lim_all;
             float s[4][4];
             scores(S, base, full, s);
+            if constexpr (NB > 1) {
+                if (!cand) continue;
+            }
             // tokens kept by at least one row
             bool kept[4][4];
             uint64_t any = 0;
@@ -803,17 +892,18 @@ void tq_decode_mfma_kernel(
     __syncthreads();   // also: every wave is done with the pair tables
     const bool writer = row_ok && (!PK || n < 8);
     float scale = 1.f;
+    // (over the waves of this wave's block: one per group)
     if constexpr (!GATED) {
         float M = -INFINITY;
 #pragma unroll
-        for (int w2 = 0; w2 < kMW; ++w2) M = fmaxf(M, wst[w2][n][0]);
+        for (int g2 = 0; g2 < NG; ++g2) M = fmaxf(M, wst[blk + NB * g2][n][0]);
         scale = exp2_diff(m_state, M);
-        if (wave == 0 && g == 0 && writer) {
+        if (grp == 0 && g == 0 && writer) {
             float L = 0.f;
 #pragma unroll
-            for (int w2 = 0; w2 < kMW; ++w2) L += wst[w2][n][1] * exp2_diff(wst[w2][n][0], M);
-            part_ml[(part * rp + col_row) * 2] = M;
-            part_ml[(part * rp + col_row) * 2 + 1] = L;
+            for (int g2 = 0; g2 < NG; ++g2) L += wst[blk + NB * g2][n][1] * exp2_diff(wst[blk + NB * g2][n][0], M);
+            part_ml[((part * rp + col_row) * NB + blk) * 2] = M;
+            part_ml[((part * rp + col_row) * NB + blk) * 2 + 1] = L;
         }
     } else {
         scale = E_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(E_run);
@@ -827,74 +917,82 @@ void tq_decode_mfma_kernel(
                 for (int e = 0; e < 4; ++e) d[8 * (4 * g + e) + j] = acc[j][e] * scale;
         }
         __syncthreads();
-        for (int i = tid; i < R * kD; i += kMBlock) {
+        // part_acc rows are [row][block][128]
+        for (int i = tid; i < R * NB * kD; i += kMBlock) {
+            const int row = i / (NB * kD), pos = i - row * (NB * kD), bb = pos / kD, e = pos - bb * kD;
             float x = 0.f;
 #pragma unroll
-            for (int w2 = 0; w2 < kMW; ++w2) x += mbuf[w2 * 8 * kD + i];
-            part_acc[(part * rp + i / kD) * kD + i % kD] = x;
+            for (int g2 = 0; g2 < NG; ++g2) x += mbuf[((bb + NB * g2) * 8 + row) * kD + e];
+            part_acc[(part * rp + row) * (NB * kD) + pos] = x;
         }
     } else if constexpr (WV) {
-        for (int w2 = 0; w2 < kMW; ++w2) {
-            if (wave == w2 && writer) {
+        for (int g2 = 0; g2 < NG; ++g2) {
+            if (grp == g2 && writer) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float *d = &mbuf[col_row * kQS + 8 * (4 * g + e) + j];
-                        *d = (w2 == 0 ? 0.f : *d) + acc[j][e] * scale;
+                        float *d = &mbuf[(blk * 16 + col_row) * kQS + 8 * (4 * g + e) + j];
+                        *d = (g2 == 0 ? 0.f : *d) + acc[j][e] * scale;
                     }
             }
             __syncthreads();
         }
-        for (int i = tid; i < R * kD; i += kMBlock)
-            part_acc[(part * rp + i / kD) * kD + i % kD] = mbuf[(i / kD) * kQS + i % kD];
+        for (int i = tid; i < R * NB * kD; i += kMBlock) {
+            const int row = i / (NB * kD), pos = i - row * (NB * kD), bb = pos / kD, e = pos - bb * kD;
+            part_acc[(part * rp + row) * (NB * kD) + pos] = mbuf[(bb * 16 + row) * kQS + e];
+        }
     }
 }
 
 // --------------------------------------------------------------------------
-// Dispatch, one translation unit per K bit width (TQ_DECODE_KB = 2, 3, 4).
+// Dispatch, one translation unit per K bit width and blocks per head
+// (TQ_DECODE_KB = 2, 3, 4, 16; TQ_DECODE_NB = 1, 2, 4).
 // --------------------------------------------------------------------------
 // ev0 / ev1 (may be null): recorded at the start and the end of the kernel's
 // execution (hipExtLaunchKernelGGL), for timing.
-template <int KB, int VB, bool PK, bool CONTIG>
+template <int KB, int VB, bool PK, bool CONTIG, int NB>
 static void launch_mfma_mode(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
                              hipEvent_t ev1) {
     const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_kv * a.n_chunks)), block(kMBlock);
 #define TQ_MFMA_ARGS a, pt, a.k_codes, a.k_norms, a.v_codes, a.v_norms, a.q, a.block_table, a.seq_lens, a.part_ml, \
         a.part_acc, a.tilemax
     if (mode == MODE_DENSE)
-        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG>), grid, block, 0, s, ev0, ev1, 0,
-                              TQ_MFMA_ARGS);
+        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG, NB>), grid, block, 0, s, ev0, ev1,
+                              0, TQ_MFMA_ARGS);
     else if (mode == MODE_SCORE)
-        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG>), grid, block, 0, s, ev0, ev1, 0,
-                              TQ_MFMA_ARGS);
+        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG, NB>), grid, block, 0, s, ev0, ev1,
+                              0, TQ_MFMA_ARGS);
     else
-        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG>), grid, block, 0, s, ev0, ev1, 0,
-                              TQ_MFMA_ARGS);
+        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB>), grid, block, 0, s, ev0, ev1,
+                              0, TQ_MFMA_ARGS);
 #undef TQ_MFMA_ARGS
 }
 
-template <int KB, int VB>
+template <int KB, int VB, int NB>
 static void launch_mfma_vb(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
                            hipEvent_t ev1) {
     const bool pk = a.rows <= 8;
     if (a.contig) {
-        if (pk) launch_mfma_mode<KB, VB, true, true>(a, pt, mode, s, ev0, ev1);
-        else launch_mfma_mode<KB, VB, false, true>(a, pt, mode, s, ev0, ev1);
+        if (pk) launch_mfma_mode<KB, VB, true, true, NB>(a, pt, mode, s, ev0, ev1);
+        else launch_mfma_mode<KB, VB, false, true, NB>(a, pt, mode, s, ev0, ev1);
     } else {
-        if (pk) launch_mfma_mode<KB, VB, true, false>(a, pt, mode, s, ev0, ev1);
-        else launch_mfma_mode<KB, VB, false, false>(a, pt, mode, s, ev0, ev1);
+        if (pk) launch_mfma_mode<KB, VB, true, false, NB>(a, pt, mode, s, ev0, ev1);
+        else launch_mfma_mode<KB, VB, false, false, NB>(a, pt, mode, s, ev0, ev1);
     }
 }
 
-#define TQ_CAT2(a, b) a##b
-#define TQ_CAT(a, b) TQ_CAT2(a, b)
-void TQ_CAT(launch_mfma_kb, TQ_DECODE_KB)(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s,
-                                          hipEvent_t ev0, hipEvent_t ev1) {
+#ifndef TQ_DECODE_NB
+#define TQ_DECODE_NB 1
+#endif
+#define TQ_CAT4(a, b, c, d) a##b##c##d
+#define TQ_NAME(a, b, c, d) TQ_CAT4(a, b, c, d)
+void TQ_NAME(launch_mfma_kb, TQ_DECODE_KB, _nb, TQ_DECODE_NB)(const DecodeArgs &a, const PairTables &pt, int mode,
+                                                             hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     switch (a.v_bits) {
-        case 2: launch_mfma_vb<TQ_DECODE_KB, 2>(a, pt, mode, s, ev0, ev1); break;
-        case 3: launch_mfma_vb<TQ_DECODE_KB, 3>(a, pt, mode, s, ev0, ev1); break;
-        default: launch_mfma_vb<TQ_DECODE_KB, 4>(a, pt, mode, s, ev0, ev1); break;
+        case 2: launch_mfma_vb<TQ_DECODE_KB, 2, TQ_DECODE_NB>(a, pt, mode, s, ev0, ev1); break;
+        case 3: launch_mfma_vb<TQ_DECODE_KB, 3, TQ_DECODE_NB>(a, pt, mode, s, ev0, ev1); break;
+        default: launch_mfma_vb<TQ_DECODE_KB, 4, TQ_DECODE_NB>(a, pt, mode, s, ev0, ev1); break;
     }
 }
 

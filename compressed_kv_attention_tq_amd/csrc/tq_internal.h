@@ -97,14 +97,14 @@ struct DecodeArgs {
     const float *v_norms;
     const uint32_t *k_signs;
     const uint32_t *v_signs;
-    const uint16_t *q;        // float16 [S][n_qtok][H_q][128]
+    const uint16_t *q;        // float16 [S][n_qtok][H_q][128 nb]
     const int32_t *seq_lens;
     const int32_t *block_table;
     float *out;
     // workspace sections
     float *qrot;              // [S][n_kv][128][RP]   rotated, scaled queries
-    float *part_ml;           // [S][n_kv][n_chunks][RP][2]  (max, sum) per chunk, log2 domain
-    float *part_acc;          // [S][n_kv][n_chunks][RP][128] rotated-domain V accumulators
+    float *part_ml;           // [S][n_kv][n_chunks][RP][nb][2]  (max, sum) per chunk, log2 domain
+    float *part_acc;          // [S][n_kv][n_chunks][RP][nb][128] rotated-domain V accumulators
     float *tilemax;           // [S][n_kv][n_tiles][RP]  (sparse only)
     float *stats;             // [S][n_kv][RP][2]  global (max, sum) (sparse only)
     int32_t n_seqs, n_qtok, n_q_heads, n_kv, group, rows, rows_pad;
@@ -118,6 +118,7 @@ struct DecodeArgs {
                               // by block_size, chunk, n_chunks, n_kv, group, n_q_heads, n_qtok
     float tau;
     int32_t k_bits, v_bits;
+    int32_t nb, nb_log2;      // 128-element blocks per head (1, 2, 4; matrix-core path only)
     int32_t mfma;             // 1: matrix-core pass kernels, 0: vector-ALU kernels
     int32_t contig;           // matrix-core path: every 64-token slice lies in one page
     float kc[TQ_MAX_LEVELS];

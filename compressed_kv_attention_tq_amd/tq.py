@@ -20,7 +20,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtq.so")
 
-HEAD_DIM = 128
+HEAD_DIM = 128   # elements per block; a head is 1, 2 or 4 blocks (head_dim 128, 256, 512)
 BITS_FP16 = 16   # a cache side kept in float16 (TQ_BITS_FP16)
 MAX_LEVELS = 16
 MAX_ROWS_PER_KV_HEAD = 16
@@ -164,33 +164,40 @@ def _dev_ptr(t, what: str, dtype=None):
 
 @dataclass
 class Cache:
-    """One side (K or V) of a paged compressed cache, device memory owned by torch."""
+    """One side (K or V) of a paged compressed cache, device memory owned by torch.
+    A head of head_dim = 128 nb elements is nb sub-heads of 128 (block i of head j
+    is sub-head nb j + i)."""
     bits: int
     n_kv_heads: int
     block_size: int
     n_blocks: int
-    codes: object      # torch.uint8 [n_blocks, n_kv_heads, block_size, 16*bits]
-    norms: object      # torch.float32 [n_blocks, n_kv_heads, block_size]
-    signs: object      # torch.int32 (bit pattern of uint32) [n_kv_heads, 4]
+    codes: object      # torch.uint8 [n_blocks, n_kv_heads * nb, block_size, 16*bits]
+    norms: object      # torch.float32 [n_blocks, n_kv_heads * nb, block_size]
+    signs: object      # torch.int32 (bit pattern of uint32) [n_kv_heads * nb, 4]
     cb: TQCodebook
+    head_dim: int = HEAD_DIM
 
     @classmethod
-    def allocate(cls, bits, n_kv_heads, block_size, n_blocks, sign_words, device="cuda", cb=None):
+    def allocate(cls, bits, n_kv_heads, block_size, n_blocks, sign_words, device="cuda", cb=None,
+                 head_dim=HEAD_DIM):
         torch = _torch()
-        codes = torch.zeros((n_blocks, n_kv_heads, block_size, 16 * bits), dtype=torch.uint8, device=device)
-        norms = torch.zeros((n_blocks, n_kv_heads, block_size), dtype=torch.float32, device=device)
-        sw = np.ascontiguousarray(np.asarray(sign_words, dtype=np.uint32).reshape(n_kv_heads, 4))
+        if head_dim not in (HEAD_DIM, 2 * HEAD_DIM, 4 * HEAD_DIM):
+            raise ValueError("head_dim must be 128, 256 or 512")
+        n_sub = n_kv_heads * (head_dim // HEAD_DIM)
+        codes = torch.zeros((n_blocks, n_sub, block_size, 16 * bits), dtype=torch.uint8, device=device)
+        norms = torch.zeros((n_blocks, n_sub, block_size), dtype=torch.float32, device=device)
+        sw = np.ascontiguousarray(np.asarray(sign_words, dtype=np.uint32).reshape(n_sub, 4))
         signs = torch.from_numpy(sw.view(np.int32)).to(device)
         if bits == BITS_FP16:
             cb = TQCodebook()   # a float16 side has no codebook
         return cls(bits, n_kv_heads, block_size, n_blocks, codes, norms, signs,
-                   tq_build_codebook(bits) if cb is None else cb)
+                   tq_build_codebook(bits) if cb is None else cb, head_dim)
 
     def desc(self) -> TQCache:
         d = TQCache()
         d.bits = self.bits
         d.n_kv_heads = self.n_kv_heads
-        d.head_dim = HEAD_DIM
+        d.head_dim = self.head_dim
         d.block_size = self.block_size
         d.n_blocks = self.n_blocks
         d.codes = _dev_ptr(self.codes, "codes").value
@@ -201,20 +208,21 @@ class Cache:
 
 
 def tq_quantize_kv(k_cache: Cache | None, k_src, v_cache: Cache | None, v_src, slot_mapping, stream=None):
-    """Quantize-on-append: k_src / v_src float16 [n_tokens, n_kv_heads, 128] (token stride
-    taken from the tensor), slot_mapping int64 [n_tokens] (negative = skip)."""
+    """Quantize-on-append: k_src / v_src float16 [n_tokens, n_kv_heads, head_dim] (token
+    stride taken from the tensor), slot_mapping int64 [n_tokens] (negative = skip)."""
     torch = _torch()
     src = k_src if k_src is not None else v_src
     if src is None:
         return
     n_tokens = src.shape[0]
     stride = src.stride(0)
-    for t, name in ((k_src, "k_src"), (v_src, "v_src")):
+    for t, c, name in ((k_src, k_cache, "k_src"), (v_src, v_cache, "v_src")):
         if t is None:
             continue
-        if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 3 or t.shape[2] != HEAD_DIM:
-            raise ValueError(f"{name} must be a float16 device tensor [n_tokens, n_kv_heads, 128]")
-        if t.stride(2) != 1 or t.stride(1) != HEAD_DIM or t.stride(0) != stride or t.shape[0] != n_tokens:
+        hd = c.head_dim if c is not None else HEAD_DIM
+        if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 3 or t.shape[2] != hd:
+            raise ValueError(f"{name} must be a float16 device tensor [n_tokens, n_kv_heads, {hd}]")
+        if t.stride(2) != 1 or t.stride(1) != hd or t.stride(0) != stride or t.shape[0] != n_tokens:
             raise ValueError(f"{name}: heads must be contiguous and both sides share one token stride")
     kd = ctypes.byref(k_cache.desc()) if k_cache is not None else None
     vd = ctypes.byref(v_cache.desc()) if v_cache is not None else None
@@ -237,20 +245,20 @@ def decode_workspace_bytes(k_cache: Cache, v_cache: Cache, n_seqs, n_qtok, n_q_h
 
 def tq_decode_attention(k_cache: Cache, v_cache: Cache, q, seq_lens, block_table, softmax_scale=0.0,
                         sparse_v_tau=0.0, out=None, workspace=None, stream=None, events=None):
-    """q float16 [n_seqs, n_qtok, n_q_heads, 128]; seq_lens int32 [n_seqs];
+    """q float16 [n_seqs, n_qtok, n_q_heads, head_dim]; seq_lens int32 [n_seqs];
     block_table int32 [n_seqs, max_blocks].  Returns float32 out like q.
     events: optional pair of raw hipEvent_t handles (ctypes.c_void_p or int) recorded
     around the main pass kernel (tq_decode_attention_timed)."""
     torch = _torch()
     n_seqs, n_qtok, n_q_heads, hd = q.shape
-    if hd != HEAD_DIM:
-        raise ValueError("head_dim must be 128")
+    if hd != k_cache.head_dim:
+        raise ValueError(f"q has head_dim {hd}, the cache {k_cache.head_dim}")
     max_blocks = block_table.shape[1]
     need = decode_workspace_bytes(k_cache, v_cache, n_seqs, n_qtok, n_q_heads, max_blocks, sparse_v_tau)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if out is None:
-        out = torch.empty((n_seqs, n_qtok, n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+        out = torch.empty((n_seqs, n_qtok, n_q_heads, hd), dtype=torch.float32, device=q.device)
     size = ctypes.c_size_t(workspace.numel())
     ev = None
     if events is not None:
@@ -266,11 +274,11 @@ def tq_decode_attention(k_cache: Cache, v_cache: Cache, q, seq_lens, block_table
 
 
 def tq_dequantize(cache: Cache, slots, fp16=False, out=None, stream=None):
-    """Dequantized rows [n_tokens, n_kv_heads, 128] of the given slots (int64)."""
+    """Dequantized rows [n_tokens, n_kv_heads, head_dim] of the given slots (int64)."""
     torch = _torch()
     n = slots.shape[0]
     if out is None:
-        out = torch.empty((n, cache.n_kv_heads, HEAD_DIM), dtype=torch.float16 if fp16 else torch.float32,
+        out = torch.empty((n, cache.n_kv_heads, cache.head_dim), dtype=torch.float16 if fp16 else torch.float32,
                           device=slots.device)
     st = load_library().tq_dequantize(ctypes.byref(cache.desc()), _dev_ptr(slots, "slots", torch.int64), n,
                                       _dev_ptr(out, "out"), 1 if fp16 else 0, _stream_ptr(stream))

@@ -16,6 +16,8 @@
  *                 turbo types; VEC flash attention forced for quantized KV on HIP).
  *   [TQ+ article] zingnex thread "TurboQuant+：面向生产环境的LLM KV缓存与权重量化技术",
  *                 "注意力门控稀疏V解压" (skipped V positions are treated as zero).
+ *                 The same README's backend table lists flash attention for a 512-element
+ *                 head on its Metal row.
  *   [TQ blog]     intelliparadigm TurboQuant article: section 3.2 (H_random = D x H,
  *                 D a random +-1 diagonal; fast Hadamard transform O(d log d)),
  *                 section 3.3 (Lloyd-Max: nearest-centre assignment and mean update,
@@ -31,6 +33,10 @@
  *   - 128 codes packed LSB-first: code i occupies bits [b*i, b*i+b) of the block's
  *     16*b-byte bitstream, stream bit k being bit k%8 of byte k/8.
  *   - Dequantized vector: x_hat = n * s * (H c[code]) / sqrt(128).
+ *   - A head of head_dim = 128 nb elements (nb = 1, 2 or 4) is nb such blocks
+ *     ([TQ+ README] types note: every format works on 128-element blocks):
+ *     elements [128 i, 128 i + 128) form block i, with its own norm and its own
+ *     sign words; the cache keeps block i of head j as sub-head nb j + i.
  *   Storage is b + 0.25 bits per value (the [TQ blog] 4.1 figures for b = 3, 4).
  *
  * Conventions for every call:
@@ -58,12 +64,12 @@ extern "C" {
 typedef enum tq_status {
     TQ_OK = 0,
     TQ_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, inconsistent shape */
-    TQ_ERR_UNSUPPORTED = 2,   /* bits not in the supported set, head_dim != 128, too many rows */
+    TQ_ERR_UNSUPPORTED = 2,   /* bits not in the supported set, head_dim not 128/256/512, too many rows */
     TQ_ERR_WORKSPACE = 3,     /* workspace smaller than the size this call needs */
     TQ_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
 } tq_status;
 
-#define TQ_HEAD_DIM 128
+#define TQ_HEAD_DIM 128          /* elements per block; head_dim is 1, 2 or 4 blocks */
 #define TQ_MAX_LEVELS 16
 #define TQ_BITS_FP16 16   /* a cache side kept in float16: see tq_cache */
 #define TQ_MAX_ROWS_PER_KV_HEAD 16   /* (n_q_heads / n_kv_heads) * n_qtok */
@@ -87,19 +93,20 @@ typedef struct tq_cache {
     int32_t  bits;          /* 2, 3 or 4; must equal cb.bits.  Or TQ_BITS_FP16: the side
                                keeps its rows as float16 (the "f16 K, turbo V" start of
                                the [TQ+ README] usage steps; [TQ+ article] deployment
-                               advice): codes holds [n_blocks][n_kv_heads][block_size][128]
-                               float16 (256 bytes a row, 16*bits as for the others), and
+                               advice): codes holds [n_blocks][n_kv_heads][head_dim/128]
+                               [block_size][128] float16 (256 bytes a row, 16*bits as for
+                               the others), and
                                norms, signs and cb are not used (norms and signs may be
                                NULL).  Only a K side may be float16 in tq_decode_attention,
                                which then scores q . k directly (no rotation of q). */
     int32_t  n_kv_heads;    /* >= 1 */
-    int32_t  head_dim;      /* must be 128 */
+    int32_t  head_dim;      /* 128, 256 or 512 (nb = head_dim / 128 blocks per head) */
     int32_t  block_size;    /* tokens per page, >= 1 */
     int64_t  n_blocks;      /* pages in the pool, >= 1 */
-    uint8_t *codes;         /* device uint8 [n_blocks][n_kv_heads][block_size][16*bits] */
-    float   *norms;         /* device float [n_blocks][n_kv_heads][block_size] */
-    const uint32_t *signs;  /* device uint32 [n_kv_heads][4]; bit i of word w set means
-                               element 32*w+i is multiplied by -1 before H */
+    uint8_t *codes;         /* device uint8 [n_blocks][n_kv_heads][nb][block_size][16*bits] */
+    float   *norms;         /* device float [n_blocks][n_kv_heads][nb][block_size] */
+    const uint32_t *signs;  /* device uint32 [n_kv_heads][nb][4]; bit i of word w of block k
+                               set means element 128*k+32*w+i is multiplied by -1 before H */
     tq_codebook cb;         /* by value */
 } tq_cache;
 
@@ -125,7 +132,8 @@ tq_status tq_build_codebook(int32_t bits, double sigma, tq_codebook *out);
  * n_vectors float16 vectors (host memory, [n_vectors][128]; vector i belongs to
  * head i % n_heads, so a token-major [n_tokens][n_heads][128] array works as
  * is, with that head's signs signs[head][4], host memory, bit i of word w
- * meaning element 32*w+i is negated).  Zero and non-finite vectors are skipped.
+ * meaning element 32*w+i is negated; for heads of nb blocks, pass the blocks as
+ * vectors [n_tokens][n_heads * nb][128] with the sign words [n_heads * nb][4]).  Zero and non-finite vectors are skipped.
  * It starts from tq_build_codebook(bits, 1/sqrt(128)) and runs at most max_iter
  * rounds.  The stored codebook follows the same format: float16-exact centroids
  * (ascending; not forced antisymmetric), exact midpoints as boundaries,
@@ -142,16 +150,17 @@ tq_status tq_fit_codebook(int32_t bits, const uint16_t *vectors, int64_t n_vecto
 /* Quantize-on-append ([TQ+ README] backend table, SET_ROWS for turbo types):
  * compress n_tokens new K and V rows and write them into their cache slots.
  *   k, v            : host descriptors; either may be NULL to skip that side.
- *   k_src, v_src    : device float16 [n_tokens][n_kv_heads][128] of the side's cache;
- *                     heads of one token are contiguous, tokens are
- *                     src_token_stride elements apart (>= n_kv_heads * 128).
+ *   k_src, v_src    : device float16 [n_tokens][n_kv_heads][head_dim] of the side's cache
+ *                     (both sides given share n_kv_heads and head_dim); heads of one
+ *                     token are contiguous, tokens are src_token_stride elements
+ *                     apart (>= n_kv_heads * head_dim).
  *   slot_mapping    : device int64 [n_tokens]; slot = block * block_size + offset,
  *                     0 <= slot < n_blocks * block_size; a negative slot skips the token.
  *   n_tokens        : >= 0 (0 is a no-op).
  * For each (token, head): norm -> cache.norms, 16*bits code bytes -> cache.codes.
  * Errors: TQ_ERR_INVALID_ARG (missing pointers for a side that is given, bad
  *         stride or sizes, codebook inconsistent with bits), TQ_ERR_UNSUPPORTED
- *         (bits not 2..4, head_dim != 128), TQ_ERR_HIP. */
+ *         (bits not 2..4 or 16, head_dim not 128/256/512), TQ_ERR_HIP. */
 tq_status tq_quantize_kv(const tq_cache *k, const void *k_src,
                          const tq_cache *v, const void *v_src,
                          int64_t src_token_stride, int32_t n_tokens,
@@ -160,20 +169,20 @@ tq_status tq_quantize_kv(const tq_cache *k, const void *k_src,
 /* Decode attention over the compressed cache ([llama-tq] Hadamard-domain Q.K;
  * [TQ+ README] VEC flash attention for quantized KV and sparse V dequantization;
  * [TQ+ article] skipped V treated as zero).
- *   k, v               : host descriptors of the two sides (same n_kv_heads and
- *                        block_size; bits may differ).
- *   q                  : device float16 [n_seqs][n_qtok][n_q_heads][128].
+ *   k, v               : host descriptors of the two sides (same n_kv_heads, head_dim
+ *                        and block_size; bits may differ).
+ *   q                  : device float16 [n_seqs][n_qtok][n_q_heads][head_dim].
  *   n_seqs >= 0, n_qtok >= 1, n_q_heads a multiple of n_kv_heads with
  *   (n_q_heads / n_kv_heads) * n_qtok <= TQ_MAX_ROWS_PER_KV_HEAD.
  *   seq_lens           : device int32 [n_seqs], 0 <= len <= max_blocks_per_seq*block_size;
  *                        each length includes the n_qtok new tokens.
  *   block_table        : device int32 [n_seqs][max_blocks_per_seq]; entry p is the
  *                        physical page holding positions [p*block_size, (p+1)*block_size).
- *   softmax_scale      : > 0, or 0 for 1/sqrt(128).
+ *   softmax_scale      : > 0, or 0 for 1/sqrt(head_dim).
  *   sparse_v_tau       : >= 0.  With p the final normalised softmax weight, position t
  *                        contributes p_t * v_hat_t iff p_t >= tau (no renormalisation);
  *                        0 is dense attention.
- *   out                : device float32 [n_seqs][n_qtok][n_q_heads][128].
+ *   out                : device float32 [n_seqs][n_qtok][n_q_heads][head_dim].
  *   workspace          : device scratch of *workspace_bytes bytes, 256-byte aligned;
  *                        NULL queries the size: the required size is written to
  *                        *workspace_bytes and nothing is launched.
@@ -184,7 +193,8 @@ tq_status tq_quantize_kv(const tq_cache *k, const void *k_src,
  * TQ_DECODE_KERNEL=valu selects the vector-ALU pass, and TQ_DECODE_CHUNK=<tokens>
  * (a multiple of 256 for the matrix-core pass, 512 for the vector-ALU pass)
  * overrides the tokens per pass block.  Both are read at every call and change
- * the workspace size.
+ * the workspace size.  A float16 K side and heads of more than one block need the
+ * matrix-core pass (TQ_ERR_UNSUPPORTED with the vector-ALU pass).
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 tq_status tq_decode_attention(const tq_cache *k, const tq_cache *v, const void *q,
                               int32_t n_seqs, int32_t n_qtok, int32_t n_q_heads,
@@ -212,7 +222,7 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
  * inverse for everything else).
  *   c           : host descriptor.
  *   slots       : device int64 [n_tokens], each in [0, n_blocks*block_size).
- *   dst         : device [n_tokens][n_kv_heads][128], float16 if dst_is_fp16 else float32.
+ *   dst         : device [n_tokens][n_kv_heads][head_dim], float16 if dst_is_fp16 else float32.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
 tq_status tq_dequantize(const tq_cache *c, const int64_t *slots, int32_t n_tokens,
                         void *dst, int32_t dst_is_fp16, void *stream);

@@ -136,6 +136,20 @@ def test_decode_validation_errors():
                                    FAKE, None, None, None) == T.TQ_ERR_INVALID_ARG
 
 
+def test_decode_wide_heads_validation(monkeypatch):
+    """Heads of 256 / 512 elements: both sides alike; the workspace holds nb
+    accumulators per row; only the matrix-core pass takes them."""
+    _, size128 = decode_call()
+    for hd in (256, 512):
+        st, size = decode_call(k=fake_cache(head_dim=hd), v=fake_cache(bits=3, head_dim=hd))
+        assert st == T.TQ_OK and size > size128
+        assert decode_call(k=fake_cache(head_dim=hd))[0] == T.TQ_ERR_INVALID_ARG   # V is 128 wide
+    assert decode_call(k=fake_cache(head_dim=384), v=fake_cache(bits=3, head_dim=384))[0] == T.TQ_ERR_UNSUPPORTED
+    monkeypatch.setenv("TQ_DECODE_KERNEL", "valu")
+    assert decode_call(k=fake_cache(head_dim=256), v=fake_cache(bits=3, head_dim=256))[0] == T.TQ_ERR_UNSUPPORTED
+    assert decode_call()[0] == T.TQ_OK
+
+
 def test_quantize_validation_errors():
     lib = T.load_library()
     k, v = fake_cache(), fake_cache(bits=3)
@@ -150,6 +164,10 @@ def test_quantize_validation_errors():
     assert call(k, FAKE, v, FAKE, slots=None) == T.TQ_ERR_INVALID_ARG
     assert call(k, FAKE, fake_cache(bits=3, n_kv=4), FAKE, stride=512) == T.TQ_ERR_INVALID_ARG
     assert call(fake_cache(head_dim=96), FAKE, None, None) == T.TQ_ERR_UNSUPPORTED
+    assert call(fake_cache(head_dim=384), FAKE, None, None) == T.TQ_ERR_UNSUPPORTED
+    # heads of 256: both sides alike, and the token stride covers n_kv * 256 elements
+    assert call(fake_cache(head_dim=256), FAKE, v, FAKE, stride=512) == T.TQ_ERR_INVALID_ARG
+    assert call(fake_cache(head_dim=256), FAKE, None, None, stride=511 - 7) == T.TQ_ERR_INVALID_ARG
     assert call(fake_cache(bits=1), FAKE, None, None) == T.TQ_ERR_UNSUPPORTED
     assert call(fake_cache(block_size=1 << 20, n_blocks=1 << 12), FAKE, None, None) == T.TQ_ERR_UNSUPPORTED
     # no-ops: nothing to do, nothing launched
@@ -164,7 +182,7 @@ def test_dequantize_validation_errors():
     assert lib.tq_dequantize(ctypes.byref(c), None, 4, FAKE, 0, None) == T.TQ_ERR_INVALID_ARG
     assert lib.tq_dequantize(ctypes.byref(c), FAKE, 4, None, 0, None) == T.TQ_ERR_INVALID_ARG
     assert lib.tq_dequantize(ctypes.byref(c), FAKE, 4, FAKE + 8, 0, None) == T.TQ_ERR_INVALID_ARG
-    assert lib.tq_dequantize(ctypes.byref(fake_cache(head_dim=256)), FAKE, 4, FAKE, 0, None) == T.TQ_ERR_UNSUPPORTED
+    assert lib.tq_dequantize(ctypes.byref(fake_cache(head_dim=384)), FAKE, 4, FAKE, 0, None) == T.TQ_ERR_UNSUPPORTED
     assert lib.tq_dequantize(ctypes.byref(c), FAKE, 0, FAKE, 0, None) == T.TQ_OK
     assert lib.tq_dequantize(None, FAKE, 4, FAKE, 0, None) == T.TQ_ERR_INVALID_ARG
 

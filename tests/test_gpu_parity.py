@@ -67,7 +67,7 @@ _ORACLE_MEMO = {}
 
 def _wl_key(wl):
     return (wl.name, wl.kind, wl.seed, wl.n_seqs, tuple(int(x) for x in wl.seq_lens), wl.n_qtok, wl.n_q_heads,
-            wl.n_kv_heads, wl.k_bits, wl.v_bits, wl.block_size, wl.n_blocks)
+            wl.n_kv_heads, wl.k_bits, wl.v_bits, wl.block_size, wl.n_blocks, wl.head_dim)
 
 
 def _memo(key, fn):
@@ -504,3 +504,145 @@ def test_graph_replay_matches_eager(kernel):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i} differs from eager"
         assert torch.equal(gk.codes, codes_eager)
+
+
+# ------------------------------------------------- heads of 256 / 512 elements (R12)
+
+def _skip_valu_for_wide_heads(kernel):
+    if kernel == "valu":
+        pytest.skip("heads of several blocks run on the matrix-core pass only (the vector-ALU pass rejects them)")
+
+
+@pytest.mark.parametrize("head_dim", [256, 512])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_wide_heads(bits, head_dim):
+    """Every 128-slice of every head is quantized with its own sign words (R12),
+    from a padded token stride and into shuffled slots."""
+    torch = _t()
+    rng = np.random.default_rng(7 * bits + head_dim)
+    nb, n_kv, n_tok, bs, pad = head_dim // 128, 3, 90, 16, 24
+    x = (rng.standard_normal((n_tok, n_kv, head_dim)) * rng.lognormal(0, 1, (1, n_kv, head_dim))).astype(np.float16)
+    signs = W.random_sign_words(rng, n_kv * nb)
+    n_blocks = -(-n_tok // bs) + 1
+    slots = rng.permutation(n_blocks * bs)[:n_tok].astype(np.int64)
+    slots[5] = -1
+    g = T.Cache.allocate(bits, n_kv, bs, n_blocks, signs, head_dim=head_dim)
+    g.codes.fill_(0xAB)
+    src = np.zeros((n_tok, n_kv * head_dim + pad), np.float16)
+    src[:, : n_kv * head_dim] = x.reshape(n_tok, -1)
+    src_t = torch.from_numpy(src).cuda()
+    view = torch.as_strided(src_t, (n_tok, n_kv, head_dim), (n_kv * head_dim + pad, head_dim, 1))
+    T.tq_quantize_kv(g, view, None, None, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    codes = g.codes.cpu().numpy().transpose(0, 2, 1, 3).reshape(-1, n_kv * nb, 16 * bits)
+    norms = g.norms.cpu().numpy().transpose(0, 2, 1).reshape(-1, n_kv * nb)
+    ok = slots >= 0
+    near = 0
+    for h in range(n_kv):
+        for i in range(nb):
+            sub = nb * h + i
+            near += U.check_codes(codes[slots[ok], sub], norms[slots[ok], sub], x[ok, h, 128 * i:128 * (i + 1)],
+                                  signs[sub], bits)
+    untouched = np.setdiff1d(np.arange(codes.shape[0]), slots[ok])
+    assert np.all(codes[untouched] == 0xAB), "a skipped or unused slot was written"
+    # the dequantized heads: every block, in order
+    oc = O.new_cache(bits, n_kv, bs, n_blocks, signs, O.build_codebook(bits), head_dim=head_dim)
+    O.cache_write(oc, x, slots)
+    rd = torch.from_numpy(slots[ok]).cuda()
+    got = T.tq_dequantize(g, rd).cpu().numpy()
+    assert got.shape == (int(ok.sum()), n_kv, head_dim)
+    for h in range(n_kv):
+        want = O.cache_read(oc, slots[ok], h)
+        err = U.row_rel_err(got[:, h], want)
+        assert np.max(err) < 1e-4, f"dequantize head {h}: {np.max(err)} (near-boundary codes {near})"
+    log(f"quantize head_dim={head_dim} bits={bits}: near-boundary {near}")
+
+
+@pytest.mark.parametrize("case", [
+    # (n_seqs, lens, n_qtok, n_q_heads, n_kv_heads, k_bits, v_bits, block_size, head_dim)
+    (1, [700], 1, 4, 1, 4, 3, 256, 256),
+    (2, [1000, 33], 1, 16, 8, 3, 2, 256, 256),
+    (2, [300, 129], 4, 16, 4, 4, 4, 64, 256),
+    (2, [1500, 600], 1, 8, 2, 4, 3, 100, 512),
+    (3, [77, 5, 260], 2, 8, 1, 2, 3, 16, 512),
+    (1, [4097], 3, 6, 2, 3, 3, 256, 512),
+    (2, [900, 70], 1, 8, 2, T.BITS_FP16, 3, 256, 256),
+    (2, [513, 64], 2, 8, 2, T.BITS_FP16, 4, 64, 512),
+], ids=lambda c: f"d{c[8]}-s{c[0]}-q{c[2]}-h{c[3]}/{c[4]}-b{c[5]}{c[6]}-bs{c[7]}")
+def test_decode_wide_heads(case, kernel):
+    """Heads of 256 / 512 elements: 1-16 rows per KV head, whole and partial slices,
+    contiguous and paged layouts, K compressed or float16."""
+    _skip_valu_for_wide_heads(kernel)
+    n_seqs, lens, n_qtok, hq, hkv, kb, vb, bs, hd = case
+    wl = W.small_decode(seed=sum(lens) + hd, n_seqs=n_seqs, lens=lens, n_qtok=n_qtok, n_q_heads=hq,
+                        n_kv_heads=hkv, k_bits=kb, v_bits=vb, block_size=bs, head_dim=hd)
+    decode_and_compare(wl)
+
+
+@pytest.mark.parametrize("head_dim", [256, 512])
+@pytest.mark.parametrize("tau", [1e-4, 3e-2, 1.5])
+def test_decode_wide_heads_sparse(tau, head_dim, kernel):
+    """Sparse V with heads of several blocks (the waves of a group share each gate
+    decision; groups decide apart)."""
+    _skip_valu_for_wide_heads(kernel)
+    wl = W.small_decode(seed=53 + head_dim, n_seqs=2, lens=[2500, 700], n_qtok=2, n_q_heads=8, n_kv_heads=2,
+                        k_bits=4, v_bits=2, tau=tau, block_size=256, head_dim=head_dim)
+    out, _ = decode_and_compare(wl)
+    if tau > 1:
+        assert np.all(out == 0)
+
+
+def test_decode_wide_heads_rows_with_no_visible_token_are_zero(kernel):
+    _skip_valu_for_wide_heads(kernel)
+    wl = W.small_decode(seed=4, n_seqs=2, lens=[2, 0], n_qtok=4, n_q_heads=2, n_kv_heads=1, k_bits=4,
+                        v_bits=3, block_size=16, head_dim=512)
+    out, _ = decode_and_compare(wl)
+    assert np.all(out[0, :2] == 0) and np.all(out[1] == 0)
+
+
+def _sampled_head_caches(wl, heads):
+    """Device caches of the whole workload whose sampled KV heads hold oracle-written
+    codes (other heads zero), and the oracle caches of the sampled heads alone."""
+    torch = _t()
+    nb = wl.blocks_per_head
+    sub = np.concatenate([np.arange(nb * h, nb * (h + 1)) for h in heads])
+
+    def build():
+        caches = []
+        for side, bits, signs in ((0, wl.k_bits, wl.signs_k), (1, wl.v_bits, wl.signs_v)):
+            c = O.new_cache(bits, len(heads), wl.block_size, wl.n_blocks, signs[sub],
+                            None if bits == O.FP16 else O.build_codebook(bits), head_dim=wl.head_dim)
+            for b in range(wl.n_seqs):
+                k, v = wl.kv_source(b)
+                O.cache_write(c, (k if side == 0 else v)[:, heads], wl.slots(b))
+            caches.append(c)
+        return caches
+
+    ok, ov = _memo(("heads", tuple(heads)) + _wl_key(wl), build)
+    gk = T.Cache.allocate(wl.k_bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, wl.signs_k, head_dim=wl.head_dim)
+    gv = T.Cache.allocate(wl.v_bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, wl.signs_v, head_dim=wl.head_dim)
+    idx = torch.as_tensor(sub, device="cuda")
+    for oc, g in ((ok, gk), (ov, gv)):
+        g.codes.index_copy_(1, idx, torch.from_numpy(oc.codes).cuda())
+        g.norms.index_copy_(1, idx, torch.from_numpy(oc.norms).cuda())
+    torch.cuda.synchronize()
+    return ok, ov, gk, gv
+
+
+@pytest.mark.parametrize("head_dim,heads", [(256, [0, 5]), (512, [2, 7])])
+def test_decode_wide_heads_llama8b_sampled(head_dim, heads, kernel):
+    """The Llama-3-8B-shaped decode (32768 tokens, 32 / 8 heads, K4 / V3) with heads of
+    256 / 512 elements, at full size: every row of two KV heads checked."""
+    _skip_valu_for_wide_heads(kernel)
+    torch = _t()
+    wl = W.llama8b_wide(head_dim)
+    ok, ov, gk, gv = _sampled_head_caches(wl, heads)
+    q = wl.queries()
+    out = T.tq_decode_attention(gk, gv, torch.from_numpy(q).cuda(), torch.from_numpy(wl.seq_lens).cuda(),
+                                torch.from_numpy(wl.block_table).cuda()).cpu().numpy()
+    qh = np.concatenate([np.arange(h * wl.group, (h + 1) * wl.group) for h in heads])
+    want = _memo(("heads-out", tuple(heads)) + _wl_key(wl),
+                 lambda: O.decode_attention(q[:, :, qh], ok, ov, wl.seq_lens, wl.block_table, wl.n_qtok))
+    err = U.row_rel_err(out[:, :, qh], want)
+    log(f"decode {wl.name} heads {heads}: worst row rel err {np.max(err):.2e}")
+    assert np.max(err) <= ATOL_ROW
