@@ -76,6 +76,16 @@ Readings taken where the pages are silent (each one also listed in the design doc):
       its own as in R1-R6 with its own norm and its own sign vector.  The cache
       keeps block i of head j as sub-head nb * j + i; the dequantized head is the
       concatenation of its blocks, and attention is R7 over the whole head.
+  R13 V outlier channels (the V family "v3" of [llama-tq], named there only as
+      V quantization with outlier-channel separation, its high-quality tier; the
+      fourth page's compression principle keeps rare high-magnitude values at 8
+      or 16 bits): per KV head a fixed set of k <= 16 channels is kept exactly
+      as float16 for every token; the vector with those channels set to zero is
+      quantized as R1-R6 (its norm and rotation see zeros there); the
+      dequantized vector is the TurboQuant reconstruction with the kept values
+      written over those channels.  The channels come from warm-up data (the
+      [TQ blog] 5.3 advice): the k with the largest mean square over the head's
+      vectors, ties to the lower index, listed in ascending order.
 """
 
 from __future__ import annotations
@@ -93,7 +103,8 @@ __all__ = [
     "gaussian_lloyd_max", "lloyd_max_from_samples", "Codebook", "build_codebook", "fit_codebook",
     "codebook_mse", "encode", "near_boundary_mask", "quantize_vectors",
     "pack_codes", "unpack_codes", "dequantize_vectors", "OracleCache",
-    "new_cache", "cache_write", "cache_read", "slots_for_sequence", "FP16",
+    "new_cache", "cache_write", "cache_read", "slots_for_sequence", "FP16", "select_outlier_channels",
+    "MAX_OUTLIERS",
     "decode_attention_rows", "decode_attention", "bits_per_value",
 ]
 
@@ -386,6 +397,9 @@ class OracleCache:
     signs: np.ndarray   # uint32 [n_sub, 4]
     cb: Codebook
     head_dim: int = D   # elements per head; n_sub = n_kv_heads * head_dim / 128 sub-heads (R12)
+    n_outliers: int = 0                      # R13: channels per sub-head kept in float16
+    outlier_channels: np.ndarray = None      # uint8 [n_sub, n_outliers], ascending
+    outliers: np.ndarray = None              # float16 [n_blocks, n_sub, block_size, n_outliers]
 
     @property
     def blocks_per_head(self) -> int:
@@ -399,19 +413,50 @@ class OracleCache:
 FP16 = 16  # bits of a side kept in float16 (R11): rows of 128 float16, no norm, no codebook
 
 
-def new_cache(bits, n_kv_heads, block_size, n_blocks, signs, cb, head_dim: int = D) -> OracleCache:
+MAX_OUTLIERS = 16   # R13: at most this many kept channels per head
+
+
+def new_cache(bits, n_kv_heads, block_size, n_blocks, signs, cb, head_dim: int = D,
+              outlier_channels=None) -> OracleCache:
     """A zeroed paged cache side; bits = FP16 keeps float16 rows (256 bytes each).
 
     head_dim is a multiple of 128 (R12); signs hold one word quadruple per
     sub-head, [n_kv_heads, head_dim / 128, 4] in any shape of that size.
+    outlier_channels (R13, a compressed side): [n_sub, k] distinct channel
+    indices per sub-head, k <= 16, kept in float16.
     """
     if head_dim % D != 0 or head_dim < D:
         raise ValueError("head_dim must be a positive multiple of 128")
     n_sub = n_kv_heads * (head_dim // D)
-    return OracleCache(bits, n_kv_heads, block_size, n_blocks,
-                       np.zeros((n_blocks, n_sub, block_size, 16 * bits), np.uint8),
-                       np.zeros((n_blocks, n_sub, block_size), np.float32),
-                       np.asarray(signs, np.uint32).reshape(n_sub, 4), cb, head_dim)
+    c = OracleCache(bits, n_kv_heads, block_size, n_blocks,
+                    np.zeros((n_blocks, n_sub, block_size, 16 * bits), np.uint8),
+                    np.zeros((n_blocks, n_sub, block_size), np.float32),
+                    np.asarray(signs, np.uint32).reshape(n_sub, 4), cb, head_dim)
+    if outlier_channels is not None:
+        idx = np.asarray(outlier_channels, np.int64).reshape(n_sub, -1)
+        k = idx.shape[1]
+        if bits == FP16 or k > MAX_OUTLIERS or np.any(idx < 0) or np.any(idx >= D):
+            raise ValueError("outlier channels: a compressed side, at most 16 channels in [0, 128)")
+        if any(len(set(row.tolist())) != k for row in idx):
+            raise ValueError("outlier channels of a head must be distinct")
+        c.n_outliers = k
+        c.outlier_channels = np.sort(idx, axis=1).astype(np.uint8)
+        c.outliers = np.zeros((n_blocks, n_sub, block_size, k), np.float16)
+    return c
+
+
+def select_outlier_channels(vectors: np.ndarray, k: int) -> np.ndarray:
+    """R13: per head, the k channels with the largest mean square over the given
+    vectors [..., n_heads, 128] (float16 values), ties to the lower index;
+    returns uint8 [n_heads, k], each row ascending."""
+    x = np.asarray(vectors).astype(np.float64)
+    x = x.reshape(-1, x.shape[-2], D)
+    ms = np.mean(x * x, axis=0)                       # [n_heads, 128]
+    out = np.zeros((ms.shape[0], k), np.uint8)
+    for h in range(ms.shape[0]):
+        order = sorted(range(D), key=lambda c: (-ms[h, c], c))
+        out[h] = np.sort(order[:k])
+    return out
 
 
 def cache_write(cache: OracleCache, src: np.ndarray, slots: np.ndarray):
@@ -435,6 +480,13 @@ def cache_write(cache: OracleCache, src: np.ndarray, slots: np.ndarray):
     norms = np.zeros((n_tok, cache.n_sub), np.float32)
     codes = np.zeros((n_tok, cache.n_sub, D), np.uint8)
     ys = np.zeros((n_tok, cache.n_sub, D), np.float64)
+    kept = None
+    if cache.n_outliers:   # R13: the kept channels leave the vector before R3-R6
+        idx = cache.outlier_channels.astype(np.int64)
+        kept = np.stack([src[:, h, idx[h]] for h in range(cache.n_sub)], axis=1).astype(np.float16)
+        src = src.copy()
+        for h in range(cache.n_sub):
+            src[:, h, idx[h]] = 0
     for h in range(cache.n_sub):
         s = sign_vector(cache.signs[h])
         nh, ch, yh = quantize_vectors(src[:, h, :], s, cache.cb)
@@ -446,6 +498,8 @@ def cache_write(cache: OracleCache, src: np.ndarray, slots: np.ndarray):
         blk, off = divmod(int(slots[t]), cache.block_size)
         cache.codes[blk, :, off, :] = packed[t]
         cache.norms[blk, :, off] = norms[t]
+        if kept is not None:
+            cache.outliers[blk, :, off, :] = kept[t]
     return norms, codes, ys
 
 
@@ -462,7 +516,10 @@ def _read_sub(cache: OracleCache, blk: np.ndarray, off: np.ndarray, sub: int) ->
     packed = cache.codes[blk, sub, off, :]
     norms = cache.norms[blk, sub, off]
     codes = unpack_codes(packed, cache.bits)
-    return dequantize_vectors(norms, codes, sign_vector(cache.signs[sub]), cache.cb)
+    x = dequantize_vectors(norms, codes, sign_vector(cache.signs[sub]), cache.cb)
+    if cache.n_outliers:   # R13: the kept values over their channels
+        x[:, cache.outlier_channels[sub].astype(np.int64)] = cache.outliers[blk, sub, off, :].astype(np.float64)
+    return x
 
 
 def cache_read(cache: OracleCache, slots: np.ndarray, head: int) -> np.ndarray:

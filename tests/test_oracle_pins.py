@@ -590,3 +590,101 @@ def test_wide_head_two_tokens_closed_form_default_scale():
     p0 = 1.0 / (1.0 + math.exp(s1 - s0))
     out = O.decode_attention(q, kc, vc, [2], np.array([[0]]), 1)
     np.testing.assert_allclose(out[0, 0, 0], p0 * vh[0] + (1 - p0) * vh[1], rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------- V outlier channels (R13)
+
+def test_select_outlier_channels_brute_force_and_planted():
+    """The k channels of largest mean square (ties to the lower index), ascending:
+    against a loop over channels, and planted x20 channels are found."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((40, 3, 128)).astype(np.float16)
+    x[:, :, 7] = 0
+    x[:, :, 9] = 0        # a tie at zero: never among the top
+    planted = [[5, 77, 100, 126], [0, 1, 2, 3], [64, 65, 90, 127]]
+    for h in range(3):
+        x[:, h, planted[h]] *= np.float16(20)
+    got = O.select_outlier_channels(x, 4)
+    for h in range(3):
+        assert list(got[h]) == planted[h]
+    got8 = O.select_outlier_channels(x, 8)
+    for h in range(3):
+        ms = []
+        for c in range(128):
+            acc = 0.0
+            for t in range(40):
+                acc += float(x[t, h, c]) ** 2
+            ms.append((-acc / 40, c))
+        want = sorted(c for _, c in sorted(ms)[:8])
+        assert list(got8[h]) == want
+    # a tie decided by the lower index
+    y = np.ones((2, 1, 128), np.float16)
+    assert list(O.select_outlier_channels(y, 3)[0]) == [0, 1, 2]
+
+
+def test_outlier_side_keeps_channels_and_quantizes_the_rest():
+    """R13: the kept channels read back exactly; every other channel equals the plain
+    TurboQuant reconstruction of the vector with the kept channels zeroed (its norm
+    and rotation see zeros there)."""
+    rng = np.random.default_rng(22)
+    n_kv, bs, n_tok = 2, 8, 21
+    x = rng.standard_normal((n_tok, n_kv, 128)).astype(np.float16)
+    idx = np.array([[3, 40, 41, 99, 127], [0, 8, 16, 64, 65]], np.uint8)
+    x[:, 0, idx[0]] *= np.float16(30)
+    sw = rng.integers(0, 2 ** 32, size=(n_kv, 4), dtype=np.uint64).astype(np.uint32)
+    cb = O.build_codebook(3)
+    c = O.new_cache(3, n_kv, bs, 4, sw, cb, outlier_channels=idx[:, ::-1])   # any order in, ascending kept
+    assert np.array_equal(c.outlier_channels, idx)
+    slots = O.slots_for_sequence(np.array([3, 1, 0]), bs, n_tok)
+    O.cache_write(c, x, slots)
+    for h in range(n_kv):
+        got = O.cache_read(c, slots, h)
+        np.testing.assert_array_equal(got[:, idx[h]], x[:, h, idx[h]].astype(np.float64))
+        z = x[:, h].copy()
+        z[:, idx[h]] = 0
+        s = O.sign_vector(sw[h])
+        n, codes, _ = O.quantize_vectors(z, s, cb)
+        want = O.dequantize_vectors(n, codes, s, cb)
+        rest = np.setdiff1d(np.arange(128), idx[h])
+        np.testing.assert_array_equal(got[:, rest], want[:, rest])
+
+
+def test_outlier_separation_cuts_the_error_of_planted_outliers():
+    """With 4 channels x20 per token, keeping them exactly leaves the quantization
+    error of an ordinary N(0,1) vector; without it the outliers dominate the norm
+    and the other channels lose most of their resolution."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((400, 1, 128))
+    ch = [10, 50, 90, 120]
+    x[:, :, ch] *= 20
+    x = x.astype(np.float16)
+    sw = rng.integers(0, 2 ** 32, size=(1, 4), dtype=np.uint64).astype(np.uint32)
+    slots = np.arange(400)
+    errs = []
+    for idx in (None, O.select_outlier_channels(x, 4)):
+        c = O.new_cache(3, 1, 400, 1, sw, O.build_codebook(3), outlier_channels=idx)
+        O.cache_write(c, x, slots)
+        d = O.cache_read(c, slots, 0) - x[:, 0].astype(np.float64)
+        errs.append(np.sum(d * d) / np.sum(x[:, 0].astype(np.float64) ** 2))
+    assert errs[1] < errs[0] / 10, errs
+
+
+def test_outlier_attention_two_tokens_closed_form():
+    """Two tokens: at a kept channel the output is p0 v0[c] + p1 v1[c] with the
+    exact stored values (p from the K side's closed form)."""
+    rng = np.random.default_rng(24)
+    k = rng.standard_normal((2, 1, 128)).astype(np.float16)
+    v = rng.standard_normal((2, 1, 128)).astype(np.float16)
+    v[:, 0, [6, 60]] = np.float16(300)
+    kc = O.new_cache(4, 1, 4, 1, [[1, 2, 3, 4]], O.build_codebook(4))
+    vc = O.new_cache(2, 1, 4, 1, [[5, 6, 7, 8]], O.build_codebook(2), outlier_channels=[[6, 60]])
+    O.cache_write(kc, k, np.array([0, 1]))
+    O.cache_write(vc, v, np.array([0, 1]))
+    q = rng.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    kh = O.cache_read(kc, np.array([0, 1]), 0)
+    s0, s1 = kh @ q[0, 0, 0].astype(np.float64) / math.sqrt(128)
+    p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    out = O.decode_attention(q, kc, vc, [2], np.array([[0]]), 1)
+    for c in (6, 60):
+        np.testing.assert_allclose(out[0, 0, 0, c], p0 * float(v[0, 0, c]) + (1 - p0) * float(v[1, 0, c]),
+                                   rtol=1e-13)
