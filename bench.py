@@ -103,7 +103,7 @@ class HipEvents:
 def decode_workload(name):
     return {"llama8b": W.llama8b, "llama8b_k16": W.llama8b_k16, "longctx": W.longctx, "ragged": W.ragged,
             "tiny": W.tiny, "llama8b_d256": lambda: W.llama8b_wide(256),
-            "llama8b_d512": lambda: W.llama8b_wide(512)}[name]()
+            "llama8b_d512": lambda: W.llama8b_wide(512), "llama8b_vout": W.llama8b_vout}[name]()
 
 
 def gen_kv_device(wl, b, torch, gen):
@@ -121,7 +121,8 @@ def gen_kv_device(wl, b, torch, gen):
 def run_decode(args, torch):
     wl = decode_workload(args.workload)
     kb, vb, hd, hb = wl.k_bits, wl.v_bits, wl.head_dim, wl.blocks_per_head
-    per_tok = hb * (cache_bytes_per_token_head(kb) + cache_bytes_per_token_head(vb))   # one token of one head
+    kept_b = 2 * wl.v_kept   # kept V channels: float16 each
+    per_tok = hb * (cache_bytes_per_token_head(kb) + cache_bytes_per_token_head(vb)) + kept_b   # one token-head
     cache_bytes = wl.total_tokens * wl.n_kv_heads * per_tok
     reps = args.replicas or min(64, max(1, math.ceil(1.5 * LLC_BYTES / cache_bytes)))
     log(f"[bench] workload {wl.name}: {wl.n_seqs} seqs, {wl.total_tokens} tokens, cache {cache_bytes / 1e6:.1f} MB, "
@@ -129,7 +130,11 @@ def run_decode(args, torch):
 
     nb = wl.n_blocks
     kc = T.Cache.allocate(kb, wl.n_kv_heads, wl.block_size, nb * reps, wl.signs_k, head_dim=hd)
-    vc = T.Cache.allocate(vb, wl.n_kv_heads, wl.block_size, nb * reps, wl.signs_v, head_dim=hd)
+    kept_idx = None
+    if wl.v_kept:   # the V side's kept channels, selected on warm-up V by the library
+        kept_idx = T.tq_select_outlier_channels(wl.warmup_v(), wl.v_kept)[:, : wl.v_kept]
+    vc = T.Cache.allocate(vb, wl.n_kv_heads, wl.block_size, nb * reps, wl.signs_v, head_dim=hd,
+                          outlier_channels=kept_idx)
     gen = torch.Generator(device="cuda").manual_seed(0)
     tables = []
     for r in range(reps):
@@ -211,7 +216,7 @@ def run_decode(args, torch):
     if wl.tau > 0:
         kept = 64 * wl.n_seqs * wl.n_kv_heads          # planted positions kept per (seq, KV head)
         cache_step = hb * (wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb) +
-                           kept * cache_bytes_per_token_head(vb))
+                           kept * cache_bytes_per_token_head(vb)) + kept * kept_b
         pass_bytes = hb * wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb)
     else:
         cache_step = cache_bytes
@@ -233,7 +238,8 @@ def run_decode(args, torch):
             "kernel": kernel + (" (scoring pass)" if wl.tau > 0 else ""), "bytes_per_launch": pass_bytes,
             "avg_launch_us": round(pass_ms * 1e3, 2)}
     cfg = {"workload": f"{wl.name}: {wl.n_seqs} seq x {int(wl.seq_lens.max())} tokens, "
-                       f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d={hd}, K{kb}/V{vb}, "
+                       f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d={hd}, K{kb}/V{vb}"
+                       f"{f' ({wl.v_kept} V channels kept in float16)' if wl.v_kept else ''}, "
                        f"{wl.n_qtok} query token(s), tau={wl.tau}, page {wl.block_size}",
            "global_batch": wl.n_seqs, "seq_len": int(wl.seq_lens.max()), "replicas": reps,
            "launch": "HIP graph replay", "ms_per_step_eager": round(ms_step_eager, 5),
@@ -374,14 +380,16 @@ def cpu_baseline(wl, budget_s=12.0):
     slots = wl.slots(b)
     q = wl.queries()
     hb = wl.blocks_per_head
-    per_tok = hb * (cache_bytes_per_token_head(wl.k_bits) + cache_bytes_per_token_head(wl.v_bits))
+    per_tok = hb * (cache_bytes_per_token_head(wl.k_bits) + cache_bytes_per_token_head(wl.v_bits)) + 2 * wl.v_kept
     lens1, table1 = wl.seq_lens[:1], wl.block_table[:1]
+    kept = O.select_outlier_channels(wl.warmup_v(), wl.v_kept) if wl.v_kept else None
     prepared = []
     for kv in range(wl.n_kv_heads):   # the context before the new tokens (not timed)
         kcache = O.new_cache(wl.k_bits, 1, wl.block_size, wl.n_blocks, wl.signs_k[kv * hb:(kv + 1) * hb],
                              None if wl.k_bits == 16 else O.build_codebook(wl.k_bits), head_dim=wl.head_dim)
         vcache = O.new_cache(wl.v_bits, 1, wl.block_size, wl.n_blocks, wl.signs_v[kv * hb:(kv + 1) * hb],
-                             O.build_codebook(wl.v_bits), head_dim=wl.head_dim)
+                             O.build_codebook(wl.v_bits), head_dim=wl.head_dim,
+                             outlier_channels=None if kept is None else kept[kv:kv + 1])
         O.cache_write(kcache, k[:-wl.n_qtok, kv:kv + 1], slots[:-wl.n_qtok])
         O.cache_write(vcache, v[:-wl.n_qtok, kv:kv + 1], slots[:-wl.n_qtok])
         prepared.append((kcache, vcache, q[:1, :, kv * wl.group:(kv + 1) * wl.group]))
@@ -410,7 +418,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b",
-                    choices=["llama8b", "llama8b_k16", "llama8b_d256", "llama8b_d512", "longctx", "ragged", "tiny"])
+                    choices=["llama8b", "llama8b_k16", "llama8b_d256", "llama8b_d512", "llama8b_vout", "longctx",
+                             "ragged", "tiny"])
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--quantize-reps", type=int, default=5)
     ap.add_argument("--no-quantize", action="store_true")

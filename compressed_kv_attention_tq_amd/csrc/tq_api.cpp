@@ -82,6 +82,13 @@ tq_status check_cache(const tq_cache *c) {
     if (!c->codes || !is_aligned(c->codes, 16)) return TQ_ERR_INVALID_ARG;
     // slots are handled as 32-bit values on the device
     if ((double)c->n_blocks * c->block_size > 2147483647.0) return TQ_ERR_UNSUPPORTED;
+    if (c->n_outliers < 0 || c->n_outliers > TQ_MAX_OUTLIERS) return TQ_ERR_INVALID_ARG;
+    if (c->n_outliers > 0) {
+        if (fp16 || c->head_dim != TQ_HEAD_DIM) return TQ_ERR_UNSUPPORTED;
+        if (!c->outlier_channels || !is_aligned(c->outlier_channels, 16) || !c->outliers ||
+            !is_aligned(c->outliers, 8))
+            return TQ_ERR_INVALID_ARG;
+    }
     if (fp16) return TQ_OK;   // rows of float16: no norms, signs or codebook
     if (!c->norms || !c->signs || !is_aligned(c->norms, 4) || !is_aligned(c->signs, 4)) return TQ_ERR_INVALID_ARG;
     return check_codebook(c->cb, c->bits);
@@ -137,6 +144,9 @@ tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, in
     q.kv_div = make_fastdiv((uint32_t)sub_heads(c));
     q.n_bnd = nb;
     for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) q.bnd[i] = i < nb ? c->cb.boundaries[i] : 0.f;
+    q.n_out = c->n_outliers;
+    q.out_idx = c->outlier_channels;
+    q.outliers = c->outliers;
     return TQ_OK;
 }
 
@@ -173,8 +183,8 @@ bool use_mfma_decode() {
 // Tokens per pass block: a multiple of the unit (one 64-token slice per wave),
 // doubled while at least kTargetBlocks blocks remain and at most 16384 tokens;
 // TQ_DECODE_CHUNK (a multiple of the unit) overrides it.
-DecodePlan plan_decode(int n_seqs, int n_kv, int nb, int rows, int max_blocks, int block_size, bool sparse,
-                       bool mfma) {
+DecodePlan plan_decode(int n_seqs, int n_kv, int nb, int acc_w, int rows, int max_blocks, int block_size,
+                       bool sparse, bool mfma) {
     DecodePlan p{};
     p.rows = rows;
     if (mfma) p.rows_pad = rows <= 8 ? 8 : 16;
@@ -196,7 +206,7 @@ DecodePlan plan_decode(int n_seqs, int n_kv, int nb, int rows, int max_blocks, i
     size_t off = 0;
     p.off_qrot = off;  if (!mfma) off = align256(off + units * kD * p.rows_pad * sizeof(float));
     p.off_ml = off;    off = align256(off + units * p.n_chunks * p.rows_pad * nb * 2 * sizeof(float));
-    p.off_acc = off;   off = align256(off + units * p.n_chunks * p.rows_pad * nb * kD * sizeof(float));
+    p.off_acc = off;   off = align256(off + units * p.n_chunks * p.rows_pad * acc_w * sizeof(float));
     p.off_tile = off;  if (sparse) off = align256(off + units * p.n_tiles * p.rows_pad * sizeof(float));
     p.off_stats = off; if (sparse && !mfma) off = align256(off + units * p.rows_pad * 2 * sizeof(float));
     p.total = off;
@@ -351,6 +361,37 @@ tq_status tq_fit_codebook(int32_t bits, const uint16_t *vectors, int64_t n_vecto
     return TQ_OK;
 }
 
+tq_status tq_select_outlier_channels(const uint16_t *vectors, int64_t n_vectors, int32_t n_heads, int32_t k,
+                                     uint8_t *channels) {
+    if (!vectors || !channels || n_vectors < 1 || n_heads < 1 || k < 1 || k > TQ_MAX_OUTLIERS)
+        return TQ_ERR_INVALID_ARG;
+    // sums of squares per (head, channel) over the finite vectors
+    std::vector<double> ss((size_t)n_heads * 128, 0.0);
+    double x[128];
+    for (int64_t i = 0; i < n_vectors; ++i) {
+        const uint16_t *v = vectors + i * 128;
+        bool finite = true;
+        for (int c = 0; c < 128; ++c) {
+            x[c] = half_to_double(v[c]);
+            finite = finite && isfinite(x[c]);
+        }
+        if (!finite) continue;
+        double *acc = ss.data() + (size_t)(i % n_heads) * 128;
+        for (int c = 0; c < 128; ++c) acc[c] += x[c] * x[c];
+    }
+    // the count of a head's vectors is the same for all its channels: sums rank as means
+    for (int h = 0; h < n_heads; ++h) {
+        const double *acc = ss.data() + (size_t)h * 128;
+        int order[128];
+        for (int c = 0; c < 128; ++c) order[c] = c;
+        std::stable_sort(order, order + 128, [&](int a, int b) { return acc[a] > acc[b]; });
+        std::sort(order, order + k);
+        uint8_t *out = channels + (size_t)h * 16;
+        for (int s = 0; s < 16; ++s) out[s] = s < k ? (uint8_t)order[s] : 0;
+    }
+    return TQ_OK;
+}
+
 tq_status tq_quantize_kv(const tq_cache *k, const void *k_src, const tq_cache *v, const void *v_src,
                          int64_t src_token_stride, int32_t n_tokens, const int64_t *slot_mapping,
                          void *stream) {
@@ -408,6 +449,9 @@ tq_status tq_dequantize(const tq_cache *c, const int64_t *slots, int32_t n_token
     a.bs_div = make_fastdiv((uint32_t)c->block_size);
     if (c->bits != TQ_BITS_FP16)
         for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = i < c->cb.n_levels ? c->cb.centroids[i] : 0.f;
+    a.n_out = c->n_outliers;
+    a.out_idx = c->outlier_channels;
+    a.outliers = c->outliers;
     if (launch_dequantize(a, c->bits, static_cast<hipStream_t>(stream)) != hipSuccess) return TQ_ERR_HIP;
     return TQ_OK;
 }
@@ -438,7 +482,9 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     // a compressed side
     const bool k_fp16 = k->bits == TQ_BITS_FP16;
     const int nb = blocks_per_head(k);
-    if (v->bits == TQ_BITS_FP16 || ((k_fp16 || nb > 1) && !use_mfma_decode())) return TQ_ERR_UNSUPPORTED;
+    const bool v_out = v->n_outliers > 0;
+    if (k->n_outliers > 0) return TQ_ERR_UNSUPPORTED;
+    if (v->bits == TQ_BITS_FP16 || ((k_fp16 || nb > 1 || v_out) && !use_mfma_decode())) return TQ_ERR_UNSUPPORTED;
     if (!is_aligned(v->codes, 4)) return TQ_ERR_INVALID_ARG;
     if (n_seqs < 0 || n_qtok < 1 || n_q_heads < 1 || max_blocks_per_seq < 1) return TQ_ERR_INVALID_ARG;
     if (n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
@@ -454,8 +500,9 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
         return TQ_ERR_UNSUPPORTED;
     const bool sparse = sparse_v_tau > 0.f;
     const bool mfma = use_mfma_decode();
-    const DecodePlan p = plan_decode(n_seqs, k->n_kv_heads, nb, (int)rows, max_blocks_per_seq, k->block_size,
-                                     sparse, mfma);
+    const int acc_w = nb * kD + (v_out ? TQ_MAX_OUTLIERS : 0);
+    const DecodePlan p = plan_decode(n_seqs, k->n_kv_heads, nb, acc_w, (int)rows, max_blocks_per_seq,
+                                     k->block_size, sparse, mfma);
     if ((int64_t)n_seqs * k->n_kv_heads * p.n_chunks > 0x7FFFFFFFLL) return TQ_ERR_UNSUPPORTED;
     if (!workspace) {
         *workspace_bytes = n_seqs == 0 ? 0 : p.total;
@@ -512,6 +559,10 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     a.v_bits = v->bits;
     a.nb = nb;
     a.nb_log2 = nb == 4 ? 2 : nb == 2 ? 1 : 0;
+    a.n_out = v->n_outliers;
+    a.v_out_idx = v->outlier_channels;
+    a.v_outliers = v->outliers;
+    a.acc_w = acc_w;
     a.mfma = mfma ? 1 : 0;
     a.contig = (k->block_size % kSlice == 0 && is_aligned(k->norms, 16) && is_aligned(v->norms, 16)) ? 1 : 0;
     for (int i = 0; i < TQ_MAX_LEVELS; ++i) {

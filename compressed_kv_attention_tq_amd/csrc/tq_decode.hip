@@ -456,8 +456,10 @@ __global__ __launch_bounds__(256) void tq_stats_kernel(DecodeArgs a) {
 // --------------------------------------------------------------------------
 // Merge the chunk partials of one 128-element block of one output row and
 // inverse-rotate it (both pass kernels write the same partial layout: per chunk
-// and row, (max, sum) per head block and the accumulator [block][128]).  One
-// block per (row, head block): 8 chunk groups x 32 float4 columns.  Dense: each thread merges its chunks (c = group,
+// and row, (max, sum) per head block and acc_w floats: the accumulator
+// [block][128], then, with kept V channels, their 16 sums, which replace the
+// rotated result at their channels).  One block per (row, head block): 8 chunk
+// groups x 32 float4 columns (+ 4 columns of kept sums).  Dense: each thread merges its chunks (c = group,
 // group + 8, ...) with the log-sum-exp rule in batches of 16 loads, then the
 // groups are merged through LDS and o = s_V * H (acc / L) / sqrt(128).  Gated:
 // the partials are already normalised and are summed.
@@ -466,8 +468,9 @@ template <bool SPARSE>
 __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     typedef float f4_t __attribute__((ext_vector_type(4)));
     __shared__ float gm[8], gl[8];
-    __shared__ __attribute__((aligned(16))) float gx[8][kD];
-    __shared__ float y[kD];
+    __shared__ __attribute__((aligned(16))) float gx[8][kD + 16];
+    __shared__ float y[kD + 16];
+    __shared__ int32_t cslot[kD];   // kept channel -> its slot, or -1
     const int tid = threadIdx.x, lane = tid & 63;
     const int cg = tid >> 5, q4 = tid & 31;
     const int nb = a.nb, hb = blockIdx.x & (nb - 1);      // head block (nb a power of two)
@@ -481,15 +484,18 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     const int len = a.seq_lens[b];
     const int nc = len > 0 ? (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div) : 0;
     const int64_t base = ((int64_t)b * a.n_kv + kv) * a.n_chunks;
-    const int64_t mstride = (int64_t)a.rows_pad * nb * 2, astride = (int64_t)a.rows_pad * nb * kD;
+    const int n_out = a.n_out;   // (head blocks and kept channels do not meet: nb = 1 then)
+    if (tid < kD) cslot[tid] = -1;
+    const int64_t mstride = (int64_t)a.rows_pad * nb * 2, astride = (int64_t)a.rows_pad * a.acc_w;
     const float *ml = a.part_ml + ((base * a.rows_pad + r) * nb + hb) * 2;                // chunk c at ml[c * mstride]
-    const float *pa = a.part_acc + ((base * a.rows_pad + r) * nb + hb) * kD + 4 * q4;     // chunk c at pa[c * astride]
+    const float *pa = a.part_acc + (base * a.rows_pad + r) * a.acc_w + hb * kD + 4 * q4;  // chunk c at pa[c * astride]
+    const bool xo = n_out > 0 && q4 < 4;   // this thread also merges kept sums 4 q4 .. 4 q4 + 3
     float M = -INFINITY, L = 0.f;
-    f4_t x = {0.f, 0.f, 0.f, 0.f};
+    f4_t x = {0.f, 0.f, 0.f, 0.f}, x2 = {0.f, 0.f, 0.f, 0.f};
     constexpr int kB = 16;   // chunks per thread per batch (one round of loads)
     for (int c0 = cg; c0 < nc; c0 += 8 * kB) {
         float m[kB], l[kB];
-        f4_t v[kB];
+        f4_t v[kB], v2[kB];
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
             const int cc = c0 + 8 * i;
@@ -497,21 +503,27 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
             m[i] = (!SPARSE && ok) ? ml[cc * mstride] : -INFINITY;
             l[i] = (!SPARSE && ok) ? ml[cc * mstride + 1] : 0.f;
             v[i] = ok ? *reinterpret_cast<const f4_t *>(pa + cc * astride) : f4_t{0.f, 0.f, 0.f, 0.f};
+            v2[i] = (ok && xo) ? *reinterpret_cast<const f4_t *>(pa + cc * astride + kD) : f4_t{0.f, 0.f, 0.f, 0.f};
         }
         if (SPARSE) {
 #pragma unroll
-            for (int i = 0; i < kB; ++i) x += v[i];
+            for (int i = 0; i < kB; ++i) {
+                x += v[i];
+                x2 += v2[i];
+            }
         } else {
             float mb = M;
 #pragma unroll
             for (int i = 0; i < kB; ++i) mb = fmaxf(mb, m[i]);
             const float sc = exp2_diff(M, mb);
             x *= sc;
+            x2 *= sc;
             L *= sc;
 #pragma unroll
             for (int i = 0; i < kB; ++i) {
                 const float f = exp2_diff(m[i], mb);
                 x += f * v[i];
+                x2 += f * v2[i];
                 L += f * l[i];
             }
             M = mb;
@@ -522,8 +534,10 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
         gl[cg] = L;
     }
     *reinterpret_cast<f4_t *>(&gx[cg][4 * q4]) = x;
+    if (xo) *reinterpret_cast<f4_t *>(&gx[cg][kD + 4 * q4]) = x2;
     __syncthreads();
-    if (tid < kD) {
+    const int ny = kD + (n_out > 0 ? 16 : 0);
+    if (tid < ny) {
         float Mx = -INFINITY;
 #pragma unroll
         for (int k = 0; k < 8; ++k) Mx = fmaxf(Mx, gm[k]);
@@ -536,6 +550,7 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
         }
         y[tid] = SPARSE ? ys : (Ls > 0.f ? ys / Ls : 0.f);
     }
+    if (tid < n_out) cslot[a.v_out_idx[kv * 16 + tid] & (kD - 1)] = tid;
     __syncthreads();
     if (tid >= 64) return;
     // o = s_V * H acc / sqrt(128)
@@ -545,6 +560,11 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     const float k = 0.088388347648318440550f;
     a0 *= ((sg[lane >> 5] >> (lane & 31)) & 1u) ? -k : k;
     a1 *= ((sg[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -k : k;
+    if (n_out > 0) {   // kept channels: their own sums
+        const int s0 = cslot[lane], s1 = cslot[lane + 64];
+        if (s0 >= 0) a0 = y[kD + s0];
+        if (s1 >= 0) a1 = y[kD + s1];
+    }
     float *o = a.out + ((((int64_t)b * a.n_qtok + jq) * a.n_q_heads + h) * nb + hb) * kD;
     o[lane] = a0;
     o[lane + 64] = a1;

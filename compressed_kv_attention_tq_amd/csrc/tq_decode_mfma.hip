@@ -41,6 +41,13 @@
 // back the sum in the same order, so they hold bitwise equal scores and softmax
 // state; each keeps the V accumulator of its own block.  Register use is that
 // of one block; the block's waves meet at two LDS barriers per slice.
+//
+// OV: the V side keeps n_out <= 16 channels per head in float16 ([llama-tq] V with
+// outlier-channel separation).  They add one value MFMA per 32 tokens whose A
+// rows are the kept channels (A[slot][token] = the stored float16 value, exact)
+// and whose B operand is the softmax weight without the V norm; the 16 sums per
+// row travel after the 128 rotated-domain sums and the merge writes them over
+// their channels.
 #include "tq_decode_common.h"
 
 namespace tq {
@@ -230,7 +237,7 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int KB, int VB, bool PK, int MODE, bool CONTIG, int NB>
+template <int KB, int VB, bool PK, int MODE, bool CONTIG, int NB, bool OV>
 __global__ __launch_bounds__(kMBlock) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<PK, VB, MODE>(), 8)))
 void tq_decode_mfma_kernel(
     DecodeArgs a, PairTables pt, const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
@@ -248,6 +255,10 @@ void tq_decode_mfma_kernel(
     constexpr int NQB = PK ? 4 : 8;                 // q'' B fragments
     constexpr int NPB = PK ? 2 : 4;                 // weight B fragments
     constexpr int NG = kMW / NB;                    // wave groups: slices the block has in flight
+    static_assert(!OV || (NB == 1 && MODE != MODE_SCORE), "kept V channels: 128-wide heads, passes with V");
+    constexpr int RW = NB * kD + (OV ? 16 : 0);     // floats per row of a chunk partial
+    constexpr int WRW = kD + (OV ? 16 : 0);         // floats per row of one wave's (block's) sums
+    constexpr int WRP = WRW + 4;                    // the same, padded (merge of 9-16 rows)
     constexpr int NS = PK ? 32 : 64;                // exchange slots per tile and wave (lanes
                                                     // holding distinct score columns)
     // the replicated K and V pair tables while slices are processed; afterwards the
@@ -259,7 +270,7 @@ void tq_decode_mfma_kernel(
     constexpr int kTabWords = (WV ? (NKT > NVT ? NKT : NVT) : NKT) * (RB / 4);   // (KF: the V halves only)
     // (NB > 1: q'' of every block, [block][row][kQS], passes through the area before
     // the tables are written)
-    constexpr int kMerge = PK ? kMW * 8 * kD : NB * 16 * kQS;
+    constexpr int kMerge = PK ? kMW * 8 * WRW : NB * 16 * WRP;
     constexpr int kQArea = NB > 1 ? NB * 16 * kQS : 0;
     constexpr int kArea0 = kTabWords > kMerge ? kTabWords : kMerge;
     constexpr int kArea = kArea0 > kQArea ? kArea0 : kQArea;
@@ -364,8 +375,13 @@ void tq_decode_mfma_kernel(
     struct Slot {
         uint32_t kw[4][KW];
         VUnit<VB> vw[2][8];
+        uint32_t ow[OV ? 2 : 1][OV ? 4 : 1];   // OV: kept values, float16 pairs (A operand)
         float knl, vnl;
     };
+    // OV: this lane's kept channel slot (row n of the A operand; lanes n >= n_out
+    // load a valid slot and use 0)
+    const int oslot = OV ? min(n, a.n_out - 1) : 0;
+    const bool olive = OV && n < a.n_out;
     Slot sa, sb;
     int myrow = 0;   // row of token base + lane (general page layout)
 
@@ -417,6 +433,42 @@ void tq_decode_mfma_kernel(
     };
     // V units of the slice's tokens; token (tile tm, e) of lane group g is loaded
     // only where keep(tm, e) holds (every token for the dense pass)
+    // (OV: the kept value of slot oslot of the same tokens, into the A pairs)
+    const uint16_t *__restrict__ v_kept = OV ? a.v_outliers : nullptr;
+    // Kept values are [page][head][slot][block_size]: the element of a cache row
+    // (page-row pr = row / bs, offset) is (pr n_out + slot) bs + offset.  Token
+    // 16 tm + 4 g + e is k index 4 (tm & 1) + e of operand half tm >> 1.
+    // Contiguous pages: the lane's 4 tokens of a tile are one 8-byte load.
+    auto load_kept_run = [&](Slot &sl, int64_t row0, auto keep) __attribute__((always_inline)) {
+        if constexpr (OV) {
+            const int pr = (int)fdiv((uint32_t)row0, bsdiv);
+            const int off = (int)row0 - pr * bs;
+            const uint16_t *op = v_kept + ((int64_t)pr * a.n_out + oslot) * bs + off + 4 * g;
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) {
+                uint2 t = make_uint2(0u, 0u);
+                if (keep(tm, 0) || keep(tm, 1) || keep(tm, 2) || keep(tm, 3))
+                    t = *reinterpret_cast<const uint2 *>(op + 16 * tm);
+                if (!keep(tm, 0)) t.x &= 0xFFFF0000u;
+                if (!keep(tm, 1)) t.x &= 0x0000FFFFu;
+                if (!keep(tm, 2)) t.y &= 0xFFFF0000u;
+                if (!keep(tm, 3)) t.y &= 0x0000FFFFu;
+                sl.ow[tm >> 1][2 * (tm & 1)] = t.x;
+                sl.ow[tm >> 1][2 * (tm & 1) + 1] = t.y;
+            }
+        }
+    };
+    // other pages: one float16 load per token, into its half of the pair
+    auto load_kept_one = [&](Slot &sl, int tm, int e, int row, bool k) __attribute__((always_inline)) {
+        if constexpr (OV) {
+            const int ee = 4 * (tm & 1) + e;
+            uint32_t &w = sl.ow[tm >> 1][ee >> 1];
+            const int pr = (int)fdiv((uint32_t)row, bsdiv);
+            const int64_t at = ((int64_t)pr * a.n_out + oslot) * bs + (row - pr * bs);
+            const uint32_t h = k ? (uint32_t)v_kept[at] : 0u;
+            w = (ee & 1) ? (w | (h << 16)) : h;
+        }
+    };
     auto load_v = [&](Slot &sl, int64_t row0, auto keep) __attribute__((always_inline)) {
         if constexpr (CONTIG) {
             const uint8_t *p = v_codes + (row0 + 4 * g) * VROW;
@@ -428,6 +480,7 @@ void tq_decode_mfma_kernel(
                     if (keep(tm, e)) load_vunit<VB>(p + (16 * tm + e) * VROW, vwi, u);
                     else u = VUnit<VB>{};
                 }
+            load_kept_run(sl, row0, keep);
             sl.vnl = v_norms[row0 + lane];
         } else {
             const int32_t *rt = rowtab[wave];
@@ -439,6 +492,7 @@ void tq_decode_mfma_kernel(
                     VUnit<VB> &u = sl.vw[tm >> 1][4 * (tm & 1) + e];
                     if (keep(tm, e)) load_vunit<VB>(v_codes + (int64_t)rr[e] * VROW, vwi, u);
                     else u = VUnit<VB>{};
+                    load_kept_one(sl, tm, e, rr[e], keep(tm, e));
                 }
             }
             sl.vnl = v_norms[myrow];
@@ -716,6 +770,47 @@ void tq_decode_mfma_kernel(
     f4_t acc[WV ? 8 : 1];
 #pragma unroll
     for (int j = 0; j < (WV ? 8 : 1); ++j) acc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+    f4_t acc_o = f4_t{0.f, 0.f, 0.f, 0.f};   // OV: kept channel sums, D rows = slots
+    // OV: wo, the weights of the kept values (score layout, no V norm)
+    // (base: the slice; kept values of tokens past the chunk's end are not data and
+    // become 0, as a zero weight would not cancel a non-finite value)
+    auto kept_mfma = [&](const Slot &sl, const float (&wo)[4][4], int base) __attribute__((always_inline)) {
+        if constexpr (OV) {
+            uint32_t ow[2][4];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ow[ks][k] = sl.ow[ks][k];
+            if (base + 64 > end) {
+                const int dl = end - base - 4 * g;   // token 16 tm + 4 g + e is data iff 16 tm + e < dl
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int tm = 2 * ks + (k >> 1), e0 = 2 * (k & 1);
+                        if (16 * tm + e0 >= dl) ow[ks][k] &= 0xFFFF0000u;
+                        if (16 * tm + e0 + 1 >= dl) ow[ks][k] &= 0x0000FFFFu;
+                    }
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u4_t pb[2];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int tm = 2 * ks + (k >> 1), e0 = 2 * (k & 1);
+                    if constexpr (PK) {
+                        pb[0][k] = split_pair(wo[tm][e0], wo[tm][e0 + 1], losel);
+                    } else {
+                        pb[0][k] = pk_rtz(wo[tm][e0], wo[tm][e0 + 1]);
+                        pb[1][k] = split_pair(wo[tm][e0], wo[tm][e0 + 1], 1.f);
+                    }
+                }
+                const u4_t af = olive ? u4_t{ow[ks][0], ow[ks][1], ow[ks][2], ow[ks][3]} : u4_t{0u, 0u, 0u, 0u};
+                acc_o = mfma_f16(af, pb[0], acc_o);
+                if constexpr (!PK) acc_o = mfma_f16(af, pb[1], acc_o);
+            }
+        }
+    };
     auto value_mfma = [&](const Slot &sl, const float (&w)[4][4]) {
         u4_t pb[NPB];
 #pragma unroll
@@ -771,7 +866,10 @@ void tq_decode_mfma_kernel(
             const float E_new = DENSE ? fmaxf(E_run, E_s) : 0.f;
             const float mu = (m_new == -INFINITY ? 0.f : m_new) + E_new;
             const float alpha = exp2_diff(m_state, mu);
-            float lsum = 0.f, w[4][4];
+            // OV: kept sums are relative to 2^m (weights 2^(s - m) = ex 2^E, exact)
+            const float alpha_o = OV ? exp2_diff(m_raw, m_new) : 1.f;
+            const float eE = OV ? __builtin_ldexpf(1.f, (int)E_new) : 0.f;
+            float lsum = 0.f, w[4][4], wo[4][4];
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm) {
                 const f4_t vn = DENSE ? *reinterpret_cast<const f4_t *>(my_vn + 16 * tm + 4 * g) : f4_t{};
@@ -780,6 +878,7 @@ void tq_decode_mfma_kernel(
                     const float ex = __builtin_amdgcn_exp2f(s[tm][e] - mu);
                     lsum += ex;
                     if constexpr (DENSE) w[tm][e] = ex * vn[e];
+                    if constexpr (OV) wo[tm][e] = ex * eE;
                 }
             }
             lsum = xg_sum(lsum);
@@ -793,6 +892,10 @@ void tq_decode_mfma_kernel(
                     for (int j = 0; j < 8; ++j) acc[j] *= alpha;
                 }
                 value_mfma(sl, w);
+                if constexpr (OV) {
+                    acc_o *= alpha_o;
+                    kept_mfma(sl, wo, base);
+                }
             }
         };
         // one exit, at the top: a branch inside the loop would merge paths with
@@ -864,15 +967,20 @@ void tq_decode_mfma_kernel(
             }
             E_run = E_new;
             const float mu = mlog + E_new;
-            float w[4][4];
+            const float eE = OV ? __builtin_ldexpf(1.f, (int)E_new) : 0.f;
+            float w[4][4], wo[4][4];
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm) {
                 const f4_t vn = *reinterpret_cast<const f4_t *>(my_vn + 16 * tm + 4 * g);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[tm][e] = s[tm][e] >= sthr ? __builtin_amdgcn_exp2f(s[tm][e] - mu) * vn[e] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const float ex = s[tm][e] >= sthr ? __builtin_amdgcn_exp2f(s[tm][e] - mu) : 0.f;
+                    w[tm][e] = ex * vn[e];
+                    if constexpr (OV) wo[tm][e] = ex * eE;   // = p, the final weight
+                }
             }
             value_mfma(sa, w);
+            kept_mfma(sa, wo, base);
         }
     }
 
@@ -882,6 +990,10 @@ void tq_decode_mfma_kernel(
         for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[j][e] += dpp<kDppRor8>(acc[j][e]);
+        if constexpr (OV) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc_o[e] += dpp<kDppRor8>(acc_o[e]);
+        }
     }
     if constexpr (!GATED) {
         if (g == 0) {
@@ -891,13 +1003,14 @@ void tq_decode_mfma_kernel(
     }
     __syncthreads();   // also: every wave is done with the pair tables
     const bool writer = row_ok && (!PK || n < 8);
-    float scale = 1.f;
+    float scale = 1.f, scale_o = 1.f;   // (OV gated: the kept sums are final)
     // (over the waves of this wave's block: one per group)
     if constexpr (!GATED) {
         float M = -INFINITY;
 #pragma unroll
         for (int g2 = 0; g2 < NG; ++g2) M = fmaxf(M, wst[blk + NB * g2][n][0]);
         scale = exp2_diff(m_state, M);
+        if constexpr (OV) scale_o = exp2_diff(m_raw, M);
         if (grp == 0 && g == 0 && writer) {
             float L = 0.f;
 #pragma unroll
@@ -908,22 +1021,27 @@ void tq_decode_mfma_kernel(
     } else {
         scale = E_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(E_run);
     }
+    // part_acc rows are [block][128] (NB blocks), then (OV) the 16 kept-channel sums
     if constexpr (WV && PK) {
         if (writer) {
-            float *d = &mbuf[(wave * 8 + col_row) * kD];
+            float *d = &mbuf[(wave * 8 + col_row) * WRW];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) d[8 * (4 * g + e) + j] = acc[j][e] * scale;
+            if constexpr (OV) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[kD + 4 * g + e] = acc_o[e] * scale_o;
+            }
         }
         __syncthreads();
-        // part_acc rows are [row][block][128]
-        for (int i = tid; i < R * NB * kD; i += kMBlock) {
-            const int row = i / (NB * kD), pos = i - row * (NB * kD), bb = pos / kD, e = pos - bb * kD;
+        for (int i = tid; i < R * RW; i += kMBlock) {
+            const int row = i / RW, pos = i - row * RW;
+            const int bb = NB == 1 ? 0 : pos / kD, e = pos - bb * kD;
             float x = 0.f;
 #pragma unroll
-            for (int g2 = 0; g2 < NG; ++g2) x += mbuf[((bb + NB * g2) * 8 + row) * kD + e];
-            part_acc[(part * rp + row) * (NB * kD) + pos] = x;
+            for (int g2 = 0; g2 < NG; ++g2) x += mbuf[((bb + NB * g2) * 8 + row) * WRW + e];
+            part_acc[(part * rp + row) * RW + pos] = x;
         }
     } else if constexpr (WV) {
         for (int g2 = 0; g2 < NG; ++g2) {
@@ -932,15 +1050,23 @@ void tq_decode_mfma_kernel(
                 for (int j = 0; j < 8; ++j)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float *d = &mbuf[(blk * 16 + col_row) * kQS + 8 * (4 * g + e) + j];
+                        float *d = &mbuf[(blk * 16 + col_row) * WRP + 8 * (4 * g + e) + j];
                         *d = (g2 == 0 ? 0.f : *d) + acc[j][e] * scale;
                     }
+                if constexpr (OV) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float *d = &mbuf[col_row * WRP + kD + 4 * g + e];
+                        *d = (g2 == 0 ? 0.f : *d) + acc_o[e] * scale_o;
+                    }
+                }
             }
             __syncthreads();
         }
-        for (int i = tid; i < R * NB * kD; i += kMBlock) {
-            const int row = i / (NB * kD), pos = i - row * (NB * kD), bb = pos / kD, e = pos - bb * kD;
-            part_acc[(part * rp + row) * (NB * kD) + pos] = mbuf[(bb * 16 + row) * kQS + e];
+        for (int i = tid; i < R * RW; i += kMBlock) {
+            const int row = i / RW, pos = i - row * RW;
+            const int bb = NB == 1 ? 0 : pos / kD, e = pos - bb * kD;
+            part_acc[(part * rp + row) * RW + pos] = mbuf[(bb * 16 + row) * WRP + e];
         }
     }
 }
@@ -957,15 +1083,26 @@ static void launch_mfma_mode(const DecodeArgs &a, const PairTables &pt, int mode
     const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_kv * a.n_chunks)), block(kMBlock);
 #define TQ_MFMA_ARGS a, pt, a.k_codes, a.k_norms, a.v_codes, a.v_norms, a.q, a.block_table, a.seq_lens, a.part_ml, \
         a.part_acc, a.tilemax
-    if (mode == MODE_DENSE)
-        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG, NB>), grid, block, 0, s, ev0, ev1,
-                              0, TQ_MFMA_ARGS);
-    else if (mode == MODE_SCORE)
-        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG, NB>), grid, block, 0, s, ev0, ev1,
-                              0, TQ_MFMA_ARGS);
-    else
-        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB>), grid, block, 0, s, ev0, ev1,
-                              0, TQ_MFMA_ARGS);
+    // (kept V channels: 128-wide heads only, checked on the host)
+    const bool ov = NB == 1 && a.n_out > 0;
+    if (mode == MODE_DENSE) {
+        if (ov)
+            hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG, NB, NB == 1>), grid, block, 0,
+                                  s, ev0, ev1, 0, TQ_MFMA_ARGS);
+        else
+            hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG, NB, false>), grid, block, 0, s,
+                                  ev0, ev1, 0, TQ_MFMA_ARGS);
+    } else if (mode == MODE_SCORE) {
+        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG, NB, false>), grid, block, 0, s, ev0,
+                              ev1, 0, TQ_MFMA_ARGS);
+    } else {
+        if (ov)
+            hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB, NB == 1>), grid, block, 0,
+                                  s, ev0, ev1, 0, TQ_MFMA_ARGS);
+        else
+            hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB, false>), grid, block, 0, s,
+                                  ev0, ev1, 0, TQ_MFMA_ARGS);
+    }
 #undef TQ_MFMA_ARGS
 }
 

@@ -67,6 +67,11 @@ struct QuantSide {
     float grid;               // t = y * grid (cells of width 1/grid in y)
     int32_t n_bnd;            // 2^bits - 1
     float bnd[TQ_MAX_LEVELS - 1];
+    // kept channels (0: none): uint8 [n_kv][16] channel lists, float16 values
+    // [n_blocks][n_kv][n_out][block_size]
+    int32_t n_out;
+    const uint8_t *out_idx;
+    uint16_t *outliers;
 };
 
 struct QuantArgs {
@@ -87,6 +92,9 @@ struct DequantArgs {
     int32_t dst_fp16;
     FastDiv kv_div, bs_div;   // division by n_kv, block_size
     float cent[TQ_MAX_LEVELS];
+    int32_t n_out;            // kept channels (0: none), as in QuantSide
+    const uint8_t *out_idx;
+    const uint16_t *outliers;
 };
 
 // Decode attention.
@@ -104,7 +112,8 @@ struct DecodeArgs {
     // workspace sections
     float *qrot;              // [S][n_kv][128][RP]   rotated, scaled queries
     float *part_ml;           // [S][n_kv][n_chunks][RP][nb][2]  (max, sum) per chunk, log2 domain
-    float *part_acc;          // [S][n_kv][n_chunks][RP][nb][128] rotated-domain V accumulators
+    float *part_acc;          // [S][n_kv][n_chunks][RP][acc_w] rotated-domain V accumulators
+                              // ([nb][128], then 16 kept-channel sums)
     float *tilemax;           // [S][n_kv][n_tiles][RP]  (sparse only)
     float *stats;             // [S][n_kv][RP][2]  global (max, sum) (sparse only)
     int32_t n_seqs, n_qtok, n_q_heads, n_kv, group, rows, rows_pad;
@@ -119,6 +128,10 @@ struct DecodeArgs {
     float tau;
     int32_t k_bits, v_bits;
     int32_t nb, nb_log2;      // 128-element blocks per head (1, 2, 4; matrix-core path only)
+    int32_t n_out;            // V channels kept in float16 (0: none; matrix-core path, nb = 1)
+    const uint8_t *v_out_idx; // uint8 [n_kv][16] kept channels of each head
+    const uint16_t *v_outliers;   // float16 [n_blocks][n_kv][n_out][block_size] kept values
+    int32_t acc_w;            // floats per row of a chunk partial: 128 nb, + 16 with kept channels
     int32_t mfma;             // 1: matrix-core pass kernels, 0: vector-ALU kernels
     int32_t contig;           // matrix-core path: every 64-token slice lies in one page
     float kc[TQ_MAX_LEVELS];

@@ -42,7 +42,10 @@ __device__ void build_lut(const QuantSide &p, LutEntry *lut) {
     }
 }
 
-template <int BITS>
+// OUTL: the side keeps p.n_out channels per head in float16 ([llama-tq] V with
+// outlier-channel separation): they are zeroed before the norm and the rotation,
+// and lane j stores the values of slots 2j and 2j + 1.
+template <int BITS, bool OUTL>
 __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__restrict__ slots,
                                            LutEntry *lut, int blk, int nblk) {
     const Lane8 L = lane8();
@@ -80,8 +83,28 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
     for (int k = 0; k < 8; ++k)
         smask[k] = (((sb >> (2 * k)) & 1u) << 15) | (((sb >> (2 * k + 1)) & 1u) << 31);
 
+    // kept channels: and-masks of this lane's float16 pairs, and its two slots' channels
+    uint32_t keep[8];
+    int oc0 = 0, oc1 = 0;
+    if constexpr (OUTL) {
+        const uint4 iw = *reinterpret_cast<const uint4 *>(p.out_idx + head * 16);
+        const uint32_t words[4] = {iw.x, iw.y, iw.z, iw.w};
+        uint32_t om = 0;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const uint32_t c = (words[s >> 2] >> (8 * (s & 3))) & 127u;
+            if (s < p.n_out && (int)(c >> 4) == j) om |= 1u << (c & 15u);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            keep[k] = (((om >> (2 * k)) & 1u) ? 0u : 0xFFFFu) | (((om >> (2 * k + 1)) & 1u) ? 0u : 0xFFFF0000u);
+        oc0 = (int)((words[j >> 1] >> (16 * (j & 1))) & 127u);
+        oc1 = (int)((words[j >> 1] >> (16 * (j & 1) + 8)) & 127u);
+    }
+
     const float kscale = lane_sign(j) * p.grid * 0.088388347648318440550f;   // grid / sqrt(128)
     const uint16_t *src = p.src + (int64_t)head * kD + j * 16;
+    const uint16_t *vsrc = p.src + (int64_t)head * kD;   // the vector's first element
     const LutEntry *lut0 = lut + p.lut_half;
 
     // One group = 8 vectors (one per 8-lane block of the wave).  Two groups'
@@ -90,6 +113,7 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
     // loop exits only at the top, so a wait never covers the group loading behind it.
     struct Group {
         uint32_t w[8];
+        uint32_t o;       // OUTL: the float16 values of slots 2j, 2j + 1
         int64_t slot;
     };
     // past the wave's last group a load re-reads that group's rows (cached)
@@ -100,6 +124,10 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
         const uint4 a = sp[0], b = sp[1];
         gr.w[0] = a.x; gr.w[1] = a.y; gr.w[2] = a.z; gr.w[3] = a.w;
         gr.w[4] = b.x; gr.w[5] = b.y; gr.w[6] = b.z; gr.w[7] = b.w;
+        if constexpr (OUTL) {
+            const uint16_t *vp = vsrc + (int64_t)t * p.src_stride;
+            gr.o = (uint32_t)vp[oc0] | ((uint32_t)vp[oc1] << 16);
+        }
         gr.slot = slots[t];
     };
     auto encode = [&](const Group &gr, int g0) __attribute__((always_inline)) {
@@ -120,7 +148,7 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
         float ss = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            w[k] = gr.w[k] ^ smask[k];
+            w[k] = (OUTL ? gr.w[k] & keep[k] : gr.w[k]) ^ smask[k];
             const half2_t h = __builtin_bit_cast(half2_t, w[k]);
             ss = __builtin_amdgcn_fdot2(h, h, ss, false);
         }
@@ -180,6 +208,11 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
                 *reinterpret_cast<uint32_t *>(d + (odd ? 2 : 0)) = odd ? ((lo >> 16) | (hi << 16)) : lo;
             }
             if (j == 0) p.norms[row] = __fsqrt_rn(ss);
+            if constexpr (OUTL) {   // [page][head][slot][block_size]
+                uint16_t *od = p.outliers + ((int64_t)blk_id * p.n_kv + head) * p.n_out * p.block_size + off;
+                if (2 * j < p.n_out) od[(2 * j) * p.block_size] = (uint16_t)(gr.o & 0xFFFFu);
+                if (2 * j + 1 < p.n_out) od[(2 * j + 1) * p.block_size] = (uint16_t)(gr.o >> 16);
+            }
         }
     };
 
@@ -214,11 +247,19 @@ __global__ __launch_bounds__(256) void tq_quantize_kernel(QuantArgs a) {
     const QuantSide &p = second ? a.side[1] : a.side[0];
     const int blk = second ? (int)blockIdx.x - a.blocks_k : (int)blockIdx.x;
     const int nblk = second ? (int)gridDim.x - a.blocks_k : a.blocks_k;
+    if (p.n_out > 0) {   // kept channels (compressed sides only)
+        switch (p.bits) {
+            case 2: quant_side<2, true>(p, a.slots, lut, blk, nblk); break;
+            case 3: quant_side<3, true>(p, a.slots, lut, blk, nblk); break;
+            default: quant_side<4, true>(p, a.slots, lut, blk, nblk); break;
+        }
+        return;
+    }
     switch (p.bits) {
-        case 2: quant_side<2>(p, a.slots, lut, blk, nblk); break;
-        case 3: quant_side<3>(p, a.slots, lut, blk, nblk); break;
-        case 16: quant_side<16>(p, a.slots, lut, blk, nblk); break;   // float16 side
-        default: quant_side<4>(p, a.slots, lut, blk, nblk); break;
+        case 2: quant_side<2, false>(p, a.slots, lut, blk, nblk); break;
+        case 3: quant_side<3, false>(p, a.slots, lut, blk, nblk); break;
+        case 16: quant_side<16, false>(p, a.slots, lut, blk, nblk); break;   // float16 side
+        default: quant_side<4, false>(p, a.slots, lut, blk, nblk); break;
     }
 }
 
@@ -347,6 +388,17 @@ __global__ __launch_bounds__(256) void tq_dequantize_kernel(DequantArgs a) {
                 d[1] = make_float4(o[4], o[5], o[6], o[7]);
                 d[2] = make_float4(o[8], o[9], o[10], o[11]);
                 d[3] = make_float4(o[12], o[13], o[14], o[15]);
+            }
+            // kept channels: their stored values over the reconstruction (this thread
+            // wrote those elements above, so its later stores land last)
+            const int64_t prow = a.n_out > 0 ? row / a.block_size : 0, poff = row - prow * a.block_size;
+            for (int s = 0; s < a.n_out; ++s) {
+                const int c = a.out_idx[head * 16 + s] & 127;
+                if ((c >> 4) != j) continue;
+                const uint16_t hv = a.outliers[(prow * a.n_out + s) * a.block_size + poff];
+                const int64_t di = ((int64_t)tok * a.n_kv + head) * kD + c;
+                if (a.dst_fp16) static_cast<uint16_t *>(a.dst)[di] = hv;
+                else static_cast<float *>(a.dst)[di] = (float)__builtin_bit_cast(_Float16, hv);
             }
         }
     }

@@ -24,10 +24,11 @@ HEAD_DIM = 128   # elements per block; a head is 1, 2 or 4 blocks (head_dim 128,
 BITS_FP16 = 16   # a cache side kept in float16 (TQ_BITS_FP16)
 MAX_LEVELS = 16
 MAX_ROWS_PER_KV_HEAD = 16
+MAX_OUTLIERS = 16   # kept channels per head (TQ_MAX_OUTLIERS)
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
-EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_fit_codebook", "tq_quantize_kv", "tq_decode_attention",
-           "tq_decode_attention_timed", "tq_dequantize")
+EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_fit_codebook", "tq_select_outlier_channels",
+           "tq_quantize_kv", "tq_decode_attention", "tq_decode_attention_timed", "tq_dequantize")
 
 
 class TQError(RuntimeError):
@@ -66,6 +67,9 @@ class TQCache(ctypes.Structure):
         ("norms", ctypes.c_void_p),
         ("signs", ctypes.c_void_p),
         ("cb", TQCodebook),
+        ("n_outliers", ctypes.c_int32),
+        ("outlier_channels", ctypes.c_void_p),
+        ("outliers", ctypes.c_void_p),
     ]
 
 
@@ -87,6 +91,9 @@ def load_library(path: str = LIB_PATH):
     lib.tq_fit_codebook.restype = ctypes.c_int
     lib.tq_fit_codebook.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(TQCodebook)]
+    lib.tq_select_outlier_channels.restype = ctypes.c_int
+    lib.tq_select_outlier_channels.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_void_p]
     lib.tq_quantize_kv.restype = ctypes.c_int
     lib.tq_quantize_kv.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.POINTER(TQCache),
                                    ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
@@ -137,6 +144,19 @@ def tq_fit_codebook(bits: int, vectors, sign_words, max_iter: int = 200) -> TQCo
     return cb
 
 
+def tq_select_outlier_channels(vectors, k: int) -> np.ndarray:
+    """Kept channels per head from host float16 vectors [..., n_heads, 128]: uint8
+    [n_heads, 16], the k channels of largest mean square (ascending), then zeros."""
+    v = np.ascontiguousarray(np.asarray(vectors, dtype=np.float16))
+    if v.ndim < 2 or v.shape[-1] != HEAD_DIM:
+        raise ValueError("vectors must be [..., n_heads, 128] float16")
+    n_heads = v.shape[-2]
+    out = np.zeros((n_heads, 16), np.uint8)
+    _check(load_library().tq_select_outlier_channels(v.ctypes.data, v.size // HEAD_DIM, n_heads, k,
+                                                     out.ctypes.data), "tq_select_outlier_channels")
+    return out
+
+
 # ---------------------------------------------------------------------------- caches
 
 def _torch():
@@ -176,10 +196,16 @@ class Cache:
     signs: object      # torch.int32 (bit pattern of uint32) [n_kv_heads * nb, 4]
     cb: TQCodebook
     head_dim: int = HEAD_DIM
+    n_outliers: int = 0
+    outlier_channels: object = None   # torch.uint8 [n_kv_heads, 16] (kept channels, ascending)
+    outliers: object = None           # torch.float16 [n_blocks, n_kv_heads, n_outliers, block_size]
 
     @classmethod
     def allocate(cls, bits, n_kv_heads, block_size, n_blocks, sign_words, device="cuda", cb=None,
-                 head_dim=HEAD_DIM):
+                 head_dim=HEAD_DIM, outlier_channels=None):
+        """outlier_channels: None, or [n_kv_heads, k] (k <= 16) channels per head kept in
+        float16 (a 16-wide row as tq_select_outlier_channels returns needs k given via
+        a [n_kv_heads, k] slice)."""
         torch = _torch()
         if head_dim not in (HEAD_DIM, 2 * HEAD_DIM, 4 * HEAD_DIM):
             raise ValueError("head_dim must be 128, 256 or 512")
@@ -190,8 +216,19 @@ class Cache:
         signs = torch.from_numpy(sw.view(np.int32)).to(device)
         if bits == BITS_FP16:
             cb = TQCodebook()   # a float16 side has no codebook
-        return cls(bits, n_kv_heads, block_size, n_blocks, codes, norms, signs,
-                   tq_build_codebook(bits) if cb is None else cb, head_dim)
+        c = cls(bits, n_kv_heads, block_size, n_blocks, codes, norms, signs,
+                tq_build_codebook(bits) if cb is None else cb, head_dim)
+        if outlier_channels is not None:
+            idx = np.asarray(outlier_channels, dtype=np.int64).reshape(n_kv_heads, -1)
+            k = idx.shape[1]
+            if not 1 <= k <= MAX_OUTLIERS:
+                raise ValueError(f"1..{MAX_OUTLIERS} kept channels per head")
+            rows = np.zeros((n_kv_heads, 16), np.uint8)
+            rows[:, :k] = np.sort(idx, axis=1)
+            c.n_outliers = k
+            c.outlier_channels = torch.from_numpy(rows).to(device)
+            c.outliers = torch.zeros((n_blocks, n_kv_heads, k, block_size), dtype=torch.float16, device=device)
+        return c
 
     def desc(self) -> TQCache:
         d = TQCache()
@@ -204,6 +241,10 @@ class Cache:
         d.norms = _dev_ptr(self.norms, "norms").value
         d.signs = _dev_ptr(self.signs, "signs").value
         d.cb = self.cb
+        d.n_outliers = self.n_outliers
+        if self.n_outliers:
+            d.outlier_channels = _dev_ptr(self.outlier_channels, "outlier_channels").value
+            d.outliers = _dev_ptr(self.outliers, "outliers").value
         return d
 
 

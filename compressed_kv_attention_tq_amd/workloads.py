@@ -30,6 +30,9 @@ model here, so these synthetic tensors stand in for real K/V activations):
   llama8b_d256, llama8b_d512
             the llama8b decode with heads of 256 / 512 elements (two / four
             128-element blocks, each with its own sign words).
+  llama8b_vout
+            the llama8b decode whose V has 4 outlier channels x20 (the same 4
+            in every head), for a V side that keeps 8 channels in float16.
 """
 
 from __future__ import annotations
@@ -71,6 +74,8 @@ class DecodeWorkload:
     kind: str                   # value recipe: tiny | llama8b | normal | longctx
     seed: int = 0
     head_dim: int = HEAD_DIM    # a multiple of 128: head_dim / 128 blocks per head
+    v_planted: int = 0          # V channels scaled x20 in every head (at most 4)
+    v_kept: int = 0             # channels per head the V side keeps in float16 (0: none)
 
     @property
     def blocks_per_head(self) -> int:
@@ -124,7 +129,13 @@ class DecodeWorkload:
             anchors, pos, ra = self._anchor_plan(seq)
             for h in range(self.n_kv_heads):
                 k[pos[h], h, :] = anchors[h] + 0.1 * ra.standard_normal((64, self.head_dim))
+        if self.v_planted:
+            v[:, :, self._outlier_channels[1][: self.v_planted]] *= 20.0
         return k.astype(np.float16), v.astype(np.float16)
+
+    def warmup_v(self, n_tokens: int = 1024) -> np.ndarray:
+        """float16 V of the first n_tokens positions of sequence 0 (warm-up data)."""
+        return self.kv_source(0)[1][:n_tokens]
 
     def queries(self) -> np.ndarray:
         """float16 [n_seqs, n_qtok, n_q_heads, head_dim]."""
@@ -179,6 +190,14 @@ def llama8b_wide(head_dim: int, seed: int = 0, context: int = 32768) -> DecodeWo
     table, nb = _identity_table(1, context, 256)
     return DecodeWorkload(f"llama8b_d{head_dim}", 1, 1, 32, 8, 4, 3, 0.0, 256,
                           np.array([context], np.int32), table, nb, "llama8b", seed, head_dim)
+
+
+def llama8b_vout(seed: int = 0, context: int = 32768) -> DecodeWorkload:
+    """The Llama-3-8B-shaped decode (K4 / V3) with 4 planted V outlier channels x20
+    and a V side keeping 8 channels per head in float16."""
+    table, nb = _identity_table(1, context, 256)
+    return DecodeWorkload("llama8b_vout", 1, 1, 32, 8, 4, 3, 0.0, 256,
+                          np.array([context], np.int32), table, nb, "llama8b", seed, v_planted=4, v_kept=8)
 
 
 def longctx(seed: int = 0, context: int = 131072, batch: int = 4) -> DecodeWorkload:
@@ -238,7 +257,8 @@ def prefill(seed: int = 0) -> PrefillWorkload:
 
 def small_decode(seed: int, n_seqs: int, lens, n_qtok: int, n_q_heads: int, n_kv_heads: int,
                  k_bits: int, v_bits: int, tau: float = 0.0, block_size: int = 256,
-                 shuffle_pages: bool = True, head_dim: int = HEAD_DIM) -> DecodeWorkload:
+                 shuffle_pages: bool = True, head_dim: int = HEAD_DIM, v_planted: int = 0,
+                 v_kept: int = 0) -> DecodeWorkload:
     """A small ragged, paged workload with N(0,1) K/V/q for parity tests."""
     lens = np.asarray(lens, np.int32)
     max_blocks = max(1, int(-(-int(np.max(lens)) // block_size))) if n_seqs else 1
@@ -252,4 +272,4 @@ def small_decode(seed: int, n_seqs: int, lens, n_qtok: int, n_q_heads: int, n_kv
         table[b, : need[b]] = perm[at: at + need[b]]
         at += need[b]
     return DecodeWorkload("small", n_seqs, n_qtok, n_q_heads, n_kv_heads, k_bits, v_bits, tau,
-                          block_size, lens, table, n_blocks, "normal", seed, head_dim)
+                          block_size, lens, table, n_blocks, "normal", seed, head_dim, v_planted, v_kept)

@@ -73,6 +73,7 @@ typedef enum tq_status {
 #define TQ_MAX_LEVELS 16
 #define TQ_BITS_FP16 16   /* a cache side kept in float16: see tq_cache */
 #define TQ_MAX_ROWS_PER_KV_HEAD 16   /* (n_q_heads / n_kv_heads) * n_qtok */
+#define TQ_MAX_OUTLIERS 16           /* channels per head a side may keep in float16 */
 
 /* Scalar codebook of one cache side ([TQ blog] 3.3).  Centroids are the Lloyd-Max
  * quantizer of N(0, sigma^2) rounded to float16-exact values; boundaries are the
@@ -108,6 +109,20 @@ typedef struct tq_cache {
     const uint32_t *signs;  /* device uint32 [n_kv_heads][nb][4]; bit i of word w of block k
                                set means element 128*k+32*w+i is multiplied by -1 before H */
     tq_codebook cb;         /* by value */
+    /* Kept channels ([llama-tq]: the V family with outlier-channel separation, its
+     * high-quality tier): 0, or 1..TQ_MAX_OUTLIERS channels of every head stored
+     * exactly as float16 for each token.  The vector with those channels set to
+     * zero is what the norm, rotation and codes above describe; the dequantized
+     * vector carries the stored values at those channels.  Only a compressed side
+     * (bits 2..4) with head_dim 128; in tq_decode_attention only the V side.
+     * Zero n_outliers: the two pointers are not used (may be NULL). */
+    int32_t  n_outliers;
+    const uint8_t *outlier_channels;   /* device uint8 [n_kv_heads][16], 16-byte aligned: the
+                                          first n_outliers bytes of each row are the head's
+                                          channels, distinct and < 128 (see
+                                          tq_select_outlier_channels) */
+    uint16_t *outliers;     /* device float16 [n_blocks][n_kv_heads][n_outliers][block_size]
+                               (slot-major within a page), 8-byte aligned */
 } tq_cache;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -147,6 +162,21 @@ tq_status tq_build_codebook(int32_t bits, double sigma, tq_codebook *out);
 tq_status tq_fit_codebook(int32_t bits, const uint16_t *vectors, int64_t n_vectors, int32_t n_heads,
                           const uint32_t *signs, int32_t max_iter, tq_codebook *out);
 
+/* Kept channels of each head from warm-up data (the [TQ blog] 5.3 advice to adapt
+ * to the task's data): for every head, the k channels with the largest mean
+ * square over its vectors, ties to the lower channel, in ascending order.
+ *   vectors  : host float16 [n_vectors][128]; vector i belongs to head i % n_heads
+ *              (a token-major [n_tokens][n_heads][128] array works as is); vectors
+ *              with a non-finite element are skipped.
+ *   k        : 1..TQ_MAX_OUTLIERS.
+ *   channels : host uint8 [n_heads][16], filled: k channels, then zeros (the
+ *              layout of tq_cache.outlier_channels, to be copied to the device).
+ * Host only; deterministic; allocates host memory for the sums only.
+ * Errors: TQ_ERR_INVALID_ARG (NULL pointer, n_vectors or n_heads < 1, k outside
+ *         1..TQ_MAX_OUTLIERS). */
+tq_status tq_select_outlier_channels(const uint16_t *vectors, int64_t n_vectors, int32_t n_heads, int32_t k,
+                                     uint8_t *channels);
+
 /* Quantize-on-append ([TQ+ README] backend table, SET_ROWS for turbo types):
  * compress n_tokens new K and V rows and write them into their cache slots.
  *   k, v            : host descriptors; either may be NULL to skip that side.
@@ -157,7 +187,8 @@ tq_status tq_fit_codebook(int32_t bits, const uint16_t *vectors, int64_t n_vecto
  *   slot_mapping    : device int64 [n_tokens]; slot = block * block_size + offset,
  *                     0 <= slot < n_blocks * block_size; a negative slot skips the token.
  *   n_tokens        : >= 0 (0 is a no-op).
- * For each (token, head): norm -> cache.norms, 16*bits code bytes -> cache.codes.
+ * For each (token, head): norm -> cache.norms, 16*bits code bytes -> cache.codes,
+ * and (n_outliers > 0) the kept channels' values -> cache.outliers.
  * Errors: TQ_ERR_INVALID_ARG (missing pointers for a side that is given, bad
  *         stride or sizes, codebook inconsistent with bits), TQ_ERR_UNSUPPORTED
  *         (bits not 2..4 or 16, head_dim not 128/256/512), TQ_ERR_HIP. */
@@ -194,7 +225,8 @@ tq_status tq_quantize_kv(const tq_cache *k, const void *k_src,
  * (a multiple of 256 for the matrix-core pass, 512 for the vector-ALU pass)
  * overrides the tokens per pass block.  Both are read at every call and change
  * the workspace size.  A float16 K side and heads of more than one block need the
- * matrix-core pass (TQ_ERR_UNSUPPORTED with the vector-ALU pass).
+ * matrix-core pass (TQ_ERR_UNSUPPORTED with the vector-ALU pass), and so does a V
+ * side with kept channels (a K side with kept channels: TQ_ERR_UNSUPPORTED).
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 tq_status tq_decode_attention(const tq_cache *k, const tq_cache *v, const void *q,
                               int32_t n_seqs, int32_t n_qtok, int32_t n_q_heads,

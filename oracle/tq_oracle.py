@@ -399,7 +399,7 @@ class OracleCache:
     head_dim: int = D   # elements per head; n_sub = n_kv_heads * head_dim / 128 sub-heads (R12)
     n_outliers: int = 0                      # R13: channels per sub-head kept in float16
     outlier_channels: np.ndarray = None      # uint8 [n_sub, n_outliers], ascending
-    outliers: np.ndarray = None              # float16 [n_blocks, n_sub, block_size, n_outliers]
+    outliers: np.ndarray = None              # float16 [n_blocks, n_sub, n_outliers, block_size]
 
     @property
     def blocks_per_head(self) -> int:
@@ -441,20 +441,23 @@ def new_cache(bits, n_kv_heads, block_size, n_blocks, signs, cb, head_dim: int =
             raise ValueError("outlier channels of a head must be distinct")
         c.n_outliers = k
         c.outlier_channels = np.sort(idx, axis=1).astype(np.uint8)
-        c.outliers = np.zeros((n_blocks, n_sub, block_size, k), np.float16)
+        c.outliers = np.zeros((n_blocks, n_sub, k, block_size), np.float16)
     return c
 
 
 def select_outlier_channels(vectors: np.ndarray, k: int) -> np.ndarray:
     """R13: per head, the k channels with the largest mean square over the given
-    vectors [..., n_heads, 128] (float16 values), ties to the lower index;
-    returns uint8 [n_heads, k], each row ascending."""
+    vectors [..., n_heads, 128] (float16 values; a vector with a non-finite
+    element is skipped), ties to the lower index; returns uint8 [n_heads, k],
+    each row ascending."""
     x = np.asarray(vectors).astype(np.float64)
     x = x.reshape(-1, x.shape[-2], D)
-    ms = np.mean(x * x, axis=0)                       # [n_heads, 128]
-    out = np.zeros((ms.shape[0], k), np.uint8)
-    for h in range(ms.shape[0]):
-        order = sorted(range(D), key=lambda c: (-ms[h, c], c))
+    out = np.zeros((x.shape[1], k), np.uint8)
+    for h in range(x.shape[1]):
+        rows = x[:, h, :]
+        rows = rows[np.all(np.isfinite(rows), axis=1)]
+        ms = np.mean(rows * rows, axis=0) if len(rows) else np.zeros(D)
+        order = sorted(range(D), key=lambda c: (-ms[c], c))
         out[h] = np.sort(order[:k])
     return out
 
@@ -499,7 +502,7 @@ def cache_write(cache: OracleCache, src: np.ndarray, slots: np.ndarray):
         cache.codes[blk, :, off, :] = packed[t]
         cache.norms[blk, :, off] = norms[t]
         if kept is not None:
-            cache.outliers[blk, :, off, :] = kept[t]
+            cache.outliers[blk, :, :, off] = kept[t]
     return norms, codes, ys
 
 
@@ -518,7 +521,7 @@ def _read_sub(cache: OracleCache, blk: np.ndarray, off: np.ndarray, sub: int) ->
     codes = unpack_codes(packed, cache.bits)
     x = dequantize_vectors(norms, codes, sign_vector(cache.signs[sub]), cache.cb)
     if cache.n_outliers:   # R13: the kept values over their channels
-        x[:, cache.outlier_channels[sub].astype(np.int64)] = cache.outliers[blk, sub, off, :].astype(np.float64)
+        x[:, cache.outlier_channels[sub].astype(np.int64)] = cache.outliers[blk, sub, :, off].astype(np.float64)
     return x
 
 

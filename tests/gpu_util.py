@@ -28,14 +28,23 @@ def tq_codebook_from(ocb):
     return cb
 
 
+def oracle_kept_channels(wl):
+    """The V side's kept channels of a workload (oracle selection on its warm-up V), or None."""
+    if not wl.v_kept:
+        return None
+    return O.select_outlier_channels(wl.warmup_v(), wl.v_kept)
+
+
 def oracle_cache(wl, side, seqs=None, n_blocks=None, cb=None):
     """Quantize the workload's K (side 0) or V (side 1) with the oracle into pages
-    (with codebook cb, by default the Gaussian one)."""
+    (with codebook cb, by default the Gaussian one; V keeps the workload's kept channels)."""
     bits = wl.k_bits if side == 0 else wl.v_bits
     signs = wl.signs_k if side == 0 else wl.signs_v
     if bits != O.FP16:
         cb = O.build_codebook(bits) if cb is None else cb
-    c = O.new_cache(bits, wl.n_kv_heads, wl.block_size, n_blocks or wl.n_blocks, signs, cb, head_dim=wl.head_dim)
+    kept = oracle_kept_channels(wl) if side == 1 else None
+    c = O.new_cache(bits, wl.n_kv_heads, wl.block_size, n_blocks or wl.n_blocks, signs, cb, head_dim=wl.head_dim,
+                    outlier_channels=kept)
     for b in (range(wl.n_seqs) if seqs is None else seqs):
         if int(wl.seq_lens[b]) == 0:
             continue
@@ -48,9 +57,12 @@ def gpu_cache_from(oc, device="cuda"):
     """A device cache holding exactly the oracle cache's codes, norms and codebook."""
     t = torch()
     g = T.Cache.allocate(oc.bits, oc.n_kv_heads, oc.block_size, oc.n_blocks, oc.signs, device,
-                         cb=None if oc.bits == O.FP16 else tq_codebook_from(oc.cb), head_dim=oc.head_dim)
+                         cb=None if oc.bits == O.FP16 else tq_codebook_from(oc.cb), head_dim=oc.head_dim,
+                         outlier_channels=oc.outlier_channels if oc.n_outliers else None)
     g.codes.copy_(t.from_numpy(oc.codes))
     g.norms.copy_(t.from_numpy(oc.norms))
+    if oc.n_outliers:
+        g.outliers.copy_(t.from_numpy(oc.outliers))
     return g
 
 
@@ -60,6 +72,8 @@ def upload_blocks(oc, g, blocks):
     idx = t.as_tensor(np.asarray(blocks, np.int64), device=g.codes.device)
     g.codes.index_copy_(0, idx, t.from_numpy(oc.codes[blocks]).to(g.codes.device))
     g.norms.index_copy_(0, idx, t.from_numpy(oc.norms[blocks]).to(g.norms.device))
+    if oc.n_outliers:
+        g.outliers.index_copy_(0, idx, t.from_numpy(oc.outliers[blocks]).to(g.outliers.device))
 
 
 def row_rel_err(got, want):

@@ -263,3 +263,61 @@ def test_float16_side_validation(monkeypatch):
     lib = T.load_library()
     assert lib.tq_quantize_kv(ctypes.byref(k16), FAKE, None, None, 2 * 128, 0, None, None) == T.TQ_OK
     assert lib.tq_dequantize(ctypes.byref(k16), FAKE, 0, FAKE, 0, None) == T.TQ_OK
+
+
+# ------------------------------------------------------------------ kept V channels
+
+def test_select_outlier_channels_matches_oracle():
+    """tq_select_outlier_channels (host) against the oracle's selection: planted
+    channels, non-finite vectors skipped, k from 1 to 16, several heads."""
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((300, 5, 128)) * rng.lognormal(0, 0.5, (1, 5, 128))
+    x[:, 2, [3, 70, 71]] *= 25
+    x = x.astype(np.float16)
+    x[7, 1, 9] = np.float16(np.inf)
+    x[8, 4, 100] = np.float16(np.nan)
+    for k in (1, 5, 16):
+        got = T.tq_select_outlier_channels(x, k)
+        want = O.select_outlier_channels(x, k)
+        assert np.array_equal(got[:, :k], want) and not got[:, k:].any(), k
+    assert set(T.tq_select_outlier_channels(x, 3)[2, :3]) == {3, 70, 71}
+
+
+def test_select_outlier_channels_rejects_bad_arguments():
+    lib = T.load_library()
+    v = np.zeros((4, 128), np.float16)
+    out = np.zeros((4, 16), np.uint8)
+    call = lambda vec, n, h, k, o: lib.tq_select_outlier_channels(vec, n, h, k, o)
+    assert call(None, 4, 1, 2, out.ctypes.data) == T.TQ_ERR_INVALID_ARG
+    assert call(v.ctypes.data, 4, 1, 2, None) == T.TQ_ERR_INVALID_ARG
+    assert call(v.ctypes.data, 0, 1, 2, out.ctypes.data) == T.TQ_ERR_INVALID_ARG
+    assert call(v.ctypes.data, 4, 0, 2, out.ctypes.data) == T.TQ_ERR_INVALID_ARG
+    assert call(v.ctypes.data, 4, 1, 0, out.ctypes.data) == T.TQ_ERR_INVALID_ARG
+    assert call(v.ctypes.data, 4, 1, 17, out.ctypes.data) == T.TQ_ERR_INVALID_ARG
+    assert call(v.ctypes.data, 4, 2, 16, out.ctypes.data) == T.TQ_OK
+
+
+def _kept(c, k=4, channels=FAKE + 0x300000, values=FAKE + 0x400000):
+    c.n_outliers, c.outlier_channels, c.outliers = k, channels, values
+    return c
+
+
+def test_kept_channel_validation(monkeypatch):
+    lib = T.load_library()
+    q_call = lambda kk: lib.tq_quantize_kv(ctypes.byref(kk), FAKE, None, None, 256, 4, FAKE, None)
+    assert q_call(_kept(fake_cache(), k=17)) == T.TQ_ERR_INVALID_ARG
+    assert q_call(_kept(fake_cache(), k=-1)) == T.TQ_ERR_INVALID_ARG
+    assert q_call(_kept(fake_cache(bits=T.BITS_FP16))) == T.TQ_ERR_UNSUPPORTED
+    assert q_call(_kept(fake_cache(head_dim=256))) == T.TQ_ERR_UNSUPPORTED
+    assert q_call(_kept(fake_cache(), channels=None)) == T.TQ_ERR_INVALID_ARG
+    assert q_call(_kept(fake_cache(), channels=FAKE + 8)) == T.TQ_ERR_INVALID_ARG    # not 16-byte aligned
+    assert q_call(_kept(fake_cache(), values=None)) == T.TQ_ERR_INVALID_ARG
+    assert q_call(_kept(fake_cache(), values=FAKE + 2)) == T.TQ_ERR_INVALID_ARG      # not 8-byte aligned
+    assert lib.tq_quantize_kv(ctypes.byref(_kept(fake_cache())), FAKE, None, None, 256, 0, FAKE, None) == T.TQ_OK
+    # decode: kept channels on V only, on the matrix-core pass; the partials grow
+    _, plain = decode_call()
+    st, size = decode_call(v=_kept(fake_cache(bits=3)))
+    assert st == T.TQ_OK and size > plain
+    assert decode_call(k=_kept(fake_cache()))[0] == T.TQ_ERR_UNSUPPORTED
+    monkeypatch.setenv("TQ_DECODE_KERNEL", "valu")
+    assert decode_call(v=_kept(fake_cache(bits=3)))[0] == T.TQ_ERR_UNSUPPORTED

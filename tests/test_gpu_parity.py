@@ -67,7 +67,7 @@ _ORACLE_MEMO = {}
 
 def _wl_key(wl):
     return (wl.name, wl.kind, wl.seed, wl.n_seqs, tuple(int(x) for x in wl.seq_lens), wl.n_qtok, wl.n_q_heads,
-            wl.n_kv_heads, wl.k_bits, wl.v_bits, wl.block_size, wl.n_blocks, wl.head_dim)
+            wl.n_kv_heads, wl.k_bits, wl.v_bits, wl.block_size, wl.n_blocks, wl.head_dim, wl.v_planted, wl.v_kept)
 
 
 def _memo(key, fn):
@@ -646,3 +646,130 @@ def test_decode_wide_heads_llama8b_sampled(head_dim, heads, kernel):
     err = U.row_rel_err(out[:, :, qh], want)
     log(f"decode {wl.name} heads {heads}: worst row rel err {np.max(err):.2e}")
     assert np.max(err) <= ATOL_ROW
+
+
+# ----------------------------------------------------------- kept V channels (R13)
+
+def _skip_valu_for_kept(kernel):
+    if kernel == "valu":
+        pytest.skip("kept V channels run on the matrix-core pass only (the vector-ALU pass rejects them)")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("n_kv,k", [(1, 1), (3, 5), (8, 16)])
+def test_quantize_kept_channels(bits, n_kv, k):
+    """The kept channels are stored exactly, slot-major per page; the codes and norms
+    are those of the vector with those channels zeroed; skipped and unused slots are
+    untouched; dequantize puts the kept values back."""
+    torch = _t()
+    rng = np.random.default_rng(11 * bits + 7 * k + n_kv)
+    n_tok, bs, pad = 77, 16, 40
+    x = rng.standard_normal((n_tok, n_kv, 128))
+    x[:, :, rng.choice(128, size=min(k, 4), replace=False)] *= 20
+    x = x.astype(np.float16)
+    signs = W.random_sign_words(rng, n_kv)
+    idx = O.select_outlier_channels(x, k)
+    n_blocks = -(-n_tok // bs) + 1
+    slots = rng.permutation(n_blocks * bs)[:n_tok].astype(np.int64)
+    slots[3] = -1
+    g = T.Cache.allocate(bits, n_kv, bs, n_blocks, signs, outlier_channels=idx)
+    g.codes.fill_(0xAB)
+    g.outliers.fill_(7)
+    src = np.zeros((n_tok, n_kv * 128 + pad), np.float16)
+    src[:, : n_kv * 128] = x.reshape(n_tok, -1)
+    view = torch.as_strided(torch.from_numpy(src).cuda(), (n_tok, n_kv, 128), (n_kv * 128 + pad, 128, 1))
+    T.tq_quantize_kv(None, None, g, view, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    ok = slots >= 0
+    oc = O.new_cache(bits, n_kv, bs, n_blocks, signs, O.build_codebook(bits), outlier_channels=idx)
+    O.cache_write(oc, x, slots)
+    kept = g.outliers.cpu().numpy()          # [n_blocks, n_kv, k, bs]
+    blk, off = slots[ok] // bs, slots[ok] % bs
+    np.testing.assert_array_equal(kept[blk, :, :, off], oc.outliers[blk, :, :, off])
+    codes = g.codes.cpu().numpy().transpose(0, 2, 1, 3).reshape(-1, n_kv, 16 * bits)
+    norms = g.norms.cpu().numpy().transpose(0, 2, 1).reshape(-1, n_kv)
+    near = 0
+    for h in range(n_kv):
+        z = x[:, h].copy()
+        z[:, idx[h].astype(np.int64)] = 0
+        near += U.check_codes(codes[slots[ok], h], norms[slots[ok], h], z[ok], signs[h], bits)
+    untouched = np.setdiff1d(np.arange(n_blocks * bs), slots[ok])
+    assert np.all(codes[untouched] == 0xAB)
+    ub, uo = untouched // bs, untouched % bs
+    assert np.all(kept[ub, :, :, uo] == np.float16(7))
+    rd = torch.from_numpy(slots[ok]).cuda()
+    got32 = T.tq_dequantize(g, rd).cpu().numpy()
+    got16 = T.tq_dequantize(g, rd, fp16=True).cpu().numpy()
+    for h in range(n_kv):
+        want = O.cache_read(oc, slots[ok], h)
+        ch = idx[h].astype(np.int64)
+        np.testing.assert_array_equal(got32[:, h][:, ch], want[:, ch])
+        np.testing.assert_array_equal(got16[:, h][:, ch].astype(np.float64), want[:, ch])
+        assert np.max(U.row_rel_err(got32[:, h], want)) < 1e-5
+    log(f"quantize kept channels bits={bits} n_kv={n_kv} k={k}: near-boundary {near}")
+
+
+@pytest.mark.parametrize("case", [
+    # (n_seqs, lens, n_qtok, n_q_heads, n_kv_heads, k_bits, v_bits, block_size, kept)
+    (1, [700], 1, 4, 1, 4, 3, 256, 8),
+    (2, [1000, 33], 1, 32, 8, 3, 2, 256, 16),
+    (2, [300, 129], 4, 16, 4, 4, 4, 64, 4),
+    (3, [77, 5, 260], 2, 8, 1, 2, 3, 16, 1),
+    (2, [1500, 600], 1, 8, 2, 4, 2, 100, 5),
+    (1, [4097], 3, 6, 2, 3, 3, 256, 16),
+    (2, [900, 70], 1, 8, 2, T.BITS_FP16, 3, 256, 8),
+], ids=lambda c: f"s{c[0]}-q{c[2]}-h{c[3]}/{c[4]}-b{c[5]}{c[6]}-bs{c[7]}-k{c[8]}")
+def test_decode_kept_channels(case, kernel):
+    """V keeping 1-16 channels in float16 (4 planted x20): 1-16 rows per KV head,
+    contiguous and paged layouts, ragged tails, K compressed or float16."""
+    _skip_valu_for_kept(kernel)
+    n_seqs, lens, n_qtok, hq, hkv, kb, vb, bs, kept = case
+    wl = W.small_decode(seed=sum(lens) + 3 * kept, n_seqs=n_seqs, lens=lens, n_qtok=n_qtok, n_q_heads=hq,
+                        n_kv_heads=hkv, k_bits=kb, v_bits=vb, block_size=bs, v_planted=4, v_kept=kept)
+    decode_and_compare(wl)
+
+
+@pytest.mark.parametrize("tau", [1e-4, 3e-2, 1.5])
+def test_decode_kept_channels_sparse(tau, kernel):
+    _skip_valu_for_kept(kernel)
+    wl = W.small_decode(seed=61, n_seqs=2, lens=[2500, 700], n_qtok=2, n_q_heads=8, n_kv_heads=2,
+                        k_bits=4, v_bits=2, tau=tau, block_size=256, v_planted=4, v_kept=8)
+    out, _ = decode_and_compare(wl)
+    if tau > 1:
+        assert np.all(out == 0)
+
+
+def test_decode_kept_channels_llama8b_full(kernel):
+    """The Llama-3-8B-shaped decode (32768 tokens, 32 / 8 heads, K4 / V3) with 4 V
+    outlier channels x20 and 8 kept channels per head: every row."""
+    _skip_valu_for_kept(kernel)
+    decode_and_compare(W.llama8b_vout())
+
+
+def test_end_to_end_kept_channels(kernel):
+    """GPU selection, GPU quantize and GPU decode against the oracle pipeline on the
+    same float16 inputs (channels selected by both sides from the same warm-up data)."""
+    _skip_valu_for_kept(kernel)
+    torch = _t()
+    wl = W.small_decode(seed=71, n_seqs=2, lens=[900, 257], n_qtok=1, n_q_heads=8, n_kv_heads=2, k_bits=4,
+                        v_bits=3, block_size=64, v_planted=4, v_kept=6)
+    gidx = T.tq_select_outlier_channels(wl.warmup_v(), wl.v_kept)
+    oidx = O.select_outlier_channels(wl.warmup_v(), wl.v_kept)
+    assert np.array_equal(gidx[:, : wl.v_kept], oidx)
+    gk = T.Cache.allocate(wl.k_bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, wl.signs_k)
+    gv = T.Cache.allocate(wl.v_bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, wl.signs_v,
+                          outlier_channels=gidx[:, : wl.v_kept])
+    for b in range(wl.n_seqs):
+        k, v = wl.kv_source(b)
+        T.tq_quantize_kv(gk, torch.from_numpy(k).cuda(), gv, torch.from_numpy(v).cuda(),
+                         torch.from_numpy(wl.slots(b)).cuda())
+    q = wl.queries()
+    out = T.tq_decode_attention(gk, gv, torch.from_numpy(q).cuda(), torch.from_numpy(wl.seq_lens).cuda(),
+                                torch.from_numpy(wl.block_table).cuda()).cpu().numpy()
+    ok, ov = oracle_caches(wl)
+    assert np.array_equal(gv.outliers.cpu().numpy(), ov.outliers)
+    flips = int(np.sum(gk.codes.cpu().numpy() != ok.codes) + np.sum(gv.codes.cpu().numpy() != ov.codes))
+    want = O.decode_attention(q, ok, ov, wl.seq_lens, wl.block_table, wl.n_qtok)
+    err = float(np.max(U.row_rel_err(out, want)))
+    log(f"end-to-end kept channels: worst row rel err {err:.2e}, differing code bytes {flips}")
+    assert err < (ATOL_ROW if flips == 0 else 1e-2)
