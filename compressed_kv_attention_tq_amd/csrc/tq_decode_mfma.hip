@@ -59,6 +59,10 @@ typedef int32_t i4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kQS = 132;   // padded row stride (floats) of the q'' / merge buffer
 
+#ifndef TQ_DECODE_SLOTS
+#define TQ_DECODE_SLOTS 2
+#endif
+
 __device__ __forceinline__ f4_t mfma_f16(u4_t a, u4_t b, f4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), c,
                                                   0, 0, 0);
@@ -255,6 +259,8 @@ void tq_decode_mfma_kernel(
     constexpr int NQB = PK ? 4 : 8;                 // q'' B fragments
     constexpr int NPB = PK ? 2 : 4;                 // weight B fragments
     constexpr int NG = kMW / NB;                    // wave groups: slices the block has in flight
+    // slices a wave's ring holds (loads in flight while one is computed)
+    constexpr int NSLOT = (KF || OV || TQ_DECODE_SLOTS < 3) ? 2 : 3;
     static_assert(!OV || (NB == 1 && MODE != MODE_SCORE), "kept V channels: 128-wide heads, passes with V");
     constexpr int RW = NB * kD + (OV ? 16 : 0);     // floats per row of a chunk partial
     constexpr int WRW = kD + (OV ? 16 : 0);         // floats per row of one wave's (block's) sums
@@ -382,7 +388,7 @@ void tq_decode_mfma_kernel(
     // load a valid slot and use 0)
     const int oslot = OV ? min(n, a.n_out - 1) : 0;
     const bool olive = OV && n < a.n_out;
-    Slot sa, sb;
+    Slot sa, sb, sc;   // (sc: with three slots in the ring)
     int myrow = 0;   // row of token base + lane (general page layout)
 
     auto row0_of = [&](int base, int page) __attribute__((always_inline)) -> int64_t {
@@ -681,6 +687,10 @@ void tq_decode_mfma_kernel(
         // slot b's loads strictly after slot a's, so waiting for a never waits for b
         __builtin_amdgcn_sched_barrier(0);
         issue(sb, first + kStride);
+        if constexpr (NSLOT == 3) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue(sc, first + 2 * kStride);
+        }
     }
 
     // ---- score MFMAs of the loaded slice
@@ -907,14 +917,19 @@ void tq_decode_mfma_kernel(
         // every wave, as the exchange's barriers need), each group's slice `lead`
         // tokens in; a slice past the end has every score masked and changes nothing.
         const int lead = first - start;
-        for (int b0 = NB == 1 ? first : start; b0 < end; b0 += 2 * kStride) {
+        for (int b0 = NB == 1 ? first : start; b0 < end; b0 += NSLOT * kStride) {
             const int base = NB == 1 ? b0 : b0 + lead;
             __builtin_amdgcn_sched_barrier(0);
-            compute(sa, base);   // slot b holds base + kStride (in flight)
-            issue(sa, base + 2 * kStride);
+            compute(sa, base);   // the other slots hold the next slices (in flight)
+            issue(sa, base + NSLOT * kStride);
             __builtin_amdgcn_sched_barrier(0);
             if (b0 + kStride < end) compute(sb, base + kStride);
-            issue(sb, base + 3 * kStride);
+            issue(sb, base + (NSLOT + 1) * kStride);
+            if constexpr (NSLOT == 3) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (b0 + 2 * kStride < end) compute(sc, base + 2 * kStride);
+                issue(sc, base + 5 * kStride);
+            }
         }
     } else {
         // ---------------- gated pass: candidate slices only (a group's decision is
