@@ -87,7 +87,8 @@ class HipEvents:
     def handles(self, i):
         return self.pairs[i]
 
-    def mean_ms(self):
+    def times_ms(self):
+        """Elapsed time of every pair (ms); the events are destroyed."""
         out = []
         for a, b in self.pairs:
             ms = self.ct.c_float()
@@ -97,7 +98,7 @@ class HipEvents:
         for a, b in self.pairs:
             self.hip.hipEventDestroy(a)
             self.hip.hipEventDestroy(b)
-        return float(np.mean(out))
+        return np.array(out)
 
 
 def decode_workload(name):
@@ -189,7 +190,11 @@ def run_decode(args, torch):
     t1.record()
     torch.cuda.synchronize()
     ms_step_eager = t0.elapsed_time(t1) / args.steps
-    pass_ms = evs.mean_ms()
+    pass_times = evs.times_ms()
+    pass_ms = float(np.mean(pass_times))
+    log(f"[bench] pass kernel by events over {len(pass_times)} launches: mean {pass_ms * 1e3:.1f} us, "
+        f"p10 / p50 / p90 {np.percentile(pass_times, 10) * 1e3:.1f} / {np.median(pass_times) * 1e3:.1f} / "
+        f"{np.percentile(pass_times, 90) * 1e3:.1f} us")
     # the same steps replayed from a HIP graph (one graph = one step on every replica)
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -236,7 +241,8 @@ def run_decode(args, torch):
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(kernel_key),
             "kernel": kernel + (" (scoring pass)" if wl.tau > 0 else ""), "bytes_per_launch": pass_bytes,
-            "avg_launch_us": round(pass_ms * 1e3, 2)}
+            "avg_launch_us": round(pass_ms * 1e3, 2),
+            "median_launch_us": round(float(np.median(pass_times)) * 1e3, 2)}
     cfg = {"workload": f"{wl.name}: {wl.n_seqs} seq x {int(wl.seq_lens.max())} tokens, "
                        f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d={hd}, K{kb}/V{vb}"
                        f"{f' ({wl.v_kept} V channels kept in float16)' if wl.v_kept else ''}, "
