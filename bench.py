@@ -171,10 +171,18 @@ def run_decode(args, torch):
                                         wl.tau)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
 
+    # the append fused into the pass (tq_append_decode_attention) where it is supported
+    fused = not args.separate_append and kb != 16 and wl.head_dim == 128 and not wl.v_kept and \
+        os.environ.get("TQ_DECODE_KERNEL", "mfma") != "valu"
+
     def step(i, events=None):
         r = i % reps
-        T.tq_quantize_kv(kc, k_new, vc, v_new, new_slots[r])
-        T.tq_decode_attention(kc, vc, q, lens, tables[r], 0.0, wl.tau, out=out, workspace=ws, events=events)
+        if fused:
+            T.tq_append_decode_attention(kc, k_new, vc, v_new, q, lens, tables[r], 0.0, wl.tau, out=out,
+                                         workspace=ws, events=events)
+        else:
+            T.tq_quantize_kv(kc, k_new, vc, v_new, new_slots[r])
+            T.tq_decode_attention(kc, vc, q, lens, tables[r], 0.0, wl.tau, out=out, workspace=ws, events=events)
 
     for i in range(args.warmup):
         step(i)
@@ -249,6 +257,8 @@ def run_decode(args, torch):
                        f"{wl.n_qtok} query token(s), tau={wl.tau}, page {wl.block_size}",
            "global_batch": wl.n_seqs, "seq_len": int(wl.seq_lens.max()), "replicas": reps,
            "launch": "HIP graph replay", "ms_per_step_eager": round(ms_step_eager, 5),
+           "append": ("fused into the pass (tq_append_decode_attention)" if fused
+                      else "tq_quantize_kv, then tq_decode_attention"),
            "decode_kernel": ("matrix-core pass (fp16 MFMA, hi/lo-split fp32 operands, fp32 accumulate)"
                              if mfma else "vector-ALU pass (fp32)"),
            "parallelism": "single GPU"}
@@ -427,6 +437,8 @@ def main():
                     choices=["llama8b", "llama8b_k16", "llama8b_d256", "llama8b_d512", "llama8b_vout", "longctx",
                              "ragged", "tiny"])
     ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append with tq_quantize_kv and decode with tq_decode_attention (two calls)")
     ap.add_argument("--quantize-reps", type=int, default=5)
     ap.add_argument("--no-quantize", action="store_true")
     ap.add_argument("--quantize-only", action="store_true", help="only the prefill quantize measurement")

@@ -466,11 +466,21 @@ tq_status tq_decode_attention(const tq_cache *k, const tq_cache *v, const void *
                                      workspace_bytes, stream, nullptr);
 }
 
-tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const void *q, int32_t n_seqs,
-                                    int32_t n_qtok, int32_t n_q_heads, const int32_t *seq_lens,
-                                    const int32_t *block_table, int32_t max_blocks_per_seq,
-                                    float softmax_scale, float sparse_v_tau, float *out, void *workspace,
-                                    size_t *workspace_bytes, void *stream, void *const *events) {
+}  // extern "C"
+
+namespace {
+
+// The new tokens of a fused append (tq_append_decode_attention), or none.
+struct AppendIn {
+    const void *k_new, *v_new;
+    int64_t stride;
+};
+
+tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32_t n_seqs, int32_t n_qtok,
+                      int32_t n_q_heads, const int32_t *seq_lens, const int32_t *block_table,
+                      int32_t max_blocks_per_seq, float softmax_scale, float sparse_v_tau, float *out,
+                      void *workspace, size_t *workspace_bytes, void *stream, void *const *events,
+                      const AppendIn *app) {
     if (!workspace_bytes) return TQ_ERR_INVALID_ARG;
     tq_status st = check_cache(k);
     if (st != TQ_OK) return st;
@@ -500,6 +510,13 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
         return TQ_ERR_UNSUPPORTED;
     const bool sparse = sparse_v_tau > 0.f;
     const bool mfma = use_mfma_decode();
+    if (app) {   // the fused append: matrix-core pass, 128-wide heads, compressed K, V without kept channels
+        if (!mfma || nb != 1 || k_fp16 || v_out) return TQ_ERR_UNSUPPORTED;
+        if (!app->k_new || !app->v_new || !is_aligned(app->k_new, 16) || !is_aligned(app->v_new, 16))
+            return TQ_ERR_INVALID_ARG;
+        if (app->stride < (int64_t)k->n_kv_heads * kD || app->stride % 8 != 0) return TQ_ERR_INVALID_ARG;
+        if (!is_aligned(k->codes, 8) || !is_aligned(v->codes, 8)) return TQ_ERR_INVALID_ARG;
+    }
     const int acc_w = nb * kD + (v_out ? TQ_MAX_OUTLIERS : 0);
     const DecodePlan p = plan_decode(n_seqs, k->n_kv_heads, nb, acc_w, (int)rows, max_blocks_per_seq,
                                      k->block_size, sparse, mfma);
@@ -569,6 +586,20 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
         a.kc[i] = !k_fp16 && i < k->cb.n_levels ? k->cb.centroids[i] : 0.f;
         a.vc[i] = i < v->cb.n_levels ? v->cb.centroids[i] : 0.f;
     }
+    if (app) {
+        a.append = 1;
+        a.k_new = static_cast<const uint16_t *>(app->k_new);
+        a.v_new = static_cast<const uint16_t *>(app->v_new);
+        a.new_stride = app->stride;
+        a.k_codes_w = k->codes;
+        a.v_codes_w = v->codes;
+        a.k_norms_w = k->norms;
+        a.v_norms_w = v->norms;
+        for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) {
+            a.kbnd[i] = i + 1 < k->cb.n_levels ? k->cb.boundaries[i] : INFINITY;
+            a.vbnd[i] = i + 1 < v->cb.n_levels ? v->cb.boundaries[i] : INFINITY;
+        }
+    }
     PairTables pt;
     memset(&pt, 0, sizeof(pt));
     if (!k_fp16)
@@ -580,6 +611,30 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
     hipEvent_t ev1 = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
     if (launch_decode(a, pt, static_cast<hipStream_t>(stream), ev0, ev1) != hipSuccess) return TQ_ERR_HIP;
     return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const void *q, int32_t n_seqs,
+                                    int32_t n_qtok, int32_t n_q_heads, const int32_t *seq_lens,
+                                    const int32_t *block_table, int32_t max_blocks_per_seq,
+                                    float softmax_scale, float sparse_v_tau, float *out, void *workspace,
+                                    size_t *workspace_bytes, void *stream, void *const *events) {
+    return decode_impl(k, v, q, n_seqs, n_qtok, n_q_heads, seq_lens, block_table, max_blocks_per_seq,
+                       softmax_scale, sparse_v_tau, out, workspace, workspace_bytes, stream, events, nullptr);
+}
+
+tq_status tq_append_decode_attention(const tq_cache *k, const void *k_new, const tq_cache *v, const void *v_new,
+                                     int64_t new_token_stride, const void *q, int32_t n_seqs, int32_t n_qtok,
+                                     int32_t n_q_heads, const int32_t *seq_lens, const int32_t *block_table,
+                                     int32_t max_blocks_per_seq, float softmax_scale, float sparse_v_tau,
+                                     float *out, void *workspace, size_t *workspace_bytes, void *stream,
+                                     void *const *events) {
+    const AppendIn app{k_new, v_new, new_token_stride};
+    return decode_impl(k, v, q, n_seqs, n_qtok, n_q_heads, seq_lens, block_table, max_blocks_per_seq,
+                       softmax_scale, sparse_v_tau, out, workspace, workspace_bytes, stream, events, &app);
 }
 
 }  // extern "C"

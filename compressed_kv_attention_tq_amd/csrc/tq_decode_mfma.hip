@@ -42,6 +42,15 @@
 // state; each keeps the V accumulator of its own block.  Register use is that
 // of one block; the block's waves meet at two LDS barriers per slice.
 //
+// Fused append (a.append, dense and scoring passes, 128-wide heads, compressed K,
+// V without kept channels): the new tokens of a (sequence, KV head) are its last n_qtok
+// positions.  The wave that computes the slice holding a new position quantizes
+// its K and V rows (the arithmetic of the quantize kernel), stores them to the
+// cache for later launches and keeps a copy in LDS, which replaces their rows in
+// that slice: within this launch those rows are never read back from memory, so
+// no ordering of the stores against the slice loads is needed, and no other wave
+// waits for the work.
+//
 // OV: the V side keeps n_out <= 16 channels per head in float16 ([llama-tq] V with
 // outlier-channel separation).  They add one value MFMA per 32 tokens whose A
 // rows are the kept channels (A[slot][token] = the stored float16 value, exact)
@@ -292,6 +301,14 @@ void tq_decode_mfma_kernel(
     __shared__ float red[kMW];
     __shared__ float gstat[16][2];
     __shared__ __attribute__((aligned(16))) int32_t rowtab[CONTIG ? 1 : kMW][64];
+    // fused append: the new tokens' code rows ([token][K row], [token][V row], then
+    // K and V norms; row = position - the chunk's first new position, 16 at most),
+    // each written and read by the wave that computes its slice
+    constexpr bool kApp = !GATED && NB == 1 && !OV && !KF;
+    // (then the K and V boundaries of the waves that encode, 16 + 16 floats each)
+    __shared__ __attribute__((aligned(16))) uint8_t apbuf[kApp ? 16 * (KROW + VROW) + 32 * 4 + kMW * 32 * 4 : 16];
+    float *const apn = reinterpret_cast<float *>(apbuf + (kApp ? 16 * (KROW + VROW) : 0));
+    float *const abnd = apn + 32;   // [wave][K 16, V 16]
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -524,6 +541,52 @@ void tq_decode_mfma_kernel(
     }
     end = min(start + a.chunk, len);
 
+    // ---- fused append: the new positions this wave computes, [own_pa, own_pa + n_own)
+    // (they lie in at most two slices of the chunk, each computed by one wave), and
+    // the float16 rows of its first 8 vectors (K rows of its new tokens, then their V
+    // rows; lanes past the last vector repeat it, unstored) with their pages, issued
+    // before the first slice so that waiting for them never waits for slice data
+    constexpr bool APP = kApp;   // (not K float16: already at the register limit)
+    const int p0 = len - a.n_qtok;
+    int own_pa = 0, n_own = 0;
+    const int app0 = max(p0, start);   // the chunk's first new position: apbuf row = position - app0
+    if constexpr (APP) {
+        if (a.append) {
+            const int pa = app0;
+            if (pa < end) {
+                const int s0 = (pa - start) >> 6, s1 = (end - 1 - start) >> 6;
+                if (s0 % NG == grp) {
+                    own_pa = pa;
+                    n_own = min(end, start + 64 * (s0 + 1)) - pa;
+                } else if (s1 != s0 && s1 % NG == grp) {
+                    own_pa = start + 64 * s1;
+                    n_own = end - own_pa;
+                }
+            }
+        }
+    }
+    const Lane8 l8 = lane8();
+    struct AppVec {
+        int pos, side;
+        bool live;
+    };
+    auto app_vec = [&](int pass) __attribute__((always_inline)) -> AppVec {
+        const int nv = 2 * n_own, vi = pass * 8 + l8.vin, vc = min(vi, nv - 1);
+        const int side = vc >= n_own ? 1 : 0;
+        return AppVec{own_pa + (side ? vc - n_own : vc), side, vi < nv};
+    };
+    uint32_t aw[8];
+    int apage = 0;
+    auto app_load = [&](const AppVec &av) __attribute__((always_inline)) {
+        const uint16_t *srcp = (av.side ? a.v_new : a.k_new) +
+                               ((int64_t)b * a.n_qtok + (av.pos - p0)) * a.new_stride + kv * kD + 16 * l8.j;
+        const uint4 x0 = reinterpret_cast<const uint4 *>(srcp)[0], x1 = reinterpret_cast<const uint4 *>(srcp)[1];
+        aw[0] = x0.x; aw[1] = x0.y; aw[2] = x0.z; aw[3] = x0.w;
+        aw[4] = x1.x; aw[5] = x1.y; aw[6] = x1.z; aw[7] = x1.w;
+        apage = btab[fdiv((uint32_t)av.pos, bsdiv)];
+    };
+    if (APP && n_own > 0) app_load(app_vec(0));   // wave-uniform
+
     // ---- the first slice's loads (r0_prev: its first row; blk_next: page of the
     // second slice)
     int64_t r0_prev = 0;
@@ -638,7 +701,6 @@ void tq_decode_mfma_kernel(
         fill_tables();
         __syncthreads();
     }
-
     const bool row_ok = col_row < R;
     // last position each row sees in this chunk (row r sees t <= len - n_qtok + r / G)
     const int lim = row_ok ? min(end - 1, len - a.n_qtok + (int)fdiv((uint32_t)col_row, a.grp_div)) : -1;
@@ -690,6 +752,76 @@ void tq_decode_mfma_kernel(
         if constexpr (NSLOT == 3) {
             __builtin_amdgcn_sched_barrier(0);
             issue(sc, first + 2 * kStride);
+        }
+    }
+
+    // ---- fused append (the waves that compute new positions): encode the rows, store
+    // them to the cache and into apbuf for the patch of their slices; after the
+    // set-up, while the first slice's data is on its way (V: the pass's own width;
+    // the scoring pass, built for one V width, stores with a.v_bits)
+    if constexpr (APP) {
+        if (n_own > 0) {   // wave-uniform
+            // the boundaries into the wave's LDS row (lane i < 15: K boundary i; 16 + i: V)
+            {
+                float bk = 0.f, bv = 0.f;
+#pragma unroll
+                for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) {
+                    bk = (lane & 15) == i ? a.kbnd[i] : bk;
+                    bv = (lane & 15) == i ? a.vbnd[i] : bv;
+                }
+                if (lane < 32) abnd[wave * 32 + lane] = lane < 16 ? bk : bv;
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+                __builtin_amdgcn_wave_barrier();
+            }
+            const float *bk = abnd + wave * 32, *bv = bk + 16;
+            for (int pass = 0; pass * 8 < 2 * n_own; ++pass) {
+                const AppVec av = app_vec(pass);
+                if (pass > 0) app_load(av);
+                const int pg = (int)fdiv((uint32_t)av.pos, bsdiv);
+                const int64_t arow = ((int64_t)apage * n_sub + kvs) * bs + (av.pos - pg * bs);
+                const int tk = av.pos - app0;
+                uint32_t code[16], lo, hi;
+                if (!av.side) {
+                    const uint32_t sb = (a.k_signs[kvs * 4 + (l8.j >> 1)] >> ((l8.j & 1) * 16)) & 0xFFFFu;
+                    const float nm = encode_block8<KB>(aw, sb, bk, l8.j, code);
+                    pack_lane_codes<KB>(code, lo, hi);
+                    if (av.live) {
+                        store_lane_packed<KB>(a.k_codes_w + arow * KROW, lo, hi, l8.j);
+                        store_lane_packed<KB>(apbuf + tk * KROW, lo, hi, l8.j);
+                        if (l8.j == 0) {
+                            a.k_norms_w[arow] = nm;
+                            apn[tk] = nm;
+                        }
+                    }
+                } else {
+                    const uint32_t sb = (a.v_signs[kvs * 4 + (l8.j >> 1)] >> ((l8.j & 1) * 16)) & 0xFFFFu;
+                    const int vb = DENSE ? VB : a.v_bits;
+                    float nm;
+                    if (vb == 4) {
+                        nm = encode_block8<4>(aw, sb, bv, l8.j, code);
+                        pack_lane_codes<4>(code, lo, hi);
+                    } else if (vb == 3) {
+                        nm = encode_block8<3>(aw, sb, bv, l8.j, code);
+                        pack_lane_codes<3>(code, lo, hi);
+                    } else {
+                        nm = encode_block8<2>(aw, sb, bv, l8.j, code);
+                        pack_lane_codes<2>(code, lo, hi);
+                    }
+                    if (av.live) {
+                        uint8_t *vrow = a.v_codes_w + arow * (16 * vb);
+                        if (vb == 4) store_lane_packed<4>(vrow, lo, hi, l8.j);
+                        else if (vb == 3) store_lane_packed<3>(vrow, lo, hi, l8.j);
+                        else store_lane_packed<2>(vrow, lo, hi, l8.j);
+                        if constexpr (DENSE) store_lane_packed<VB>(apbuf + 16 * KROW + tk * VROW, lo, hi, l8.j);
+                        if (l8.j == 0) {
+                            a.v_norms_w[arow] = nm;
+                            apn[16 + tk] = nm;
+                        }
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's copies are in LDS
+            __builtin_amdgcn_wave_barrier();
         }
     }
 
@@ -855,7 +987,38 @@ void tq_decode_mfma_kernel(
     if constexpr (!GATED) {
         // ---------------- dense / scoring pass: a two-slot ring, the next slice's
         // loads in flight while a slice is computed
-        auto compute = [&](const Slot &sl, int base) __attribute__((always_inline)) {
+        // fused append: a slice holding this wave's new tokens takes their rows from
+        // apbuf (K words: token base + 16 tm + n; V units: token base + 16 tm + 4 g + e;
+        // norms: token base + lane)
+        auto patch = [&](Slot &sl, int base) __attribute__((always_inline)) {
+            if constexpr (APP) {
+                if (n_own == 0 || base + 64 <= own_pa || base >= own_pa + n_own) return;   // uniform
+#pragma unroll
+                for (int tm = 0; tm < 4; ++tm) {
+                    const int to = base + 16 * tm + n - own_pa, tk = to + own_pa - app0;
+                    if ((unsigned)to < (unsigned)n_own) {
+                        const uint32_t *r = reinterpret_cast<const uint32_t *>(apbuf + tk * KROW + 4 * KW * g);
+#pragma unroll
+                        for (int i = 0; i < KW; ++i) sl.kw[tm][i] = r[i];
+                    }
+                }
+                const int tlo = base + lane - own_pa, tl = tlo + own_pa - app0;
+                if ((unsigned)tlo < (unsigned)n_own) sl.knl = apn[tl];
+                if constexpr (DENSE) {
+#pragma unroll
+                    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int to = base + 16 * tm + 4 * g + e - own_pa, tk = to + own_pa - app0;
+                            if ((unsigned)to < (unsigned)n_own)
+                                load_vunit<VB>(apbuf + 16 * KROW + tk * VROW, vwi, sl.vw[tm >> 1][4 * (tm & 1) + e]);
+                        }
+                    if ((unsigned)tlo < (unsigned)n_own) sl.vnl = apn[16 + tl];
+                }
+            }
+        };
+        auto compute = [&](Slot &sl, int base) __attribute__((always_inline)) {
+            patch(sl, base);
             const float E_s = stage_norms(sl, base);
             f4_t S[4];
             score_mfma(sl, S);

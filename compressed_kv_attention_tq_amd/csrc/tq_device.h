@@ -149,4 +149,91 @@ __device__ __forceinline__ uint32_t stream_code(const uint32_t *w) {
     }
 }
 
+// Quantize one 128-element block held in the 8-lane layout above: lane j has
+// elements 16j .. 16j+15 as float16 pairs w16 and their 16 sign bits sb; bnd
+// (any address space) holds the 2^BITS - 1 boundaries in ascending order.
+// code[k] = the number of boundaries below y = H (s * x / |x|) / sqrt(128) for
+// element 16j + k, found by binary descent (BITS steps; equal to the count for
+// sorted boundaries); a zero or non-finite vector encodes y = 0.  Returns the
+// norm |x| (every lane of the block).  The arithmetic of the quantize kernel.
+template <int BITS, typename BndPtr>
+__device__ __forceinline__ float encode_block8(const uint32_t (&w16)[8], uint32_t sb, BndPtr bnd, int j,
+                                               uint32_t (&code)[16]) {
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    uint32_t w[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t m = (((sb >> (2 * k)) & 1u) << 15) | (((sb >> (2 * k + 1)) & 1u) << 31);
+        w[k] = w16[k] ^ m;
+        const h2_t h = __builtin_bit_cast(h2_t, w[k]);
+        ss = __builtin_amdgcn_fdot2(h, h, ss, false);
+    }
+    ss = block8_sum(ss);
+    const bool finite = ss <= 3.402823466e38f;   // false for inf and NaN
+    if (!finite) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = 0;
+    }
+    const float tscale = (finite && ss > 0.f) ? lane_sign(j) * 0.088388347648318440550f * __frsqrt_rn(ss) : 0.f;
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) half_pair_butterfly(w[k], v[2 * k], v[2 * k + 1]);
+    wht16<2>(v);
+    wht_cross(v, j);
+    float y[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        y[k] = v[k] * tscale;
+        code[k] = 0;
+    }
+#pragma unroll
+    for (int lvl = BITS - 1; lvl >= 0; --lvl)
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            code[k] += y[k] > bnd[code[k] + (1u << lvl) - 1u] ? (1u << lvl) : 0u;
+    return __fsqrt_rn(ss);
+}
+
+// Lane j's 16 codes (elements 16j .. 16j+15 of a block) as its 2 * BITS bytes of
+// the block's LSB-first bitstream: lo, then (3 and 4 bits) hi.
+template <int BITS>
+__device__ __forceinline__ void pack_lane_codes(const uint32_t (&code)[16], uint32_t &lo, uint32_t &hi) {
+    lo = 0;
+    hi = 0;
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) lo |= code[k] << (4 * k);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) hi |= code[8 + k] << (4 * k);
+    } else if constexpr (BITS == 2) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) lo |= code[k] << (2 * k);
+    } else {  // 3 bits: 48 bits
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (3 * k + 3 <= 32) lo |= code[k] << (3 * k);
+            else if (3 * k >= 32) hi |= code[k] << (3 * k - 32);
+            else { lo |= code[k] << (3 * k); hi |= code[k] >> (32 - 3 * k); }
+        }
+    }
+}
+
+// Store those bytes into the block's row of 16 * BITS bytes, at byte 2 * BITS * j
+// (3 bits: 48 bits at byte 6j as a dword and a ushort, both 2-byte aligned).
+template <int BITS, typename Ptr>
+__device__ __forceinline__ void store_lane_packed(Ptr row, uint32_t lo, uint32_t hi, int j) {
+    if constexpr (BITS == 4) {
+        *reinterpret_cast<uint2 *>(row + 8 * j) = make_uint2(lo, hi);
+    } else if constexpr (BITS == 2) {
+        *reinterpret_cast<uint32_t *>(row + 4 * j) = lo;
+    } else {
+        // (even j: dword then ushort; odd j: ushort then dword)
+        auto d = row + 6 * j;
+        const bool odd = j & 1;
+        *reinterpret_cast<uint16_t *>(d + (odd ? 0 : 4)) = (uint16_t)(odd ? lo : hi);
+        *reinterpret_cast<uint32_t *>(d + (odd ? 2 : 0)) = odd ? ((lo >> 16) | (hi << 16)) : lo;
+    }
+}
+
 }  // namespace tq

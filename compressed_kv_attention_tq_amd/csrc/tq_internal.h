@@ -132,6 +132,15 @@ struct DecodeArgs {
     const uint8_t *v_out_idx; // uint8 [n_kv][16] kept channels of each head
     const uint16_t *v_outliers;   // float16 [n_blocks][n_kv][n_out][block_size] kept values
     int32_t acc_w;            // floats per row of a chunk partial: 128 nb, + 16 with kept channels
+    // fused append (matrix-core pass, nb = 1, no kept channels): the float16 K / V rows
+    // of the new tokens, [n_seqs * n_qtok][n_kv][128] with new_stride elements between
+    // tokens; token j of sequence b goes to position seq_len - n_qtok + j
+    int32_t append;
+    const uint16_t *k_new, *v_new;
+    int64_t new_stride;
+    uint8_t *k_codes_w, *v_codes_w;   // the caches written by the append (same memory)
+    float *k_norms_w, *v_norms_w;
+    float kbnd[TQ_MAX_LEVELS - 1], vbnd[TQ_MAX_LEVELS - 1];   // boundaries, unused entries +inf
     int32_t mfma;             // 1: matrix-core pass kernels, 0: vector-ALU kernels
     int32_t contig;           // matrix-core path: every 64-token slice lies in one page
     float kc[TQ_MAX_LEVELS];

@@ -28,7 +28,8 @@ MAX_OUTLIERS = 16   # kept channels per head (TQ_MAX_OUTLIERS)
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
 EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_fit_codebook", "tq_select_outlier_channels",
-           "tq_quantize_kv", "tq_decode_attention", "tq_decode_attention_timed", "tq_dequantize")
+           "tq_quantize_kv", "tq_decode_attention", "tq_decode_attention_timed", "tq_append_decode_attention",
+           "tq_dequantize")
 
 
 class TQError(RuntimeError):
@@ -106,6 +107,10 @@ def load_library(path: str = LIB_PATH):
                                         ctypes.c_void_p]
     lib.tq_decode_attention_timed.restype = ctypes.c_int
     lib.tq_decode_attention_timed.argtypes = lib.tq_decode_attention.argtypes + [ctypes.c_void_p]
+    lib.tq_append_decode_attention.restype = ctypes.c_int
+    lib.tq_append_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.POINTER(TQCache),
+                                               ctypes.c_void_p, ctypes.c_int64] + \
+        lib.tq_decode_attention.argtypes[2:] + [ctypes.c_void_p]
     lib.tq_dequantize.restype = ctypes.c_int
     lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_int32, ctypes.c_void_p]
@@ -311,6 +316,42 @@ def tq_decode_attention(k_cache: Cache, v_cache: Cache, q, seq_lens, block_table
         float(sparse_v_tau), _dev_ptr(out, "out", torch.float32), _dev_ptr(workspace, "workspace"),
         ctypes.byref(size), _stream_ptr(stream), ev)
     _check(st, "tq_decode_attention")
+    return out
+
+
+def tq_append_decode_attention(k_cache: Cache, k_new, v_cache: Cache, v_new, q, seq_lens, block_table,
+                               softmax_scale=0.0, sparse_v_tau=0.0, out=None, workspace=None, stream=None,
+                               events=None):
+    """Quantize-on-append of the new tokens and decode attention in one call (the
+    fused pass): k_new / v_new float16 [n_seqs * n_qtok, n_kv_heads, 128] (token
+    stride from the tensor), token j of sequence b going to position
+    seq_lens[b] - n_qtok + j; the rest as tq_decode_attention."""
+    torch = _torch()
+    n_seqs, n_qtok, n_q_heads, hd = q.shape
+    if hd != k_cache.head_dim:
+        raise ValueError(f"q has head_dim {hd}, the cache {k_cache.head_dim}")
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 3 or t.shape[0] != n_seqs * n_qtok:
+            raise ValueError(f"{name} must be a float16 device tensor [n_seqs * n_qtok, n_kv_heads, 128]")
+        if t.stride(2) != 1 or t.stride(1) != HEAD_DIM or t.stride(0) != k_new.stride(0):
+            raise ValueError(f"{name}: heads must be contiguous and both share one token stride")
+    max_blocks = block_table.shape[1]
+    need = decode_workspace_bytes(k_cache, v_cache, n_seqs, n_qtok, n_q_heads, max_blocks, sparse_v_tau)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((n_seqs, n_qtok, n_q_heads, hd), dtype=torch.float32, device=q.device)
+    size = ctypes.c_size_t(workspace.numel())
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * 2)(*[e.value if isinstance(e, ctypes.c_void_p) else e for e in events])
+    st = load_library().tq_append_decode_attention(
+        ctypes.byref(k_cache.desc()), ctypes.c_void_p(k_new.data_ptr()), ctypes.byref(v_cache.desc()),
+        ctypes.c_void_p(v_new.data_ptr()), k_new.stride(0), _dev_ptr(q, "q", torch.float16), n_seqs, n_qtok,
+        n_q_heads, _dev_ptr(seq_lens, "seq_lens", torch.int32), _dev_ptr(block_table, "block_table", torch.int32),
+        max_blocks, float(softmax_scale), float(sparse_v_tau), _dev_ptr(out, "out", torch.float32),
+        _dev_ptr(workspace, "workspace"), ctypes.byref(size), _stream_ptr(stream), ev)
+    _check(st, "tq_append_decode_attention")
     return out
 
 

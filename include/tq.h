@@ -249,6 +249,32 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
                                     float sparse_v_tau, float *out, void *workspace,
                                     size_t *workspace_bytes, void *stream, void *const *events);
 
+/* Quantize-on-append and decode attention in one call: the same result as
+ * tq_quantize_kv(k, k_new, v, v_new, new_token_stride, n_seqs * n_qtok, slots)
+ * followed by tq_decode_attention(k, v, q, ...), where new token j of sequence b
+ * (row b * n_qtok + j of k_new / v_new, device float16 [n_seqs * n_qtok][n_kv_heads]
+ * [128], tokens new_token_stride elements apart, >= n_kv_heads * 128, a multiple
+ * of 8) goes to position seq_lens[b] - n_qtok + j of sequence b, i.e. to the slot
+ * that block_table gives that position (positions below 0 are skipped) - the
+ * [TQ+ README] backend table's quantize on append, fused into the pass kernel.
+ * The pass block whose chunk holds a new position quantizes it, stores its codes
+ * and norm, and uses them for this attention from its own copy; the new tokens'
+ * slots must not be read by other sequences of the call.  Supported: the
+ * matrix-core pass, head_dim 128, K with 2..4 bits, V without kept channels
+ * (TQ_ERR_UNSUPPORTED otherwise: use the two calls).  Codes of elements within
+ * rounding of a decision boundary may differ from tq_quantize_kv's (both count
+ * the boundaries below the rotated value, in float32 with different roundings).
+ * events: as in tq_decode_attention_timed (may be NULL).  Workspace: as
+ * tq_decode_attention (query with workspace NULL).
+ * Errors: as tq_decode_attention; TQ_ERR_INVALID_ARG for NULL or misaligned new
+ *         rows or a bad stride. */
+tq_status tq_append_decode_attention(const tq_cache *k, const void *k_new, const tq_cache *v, const void *v_new,
+                                     int64_t new_token_stride, const void *q, int32_t n_seqs, int32_t n_qtok,
+                                     int32_t n_q_heads, const int32_t *seq_lens, const int32_t *block_table,
+                                     int32_t max_blocks_per_seq, float softmax_scale, float sparse_v_tau,
+                                     float *out, void *workspace, size_t *workspace_bytes, void *stream,
+                                     void *const *events);
+
 /* Dequantize cache rows: dst[t][h][:] = x_hat of slot slots[t], head h
  * ([llama-tq]: K needs no dequantization inside attention; this is the explicit
  * inverse for everything else).

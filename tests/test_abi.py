@@ -321,3 +321,31 @@ def test_kept_channel_validation(monkeypatch):
     assert decode_call(k=_kept(fake_cache()))[0] == T.TQ_ERR_UNSUPPORTED
     monkeypatch.setenv("TQ_DECODE_KERNEL", "valu")
     assert decode_call(v=_kept(fake_cache(bits=3)))[0] == T.TQ_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------- fused append + decode
+
+def test_append_decode_validation(monkeypatch):
+    """tq_append_decode_attention: the decode checks plus the new rows; only the
+    matrix-core pass with 128-wide heads, compressed K and V without kept channels."""
+    lib = T.load_library()
+
+    def call(k=None, v=None, k_new=FAKE, v_new=FAKE, stride=256, ws=None, ws_bytes=0):
+        k = fake_cache() if k is None else k
+        v = fake_cache(bits=3) if v is None else v
+        size = ctypes.c_size_t(ws_bytes)
+        return lib.tq_append_decode_attention(ctypes.byref(k), k_new, ctypes.byref(v), v_new, stride, FAKE, 1, 1,
+                                              2, FAKE, FAKE, 4, 0.0, 0.0, FAKE, ws, ctypes.byref(size), None,
+                                              None), size.value
+    st, size = call()
+    assert st == T.TQ_OK and size == decode_call()[1]          # workspace query, as decode
+    assert call(k_new=None)[0] == T.TQ_ERR_INVALID_ARG
+    assert call(v_new=FAKE + 8)[0] == T.TQ_ERR_INVALID_ARG      # not 16-byte aligned
+    assert call(stride=255)[0] == T.TQ_ERR_INVALID_ARG          # < n_kv * 128
+    assert call(stride=260)[0] == T.TQ_ERR_INVALID_ARG          # not a multiple of 8
+    assert call(k=fake_cache(bits=T.BITS_FP16))[0] == T.TQ_ERR_UNSUPPORTED
+    assert call(v=_kept(fake_cache(bits=3)))[0] == T.TQ_ERR_UNSUPPORTED
+    assert call(k=fake_cache(head_dim=256), v=fake_cache(bits=3, head_dim=256), stride=512)[0] == \
+        T.TQ_ERR_UNSUPPORTED
+    monkeypatch.setenv("TQ_DECODE_KERNEL", "valu")
+    assert call()[0] == T.TQ_ERR_UNSUPPORTED

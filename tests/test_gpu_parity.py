@@ -773,3 +773,106 @@ def test_end_to_end_kept_channels(kernel):
     err = float(np.max(U.row_rel_err(out, want)))
     log(f"end-to-end kept channels: worst row rel err {err:.2e}, differing code bytes {flips}")
     assert err < (ATOL_ROW if flips == 0 else 1e-2)
+
+
+# ----------------------------------------------------------- fused append + decode
+
+def _old_context_cache(wl, side):
+    """Oracle cache of every position but each sequence's last n_qtok (the context
+    before the new tokens)."""
+    bits = wl.k_bits if side == 0 else wl.v_bits
+    signs = wl.signs_k if side == 0 else wl.signs_v
+    c = O.new_cache(bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, signs, O.build_codebook(bits))
+    for b in range(wl.n_seqs):
+        n_old = int(wl.seq_lens[b]) - wl.n_qtok
+        if n_old <= 0:
+            continue
+        k, v = wl.kv_source(b)
+        O.cache_write(c, (k if side == 0 else v)[:n_old], wl.slots(b)[:n_old])
+    return c
+
+
+def append_and_compare(wl, tau=None):
+    """tq_append_decode_attention on caches holding the old context, against (a) the
+    oracle pipeline (oracle-quantized new tokens, oracle attention) and (b) the two
+    calls tq_quantize_kv + tq_decode_attention on the same caches."""
+    torch = _t()
+    tau = wl.tau if tau is None else tau
+    ok_old, ov_old = _memo(("old",) + _wl_key(wl), lambda: (_old_context_cache(wl, 0), _old_context_cache(wl, 1)))
+    ok, ov = oracle_caches(wl)
+    n_new = wl.n_seqs * wl.n_qtok
+    k_new = np.zeros((n_new, wl.n_kv_heads, 128), np.float16)
+    v_new = np.zeros((n_new, wl.n_kv_heads, 128), np.float16)
+    slots = np.full(n_new, -1, np.int64)
+    for b in range(wl.n_seqs):
+        length = int(wl.seq_lens[b])
+        if length == 0:
+            continue
+        k, v = wl.kv_source(b)
+        sl = wl.slots(b)
+        for j in range(wl.n_qtok):
+            p = length - wl.n_qtok + j
+            if p >= 0:
+                k_new[b * wl.n_qtok + j], v_new[b * wl.n_qtok + j] = k[p], v[p]
+                slots[b * wl.n_qtok + j] = sl[p]
+    q = torch.from_numpy(wl.queries()).cuda()
+    lens = torch.from_numpy(wl.seq_lens).cuda()
+    table = torch.from_numpy(wl.block_table).cuda()
+    kn, vn = torch.from_numpy(k_new).cuda(), torch.from_numpy(v_new).cuda()
+    # (b) the two calls
+    gk2, gv2 = U.gpu_cache_from(ok_old), U.gpu_cache_from(ov_old)
+    T.tq_quantize_kv(gk2, kn, gv2, vn, torch.from_numpy(slots).cuda())
+    out2 = T.tq_decode_attention(gk2, gv2, q, lens, table, 0.0, tau).cpu().numpy()
+    # the fused call
+    gk, gv = U.gpu_cache_from(ok_old), U.gpu_cache_from(ov_old)
+    out = T.tq_append_decode_attention(gk, kn, gv, vn, q, lens, table, 0.0, tau).cpu().numpy()
+    torch.cuda.synchronize()
+    # the new rows: codes as the oracle's (away from boundaries), norms, untouched elsewhere
+    kc, vc = gk.codes.cpu().numpy(), gv.codes.cpu().numpy()
+    knm, vnm = gk.norms.cpu().numpy(), gv.norms.cpu().numpy()
+    m = slots >= 0
+    blk, off = slots[m] // wl.block_size, slots[m] % wl.block_size
+    near = 0
+    for h in range(wl.n_kv_heads):
+        near += U.check_codes(kc[blk, h, off], knm[blk, h, off], k_new[m, h], wl.signs_k[h], wl.k_bits)
+        near += U.check_codes(vc[blk, h, off], vnm[blk, h, off], v_new[m, h], wl.signs_v[h], wl.v_bits)
+    old = np.ones(kc.shape[:3], bool)
+    old[blk, :, off] = False
+    assert np.array_equal(kc[old], ok_old.codes[old]) and np.array_equal(vc[old], ov_old.codes[old])
+    flips = int(np.sum(kc != ok.codes) + np.sum(vc != ov.codes))
+    want = _memo(("decode-app", tau) + _wl_key(wl),
+                 lambda: O.decode_attention(wl.queries(), ok, ov, wl.seq_lens, wl.block_table, wl.n_qtok, 0.0, tau))
+    err = float(np.max(U.row_rel_err(out, want)))
+    err2 = float(np.max(U.row_rel_err(out, out2)))
+    log(f"append+decode {wl.name}: worst row rel err {err:.2e} (vs two calls {err2:.2e}), near-boundary {near}, "
+        f"code bytes unlike the oracle's {flips}")
+    bar = ATOL_ROW if flips == 0 else 1e-2
+    assert err <= bar and err2 <= bar
+    return out
+
+
+@pytest.mark.parametrize("case", [
+    # (n_seqs, lens, n_qtok, n_q_heads, n_kv_heads, k_bits, v_bits, block_size)
+    (1, [700], 1, 4, 1, 4, 3, 256),
+    (1, [258], 4, 4, 1, 4, 3, 64),            # the new positions cross a 256-token chunk
+    (3, [1000, 2, 257], 4, 8, 2, 3, 2, 16),   # a sequence shorter than n_qtok
+    (2, [1500, 600], 2, 16, 2, 4, 4, 100),    # 16 rows per KV head
+    (2, [513, 64], 3, 6, 2, 2, 3, 64),
+    (1, [32768], 1, 32, 8, 4, 3, 256),        # the Llama-3-8B decode shape
+], ids=lambda c: f"s{c[0]}-q{c[2]}-h{c[3]}/{c[4]}-b{c[5]}{c[6]}-bs{c[7]}")
+def test_append_decode(case, kernel):
+    if kernel == "valu":
+        pytest.skip("the fused append runs on the matrix-core pass only (the vector-ALU pass rejects it)")
+    n_seqs, lens, n_qtok, hq, hkv, kb, vb, bs = case
+    wl = W.small_decode(seed=sum(lens) + 5 * n_qtok, n_seqs=n_seqs, lens=lens, n_qtok=n_qtok, n_q_heads=hq,
+                        n_kv_heads=hkv, k_bits=kb, v_bits=vb, block_size=bs)
+    append_and_compare(wl)
+
+
+@pytest.mark.parametrize("tau", [1e-4, 3e-2])
+def test_append_decode_sparse(tau, kernel):
+    if kernel == "valu":
+        pytest.skip("the fused append runs on the matrix-core pass only (the vector-ALU pass rejects it)")
+    wl = W.small_decode(seed=83, n_seqs=2, lens=[2500, 700], n_qtok=2, n_q_heads=8, n_kv_heads=2, k_bits=4,
+                        v_bits=2, tau=tau, block_size=256)
+    append_and_compare(wl)
