@@ -1,9 +1,10 @@
 """Benchmark of the compressed-KV hot path on one MI355X.
 
 A step is one pass of the whole hot path over one batch: quantize-on-append of
-the new tokens' K and V into the paged compressed cache (tq_quantize_kv) and
-decode attention of the new query tokens over the whole cache
-(tq_decode_attention).  The default workload is the Llama-3-8B-shaped decode:
+the new tokens' K and V into the paged compressed cache and decode attention of
+the new query tokens over the whole cache, in one call
+(tq_append_decode_attention, the append fused into the decode pass) where that
+is supported, else tq_quantize_kv then tq_decode_attention.  The default workload is the Llama-3-8B-shaped decode:
 1 sequence of 32768 tokens, 32 query / 8 KV heads, d = 128, K 4-bit, V 3-bit.
 
 The cache is replicated R times (R x 31.5 MB > the 256 MB last-level cache)
