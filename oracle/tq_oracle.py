@@ -32,7 +32,7 @@ Sources, cited below by key (page title, then the section / table used):
                  repeat; separate quantizers for K and V), section 4.1 table
                  (bits per value 3.25 / 4.25 for turbo3 / turbo4).
 
-Readings taken where the pages are silent (each one also listed in the design doc):
+Readings taken where the pages are silent:
 
   R1  Hadamard order and scale: Sylvester matrix in natural order,
       H[i, j] = (-1)^popcount(i & j), scaled by 1/sqrt(d) so the rotation is
