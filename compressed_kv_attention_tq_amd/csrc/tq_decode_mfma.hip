@@ -577,15 +577,29 @@ void tq_decode_mfma_kernel(
     };
     uint32_t aw[8];
     int apage = 0;
+    // (the two row pointers are held in scalar registers, so the per-lane choice
+    // between them is a register select, not a load of the selected argument)
+    typedef const __attribute__((address_space(1))) uint16_t g_u16;
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(1))) u4v g_u4;
+    g_u16 *k_new = (g_u16 *)a.k_new, *v_new = (g_u16 *)a.v_new;
+    asm volatile("" : "+s"(k_new), "+s"(v_new));
     auto app_load = [&](const AppVec &av) __attribute__((always_inline)) {
-        const uint16_t *srcp = (av.side ? a.v_new : a.k_new) +
-                               ((int64_t)b * a.n_qtok + (av.pos - p0)) * a.new_stride + kv * kD + 16 * l8.j;
-        const uint4 x0 = reinterpret_cast<const uint4 *>(srcp)[0], x1 = reinterpret_cast<const uint4 *>(srcp)[1];
+        g_u16 *srcp = (av.side ? v_new : k_new) +
+                      ((int64_t)b * a.n_qtok + (av.pos - p0)) * a.new_stride + kv * kD + 16 * l8.j;
+        const u4v x0 = reinterpret_cast<g_u4 *>(srcp)[0], x1 = reinterpret_cast<g_u4 *>(srcp)[1];
         aw[0] = x0.x; aw[1] = x0.y; aw[2] = x0.z; aw[3] = x0.w;
         aw[4] = x1.x; aw[5] = x1.y; aw[6] = x1.z; aw[7] = x1.w;
         apage = btab[fdiv((uint32_t)av.pos, bsdiv)];
     };
-    if (APP && n_own > 0) app_load(app_vec(0));   // wave-uniform
+    // the first 8 vectors go out with the first slice's loads: after its page is
+    // read (so the wait for the page never covers them) and before its data
+    auto app_first = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (APP && n_own > 0) app_load(app_vec(0));   // wave-uniform
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (GATED) app_first();
 
     // ---- the first slice's loads (r0_prev: its first row; blk_next: page of the
     // second slice)
@@ -596,11 +610,13 @@ void tq_decode_mfma_kernel(
             const int blk0 = __builtin_amdgcn_readfirstlane(vb0);
             const int pg = (int)fdiv((uint32_t)first, bsdiv);
             r0_prev = ((int64_t)min(max(blk0, 0), a.max_page) * n_sub + kvs) * bs + (first - pg * bs);
+            app_first();
             load_k(sa, r0_prev);
             if constexpr (DENSE) load_v(sa, r0_prev, all_tokens);
             blk_next = vb1;
         } else {
             fill_rows(first, first + lane < end ? vb0 : 0);
+            app_first();
             load_k(sa, 0);
             if constexpr (DENSE) load_v(sa, 0, all_tokens);
             blk_next = first + kStride + lane < end ? vb1 : 0;
