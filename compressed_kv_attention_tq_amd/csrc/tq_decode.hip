@@ -464,7 +464,7 @@ __global__ __launch_bounds__(256) void tq_stats_kernel(DecodeArgs a) {
 // groups are merged through LDS and o = s_V * H (acc / L) / sqrt(128).  Gated:
 // the partials are already normalised and are summed.
 // --------------------------------------------------------------------------
-template <bool SPARSE>
+template <bool SPARSE, bool KEPT>   // KEPT: the V side keeps channels (a.n_out > 0)
 __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     typedef float f4_t __attribute__((ext_vector_type(4)));
     __shared__ float gm[8], gl[8];
@@ -481,30 +481,57 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     const int jq = bj - b * a.n_qtok;
     const int kv = (int)fdiv((uint32_t)h, a.grp_div);
     const int r = jq * a.group + (h - kv * a.group);
-    const int len = a.seq_lens[b];
-    const int nc = len > 0 ? (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div) : 0;
     const int64_t base = ((int64_t)b * a.n_kv + kv) * a.n_chunks;
-    const int n_out = a.n_out;   // (head blocks and kept channels do not meet: nb = 1 then)
+    const int n_out = KEPT ? a.n_out : 0;   // (head blocks and kept channels do not meet: nb = 1 then)
     if (tid < kD) cslot[tid] = -1;
+    // the output stage's sign words and kept-channel indices, loaded up front
+    const uint32_t *sg = a.v_signs + (kv * nb + hb) * 4;
+    const uint32_t sgw0 = sg[(lane >> 5) & 1], sgw1 = sg[2 + ((lane >> 5) & 1)];
+    int oidx = 0;
+    if constexpr (KEPT) oidx = a.v_out_idx[kv * 16 + min(tid, 15)];
     const int64_t mstride = (int64_t)a.rows_pad * nb * 2, astride = (int64_t)a.rows_pad * a.acc_w;
     const float *ml = a.part_ml + ((base * a.rows_pad + r) * nb + hb) * 2;                // chunk c at ml[c * mstride]
     const float *pa = a.part_acc + (base * a.rows_pad + r) * a.acc_w + hb * kD + 4 * q4;  // chunk c at pa[c * astride]
-    const bool xo = n_out > 0 && q4 < 4;   // this thread also merges kept sums 4 q4 .. 4 q4 + 3
+    const bool xo = KEPT && q4 < 4;   // this thread also merges kept sums 4 q4 .. 4 q4 + 3
+    // kept sums of the row (threads with q4 >= 4 read those of q4 = 3, unused)
+    const float *pa2 = pa - 4 * q4 + kD + 4 * min(q4, 3);
     float M = -INFINITY, L = 0.f;
     f4_t x = {0.f, 0.f, 0.f, 0.f}, x2 = {0.f, 0.f, 0.f, 0.f};
     constexpr int kB = 16;   // chunks per thread per batch (one round of loads)
-    for (int c0 = cg; c0 < nc; c0 += 8 * kB) {
-        float m[kB], l[kB];
-        f4_t v[kB], v2[kB];
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    f2_t mlr[kB];
+    float m[kB], l[kB];
+    f4_t v[kB], v2[kB];
+    // One round: chunks c0, c0 + 8, ..., every load issued (indices clamped below
+    // `issue`, so no load sits behind a branch and each waits only where it is used);
+    // then those at or past `lim` are replaced by empty ones.
+    auto load_round = [&](int c0, int issue) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
-            const int cc = c0 + 8 * i;
-            const bool ok = cc < nc;
-            m[i] = (!SPARSE && ok) ? ml[cc * mstride] : -INFINITY;
-            l[i] = (!SPARSE && ok) ? ml[cc * mstride + 1] : 0.f;
-            v[i] = ok ? *reinterpret_cast<const f4_t *>(pa + cc * astride) : f4_t{0.f, 0.f, 0.f, 0.f};
-            v2[i] = (ok && xo) ? *reinterpret_cast<const f4_t *>(pa + cc * astride + kD) : f4_t{0.f, 0.f, 0.f, 0.f};
+            const int ci = min(c0 + 8 * i, issue - 1);
+            if constexpr (!SPARSE) mlr[i] = *reinterpret_cast<const f2_t *>(ml + ci * mstride);
+            v[i] = *reinterpret_cast<const f4_t *>(pa + ci * astride);
         }
+        if constexpr (KEPT) {
+#pragma unroll
+            for (int i = 0; i < kB; ++i)
+                v2[i] = *reinterpret_cast<const f4_t *>(pa2 + min(c0 + 8 * i, issue - 1) * astride);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kB; ++i) v2[i] = f4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    auto mask_round = [&](int c0, int lim) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            const bool ok = c0 + 8 * i < lim;
+            m[i] = (!SPARSE && ok) ? mlr[i].x : -INFINITY;
+            l[i] = (!SPARSE && ok) ? mlr[i].y : 0.f;
+            v[i] = ok ? v[i] : f4_t{0.f, 0.f, 0.f, 0.f};
+            v2[i] = (ok && xo) ? v2[i] : f4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    auto fold_round = [&]() __attribute__((always_inline)) {
         if (SPARSE) {
 #pragma unroll
             for (int i = 0; i < kB; ++i) {
@@ -528,6 +555,20 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
             }
             M = mb;
         }
+    };
+    // The first round goes out before the sequence length is read: every chunk the
+    // workspace holds for this row (n_chunks >= 1) is loaded, and those past the
+    // sequence's own chunks (not written by this call) are then dropped.
+    load_round(cg, min(a.n_chunks, 8 * kB));
+    __builtin_amdgcn_sched_barrier(0);
+    const int len = a.seq_lens[b];
+    const int nc = len > 0 ? (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div) : 0;
+    mask_round(cg, nc);
+    fold_round();
+    for (int c0 = cg + 8 * kB; c0 < nc; c0 += 8 * kB) {
+        load_round(c0, nc);
+        mask_round(c0, nc);
+        fold_round();
     }
     if (q4 == 0) {
         gm[cg] = M;
@@ -550,16 +591,15 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
         }
         y[tid] = SPARSE ? ys : (Ls > 0.f ? ys / Ls : 0.f);
     }
-    if (tid < n_out) cslot[a.v_out_idx[kv * 16 + tid] & (kD - 1)] = tid;
+    if (tid < n_out) cslot[oidx & (kD - 1)] = tid;
     __syncthreads();
     if (tid >= 64) return;
     // o = s_V * H acc / sqrt(128)
     float a0 = y[lane], a1 = y[lane + 64];
     hadamard128(a0, a1, lane);
-    const uint32_t *sg = a.v_signs + (kv * nb + hb) * 4;
     const float k = 0.088388347648318440550f;
-    a0 *= ((sg[lane >> 5] >> (lane & 31)) & 1u) ? -k : k;
-    a1 *= ((sg[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -k : k;
+    a0 *= ((sgw0 >> (lane & 31)) & 1u) ? -k : k;
+    a1 *= ((sgw1 >> (lane & 31)) & 1u) ? -k : k;
     if (n_out > 0) {   // kept channels: their own sums
         const int s0 = cslot[lane], s1 = cslot[lane + 64];
         if (s0 >= 0) a0 = y[kD + s0];
@@ -668,6 +708,12 @@ static void launch_pass_any(const DecodeArgs &a, int mode, hipStream_t s, hipEve
     }
 }
 
+template <bool SPARSE>
+static void launch_merge(const DecodeArgs &a, dim3 grid, hipStream_t s) {
+    if (a.n_out > 0) hipLaunchKernelGGL((tq_merge_kernel<SPARSE, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((tq_merge_kernel<SPARSE, false>), grid, dim3(256), 0, s, a);
+}
+
 hipError_t launch_decode(const DecodeArgs &a, const PairTables &pt, hipStream_t s, hipEvent_t ev_before,
                          hipEvent_t ev_after) {
     const dim3 rows_grid((unsigned)((int64_t)a.n_seqs * a.n_qtok * a.n_q_heads * a.nb));   // x head blocks
@@ -675,10 +721,10 @@ hipError_t launch_decode(const DecodeArgs &a, const PairTables &pt, hipStream_t 
         if (a.tau > 0.f) {
             launch_mfma_any(a, pt, MODE_SCORE, s, ev_before, ev_after);
             launch_mfma_any(a, pt, MODE_GATED, s);
-            hipLaunchKernelGGL(tq_merge_kernel<true>, rows_grid, dim3(256), 0, s, a);
+            launch_merge<true>(a, rows_grid, s);
         } else {
             launch_mfma_any(a, pt, MODE_DENSE, s, ev_before, ev_after);
-            hipLaunchKernelGGL(tq_merge_kernel<false>, rows_grid, dim3(256), 0, s, a);
+            launch_merge<false>(a, rows_grid, s);
         }
         return hipGetLastError();
     }
@@ -687,10 +733,10 @@ hipError_t launch_decode(const DecodeArgs &a, const PairTables &pt, hipStream_t 
         launch_pass_any(a, MODE_SCORE, s, ev_before, ev_after);
         hipLaunchKernelGGL(tq_stats_kernel, dim3(a.n_seqs * a.n_kv), dim3(256), 0, s, a);
         launch_pass_any(a, MODE_GATED, s);
-        hipLaunchKernelGGL(tq_merge_kernel<true>, rows_grid, dim3(256), 0, s, a);
+        launch_merge<true>(a, rows_grid, s);
     } else {
         launch_pass_any(a, MODE_DENSE, s, ev_before, ev_after);
-        hipLaunchKernelGGL(tq_merge_kernel<false>, rows_grid, dim3(256), 0, s, a);
+        launch_merge<false>(a, rows_grid, s);
     }
     return hipGetLastError();
 }
