@@ -582,9 +582,13 @@ void tq_decode_mfma_kernel(
     typedef const __attribute__((address_space(1))) uint16_t g_u16;
     typedef uint32_t u4v __attribute__((ext_vector_type(4)));
     typedef const __attribute__((address_space(1))) u4v g_u4;
+    typedef const __attribute__((address_space(1))) uint32_t g_u32;
     g_u16 *k_new = (g_u16 *)a.k_new, *v_new = (g_u16 *)a.v_new;
-    asm volatile("" : "+s"(k_new), "+s"(v_new));
+    g_u32 *k_sg = (g_u32 *)a.k_signs, *v_sg = (g_u32 *)a.v_signs;
+    asm volatile("" : "+s"(k_new), "+s"(v_new), "+s"(k_sg), "+s"(v_sg));
+    uint32_t asg = 0;   // the vector's sign word (its side, this lane's 16 elements)
     auto app_load = [&](const AppVec &av) __attribute__((always_inline)) {
+        asg = (av.side ? v_sg : k_sg)[kvs * 4 + (l8.j >> 1)];
         g_u16 *srcp = (av.side ? v_new : k_new) +
                       ((int64_t)b * a.n_qtok + (av.pos - p0)) * a.new_stride + kv * kD + 16 * l8.j;
         const u4v x0 = reinterpret_cast<g_u4 *>(srcp)[0], x1 = reinterpret_cast<g_u4 *>(srcp)[1];
@@ -703,8 +707,10 @@ void tq_decode_mfma_kernel(
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
+            // (read for every lane: the buffer holds 16 rows; rows past R are dropped)
             const float *qr = &qbuf[col_row * kQS + 32 * g + 8 * ks + 2 * k];
-            const float q0 = col_row < R ? qr[0] * sq : 0.f, q1 = col_row < R ? qr[1] * sq : 0.f;
+            const float r0 = qr[0], r1 = qr[1];
+            const float q0 = col_row < R ? r0 * sq : 0.f, q1 = col_row < R ? r1 * sq : 0.f;
             if constexpr (PK) {
                 qb[ks][k] = split_pair(q0, q1, losel);
             } else {
@@ -790,15 +796,15 @@ void tq_decode_mfma_kernel(
                 __builtin_amdgcn_wave_barrier();
             }
             const float *bk = abnd + wave * 32, *bv = bk + 16;
-            for (int pass = 0; pass * 8 < 2 * n_own; ++pass) {
-                const AppVec av = app_vec(pass);
-                if (pass > 0) app_load(av);
+            // one pass: the 8 vectors whose rows are in aw (pass 0's were loaded with the
+            // first slice; a later pass loads its own, then waits for them)
+            auto encode_pass = [&](const AppVec &av) __attribute__((always_inline)) {
                 const int pg = (int)fdiv((uint32_t)av.pos, bsdiv);
                 const int64_t arow = ((int64_t)apage * n_sub + kvs) * bs + (av.pos - pg * bs);
                 const int tk = av.pos - app0;
+                const uint32_t sb = (asg >> ((l8.j & 1) * 16)) & 0xFFFFu;
                 uint32_t code[16], lo, hi;
                 if (!av.side) {
-                    const uint32_t sb = (a.k_signs[kvs * 4 + (l8.j >> 1)] >> ((l8.j & 1) * 16)) & 0xFFFFu;
                     const float nm = encode_block8<KB>(aw, sb, bk, l8.j, code);
                     pack_lane_codes<KB>(code, lo, hi);
                     if (av.live) {
@@ -810,7 +816,6 @@ void tq_decode_mfma_kernel(
                         }
                     }
                 } else {
-                    const uint32_t sb = (a.v_signs[kvs * 4 + (l8.j >> 1)] >> ((l8.j & 1) * 16)) & 0xFFFFu;
                     const int vb = DENSE ? VB : a.v_bits;
                     float nm;
                     if (vb == 4) {
@@ -835,6 +840,12 @@ void tq_decode_mfma_kernel(
                         }
                     }
                 }
+            };
+            encode_pass(app_vec(0));
+            for (int pass = 1; pass * 8 < 2 * n_own; ++pass) {
+                const AppVec av = app_vec(pass);
+                app_load(av);
+                encode_pass(av);
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's copies are in LDS
             __builtin_amdgcn_wave_barrier();
