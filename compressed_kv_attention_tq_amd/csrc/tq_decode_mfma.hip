@@ -615,8 +615,7 @@ void tq_decode_mfma_kernel(
             const int pg = (int)fdiv((uint32_t)first, bsdiv);
             r0_prev = ((int64_t)min(max(blk0, 0), a.max_page) * n_sub + kvs) * bs + (first - pg * bs);
             app_first();
-            load_k(sa, r0_prev);
-            if constexpr (DENSE) load_v(sa, r0_prev, all_tokens);
+            load_k(sa, r0_prev);   // (its V units go out after the set-up, below)
             blk_next = vb1;
         } else {
             fill_rows(first, first + lane < end ? vb0 : 0);
@@ -768,6 +767,13 @@ void tq_decode_mfma_kernel(
         if constexpr (DENSE) load_v(sl, r0, all_tokens);
     };
     if constexpr (!GATED) {
+        // contiguous pages: the first slice's V units now (its K words went out before
+        // the set-up: fewer loads ahead of the set-up's own instructions, which wait
+        // behind them when the memory pipeline is full)
+        if constexpr (CONTIG && DENSE) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_v(sa, r0_prev, all_tokens);
+        }
         // slot b's loads strictly after slot a's, so waiting for a never waits for b
         __builtin_amdgcn_sched_barrier(0);
         issue(sb, first + kStride);
