@@ -740,8 +740,8 @@ void tq_decode_mfma_kernel(
     }
 
     // ---- the second slice's loads, once the set-up above is done: the first
-    // slice's went out before it, both would fill the memory pipeline and hold
-    // the set-up up.  Every issue loads, whether or not its slice lies below the end: one past the
+    // slice's went out before it (on contiguous pages its K words only; its V units
+    // follow here), both would fill the memory pipeline and hold the set-up up.  Every issue loads, whether or not its slice lies below the end: one past the
     // end re-reads the rows of the last slice issued (cached, and never used), so
     // the loads of both slots are the same instructions on every path and each
     // wait covers only the slot it needs, never the one in flight behind it.
