@@ -878,19 +878,27 @@ void tq_decode_mfma_kernel(
     // not data and become 0); returns the V exponent E: max V norm < 2^E, so the
     // weights e * vn * 2^-E stay below 1
     float *my_kn = nrm[wave][0], *my_vn = nrm[wave][1];
-    auto stage_norms = [&](const Slot &sl, int base) __attribute__((always_inline)) -> float {
+    // The slice's norms into the wave's LDS rows: K before the score MFMAs, V (and
+    // the exponent E_s of its largest) before the weights, so the scores never wait
+    // for the V loads, which go out after the K loads.
+    auto stage_knorms = [&](const Slot &sl) __attribute__((always_inline)) {
         my_kn[lane] = sl.knl * kscale;
-        float v = 0.f;
-        if constexpr (WV) {
-            v = base + lane < end ? sl.vnl : 0.f;
-            my_vn[lane] = v;
-        }
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
+    };
+    auto stage_vnorms = [&](const Slot &sl, int base) __attribute__((always_inline)) -> float {
         if constexpr (!WV) return 0.f;
+        const float v = base + lane < end ? sl.vnl : 0.f;
+        my_vn[lane] = v;
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
         const float vm = wave_max(v);
         const int ex = vm > 0.f ? (int)((__float_as_uint(vm) >> 23) & 0xFF) - 126 : -40;
         return (float)min(max(ex, -40), 40);
+    };
+    auto stage_norms = [&](const Slot &sl, int base) __attribute__((always_inline)) -> float {
+        stage_knorms(sl);
+        return stage_vnorms(sl, base);
     };
     // NB > 1: replace each partial score by the sum of the group's partials, blocks
     // in ascending order (called by every wave of the block, the same number of
@@ -1052,7 +1060,7 @@ void tq_decode_mfma_kernel(
         };
         auto compute = [&](Slot &sl, int base) __attribute__((always_inline)) {
             patch(sl, base);
-            const float E_s = stage_norms(sl, base);
+            stage_knorms(sl);
             f4_t S[4];
             score_mfma(sl, S);
             const bool full = base + 63 <= lim_all;
@@ -1068,6 +1076,7 @@ void tq_decode_mfma_kernel(
                 if (g == 0 && row_ok && (!PK || n < 8) && blk == 0)
                     tilemax[(tile0 + (base >> 6)) * rp + col_row] = wm;
             }
+            const float E_s = stage_vnorms(sl, base);
             const float m_new = fmaxf(m_raw, wm);
             const float E_new = DENSE ? fmaxf(E_run, E_s) : 0.f;
             const float mu = (m_new == -INFINITY ? 0.f : m_new) + E_new;
