@@ -371,6 +371,19 @@ def test_decode_sparse_small(tau, kernel):
         assert np.all(out == 0)
 
 
+@pytest.mark.parametrize("tau", [0.0, 1e-3])
+def test_decode_many_chunks(tau, monkeypatch):
+    """More chunks per row than the merge takes in one round of loads (a 40000-token
+    sequence in 256-token chunks: 157 of them), next to a 700-token sequence (3): the
+    merge's first round is loaded before the lengths are read, clamped to the chunks
+    the workspace holds, and drops the chunks past each sequence's own."""
+    monkeypatch.setenv("TQ_DECODE_KERNEL", "mfma")
+    monkeypatch.setenv("TQ_DECODE_CHUNK", "256")
+    wl = W.small_decode(seed=23, n_seqs=2, lens=[40000, 700], n_qtok=1, n_q_heads=4, n_kv_heads=1, k_bits=4,
+                        v_bits=3, tau=tau, block_size=256)
+    decode_and_compare(wl)
+
+
 @pytest.mark.parametrize("variant", ["large-q", "small-q"])
 def test_decode_extreme_magnitudes(variant, kernel):
     """Queries scaled far from unit size (K norms scaled back for large ones, so the
