@@ -251,7 +251,9 @@ def run_decode(args, torch):
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(kernel_key),
             "kernel": kernel + (" (scoring pass)" if wl.tau > 0 else ""), "bytes_per_launch": pass_bytes,
             "avg_launch_us": round(pass_ms * 1e3, 2),
-            "median_launch_us": round(float(np.median(pass_times)) * 1e3, 2)}
+            "median_launch_us": round(float(np.median(pass_times)) * 1e3, 2),
+            "p10_launch_us": round(float(np.percentile(pass_times, 10)) * 1e3, 2),
+            "p90_launch_us": round(float(np.percentile(pass_times, 90)) * 1e3, 2)}
     cfg = {"workload": f"{wl.name}: {wl.n_seqs} seq x {int(wl.seq_lens.max())} tokens, "
                        f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d={hd}, K{kb}/V{vb}"
                        f"{f' ({wl.v_kept} V channels kept in float16)' if wl.v_kept else ''}, "
@@ -479,8 +481,12 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": cfg, "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "step_bytes": step_bytes, "roofline": roof, "cpu_baseline": cpu, "quantize": quant,
-        "codebook_fit": fitted,
+        "step_bytes": step_bytes,
+        # per step: the query tokens answered and the KV token-heads scanned (each
+        # sequence's KV heads over its whole context), each per second
+        "query_tokens_per_s": round(wl.n_seqs * wl.n_qtok / (ms_step * 1e-3), 1),
+        "kv_token_heads_per_s": round(wl.total_tokens * wl.n_kv_heads / (ms_step * 1e-3), 1),
+        "roofline": roof, "cpu_baseline": cpu, "quantize": quant, "codebook_fit": fitted,
     }
     print(json.dumps(rec), flush=True)
 
