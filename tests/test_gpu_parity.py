@@ -519,6 +519,52 @@ def test_graph_replay_matches_eager(kernel):
         assert torch.equal(gk.codes, codes_eager)
 
 
+@pytest.mark.parametrize("tau", [0.0, 1e-3])
+def test_graph_replay_fused_append_matches_eager(tau, monkeypatch):
+    """The fused append + decode call captured in a HIP graph (as the benchmark
+    replays it): every replay equals the eager result, output and cache rows."""
+    monkeypatch.setenv("TQ_DECODE_KERNEL", "mfma")
+    monkeypatch.delenv("TQ_DECODE_CHUNK", raising=False)
+    torch = _t()
+    wl = W.small_decode(seed=22, n_seqs=2, lens=[1500, 700], n_qtok=2, n_q_heads=8, n_kv_heads=2, k_bits=4,
+                        v_bits=3, tau=tau, block_size=64)
+    ok, ov = U.oracle_cache(wl, 0), U.oracle_cache(wl, 1)
+    gk, gv = U.gpu_cache_from(ok), U.gpu_cache_from(ov)
+    q = torch.from_numpy(wl.queries()).cuda()
+    lens = torch.from_numpy(wl.seq_lens).cuda()
+    table = torch.from_numpy(wl.block_table).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    knew = torch.randn((4, 2, 128), generator=gen, device="cuda").half()
+    vnew = torch.randn((4, 2, 128), generator=gen, device="cuda").half()
+    out = torch.zeros((2, 2, 8, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(T.decode_workspace_bytes(gk, gv, 2, 2, 8, wl.block_table.shape[1], tau), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        T.tq_append_decode_attention(gk, knew, gv, vnew, q, lens, table, 0.0, tau, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    kc, vc, kn, vn = gk.codes.clone(), gv.codes.clone(), gk.norms.clone(), gv.norms.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from eager"
+        assert torch.equal(gk.codes, kc) and torch.equal(gv.codes, vc)
+        assert torch.equal(gk.norms, kn) and torch.equal(gv.norms, vn)
+
+
 # ------------------------------------------------- heads of 256 / 512 elements (R12)
 
 def _skip_valu_for_wide_heads(kernel):
