@@ -917,6 +917,7 @@ def append_and_compare(wl, tau=None):
     (3, [1000, 2, 257], 4, 8, 2, 3, 2, 16),   # a sequence shorter than n_qtok
     (2, [1500, 600], 2, 16, 2, 4, 4, 100),    # 16 rows per KV head
     (2, [513, 64], 3, 6, 2, 2, 3, 64),
+    (3, [300, 0, 5], 2, 4, 1, 4, 3, 64),      # an empty sequence between two others
     (1, [32768], 1, 32, 8, 4, 3, 256),        # the Llama-3-8B decode shape
 ], ids=lambda c: f"s{c[0]}-q{c[2]}-h{c[3]}/{c[4]}-b{c[5]}{c[6]}-bs{c[7]}")
 def test_append_decode(case, kernel):
