@@ -426,9 +426,16 @@ def cpu_baseline(wl, budget_s=12.0):
     gbs = done_bytes / spent / 1e9
     log(f"[bench] cpu oracle: {units} (KV head, step) units of seq 0 in {spent:.1f} s -> {gbs:.4f} GB/s, "
         f"{cores} threads")
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{wl.name}: sequence 0, {units} single-KV-head steps (append + decode of "
-                      f"{wl.group * wl.n_qtok} query rows over {length} tokens each), {spent:.1f} s"}
+                      f"{wl.group * wl.n_qtok} query rows over {length} tokens each), {spent:.1f} s",
+            "host": {"cpu_model": cpu_model, "nproc": os.cpu_count()}}
 
 
 def main():
