@@ -86,6 +86,11 @@ Readings taken where the pages are silent:
       written over those channels.  The channels come from warm-up data (the
       [TQ blog] 5.3 advice): the k with the largest mean square over the head's
       vectors, ties to the lower index, listed in ascending order.
+  R14 Non-finite input (the pages say nothing of it): a vector with an inf or
+      NaN element has no direction to quantize.  It is stored like the zero
+      vector of R3 (every rotated coordinate 0, so every code is that of y = 0,
+      2^(b-1) - 1 under R5), with its norm as computed: inf, or NaN when an
+      element is NaN.
 """
 
 from __future__ import annotations
@@ -333,14 +338,17 @@ def quantize_vectors(x: np.ndarray, s: np.ndarray, cb: Codebook):
 
     Returns (norms float32, codes uint8 [..., 128], y float64 [..., 128]).
       n = ||x||_2 (float64, stored rounded to float32)           R3
-      u = x / n   (u = 0 when n = 0)                              R3
+      u = x / n   (u = 0 when n = 0, or when x has a non-finite   R3, R14
+                   element: then n is inf or NaN)
       y = H (s * u) / sqrt(128)                                   R1, R2
       code_i = #{j : y_i > b_j}                                   R5
     """
     x = np.asarray(x).astype(np.float64)
-    n = np.sqrt(np.sum(x * x, axis=-1))
-    safe = np.where(n > 0, n, 1.0)
-    u = np.where((n > 0)[..., None], x / safe[..., None], 0.0)
+    with np.errstate(invalid="ignore", over="ignore"):
+        n = np.sqrt(np.sum(x * x, axis=-1))
+        has_dir = (n > 0) & np.all(np.isfinite(x), axis=-1)
+        safe = np.where(has_dir, n, 1.0)
+        u = np.where(has_dir[..., None], x / safe[..., None], 0.0)
     y = rotate(u.reshape(-1, D), s).reshape(u.shape)
     codes = encode(y, cb.boundaries)
     return n.astype(np.float32), codes, y

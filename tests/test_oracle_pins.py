@@ -184,6 +184,30 @@ def test_zero_vector_quantizes_to_middle_code():
     assert n[0] == 0 and np.all(y == 0) and np.all(codes == 3)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_non_finite_vector_stored_as_zero_direction(bits):
+    """R14: an inf or NaN element leaves no direction: the codes are the zero
+    vector's (the middle code 2^(b-1) - 1, where y = 0 falls), the norm is inf, or
+    NaN when an element is NaN; finite rows in the same call are unaffected."""
+    cb = O.build_codebook(bits)
+    rng = np.random.default_rng(bits)
+    x = rng.standard_normal((5, 128)).astype(np.float16)
+    x[0, 7] = np.inf
+    x[1, 100] = -np.inf
+    x[2, 3] = np.nan
+    x[3, :] = np.inf
+    s = O.sign_vector(rng.integers(0, 2**32, size=4, dtype=np.uint64).astype(np.uint32))
+    n, codes, y = O.quantize_vectors(x, s, cb)
+    mid = (1 << (bits - 1)) - 1
+    assert np.all(codes[:4] == mid) and np.all(y[:4] == 0)
+    assert np.isposinf(n[0]) and np.isposinf(n[1]) and np.isnan(n[2]) and np.isposinf(n[3])
+    n4, c4, _ = O.quantize_vectors(x[4:], s, cb)
+    assert np.array_equal(codes[4:], c4) and n[4] == n4[0] and np.isfinite(n[4])
+    # the zero vector takes the same codes (R3, R5)
+    _, cz, _ = O.quantize_vectors(np.zeros((1, 128), np.float16), s, cb)
+    assert np.array_equal(cz[0], codes[0])
+
+
 @pytest.mark.parametrize("row", read_golden("pack_patterns.txt"), ids=lambda r: r[0] + ":" + r[1])
 def test_pack_hand_patterns(row):
     bits = int(row[0])
