@@ -110,6 +110,7 @@ tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, in
         q.src_stride = stride;
         q.n_vec = (int64_t)n_tokens * sub_heads(c);
         q.n_tokens = n_tokens;
+        q.cap = c->n_blocks * c->block_size;
         q.gpw = quant_gpw(sub_heads(c));
         q.n_kv = sub_heads(c);
         q.block_size = c->block_size;
@@ -134,6 +135,7 @@ tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, in
     q.src_stride = stride;
     q.n_vec = (int64_t)n_tokens * sub_heads(c);
     q.n_tokens = n_tokens;
+    q.cap = c->n_blocks * c->block_size;
     q.gpw = quant_gpw(sub_heads(c));
     q.n_kv = sub_heads(c);
     q.block_size = c->block_size;
@@ -173,18 +175,11 @@ struct DecodePlan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Decode kernels: the matrix-core pass (default) or the vector-ALU pass, chosen
-// by the environment variable TQ_DECODE_KERNEL ("mfma" / "valu").
-bool use_mfma_decode() {
-    const char *e = getenv("TQ_DECODE_KERNEL");
-    return !(e && strcmp(e, "valu") == 0);
-}
-
 // Tokens per pass block: a multiple of the unit (one 64-token slice per wave),
 // doubled while at least kTargetBlocks blocks remain and at most 16384 tokens;
-// TQ_DECODE_CHUNK (a multiple of the unit) overrides it.
+// chunk_opt > 0 (a multiple of the unit, checked by the caller) overrides it.
 DecodePlan plan_decode(int n_seqs, int n_kv, int nb, int acc_w, int rows, int max_blocks, int block_size,
-                       bool sparse, bool mfma) {
+                       bool sparse, bool mfma, int chunk_opt) {
     DecodePlan p{};
     p.rows = rows;
     if (mfma) p.rows_pad = rows <= 8 ? 8 : 16;
@@ -195,10 +190,7 @@ DecodePlan plan_decode(int n_seqs, int n_kv, int nb, int acc_w, int rows, int ma
     const int64_t target = 512;
     int chunk = unit;
     while (chunk < 16384 && total / (2 * chunk) >= target) chunk *= 2;
-    if (const char *e = getenv("TQ_DECODE_CHUNK")) {
-        const long v = strtol(e, nullptr, 10);
-        if (v >= unit && v <= (1 << 20) && v % unit == 0) chunk = (int)v;
-    }
+    if (chunk_opt > 0) chunk = chunk_opt;
     p.chunk = chunk;
     p.n_chunks = (int)((cap + chunk - 1) / chunk);
     p.n_tiles = p.n_chunks * (chunk / kSlice);
@@ -442,6 +434,7 @@ tq_status tq_dequantize(const tq_cache *c, const int64_t *slots, int32_t n_token
     a.slots = slots;
     a.dst = dst;
     a.n_vec = (int64_t)n_tokens * sub_heads(c);
+    a.cap = c->n_blocks * c->block_size;
     a.n_kv = sub_heads(c);
     a.block_size = c->block_size;
     a.dst_fp16 = dst_is_fp16 ? 1 : 0;
@@ -461,9 +454,9 @@ tq_status tq_decode_attention(const tq_cache *k, const tq_cache *v, const void *
                               const int32_t *block_table, int32_t max_blocks_per_seq,
                               float softmax_scale, float sparse_v_tau, float *out, void *workspace,
                               size_t *workspace_bytes, void *stream) {
-    return tq_decode_attention_timed(k, v, q, n_seqs, n_qtok, n_q_heads, seq_lens, block_table,
-                                     max_blocks_per_seq, softmax_scale, sparse_v_tau, out, workspace,
-                                     workspace_bytes, stream, nullptr);
+    return tq_decode_attention_ex(k, v, q, n_seqs, n_qtok, n_q_heads, seq_lens, block_table, max_blocks_per_seq,
+                                  softmax_scale, sparse_v_tau, out, workspace, workspace_bytes, stream, nullptr,
+                                  nullptr);
 }
 
 }  // extern "C"
@@ -479,9 +472,17 @@ struct AppendIn {
 tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32_t n_seqs, int32_t n_qtok,
                       int32_t n_q_heads, const int32_t *seq_lens, const int32_t *block_table,
                       int32_t max_blocks_per_seq, float softmax_scale, float sparse_v_tau, float *out,
-                      void *workspace, size_t *workspace_bytes, void *stream, void *const *events,
-                      const AppendIn *app) {
+                      void *workspace, size_t *workspace_bytes, void *stream, const tq_decode_options *opts,
+                      void *const *events, const AppendIn *app) {
     if (!workspace_bytes) return TQ_ERR_INVALID_ARG;
+    // the kernel and the chunk of this call (explicit options; no process state)
+    const int kern = opts ? opts->kernel : TQ_DECODE_KERNEL_DEFAULT;
+    if (kern != TQ_DECODE_KERNEL_DEFAULT && kern != TQ_DECODE_KERNEL_MFMA && kern != TQ_DECODE_KERNEL_VALU)
+        return TQ_ERR_INVALID_ARG;
+    const bool mfma = kern != TQ_DECODE_KERNEL_VALU;
+    const int chunk_opt = opts ? opts->chunk : 0;
+    if (chunk_opt != 0 && (chunk_opt < 0 || chunk_opt > (1 << 20) || chunk_opt % (mfma ? kMBlock : kChunkUnit) != 0))
+        return TQ_ERR_INVALID_ARG;
     tq_status st = check_cache(k);
     if (st != TQ_OK) return st;
     st = check_cache(v);
@@ -494,7 +495,7 @@ tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32
     const int nb = blocks_per_head(k);
     const bool v_out = v->n_outliers > 0;
     if (k->n_outliers > 0) return TQ_ERR_UNSUPPORTED;
-    if (v->bits == TQ_BITS_FP16 || ((k_fp16 || nb > 1 || v_out) && !use_mfma_decode())) return TQ_ERR_UNSUPPORTED;
+    if (v->bits == TQ_BITS_FP16 || ((k_fp16 || nb > 1 || v_out) && !mfma)) return TQ_ERR_UNSUPPORTED;
     if (!is_aligned(v->codes, 4)) return TQ_ERR_INVALID_ARG;
     if (n_seqs < 0 || n_qtok < 1 || n_q_heads < 1 || max_blocks_per_seq < 1) return TQ_ERR_INVALID_ARG;
     if (n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
@@ -509,7 +510,6 @@ tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32
         (double)v->n_blocks * sub_heads(v) * v->block_size > 2147483647.0)
         return TQ_ERR_UNSUPPORTED;
     const bool sparse = sparse_v_tau > 0.f;
-    const bool mfma = use_mfma_decode();
     if (app) {   // the fused append: matrix-core pass, 128-wide heads, compressed K, V without kept channels
         if (!mfma || nb != 1 || k_fp16 || v_out) return TQ_ERR_UNSUPPORTED;
         if (!app->k_new || !app->v_new || !is_aligned(app->k_new, 16) || !is_aligned(app->v_new, 16))
@@ -519,7 +519,7 @@ tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32
     }
     const int acc_w = nb * kD + (v_out ? TQ_MAX_OUTLIERS : 0);
     const DecodePlan p = plan_decode(n_seqs, k->n_kv_heads, nb, acc_w, (int)rows, max_blocks_per_seq,
-                                     k->block_size, sparse, mfma);
+                                     k->block_size, sparse, mfma, chunk_opt);
     if ((int64_t)n_seqs * k->n_kv_heads * p.n_chunks > 0x7FFFFFFFLL) return TQ_ERR_UNSUPPORTED;
     if (!workspace) {
         *workspace_bytes = n_seqs == 0 ? 0 : p.total;
@@ -581,6 +581,7 @@ tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32
     a.v_outliers = v->outliers;
     a.acc_w = acc_w;
     a.mfma = mfma ? 1 : 0;
+    a.v_rows_read = (sparse && opts) ? reinterpret_cast<unsigned long long *>(opts->v_rows_read) : nullptr;
     a.contig = (k->block_size % kSlice == 0 && is_aligned(k->norms, 16) && is_aligned(v->norms, 16)) ? 1 : 0;
     for (int i = 0; i < TQ_MAX_LEVELS; ++i) {
         a.kc[i] = !k_fp16 && i < k->cb.n_levels ? k->cb.centroids[i] : 0.f;
@@ -617,13 +618,13 @@ tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32
 
 extern "C" {
 
-tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const void *q, int32_t n_seqs,
-                                    int32_t n_qtok, int32_t n_q_heads, const int32_t *seq_lens,
-                                    const int32_t *block_table, int32_t max_blocks_per_seq,
-                                    float softmax_scale, float sparse_v_tau, float *out, void *workspace,
-                                    size_t *workspace_bytes, void *stream, void *const *events) {
+tq_status tq_decode_attention_ex(const tq_cache *k, const tq_cache *v, const void *q, int32_t n_seqs,
+                                 int32_t n_qtok, int32_t n_q_heads, const int32_t *seq_lens,
+                                 const int32_t *block_table, int32_t max_blocks_per_seq, float softmax_scale,
+                                 float sparse_v_tau, float *out, void *workspace, size_t *workspace_bytes,
+                                 void *stream, const tq_decode_options *opts, void *const *events) {
     return decode_impl(k, v, q, n_seqs, n_qtok, n_q_heads, seq_lens, block_table, max_blocks_per_seq,
-                       softmax_scale, sparse_v_tau, out, workspace, workspace_bytes, stream, events, nullptr);
+                       softmax_scale, sparse_v_tau, out, workspace, workspace_bytes, stream, opts, events, nullptr);
 }
 
 tq_status tq_append_decode_attention(const tq_cache *k, const void *k_new, const tq_cache *v, const void *v_new,
@@ -631,10 +632,10 @@ tq_status tq_append_decode_attention(const tq_cache *k, const void *k_new, const
                                      int32_t n_q_heads, const int32_t *seq_lens, const int32_t *block_table,
                                      int32_t max_blocks_per_seq, float softmax_scale, float sparse_v_tau,
                                      float *out, void *workspace, size_t *workspace_bytes, void *stream,
-                                     void *const *events) {
+                                     const tq_decode_options *opts, void *const *events) {
     const AppendIn app{k_new, v_new, new_token_stride};
     return decode_impl(k, v, q, n_seqs, n_qtok, n_q_heads, seq_lens, block_table, max_blocks_per_seq,
-                       softmax_scale, sparse_v_tau, out, workspace, workspace_bytes, stream, events, &app);
+                       softmax_scale, sparse_v_tau, out, workspace, workspace_bytes, stream, opts, events, &app);
 }
 
 }  // extern "C"

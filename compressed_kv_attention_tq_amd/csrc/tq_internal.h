@@ -57,6 +57,7 @@ struct QuantSide {
     int64_t src_stride;       // elements between tokens
     int64_t n_vec;            // n_tokens * n_kv
     int32_t n_tokens;
+    int64_t cap;              // slots of the cache (n_blocks * block_size): larger slots are skipped
     int32_t gpw;              // groups of 8 vectors per wave (consecutive), or 0: grid stride
     int32_t n_kv;
     int32_t block_size;
@@ -87,6 +88,7 @@ struct DequantArgs {
     const int64_t *slots;
     void *dst;
     int64_t n_vec;
+    int64_t cap;              // slots of the cache: a slot outside [0, cap) reads as zeros
     int32_t n_kv;
     int32_t block_size;
     int32_t dst_fp16;
@@ -142,6 +144,8 @@ struct DecodeArgs {
     float *k_norms_w, *v_norms_w;
     float kbnd[TQ_MAX_LEVELS - 1], vbnd[TQ_MAX_LEVELS - 1];   // boundaries, unused entries +inf
     int32_t mfma;             // 1: matrix-core pass kernels, 0: vector-ALU kernels
+    unsigned long long *v_rows_read;   // null, or a device counter: the gated pass adds the V
+                                       // code rows it reads (one atomic per wave that read any)
     int32_t contig;           // matrix-core path: every 64-token slice lies in one page
     float kc[TQ_MAX_LEVELS];
     float vc[TQ_MAX_LEVELS];

@@ -28,8 +28,9 @@ MAX_OUTLIERS = 16   # kept channels per head (TQ_MAX_OUTLIERS)
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
 EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_fit_codebook", "tq_select_outlier_channels",
-           "tq_quantize_kv", "tq_decode_attention", "tq_decode_attention_timed", "tq_append_decode_attention",
+           "tq_quantize_kv", "tq_decode_attention", "tq_decode_attention_ex", "tq_append_decode_attention",
            "tq_dequantize")
+DECODE_KERNEL_DEFAULT, DECODE_KERNEL_MFMA, DECODE_KERNEL_VALU = 0, 1, 2   # tq_decode_kernel
 
 
 class TQError(RuntimeError):
@@ -74,6 +75,43 @@ class TQCache(ctypes.Structure):
     ]
 
 
+class TQDecodeOptions(ctypes.Structure):
+    _fields_ = [
+        ("kernel", ctypes.c_int32),
+        ("chunk", ctypes.c_int32),
+        ("v_rows_read", ctypes.c_void_p),
+    ]
+
+
+@dataclass
+class DecodeOptions:
+    """tq_decode_options: the decode kernel (DECODE_KERNEL_*), the tokens per pass
+    block (0 = the library's choice) and an optional device counter (a torch int64
+    tensor of one element, zeroed by the caller) of the V rows the sparse gated
+    pass reads."""
+    kernel: int = DECODE_KERNEL_DEFAULT
+    chunk: int = 0
+    v_rows_read: object = None
+
+    def c(self) -> TQDecodeOptions:
+        o = TQDecodeOptions()
+        o.kernel = self.kernel
+        o.chunk = self.chunk
+        o.v_rows_read = None if self.v_rows_read is None else _dev_ptr(self.v_rows_read, "v_rows_read").value
+        return o
+
+
+# Options used by the decode calls that are given none.  The library reads no
+# process state; this is the binding's own default, which the tests replace to
+# run every decode call of a test on another kernel variant.  None = defaults.
+default_options: DecodeOptions | None = None
+
+
+def _opts(options):
+    o = default_options if options is None else options
+    return None if o is None else ctypes.byref(o.c())
+
+
 _lib = None
 
 
@@ -105,12 +143,12 @@ def load_library(path: str = LIB_PATH):
                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
                                         ctypes.c_void_p]
-    lib.tq_decode_attention_timed.restype = ctypes.c_int
-    lib.tq_decode_attention_timed.argtypes = lib.tq_decode_attention.argtypes + [ctypes.c_void_p]
+    lib.tq_decode_attention_ex.restype = ctypes.c_int
+    lib.tq_decode_attention_ex.argtypes = lib.tq_decode_attention.argtypes + [ctypes.c_void_p, ctypes.c_void_p]
     lib.tq_append_decode_attention.restype = ctypes.c_int
     lib.tq_append_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.POINTER(TQCache),
                                                ctypes.c_void_p, ctypes.c_int64] + \
-        lib.tq_decode_attention.argtypes[2:] + [ctypes.c_void_p]
+        lib.tq_decode_attention.argtypes[2:] + [ctypes.c_void_p, ctypes.c_void_p]
     lib.tq_dequantize.restype = ctypes.c_int
     lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_int32, ctypes.c_void_p]
@@ -280,27 +318,30 @@ def tq_quantize_kv(k_cache: Cache | None, k_src, v_cache: Cache | None, v_src, s
 
 
 def decode_workspace_bytes(k_cache: Cache, v_cache: Cache, n_seqs, n_qtok, n_q_heads, max_blocks_per_seq,
-                           tau=0.0) -> int:
+                           tau=0.0, options: DecodeOptions | None = None) -> int:
+    """The workspace size of a decode call with these shapes and options."""
     size = ctypes.c_size_t(0)
-    st = load_library().tq_decode_attention(ctypes.byref(k_cache.desc()), ctypes.byref(v_cache.desc()), None,
-                                            n_seqs, n_qtok, n_q_heads, None, None, max_blocks_per_seq,
-                                            0.0, float(tau), None, None, ctypes.byref(size), None)
+    st = load_library().tq_decode_attention_ex(ctypes.byref(k_cache.desc()), ctypes.byref(v_cache.desc()), None,
+                                               n_seqs, n_qtok, n_q_heads, None, None, max_blocks_per_seq,
+                                               0.0, float(tau), None, None, ctypes.byref(size), None,
+                                               _opts(options), None)
     _check(st, "tq_decode_attention (workspace query)")
     return size.value
 
 
 def tq_decode_attention(k_cache: Cache, v_cache: Cache, q, seq_lens, block_table, softmax_scale=0.0,
-                        sparse_v_tau=0.0, out=None, workspace=None, stream=None, events=None):
+                        sparse_v_tau=0.0, out=None, workspace=None, stream=None, events=None,
+                        options: DecodeOptions | None = None):
     """q float16 [n_seqs, n_qtok, n_q_heads, head_dim]; seq_lens int32 [n_seqs];
     block_table int32 [n_seqs, max_blocks].  Returns float32 out like q.
     events: optional pair of raw hipEvent_t handles (ctypes.c_void_p or int) recorded
-    around the main pass kernel (tq_decode_attention_timed)."""
+    around the main pass kernel; options: DecodeOptions (tq_decode_attention_ex)."""
     torch = _torch()
     n_seqs, n_qtok, n_q_heads, hd = q.shape
     if hd != k_cache.head_dim:
         raise ValueError(f"q has head_dim {hd}, the cache {k_cache.head_dim}")
     max_blocks = block_table.shape[1]
-    need = decode_workspace_bytes(k_cache, v_cache, n_seqs, n_qtok, n_q_heads, max_blocks, sparse_v_tau)
+    need = decode_workspace_bytes(k_cache, v_cache, n_seqs, n_qtok, n_q_heads, max_blocks, sparse_v_tau, options)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if out is None:
@@ -309,19 +350,19 @@ def tq_decode_attention(k_cache: Cache, v_cache: Cache, q, seq_lens, block_table
     ev = None
     if events is not None:
         ev = (ctypes.c_void_p * 2)(*[e.value if isinstance(e, ctypes.c_void_p) else e for e in events])
-    st = load_library().tq_decode_attention_timed(
+    st = load_library().tq_decode_attention_ex(
         ctypes.byref(k_cache.desc()), ctypes.byref(v_cache.desc()), _dev_ptr(q, "q", torch.float16),
         n_seqs, n_qtok, n_q_heads, _dev_ptr(seq_lens, "seq_lens", torch.int32),
         _dev_ptr(block_table, "block_table", torch.int32), max_blocks, float(softmax_scale),
         float(sparse_v_tau), _dev_ptr(out, "out", torch.float32), _dev_ptr(workspace, "workspace"),
-        ctypes.byref(size), _stream_ptr(stream), ev)
+        ctypes.byref(size), _stream_ptr(stream), _opts(options), ev)
     _check(st, "tq_decode_attention")
     return out
 
 
 def tq_append_decode_attention(k_cache: Cache, k_new, v_cache: Cache, v_new, q, seq_lens, block_table,
                                softmax_scale=0.0, sparse_v_tau=0.0, out=None, workspace=None, stream=None,
-                               events=None):
+                               events=None, options: DecodeOptions | None = None):
     """Quantize-on-append of the new tokens and decode attention in one call (the
     fused pass): k_new / v_new float16 [n_seqs * n_qtok, n_kv_heads, 128] (token
     stride from the tensor), token j of sequence b going to position
@@ -336,7 +377,7 @@ def tq_append_decode_attention(k_cache: Cache, k_new, v_cache: Cache, v_new, q, 
         if t.stride(2) != 1 or t.stride(1) != HEAD_DIM or t.stride(0) != k_new.stride(0):
             raise ValueError(f"{name}: heads must be contiguous and both share one token stride")
     max_blocks = block_table.shape[1]
-    need = decode_workspace_bytes(k_cache, v_cache, n_seqs, n_qtok, n_q_heads, max_blocks, sparse_v_tau)
+    need = decode_workspace_bytes(k_cache, v_cache, n_seqs, n_qtok, n_q_heads, max_blocks, sparse_v_tau, options)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if out is None:
@@ -350,7 +391,7 @@ def tq_append_decode_attention(k_cache: Cache, k_new, v_cache: Cache, v_new, q, 
         ctypes.c_void_p(v_new.data_ptr()), k_new.stride(0), _dev_ptr(q, "q", torch.float16), n_seqs, n_qtok,
         n_q_heads, _dev_ptr(seq_lens, "seq_lens", torch.int32), _dev_ptr(block_table, "block_table", torch.int32),
         max_blocks, float(softmax_scale), float(sparse_v_tau), _dev_ptr(out, "out", torch.float32),
-        _dev_ptr(workspace, "workspace"), ctypes.byref(size), _stream_ptr(stream), ev)
+        _dev_ptr(workspace, "workspace"), ctypes.byref(size), _stream_ptr(stream), _opts(options), ev)
     _check(st, "tq_append_decode_attention")
     return out
 

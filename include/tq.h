@@ -46,8 +46,11 @@
  *     hipStream_t; NULL is the default stream) and may be captured in a HIP graph.
  *   - All arguments are validated on the host before anything is launched; an
  *     invalid call returns an error and launches nothing.  Contents of device
- *     buffers (slots, block ids, lengths) cannot be checked on the host: values
- *     outside the documented ranges are undefined behaviour.
+ *     buffers (slots, block ids, lengths) cannot be checked on the host; the
+ *     kernels keep every access inside the given buffers whatever they hold
+ *     (slots outside the cache are skipped, page ids are clamped to the pool,
+ *     lengths to the page table's capacity), but the results for values outside
+ *     the documented ranges are unspecified.
  *   - TQ_ERR_HIP is returned when a kernel launch fails; faults inside kernels
  *     surface on the stream, as for any HIP kernel.
  */
@@ -185,7 +188,8 @@ tq_status tq_select_outlier_channels(const uint16_t *vectors, int64_t n_vectors,
  *                     token are contiguous, tokens are src_token_stride elements
  *                     apart (>= n_kv_heads * head_dim).
  *   slot_mapping    : device int64 [n_tokens]; slot = block * block_size + offset,
- *                     0 <= slot < n_blocks * block_size; a negative slot skips the token.
+ *                     0 <= slot < n_blocks * block_size of the side; a slot outside that
+ *                     range (a negative one marks padding) skips the token on that side.
  *   n_tokens        : >= 0 (0 is a no-op).
  * For each (token, head): norm -> cache.norms, 16*bits code bytes -> cache.codes,
  * and (n_outliers > 0) the kept channels' values -> cache.outliers.
@@ -220,13 +224,10 @@ tq_status tq_quantize_kv(const tq_cache *k, const void *k_src,
  * Query token j of a sequence of length len attends to positions t <= len - n_qtok + j;
  * query head h reads KV head h / (n_q_heads / n_kv_heads).  A row that sees no
  * position outputs zeros.
- * Kernels: the pass runs on the matrix cores by default; the environment variable
- * TQ_DECODE_KERNEL=valu selects the vector-ALU pass, and TQ_DECODE_CHUNK=<tokens>
- * (a multiple of 256 for the matrix-core pass, 512 for the vector-ALU pass)
- * overrides the tokens per pass block.  Both are read at every call and change
- * the workspace size.  A float16 K side and heads of more than one block need the
- * matrix-core pass (TQ_ERR_UNSUPPORTED with the vector-ALU pass), and so does a V
- * side with kept channels (a K side with kept channels: TQ_ERR_UNSUPPORTED).
+ * The pass runs on the matrix cores with the library's choice of tokens per pass
+ * block (tq_decode_attention_ex selects otherwise).  A float16 K side, heads of
+ * more than one block and a V side with kept channels are supported by the
+ * matrix-core pass (a K side with kept channels: TQ_ERR_UNSUPPORTED).
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 tq_status tq_decode_attention(const tq_cache *k, const tq_cache *v, const void *q,
                               int32_t n_seqs, int32_t n_qtok, int32_t n_q_heads,
@@ -235,19 +236,44 @@ tq_status tq_decode_attention(const tq_cache *k, const tq_cache *v, const void *
                               float sparse_v_tau, float *out, void *workspace,
                               size_t *workspace_bytes, void *stream);
 
-/* Same call as tq_decode_attention, for timing the dominant kernel: when `events`
- * is not NULL, events[0] and events[1] (hipEvent_t handles created by the caller)
- * mark the start and the end of the execution of the main pass kernel (the one
- * that streams every K code: the dense pass, or the scoring pass when
- * sparse_v_tau > 0), as hipExtLaunchKernelGGL records them.  events == NULL
- * behaves exactly like tq_decode_attention.
- * Errors: as tq_decode_attention. */
-tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const void *q,
-                                    int32_t n_seqs, int32_t n_qtok, int32_t n_q_heads,
-                                    const int32_t *seq_lens, const int32_t *block_table,
-                                    int32_t max_blocks_per_seq, float softmax_scale,
-                                    float sparse_v_tau, float *out, void *workspace,
-                                    size_t *workspace_bytes, void *stream, void *const *events);
+/* Options of one decode call (tq_decode_attention_ex, tq_append_decode_attention).
+ * A NULL options pointer, or a zeroed struct, is the default: what
+ * tq_decode_attention does.  The kernel and the chunk change the workspace size,
+ * so a workspace query must pass the same options as the call it sizes. */
+typedef enum tq_decode_kernel {
+    TQ_DECODE_KERNEL_DEFAULT = 0,   /* the matrix-core pass */
+    TQ_DECODE_KERNEL_MFMA = 1,      /* the matrix-core pass (fp16 MFMA, fp32-level operands) */
+    TQ_DECODE_KERNEL_VALU = 2       /* the vector-ALU pass: 128-wide heads, compressed K, V
+                                       without kept channels, no fused append
+                                       (TQ_ERR_UNSUPPORTED otherwise) */
+} tq_decode_kernel;
+
+typedef struct tq_decode_options {
+    int32_t  kernel;          /* a tq_decode_kernel value */
+    int32_t  chunk;           /* tokens per pass block: 0 = the library's choice, else a multiple
+                                 of 256 (matrix-core pass) or 512 (vector-ALU pass), at most
+                                 1 << 20 (TQ_ERR_INVALID_ARG otherwise) */
+    uint64_t *v_rows_read;    /* NULL, or a device counter: with sparse_v_tau > 0 the gated pass
+                                 adds the number of V code rows it read (one per token and
+                                 128-element block of a KV head whose weight some query row
+                                 keeps); the caller zeroes it.  Not touched when tau = 0. */
+} tq_decode_options;
+
+/* tq_decode_attention with options, and with start / stop events on the dominant
+ * kernel: when `events` is not NULL, events[0] and events[1] (hipEvent_t handles
+ * created by the caller) mark the start and the end of the execution of the main
+ * pass kernel (the one that streams every K code: the dense pass, or the scoring
+ * pass when sparse_v_tau > 0), as hipExtLaunchKernelGGL records them.
+ *   opts   : host, may be NULL (defaults).
+ *   events : host array of two hipEvent_t, may be NULL.
+ * Errors: as tq_decode_attention; TQ_ERR_INVALID_ARG for a bad chunk or kernel. */
+tq_status tq_decode_attention_ex(const tq_cache *k, const tq_cache *v, const void *q,
+                                 int32_t n_seqs, int32_t n_qtok, int32_t n_q_heads,
+                                 const int32_t *seq_lens, const int32_t *block_table,
+                                 int32_t max_blocks_per_seq, float softmax_scale,
+                                 float sparse_v_tau, float *out, void *workspace,
+                                 size_t *workspace_bytes, void *stream,
+                                 const tq_decode_options *opts, void *const *events);
 
 /* Quantize-on-append and decode attention in one call: the same result as
  * tq_quantize_kv(k, k_new, v, v_new, new_token_stride, n_seqs * n_qtok, slots)
@@ -264,8 +290,9 @@ tq_status tq_decode_attention_timed(const tq_cache *k, const tq_cache *v, const 
  * (TQ_ERR_UNSUPPORTED otherwise: use the two calls).  Codes of elements within
  * rounding of a decision boundary may differ from tq_quantize_kv's (both count
  * the boundaries below the rotated value, in float32 with different roundings).
- * events: as in tq_decode_attention_timed (may be NULL).  Workspace: as
- * tq_decode_attention (query with workspace NULL).
+ * opts, events: as in tq_decode_attention_ex (either may be NULL; the kernel must
+ * be the matrix-core pass).  Workspace: as tq_decode_attention (query with
+ * workspace NULL and the same options).
  * Errors: as tq_decode_attention; TQ_ERR_INVALID_ARG for NULL or misaligned new
  *         rows or a bad stride. */
 tq_status tq_append_decode_attention(const tq_cache *k, const void *k_new, const tq_cache *v, const void *v_new,
@@ -273,13 +300,14 @@ tq_status tq_append_decode_attention(const tq_cache *k, const void *k_new, const
                                      int32_t n_q_heads, const int32_t *seq_lens, const int32_t *block_table,
                                      int32_t max_blocks_per_seq, float softmax_scale, float sparse_v_tau,
                                      float *out, void *workspace, size_t *workspace_bytes, void *stream,
-                                     void *const *events);
+                                     const tq_decode_options *opts, void *const *events);
 
 /* Dequantize cache rows: dst[t][h][:] = x_hat of slot slots[t], head h
  * ([llama-tq]: K needs no dequantization inside attention; this is the explicit
  * inverse for everything else).
  *   c           : host descriptor.
- *   slots       : device int64 [n_tokens], each in [0, n_blocks*block_size).
+ *   slots       : device int64 [n_tokens]; a slot outside [0, n_blocks*block_size)
+ *                 yields a row of zeros.
  *   dst         : device [n_tokens][n_kv_heads][head_dim], float16 if dst_is_fp16 else float32.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
 tq_status tq_dequantize(const tq_cache *c, const int64_t *slots, int32_t n_tokens,

@@ -80,15 +80,41 @@ def fake_cache(bits=4, n_kv=2, block_size=256, n_blocks=4, head_dim=128):
     return d
 
 
+VALU = T.DecodeOptions(kernel=T.DECODE_KERNEL_VALU)
+
+
 def decode_call(k=None, v=None, n_seqs=1, n_qtok=1, n_q_heads=2, max_blocks=4, scale=0.0, tau=0.0,
-                ws=None, ws_bytes=None, q=FAKE, out=FAKE):
+                ws=None, ws_bytes=None, q=FAKE, out=FAKE, options=None):
+    """tq_decode_attention (options None) or tq_decode_attention_ex with the options."""
     lib = T.load_library()
     k = fake_cache() if k is None else k
     v = fake_cache(bits=3) if v is None else v
     size = ctypes.c_size_t(0 if ws_bytes is None else ws_bytes)
-    st = lib.tq_decode_attention(ctypes.byref(k), ctypes.byref(v), q, n_seqs, n_qtok, n_q_heads, FAKE, FAKE,
-                                 max_blocks, scale, tau, out, ws, ctypes.byref(size), None)
+    if options is None:
+        st = lib.tq_decode_attention(ctypes.byref(k), ctypes.byref(v), q, n_seqs, n_qtok, n_q_heads, FAKE, FAKE,
+                                     max_blocks, scale, tau, out, ws, ctypes.byref(size), None)
+    else:
+        st = lib.tq_decode_attention_ex(ctypes.byref(k), ctypes.byref(v), q, n_seqs, n_qtok, n_q_heads, FAKE,
+                                        FAKE, max_blocks, scale, tau, out, ws, ctypes.byref(size), None,
+                                        ctypes.byref(options.c()), None)
     return st, size.value
+
+
+def test_decode_options():
+    """The kernel and the chunk are arguments: the workspace follows them, bad values
+    are rejected, and a zeroed options struct is the default call."""
+    _, dflt = decode_call()
+    assert decode_call(options=T.DecodeOptions()) == (T.TQ_OK, dflt)
+    assert decode_call(options=T.DecodeOptions(kernel=T.DECODE_KERNEL_MFMA)) == (T.TQ_OK, dflt)
+    st, valu = decode_call(options=VALU)
+    assert st == T.TQ_OK and valu != dflt            # the vector-ALU pass keeps rotated queries too
+    _, big = decode_call(max_blocks=64, options=T.DecodeOptions(chunk=256))
+    _, small = decode_call(max_blocks=64, options=T.DecodeOptions(chunk=1024))
+    assert big > small                               # more chunks, more partials
+    for bad in (T.DecodeOptions(kernel=3), T.DecodeOptions(kernel=-1), T.DecodeOptions(chunk=100),
+                T.DecodeOptions(chunk=-256), T.DecodeOptions(chunk=1 << 21),
+                T.DecodeOptions(kernel=T.DECODE_KERNEL_VALU, chunk=256)):   # the ALU pass's unit is 512
+        assert decode_call(options=bad)[0] == T.TQ_ERR_INVALID_ARG, bad
 
 
 def test_decode_workspace_query():
@@ -136,7 +162,7 @@ def test_decode_validation_errors():
                                    FAKE, None, None, None) == T.TQ_ERR_INVALID_ARG
 
 
-def test_decode_wide_heads_validation(monkeypatch):
+def test_decode_wide_heads_validation():
     """Heads of 256 / 512 elements: both sides alike; the workspace holds nb
     accumulators per row; only the matrix-core pass takes them."""
     _, size128 = decode_call()
@@ -145,9 +171,9 @@ def test_decode_wide_heads_validation(monkeypatch):
         assert st == T.TQ_OK and size > size128
         assert decode_call(k=fake_cache(head_dim=hd))[0] == T.TQ_ERR_INVALID_ARG   # V is 128 wide
     assert decode_call(k=fake_cache(head_dim=384), v=fake_cache(bits=3, head_dim=384))[0] == T.TQ_ERR_UNSUPPORTED
-    monkeypatch.setenv("TQ_DECODE_KERNEL", "valu")
-    assert decode_call(k=fake_cache(head_dim=256), v=fake_cache(bits=3, head_dim=256))[0] == T.TQ_ERR_UNSUPPORTED
-    assert decode_call()[0] == T.TQ_OK
+    assert decode_call(k=fake_cache(head_dim=256), v=fake_cache(bits=3, head_dim=256), options=VALU)[0] == \
+        T.TQ_ERR_UNSUPPORTED
+    assert decode_call(options=VALU)[0] == T.TQ_OK
 
 
 def test_quantize_validation_errors():
@@ -241,10 +267,9 @@ def test_fit_codebook_rejects_bad_arguments():
     assert ok(3, 4, 1, 10, v=z) == T.TQ_ERR_INVALID_ARG     # no nonzero vector
 
 
-def test_float16_side_validation(monkeypatch):
+def test_float16_side_validation():
     """A float16 side needs no norms, signs or codebook; only K may be float16 in
     decode, and only with the matrix-core pass."""
-    monkeypatch.delenv("TQ_DECODE_KERNEL", raising=False)
     k16 = fake_cache(bits=T.BITS_FP16)
     k16.norms, k16.signs = None, None
     st, need = decode_call(k=k16)
@@ -252,9 +277,7 @@ def test_float16_side_validation(monkeypatch):
     assert decode_call(k=k16, tau=1e-3)[0] == T.TQ_OK
     assert decode_call(v=fake_cache(bits=T.BITS_FP16))[0] == T.TQ_ERR_UNSUPPORTED
     assert decode_call(k=fake_cache(bits=8))[0] == T.TQ_ERR_UNSUPPORTED
-    monkeypatch.setenv("TQ_DECODE_KERNEL", "valu")
-    assert decode_call(k=k16)[0] == T.TQ_ERR_UNSUPPORTED
-    monkeypatch.delenv("TQ_DECODE_KERNEL")
+    assert decode_call(k=k16, options=VALU)[0] == T.TQ_ERR_UNSUPPORTED
     # a compressed side still needs its norms, signs and codebook
     k4 = fake_cache()
     k4.norms = None
@@ -302,7 +325,7 @@ def _kept(c, k=4, channels=FAKE + 0x300000, values=FAKE + 0x400000):
     return c
 
 
-def test_kept_channel_validation(monkeypatch):
+def test_kept_channel_validation():
     lib = T.load_library()
     q_call = lambda kk: lib.tq_quantize_kv(ctypes.byref(kk), FAKE, None, None, 256, 4, FAKE, None)
     assert q_call(_kept(fake_cache(), k=17)) == T.TQ_ERR_INVALID_ARG
@@ -319,23 +342,23 @@ def test_kept_channel_validation(monkeypatch):
     st, size = decode_call(v=_kept(fake_cache(bits=3)))
     assert st == T.TQ_OK and size > plain
     assert decode_call(k=_kept(fake_cache()))[0] == T.TQ_ERR_UNSUPPORTED
-    monkeypatch.setenv("TQ_DECODE_KERNEL", "valu")
-    assert decode_call(v=_kept(fake_cache(bits=3)))[0] == T.TQ_ERR_UNSUPPORTED
+    assert decode_call(v=_kept(fake_cache(bits=3)), options=VALU)[0] == T.TQ_ERR_UNSUPPORTED
 
 
 # ------------------------------------------------------------- fused append + decode
 
-def test_append_decode_validation(monkeypatch):
+def test_append_decode_validation():
     """tq_append_decode_attention: the decode checks plus the new rows; only the
     matrix-core pass with 128-wide heads, compressed K and V without kept channels."""
     lib = T.load_library()
 
-    def call(k=None, v=None, k_new=FAKE, v_new=FAKE, stride=256, ws=None, ws_bytes=0):
+    def call(k=None, v=None, k_new=FAKE, v_new=FAKE, stride=256, ws=None, ws_bytes=0, options=None):
         k = fake_cache() if k is None else k
         v = fake_cache(bits=3) if v is None else v
         size = ctypes.c_size_t(ws_bytes)
         return lib.tq_append_decode_attention(ctypes.byref(k), k_new, ctypes.byref(v), v_new, stride, FAKE, 1, 1,
                                               2, FAKE, FAKE, 4, 0.0, 0.0, FAKE, ws, ctypes.byref(size), None,
+                                              None if options is None else ctypes.byref(options.c()),
                                               None), size.value
     st, size = call()
     assert st == T.TQ_OK and size == decode_call()[1]          # workspace query, as decode
@@ -347,5 +370,6 @@ def test_append_decode_validation(monkeypatch):
     assert call(v=_kept(fake_cache(bits=3)))[0] == T.TQ_ERR_UNSUPPORTED
     assert call(k=fake_cache(head_dim=256), v=fake_cache(bits=3, head_dim=256), stride=512)[0] == \
         T.TQ_ERR_UNSUPPORTED
-    monkeypatch.setenv("TQ_DECODE_KERNEL", "valu")
-    assert call()[0] == T.TQ_ERR_UNSUPPORTED
+    assert call(options=VALU)[0] == T.TQ_ERR_UNSUPPORTED
+    assert call(options=T.DecodeOptions(chunk=1024))[0] == T.TQ_OK
+
