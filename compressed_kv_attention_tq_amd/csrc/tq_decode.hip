@@ -276,6 +276,7 @@ void tq_decode_pass_kernel(DecodeArgs a,
     warm_q<RP>(launder_sgpr(qr));
     __syncthreads();                                   // ktab / vtab
 
+    uint32_t v_rows = 0;   // gated: V rows this wave reads
     for (int base = first; base < end; base += kStride) {   // uniform per wave
         const int t = base + lane;
         float s[RP];
@@ -300,6 +301,7 @@ void tq_decode_pass_kernel(DecodeArgs a,
             }
             const uint64_t bal = __ballot(kept);
             const int total = __popcll(bal);
+            v_rows += total;
             if (kept) keep_idx[wave][__popcll(bal & ((1ull << lane) - 1ull))] = lane;
             __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): this wave's LDS writes done
             __builtin_amdgcn_wave_barrier();
@@ -369,6 +371,9 @@ void tq_decode_pass_kernel(DecodeArgs a,
         }
     }
 
+    if constexpr (MODE == MODE_GATED) {
+        if (a.v_rows_read && lane == 0 && v_rows > 0) atomicAdd(a.v_rows_read, (unsigned long long)v_rows);
+    }
     // ---------------- merge the waves' partials and write the chunk's result
     if constexpr (MODE != MODE_GATED) {
         if (lane == 0) {
@@ -435,7 +440,8 @@ __global__ __launch_bounds__(256) void tq_stats_kernel(DecodeArgs a) {
     const int b = (int)fdiv(blockIdx.x, a.kv_div), kv = blockIdx.x - b * a.n_kv;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int len = a.seq_lens[b];
-    const int nc = (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div);
+    // (a length past the table's capacity is clamped to the chunks the workspace holds)
+    const int nc = min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), a.n_chunks);
     const float *ml = a.part_ml + ((int64_t)b * a.n_kv + kv) * a.n_chunks * a.rows_pad * 2;
     for (int r = wave; r < a.rows_pad; r += 4) {
         float m = -INFINITY;
@@ -464,7 +470,10 @@ __global__ __launch_bounds__(256) void tq_stats_kernel(DecodeArgs a) {
 // groups are merged through LDS and o = s_V * H (acc / L) / sqrt(128).  Gated:
 // the partials are already normalised and are summed.
 // --------------------------------------------------------------------------
-template <bool SPARSE, bool KEPT>   // KEPT: the V side keeps channels (a.n_out > 0)
+// KEPT: the V side keeps channels (a.n_out > 0); KB: chunks per thread per round
+// of loads (2, 4, 8 or 16: the smallest with 8 KB >= n_chunks, so a row's loads are
+// one round and the registers, hence the blocks per CU, follow the chunk count)
+template <bool SPARSE, bool KEPT, int KB>
 __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     typedef float f4_t __attribute__((ext_vector_type(4)));
     __shared__ float gm[8], gl[8];
@@ -497,7 +506,7 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     const float *pa2 = pa - 4 * q4 + kD + 4 * min(q4, 3);
     float M = -INFINITY, L = 0.f;
     f4_t x = {0.f, 0.f, 0.f, 0.f}, x2 = {0.f, 0.f, 0.f, 0.f};
-    constexpr int kB = 16;   // chunks per thread per batch (one round of loads)
+    constexpr int kB = KB;   // chunks per thread per batch (one round of loads)
     typedef float f2_t __attribute__((ext_vector_type(2)));
     f2_t mlr[kB];
     float m[kB], l[kB];
@@ -562,7 +571,8 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     load_round(cg, min(a.n_chunks, 8 * kB));
     __builtin_amdgcn_sched_barrier(0);
     const int len = a.seq_lens[b];
-    const int nc = len > 0 ? (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div) : 0;
+    // (clamped to the chunks the workspace holds, whatever the length)
+    const int nc = len > 0 ? min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), a.n_chunks) : 0;
     mask_round(cg, nc);
     fold_round();
     for (int c0 = cg + 8 * kB; c0 < nc; c0 += 8 * kB) {
@@ -708,10 +718,18 @@ static void launch_pass_any(const DecodeArgs &a, int mode, hipStream_t s, hipEve
     }
 }
 
+template <bool SPARSE, int KB>
+static void launch_merge_kb(const DecodeArgs &a, dim3 grid, hipStream_t s) {
+    if (a.n_out > 0) hipLaunchKernelGGL((tq_merge_kernel<SPARSE, true, KB>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((tq_merge_kernel<SPARSE, false, KB>), grid, dim3(256), 0, s, a);
+}
+
 template <bool SPARSE>
 static void launch_merge(const DecodeArgs &a, dim3 grid, hipStream_t s) {
-    if (a.n_out > 0) hipLaunchKernelGGL((tq_merge_kernel<SPARSE, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((tq_merge_kernel<SPARSE, false>), grid, dim3(256), 0, s, a);
+    if (a.n_chunks <= 16) launch_merge_kb<SPARSE, 2>(a, grid, s);
+    else if (a.n_chunks <= 32) launch_merge_kb<SPARSE, 4>(a, grid, s);
+    else if (a.n_chunks <= 64) launch_merge_kb<SPARSE, 8>(a, grid, s);
+    else launch_merge_kb<SPARSE, 16>(a, grid, s);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, const PairTables &pt, hipStream_t s, hipEvent_t ev_before,

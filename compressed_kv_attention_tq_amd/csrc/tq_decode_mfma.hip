@@ -594,7 +594,7 @@ void tq_decode_mfma_kernel(
         const u4v x0 = reinterpret_cast<g_u4 *>(srcp)[0], x1 = reinterpret_cast<g_u4 *>(srcp)[1];
         aw[0] = x0.x; aw[1] = x0.y; aw[2] = x0.z; aw[3] = x0.w;
         aw[4] = x1.x; aw[5] = x1.y; aw[6] = x1.z; aw[7] = x1.w;
-        apage = btab[fdiv((uint32_t)av.pos, bsdiv)];
+        apage = btab[min((int)fdiv((uint32_t)av.pos, bsdiv), last_entry)];
     };
     // the first 8 vectors go out with the first slice's loads: after its page is
     // read (so the wait for the page never covers them) and before its data
@@ -673,7 +673,7 @@ void tq_decode_mfma_kernel(
     // sparse: global (max, sum) of each row from the scoring pass's chunk partials
     // (part_ml is [chunk][row][block][2]; the blocks' entries are equal, block 0's is read)
     if constexpr (GATED) {
-        const int nc = (int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div);
+        const int nc = min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), a.n_chunks);
         const float *ml = part_ml + (int64_t)unit * a.n_chunks * rp * NB * 2;
         for (int r = wave; r < R; r += kMW) {
             float m = -INFINITY;
@@ -810,14 +810,17 @@ void tq_decode_mfma_kernel(
                 const int tk = av.pos - app0;
                 const uint32_t sb = (asg >> ((l8.j & 1) * 16)) & 0xFFFFu;
                 uint32_t code[16], lo, hi;
+                // (the cache rows are written only for a page inside the pool; the
+                // copy for this launch's attention always)
+                const bool in_pool = (unsigned)apage <= (unsigned)a.max_page;
                 if (!av.side) {
                     const float nm = encode_block8<KB>(aw, sb, bk, l8.j, code);
                     pack_lane_codes<KB>(code, lo, hi);
                     if (av.live) {
-                        store_lane_packed<KB>(a.k_codes_w + arow * KROW, lo, hi, l8.j);
+                        if (in_pool) store_lane_packed<KB>(a.k_codes_w + arow * KROW, lo, hi, l8.j);
                         store_lane_packed<KB>(apbuf + tk * KROW, lo, hi, l8.j);
                         if (l8.j == 0) {
-                            a.k_norms_w[arow] = nm;
+                            if (in_pool) a.k_norms_w[arow] = nm;
                             apn[tk] = nm;
                         }
                     }
@@ -836,12 +839,14 @@ void tq_decode_mfma_kernel(
                     }
                     if (av.live) {
                         uint8_t *vrow = a.v_codes_w + arow * (16 * vb);
-                        if (vb == 4) store_lane_packed<4>(vrow, lo, hi, l8.j);
-                        else if (vb == 3) store_lane_packed<3>(vrow, lo, hi, l8.j);
-                        else store_lane_packed<2>(vrow, lo, hi, l8.j);
+                        if (in_pool) {
+                            if (vb == 4) store_lane_packed<4>(vrow, lo, hi, l8.j);
+                            else if (vb == 3) store_lane_packed<3>(vrow, lo, hi, l8.j);
+                            else store_lane_packed<2>(vrow, lo, hi, l8.j);
+                        }
                         if constexpr (DENSE) store_lane_packed<VB>(apbuf + 16 * KROW + tk * VROW, lo, hi, l8.j);
                         if (l8.j == 0) {
-                            a.v_norms_w[arow] = nm;
+                            if (in_pool) a.v_norms_w[arow] = nm;
                             apn[16 + tk] = nm;
                         }
                     }
@@ -858,20 +863,45 @@ void tq_decode_mfma_kernel(
         }
     }
 
-    // ---- score MFMAs of the loaded slice
+    // ---- score MFMAs of the loaded slice.  The 16 table lookups of tile tm + 1 are
+    // issued before the MFMAs of tile tm (the scheduling barriers keep that order),
+    // so the LDS round trip of one tile is covered by the previous tile's MFMAs
+    // instead of being waited for in front of every MFMA.
     auto score_mfma = [&](const Slot &sl, f4_t (&S)[4]) {
+        if constexpr (KF) {
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            S[tm] = f4_t{0.f, 0.f, 0.f, 0.f};
+            for (int tm = 0; tm < 4; ++tm) {
+                S[tm] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                u4_t af;
-                if constexpr (KF) af = u4_t{sl.kw[tm][4 * ks], sl.kw[tm][4 * ks + 1], sl.kw[tm][4 * ks + 2],
-                                            sl.kw[tm][4 * ks + 3]};
-                else af = k_frag<KB, RB>(sl.kw[tm], ks, ktab, lane_off);
-                S[tm] = mfma_f16(af, qb[ks], S[tm]);
-                if constexpr (!PK) S[tm] = mfma_f16(af, qb[4 + ks], S[tm]);
+                for (int ks = 0; ks < 4; ++ks) {
+                    const u4_t af = u4_t{sl.kw[tm][4 * ks], sl.kw[tm][4 * ks + 1], sl.kw[tm][4 * ks + 2],
+                                         sl.kw[tm][4 * ks + 3]};
+                    S[tm] = mfma_f16(af, qb[ks], S[tm]);
+                    if constexpr (!PK) S[tm] = mfma_f16(af, qb[4 + ks], S[tm]);
+                }
             }
+        } else {
+            u4_t fa[4], fb[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) fa[ks] = k_frag<KB, RB>(sl.kw[0], ks, ktab, lane_off);
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (tm < 3) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) fb[ks] = k_frag<KB, RB>(sl.kw[tm + 1], ks, ktab, lane_off);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                S[tm] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    S[tm] = mfma_f16(fa[ks], qb[ks], S[tm]);
+                    if constexpr (!PK) S[tm] = mfma_f16(fa[ks], qb[4 + ks], S[tm]);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) fa[ks] = fb[ks];
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     // the slice's norms to the wave's LDS rows (V norms past the chunk's end are
@@ -1008,22 +1038,42 @@ void tq_decode_mfma_kernel(
                     pb[2 + ks][k] = split_pair(w[tm][e0], w[tm][e0 + 1], 1.f);
                 }
             }
+        // four groups of four position tiles (ks, j0 .. j0 + 3); the lookups of the
+        // next group go out before the MFMAs of the current one, as for the scores
+        uint32_t x[2][4], y[2][4];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            uint32_t u[8], x[4], y[4];
+            uint32_t u[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) u[e] = vunit_bits<VB>(sl.vw[ks][e], vo);
-            v_pairs<VB>(u, x, y);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const u4_t af = v_frag<VB>(x, y, j, vtab, lane_off);
-                acc[j] = mfma_f16(af, pb[ks], acc[j]);
-                if constexpr (!PK) acc[j] = mfma_f16(af, pb[2 + ks], acc[j]);
-            }
+            v_pairs<VB>(u, x[ks], y[ks]);
         }
+        u4_t fa[4], fb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = v_frag<VB>(x[0], y[0], i, vtab, lane_off);
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            const int ks = gi >> 1, j0 = 4 * (gi & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (gi < 3) {
+                const int ksn = (gi + 1) >> 1, jn = 4 * ((gi + 1) & 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fb[i] = v_frag<VB>(x[ksn], y[ksn], jn + i, vtab, lane_off);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[j0 + i] = mfma_f16(fa[i], pb[ks], acc[j0 + i]);
+                if constexpr (!PK) acc[j0 + i] = mfma_f16(fa[i], pb[2 + ks], acc[j0 + i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[i] = fb[i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     float m_raw = -INFINITY, m_state = -INFINITY, l_run = 0.f, E_run = -INFINITY;
+    uint32_t v_rows = 0;   // gated: V code rows this wave reads
 
     if constexpr (!GATED) {
         // ---------------- dense / scoring pass: a two-slot ring, the next slice's
@@ -1140,11 +1190,41 @@ void tq_decode_mfma_kernel(
         // ---------------- gated pass: candidate slices only (a group's decision is
         // the same in its NB waves; NB > 1: every wave takes part in each step's
         // exchange, as in the dense loop)
+        // The candidate test of 64 steps at a time: lane i loads the tile maxima of
+        // every row for step i of the round and compares them with the rows'
+        // thresholds (the same values and compare as sthr), so the loop waits for
+        // one round trip per 64 slices instead of one per slice.
+        float sthr_r[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            sthr_r[r] = INFINITY;
+            if (r < R) {
+                const float M = gstat[r][0], L = gstat[r][1];
+                if (L > 0.f && M > -INFINITY) sthr_r[r] = (M + log2f(L)) + log2f(a.tau);
+            }
+        }
         const int lead = first - start;
-        for (int b0 = NB == 1 ? first : start; b0 < end; b0 += kStride) {
+        uint64_t cmask = 0;
+        int step = 0;
+        for (int b0 = NB == 1 ? first : start; b0 < end; b0 += kStride, ++step) {
             const int base = NB == 1 ? b0 : b0 + lead;
-            const float tmx = row_ok && base < end ? tilemax[(tile0 + (base >> 6)) * rp + col_row] : -INFINITY;
-            const bool cand = __ballot(tmx >= sthr) != 0ull;
+            if ((step & 63) == 0) {
+                const int bi = base + lane * kStride;
+                bool c = false;
+                if (bi < end) {
+                    const f4_t *tp = reinterpret_cast<const f4_t *>(tilemax + (tile0 + (bi >> 6)) * rp);
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        if (4 * r4 < rp) {
+                            const f4_t t = tp[r4];
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) c = c || (4 * r4 + k < R && t[k] >= sthr_r[4 * r4 + k]);
+                        }
+                    }
+                }
+                cmask = __ballot(c);
+            }
+            const bool cand = ((cmask >> (step & 63)) & 1ull) != 0ull;
             if constexpr (NB == 1) {
                 if (!cand) continue;
             }
@@ -1178,6 +1258,17 @@ void tq_decode_mfma_kernel(
                     kept[tm][e] = ((bal >> (16 * g)) & 0xFFFFull) != 0ull;
                 }
             if (!any) continue;
+            if (a.v_rows_read) {   // the V rows this slice reads (token groups g with a kept row)
+                uint32_t cnt = 0;
+#pragma unroll
+                for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint64_t bal = __ballot(kept[tm][e] && n == 0);
+                        cnt += (uint32_t)__popcll(bal);
+                    }
+                v_rows += cnt;
+            }
             load_v(sa, r0, [&](int tm, int e) { return kept[tm][e]; });
             const float E_new = fmaxf(E_run, E_s);
             if (E_run != -INFINITY && E_new != E_run) {
@@ -1204,6 +1295,9 @@ void tq_decode_mfma_kernel(
         }
     }
 
+    if constexpr (GATED) {
+        if (a.v_rows_read && lane == 0 && v_rows > 0) atomicAdd(a.v_rows_read, (unsigned long long)v_rows);
+    }
     // ---------------- merge the waves' partials into the chunk's partial
     if constexpr (WV && PK) {
 #pragma unroll

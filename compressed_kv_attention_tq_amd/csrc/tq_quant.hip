@@ -134,7 +134,7 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
         const bool valid = g0 + L.vin < p.n_vec;
         if constexpr (BITS == 16) {
             const int64_t slot = gr.slot;
-            if (valid && slot >= 0) {
+            if (valid && slot >= 0 && slot < p.cap) {
                 const uint32_t blk_id = fdiv((uint32_t)slot, bsdiv);
                 const uint32_t off = (uint32_t)slot - blk_id * (uint32_t)p.block_size;
                 const int64_t row = ((int64_t)blk_id * p.n_kv + head) * p.block_size + off;
@@ -176,7 +176,7 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
         }
 
         const int64_t slot = gr.slot;
-        if (valid && slot >= 0) {
+        if (valid && slot >= 0 && slot < p.cap) {
             const uint32_t blk_id = fdiv((uint32_t)slot, bsdiv);
             const uint32_t off = (uint32_t)slot - blk_id * (uint32_t)p.block_size;
             const int64_t row = ((int64_t)blk_id * p.n_kv + head) * p.block_size + off;
@@ -278,12 +278,18 @@ __global__ __launch_bounds__(256) void tq_dequantize_fp16_kernel(DequantArgs a) 
         if (vid >= a.n_vec) continue;
         const int tok = (int)fdiv((uint32_t)vid, a.kv_div);
         const int head = vid - tok * a.n_kv;
-        const uint32_t slot = (uint32_t)a.slots[tok];
-        const uint32_t blk_id = fdiv(slot, a.bs_div);
-        const uint32_t off = slot - blk_id * (uint32_t)a.block_size;
-        const int64_t row = ((int64_t)blk_id * a.n_kv + head) * a.block_size + off;
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.codes + row * 256 + 32 * j);
-        const uint4 x0 = src[0], x1 = src[1];
+        // (a slot outside the cache reads as a row of zeros)
+        const int64_t sl = a.slots[tok];
+        uint4 x0 = make_uint4(0u, 0u, 0u, 0u), x1 = x0;
+        if (sl >= 0 && sl < a.cap) {
+            const uint32_t slot = (uint32_t)sl;
+            const uint32_t blk_id = fdiv(slot, a.bs_div);
+            const uint32_t off = slot - blk_id * (uint32_t)a.block_size;
+            const int64_t row = ((int64_t)blk_id * a.n_kv + head) * a.block_size + off;
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.codes + row * 256 + 32 * j);
+            x0 = src[0];
+            x1 = src[1];
+        }
         const int64_t dbase = ((int64_t)tok * a.n_kv + head) * kD + 16 * j;
         if (a.dst_fp16) {
             uint4 *d = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.dst) + dbase);
@@ -328,8 +334,11 @@ __global__ __launch_bounds__(256) void tq_dequantize_kernel(DequantArgs a) {
         int64_t row = 0;
         uint32_t w[2] = {0, 0};
         float n = 0.f;
-        if (valid) {
-            const uint32_t slot = (uint32_t)a.slots[tok];
+        // (a slot outside the cache reads as a row of zeros: norm 0, no kept values)
+        const int64_t sl = valid ? a.slots[tok] : -1;
+        const bool in_cache = sl >= 0 && sl < a.cap;
+        if (in_cache) {
+            const uint32_t slot = (uint32_t)sl;
             const uint32_t blk_id = fdiv(slot, bsdiv);
             const uint32_t off = slot - blk_id * (uint32_t)a.block_size;
             row = ((int64_t)blk_id * a.n_kv + head) * a.block_size + off;
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(256) void tq_dequantize_kernel(DequantArgs a) {
             // kept channels: their stored values over the reconstruction (this thread
             // wrote those elements above, so its later stores land last)
             const int64_t prow = a.n_out > 0 ? row / a.block_size : 0, poff = row - prow * a.block_size;
-            for (int s = 0; s < a.n_out; ++s) {
+            for (int s = 0; in_cache && s < a.n_out; ++s) {
                 const int c = a.out_idx[head * 16 + s] & 127;
                 if ((c >> 4) != j) continue;
                 const uint16_t hv = a.outliers[(prow * a.n_out + s) * a.block_size + poff];
