@@ -76,6 +76,56 @@ def upload_blocks(oc, g, blocks):
         g.outliers.index_copy_(0, idx, t.from_numpy(oc.outliers[blocks]).to(g.outliers.device))
 
 
+def oracle_cache_from_gpu(g, like):
+    """An oracle cache holding what a device cache holds (codes, norms, kept values),
+    with the signs, codebook and kept-channel list of the oracle cache `like`: the
+    oracle's attention over it checks the attention arithmetic alone, whatever codes
+    the GPU wrote."""
+    c = O.new_cache(like.bits, like.n_kv_heads, like.block_size, like.n_blocks, like.signs, like.cb,
+                    head_dim=like.head_dim,
+                    outlier_channels=like.outlier_channels if like.n_outliers else None)
+    c.codes[...] = g.codes.cpu().numpy()
+    c.norms[...] = g.norms.cpu().numpy()
+    if like.n_outliers:
+        c.outliers[...] = g.outliers.cpu().numpy()
+    return c
+
+
+ELEM_TOL = 1e-3
+
+
+def assert_attention_close(got, want, slack=None, what=""):
+    """Attention outputs [..., d] against the oracle's, row by row and element by element.
+
+    Per row: ||got - want|| <= 1e-3 ||want|| (+ slack).  Per element:
+    |got_i - want_i| <= 1e-3 max(|want_i|, ||want|| / sqrt(d)) (+ slack_i).  A row
+    whose oracle output is zero must be zero within 1e-6 (+ slack).  slack: None, or
+    (row slack [...], element slack [..., d]) for gate decisions within rounding of
+    tau.  Returns the worst per-row relative error and the worst element error
+    relative to its bound."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    d = want.shape[-1]
+    rs = np.zeros(want.shape[:-1]) if slack is None else np.asarray(slack[0], np.float64)
+    es = np.zeros(want.shape) if slack is None else np.asarray(slack[1], np.float64)
+    den = np.linalg.norm(want, axis=-1)
+    err = np.linalg.norm(got - want, axis=-1)
+    zero = den == 0
+    bad = zero & (err > 1e-6 + rs)
+    assert not bad.any(), f"{what}: {int(bad.sum())} rows should be zero (worst |got| {float(err[bad].max()):.3e})"
+    bad = ~zero & (err > ELEM_TOL * den + rs)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} rows beyond 1e-3 relative L2 "
+                           f"(worst {float((err / np.where(zero, 1.0, den))[bad].max()):.3e})")
+    bound = ELEM_TOL * np.maximum(np.abs(want), (den / np.sqrt(d))[..., None])
+    eerr = np.abs(got - want)
+    ebad = ~zero[..., None] & (eerr > bound + es)
+    assert not ebad.any(), (f"{what}: {int(ebad.sum())} elements beyond 1e-3 max(|want_i|, ||want||/sqrt(d)) "
+                            f"(worst ratio {float((eerr / np.maximum(bound, 1e-300))[ebad].max()):.3e})")
+    rel = np.where(zero, 0.0, err / np.where(zero, 1.0, den))
+    eratio = np.where(zero[..., None], 0.0, eerr / np.maximum(bound, 1e-300))
+    return float(rel.max()) if rel.size else 0.0, float(eratio.max()) if eratio.size else 0.0
+
+
 def row_rel_err(got, want):
     """Per-row ||got - want|| / ||want|| over the last axis (rows with ||want|| = 0 use 1)."""
     got = np.asarray(got, np.float64)
