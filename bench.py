@@ -3,19 +3,32 @@
 A step is one pass of the whole hot path over one batch: quantize-on-append of
 the new tokens' K and V into the paged compressed cache and decode attention of
 the new query tokens over the whole cache, in one call
-(tq_append_decode_attention, the append fused into the decode pass) where that
-is supported, else tq_quantize_kv then tq_decode_attention.  The default workload is the Llama-3-8B-shaped decode:
-1 sequence of 32768 tokens, 32 query / 8 KV heads, d = 128, K 4-bit, V 3-bit.
+(tq_append_decode_attention: the append fused into the decode pass).
 
-The cache is replicated R times (R x 31.5 MB > the 256 MB last-level cache)
-and step i works on replica i mod R, so every step streams its cache from HBM.
-`value` = algorithmic bytes of a step / time of a step (inputs resident in HBM).
-The second half of the metric, quantize throughput, is measured on the prefill
-workload (32 layers x 8192 tokens x 8 KV heads, K 3-bit, V 2-bit): one call per
-layer, the 32 calls replayed from a HIP graph (and, reported beside it, launched
-back to back from the host).
+The headline is the largest single-GPU workload, the ragged batched verify
+decode: 64 sequences of 4K-64K tokens, 32 query / 8 KV heads, d = 128, 4 query
+tokens per sequence, K 4-bit / V 4-bit, 256-token pages in random physical
+order (about 2.4 GB of compressed cache per step).  `value` = algorithmic bytes
+of a step / time of a step, with the cache resident in HBM.
 
-python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload llama8b]
+The same line carries sub-records, each with its own roofline and CPU baseline:
+  llama8b   Llama-3-8B-shaped decode, 1 x 32768 tokens, 32 / 8 heads, K4 / V3
+  longctx   4 x 131072 tokens, 40 / 4 heads, K3 / V2, sparse V at tau = 1e-4
+  tiny      1 x 1024 tokens, 1 / 1 head, K4 / V3 (latency-bound, reported only)
+  quantize  prefill: 32 layers x 8192 tokens x 8 KV heads, K3 / V2 (tq_quantize_kv)
+
+Caches smaller than 1.5 x the 256 MB last-level cache are replicated and step i
+works on replica i mod R, so every step streams its cache from HBM.  The
+dominant kernel of each workload is timed by HIP events recorded around its own
+launch on its own stream (tq_decode_attention_ex / tq_append_decode_attention
+events), steps by a HIP graph replay.  A device copy of the same bytes gives the
+practical streaming ceiling beside the 8 TB/s peak.
+
+CPU baseline: the float64 oracle (oracle/), unchanged, on the host cores: one
+process, then one process per core over independent units (a (sequence, KV
+head) decode step, or a (layer, side) quantize); see cpu_baseline().
+
+python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload all|ragged|llama8b|...]
 """
 
 from __future__ import annotations
@@ -41,6 +54,9 @@ HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
 KERNEL_SOURCES = ["tq_decode.hip", "tq_decode_mfma.hip", "tq_decode_common.h", "tq_device.h", "tq_quant.hip",
                   "tq_internal.h", "tq_api.cpp"]
+DECODE_DTYPE = "fp16 hi/lo-split operands (fp32-level), fp32 accumulate"
+DECODE_WORKLOADS = ["llama8b", "llama8b_k16", "llama8b_d256", "llama8b_d512", "llama8b_vout", "longctx", "ragged",
+                    "tiny"]
 
 
 def log(*a):
@@ -60,7 +76,9 @@ def source_hash():
 
 
 def pmc_traffic(kernel_key):
-    """HBM bytes per launch from a committed PMC record of the same kernel sources, else None."""
+    """HBM bytes per launch from the committed rocprofv3 PMC record
+    (profiles/pmc_traffic.json: FETCH_SIZE and WRITE_SIZE scaled by the copy
+    calibration) of exactly these kernel sources, else None."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(path):
         return None
@@ -70,6 +88,20 @@ def pmc_traffic(kernel_key):
     if not r or r.get("source_hash") != source_hash():
         return None
     return r.get("bytes_per_launch")
+
+
+def host_info():
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": cpu_model, "nproc": os.cpu_count(), "usable_cpus": usable}
 
 
 class HipEvents:
@@ -108,6 +140,13 @@ def decode_workload(name):
             "llama8b_d512": lambda: W.llama8b_wide(512), "llama8b_vout": W.llama8b_vout}[name]()
 
 
+def describe(wl):
+    return (f"{wl.name}: {wl.n_seqs} seq x {int(wl.seq_lens.max())} tokens (total {wl.total_tokens}), "
+            f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d={wl.head_dim}, K{wl.k_bits}/V{wl.v_bits}"
+            f"{f' ({wl.v_kept} V channels kept in float16)' if wl.v_kept else ''}, "
+            f"{wl.n_qtok} query token(s), tau={wl.tau}, page {wl.block_size}")
+
+
 def gen_kv_device(wl, b, torch, gen):
     """K/V of sequence b: the workload's own seeded numpy recipe, except the ragged
     workload (2.2 M tokens), whose N(0,1) K/V come from a seeded device generator."""
@@ -120,8 +159,39 @@ def gen_kv_device(wl, b, torch, gen):
     return torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
 
 
-def run_decode(args, torch):
-    wl = decode_workload(args.workload)
+def copy_ceiling(torch, nbytes):
+    """Practical streaming rate for nbytes: a device-to-device copy of that many bytes
+    (read + write) and a read-only sum over them, each timed by events over copies
+    totalling > 1.5 x the last-level cache.  Returns GB/s of the bytes each moves."""
+    n = max(1, nbytes // 4)
+    reps = max(1, math.ceil(1.5 * LLC_BYTES / (4 * n)))
+    srcs = [torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(reps)]
+    dsts = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(reps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rounds = max(3, 20 // reps)
+    res = {}
+    for name, fn, moved in (("copy", lambda i: dsts[i].copy_(srcs[i]), 8 * n),
+                            ("read_sum", lambda i: torch.sum(srcs[i]), 4 * n)):
+        for i in range(reps):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(rounds):
+            for i in range(reps):
+                fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / (rounds * reps) * 1e-3
+        res[name] = round(moved / t / 1e9, 1)
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_decode(args, torch, name):
+    """One decode workload: fill the caches (GPU quantize), time the fused append +
+    decode step (events on the pass kernel, graph replay for the step)."""
+    wl = decode_workload(name)
     kb, vb, hd, hb = wl.k_bits, wl.v_bits, wl.head_dim, wl.blocks_per_head
     kept_b = 2 * wl.v_kept   # kept V channels: float16 each
     per_tok = hb * (cache_bytes_per_token_head(kb) + cache_bytes_per_token_head(vb)) + kept_b   # one token-head
@@ -173,23 +243,30 @@ def run_decode(args, torch):
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
 
     # the append fused into the pass (tq_append_decode_attention) where it is supported
-    fused = not args.separate_append and kb != 16 and wl.head_dim == 128 and not wl.v_kept and \
-        os.environ.get("TQ_DECODE_KERNEL", "mfma") != "valu"
+    fused = not args.separate_append and kb != 16 and wl.head_dim == 128 and not wl.v_kept
 
-    def step(i, events=None):
+    def step(i, events=None, options=None):
         r = i % reps
         if fused:
             T.tq_append_decode_attention(kc, k_new, vc, v_new, q, lens, tables[r], 0.0, wl.tau, out=out,
-                                         workspace=ws, events=events)
+                                         workspace=ws, events=events, options=options)
         else:
             T.tq_quantize_kv(kc, k_new, vc, v_new, new_slots[r])
-            T.tq_decode_attention(kc, vc, q, lens, tables[r], 0.0, wl.tau, out=out, workspace=ws, events=events)
+            T.tq_decode_attention(kc, vc, q, lens, tables[r], 0.0, wl.tau, out=out, workspace=ws, events=events,
+                                  options=options)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # sparse V: the V rows the gated pass reads, counted on the device (one step)
+    v_rows = None
+    if wl.tau > 0:
+        cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        step(0, options=T.DecodeOptions(v_rows_read=cnt))
+        torch.cuda.synchronize()
+        v_rows = int(cnt.item())
     # eager steps; the library launches the dominant kernel with start / stop events
-    # (hipExtLaunchKernelGGL), which time that kernel's execution
+    # (hipExtLaunchKernelGGL), which time that kernel's execution on its own stream
     evs = HipEvents(args.steps)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -225,12 +302,12 @@ def run_decode(args, torch):
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / (n_replay * reps)
+    del graph
 
     # algorithmic bytes
     if wl.tau > 0:
-        kept = 64 * wl.n_seqs * wl.n_kv_heads          # planted positions kept per (seq, KV head)
-        cache_step = hb * (wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb) +
-                           kept * cache_bytes_per_token_head(vb)) + kept * kept_b
+        cache_step = hb * wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb) + \
+            v_rows * (cache_bytes_per_token_head(vb) + (kept_b if wl.v_kept else 0))
         pass_bytes = hb * wl.total_tokens * wl.n_kv_heads * cache_bytes_per_token_head(kb)
     else:
         cache_step = cache_bytes
@@ -241,31 +318,39 @@ def run_decode(args, torch):
     step_bytes = cache_step + qo + meta + append
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
+    del kc, vc, ws, tables
+    torch.cuda.empty_cache()
+    ceiling = copy_ceiling(torch, pass_bytes)
     log(f"[bench] {ms_step * 1e3:.1f} us/step (graph), {ms_step_eager * 1e3:.1f} us/step (eager), "
-        f"pass kernel {pass_ms * 1e3:.1f} us, "
-        f"step {value:.0f} GB/s, pass {achieved:.0f} GB/s")
-    mfma = os.environ.get("TQ_DECODE_KERNEL", "mfma") != "valu"
-    kernel = "tq_decode_mfma_kernel" if mfma else "tq_decode_pass_kernel"
-    kernel_key = f"{kernel}:{wl.name}"
+        f"pass kernel {pass_ms * 1e3:.1f} us, step {value:.0f} GB/s, pass {achieved:.0f} GB/s, "
+        f"streaming ceiling {ceiling}")
+    kernel = "tq_decode_mfma_kernel"
+    best = max(ceiling.values())
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(kernel_key),
-            "kernel": kernel + (" (scoring pass)" if wl.tau > 0 else ""), "bytes_per_launch": pass_bytes,
-            "avg_launch_us": round(pass_ms * 1e3, 2),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(f"{kernel}:{wl.name}"),
+            "traffic_source": "committed rocprofv3 PMC record of these kernel sources (profiles/pmc_traffic.json); "
+                              "null when the sources changed since",
+            "kernel": kernel + (" (scoring pass: every K code; V in the gated pass)" if wl.tau > 0 else ""),
+            "bytes_per_launch": pass_bytes, "avg_launch_us": round(pass_ms * 1e3, 2),
             "median_launch_us": round(float(np.median(pass_times)) * 1e3, 2),
             "p10_launch_us": round(float(np.percentile(pass_times, 10)) * 1e3, 2),
-            "p90_launch_us": round(float(np.percentile(pass_times, 90)) * 1e3, 2)}
-    cfg = {"workload": f"{wl.name}: {wl.n_seqs} seq x {int(wl.seq_lens.max())} tokens, "
-                       f"{wl.n_q_heads} q / {wl.n_kv_heads} KV heads, d={hd}, K{kb}/V{vb}"
-                       f"{f' ({wl.v_kept} V channels kept in float16)' if wl.v_kept else ''}, "
-                       f"{wl.n_qtok} query token(s), tau={wl.tau}, page {wl.block_size}",
-           "global_batch": wl.n_seqs, "seq_len": int(wl.seq_lens.max()), "replicas": reps,
-           "launch": "HIP graph replay", "ms_per_step_eager": round(ms_step_eager, 5),
+            "p90_launch_us": round(float(np.percentile(pass_times, 90)) * 1e3, 2),
+            "streaming_ceiling_gbs": ceiling, "frac_of_ceiling": round(achieved / best, 4)}
+    rec = {"workload": describe(wl), "value": round(value, 2), "unit": "GB/s", "ms_per_step": round(ms_step, 5),
+           "ms_per_step_eager": round(ms_step_eager, 5), "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+           "step_bytes": step_bytes, "replicas": reps, "launch": "HIP graph replay",
            "append": ("fused into the pass (tq_append_decode_attention)" if fused
                       else "tq_quantize_kv, then tq_decode_attention"),
-           "decode_kernel": ("matrix-core pass (fp16 MFMA, hi/lo-split fp32 operands, fp32 accumulate)"
-                             if mfma else "vector-ALU pass (fp32)"),
-           "parallelism": "single GPU"}
-    return wl, value, ms_step, roof, cfg, step_bytes
+           "decode_kernel": "matrix-core pass (fp16 MFMA, hi/lo-split fp32 operands, fp32 accumulate)",
+           "dtype": DECODE_DTYPE,
+           # per step: the query tokens answered and the KV token-heads scanned
+           "query_tokens_per_s": round(wl.n_seqs * wl.n_qtok / (ms_step * 1e-3), 1),
+           "kv_token_heads_per_s": round(wl.total_tokens * wl.n_kv_heads / (ms_step * 1e-3), 1),
+           "roofline": roof}
+    if v_rows is not None:
+        rec["sparse_v"] = {"v_rows_read": v_rows, "per_seq_kv_head": round(v_rows / (wl.n_seqs * wl.n_kv_heads), 1),
+                           "counted_by": "the gated pass (tq_decode_options.v_rows_read)"}
+    return wl, rec
 
 
 def run_quantize(args, torch):
@@ -307,7 +392,7 @@ def run_quantize(args, torch):
     t1.record()
     torch.cuda.synchronize()
     pass_ms_eager = t0.elapsed_time(t1) / reps
-    # the kernel alone: events around every call (one more pass)
+    # the kernel alone: events around every call on the launch stream (one more pass)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(wl.n_layers)]
     one_pass(evs)
@@ -333,18 +418,26 @@ def run_quantize(args, torch):
     # so its time / 32 is the kernel's own time per call
     launch_ms = pass_ms / wl.n_layers
     achieved = bytes_per_call / (launch_ms * 1e-3) / 1e9
+    del srcs, caches, graph
+    torch.cuda.empty_cache()
+    ceiling = copy_ceiling(torch, bytes_per_call)
     log(f"[bench] quantize: {pass_ms * 1e3:.1f} us / 32 layers (graph), {pass_ms_eager * 1e3:.1f} us (eager), "
-        f"{kern_ms * 1e3:.2f} us/kernel, {mtok:.0f} M token-layers/s, {achieved:.0f} GB/s")
+        f"{kern_ms * 1e3:.2f} us/kernel by events, {mtok:.0f} M token-layers/s, {achieved:.0f} GB/s")
     return {"workload": "prefill: 32 layers x 8192 tokens x 8 KV heads, d=128, K3/V2 (Laplace, 1% x30)",
             "value": round(mtok, 1), "unit": "M token-layers/s", "launch": "HIP graph replay of the 32 calls",
+            "dtype": "f32 (codes u8)",
             "ms_per_32_layers": round(pass_ms, 4), "ms_per_32_layers_eager": round(pass_ms_eager, 4),
             "value_eager": round(n * wl.n_layers / (pass_ms_eager * 1e-3) / 1e6, 1),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": pmc_traffic("tq_quantize_kernel:prefill"),
+                         "traffic_source": "committed rocprofv3 PMC record of these kernel sources "
+                                           "(profiles/pmc_traffic.json); null when the sources changed since",
                          "kernel": "tq_quantize_kernel", "bytes_per_launch": bytes_per_call,
                          "vectors_per_launch": vec_per_call, "avg_launch_us": round(launch_ms * 1e3, 2),
-                         "avg_launch_us_events": round(kern_ms * 1e3, 2)}}
+                         "avg_launch_us_events": round(kern_ms * 1e3, 2),
+                         "streaming_ceiling_gbs": ceiling,
+                         "frac_of_ceiling": round(achieved / max(ceiling.values()), 4)}}
 
 
 def run_codebook_fit(torch):
@@ -382,60 +475,150 @@ def run_codebook_fit(torch):
     return res
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The oracle (unchanged) on a bounded sample of the same decode step: for the KV
-    heads of sequence 0 in turn (cycling), quantize-append the new token and decode its
-    query rows over the whole context, until budget_s seconds are spent.  GB/s of
-    algorithmic bytes processed."""
-    import oracle as O
+# ------------------------------------------------------------------ CPU baseline
+#
+# The oracle, unchanged, on independent units of the same workloads.  A decode
+# unit is one step of one (sequence, KV head): quantize-append of its n_qtok new
+# K and V rows (oracle cache_write) and the oracle's attention of its G * n_qtok
+# query rows over the whole context (decode_attention).  The context's codes and
+# norms are seeded random bytes written before the clock starts (the oracle's
+# work does not depend on the code values, and quantizing millions of context
+# rows first would only add untimed set-up).  A quantize unit is one (layer, side)
+# of the prefill: oracle cache_write of 8192 tokens x 8 KV heads.
+# Each unit runs with one BLAS thread.  Single process: units one after another
+# for a bounded time.  All cores: one process per usable core (at most 16), the
+# units dealt round-robin; the time is the slowest process's own timed total.
+
+def _one_thread():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
     except Exception:
-        cores = 1
-    b = 0
+        return None
+
+
+def _cpu_decode_unit(job):
+    """(seconds, algorithmic bytes) of one oracle decode step of one (sequence, KV head)."""
+    import oracle as O
+    name, b, kv = job
+    wl = decode_workload(name)
     length = int(wl.seq_lens[b])
-    k, v = wl.kv_source(b)
-    slots = wl.slots(b)
-    q = wl.queries()
-    hb = wl.blocks_per_head
-    per_tok = hb * (cache_bytes_per_token_head(wl.k_bits) + cache_bytes_per_token_head(wl.v_bits)) + 2 * wl.v_kept
-    lens1, table1 = wl.seq_lens[:1], wl.block_table[:1]
-    kept = O.select_outlier_channels(wl.warmup_v(), wl.v_kept) if wl.v_kept else None
-    prepared = []
-    for kv in range(wl.n_kv_heads):   # the context before the new tokens (not timed)
-        kcache = O.new_cache(wl.k_bits, 1, wl.block_size, wl.n_blocks, wl.signs_k[kv * hb:(kv + 1) * hb],
-                             None if wl.k_bits == 16 else O.build_codebook(wl.k_bits), head_dim=wl.head_dim)
-        vcache = O.new_cache(wl.v_bits, 1, wl.block_size, wl.n_blocks, wl.signs_v[kv * hb:(kv + 1) * hb],
-                             O.build_codebook(wl.v_bits), head_dim=wl.head_dim,
-                             outlier_channels=None if kept is None else kept[kv:kv + 1])
-        O.cache_write(kcache, k[:-wl.n_qtok, kv:kv + 1], slots[:-wl.n_qtok])
-        O.cache_write(vcache, v[:-wl.n_qtok, kv:kv + 1], slots[:-wl.n_qtok])
-        prepared.append((kcache, vcache, q[:1, :, kv * wl.group:(kv + 1) * wl.group]))
-    done_bytes, spent, units = 0, 0.0, 0
-    while spent < budget_s:
-        kv = units % wl.n_kv_heads
-        kcache, vcache, qh = prepared[kv]
-        t0 = time.perf_counter()
-        O.cache_write(kcache, k[-wl.n_qtok:, kv:kv + 1], slots[-wl.n_qtok:])
-        O.cache_write(vcache, v[-wl.n_qtok:, kv:kv + 1], slots[-wl.n_qtok:])
-        O.decode_attention(qh, kcache, vcache, lens1, table1, wl.n_qtok, 0.0, wl.tau)
-        spent += time.perf_counter() - t0
-        units += 1
-        done_bytes += length * per_tok + wl.n_qtok * (2 * 2 * wl.head_dim + per_tok) + qh.size * 6
-    gbs = done_bytes / spent / 1e9
-    log(f"[bench] cpu oracle: {units} (KV head, step) units of seq 0 in {spent:.1f} s -> {gbs:.4f} GB/s, "
-        f"{cores} threads")
-    cpu_model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
-    return {"value": round(gbs, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{wl.name}: sequence 0, {units} single-KV-head steps (append + decode of "
-                      f"{wl.group * wl.n_qtok} query rows over {length} tokens each), {spent:.1f} s",
-            "host": {"cpu_model": cpu_model, "nproc": os.cpu_count()}}
+    bs, hb, g, n_qtok = wl.block_size, wl.blocks_per_head, wl.group, wl.n_qtok
+    n_pages = -(-length // bs)
+    rng = np.random.default_rng([7, b, kv])
+    caches = []
+    for bits, signs in ((wl.k_bits, wl.signs_k), (wl.v_bits, wl.signs_v)):
+        c = O.new_cache(bits, 1, bs, n_pages, signs[kv * hb:(kv + 1) * hb],
+                        None if bits == 16 else O.build_codebook(bits), head_dim=wl.head_dim)
+        c.codes[...] = rng.integers(0, 256, size=c.codes.shape, dtype=np.uint8)
+        if bits == 16:   # float16 rows: finite values
+            c.codes.view(np.float16)[...] = rng.standard_normal(c.codes.view(np.float16).shape).astype(np.float16)
+        c.norms[...] = rng.uniform(5.0, 15.0, size=c.norms.shape).astype(np.float32)
+        caches.append(c)
+    new = rng.standard_normal((2, n_qtok, 1, wl.head_dim)).astype(np.float16)
+    q = wl.queries()[b:b + 1, :, kv * g:(kv + 1) * g]
+    table = np.arange(n_pages, dtype=np.int32)[None, :]
+    lens = np.array([length], np.int32)
+    new_slots = np.arange(length - n_qtok, length, dtype=np.int64)
+    with_limits = _one_thread()
+    t0 = time.perf_counter()
+    O.cache_write(caches[0], new[0], new_slots)
+    O.cache_write(caches[1], new[1], new_slots)
+    O.decode_attention(q, caches[0], caches[1], lens, table, n_qtok, 0.0, wl.tau)
+    dt = time.perf_counter() - t0
+    del with_limits
+    per_tok = hb * (cache_bytes_per_token_head(wl.k_bits) + cache_bytes_per_token_head(wl.v_bits))
+    nbytes = length * per_tok + n_qtok * (2 * 2 * wl.head_dim + per_tok) + q.size * 6
+    return dt, nbytes
+
+
+def _cpu_quant_unit(job):
+    """(seconds, token-layers) of the oracle quantize of one (layer, side) of the prefill."""
+    import oracle as O
+    _, layer, side = job
+    wl = W.prefill()
+    x = wl.kv_source(layer)[side]
+    bits = wl.k_bits if side == 0 else wl.v_bits
+    c = O.new_cache(bits, wl.n_kv_heads, wl.block_size, wl.n_blocks, wl.signs(layer)[side], O.build_codebook(bits))
+    slots = np.arange(wl.n_tokens, dtype=np.int64)
+    with_limits = _one_thread()
+    t0 = time.perf_counter()
+    O.cache_write(c, x, slots)
+    dt = time.perf_counter() - t0
+    del with_limits
+    return dt, 0.5 * wl.n_tokens   # a token-layer is K and V of all heads: half of it per side
+
+
+def _cpu_worker(jobs):
+    out = []
+    for kind, job in jobs:
+        out.append(_cpu_quant_unit(job) if kind == "q" else _cpu_decode_unit(job))
+    return out
+
+
+def cpu_units(name):
+    """Every independent unit of a workload, in a seeded order, and a description."""
+    if name == "quantize":
+        wl = W.prefill()
+        units = [("q", ("prefill", layer, side)) for layer in range(wl.n_layers) for side in (0, 1)]
+        return units, "prefill: (layer, side) units"
+    wl = decode_workload(name)
+    units = [("d", (name, b, kv)) for b in range(wl.n_seqs) for kv in range(wl.n_kv_heads)
+             if int(wl.seq_lens[b]) > 0]
+    order = np.random.default_rng(11).permutation(len(units))
+    return [units[i] for i in order], f"{name}: (sequence, KV head) decode steps"
+
+
+def cpu_baseline(name, budget_s=6.0, max_units=None, procs=None):
+    """The oracle on the host: a single process for about budget_s seconds, then one
+    process per core over max_units units (all of them by default)."""
+    import multiprocessing as mp
+    units, what = cpu_units(name)
+    info = host_info()
+    # single process, bounded (the units in order, cycling for a small workload)
+    done, spent, amount = 0, 0.0, 0.0
+    while done == 0 or spent < budget_s:
+        dt, x = _cpu_worker([units[done % len(units)]])[0]
+        spent += dt
+        amount += x
+        done += 1
+        if done >= len(units) and spent >= 0.5 * budget_s:
+            break
+    single = amount / spent
+    # all cores: the sample (repeated when it is too small to keep every process
+    # busy for about a second)
+    p = procs or min(16, info["usable_cpus"])
+    sample = units if max_units is None else units[:max_units]
+    rep = max(1, min(64, math.ceil(p * 1.0 / (spent / done * len(sample)))))
+    work = sample * rep
+    p = min(p, len(work))
+    jobs = [work[i::p] for i in range(p)]
+    t_wall = time.perf_counter()
+    with mp.get_context("spawn").Pool(p) as pool:
+        res = pool.map(_cpu_worker, jobs)
+    t_wall = time.perf_counter() - t_wall
+    makespan = max(sum(dt for dt, _ in r) for r in res)
+    total = sum(x for r in res for _, x in r)
+    multi = total / makespan
+    scale, unit = (1e6, "M token-layers/s") if name == "quantize" else (1e9, "GB/s")
+    full = len(sample) == len(units)
+    log(f"[bench] cpu oracle {name}: 1 process {done} units in {spent:.1f} s -> {single / scale:.4f} {unit}; "
+        f"{p} processes {len(work)} units, slowest {makespan:.1f} s (wall {t_wall:.1f} s) -> "
+        f"{multi / scale:.4f} {unit}")
+    return {"value": round(multi / scale, 5), "unit": unit, "cores": p, "kind": "oracle",
+            "sample": f"{what}: {len(sample)} of {len(units)} units"
+                      f"{' (the whole workload)' if full else ' (seeded subset; the rate needs no scaling)'}"
+                      f"{f', each run {rep} times' if rep > 1 else ''}, "
+                      f"{p} processes x 1 thread, units dealt round-robin, time = the slowest process's timed "
+                      f"total {makespan:.1f} s; context codes are seeded random bytes (the oracle's work does not "
+                      f"depend on them)",
+            "single_process": {"value": round(single / scale, 5), "unit": unit, "cores": 1,
+                               "sample": f"{done} units, {spent:.1f} s"},
+            "host": info}
+
+
+# per workload: units of the all-core run (None = all)
+CPU_SAMPLE = {"ragged": 64, "longctx": None, "llama8b": None, "tiny": None, "quantize": None}
 
 
 def main():
@@ -443,9 +626,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b",
-                    choices=["llama8b", "llama8b_k16", "llama8b_d256", "llama8b_d512", "llama8b_vout", "longctx",
-                             "ragged", "tiny"])
+    ap.add_argument("--workload", default="all", choices=["all"] + DECODE_WORKLOADS,
+                    help="all: the ragged headline with the llama8b, longctx, tiny and quantize sub-records")
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--separate-append", action="store_true",
                     help="append with tq_quantize_kv and decode with tq_decode_attention (two calls)")
@@ -474,28 +656,42 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 256 << 20, "copies": 5}), flush=True)
         return
-
     if args.quantize_only:
         print(json.dumps({"quantize": run_quantize(args, torch), "codebook_fit": run_codebook_fit(torch)}),
               flush=True)
         return
-    wl, value, ms_step, roof, cfg, step_bytes = run_decode(args, torch)
-    quant = None if args.no_quantize else run_quantize(args, torch)
-    fitted = None if args.no_quantize else run_codebook_fit(torch)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
-    rec = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic", "config": cfg, "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "step_bytes": step_bytes,
-        # per step: the query tokens answered and the KV token-heads scanned (each
-        # sequence's KV heads over its whole context), each per second
-        "query_tokens_per_s": round(wl.n_seqs * wl.n_qtok / (ms_step * 1e-3), 1),
-        "kv_token_heads_per_s": round(wl.total_tokens * wl.n_kv_heads / (ms_step * 1e-3), 1),
-        "roofline": roof, "cpu_baseline": cpu, "quantize": quant, "codebook_fit": fitted,
+
+    head = "ragged" if args.workload == "all" else args.workload
+    subs = ["llama8b", "longctx", "tiny"] if args.workload == "all" else []
+    wl, rec = run_decode(args, torch, head)
+    sub = {}
+    for name in subs:
+        sub[name] = run_decode(args, torch, name)[1]
+    if not args.no_quantize:
+        sub["quantize"] = run_quantize(args, torch)
+        sub["codebook_fit"] = run_codebook_fit(torch)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(head, max_units=CPU_SAMPLE.get(head, 64))
+        for name in subs + ([] if args.no_quantize else ["quantize"]):
+            sub[name]["cpu_baseline"] = cpu_baseline(name, max_units=CPU_SAMPLE.get(name))
+    else:
+        rec["cpu_baseline"] = None
+    out = {
+        "metric": METRIC, "value": rec["value"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rec["dtype"],
+        "data": "synthetic",
+        "config": {"workload": rec["workload"], "global_batch": wl.n_seqs, "seq_len": int(wl.seq_lens.max()),
+                   "replicas": rec["replicas"], "launch": rec["launch"], "ms_per_step_eager": rec["ms_per_step_eager"],
+                   "append": rec["append"], "decode_kernel": rec["decode_kernel"], "parallelism": "single GPU"},
+        "pct_of_peak": rec["pct_of_peak"], "step_bytes": rec["step_bytes"],
+        "query_tokens_per_s": rec["query_tokens_per_s"], "kv_token_heads_per_s": rec["kv_token_heads_per_s"],
+        "roofline": rec["roofline"], "cpu_baseline": rec["cpu_baseline"],
     }
-    print(json.dumps(rec), flush=True)
+    if "sparse_v" in rec:
+        out["sparse_v"] = rec["sparse_v"]
+    out["sub_records"] = sub
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
