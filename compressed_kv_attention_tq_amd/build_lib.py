@@ -24,6 +24,7 @@ LIB = os.path.join(PKG, "libtq.so")
 # K bit width (and blocks per head) so the slow units compile in parallel.
 SOURCES = [
     ("tq_api.cpp", "tq_api", []),
+    ("tq_noalloc.hip", "tq_noalloc", []),
     ("tq_quant.hip", "tq_quant", []),
     ("tq_decode.hip", "tq_decode", []),
     ("tq_decode.hip", "tq_decode_kb2", ["-DTQ_DECODE_KB=2"]),

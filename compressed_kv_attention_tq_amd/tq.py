@@ -29,7 +29,8 @@ MAX_OUTLIERS = 16   # kept channels per head (TQ_MAX_OUTLIERS)
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
 EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_fit_codebook", "tq_select_outlier_channels",
            "tq_quantize_kv", "tq_decode_attention", "tq_decode_attention_ex", "tq_append_decode_attention",
-           "tq_dequantize")
+           "tq_decode_attention_noalloc", "tq_dequantize")
+NOALLOC_SCRATCH_BYTES = 32 << 20   # TQ_NOALLOC_SCRATCH_BYTES
 DECODE_KERNEL_DEFAULT, DECODE_KERNEL_MFMA, DECODE_KERNEL_VALU = 0, 1, 2   # tq_decode_kernel
 
 
@@ -149,6 +150,8 @@ def load_library(path: str = LIB_PATH):
     lib.tq_append_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.POINTER(TQCache),
                                                ctypes.c_void_p, ctypes.c_int64] + \
         lib.tq_decode_attention.argtypes[2:] + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.tq_decode_attention_noalloc.restype = ctypes.c_int
+    lib.tq_decode_attention_noalloc.argtypes = lib.tq_decode_attention.argtypes[:12] + [ctypes.c_void_p]
     lib.tq_dequantize.restype = ctypes.c_int
     lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_int32, ctypes.c_void_p]
@@ -393,6 +396,25 @@ def tq_append_decode_attention(k_cache: Cache, k_new, v_cache: Cache, v_new, q, 
         max_blocks, float(softmax_scale), float(sparse_v_tau), _dev_ptr(out, "out", torch.float32),
         _dev_ptr(workspace, "workspace"), ctypes.byref(size), _stream_ptr(stream), _opts(options), ev)
     _check(st, "tq_append_decode_attention")
+    return out
+
+
+def tq_decode_attention_noalloc(k_cache: Cache, v_cache: Cache, q, seq_lens, block_table, softmax_scale=0.0,
+                                sparse_v_tau=0.0, out=None, stream=None):
+    """tq_decode_attention with the library's fixed scratch array in place of a
+    workspace (the C call allocates nothing; `out` is allocated here if not given)."""
+    torch = _torch()
+    n_seqs, n_qtok, n_q_heads, hd = q.shape
+    if hd != k_cache.head_dim:
+        raise ValueError(f"q has head_dim {hd}, the cache {k_cache.head_dim}")
+    if out is None:
+        out = torch.empty((n_seqs, n_qtok, n_q_heads, hd), dtype=torch.float32, device=q.device)
+    st = load_library().tq_decode_attention_noalloc(
+        ctypes.byref(k_cache.desc()), ctypes.byref(v_cache.desc()), _dev_ptr(q, "q", torch.float16),
+        n_seqs, n_qtok, n_q_heads, _dev_ptr(seq_lens, "seq_lens", torch.int32),
+        _dev_ptr(block_table, "block_table", torch.int32), block_table.shape[1], float(softmax_scale),
+        float(sparse_v_tau), _dev_ptr(out, "out", torch.float32), _stream_ptr(stream))
+    _check(st, "tq_decode_attention_noalloc")
     return out
 
 

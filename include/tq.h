@@ -302,6 +302,28 @@ tq_status tq_append_decode_attention(const tq_cache *k, const void *k_new, const
                                      float *out, void *workspace, size_t *workspace_bytes, void *stream,
                                      const tq_decode_options *opts, void *const *events);
 
+/* Decode attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * result of tq_decode_attention with the same arguments and no workspace argument.
+ * The chunk partials go to a fixed device array inside the library of
+ * TQ_NOALLOC_SCRATCH_BYTES (32 MiB), one copy per GPU, held until the process
+ * ends; its address on the current device is looked up on the first call on that
+ * device.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * routine).  Every call on a GPU shares that GPU's array: calls that overlap on
+ * one GPU (on different streams, or from several threads) race; calls ordered on
+ * one stream do not.  Nothing in the array needs to start at zero (each call
+ * writes every partial it reads).
+ * Errors: as tq_decode_attention; TQ_ERR_WORKSPACE (nothing launched) when the
+ *         call would need more than TQ_NOALLOC_SCRATCH_BYTES of partials (the size
+ *         a tq_decode_attention workspace query returns); TQ_ERR_HIP when the
+ *         array's address cannot be found. */
+#define TQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+tq_status tq_decode_attention_noalloc(const tq_cache *k, const tq_cache *v, const void *q,
+                                      int32_t n_seqs, int32_t n_qtok, int32_t n_q_heads,
+                                      const int32_t *seq_lens, const int32_t *block_table,
+                                      int32_t max_blocks_per_seq, float softmax_scale,
+                                      float sparse_v_tau, float *out, void *stream);
+
 /* Dequantize cache rows: dst[t][h][:] = x_hat of slot slots[t], head h
  * ([llama-tq]: K needs no dequantization inside attention; this is the explicit
  * inverse for everything else).

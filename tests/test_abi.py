@@ -373,3 +373,18 @@ def test_append_decode_validation():
     assert call(options=VALU)[0] == T.TQ_ERR_UNSUPPORTED
     assert call(options=T.DecodeOptions(chunk=1024))[0] == T.TQ_OK
 
+
+def test_decode_noalloc_host_checks():
+    """tq_decode_attention_noalloc validates like tq_decode_attention and refuses,
+    before touching a device, a call whose partials exceed its fixed array."""
+    lib = T.load_library()
+    k, v = fake_cache(), fake_cache(bits=3)
+    call = lambda n_seqs=1, max_blocks=4, n_q_heads=2, kk=k: lib.tq_decode_attention_noalloc(
+        ctypes.byref(kk), ctypes.byref(v), FAKE, n_seqs, 1, n_q_heads, FAKE, FAKE, max_blocks, 0.0, 0.0, FAKE, None)
+    assert call(n_q_heads=3) == T.TQ_ERR_INVALID_ARG
+    assert call(kk=fake_cache(head_dim=64)) == T.TQ_ERR_UNSUPPORTED
+    assert call(n_seqs=0) == T.TQ_OK                                      # nothing to do
+    n_seqs, max_blocks = 256, 4096
+    _, need = decode_call(n_seqs=n_seqs, max_blocks=max_blocks)
+    assert need > T.NOALLOC_SCRATCH_BYTES
+    assert call(n_seqs=n_seqs, max_blocks=max_blocks) == T.TQ_ERR_WORKSPACE
