@@ -160,18 +160,20 @@ def gen_kv_device(wl, b, torch, gen):
 
 
 def copy_ceiling(torch, nbytes):
-    """Practical streaming rate for nbytes: a device-to-device copy of that many bytes
-    (read + write) and a read-only sum over them, each timed by events over copies
-    totalling > 1.5 x the last-level cache.  Returns GB/s of the bytes each moves."""
-    n = max(1, nbytes // 4)
+    """Practical streaming rates for nbytes, one launch per buffer: the library's
+    plain streaming read (tq_stream_read) and a device-to-device copy (read + write),
+    each timed by events over buffers totalling > 1.5 x the last-level cache.
+    Returns GB/s of the bytes each moves."""
+    n = max(4, (nbytes // 16) * 4)
     reps = max(1, math.ceil(1.5 * LLC_BYTES / (4 * n)))
     srcs = [torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(reps)]
     dsts = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(reps)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     rounds = max(3, 20 // reps)
     res = {}
-    for name, fn, moved in (("copy", lambda i: dsts[i].copy_(srcs[i]), 8 * n),
-                            ("read_sum", lambda i: torch.sum(srcs[i]), 4 * n)):
+    for name, fn, moved in (("read", lambda i: T.tq_stream_read(srcs[i], sink), 4 * n),
+                            ("copy", lambda i: dsts[i].copy_(srcs[i]), 8 * n)):
         for i in range(reps):
             fn(i)
         torch.cuda.synchronize()
@@ -183,7 +185,7 @@ def copy_ceiling(torch, nbytes):
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / (rounds * reps) * 1e-3
         res[name] = round(moved / t / 1e9, 1)
-    del srcs, dsts
+    del srcs, dsts, sink
     torch.cuda.empty_cache()
     return res
 
@@ -325,7 +327,7 @@ def run_decode(args, torch, name):
         f"pass kernel {pass_ms * 1e3:.1f} us, step {value:.0f} GB/s, pass {achieved:.0f} GB/s, "
         f"streaming ceiling {ceiling}")
     kernel = "tq_decode_mfma_kernel"
-    best = max(ceiling.values())
+    best = ceiling["read"]
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(f"{kernel}:{wl.name}"),
             "traffic_source": "committed rocprofv3 PMC record of these kernel sources (profiles/pmc_traffic.json); "
@@ -335,7 +337,7 @@ def run_decode(args, torch, name):
             "median_launch_us": round(float(np.median(pass_times)) * 1e3, 2),
             "p10_launch_us": round(float(np.percentile(pass_times, 10)) * 1e3, 2),
             "p90_launch_us": round(float(np.percentile(pass_times, 90)) * 1e3, 2),
-            "streaming_ceiling_gbs": ceiling, "frac_of_ceiling": round(achieved / best, 4)}
+            "streaming_ceiling_gbs": ceiling, "frac_of_read_ceiling": round(achieved / best, 4)}
     rec = {"workload": describe(wl), "value": round(value, 2), "unit": "GB/s", "ms_per_step": round(ms_step, 5),
            "ms_per_step_eager": round(ms_step_eager, 5), "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
            "step_bytes": step_bytes, "replicas": reps, "launch": "HIP graph replay",
@@ -437,7 +439,7 @@ def run_quantize(args, torch):
                          "vectors_per_launch": vec_per_call, "avg_launch_us": round(launch_ms * 1e3, 2),
                          "avg_launch_us_events": round(kern_ms * 1e3, 2),
                          "streaming_ceiling_gbs": ceiling,
-                         "frac_of_ceiling": round(achieved / max(ceiling.values()), 4)}}
+                         "frac_of_read_ceiling": round(achieved / ceiling["read"], 4)}}
 
 
 def run_codebook_fit(torch):

@@ -25,6 +25,7 @@ LIB = os.path.join(PKG, "libtq.so")
 SOURCES = [
     ("tq_api.cpp", "tq_api", []),
     ("tq_noalloc.hip", "tq_noalloc", []),
+    ("tq_stream.hip", "tq_stream", []),
     ("tq_quant.hip", "tq_quant", []),
     ("tq_decode.hip", "tq_decode", []),
     ("tq_decode.hip", "tq_decode_kb2", ["-DTQ_DECODE_KB=2"]),

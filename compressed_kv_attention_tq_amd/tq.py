@@ -29,7 +29,7 @@ MAX_OUTLIERS = 16   # kept channels per head (TQ_MAX_OUTLIERS)
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
 EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_fit_codebook", "tq_select_outlier_channels",
            "tq_quantize_kv", "tq_decode_attention", "tq_decode_attention_ex", "tq_append_decode_attention",
-           "tq_decode_attention_noalloc", "tq_dequantize")
+           "tq_decode_attention_noalloc", "tq_dequantize", "tq_stream_read")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # TQ_NOALLOC_SCRATCH_BYTES
 DECODE_KERNEL_DEFAULT, DECODE_KERNEL_MFMA, DECODE_KERNEL_VALU = 0, 1, 2   # tq_decode_kernel
 
@@ -123,6 +123,11 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"libtq.so not built at {path}; run __graft_entry__.build()")
+    # torch first: its wheel carries its own HIP runtime (soname libamdhip64.so.7),
+    # which libtq's dependency then resolves to.  Loaded the other way round, the
+    # process would hold two HIP runtimes and torch's streams and memory would be
+    # foreign to the library's launches.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     lib.tq_status_string.restype = ctypes.c_char_p
     lib.tq_status_string.argtypes = [ctypes.c_int]
@@ -152,6 +157,8 @@ def load_library(path: str = LIB_PATH):
         lib.tq_decode_attention.argtypes[2:] + [ctypes.c_void_p, ctypes.c_void_p]
     lib.tq_decode_attention_noalloc.restype = ctypes.c_int
     lib.tq_decode_attention_noalloc.argtypes = lib.tq_decode_attention.argtypes[:12] + [ctypes.c_void_p]
+    lib.tq_stream_read.restype = ctypes.c_int
+    lib.tq_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     lib.tq_dequantize.restype = ctypes.c_int
     lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_int32, ctypes.c_void_p]
@@ -429,3 +436,12 @@ def tq_dequantize(cache: Cache, slots, fp16=False, out=None, stream=None):
                                       _dev_ptr(out, "out"), 1 if fp16 else 0, _stream_ptr(stream))
     _check(st, "tq_dequantize")
     return out
+
+
+def tq_stream_read(src, sink, stream=None):
+    """Read every byte of the contiguous device tensor src once (the streaming
+    ceiling kernel); sink: a device int32 tensor of one element."""
+    torch = _torch()
+    _check(load_library().tq_stream_read(_dev_ptr(src, "src"), src.numel() * src.element_size(),
+                                         _dev_ptr(sink, "sink", torch.int32), _stream_ptr(stream)),
+           "tq_stream_read")

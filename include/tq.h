@@ -254,9 +254,11 @@ typedef struct tq_decode_options {
                                  of 256 (matrix-core pass) or 512 (vector-ALU pass), at most
                                  1 << 20 (TQ_ERR_INVALID_ARG otherwise) */
     uint64_t *v_rows_read;    /* NULL, or a device counter: with sparse_v_tau > 0 the gated pass
-                                 adds the number of V code rows it read (one per token and
-                                 128-element block of a KV head whose weight some query row
-                                 keeps); the caller zeroes it.  Not touched when tau = 0. */
+                                 adds the number of V code rows the sparse rule needs: one per
+                                 token and 128-element block of a KV head whose weight some
+                                 query row keeps (the pass may read more: with 128-wide heads
+                                 it reads the whole 64-token slice of a kept token).  The
+                                 caller zeroes it.  Not touched when tau = 0. */
 } tq_decode_options;
 
 /* tq_decode_attention with options, and with start / stop events on the dominant
@@ -323,6 +325,14 @@ tq_status tq_decode_attention_noalloc(const tq_cache *k, const tq_cache *v, cons
                                       const int32_t *seq_lens, const int32_t *block_table,
                                       int32_t max_blocks_per_seq, float softmax_scale,
                                       float sparse_v_tau, float *out, void *stream);
+
+/* A plain streaming read of n_bytes (a multiple of 16) at src (device, 16-byte
+ * aligned): 16-byte nontemporal loads, grid-stride, the words xor-folded; *sink
+ * (device uint32) is written only if the fold equals a fixed value, which keeps
+ * the loads alive.  Not part of the method: it measures the practical HBM read
+ * ceiling that the decode and quantize kernels are compared with.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_HIP. */
+tq_status tq_stream_read(const void *src, size_t n_bytes, uint32_t *sink, void *stream);
 
 /* Dequantize cache rows: dst[t][h][:] = x_hat of slot slots[t], head h
  * ([llama-tq]: K needs no dequantization inside attention; this is the explicit

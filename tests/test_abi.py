@@ -388,3 +388,20 @@ def test_decode_noalloc_host_checks():
     _, need = decode_call(n_seqs=n_seqs, max_blocks=max_blocks)
     assert need > T.NOALLOC_SCRATCH_BYTES
     assert call(n_seqs=n_seqs, max_blocks=max_blocks) == T.TQ_ERR_WORKSPACE
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library before anything imports torch still leaves one HIP
+    runtime in the process (torch's), so torch's streams and memory are the
+    library's own."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from compressed_kv_attention_tq_amd import tq as T\n"
+            "T.load_library()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1", out.stdout
