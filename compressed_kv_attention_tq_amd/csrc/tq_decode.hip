@@ -224,7 +224,7 @@ void tq_decode_pass_kernel(DecodeArgs a,
     const int bk = (int)fdiv(blockIdx.x, a.chunk_div_n);
     const int c = blockIdx.x - bk * a.n_chunks;
     const int b = (int)fdiv((uint32_t)bk, a.kv_div), kv = bk - b * a.n_kv;
-    const int len = seq_lens[b];
+    const int len = min(seq_lens[b], a.max_blocks * a.block_size);   // (clamped to the table's capacity)
     const int start = c * a.chunk;
     if (start >= len) return;
     const int end = min(start + a.chunk, len);
@@ -270,8 +270,8 @@ void tq_decode_pass_kernel(DecodeArgs a,
     int blk_next = 0;
     if constexpr (MODE != MODE_GATED) {
         cur.load(k_codes, k_norms, v_codes, v_norms, bsdiv, bs, a.n_kv, kv, first + lane, end,
-                 page_of(btab, bsdiv, first + lane, end));
-        blk_next = page_of(btab, bsdiv, first + kStride + lane, end);
+                 page_of(btab, bsdiv, first + lane, end, a.max_blocks - 1, a.max_page));
+        blk_next = page_of(btab, bsdiv, first + kStride + lane, end, a.max_blocks - 1, a.max_page);
     }
     warm_q<RP>(launder_sgpr(qr));
     __syncthreads();                                   // ktab / vtab
@@ -289,7 +289,7 @@ void tq_decode_pass_kernel(DecodeArgs a,
                 if (r < a.rows) cand |= (exp2_diff(tm[r], gM[r]) * gInvL[r] >= a.tau);
             if (!cand) continue;
             cur.load(k_codes, k_norms, v_codes, v_norms, bsdiv, bs, a.n_kv, kv, t, end,
-                     page_of(btab, bsdiv, t, end));
+                     page_of(btab, bsdiv, t, end, a.max_blocks - 1, a.max_page));
             score_rows<KB, RP>(cur.k, cur.kn, cur.active, t, last_vis, a.grp_div, qr, ktab, s);
             bool kept = false;
 #pragma unroll
@@ -332,7 +332,7 @@ void tq_decode_pass_kernel(DecodeArgs a,
             }
             if (base + kStride < end) {
                 cur.load(k_codes, k_norms, v_codes, v_norms, bsdiv, bs, a.n_kv, kv, t + kStride, end, blk_next);
-                blk_next = page_of(btab, bsdiv, t + 2 * kStride, end);
+                blk_next = page_of(btab, bsdiv, t + 2 * kStride, end, a.max_blocks - 1, a.max_page);
             }
             // ---------------- online softmax over the wave's slice
             float e[RP];

@@ -99,8 +99,11 @@ __device__ __forceinline__ float in_vgpr(float x) {
 // One token's cache rows, loaded by the lane that scores it.  The physical page
 // of a token is looked up one slice before its rows are loaded (page_of), so the
 // block-table load never stalls the row loads.
-__device__ __forceinline__ int page_of(const int32_t *__restrict__ btab, const FastDiv &bsdiv, int t, int end) {
-    return t < end ? btab[fdiv((uint32_t)t, bsdiv)] : 0;
+// (the table index is clamped to the table and the page to the pool, so a bad
+// entry or length reads another page, never outside the cache)
+__device__ __forceinline__ int page_of(const int32_t *__restrict__ btab, const FastDiv &bsdiv, int t, int end,
+                                       int last_entry, int max_page) {
+    return t < end ? min(max(btab[min((int)fdiv((uint32_t)t, bsdiv), last_entry)], 0), max_page) : 0;
 }
 
 template <int KB, int VB, bool WITH_V>

@@ -150,8 +150,14 @@ __device__ __forceinline__ uint32_t tab_off(uint32_t u, int sh, uint32_t lane_of
         // v_perm_b32 bytes: 0 <- byte 0 of lane_off, 1 <- byte sh/8 of u, 2, 3 <- 0
         return __builtin_amdgcn_perm(u, lane_off, 0x0C0C0000u | ((4u + (uint32_t)(sh >> 3)) << 8));
     } else {
+        // the field moved to bit RS by one shift, then masked and merged with the copy
+        // offset in one v_and_or_b32 (left to itself the compiler spends a shift, an
+        // and and an add)
         constexpr int RS = RB == 256 ? 8 : 7;
-        return (((u >> sh) & ((1u << FB) - 1u)) << RS) | lane_off;
+        const uint32_t moved = sh >= RS ? (u >> (sh - RS)) : (u << (RS - sh));
+        uint32_t r;
+        asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(moved), "s"(((1u << FB) - 1u) << RS), "v"(lane_off));
+        return r;
     }
 }
 
@@ -237,10 +243,10 @@ __device__ __forceinline__ u4_t v_frag(const uint32_t (&x)[4], const uint32_t (&
 // CONTIG: block_size is a multiple of 64, so a slice lies in one page.
 // --------------------------------------------------------------------------
 // Waves per SIMD the register allocation aims for (without spilling): the dense
-// pass holds two slices' loads and fits two; the scoring and gated passes with
-// at most 8 rows fit three.
+// pass holds two slices' loads and fits two; so does the gated pass, which keeps
+// two candidate slices in flight; the scoring pass with at most 8 rows fits three.
 template <bool PK, int VB, int MODE>
-constexpr int mfma_waves_per_eu() { return (PK && MODE != MODE_DENSE) ? 3 : 2; }
+constexpr int mfma_waves_per_eu() { return (PK && MODE == MODE_SCORE) ? 3 : 2; }
 
 // Barrier of the block's waves that orders their LDS accesses only: the global
 // loads in flight are not waited for.
@@ -408,9 +414,11 @@ void tq_decode_mfma_kernel(
     Slot sa, sb, sc;   // (sc: with three slots in the ring)
     int myrow = 0;   // row of token base + lane (general page layout)
 
+    // (page ids are clamped to the pool: a bad table entry reads another page, never
+    // outside the cache)
     auto row0_of = [&](int base, int page) __attribute__((always_inline)) -> int64_t {
         const int pg = (int)fdiv((uint32_t)base, bsdiv);
-        return ((int64_t)page * n_sub + kvs) * bs + (base - pg * bs);
+        return ((int64_t)min(max(page, 0), a.max_page) * n_sub + kvs) * bs + (base - pg * bs);
     };
     // general layout: the row of every token of the slice into the wave's table
     auto fill_rows = [&](int base, int blk_lane) __attribute__((always_inline)) {
@@ -418,7 +426,7 @@ void tq_decode_mfma_kernel(
         myrow = 0;
         if (t < end) {
             const int pg = (int)fdiv((uint32_t)t, bsdiv);
-            myrow = (blk_lane * n_sub + kvs) * bs + (t - pg * bs);
+            myrow = (min(max(blk_lane, 0), a.max_page) * n_sub + kvs) * bs + (t - pg * bs);
         }
         rowtab[CONTIG ? 0 : wave][lane] = myrow;
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's row table is written
@@ -523,7 +531,8 @@ void tq_decode_mfma_kernel(
     };
     auto all_tokens = [](int, int) { return true; };
 
-    len = __builtin_amdgcn_readfirstlane(len_v);
+    // (a length past the page table's capacity is clamped to it)
+    len = min(__builtin_amdgcn_readfirstlane(len_v), a.max_blocks * bs);
     if (start >= len) {
         // the small loads are consumed on this path too, so they stay ahead of
         // the length test instead of being moved below it
@@ -613,7 +622,7 @@ void tq_decode_mfma_kernel(
         if constexpr (CONTIG) {
             const int blk0 = __builtin_amdgcn_readfirstlane(vb0);
             const int pg = (int)fdiv((uint32_t)first, bsdiv);
-            r0_prev = ((int64_t)min(max(blk0, 0), a.max_page) * n_sub + kvs) * bs + (first - pg * bs);
+            r0_prev = ((int64_t)min(max(blk0, 0), a.max_page) * n_sub + kvs) * bs + (first - pg * bs);   // (row0_of)
             app_first();
             load_k(sa, r0_prev);   // (its V units go out after the set-up, below)
             blk_next = vb1;
@@ -672,10 +681,51 @@ void tq_decode_mfma_kernel(
     }
     // sparse: global (max, sum) of each row from the scoring pass's chunk partials
     // (part_ml is [chunk][row][block][2]; the blocks' entries are equal, block 0's is read)
+    // Gated pass: the first round's candidate inputs (each step's tile maxima and, on
+    // contiguous pages, its page-table entry; lane i = step i of the wave) go out
+    // before the statistics below, so the two round trips overlap.
+    f4_t tmx0[4] = {};
+    int cpage0 = 0;
+    if constexpr (GATED) {
+        const int bic = min(first + lane * kStride, end - 1);
+        const f4_t *tp = reinterpret_cast<const f4_t *>(tilemax + (tile0 + (bic >> 6)) * rp);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            if (4 * r4 < rp) tmx0[r4] = tp[r4];
+        if constexpr (CONTIG) {
+            int pi = min((int)fdiv((uint32_t)bic, bsdiv), last_entry);
+            asm volatile("" : "+v"(pi));
+            cpage0 = btab[pi];
+        }
+    }
+    // With at most 64 chunks (one per lane) every row's pairs are loaded at once, so
+    // the statistics cost one round trip; the sums are the same either way.
     if constexpr (GATED) {
         const int nc = min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), a.n_chunks);
         const float *ml = part_ml + (int64_t)unit * a.n_chunks * rp * NB * 2;
-        for (int r = wave; r < R; r += kMW) {
+        constexpr int kRW = 16 / kMW;   // rows a wave reduces
+        if (nc <= 64) {
+            typedef float f2v __attribute__((ext_vector_type(2)));
+            f2v v[kRW];
+            const int cc = min(lane, max(nc - 1, 0));
+#pragma unroll
+            for (int i = 0; i < kRW; ++i) {
+                const int rr = min(wave + kMW * i, R - 1);
+                v[i] = *reinterpret_cast<const f2v *>(&ml[(cc * rp + rr) * NB * 2]);
+            }
+#pragma unroll
+            for (int i = 0; i < kRW; ++i) {
+                const int r = wave + kMW * i;
+                if (r < R) {
+                    const float M = wave_max(lane < nc ? v[i].x : -INFINITY);
+                    const float L = wave_sum(lane < nc ? v[i].y * exp2_diff(v[i].x, M) : 0.f);
+                    if (lane == 0) {
+                        gstat[r][0] = M;
+                        gstat[r][1] = L;
+                    }
+                }
+            }
+        } else for (int r = wave; r < R; r += kMW) {
             float m = -INFINITY;
             for (int cc = lane; cc < nc; cc += 64) m = fmaxf(m, ml[(cc * rp + r) * NB * 2]);
             const float M = wave_max(m);
@@ -1203,50 +1253,45 @@ void tq_decode_mfma_kernel(
                 if (L > 0.f && M > -INFINITY) sthr_r[r] = (M + log2f(L)) + log2f(a.tau);
             }
         }
+        // (contiguous pages: the same round loads each step's page-table entry, so a
+        // candidate slice's codes go out without another round trip)
         const int lead = first - start;
         uint64_t cmask = 0;
-        int step = 0;
-        for (int b0 = NB == 1 ? first : start; b0 < end; b0 += kStride, ++step) {
-            const int base = NB == 1 ? b0 : b0 + lead;
-            if ((step & 63) == 0) {
-                const int bi = base + lane * kStride;
-                bool c = false;
-                if (bi < end) {
-                    const f4_t *tp = reinterpret_cast<const f4_t *>(tilemax + (tile0 + (bi >> 6)) * rp);
+        int cpage = 0;
+        // the candidate test of the 64 steps from `step` (lane i: step + i)
+        auto round_mask = [&](int step, int base) __attribute__((always_inline)) {
+            const int bi = base + lane * kStride;
+            f4_t t[4] = {tmx0[0], tmx0[1], tmx0[2], tmx0[3]};
+            if (step == 0) {
+                cpage = cpage0;
+            } else {
+                const int bic = min(bi, end - 1);
+                if constexpr (CONTIG) {
+                    int pi = min((int)fdiv((uint32_t)bic, bsdiv), last_entry);
+                    asm volatile("" : "+v"(pi));
+                    cpage = btab[pi];
+                }
+                const f4_t *tp = reinterpret_cast<const f4_t *>(tilemax + (tile0 + (bic >> 6)) * rp);
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        if (4 * r4 < rp) {
-                            const f4_t t = tp[r4];
+                for (int r4 = 0; r4 < 4; ++r4)
+                    if (4 * r4 < rp) t[r4] = tp[r4];
+            }
+            bool c = false;
+            if (bi < end) {
 #pragma unroll
-                            for (int k = 0; k < 4; ++k) c = c || (4 * r4 + k < R && t[k] >= sthr_r[4 * r4 + k]);
-                        }
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    if (4 * r4 < rp) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) c = c || (4 * r4 + k < R && t[r4][k] >= sthr_r[4 * r4 + k]);
                     }
                 }
-                cmask = __ballot(c);
             }
-            const bool cand = ((cmask >> (step & 63)) & 1ull) != 0ull;
-            if constexpr (NB == 1) {
-                if (!cand) continue;
-            }
-            int64_t r0 = 0;
-            float E_s = 0.f;
-            f4_t S[4] = {};
-            if (cand) {
-                if constexpr (CONTIG) r0 = row0_of(base, btab[fdiv((uint32_t)base, bsdiv)]);
-                else fill_rows(base, page_of(btab, bsdiv, base + lane, end));
-                load_k(sa, r0);
-                if constexpr (CONTIG) sa.vnl = v_norms[r0 + lane];
-                else sa.vnl = v_norms[myrow];
-                E_s = stage_norms(sa, base);
-                score_mfma(sa, S);
-            }
-            const bool full = base + 63 <= lim_all;
-            float s[4][4];
-            scores(S, base, full, s);
-            if constexpr (NB > 1) {
-                if (!cand) continue;
-            }
-            // tokens kept by at least one row
+            cmask = __ballot(c);
+        };
+        // the V accumulation of a scored candidate slice (scores s): tokens kept by at
+        // least one row; weights p = 2^(s - mlog) where kept, else 0
+        auto gated_values = [&](Slot &sl, const float (&s)[4][4], float E_s, int base, int64_t r0, bool v_loaded)
+            __attribute__((always_inline)) -> void {
             bool kept[4][4];
             uint64_t any = 0;
 #pragma unroll
@@ -1257,8 +1302,8 @@ void tq_decode_mfma_kernel(
                     any |= bal;
                     kept[tm][e] = ((bal >> (16 * g)) & 0xFFFFull) != 0ull;
                 }
-            if (!any) continue;
-            if (a.v_rows_read) {   // the V rows this slice reads (token groups g with a kept row)
+            if (!any) return;
+            if (a.v_rows_read) {   // the V rows the rule needs (token groups g with a kept row)
                 uint32_t cnt = 0;
 #pragma unroll
                 for (int tm = 0; tm < 4; ++tm)
@@ -1269,7 +1314,7 @@ void tq_decode_mfma_kernel(
                     }
                 v_rows += cnt;
             }
-            load_v(sa, r0, [&](int tm, int e) { return kept[tm][e]; });
+            if (!v_loaded) load_v(sl, r0, [&](int tm, int e) { return kept[tm][e]; });
             const float E_new = fmaxf(E_run, E_s);
             if (E_run != -INFINITY && E_new != E_run) {
                 const float f = __builtin_amdgcn_exp2f(E_run - E_new);
@@ -1290,8 +1335,92 @@ void tq_decode_mfma_kernel(
                     if constexpr (OV) wo[tm][e] = ex * eE;   // = p, the final weight
                 }
             }
-            value_mfma(sa, w);
-            kept_mfma(sa, wo, base);
+            value_mfma(sl, w);
+            kept_mfma(sl, wo, base);
+        };
+        if constexpr (NB == 1 && CONTIG && !KF && !OV) {
+            // (float16 K and kept V channels keep one slot: their slots are too large
+            // for two in the registers)
+            // One 64-step round at a time; its candidate slices two at a time: each
+            // candidate's K words, norms and every V unit go out together, and the
+            // next candidate's go out before the current one is computed (when there is
+            // none, the loads repeat a slice already read: the same instructions on
+            // every path, so each wait covers only the slot it needs).
+            auto pop = [](uint64_t &m) __attribute__((always_inline)) -> int {
+                if (!m) return -1;
+                const int k = __builtin_ctzll(m);
+                m &= m - 1;
+                return k;
+            };
+            for (int rs = 0; first + rs * kStride < end; rs += 64) {
+                const int rbase = first + rs * kStride;
+                round_mask(rs, rbase);
+                uint64_t m = cmask;
+                int kA = pop(m), kB = pop(m);
+                if (kA < 0) continue;   // (wave-uniform)
+                auto issue_c = [&](Slot &sl, int k) __attribute__((always_inline)) -> int64_t {
+                    const int64_t r0 = row0_of(rbase + k * kStride, __builtin_amdgcn_readlane(cpage, k));
+                    load_k(sl, r0);
+                    sl.vnl = v_norms[r0 + lane];
+                    load_v(sl, r0, all_tokens);
+                    return r0;
+                };
+                auto compute_c = [&](Slot &sl, int k, int64_t r0) __attribute__((always_inline)) {
+                    const int base = rbase + k * kStride;
+                    const float E_s = stage_norms(sl, base);
+                    f4_t S[4];
+                    score_mfma(sl, S);
+                    float s[4][4];
+                    scores(S, base, base + 63 <= lim_all, s);
+                    gated_values(sl, s, E_s, base, r0, true);
+                };
+                int64_t rA = issue_c(sa, kA);
+                __builtin_amdgcn_sched_barrier(0);
+                int64_t rB = issue_c(sb, kB >= 0 ? kB : kA);
+                for (;;) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_c(sa, kA, rA);
+                    const int nA = pop(m);
+                    rA = issue_c(sa, nA >= 0 ? nA : kA);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (kB < 0) break;
+                    compute_c(sb, kB, rB);
+                    const int nB = pop(m);
+                    rB = issue_c(sb, nB >= 0 ? nB : kB);
+                    kA = nA;
+                    kB = nB;
+                    if (kA < 0) break;
+                }
+            }
+        } else {
+            int step = 0;
+            for (int b0 = NB == 1 ? first : start; b0 < end; b0 += kStride, ++step) {
+                const int base = NB == 1 ? b0 : b0 + lead;
+                if ((step & 63) == 0) round_mask(step, base);
+                const bool cand = ((cmask >> (step & 63)) & 1ull) != 0ull;
+                if constexpr (NB == 1) {
+                    if (!cand) continue;
+                }
+                int64_t r0 = 0;
+                float E_s = 0.f;
+                f4_t S[4] = {};
+                if (cand) {
+                    if constexpr (CONTIG) r0 = row0_of(base, __builtin_amdgcn_readlane(cpage, step & 63));
+                    else fill_rows(base, page_of(btab, bsdiv, base + lane, end, a.max_blocks - 1, a.max_page));
+                    load_k(sa, r0);
+                    if constexpr (CONTIG) sa.vnl = v_norms[r0 + lane];
+                    else sa.vnl = v_norms[myrow];
+                    E_s = stage_norms(sa, base);
+                    score_mfma(sa, S);
+                }
+                const bool full = base + 63 <= lim_all;
+                float s[4][4];
+                scores(S, base, full, s);
+                if constexpr (NB > 1) {
+                    if (!cand) continue;
+                }
+                gated_values(sa, s, E_s, base, r0, false);
+            }
         }
     }
 
