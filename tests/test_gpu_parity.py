@@ -203,6 +203,50 @@ def test_float16_side_store_and_read(n_kv, n_tok):
 # --------------------------------------------------------------------------- dequantize
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_non_finite_vectors(bits):
+    """R14: vectors with a +inf, -inf or NaN element (and an all-inf one) store the
+    zero direction with the norm as computed; finite rows of the same call are
+    unaffected; dequantize agrees with the oracle NaN for NaN."""
+    torch = _t()
+    rng = np.random.default_rng(300 + bits)
+    n_tok, n_kv = 24, 2
+    x = rng.standard_normal((n_tok, n_kv, 128)).astype(np.float16)
+    x[0, 0, 5] = np.inf
+    x[3, 1, 127] = -np.inf
+    x[7, 0, 0] = np.nan
+    x[9, 1, :] = np.inf
+    x[12, 0, 64] = np.nan
+    x[12, 0, 65] = np.inf
+    signs = W.random_sign_words(rng, n_kv)
+    g = T.Cache.allocate(bits, n_kv, 16, 2, signs)
+    slots = np.arange(n_tok, dtype=np.int64)
+    T.tq_quantize_kv(g, torch.from_numpy(x).cuda(), None, None, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    codes = g.codes.cpu().numpy().transpose(0, 2, 1, 3).reshape(-1, n_kv, 16 * bits)[:n_tok]
+    norms = g.norms.cpu().numpy().transpose(0, 2, 1).reshape(-1, n_kv)[:n_tok]
+    cb = O.build_codebook(bits)
+    bad = ~np.all(np.isfinite(x.astype(np.float64)), axis=-1)
+    for h in range(n_kv):
+        on, oc, oy = O.quantize_vectors(x[:, h], O.sign_vector(signs[h]), cb)
+        got = O.unpack_codes(codes[:, h], bits)
+        b = bad[:, h]
+        assert np.array_equal(got[b], oc[b]) and np.all(oc[b] == (1 << (bits - 1)) - 1)
+        np.testing.assert_array_equal(norms[b, h], on[b])          # inf == inf, NaN == NaN
+        U.check_codes(codes[~b, h], norms[~b, h], x[~b, h], signs[h], bits)
+    # dequantize: the oracle's reconstruction of the same stored rows, NaN for NaN
+    out = T.tq_dequantize(g, torch.from_numpy(slots).cuda()).cpu().numpy()
+    oc_cache = O.new_cache(bits, n_kv, 16, 2, signs, cb)
+    O.cache_write(oc_cache, x, slots)
+    for h in range(n_kv):
+        want = O.cache_read(oc_cache, slots, h)
+        b = bad[:, h]
+        np.testing.assert_array_equal(np.isnan(out[b, h]), np.isnan(want[b]))
+        fin = ~np.isnan(want[b])
+        np.testing.assert_array_equal(out[b, h][fin], want[b][fin])   # the +-inf entries
+    log(f"quantize non-finite bits={bits}: {int(bad.sum())} rows stored as the zero direction")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_dequantize_matches_oracle(bits):
     torch = _t()
     wl = W.small_decode(seed=bits, n_seqs=2, lens=[300, 77], n_qtok=1, n_q_heads=3, n_kv_heads=3,
