@@ -240,8 +240,9 @@ def run_decode(args, torch, name):
         new_slots.append(torch.tensor(s, dtype=torch.int64, device="cuda"))
     lens = torch.from_numpy(wl.seq_lens).cuda()
     out = torch.empty((wl.n_seqs, wl.n_qtok, wl.n_q_heads, hd), dtype=torch.float32, device="cuda")
+    base_opts = T.DecodeOptions(chunk=args.chunk)
     ws_bytes = T.decode_workspace_bytes(kc, vc, wl.n_seqs, wl.n_qtok, wl.n_q_heads, wl.block_table.shape[1],
-                                        wl.tau)
+                                        wl.tau, options=base_opts)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
 
     # the append fused into the pass (tq_append_decode_attention) where it is supported
@@ -249,6 +250,7 @@ def run_decode(args, torch, name):
 
     def step(i, events=None, options=None):
         r = i % reps
+        options = options or base_opts
         if fused:
             T.tq_append_decode_attention(kc, k_new, vc, v_new, q, lens, tables[r], 0.0, wl.tau, out=out,
                                          workspace=ws, events=events, options=options)
@@ -264,7 +266,7 @@ def run_decode(args, torch, name):
     v_rows = None
     if wl.tau > 0:
         cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
-        step(0, options=T.DecodeOptions(v_rows_read=cnt))
+        step(0, options=T.DecodeOptions(chunk=args.chunk, v_rows_read=cnt))
         torch.cuda.synchronize()
         v_rows = int(cnt.item())
     # eager steps; the library launches the dominant kernel with start / stop events
@@ -634,6 +636,8 @@ def main():
     ap.add_argument("--separate-append", action="store_true",
                     help="append with tq_quantize_kv and decode with tq_decode_attention (two calls)")
     ap.add_argument("--quantize-reps", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="tokens per decode pass block (0: the library's choice)")
     ap.add_argument("--no-quantize", action="store_true")
     ap.add_argument("--quantize-only", action="store_true", help="only the prefill quantize measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -170,7 +170,8 @@ int quant_blocks(int64_t n_vec, int n_kv) {
 
 struct DecodePlan {
     int rows, rows_pad, chunk, n_chunks, n_tiles;
-    size_t off_qrot, off_ml, off_acc, off_tile, off_stats, total;
+    size_t off_qrot, off_ml, off_acc, off_tile, off_stats, off_ctrl, total;
+    bool list;   // the workspace holds a work list (persistent matrix-core passes)
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -201,6 +202,10 @@ DecodePlan plan_decode(int n_seqs, int n_kv, int nb, int acc_w, int rows, int ma
     p.off_acc = off;   off = align256(off + units * p.n_chunks * p.rows_pad * acc_w * sizeof(float));
     p.off_tile = off;  if (sparse) off = align256(off + units * p.n_tiles * p.rows_pad * sizeof(float));
     p.off_stats = off; if (sparse && !mfma) off = align256(off + units * p.rows_pad * 2 * sizeof(float));
+    // control words, units by chunk count, (chunk, unit) items
+    const int64_t items = (int64_t)units * p.n_chunks;
+    p.list = mfma && p.n_chunks <= kMaxListChunks && items <= kMaxListItems;
+    p.off_ctrl = off;  if (p.list) off = align256(off + (kCtrlWords + units + items) * sizeof(uint32_t));
     p.total = off;
     return p;
 }
@@ -548,6 +553,9 @@ tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32
     a.part_acc = reinterpret_cast<float *>(ws + p.off_acc);
     a.tilemax = sparse ? reinterpret_cast<float *>(ws + p.off_tile) : nullptr;
     a.stats = (sparse && !mfma) ? reinterpret_cast<float *>(ws + p.off_stats) : nullptr;
+    a.ctrl = p.list ? reinterpret_cast<uint32_t *>(ws + p.off_ctrl) : nullptr;
+    a.persist = 0;
+    a.pass_slot = 0;
     a.n_seqs = n_seqs;
     a.n_qtok = n_qtok;
     a.n_q_heads = n_q_heads;
@@ -566,7 +574,7 @@ tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32
     a.max_page = (int32_t)(std::min(k->n_blocks, v->n_blocks) - 1);
     a.bs_div = make_fastdiv((uint32_t)a.block_size);
     a.chunk_div = make_fastdiv((uint32_t)a.chunk);
-    a.chunk_div_n = make_fastdiv((uint32_t)a.n_chunks);
+    a.units_div = make_fastdiv((uint32_t)(n_seqs * k->n_kv_heads));
     a.kv_div = make_fastdiv((uint32_t)a.n_kv);
     a.grp_div = make_fastdiv((uint32_t)a.group);
     a.qh_div = make_fastdiv((uint32_t)a.n_q_heads);

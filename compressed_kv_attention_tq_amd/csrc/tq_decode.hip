@@ -17,6 +17,7 @@
 //            inverse-rotate once: o = s_V * H acc / sqrt(128)
 #include <float.h>
 
+#include <atomic>
 #include <utility>
 
 #include "tq_decode_common.h"
@@ -221,8 +222,9 @@ void tq_decode_pass_kernel(DecodeArgs a,
     __shared__ float accbuf[(MODE == MODE_SCORE) ? 1 : RP * kD];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bk = (int)fdiv(blockIdx.x, a.chunk_div_n);
-    const int c = blockIdx.x - bk * a.n_chunks;
+    // chunk-major block order (the same as the matrix-core pass)
+    const int c = (int)fdiv(blockIdx.x, a.units_div);
+    const int bk = blockIdx.x - c * a.n_seqs * a.n_kv;
     const int b = (int)fdiv((uint32_t)bk, a.kv_div), kv = bk - b * a.n_kv;
     const int len = min(seq_lens[b], a.max_blocks * a.block_size);   // (clamped to the table's capacity)
     const int start = c * a.chunk;
@@ -620,6 +622,106 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     o[lane + 64] = a1;
 }
 
+// --------------------------------------------------------------------------
+// Work list of the persistent matrix-core passes, one block: the non-empty
+// (chunk, unit) items in chunk-major order (every unit's chunk 0, then chunk 1,
+// ...), so the full chunks are taken first and the short last chunks of ragged
+// sequences last.  Units are counting-sorted by their chunk count n_c(u)
+// (decreasing): the units with more than c chunks are then a prefix of that order,
+// cnt[c] of them, and chunk c's items are list[off[c] .. off[c] + cnt[c]).
+// Also zeroes the passes' item counters.  (n_chunks <= kMaxListChunks.)
+// --------------------------------------------------------------------------
+// Exclusive prefix sum of v[0 .. n) in place by wave 0 (16 elements per lane at a
+// time); returns the total in every lane of wave 0.
+__device__ int wave0_exclusive_scan(int *v, int n) {
+    const int lane = threadIdx.x & 63;
+    int carry = 0;
+    for (int base = 0; base < n; base += 64 * 16) {
+        int loc[16], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int k = base + lane * 16 + i;
+            loc[i] = k < n ? v[k] : 0;
+            sum += loc[i];
+        }
+        int incl = sum;   // inclusive scan of the lane sums
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        int run = carry + incl - sum;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int k = base + lane * 16 + i;
+            if (k < n) v[k] = run;
+            run += loc[i];
+        }
+        carry += __shfl(incl, 63);
+    }
+    return carry;
+}
+
+__global__ __launch_bounds__(1024) void tq_worklist_kernel(DecodeArgs a) {
+    __shared__ int hist[kMaxListChunks + 2];   // units with n_c = k
+    __shared__ int cnt[kMaxListChunks + 2];    // units with n_c > c
+    __shared__ int off[kMaxListChunks + 2];    // first list entry of chunk c
+    __shared__ int fill[kMaxListChunks + 2];
+    const int tid = threadIdx.x, nch = a.n_chunks, n_units = a.n_seqs * a.n_kv;
+    int32_t *const sorted = reinterpret_cast<int32_t *>(a.ctrl + kCtrlWords);
+    int32_t *const list = sorted + n_units;
+    const int cap = a.max_blocks * a.block_size;
+    auto nc_of = [&](int u) {
+        const int b = (int)fdiv((uint32_t)u, a.kv_div);
+        const int len = min(max(a.seq_lens[b], 0), cap);
+        return min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), nch);
+    };
+    for (int i = tid; i <= nch + 1; i += 1024) {
+        hist[i] = 0;
+        fill[i] = 0;
+    }
+    __syncthreads();
+    for (int u = tid; u < n_units; u += 1024) atomicAdd(&hist[nc_of(u)], 1);
+    __syncthreads();
+    // cnt[c] = sum of hist[k] over k > c, as an exclusive scan of the reversed
+    // histogram; off = exclusive scan of cnt
+    for (int i = tid; i <= nch; i += 1024) cnt[i] = hist[nch - i];
+    __syncthreads();
+    if (tid < 64) wave0_exclusive_scan(cnt, nch + 1);   // cnt[i] = units with n_c > nch - i
+    __syncthreads();
+    for (int i = tid; i <= nch; i += 1024) off[i] = cnt[nch - i];   // units with n_c > i
+    __syncthreads();
+    for (int i = tid; i <= nch; i += 1024) cnt[i] = off[i];
+    __syncthreads();
+    int total = 0;
+    if (tid < 64) total = wave0_exclusive_scan(off, nch + 1);   // off[nch] = total items
+    __syncthreads();
+    // units in order of decreasing n_c: those with n_c = k take positions
+    // [cnt[k], cnt[k] + hist[k]) (the order inside a group does not matter)
+    for (int u = tid; u < n_units; u += 1024) {
+        const int k = nc_of(u);
+        if (k > 0) sorted[cnt[k] + atomicAdd(&fill[k], 1)] = u;
+    }
+    __threadfence_block();
+    __syncthreads();
+    const int n_items = off[nch];
+    for (int t = tid; t < n_items; t += 1024) {
+        int lo = 0, hi = nch - 1;   // the last c with off[c] <= t
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        list[t] = lo * n_units + sorted[t - off[lo]];
+    }
+    if (tid == 0) {
+        a.ctrl[0] = 0u;
+        a.ctrl[1] = 0u;
+        a.ctrl[2] = (uint32_t)n_items;
+    }
+    (void)total;
+}
+
 #endif  // !TQ_DECODE_KB
 
 // --------------------------------------------------------------------------
@@ -732,16 +834,37 @@ static void launch_merge(const DecodeArgs &a, dim3 grid, hipStream_t s) {
     else launch_merge_kb<SPARSE, 16>(a, grid, s);
 }
 
+// CUs of the current device (looked up once per device; 0 if unknown).
+static int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 hipError_t launch_decode(const DecodeArgs &a, const PairTables &pt, hipStream_t s, hipEvent_t ev_before,
                          hipEvent_t ev_after) {
     const dim3 rows_grid((unsigned)((int64_t)a.n_seqs * a.n_qtok * a.n_q_heads * a.nb));   // x head blocks
     if (a.mfma) {   // q rotation runs inside the pass kernels
+        // More (chunk, unit) items than two blocks per CU: build the work list of the
+        // persistent passes (each pass launch then decides from its own occupancy).
+        DecodeArgs b = a;
+        b.persist = 0;
+        const int64_t items = (int64_t)a.n_seqs * a.n_kv * a.n_chunks;
+        const int cus = device_cus();
+        if (a.ctrl && cus > 0 && items > 2 * (int64_t)cus) {
+            hipLaunchKernelGGL(tq_worklist_kernel, dim3(1), dim3(1024), 0, s, a);
+            b.persist = 1;
+        }
         if (a.tau > 0.f) {
-            launch_mfma_any(a, pt, MODE_SCORE, s, ev_before, ev_after);
-            launch_mfma_any(a, pt, MODE_GATED, s);
+            launch_mfma_any(b, pt, MODE_SCORE, s, ev_before, ev_after);
+            launch_mfma_any(b, pt, MODE_GATED, s);
             launch_merge<true>(a, rows_grid, s);
         } else {
-            launch_mfma_any(a, pt, MODE_DENSE, s, ev_before, ev_after);
+            launch_mfma_any(b, pt, MODE_DENSE, s, ev_before, ev_after);
             launch_merge<false>(a, rows_grid, s);
         }
         return hipGetLastError();

@@ -57,6 +57,10 @@
 // and whose B operand is the softmax weight without the V norm; the 16 sums per
 // row travel after the 128 rotated-domain sums and the merge writes them over
 // their channels.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "tq_decode_common.h"
 
 namespace tq {
@@ -256,13 +260,13 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// One (chunk, unit) item of a pass: item = c * n_seqs * n_kv + unit.
 template <int KB, int VB, bool PK, int MODE, bool CONTIG, int NB, bool OV>
-__global__ __launch_bounds__(kMBlock) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<PK, VB, MODE>(), 8)))
-void tq_decode_mfma_kernel(
-    DecodeArgs a, PairTables pt, const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
-    const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms, const uint16_t *__restrict__ qin,
-    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens, float *__restrict__ part_ml,
-    float *__restrict__ part_acc, float *__restrict__ tilemax) {
+__device__ __forceinline__ void decode_item(
+    const int item, const int tid, const DecodeArgs &a, const PairTables &pt, const uint8_t *__restrict__ k_codes,
+    const float *__restrict__ k_norms, const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms,
+    const uint16_t *__restrict__ qin, const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
+    float *__restrict__ part_ml, float *__restrict__ part_acc, float *__restrict__ tilemax) {
     constexpr bool DENSE = MODE == MODE_DENSE, SCORE = MODE == MODE_SCORE, GATED = MODE == MODE_GATED;
     constexpr bool WV = !SCORE;
     // KF: the K side is plain float16 (KB = 16): its rows are the score MFMA's A
@@ -316,11 +320,12 @@ void tq_decode_mfma_kernel(
     float *const apn = reinterpret_cast<float *>(apbuf + (kApp ? 16 * (KROW + VROW) : 0));
     float *const abnd = apn + 32;   // [wave][K 16, V 16]
 
-    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+    __builtin_assume(tid >= 0 && tid < kMBlock);
+    const int lane = tid & 63, g = lane >> 4, n = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int blk = wave % NB, grp = wave / NB;   // head block and group of this wave
-    const int unit = (int)fdiv(blockIdx.x, a.chunk_div_n);
-    const int c = blockIdx.x - unit * a.n_chunks;
+    const int c = (int)fdiv((uint32_t)item, a.units_div);
+    const int unit = item - c * a.n_seqs * a.n_kv;
     const int b = (int)fdiv((uint32_t)unit, a.kv_div);
     const int kv = unit - b * a.n_kv;
     const int R = a.rows, rp = a.rows_pad;
@@ -1514,39 +1519,132 @@ void tq_decode_mfma_kernel(
     }
 }
 
+// The pass kernel.  Items are numbered chunk-major (c * units + unit).  The
+// hardware deals consecutive blocks to the XCDs in turn, so with one item per block
+// every XCD gets an equal share of each chunk index (with ragged lengths the later
+// chunks of a sequence are short or empty; a unit-major order would leave the XCDs
+// that receive the first chunks with most of the work), and the full chunks start
+// first.  With more items than the GPU holds blocks at once the launch is
+// persistent: each block takes items from the work list (non-empty items only,
+// chunk-major) through an atomic counter until the list is exhausted, so no block
+// slot waits on the dispatcher and the short last chunks fill the end.
+// PER: the persistent form (one-block-per-item launches use the form without the
+// loop, whose registers stay those of one item).
+template <int KB, int VB, bool PK, int MODE, bool CONTIG, int NB, bool OV, bool PER>
+__global__ __launch_bounds__(kMBlock) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<PK, VB, MODE>(), 8)))
+void tq_decode_mfma_kernel(
+    DecodeArgs a, PairTables pt, const uint8_t *__restrict__ k_codes, const float *__restrict__ k_norms,
+    const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms, const uint16_t *__restrict__ qin,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens, float *__restrict__ part_ml,
+    float *__restrict__ part_acc, float *__restrict__ tilemax) {
+    if constexpr (!PER) {
+        decode_item<KB, VB, PK, MODE, CONTIG, NB, OV>((int)blockIdx.x, (int)threadIdx.x, a, pt, k_codes, k_norms,
+                                                     v_codes, v_norms, qin, block_table, seq_lens, part_ml, part_acc,
+                                                     tilemax);
+    } else {
+        __shared__ int qitem[2];   // the item the block takes next (two rounds alternate)
+        for (int it = 0;; ++it) {
+            // (the barrier also ends the previous item's use of the LDS)
+            if (threadIdx.x == 0) {
+                const uint32_t t = atomicAdd(a.ctrl + a.pass_slot, 1u);
+                qitem[it & 1] = t < a.ctrl[2] ? (int)a.ctrl[kCtrlWords + a.n_seqs * a.n_kv + t] : -1;
+            }
+            __syncthreads();
+            const int item = __builtin_amdgcn_readfirstlane(qitem[it & 1]);   // (block-uniform)
+            if (item < 0) break;
+            // The thread index passes through an empty asm each round, so nothing
+            // derived from it is hoisted out of the loop and held in registers across
+            // items (the pass is at its register limit).
+            int tid = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            decode_item<KB, VB, PK, MODE, CONTIG, NB, OV>(item, tid, a, pt, k_codes, k_norms, v_codes, v_norms, qin,
+                                                         block_table, seq_lens, part_ml, part_acc, tilemax);
+        }
+    }
+}
+
 // --------------------------------------------------------------------------
 // Dispatch, one translation unit per K bit width and blocks per head
 // (TQ_DECODE_KB = 2, 3, 4, 16; TQ_DECODE_NB = 1, 2, 4).
 // --------------------------------------------------------------------------
 // ev0 / ev1 (may be null): recorded at the start and the end of the kernel's
 // execution (hipExtLaunchKernelGGL), for timing.
+// Blocks of `kern` the current device holds at once (its CUs x the blocks one CU
+// holds), looked up once per kernel and device; 0 if the runtime cannot say.
+static int resident_blocks(const void *kern) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, kern);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kMBlock, 0) != hipSuccess)
+        return 0;
+    return cache[key] = cus * per_cu;
+}
+
+// a.persist on entry: the work list is built for this call; the launch is then
+// persistent if the items outnumber the blocks the GPU holds at once (one-block
+// heads without kept V channels, K compressed: the shapes long and batched decode
+// takes).
 template <int KB, int VB, bool PK, bool CONTIG, int NB>
 static void launch_mfma_mode(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
                              hipEvent_t ev1) {
-    const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_kv * a.n_chunks)), block(kMBlock);
-#define TQ_MFMA_ARGS a, pt, a.k_codes, a.k_norms, a.v_codes, a.v_norms, a.q, a.block_table, a.seq_lens, a.part_ml, \
-        a.part_acc, a.tilemax
+    const int64_t items = (int64_t)a.n_seqs * a.n_kv * a.n_chunks;
+    DecodeArgs b = a;
+    b.pass_slot = mode == MODE_GATED ? 1 : 0;
+    b.persist = 0;
+    auto launch = [&](auto kern, int64_t grid) {
+        hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMBlock), 0, s, ev0, ev1, 0, b, pt, b.k_codes,
+                              b.k_norms, b.v_codes, b.v_norms, b.q, b.block_table, b.seq_lens, b.part_ml, b.part_acc,
+                              b.tilemax);
+    };
+    // one block per item, or (a persistent form given) as many as the GPU holds
+    auto go = [&](auto kern, auto kern_persistent) {
+        if constexpr (!std::is_same_v<decltype(kern_persistent), std::nullptr_t>) {
+            if (a.persist) {
+                const int cap = resident_blocks(reinterpret_cast<const void *>(kern_persistent));
+                if (cap > 0 && items > cap) {
+                    b.persist = 1;
+                    launch(kern_persistent, cap);
+                    return;
+                }
+            }
+        }
+        launch(kern, items);
+    };
+    constexpr bool kPer = NB == 1 && KB != 16;
     // (kept V channels: 128-wide heads only, checked on the host)
     const bool ov = NB == 1 && a.n_out > 0;
     if (mode == MODE_DENSE) {
-        if (ov)
-            hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG, NB, NB == 1>), grid, block, 0,
-                                  s, ev0, ev1, 0, TQ_MFMA_ARGS);
-        else
-            hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG, NB, false>), grid, block, 0, s,
-                                  ev0, ev1, 0, TQ_MFMA_ARGS);
+        if (ov) {
+            go(tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG, NB, NB == 1, false>, nullptr);
+        } else if constexpr (kPer) {
+            go(tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG, NB, false, false>,
+               tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG, NB, false, true>);
+        } else {
+            go(tq_decode_mfma_kernel<KB, VB, PK, MODE_DENSE, CONTIG, NB, false, false>, nullptr);
+        }
     } else if (mode == MODE_SCORE) {
-        hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG, NB, false>), grid, block, 0, s, ev0,
-                              ev1, 0, TQ_MFMA_ARGS);
-    } else {
-        if (ov)
-            hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB, NB == 1>), grid, block, 0,
-                                  s, ev0, ev1, 0, TQ_MFMA_ARGS);
+        if constexpr (kPer)
+            go(tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG, NB, false, false>,
+               tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG, NB, false, true>);
         else
-            hipExtLaunchKernelGGL((tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB, false>), grid, block, 0, s,
-                                  ev0, ev1, 0, TQ_MFMA_ARGS);
+            go(tq_decode_mfma_kernel<KB, 2, PK, MODE_SCORE, CONTIG, NB, false, false>, nullptr);
+    } else {
+        if (ov) {
+            go(tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB, NB == 1, false>, nullptr);
+        } else if constexpr (kPer) {
+            go(tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB, false, false>,
+               tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB, false, true>);
+        } else {
+            go(tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB, false, false>, nullptr);
+        }
     }
-#undef TQ_MFMA_ARGS
 }
 
 template <int KB, int VB, int NB>

@@ -47,6 +47,9 @@ constexpr int kChunkUnit = kBlock; // decode: chunks are multiples of this many 
 constexpr int kMW = 4;             // decode, matrix-core path: waves per block
 constexpr int kMBlock = 64 * kMW;  //   threads per block; chunks are multiples of kMBlock tokens
 constexpr int kLutMax = 256;       // quantize: max entries of the encode lookup table
+constexpr int kMaxListChunks = 1024;   // decode: chunks per sequence a work list covers
+constexpr int64_t kMaxListItems = 4 << 20;   //   and (chunk, unit) items
+constexpr int kCtrlWords = 64;     // decode: control words before the sorted units
 
 // One side of a quantize launch.
 struct QuantSide {
@@ -125,8 +128,8 @@ struct DecodeArgs {
     int32_t n_chunks;         // chunks per sequence capacity
     int32_t n_tiles;          // tiles per sequence capacity
     float qscale;             // softmax_scale * log2(e) / sqrt(128)
-    FastDiv bs_div, chunk_div, chunk_div_n, kv_div, grp_div, qh_div, qt_div;
-                              // by block_size, chunk, n_chunks, n_kv, group, n_q_heads, n_qtok
+    FastDiv bs_div, chunk_div, units_div, kv_div, grp_div, qh_div, qt_div;
+                              // by block_size, chunk, n_seqs * n_kv, n_kv, group, n_q_heads, n_qtok
     float tau;
     int32_t k_bits, v_bits;
     int32_t nb, nb_log2;      // 128-element blocks per head (1, 2, 4; matrix-core path only)
@@ -147,6 +150,14 @@ struct DecodeArgs {
     unsigned long long *v_rows_read;   // null, or a device counter: the gated pass adds the V
                                        // code rows it reads (one atomic per wave that read any)
     int32_t contig;           // matrix-core path: every 64-token slice lies in one page
+    // Persistent matrix-core passes: a control block and work list in the workspace
+    // (null: no list).  ctrl[0], ctrl[1]: item counters of the first pass (dense or
+    // scoring) and the gated pass; ctrl[2]: items in the list; from word kCtrlWords:
+    // the units sorted by decreasing chunk count, then the list of (chunk, unit)
+    // items, c * n_seqs * n_kv + unit, chunk-major.
+    uint32_t *ctrl;
+    int32_t persist;          // per launch: 1 = blocks take items from the list
+    int32_t pass_slot;        // per launch: the ctrl counter this pass takes items from
     float kc[TQ_MAX_LEVELS];
     float vc[TQ_MAX_LEVELS];
 };

@@ -443,6 +443,34 @@ def test_decode_many_chunks(tau, monkeypatch):
     decode_and_compare(wl)
 
 
+def _persistent_workload(seed, tau, n_qtok, n_q_heads, block_size):
+    """48 ragged sequences (empty, single-token, chunk-edge and ~3000-token ones), 8 KV
+    heads: in 256-token chunks that is 48 x 8 x 12 = 4608 (chunk, unit) items, more
+    than any GPU holds blocks at once, so the matrix-core passes run persistent and
+    take their items from the work list; about half the items are empty."""
+    rng = np.random.default_rng(seed)
+    lens = [0, 1, 255, 256, 257, 512, 3072, 3000] + [int(x) for x in rng.integers(0, 3073, 40)]
+    return W.small_decode(seed=seed, n_seqs=len(lens), lens=lens, n_qtok=n_qtok, n_q_heads=n_q_heads,
+                          n_kv_heads=8, k_bits=4, v_bits=3, tau=tau, block_size=block_size)
+
+
+@pytest.mark.parametrize("tau", [0.0, 1e-3])
+@pytest.mark.parametrize("shape", [(1, 32, 256), (4, 32, 64), (2, 64, 100)],
+                         ids=["q1-rows4-bs256", "q4-rows16-bs64", "q2-rows16-bs100"])
+def test_decode_persistent_work_list(tau, shape, monkeypatch):
+    n_qtok, hq, bs = shape
+    monkeypatch.setattr(T, "default_options", T.DecodeOptions(kernel=T.DECODE_KERNEL_MFMA, chunk=256))
+    wl = _persistent_workload(400 + n_qtok + bs, tau, n_qtok, hq, bs)
+    decode_and_compare(wl)
+
+
+@pytest.mark.parametrize("tau", [0.0, 1e-3])
+def test_append_decode_persistent_work_list(tau, monkeypatch):
+    monkeypatch.setattr(T, "default_options", T.DecodeOptions(kernel=T.DECODE_KERNEL_MFMA, chunk=256))
+    wl = _persistent_workload(411, tau, 2, 32, 256)
+    append_and_compare(wl)
+
+
 @pytest.mark.parametrize("variant", ["large-q", "small-q"])
 def test_decode_extreme_magnitudes(variant, kernel):
     """Queries scaled far from unit size (K norms scaled back for large ones, so the
