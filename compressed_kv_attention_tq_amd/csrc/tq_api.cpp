@@ -172,6 +172,7 @@ struct DecodePlan {
     int rows, rows_pad, chunk, n_chunks, n_tiles;
     size_t off_qrot, off_ml, off_acc, off_tile, off_stats, off_ctrl, total;
     bool list;   // the workspace holds a work list (persistent matrix-core passes)
+    bool pair;   // the list pairs chunks (the library's chunk, halved)
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -191,7 +192,16 @@ DecodePlan plan_decode(int n_seqs, int n_kv, int nb, int acc_w, int rows, int ma
     const int64_t target = 512;
     int chunk = unit;
     while (chunk < 16384 && total / (2 * chunk) >= target) chunk *= 2;
-    if (chunk_opt > 0) chunk = chunk_opt;
+    // Matrix-core pass with more items than two blocks per CU of the largest GPUs
+    // hold (a persistent launch): half the chunk, taken in pairs by the work list,
+    // so the items are as long but the last ones half as long.
+    p.pair = false;
+    if (chunk_opt > 0) {
+        chunk = chunk_opt;
+    } else if (mfma && chunk >= 2 * unit && (int64_t)n_seqs * n_kv * ((cap + chunk - 1) / chunk) > 2 * target) {
+        chunk /= 2;
+        p.pair = true;
+    }
     p.chunk = chunk;
     p.n_chunks = (int)((cap + chunk - 1) / chunk);
     p.n_tiles = p.n_chunks * (chunk / kSlice);
@@ -556,6 +566,7 @@ tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32
     a.ctrl = p.list ? reinterpret_cast<uint32_t *>(ws + p.off_ctrl) : nullptr;
     a.persist = 0;
     a.pass_slot = 0;
+    a.pair = p.pair && p.list ? 1 : 0;
     a.n_seqs = n_seqs;
     a.n_qtok = n_qtok;
     a.n_q_heads = n_q_heads;

@@ -626,10 +626,13 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
 // Work list of the persistent matrix-core passes, one block: the non-empty
 // (chunk, unit) items in chunk-major order (every unit's chunk 0, then chunk 1,
 // ...), so the full chunks are taken first and the short last chunks of ragged
-// sequences last.  Units are counting-sorted by their chunk count n_c(u)
-// (decreasing): the units with more than c chunks are then a prefix of that order,
-// cnt[c] of them, and chunk c's items are list[off[c] .. off[c] + cnt[c]).
-// Also zeroes the passes' item counters.  (n_chunks <= kMaxListChunks.)
+// sequences last.  With a.pair the items of the first part are pairs of chunks
+// (2p, 2p + 1), pair-major, and the last chunk of every unit with an odd count
+// follows as an item of its own: long items first, a tail of short ones.  Units
+// are counting-sorted by their item count k(u) (decreasing): the units with more
+// than c items are then a prefix of that order, cnt[c] of them, and item row c is
+// list[off[c] .. off[c] + cnt[c]).  Also zeroes the passes' item counters.
+// (n_chunks <= kMaxListChunks.)
 // --------------------------------------------------------------------------
 // Exclusive prefix sum of v[0 .. n) in place by wave 0 (16 elements per lane at a
 // time); returns the total in every lane of wave 0.
@@ -663,63 +666,75 @@ __device__ int wave0_exclusive_scan(int *v, int n) {
 }
 
 __global__ __launch_bounds__(1024) void tq_worklist_kernel(DecodeArgs a) {
-    __shared__ int hist[kMaxListChunks + 2];   // units with n_c = k
-    __shared__ int cnt[kMaxListChunks + 2];    // units with n_c > c
-    __shared__ int off[kMaxListChunks + 2];    // first list entry of chunk c
+    __shared__ int hist[kMaxListChunks + 2];   // units with k(u) = k
+    __shared__ int cnt[kMaxListChunks + 2];    // units with k(u) > c
+    __shared__ int off[kMaxListChunks + 2];    // first list entry of item row c
     __shared__ int fill[kMaxListChunks + 2];
+    __shared__ int n_single;
     const int tid = threadIdx.x, nch = a.n_chunks, n_units = a.n_seqs * a.n_kv;
+    const bool pair = a.pair != 0;
+    const int nk = pair ? nch / 2 : nch;       // item rows of the first part
     int32_t *const sorted = reinterpret_cast<int32_t *>(a.ctrl + kCtrlWords);
     int32_t *const list = sorted + n_units;
     const int cap = a.max_blocks * a.block_size;
-    auto nc_of = [&](int u) {
+    auto nc_of = [&](int u) {   // chunks holding tokens of unit u
         const int b = (int)fdiv((uint32_t)u, a.kv_div);
         const int len = min(max(a.seq_lens[b], 0), cap);
         return min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), nch);
     };
-    for (int i = tid; i <= nch + 1; i += 1024) {
+    auto k_of = [&](int u) { return pair ? nc_of(u) >> 1 : nc_of(u); };
+    for (int i = tid; i <= nk + 1; i += 1024) {
         hist[i] = 0;
         fill[i] = 0;
     }
+    if (tid == 0) n_single = 0;
     __syncthreads();
-    for (int u = tid; u < n_units; u += 1024) atomicAdd(&hist[nc_of(u)], 1);
+    for (int u = tid; u < n_units; u += 1024) atomicAdd(&hist[k_of(u)], 1);
     __syncthreads();
     // cnt[c] = sum of hist[k] over k > c, as an exclusive scan of the reversed
     // histogram; off = exclusive scan of cnt
-    for (int i = tid; i <= nch; i += 1024) cnt[i] = hist[nch - i];
+    for (int i = tid; i <= nk; i += 1024) cnt[i] = hist[nk - i];
     __syncthreads();
-    if (tid < 64) wave0_exclusive_scan(cnt, nch + 1);   // cnt[i] = units with n_c > nch - i
+    if (tid < 64) wave0_exclusive_scan(cnt, nk + 1);   // cnt[i] = units with k > nk - i
     __syncthreads();
-    for (int i = tid; i <= nch; i += 1024) off[i] = cnt[nch - i];   // units with n_c > i
+    for (int i = tid; i <= nk; i += 1024) off[i] = cnt[nk - i];   // units with k > i
     __syncthreads();
-    for (int i = tid; i <= nch; i += 1024) cnt[i] = off[i];
+    for (int i = tid; i <= nk; i += 1024) cnt[i] = off[i];
     __syncthreads();
-    int total = 0;
-    if (tid < 64) total = wave0_exclusive_scan(off, nch + 1);   // off[nch] = total items
+    if (tid < 64) wave0_exclusive_scan(off, nk + 1);   // off[nk] = items of the first part
     __syncthreads();
-    // units in order of decreasing n_c: those with n_c = k take positions
+    // units in order of decreasing k: those with k(u) = k take positions
     // [cnt[k], cnt[k] + hist[k]) (the order inside a group does not matter)
     for (int u = tid; u < n_units; u += 1024) {
-        const int k = nc_of(u);
+        const int k = k_of(u);
         if (k > 0) sorted[cnt[k] + atomicAdd(&fill[k], 1)] = u;
     }
     __threadfence_block();
     __syncthreads();
-    const int n_items = off[nch];
-    for (int t = tid; t < n_items; t += 1024) {
-        int lo = 0, hi = nch - 1;   // the last c with off[c] <= t
+    const int n_main = off[nk];
+    for (int t = tid; t < n_main; t += 1024) {
+        int lo = 0, hi = nk - 1;   // the last c with off[c] <= t
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (off[mid] <= t) lo = mid;
             else hi = mid - 1;
         }
-        list[t] = lo * n_units + sorted[t - off[lo]];
+        const int u = sorted[t - off[lo]];
+        list[t] = pair ? ((2 * lo) * n_units + u) | kListDouble : lo * n_units + u;
     }
+    // pairs: the odd last chunks, after every pair
+    if (pair) {
+        for (int u = tid; u < n_units; u += 1024) {
+            const int f = nc_of(u);
+            if (f & 1) list[n_main + atomicAdd(&n_single, 1)] = (f - 1) * n_units + u;
+        }
+    }
+    __syncthreads();
     if (tid == 0) {
         a.ctrl[0] = 0u;
         a.ctrl[1] = 0u;
-        a.ctrl[2] = (uint32_t)n_items;
+        a.ctrl[2] = (uint32_t)(n_main + n_single);
     }
-    (void)total;
 }
 
 #endif  // !TQ_DECODE_KB

@@ -260,10 +260,12 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// One (chunk, unit) item of a pass: item = c * n_seqs * n_kv + unit.
+// One (chunk, unit) item of a pass: item = c * n_seqs * n_kv + unit, covering `span`
+// chunks from chunk c (a persistent pass's double items: span 2; their partial is
+// written to chunk c's slot and chunk c + 1's slot gets an empty one).
 template <int KB, int VB, bool PK, int MODE, bool CONTIG, int NB, bool OV>
 __device__ __forceinline__ void decode_item(
-    const int item, const int tid, const DecodeArgs &a, const PairTables &pt, const uint8_t *__restrict__ k_codes,
+    const int item, const int span, const int tid, const DecodeArgs &a, const PairTables &pt, const uint8_t *__restrict__ k_codes,
     const float *__restrict__ k_norms, const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms,
     const uint16_t *__restrict__ qin, const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     float *__restrict__ part_ml, float *__restrict__ part_acc, float *__restrict__ tilemax) {
@@ -295,7 +297,7 @@ __device__ __forceinline__ void decode_item(
     constexpr int kTabWords = (WV ? (NKT > NVT ? NKT : NVT) : NKT) * (RB / 4);   // (KF: the V halves only)
     // (NB > 1: q'' of every block, [block][row][kQS], passes through the area before
     // the tables are written)
-    constexpr int kMerge = PK ? kMW * 8 * WRW : NB * 16 * WRP;
+    constexpr int kMerge = PK ? kMW * 8 * WRW : kMW * 16 * WRP;
     constexpr int kQArea = NB > 1 ? NB * 16 * kQS : 0;
     constexpr int kArea0 = kTabWords > kMerge ? kTabWords : kMerge;
     constexpr int kArea = kArea0 > kQArea ? kArea0 : kQArea;
@@ -553,7 +555,7 @@ __device__ __forceinline__ void decode_item(
         asm volatile("" ::"v"(x));
         return;
     }
-    end = min(start + a.chunk, len);
+    end = min(start + span * a.chunk, len);
 
     // ---- fused append: the new positions this wave computes, [own_pa, own_pa + n_own)
     // (they lie in at most two slices of the chunk, each computed by one wave), and
@@ -1465,6 +1467,10 @@ __device__ __forceinline__ void decode_item(
             for (int g2 = 0; g2 < NG; ++g2) L += wst[blk + NB * g2][n][1] * exp2_diff(wst[blk + NB * g2][n][0], M);
             part_ml[((part * rp + col_row) * NB + blk) * 2] = M;
             part_ml[((part * rp + col_row) * NB + blk) * 2 + 1] = L;
+            if (span > 1) {   // (uniform)
+                part_ml[(((part + 1) * rp + col_row) * NB + blk) * 2] = -INFINITY;
+                part_ml[(((part + 1) * rp + col_row) * NB + blk) * 2 + 1] = 0.f;
+            }
         }
     } else {
         scale = E_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(E_run);
@@ -1490,31 +1496,31 @@ __device__ __forceinline__ void decode_item(
 #pragma unroll
             for (int g2 = 0; g2 < NG; ++g2) x += mbuf[((bb + NB * g2) * 8 + row) * WRW + e];
             part_acc[(part * rp + row) * RW + pos] = x;
+            if (span > 1) part_acc[((part + 1) * rp + row) * RW + pos] = 0.f;
         }
     } else if constexpr (WV) {
-        for (int g2 = 0; g2 < NG; ++g2) {
-            if (grp == g2 && writer) {
+        // every wave's scaled sums to its own rows ([wave][row][WRP]), one barrier,
+        // then each element is the sum over the block's groups
+        if (writer) {
+            float *d = &mbuf[(wave * 16 + col_row) * WRP];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 8; ++j)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float *d = &mbuf[(blk * 16 + col_row) * WRP + 8 * (4 * g + e) + j];
-                        *d = (g2 == 0 ? 0.f : *d) + acc[j][e] * scale;
-                    }
-                if constexpr (OV) {
+                for (int e = 0; e < 4; ++e) d[8 * (4 * g + e) + j] = acc[j][e] * scale;
+            if constexpr (OV) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float *d = &mbuf[col_row * WRP + kD + 4 * g + e];
-                        *d = (g2 == 0 ? 0.f : *d) + acc_o[e] * scale_o;
-                    }
-                }
+                for (int e = 0; e < 4; ++e) d[kD + 4 * g + e] = acc_o[e] * scale_o;
             }
-            __syncthreads();
         }
+        __syncthreads();
         for (int i = tid; i < R * RW; i += kMBlock) {
             const int row = i / RW, pos = i - row * RW;
             const int bb = NB == 1 ? 0 : pos / kD, e = pos - bb * kD;
-            part_acc[(part * rp + row) * RW + pos] = mbuf[(bb * 16 + row) * WRP + e];
+            float x = 0.f;
+#pragma unroll
+            for (int g2 = 0; g2 < NG; ++g2) x += mbuf[((g2 * NB + bb) * 16 + row) * WRP + e];
+            part_acc[(part * rp + row) * RW + pos] = x;
+            if (span > 1) part_acc[((part + 1) * rp + row) * RW + pos] = 0.f;
         }
     }
 }
@@ -1538,7 +1544,7 @@ void tq_decode_mfma_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens, float *__restrict__ part_ml,
     float *__restrict__ part_acc, float *__restrict__ tilemax) {
     if constexpr (!PER) {
-        decode_item<KB, VB, PK, MODE, CONTIG, NB, OV>((int)blockIdx.x, (int)threadIdx.x, a, pt, k_codes, k_norms,
+        decode_item<KB, VB, PK, MODE, CONTIG, NB, OV>((int)blockIdx.x, 1, (int)threadIdx.x, a, pt, k_codes, k_norms,
                                                      v_codes, v_norms, qin, block_table, seq_lens, part_ml, part_acc,
                                                      tilemax);
     } else {
@@ -1550,14 +1556,15 @@ void tq_decode_mfma_kernel(
                 qitem[it & 1] = t < a.ctrl[2] ? (int)a.ctrl[kCtrlWords + a.n_seqs * a.n_kv + t] : -1;
             }
             __syncthreads();
-            const int item = __builtin_amdgcn_readfirstlane(qitem[it & 1]);   // (block-uniform)
-            if (item < 0) break;
+            const int entry = __builtin_amdgcn_readfirstlane(qitem[it & 1]);   // (block-uniform)
+            if (entry < 0) break;
+            const int item = entry & (kListDouble - 1), span = (entry & kListDouble) ? 2 : 1;
             // The thread index passes through an empty asm each round, so nothing
             // derived from it is hoisted out of the loop and held in registers across
             // items (the pass is at its register limit).
             int tid = (int)threadIdx.x;
             asm volatile("" : "+v"(tid));
-            decode_item<KB, VB, PK, MODE, CONTIG, NB, OV>(item, tid, a, pt, k_codes, k_norms, v_codes, v_norms, qin,
+            decode_item<KB, VB, PK, MODE, CONTIG, NB, OV>(item, span, tid, a, pt, k_codes, k_norms, v_codes, v_norms, qin,
                                                          block_table, seq_lens, part_ml, part_acc, tilemax);
         }
     }

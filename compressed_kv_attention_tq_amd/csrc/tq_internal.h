@@ -50,6 +50,7 @@ constexpr int kLutMax = 256;       // quantize: max entries of the encode lookup
 constexpr int kMaxListChunks = 1024;   // decode: chunks per sequence a work list covers
 constexpr int64_t kMaxListItems = 4 << 20;   //   and (chunk, unit) items
 constexpr int kCtrlWords = 64;     // decode: control words before the sorted units
+constexpr int kListDouble = 1 << 30;   // decode: work-list flag of an item of two chunks
 
 // One side of a quantize launch.
 struct QuantSide {
@@ -158,6 +159,8 @@ struct DecodeArgs {
     uint32_t *ctrl;
     int32_t persist;          // per launch: 1 = blocks take items from the list
     int32_t pass_slot;        // per launch: the ctrl counter this pass takes items from
+    int32_t pair;             // work list: pairs of chunks form one item (then the single
+                              // last chunks of odd-count units), the library's chunk halved
     float kc[TQ_MAX_LEVELS];
     float vc[TQ_MAX_LEVELS];
 };

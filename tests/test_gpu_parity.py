@@ -464,6 +464,29 @@ def test_decode_persistent_work_list(tau, shape, monkeypatch):
     decode_and_compare(wl)
 
 
+def _paired_workload(seed, tau, n_qtok):
+    """64 sequences of a 262144-token page table (2 KV heads): at the library's chunk
+    choice that is 2048 (chunk, unit) items of 16384 tokens, so the chunk is halved
+    and the work list pairs chunks (items of 16384 tokens, then the odd last 8192-token
+    chunks).  Most sequences are short; three are long enough for pairs (one with an
+    odd chunk count, one ending on a chunk edge)."""
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(0, 1200, 61)] + [40000, 24576, 17000]
+    wl = W.small_decode(seed=seed, n_seqs=len(lens), lens=lens, n_qtok=n_qtok, n_q_heads=8, n_kv_heads=2,
+                        k_bits=4, v_bits=3, tau=tau, block_size=256)
+    table = np.full((wl.n_seqs, 1024), -1, np.int32)
+    table[:, : wl.block_table.shape[1]] = wl.block_table
+    wl.block_table = table
+    return wl
+
+
+@pytest.mark.parametrize("tau", [0.0, 1e-3])
+@pytest.mark.parametrize("n_qtok", [1, 4])
+def test_decode_persistent_paired_items(tau, n_qtok, monkeypatch):
+    monkeypatch.setattr(T, "default_options", T.DecodeOptions(kernel=T.DECODE_KERNEL_MFMA))
+    decode_and_compare(_paired_workload(500 + n_qtok, tau, n_qtok))
+
+
 @pytest.mark.parametrize("tau", [0.0, 1e-3])
 def test_append_decode_persistent_work_list(tau, monkeypatch):
     monkeypatch.setattr(T, "default_options", T.DecodeOptions(kernel=T.DECODE_KERNEL_MFMA, chunk=256))
