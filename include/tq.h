@@ -220,7 +220,11 @@ tq_status tq_quantize_kv(const tq_cache *k, const void *k_src,
  *   out                : device float32 [n_seqs][n_qtok][n_q_heads][head_dim].
  *   workspace          : device scratch of *workspace_bytes bytes, 256-byte aligned;
  *                        NULL queries the size: the required size is written to
- *                        *workspace_bytes and nothing is launched.
+ *                        *workspace_bytes and nothing is launched.  Its contents
+ *                        need no initialisation (every call writes what it reads:
+ *                        the per-chunk partials and, for a large call, the work
+ *                        list and item counters of the persistent pass); calls that
+ *                        share one workspace must be ordered on the stream.
  * Query token j of a sequence of length len attends to positions t <= len - n_qtok + j;
  * query head h reads KV head h / (n_q_heads / n_kv_heads).  A row that sees no
  * position outputs zeros.
