@@ -614,8 +614,8 @@ def cpu_baseline(name, budget_s=6.0, max_units=None, procs=None):
                       f"{' (the whole workload)' if full else ' (seeded subset; the rate needs no scaling)'}"
                       f"{f', each run {rep} times' if rep > 1 else ''}, "
                       f"{p} processes x 1 thread, units dealt round-robin, time = the slowest process's timed "
-                      f"total {makespan:.1f} s; context codes are seeded random bytes (the oracle's work does not "
-                      f"depend on them)",
+                      f"total {makespan:.1f} s"
+                      f"{'' if name == 'quantize' else '; context codes are seeded random bytes (the work does not depend on them)'}",
             "single_process": {"value": round(single / scale, 5), "unit": unit, "cores": 1,
                                "sample": f"{done} units, {spent:.1f} s"},
             "host": info}
