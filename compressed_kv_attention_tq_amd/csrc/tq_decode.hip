@@ -730,11 +730,8 @@ __global__ __launch_bounds__(1024) void tq_worklist_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    if (tid == 0) {
-        a.ctrl[0] = 0u;
-        a.ctrl[1] = 0u;
-        a.ctrl[2] = (uint32_t)(n_main + n_single);
-    }
+    if (tid < 2 * kListParts) a.ctrl[tid * kCtrlLine] = 0u;
+    if (tid == 0) a.ctrl[kCtrlCount] = (uint32_t)(n_main + n_single);
 }
 
 #endif  // !TQ_DECODE_KB

@@ -1551,9 +1551,20 @@ void tq_decode_mfma_kernel(
         __shared__ int qitem[2];   // the item the block takes next (two rounds alternate)
         for (int it = 0;; ++it) {
             // (the barrier also ends the previous item's use of the LDS)
+            // Blocks of partition p = block mod kListParts take the partition's items
+            // t = p, p + kListParts, ... in order: the first round's are the blocks'
+            // own indices, later ones come from the partition's counter, so the blocks
+            // that finish together spread their atomics over kListParts lines instead
+            // of queueing on one.
             if (threadIdx.x == 0) {
-                const uint32_t t = atomicAdd(a.ctrl + a.pass_slot, 1u);
-                qitem[it & 1] = t < a.ctrl[2] ? (int)a.ctrl[kCtrlWords + a.n_seqs * a.n_kv + t] : -1;
+                const uint32_t part = blockIdx.x % kListParts;
+                uint32_t t = blockIdx.x;
+                if (it > 0) {
+                    const uint32_t first_round = (gridDim.x - part + kListParts - 1) / kListParts;
+                    const uint32_t k = atomicAdd(a.ctrl + (a.pass_slot * kListParts + part) * kCtrlLine, 1u);
+                    t = (first_round + k) * kListParts + part;
+                }
+                qitem[it & 1] = t < a.ctrl[kCtrlCount] ? (int)a.ctrl[kCtrlWords + a.n_seqs * a.n_kv + t] : -1;
             }
             __syncthreads();
             const int entry = __builtin_amdgcn_readfirstlane(qitem[it & 1]);   // (block-uniform)
@@ -1615,7 +1626,7 @@ static void launch_mfma_mode(const DecodeArgs &a, const PairTables &pt, int mode
         if constexpr (!std::is_same_v<decltype(kern_persistent), std::nullptr_t>) {
             if (a.persist) {
                 const int cap = resident_blocks(reinterpret_cast<const void *>(kern_persistent));
-                if (cap > 0 && items > cap) {
+                if (cap >= kListParts && items > cap) {   // (every partition has a block)
                     b.persist = 1;
                     launch(kern_persistent, cap);
                     return;

@@ -49,7 +49,10 @@ constexpr int kMBlock = 64 * kMW;  //   threads per block; chunks are multiples 
 constexpr int kLutMax = 256;       // quantize: max entries of the encode lookup table
 constexpr int kMaxListChunks = 1024;   // decode: chunks per sequence a work list covers
 constexpr int64_t kMaxListItems = 4 << 20;   //   and (chunk, unit) items
-constexpr int kCtrlWords = 64;     // decode: control words before the sorted units
+constexpr int kListParts = 16;     // decode: work-list partitions, one item counter each
+constexpr int kCtrlLine = 64;      //   words between counters (one 256-byte line each)
+constexpr int kCtrlCount = 2 * kListParts * kCtrlLine;   //   word holding the item count
+constexpr int kCtrlWords = kCtrlCount + 64;   // control words before the sorted units
 constexpr int kListDouble = 1 << 30;   // decode: work-list flag of an item of two chunks
 
 // One side of a quantize launch.
@@ -152,10 +155,12 @@ struct DecodeArgs {
                                        // code rows it reads (one atomic per wave that read any)
     int32_t contig;           // matrix-core path: every 64-token slice lies in one page
     // Persistent matrix-core passes: a control block and work list in the workspace
-    // (null: no list).  ctrl[0], ctrl[1]: item counters of the first pass (dense or
-    // scoring) and the gated pass; ctrl[2]: items in the list; from word kCtrlWords:
-    // the units sorted by decreasing chunk count, then the list of (chunk, unit)
-    // items, c * n_seqs * n_kv + unit, chunk-major.
+    // (null: no list).  ctrl[(pass * kListParts + p) * kCtrlLine]: the item counter
+    // of partition p of the first pass (dense or scoring, pass 0) or the gated pass
+    // (1); ctrl[kCtrlCount]: items in the list; from word kCtrlWords: the units
+    // sorted by decreasing chunk count, then the list of (chunk, unit) items,
+    // c * n_seqs * n_kv + unit, chunk-major.  Partition p holds the items
+    // t = p, p + kListParts, ...
     uint32_t *ctrl;
     int32_t persist;          // per launch: 1 = blocks take items from the list
     int32_t pass_slot;        // per launch: the ctrl counter this pass takes items from
