@@ -567,6 +567,7 @@ tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32
     a.persist = 0;
     a.pass_slot = 0;
     a.pair = p.pair && p.list ? 1 : 0;
+    a.merge_step = 1;
     a.n_seqs = n_seqs;
     a.n_qtok = n_qtok;
     a.n_q_heads = n_q_heads;

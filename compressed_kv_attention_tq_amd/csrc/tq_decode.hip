@@ -500,7 +500,9 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     const uint32_t sgw0 = sg[(lane >> 5) & 1], sgw1 = sg[2 + ((lane >> 5) & 1)];
     int oidx = 0;
     if constexpr (KEPT) oidx = a.v_out_idx[kv * 16 + min(tid, 15)];
-    const int64_t mstride = (int64_t)a.rows_pad * nb * 2, astride = (int64_t)a.rows_pad * a.acc_w;
+    // (merge_step 2: only the even chunk slots hold partials)
+    const int step = a.merge_step;
+    const int64_t mstride = (int64_t)a.rows_pad * nb * 2 * step, astride = (int64_t)a.rows_pad * a.acc_w * step;
     const float *ml = a.part_ml + ((base * a.rows_pad + r) * nb + hb) * 2;                // chunk c at ml[c * mstride]
     const float *pa = a.part_acc + (base * a.rows_pad + r) * a.acc_w + hb * kD + 4 * q4;  // chunk c at pa[c * astride]
     const bool xo = KEPT && q4 < 4;   // this thread also merges kept sums 4 q4 .. 4 q4 + 3
@@ -570,11 +572,12 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
     // The first round goes out before the sequence length is read: every chunk the
     // workspace holds for this row (n_chunks >= 1) is loaded, and those past the
     // sequence's own chunks (not written by this call) are then dropped.
-    load_round(cg, min(a.n_chunks, 8 * kB));
+    load_round(cg, min((a.n_chunks + step - 1) / step, 8 * kB));
     __builtin_amdgcn_sched_barrier(0);
     const int len = a.seq_lens[b];
-    // (clamped to the chunks the workspace holds, whatever the length)
-    const int nc = len > 0 ? min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), a.n_chunks) : 0;
+    // (clamped to the chunks the workspace holds, whatever the length; counted in slots)
+    const int nc = len > 0 ? (min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), a.n_chunks) + step - 1) / step
+                           : 0;
     mask_round(cg, nc);
     fold_round();
     for (int c0 = cg + 8 * kB; c0 < nc; c0 += 8 * kB) {
@@ -796,7 +799,7 @@ void TQ_CAT(launch_pass_kb, TQ_DECODE_KB)(const DecodeArgs &a, int mode, hipStre
 #else
 
 #define TQ_DECL_MFMA(KB, NB)                                                                                  \
-    void launch_mfma_kb##KB##_nb##NB(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s,        \
+    bool launch_mfma_kb##KB##_nb##NB(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s,        \
                                      hipEvent_t ev0, hipEvent_t ev1);
 #define TQ_DECL_MFMA_KB(KB) TQ_DECL_MFMA(KB, 1) TQ_DECL_MFMA(KB, 2) TQ_DECL_MFMA(KB, 4)
 TQ_DECL_MFMA_KB(2)
@@ -806,19 +809,20 @@ TQ_DECL_MFMA_KB(16)   // K float16
 #undef TQ_DECL_MFMA_KB
 #undef TQ_DECL_MFMA
 
-static void launch_mfma_any(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s,
+// Returns whether the pass launch is persistent.
+static bool launch_mfma_any(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s,
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
 #define TQ_CASE_NB(KB)                                                                  \
     switch (a.nb) {                                                                     \
-        case 2: launch_mfma_kb##KB##_nb2(a, pt, mode, s, ev0, ev1); break;              \
-        case 4: launch_mfma_kb##KB##_nb4(a, pt, mode, s, ev0, ev1); break;              \
-        default: launch_mfma_kb##KB##_nb1(a, pt, mode, s, ev0, ev1); break;             \
+        case 2: return launch_mfma_kb##KB##_nb2(a, pt, mode, s, ev0, ev1);              \
+        case 4: return launch_mfma_kb##KB##_nb4(a, pt, mode, s, ev0, ev1);              \
+        default: return launch_mfma_kb##KB##_nb1(a, pt, mode, s, ev0, ev1);             \
     }
     switch (a.k_bits) {
-        case 2: TQ_CASE_NB(2) break;
-        case 3: TQ_CASE_NB(3) break;
-        case 16: TQ_CASE_NB(16) break;
-        default: TQ_CASE_NB(4) break;
+        case 2: TQ_CASE_NB(2)
+        case 3: TQ_CASE_NB(3)
+        case 16: TQ_CASE_NB(16)
+        default: TQ_CASE_NB(4)
     }
 #undef TQ_CASE_NB
 }
@@ -871,13 +875,16 @@ hipError_t launch_decode(const DecodeArgs &a, const PairTables &pt, hipStream_t 
             hipLaunchKernelGGL(tq_worklist_kernel, dim3(1), dim3(1024), 0, s, a);
             b.persist = 1;
         }
+        // (a persistent pass over a paired list leaves its partials in the even chunk
+        // slots only: the merge reads those)
+        DecodeArgs m = a;
         if (a.tau > 0.f) {
             launch_mfma_any(b, pt, MODE_SCORE, s, ev_before, ev_after);
-            launch_mfma_any(b, pt, MODE_GATED, s);
-            launch_merge<true>(a, rows_grid, s);
+            m.merge_step = launch_mfma_any(b, pt, MODE_GATED, s) && a.pair ? 2 : 1;
+            launch_merge<true>(m, rows_grid, s);
         } else {
-            launch_mfma_any(b, pt, MODE_DENSE, s, ev_before, ev_after);
-            launch_merge<false>(a, rows_grid, s);
+            m.merge_step = launch_mfma_any(b, pt, MODE_DENSE, s, ev_before, ev_after) && a.pair ? 2 : 1;
+            launch_merge<false>(m, rows_grid, s);
         }
         return hipGetLastError();
     }

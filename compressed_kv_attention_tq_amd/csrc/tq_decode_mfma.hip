@@ -262,7 +262,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 // One (chunk, unit) item of a pass: item = c * n_seqs * n_kv + unit, covering `span`
 // chunks from chunk c (a persistent pass's double items: span 2; their partial is
-// written to chunk c's slot and chunk c + 1's slot gets an empty one).
+// written to chunk c's slot, and chunk c + 1's (max, sum) slot gets the empty pair,
+// which the gated pass's statistics read; the merge of a paired list reads the even
+// chunk slots only, so the second slot's accumulator is not written).
 template <int KB, int VB, bool PK, int MODE, bool CONTIG, int NB, bool OV>
 __device__ __forceinline__ void decode_item(
     const int item, const int span, const int tid, const DecodeArgs &a, const PairTables &pt, const uint8_t *__restrict__ k_codes,
@@ -1496,7 +1498,6 @@ __device__ __forceinline__ void decode_item(
 #pragma unroll
             for (int g2 = 0; g2 < NG; ++g2) x += mbuf[((bb + NB * g2) * 8 + row) * WRW + e];
             part_acc[(part * rp + row) * RW + pos] = x;
-            if (span > 1) part_acc[((part + 1) * rp + row) * RW + pos] = 0.f;
         }
     } else if constexpr (WV) {
         // every wave's scaled sums to its own rows ([wave][row][WRP]), one barrier,
@@ -1520,7 +1521,6 @@ __device__ __forceinline__ void decode_item(
 #pragma unroll
             for (int g2 = 0; g2 < NG; ++g2) x += mbuf[((g2 * NB + bb) * 16 + row) * WRP + e];
             part_acc[(part * rp + row) * RW + pos] = x;
-            if (span > 1) part_acc[((part + 1) * rp + row) * RW + pos] = 0.f;
         }
     }
 }
@@ -1609,8 +1609,9 @@ static int resident_blocks(const void *kern) {
 // persistent if the items outnumber the blocks the GPU holds at once (one-block
 // heads without kept V channels, K compressed: the shapes long and batched decode
 // takes).
+// Returns whether the launch is persistent.
 template <int KB, int VB, bool PK, bool CONTIG, int NB>
-static void launch_mfma_mode(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
+static bool launch_mfma_mode(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
                              hipEvent_t ev1) {
     const int64_t items = (int64_t)a.n_seqs * a.n_kv * a.n_chunks;
     DecodeArgs b = a;
@@ -1663,19 +1664,19 @@ static void launch_mfma_mode(const DecodeArgs &a, const PairTables &pt, int mode
             go(tq_decode_mfma_kernel<KB, VB, PK, MODE_GATED, CONTIG, NB, false, false>, nullptr);
         }
     }
+    return b.persist != 0;
 }
 
 template <int KB, int VB, int NB>
-static void launch_mfma_vb(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
+static bool launch_mfma_vb(const DecodeArgs &a, const PairTables &pt, int mode, hipStream_t s, hipEvent_t ev0,
                            hipEvent_t ev1) {
     const bool pk = a.rows <= 8;
     if (a.contig) {
-        if (pk) launch_mfma_mode<KB, VB, true, true, NB>(a, pt, mode, s, ev0, ev1);
-        else launch_mfma_mode<KB, VB, false, true, NB>(a, pt, mode, s, ev0, ev1);
-    } else {
-        if (pk) launch_mfma_mode<KB, VB, true, false, NB>(a, pt, mode, s, ev0, ev1);
-        else launch_mfma_mode<KB, VB, false, false, NB>(a, pt, mode, s, ev0, ev1);
+        if (pk) return launch_mfma_mode<KB, VB, true, true, NB>(a, pt, mode, s, ev0, ev1);
+        return launch_mfma_mode<KB, VB, false, true, NB>(a, pt, mode, s, ev0, ev1);
     }
+    if (pk) return launch_mfma_mode<KB, VB, true, false, NB>(a, pt, mode, s, ev0, ev1);
+    return launch_mfma_mode<KB, VB, false, false, NB>(a, pt, mode, s, ev0, ev1);
 }
 
 #ifndef TQ_DECODE_NB
@@ -1683,12 +1684,12 @@ static void launch_mfma_vb(const DecodeArgs &a, const PairTables &pt, int mode, 
 #endif
 #define TQ_CAT4(a, b, c, d) a##b##c##d
 #define TQ_NAME(a, b, c, d) TQ_CAT4(a, b, c, d)
-void TQ_NAME(launch_mfma_kb, TQ_DECODE_KB, _nb, TQ_DECODE_NB)(const DecodeArgs &a, const PairTables &pt, int mode,
+bool TQ_NAME(launch_mfma_kb, TQ_DECODE_KB, _nb, TQ_DECODE_NB)(const DecodeArgs &a, const PairTables &pt, int mode,
                                                              hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     switch (a.v_bits) {
-        case 2: launch_mfma_vb<TQ_DECODE_KB, 2, TQ_DECODE_NB>(a, pt, mode, s, ev0, ev1); break;
-        case 3: launch_mfma_vb<TQ_DECODE_KB, 3, TQ_DECODE_NB>(a, pt, mode, s, ev0, ev1); break;
-        default: launch_mfma_vb<TQ_DECODE_KB, 4, TQ_DECODE_NB>(a, pt, mode, s, ev0, ev1); break;
+        case 2: return launch_mfma_vb<TQ_DECODE_KB, 2, TQ_DECODE_NB>(a, pt, mode, s, ev0, ev1);
+        case 3: return launch_mfma_vb<TQ_DECODE_KB, 3, TQ_DECODE_NB>(a, pt, mode, s, ev0, ev1);
+        default: return launch_mfma_vb<TQ_DECODE_KB, 4, TQ_DECODE_NB>(a, pt, mode, s, ev0, ev1);
     }
 }
 

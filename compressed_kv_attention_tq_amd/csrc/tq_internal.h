@@ -166,6 +166,7 @@ struct DecodeArgs {
     int32_t pass_slot;        // per launch: the ctrl counter this pass takes items from
     int32_t pair;             // work list: pairs of chunks form one item (then the single
                               // last chunks of odd-count units), the library's chunk halved
+    int32_t merge_step;       // merge: chunk slots between partials (2 after a paired list)
     float kc[TQ_MAX_LEVELS];
     float vc[TQ_MAX_LEVELS];
 };
