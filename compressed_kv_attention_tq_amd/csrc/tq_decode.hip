@@ -669,15 +669,19 @@ __device__ int wave0_exclusive_scan(int *v, int n) {
 }
 
 __global__ __launch_bounds__(1024) void tq_worklist_kernel(DecodeArgs a) {
+    constexpr int kUnitsHeld = 4;               // units per thread whose counts stay in registers
+    constexpr int kSortedLds = 1024 * kUnitsHeld;   // units whose sorted order stays in LDS
     __shared__ int hist[kMaxListChunks + 2];   // units with k(u) = k
     __shared__ int cnt[kMaxListChunks + 2];    // units with k(u) > c
     __shared__ int off[kMaxListChunks + 2];    // first list entry of item row c
     __shared__ int fill[kMaxListChunks + 2];
+    __shared__ int sorted_l[kSortedLds];
     __shared__ int n_single;
     const int tid = threadIdx.x, nch = a.n_chunks, n_units = a.n_seqs * a.n_kv;
     const bool pair = a.pair != 0;
     const int nk = pair ? nch / 2 : nch;       // item rows of the first part
-    int32_t *const sorted = reinterpret_cast<int32_t *>(a.ctrl + kCtrlWords);
+    const bool in_lds = n_units <= kSortedLds;
+    int32_t *const sorted = reinterpret_cast<int32_t *>(a.ctrl + kCtrlWords);   // (more units)
     int32_t *const list = sorted + n_units;
     const int cap = a.max_blocks * a.block_size;
     auto nc_of = [&](int u) {   // chunks holding tokens of unit u
@@ -685,14 +689,19 @@ __global__ __launch_bounds__(1024) void tq_worklist_kernel(DecodeArgs a) {
         const int len = min(max(a.seq_lens[b], 0), cap);
         return min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), nch);
     };
-    auto k_of = [&](int u) { return pair ? nc_of(u) >> 1 : nc_of(u); };
+    // the chunk counts of this thread's first units (u = tid + 1024 i), read once
+    int ncr[kUnitsHeld];
+#pragma unroll
+    for (int i = 0; i < kUnitsHeld; ++i) ncr[i] = tid + 1024 * i < n_units ? nc_of(tid + 1024 * i) : 0;
+    auto nc_at = [&](int i, int u) { return i < kUnitsHeld ? ncr[i] : nc_of(u); };   // u = tid + 1024 i
+    auto k_at = [&](int i, int u) { return pair ? nc_at(i, u) >> 1 : nc_at(i, u); };
     for (int i = tid; i <= nk + 1; i += 1024) {
         hist[i] = 0;
         fill[i] = 0;
     }
     if (tid == 0) n_single = 0;
     __syncthreads();
-    for (int u = tid; u < n_units; u += 1024) atomicAdd(&hist[k_of(u)], 1);
+    for (int u = tid, i = 0; u < n_units; u += 1024, ++i) atomicAdd(&hist[k_at(i, u)], 1);
     __syncthreads();
     // cnt[c] = sum of hist[k] over k > c, as an exclusive scan of the reversed
     // histogram; off = exclusive scan of cnt
@@ -708,9 +717,13 @@ __global__ __launch_bounds__(1024) void tq_worklist_kernel(DecodeArgs a) {
     __syncthreads();
     // units in order of decreasing k: those with k(u) = k take positions
     // [cnt[k], cnt[k] + hist[k]) (the order inside a group does not matter)
-    for (int u = tid; u < n_units; u += 1024) {
-        const int k = k_of(u);
-        if (k > 0) sorted[cnt[k] + atomicAdd(&fill[k], 1)] = u;
+    for (int u = tid, i = 0; u < n_units; u += 1024, ++i) {
+        const int k = k_at(i, u);
+        if (k > 0) {
+            const int pos = cnt[k] + atomicAdd(&fill[k], 1);
+            if (in_lds) sorted_l[pos] = u;
+            else sorted[pos] = u;
+        }
     }
     __threadfence_block();
     __syncthreads();
@@ -722,13 +735,13 @@ __global__ __launch_bounds__(1024) void tq_worklist_kernel(DecodeArgs a) {
             if (off[mid] <= t) lo = mid;
             else hi = mid - 1;
         }
-        const int u = sorted[t - off[lo]];
+        const int u = in_lds ? sorted_l[t - off[lo]] : sorted[t - off[lo]];
         list[t] = pair ? ((2 * lo) * n_units + u) | kListDouble : lo * n_units + u;
     }
     // pairs: the odd last chunks, after every pair
     if (pair) {
-        for (int u = tid; u < n_units; u += 1024) {
-            const int f = nc_of(u);
+        for (int u = tid, i = 0; u < n_units; u += 1024, ++i) {
+            const int f = nc_at(i, u);
             if (f & 1) list[n_main + atomicAdd(&n_single, 1)] = (f - 1) * n_units + u;
         }
     }
