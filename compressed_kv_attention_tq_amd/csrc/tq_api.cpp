@@ -173,6 +173,7 @@ struct DecodePlan {
     size_t off_qrot, off_ml, off_acc, off_tile, off_stats, off_ctrl, total;
     bool list;   // the workspace holds a work list (persistent matrix-core passes)
     bool pair;   // the list pairs chunks (the library's chunk, halved)
+    bool gate_pairs;   // sparse: the gated pass takes pairs of chunks
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -196,11 +197,20 @@ DecodePlan plan_decode(int n_seqs, int n_kv, int nb, int acc_w, int rows, int ma
     // hold (a persistent launch): half the chunk, taken in pairs by the work list,
     // so the items are as long but the last ones half as long.
     p.pair = false;
+    p.gate_pairs = false;
     if (chunk_opt > 0) {
         chunk = chunk_opt;
     } else if (mfma && chunk >= 2 * unit && (int64_t)n_seqs * n_kv * ((cap + chunk - 1) / chunk) > 2 * target) {
         chunk /= 2;
         p.pair = true;
+    } else if (mfma && sparse && nb == 1) {
+        // Sparse V, one block per item: the scoring pass holds three blocks per CU and
+        // the gated pass two, so the chunks are sized for about three scoring blocks per
+        // CU of the largest GPUs and the gated pass takes them in pairs.
+        const int64_t want = 3 * target / 2;
+        const int64_t cs = ((total + want - 1) / want + unit - 1) / unit * unit;
+        chunk = (int)std::min<int64_t>(std::max<int64_t>(cs, unit), 16384);
+        p.gate_pairs = true;
     }
     p.chunk = chunk;
     p.n_chunks = (int)((cap + chunk - 1) / chunk);
@@ -568,6 +578,7 @@ tq_status decode_impl(const tq_cache *k, const tq_cache *v, const void *q, int32
     a.pass_slot = 0;
     a.pair = p.pair && p.list ? 1 : 0;
     a.merge_step = 1;
+    a.gate_pairs = p.gate_pairs ? 1 : 0;
     a.n_seqs = n_seqs;
     a.n_qtok = n_qtok;
     a.n_q_heads = n_q_heads;

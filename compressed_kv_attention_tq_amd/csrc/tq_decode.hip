@@ -884,16 +884,16 @@ hipError_t launch_decode(const DecodeArgs &a, const PairTables &pt, hipStream_t 
         b.persist = 0;
         const int64_t items = (int64_t)a.n_seqs * a.n_kv * a.n_chunks;
         const int cus = device_cus();
-        if (a.ctrl && cus > 0 && items > 2 * (int64_t)cus) {
+        if (a.ctrl && cus > 0 && items > 2 * (int64_t)cus && !a.gate_pairs) {
             hipLaunchKernelGGL(tq_worklist_kernel, dim3(1), dim3(1024), 0, s, a);
             b.persist = 1;
         }
-        // (a persistent pass over a paired list leaves its partials in the even chunk
-        // slots only: the merge reads those)
+        // (a persistent pass over a paired list, and a gated pass over pairs of chunks,
+        // leave their partials in the even chunk slots only: the merge reads those)
         DecodeArgs m = a;
         if (a.tau > 0.f) {
             launch_mfma_any(b, pt, MODE_SCORE, s, ev_before, ev_after);
-            m.merge_step = launch_mfma_any(b, pt, MODE_GATED, s) && a.pair ? 2 : 1;
+            m.merge_step = (launch_mfma_any(b, pt, MODE_GATED, s) && a.pair) || a.gate_pairs ? 2 : 1;
             launch_merge<true>(m, rows_grid, s);
         } else {
             m.merge_step = launch_mfma_any(b, pt, MODE_DENSE, s, ev_before, ev_after) && a.pair ? 2 : 1;

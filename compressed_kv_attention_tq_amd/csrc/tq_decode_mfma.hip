@@ -1544,7 +1544,16 @@ void tq_decode_mfma_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens, float *__restrict__ part_ml,
     float *__restrict__ part_acc, float *__restrict__ tilemax) {
     if constexpr (!PER) {
-        decode_item<KB, VB, PK, MODE, CONTIG, NB, OV>((int)blockIdx.x, 1, (int)threadIdx.x, a, pt, k_codes, k_norms,
+        // (a gated pass over pairs of the scoring pass's chunks: block = pair * units + unit)
+        int item = (int)blockIdx.x, span = 1;
+        if constexpr (MODE == MODE_GATED) {
+            if (a.gate_pairs) {
+                const int pr = (int)fdiv(blockIdx.x, a.units_div);
+                item = item + pr * a.n_seqs * a.n_kv;   // (2 pr) * units + unit
+                span = 2;
+            }
+        }
+        decode_item<KB, VB, PK, MODE, CONTIG, NB, OV>(item, span, (int)threadIdx.x, a, pt, k_codes, k_norms,
                                                      v_codes, v_norms, qin, block_table, seq_lens, part_ml, part_acc,
                                                      tilemax);
     } else {
@@ -1624,6 +1633,10 @@ static bool launch_mfma_mode(const DecodeArgs &a, const PairTables &pt, int mode
     };
     // one block per item, or (a persistent form given) as many as the GPU holds
     auto go = [&](auto kern, auto kern_persistent) {
+        if (mode == MODE_GATED && a.gate_pairs) {   // pairs of chunks, one block each
+            launch(kern, (int64_t)a.n_seqs * a.n_kv * ((a.n_chunks + 1) / 2));
+            return;
+        }
         if constexpr (!std::is_same_v<decltype(kern_persistent), std::nullptr_t>) {
             if (a.persist) {
                 const int cap = resident_blocks(reinterpret_cast<const void *>(kern_persistent));

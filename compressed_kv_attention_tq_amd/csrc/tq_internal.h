@@ -167,6 +167,8 @@ struct DecodeArgs {
     int32_t pair;             // work list: pairs of chunks form one item (then the single
                               // last chunks of odd-count units), the library's chunk halved
     int32_t merge_step;       // merge: chunk slots between partials (2 after a paired list)
+    int32_t gate_pairs;       // sparse, one block per item: the gated pass takes pairs of the
+                              // scoring pass's chunks (chunks sized for three scoring blocks per CU)
     float kc[TQ_MAX_LEVELS];
     float vc[TQ_MAX_LEVELS];
 };
