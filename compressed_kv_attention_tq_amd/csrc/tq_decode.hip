@@ -626,6 +626,93 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(DecodeArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// Merge for few chunk slots (at most KS in the workspace, no kept V channels): one
+// block takes 8 consecutive (row, head block) outputs t, 32 float4 columns each, and
+// every thread merges all chunk slots of its column in one round of loads (issued
+// before the sequence length is read; slots past the sequence's own are then
+// dropped).  Same log-sum-exp rule and output stage as tq_merge_kernel, without
+// the chunk groups and their LDS reduction, and with about one block per 8
+// outputs instead of one per output: ragged batches of short sequences are many
+// rows with a handful of partials each.
+// --------------------------------------------------------------------------
+template <bool SPARSE, int KS>
+__global__ __launch_bounds__(256) void tq_merge_rows_kernel(DecodeArgs a, uint32_t n_out_rows) {
+    typedef float f4_t __attribute__((ext_vector_type(4)));
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    __shared__ __attribute__((aligned(16))) float y[8][kD + 4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rr = tid >> 5, q4 = tid & 31;
+    const int nb = a.nb;
+    // this thread's output t = (row, head block), row = (b, jq, h)
+    const uint32_t t = min(blockIdx.x * 8u + (uint32_t)rr, n_out_rows - 1);
+    const int hb = (int)(t & (uint32_t)(nb - 1));
+    const uint32_t row_id = t >> a.nb_log2;
+    const int bj = (int)fdiv(row_id, a.qh_div);
+    const int h = (int)row_id - bj * a.n_q_heads;
+    const int b = (int)fdiv((uint32_t)bj, a.qt_div);
+    const int jq = bj - b * a.n_qtok;
+    const int kv = (int)fdiv((uint32_t)h, a.grp_div);
+    const int r = jq * a.group + (h - kv * a.group);
+    const int64_t base = ((int64_t)b * a.n_kv + kv) * a.n_chunks;
+    const int step = a.merge_step;   // 2: only the even chunk slots hold partials
+    const int64_t mstride = (int64_t)a.rows_pad * nb * 2 * step, astride = (int64_t)a.rows_pad * a.acc_w * step;
+    const float *ml = a.part_ml + ((base * a.rows_pad + r) * nb + hb) * 2;
+    const float *pa = a.part_acc + (base * a.rows_pad + r) * a.acc_w + hb * kD + 4 * q4;
+    const int slots = (a.n_chunks + step - 1) / step;   // <= KS
+    f2_t mlr[KS];
+    f4_t v[KS];
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        const int ci = min(i, slots - 1);
+        if constexpr (!SPARSE) mlr[i] = *reinterpret_cast<const f2_t *>(ml + ci * mstride);
+        v[i] = *reinterpret_cast<const f4_t *>(pa + ci * astride);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int len = a.seq_lens[b];
+    const int nc = len > 0 ? (min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), a.n_chunks) + step - 1) / step
+                           : 0;
+    f4_t x = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (SPARSE) {
+#pragma unroll
+        for (int i = 0; i < KS; ++i) x += i < nc ? v[i] : f4_t{0.f, 0.f, 0.f, 0.f};
+    } else {
+        float M = -INFINITY, L = 0.f;
+#pragma unroll
+        for (int i = 0; i < KS; ++i) M = fmaxf(M, i < nc ? mlr[i].x : -INFINITY);
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            const float f = i < nc ? exp2_diff(mlr[i].x, M) : 0.f;
+            x += f * (i < nc ? v[i] : f4_t{0.f, 0.f, 0.f, 0.f});
+            L += f * (i < nc ? mlr[i].y : 0.f);
+        }
+        x = L > 0.f ? x / L : f4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    *reinterpret_cast<f4_t *>(&y[rr][4 * q4]) = x;
+    __syncthreads();
+    // o = s_V * H y / sqrt(128): wave w takes outputs 2w and 2w + 1 of the block
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int ro = 2 * wave + k;
+        const uint32_t to = blockIdx.x * 8u + (uint32_t)ro;
+        if (to >= n_out_rows) break;
+        const int hbo = (int)(to & (uint32_t)(nb - 1));
+        const uint32_t hro = to >> a.nb_log2;
+        const int ho = (int)hro - (int)fdiv(hro, a.qh_div) * a.n_q_heads;
+        const int kvo = (int)fdiv((uint32_t)ho, a.grp_div);
+        const uint32_t *sg = a.v_signs + (kvo * nb + hbo) * 4;
+        const uint32_t sgw0 = sg[(lane >> 5) & 1], sgw1 = sg[2 + ((lane >> 5) & 1)];
+        float a0 = y[ro][lane], a1 = y[ro][lane + 64];
+        hadamard128(a0, a1, lane);
+        const float kk = 0.088388347648318440550f;
+        a0 *= ((sgw0 >> (lane & 31)) & 1u) ? -kk : kk;
+        a1 *= ((sgw1 >> (lane & 31)) & 1u) ? -kk : kk;
+        float *o = a.out + (int64_t)to * kD;
+        o[lane] = a0;
+        o[lane + 64] = a1;
+    }
+}
+
+// --------------------------------------------------------------------------
 // Work list of the persistent matrix-core passes, one block: the non-empty
 // (chunk, unit) items in chunk-major order (every unit's chunk 0, then chunk 1,
 // ...), so the full chunks are taken first and the short last chunks of ragged
@@ -857,6 +944,13 @@ static void launch_merge_kb(const DecodeArgs &a, dim3 grid, hipStream_t s) {
 
 template <bool SPARSE>
 static void launch_merge(const DecodeArgs &a, dim3 grid, hipStream_t s) {
+    const int slots = (a.n_chunks + a.merge_step - 1) / a.merge_step;
+    if (a.n_out == 0 && slots <= 8) {   // few partials per row: 8 outputs per block
+        const dim3 g((grid.x + 7) / 8);
+        if (slots <= 4) hipLaunchKernelGGL((tq_merge_rows_kernel<SPARSE, 4>), g, dim3(256), 0, s, a, grid.x);
+        else hipLaunchKernelGGL((tq_merge_rows_kernel<SPARSE, 8>), g, dim3(256), 0, s, a, grid.x);
+        return;
+    }
     if (a.n_chunks <= 16) launch_merge_kb<SPARSE, 2>(a, grid, s);
     else if (a.n_chunks <= 32) launch_merge_kb<SPARSE, 4>(a, grid, s);
     else if (a.n_chunks <= 64) launch_merge_kb<SPARSE, 8>(a, grid, s);
