@@ -444,7 +444,7 @@ def test_decode_many_chunks(tau, monkeypatch):
 
 
 @pytest.mark.parametrize("tau", [0.0, 1e-3])
-@pytest.mark.parametrize("case", [(2048, 1, 4, 128), (1280, 4, 32, 128), (1024, 1, 8, 256)],
+@pytest.mark.parametrize("case", [(2048, 1, 4, 2, 128), (1280, 4, 32, 8, 128), (1024, 1, 8, 1, 256)],
                          ids=["8slots-rows2", "5slots-rows16", "4slots-d256"])
 def test_decode_merge_few_slots(tau, case, monkeypatch):
     """The merge for at most 8 chunk slots (8 outputs per block, every slot of a
@@ -452,11 +452,11 @@ def test_decode_merge_few_slots(tau, case, monkeypatch):
     on chunk edges and one token past them, an empty sequence, 2 and 16 rows per KV
     head, and two 128-element blocks per head; the output count is not a multiple of
     8 for the first case (9 sequences x 4 heads)."""
-    cap, n_qtok, hq, d = case
+    cap, n_qtok, hq, n_kv, d = case
     monkeypatch.setattr(T, "default_options", T.DecodeOptions(kernel=T.DECODE_KERNEL_MFMA, chunk=256))
     lens = [0, 1, 256, 257, 700, cap // 2 + 3, cap - 256, cap - 1, cap]
     wl = W.small_decode(seed=31 + cap + d, n_seqs=len(lens), lens=lens, n_qtok=n_qtok, n_q_heads=hq,
-                        n_kv_heads=2 if d == 128 else 1, k_bits=4, v_bits=3, tau=tau, block_size=256,
+                        n_kv_heads=n_kv, k_bits=4, v_bits=3, tau=tau, block_size=256,
                         head_dim=d)
     decode_and_compare(wl)
 
