@@ -396,6 +396,40 @@ __device__ __forceinline__ void decode_item(
         vb0 = btab[i0];
         vb1 = btab[i1];
     }
+    // Gated pass: the first round's candidate inputs (each step's tile maxima and, on
+    // contiguous pages, its page-table entry; lane i = step i of the wave) and the
+    // scoring pass's chunk (max, sum) pairs (lane = chunk, for at most 64 chunks) go
+    // out with the small loads, before the length is known: indices are bounded by
+    // the chunk and the workspace instead, and what lies past the sequence is dropped
+    // later (steps at or past the end, chunks past the sequence's own).
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    constexpr int kRW = 16 / kMW;   // rows a wave reduces
+    f4_t tmx0[4] = {};
+    int cpage0 = 0;
+    f2v mlv[kRW] = {};
+    const int64_t part_u = (int64_t)unit * a.n_chunks;
+    if constexpr (GATED) {
+        const int cend = min(start + span * a.chunk, a.n_chunks * a.chunk);   // (tile index < n_tiles)
+        const int bic = min(first + lane * kStride, cend - 1);
+        const f4_t *tp = reinterpret_cast<const f4_t *>(tilemax + ((int64_t)unit * a.n_tiles + (bic >> 6)) * rp);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            if (4 * r4 < rp) tmx0[r4] = tp[r4];
+        if constexpr (CONTIG) {
+            int pi = min((int)fdiv((uint32_t)bic, bsdiv), last_entry);
+            asm volatile("" : "+v"(pi));
+            cpage0 = btab[pi];
+        }
+        if (a.n_chunks <= 64) {
+            const float *ml = part_ml + part_u * rp * NB * 2;
+            const int cc = min(lane, a.n_chunks - 1);
+#pragma unroll
+            for (int i = 0; i < kRW; ++i) {
+                const int rr = min(wave + kMW * i, R - 1);
+                mlv[i] = *reinterpret_cast<const f2v *>(&ml[(cc * rp + rr) * NB * 2]);
+            }
+        }
+    }
     int len = 0, end = 0;
     const int64_t part = (int64_t)unit * a.n_chunks + c;
     const int64_t tile0 = (int64_t)unit * a.n_tiles;
@@ -546,6 +580,14 @@ __device__ __forceinline__ void decode_item(
         // the small loads are consumed on this path too, so they stay ahead of
         // the length test instead of being moved below it
         uint32_t x = ksg0 ^ ksg1 ^ (uint32_t)len_v ^ (uint32_t)vb0 ^ (uint32_t)vb1;
+        if constexpr (GATED) {
+            x ^= (uint32_t)cpage0;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                x ^= __float_as_uint(tmx0[r4][0] + tmx0[r4][1] + tmx0[r4][2] + tmx0[r4][3]);
+#pragma unroll
+            for (int i = 0; i < kRW; ++i) x ^= __float_as_uint(mlv[i].x + mlv[i].y);
+        }
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) x ^= qh0[i] ^ qh1[i];
 #pragma unroll
@@ -689,45 +731,20 @@ __device__ __forceinline__ void decode_item(
         if (lane == 0) red[wave] = qm;
     }
     // sparse: global (max, sum) of each row from the scoring pass's chunk partials
-    // (part_ml is [chunk][row][block][2]; the blocks' entries are equal, block 0's is read)
-    // Gated pass: the first round's candidate inputs (each step's tile maxima and, on
-    // contiguous pages, its page-table entry; lane i = step i of the wave) go out
-    // before the statistics below, so the two round trips overlap.
-    f4_t tmx0[4] = {};
-    int cpage0 = 0;
-    if constexpr (GATED) {
-        const int bic = min(first + lane * kStride, end - 1);
-        const f4_t *tp = reinterpret_cast<const f4_t *>(tilemax + (tile0 + (bic >> 6)) * rp);
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-            if (4 * r4 < rp) tmx0[r4] = tp[r4];
-        if constexpr (CONTIG) {
-            int pi = min((int)fdiv((uint32_t)bic, bsdiv), last_entry);
-            asm volatile("" : "+v"(pi));
-            cpage0 = btab[pi];
-        }
-    }
-    // With at most 64 chunks (one per lane) every row's pairs are loaded at once, so
-    // the statistics cost one round trip; the sums are the same either way.
+    // (part_ml is [chunk][row][block][2]; the blocks' entries are equal, block 0's is
+    // read).  With at most 64 chunks (one per lane) every row's pairs were loaded
+    // with the small loads, so the statistics cost no round trip of their own; the
+    // sums are the same either way.
     if constexpr (GATED) {
         const int nc = min((int)fdiv((uint32_t)(len + a.chunk - 1), a.chunk_div), a.n_chunks);
-        const float *ml = part_ml + (int64_t)unit * a.n_chunks * rp * NB * 2;
-        constexpr int kRW = 16 / kMW;   // rows a wave reduces
-        if (nc <= 64) {
-            typedef float f2v __attribute__((ext_vector_type(2)));
-            f2v v[kRW];
-            const int cc = min(lane, max(nc - 1, 0));
-#pragma unroll
-            for (int i = 0; i < kRW; ++i) {
-                const int rr = min(wave + kMW * i, R - 1);
-                v[i] = *reinterpret_cast<const f2v *>(&ml[(cc * rp + rr) * NB * 2]);
-            }
+        const float *ml = part_ml + part_u * rp * NB * 2;
+        if (a.n_chunks <= 64) {
 #pragma unroll
             for (int i = 0; i < kRW; ++i) {
                 const int r = wave + kMW * i;
                 if (r < R) {
-                    const float M = wave_max(lane < nc ? v[i].x : -INFINITY);
-                    const float L = wave_sum(lane < nc ? v[i].y * exp2_diff(v[i].x, M) : 0.f);
+                    const float M = wave_max(lane < nc ? mlv[i].x : -INFINITY);
+                    const float L = wave_sum(lane < nc ? mlv[i].y * exp2_diff(mlv[i].x, M) : 0.f);
                     if (lane == 0) {
                         gstat[r][0] = M;
                         gstat[r][1] = L;
@@ -1253,14 +1270,17 @@ __device__ __forceinline__ void decode_item(
         // every row for step i of the round and compares them with the rows'
         // thresholds (the same values and compare as sthr), so the loop waits for
         // one round trip per 64 slices instead of one per slice.
+        // (lane r < 16 forms row r's threshold, the same expression as sthr, and every
+        // row's is read from its lane: one LDS read and one logarithm per lane instead
+        // of a dependent read and logarithm per row)
         float sthr_r[16];
+        {
+            const int rl = lane & 15;
+            const float Mr = gstat[rl][0], Lr = gstat[rl][1];   // (rows >= R: not used)
+            const float thr = (rl < R && Lr > 0.f && Mr > -INFINITY) ? (Mr + log2f(Lr)) + log2f(a.tau) : INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            sthr_r[r] = INFINITY;
-            if (r < R) {
-                const float M = gstat[r][0], L = gstat[r][1];
-                if (L > 0.f && M > -INFINITY) sthr_r[r] = (M + log2f(L)) + log2f(a.tau);
-            }
+            for (int r = 0; r < 16; ++r)
+                sthr_r[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr), r));
         }
         // (contiguous pages: the same round loads each step's page-table entry, so a
         // candidate slice's codes go out without another round trip)
@@ -1350,32 +1370,70 @@ __device__ __forceinline__ void decode_item(
         if constexpr (NB == 1 && CONTIG && !KF && !OV) {
             // (float16 K and kept V channels keep one slot: their slots are too large
             // for two in the registers)
-            // One 64-step round at a time; its candidate slices two at a time: each
-            // candidate's K words, norms and every V unit go out together, and the
-            // next candidate's go out before the current one is computed (when there is
-            // none, the loads repeat a slice already read: the same instructions on
-            // every path, so each wait covers only the slot it needs).
-            auto pop = [](uint64_t &m) __attribute__((always_inline)) -> int {
-                if (!m) return -1;
-                const int k = __builtin_ctzll(m);
-                m &= m - 1;
+            // One 64-step round at a time.  Each wave tests its own steps; the masks
+            // and the steps' page entries meet in LDS, and the block's candidate slices,
+            // in (wave, step) order, are dealt to the waves in turn, so no wave has more
+            // than one candidate more than another wherever the kept positions lie.
+            // A wave's share goes two at a time: each candidate's K words, norms and
+            // every V unit go out together, and the next candidate's go out before the
+            // current one is computed (when there is none, the loads repeat a slice
+            // already read: the same instructions on every path, so each wait covers
+            // only the slot it needs).  Every wave takes part in every round (the
+            // block's rounds), and the exchange alternates between two buffers, so a
+            // round's writes never meet the previous round's reads.
+            __shared__ uint64_t cmask_s[2][kMW];
+            __shared__ int cpage_s[2][kMW][64];
+            // this wave's share, per owner wave: bit i = the owner's step i
+            uint64_t my0 = 0, my1 = 0, my2 = 0, my3 = 0;
+            static_assert(kMW == 4, "four owner masks");
+            // next candidate of the share as owner * 64 + step, or -1
+            auto pop = [&]() __attribute__((always_inline)) -> int {
+                int k = -1;
+                if (my0) { k = __builtin_ctzll(my0); my0 &= my0 - 1; }
+                else if (my1) { k = 64 + __builtin_ctzll(my1); my1 &= my1 - 1; }
+                else if (my2) { k = 128 + __builtin_ctzll(my2); my2 &= my2 - 1; }
+                else if (my3) { k = 192 + __builtin_ctzll(my3); my3 &= my3 - 1; }
                 return k;
             };
-            for (int rs = 0; first + rs * kStride < end; rs += 64) {
+            for (int rs = 0; start + rs * kStride < end; rs += 64) {
                 const int rbase = first + rs * kStride;
+                const int par = (rs >> 6) & 1;
                 round_mask(rs, rbase);
-                uint64_t m = cmask;
-                int kA = pop(m), kB = pop(m);
+                if (lane == 0) cmask_s[par][wave] = cmask;
+                cpage_s[par][wave][lane] = cpage;
+                lds_barrier();
+                {
+                    // candidate (owner o, step i) has rank (candidates of owners < o) +
+                    // (the owner's candidates below step i); this wave takes the ranks
+                    // equal to its index modulo kMW
+                    const uint64_t m0 = cmask_s[par][0], m1 = cmask_s[par][1];
+                    const uint64_t m2 = cmask_s[par][2], m3 = cmask_s[par][3];
+                    auto below = [&](uint64_t m) __attribute__((always_inline)) -> int {
+                        return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    };
+                    const int b1 = __popcll(m0), b2 = b1 + __popcll(m1), b3 = b2 + __popcll(m2);
+                    my0 = __ballot(((m0 >> lane) & 1ull) && ((below(m0)) & (kMW - 1)) == wave);
+                    my1 = __ballot(((m1 >> lane) & 1ull) && ((b1 + below(m1)) & (kMW - 1)) == wave);
+                    my2 = __ballot(((m2 >> lane) & 1ull) && ((b2 + below(m2)) & (kMW - 1)) == wave);
+                    my3 = __ballot(((m3 >> lane) & 1ull) && ((b3 + below(m3)) & (kMW - 1)) == wave);
+                }
+                int kA = pop(), kB = pop();
                 if (kA < 0) continue;   // (wave-uniform)
+                // first token of candidate k's slice: the owner's steps start 64 owner
+                // tokens into the chunk
+                auto cbase = [&](int k) __attribute__((always_inline)) -> int {
+                    return start + (k >> 6) * 64 + (rs + (k & 63)) * kStride;
+                };
                 auto issue_c = [&](Slot &sl, int k) __attribute__((always_inline)) -> int64_t {
-                    const int64_t r0 = row0_of(rbase + k * kStride, __builtin_amdgcn_readlane(cpage, k));
+                    const int64_t r0 = row0_of(cbase(k), cpage_s[par][k >> 6][k & 63]);
                     load_k(sl, r0);
                     sl.vnl = v_norms[r0 + lane];
                     load_v(sl, r0, all_tokens);
                     return r0;
                 };
                 auto compute_c = [&](Slot &sl, int k, int64_t r0) __attribute__((always_inline)) {
-                    const int base = rbase + k * kStride;
+                    const int base = cbase(k);
                     const float E_s = stage_norms(sl, base);
                     f4_t S[4];
                     score_mfma(sl, S);
@@ -1389,12 +1447,12 @@ __device__ __forceinline__ void decode_item(
                 for (;;) {
                     __builtin_amdgcn_sched_barrier(0);
                     compute_c(sa, kA, rA);
-                    const int nA = pop(m);
+                    const int nA = pop();
                     rA = issue_c(sa, nA >= 0 ? nA : kA);
                     __builtin_amdgcn_sched_barrier(0);
                     if (kB < 0) break;
                     compute_c(sb, kB, rB);
-                    const int nB = pop(m);
+                    const int nB = pop();
                     rB = issue_c(sb, nB >= 0 ? nB : kB);
                     kA = nA;
                     kB = nB;
