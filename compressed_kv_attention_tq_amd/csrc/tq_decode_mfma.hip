@@ -265,7 +265,9 @@ __device__ __forceinline__ void lds_barrier() {
 // written to chunk c's slot, and chunk c + 1's (max, sum) slot gets the empty pair,
 // which the gated pass's statistics read; the merge of a paired list reads the even
 // chunk slots only, so the second slot's accumulator is not written).
-template <int KB, int VB, bool PK, int MODE, bool CONTIG, int NB, bool OV>
+// PRIO: raise the wave's issue priority while it is behind (one-item-per-block
+// scoring passes, which hold three blocks per CU).
+template <int KB, int VB, bool PK, int MODE, bool CONTIG, int NB, bool OV, bool PRIO = false>
 __device__ __forceinline__ void decode_item(
     const int item, const int span, const int tid, const DecodeArgs &a, const PairTables &pt, const uint8_t *__restrict__ k_codes,
     const float *__restrict__ k_norms, const uint8_t *__restrict__ v_codes, const float *__restrict__ v_norms,
@@ -1248,8 +1250,21 @@ __device__ __forceinline__ void decode_item(
         // every wave, as the exchange's barriers need), each group's slice `lead`
         // tokens in; a slice past the end has every score masked and changes nothing.
         const int lead = first - start;
+        // PRIO: the SIMD's arbiter favours its oldest wave, so of the blocks sharing a
+        // CU the first one dispatched would finish well before the last, which then
+        // runs with the SIMDs half idle.  Each wave's priority falls from 3 to 0 as it
+        // passes each quarter of its steps, so the waves that are behind issue first
+        // and the blocks end together.
+        const int pq1 = first + (end - first) / 4, pq2 = first + (end - first) / 2,
+                  pq3 = first + 3 * ((end - first) / 4);
         for (int b0 = NB == 1 ? first : start; b0 < end; b0 += NSLOT * kStride) {
             const int base = NB == 1 ? b0 : b0 + lead;
+            if constexpr (PRIO) {
+                if (b0 < pq1) __builtin_amdgcn_s_setprio(3);
+                else if (b0 < pq2) __builtin_amdgcn_s_setprio(2);
+                else if (b0 < pq3) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+            }
             __builtin_amdgcn_sched_barrier(0);
             compute(sa, base);   // the other slots hold the next slices (in flight)
             issue(sa, base + NSLOT * kStride);
@@ -1262,6 +1277,7 @@ __device__ __forceinline__ void decode_item(
                 issue(sc, base + 5 * kStride);
             }
         }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     } else {
         // ---------------- gated pass: candidate slices only (a group's decision is
         // the same in its NB waves; NB > 1: every wave takes part in each step's
@@ -1611,9 +1627,9 @@ void tq_decode_mfma_kernel(
                 span = 2;
             }
         }
-        decode_item<KB, VB, PK, MODE, CONTIG, NB, OV>(item, span, (int)threadIdx.x, a, pt, k_codes, k_norms,
-                                                     v_codes, v_norms, qin, block_table, seq_lens, part_ml, part_acc,
-                                                     tilemax);
+        decode_item<KB, VB, PK, MODE, CONTIG, NB, OV, MODE == MODE_SCORE>(
+            item, span, (int)threadIdx.x, a, pt, k_codes, k_norms, v_codes, v_norms, qin, block_table, seq_lens,
+            part_ml, part_acc, tilemax);
     } else {
         __shared__ int qitem[2];   // the item the block takes next (two rounds alternate)
         for (int it = 0;; ++it) {
