@@ -52,8 +52,13 @@ from compressed_kv_attention_tq_amd import workloads as W  # noqa: E402
 METRIC = "compressed-KV decode attention HBM GB/s (% of peak) + quantize Mtok/s"
 HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
-KERNEL_SOURCES = ["tq_decode.hip", "tq_decode_mfma.hip", "tq_decode_common.h", "tq_device.h", "tq_quant.hip",
-                  "tq_internal.h", "tq_api.cpp"]
+# the sources each measured kernel is built from (its traffic record is tied to them)
+KERNEL_SOURCES = {
+    "tq_decode_mfma_kernel": ["tq_decode.hip", "tq_decode_mfma.hip", "tq_decode_common.h", "tq_device.h",
+                              "tq_internal.h", "tq_api.cpp"],
+    "tq_quantize_kernel": ["tq_quant.hip", "tq_device.h", "tq_internal.h", "tq_api.cpp"],
+}
+PMC_RECORD = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 DECODE_DTYPE = "fp16 hi/lo-split operands (fp32-level), fp32 accumulate"
 DECODE_WORKLOADS = ["llama8b", "llama8b_k16", "llama8b_d256", "llama8b_d512", "llama8b_vout", "longctx", "ragged",
                     "tiny"]
@@ -67,9 +72,9 @@ def cache_bytes_per_token_head(bits):
     return 256 if bits == 16 else 16 * bits + 4   # a float16 side: the row, no norm
 
 
-def source_hash():
+def source_hash(kernel):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "compressed_kv_attention_tq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -79,15 +84,56 @@ def pmc_traffic(kernel_key):
     """HBM bytes per launch from the committed rocprofv3 PMC record
     (profiles/pmc_traffic.json: FETCH_SIZE and WRITE_SIZE scaled by the copy
     calibration) of exactly these kernel sources, else None."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(PMC_RECORD):
         return None
-    with open(path) as f:
+    with open(PMC_RECORD) as f:
         rec = json.load(f)
     r = rec.get(kernel_key)
-    if not r or r.get("source_hash") != source_hash():
+    if not r or r.get("source_hash") != source_hash(kernel_key.split(":")[0]):
         return None
     return r.get("bytes_per_launch")
+
+
+# rocprofv3 FETCH_SIZE counts half of the bytes a plain device copy reads, WRITE_SIZE
+# all it writes (profiles/copy_calibration_pmc.md)
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+
+
+def record_traffic(kernel_key, fetch_csv, write_csv):
+    """Write the HBM bytes per launch of one kernel into the traffic record, from two
+    rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; counter_collection.csv, KiB
+    per dispatch): the mean over that kernel's dispatches, scaled as above."""
+    import csv
+    kernel = kernel_key.split(":")[0]
+
+    def per_dispatch(path, counter):
+        tot = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter or kernel not in row.get("Kernel_Name", ""):
+                    continue
+                d = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                tot[d] = tot.get(d, 0.0) + float(row["Counter_Value"])
+        if not tot:
+            raise SystemExit(f"no {counter} rows for {kernel} in {path}")
+        return sum(tot.values()) / len(tot), len(tot)
+
+    fetch_kib, nf = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write_kib, nw = per_dispatch(write_csv, "WRITE_SIZE")
+    fetch_b = FETCH_SCALE * fetch_kib * 1024
+    write_b = WRITE_SCALE * write_kib * 1024
+    rec = {}
+    if os.path.exists(PMC_RECORD):
+        with open(PMC_RECORD) as f:
+            rec = json.load(f)
+    rec[kernel_key] = {"bytes_per_launch": int(round(fetch_b + write_b)), "fetch_bytes": int(round(fetch_b)),
+                       "write_bytes": int(round(write_b)), "source_hash": source_hash(kernel),
+                       "dispatches": [nf, nw], "fetch_kib_per_dispatch": round(fetch_kib, 1),
+                       "write_kib_per_dispatch": round(write_kib, 1)}
+    with open(PMC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps({kernel_key: rec[kernel_key]}))
 
 
 def host_info():
@@ -429,7 +475,7 @@ def run_quantize(args, torch):
         f"{kern_ms * 1e3:.2f} us/kernel by events, {mtok:.0f} M token-layers/s, {achieved:.0f} GB/s")
     return {"workload": "prefill: 32 layers x 8192 tokens x 8 KV heads, d=128, K3/V2 (Laplace, 1% x30)",
             "value": round(mtok, 1), "unit": "M token-layers/s", "launch": "HIP graph replay of the 32 calls",
-            "dtype": "f32 (codes u8)",
+            "dtype": "fp16 inputs, fp32 accumulate (transform on MFMA), codes u8",
             "ms_per_32_layers": round(pass_ms, 4), "ms_per_32_layers_eager": round(pass_ms_eager, 4),
             "value_eager": round(n * wl.n_layers / (pass_ms_eager * 1e-3) / 1e6, 1),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -643,7 +689,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 256 MiB (reference for HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=3, metavar=("KERNEL:WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
+                    help="(no GPU) write one kernel's HBM bytes per launch from two rocprofv3 --pmc "
+                         "counter_collection.csv files into profiles/pmc_traffic.json")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               f"(the hot path does not shard across GPUs here)", file=sys.stderr)

@@ -5,6 +5,10 @@
 //   domain, sum of squares with v_dot2_f32_f16, 8-lane DPP reduction -> norm,
 //   Walsh-Hadamard transform (4 in-register stages + 3 DPP stages), scale to
 //   the encode grid, encode with a small LDS table, bit-pack, store.
+// When the KV heads divide 8 (every cache without kept channels of the usual
+// head counts) the transform runs on the matrix cores instead, 16 vectors per
+// tile (quant_side_mx below): same encode table and cache layout, about 45%
+// fewer vector instructions.
 // Sources: [TQ blog] 3.2 (signs then Hadamard, fast transform), [TQ blog] 3.3
 // (Lloyd-Max codebook), [TQ+ README] quantization-types note (128-element
 // blocks) and backend table (SET_ROWS quantize-on-append).
@@ -241,12 +245,212 @@ __device__ __forceinline__ void quant_side(const QuantSide &p, const int64_t *__
     }
 }
 
+// --------------------------------------------------------------------------
+// The same quantizer with the Walsh-Hadamard transform on the matrix cores
+// ([TQ blog] 3.2: the rotation is a +-1 diagonal followed by a Hadamard matrix;
+// here the Hadamard product itself is a dense 128 x 128 contraction with exact
+// +-1 operands and float32 accumulation).
+//
+// A wave takes tiles of 16 vectors.  Y = H X' (X' = the sign-flipped float16
+// vectors, one per column) runs as 8 output tiles x 4 k-steps of
+// v_mfma_f32_16x16x32_f16.  Rows and columns of H are taken in an order that
+// makes the lane layouts line up with no data movement:
+//   input  element c = i + 8 s + 32 g   (lane group g = lane >> 4, k-step s,
+//                                        register element i = 0..7)
+//   output element r = jj + 4 t + 32 g  (output tile t, accumulator jj = 0..3)
+// so lane (g, n) loads the 64-byte quarter g of vector n (four 16-byte loads)
+// and receives the 32 consecutive output elements of that same quarter, which it
+// encodes, bit-packs and stores by itself (4·BITS bytes at byte 4·BITS·g of the
+// code row).  With that order, bit by bit,
+//   popcount(r & c) = (m0 i0 + m1 i1 + m2 g0 + m3 g1) + t0 i2 + (t1 s0 + t2 s1)
+// (m = 4 g' + jj the A-tile row, g' the row's group), so every A tile is one of
+// two base tiles (t0 = 0 / 1, differing by the sign of i2) times a scalar sign
+// (-1)^popcount((t >> 1) & s): four constant operands in all.
+// --------------------------------------------------------------------------
+typedef _Float16 qh8_t __attribute__((ext_vector_type(8)));
+typedef float qf4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t qu4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ qf4_t mfma_16x16x32(qu4_t a, qu4_t b, qf4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(qh8_t, a), __builtin_bit_cast(qh8_t, b), c,
+                                                  0, 0, 0);
+}
+
+// A operand (lane: row m = lane & 15, k = 8 (lane >> 4) + i) of the base tile t0
+// = odd, negated when neg: entries (-1)^(m0 i0 + m1 i1 + m2 g0 + m3 g1 + odd i2) as
+// float16 +-1.
+__device__ __forceinline__ qu4_t hadamard_operand(int lane, int odd, int neg) {
+    const int m = lane & 15, g = lane >> 4;
+    const int row = (__popc((m >> 2) & g) + neg) & 1;
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = 2 * d + h;
+            const int sg = (row + __popc((m & 3) & (i & 3)) + odd * (i >> 2)) & 1;
+            word |= (sg ? 0xBC00u : 0x3C00u) << (16 * h);
+        }
+        w[d] = word;
+    }
+    return qu4_t{w[0], w[1], w[2], w[3]};
+}
+
+// Requires n_kv | 8 (p.gpw > 0): a tile of 16 consecutive vectors then holds
+// whole tokens, so the KV head of each lane's vector is fixed for the wave.
+template <int BITS>
+__device__ __forceinline__ void quant_side_mx(const QuantSide &p, const int64_t *__restrict__ slots, LutEntry *lut,
+                                              int blk) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, n = lane & 15;
+    const int wpb = blockDim.x >> 6;
+    const int wave_id = __builtin_amdgcn_readfirstlane(blk * wpb + (int)(threadIdx.x >> 6));
+    const int first = wave_id * p.gpw * 8;   // a multiple of 32 vectors
+    int n_tiles = first < p.n_vec ? (int)min<int64_t>(p.gpw / 2, (p.n_vec - first + 15) / 16) : 0;
+    n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+    const int v0 = first + n;
+    const int tok0 = (int)fdiv((uint32_t)v0, p.kv_div);
+    const int head = v0 - tok0 * p.n_kv;
+    const int tok_step = (int)fdiv(16u, p.kv_div);
+    const FastDiv bsdiv = p.bs_div;
+
+    // sign flips of the lane's 32 elements (one sign word): float16 sign-bit masks
+    // of its 16 float16 pairs, pair d of k-step s = elements 32g + 8s + 2d, +1
+    const uint32_t sb = p.signs[head * 4 + g];
+    uint32_t smask[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            smask[s][d] = (((sb >> (8 * s + 2 * d)) & 1u) << 15) | (((sb >> (8 * s + 2 * d + 1)) & 1u) << 31);
+    const qu4_t hop[2][2] = {{hadamard_operand(lane, 0, 0), hadamard_operand(lane, 0, 1)},
+                             {hadamard_operand(lane, 1, 0), hadamard_operand(lane, 1, 1)}};
+
+    const float kscale = p.grid * 0.088388347648318440550f;   // grid / sqrt(128)
+    const uint16_t *src = p.src + (int64_t)head * kD + 32 * g;
+    const LutEntry *lut0 = lut + p.lut_half;
+
+    struct Tile {
+        qu4_t x[4];
+        int64_t slot;
+    };
+    const int tok_last = tok0 + max(n_tiles - 1, 0) * tok_step;
+    auto load = [&](Tile &tl, int tk) __attribute__((always_inline)) {
+        const int t = min(min(tk, tok_last), p.n_tokens - 1);
+        const qu4_t *sp = reinterpret_cast<const qu4_t *>(src + (int64_t)t * p.src_stride);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) tl.x[s] = sp[s];
+        tl.slot = slots[t];
+    };
+    auto encode = [&](const Tile &tl, int vt) __attribute__((always_inline)) {
+        qu4_t xs[4];
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                xs[s][d] = tl.x[s][d] ^ smask[s][d];
+                const half2_t h = __builtin_bit_cast(half2_t, (uint32_t)xs[s][d]);
+                ss = __builtin_amdgcn_fdot2(h, h, ss, false);
+            }
+        }
+        // the four quarters of vector n sit in lanes n, n + 16, n + 32, n + 48
+        {
+            const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+            ss = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+            const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+            ss = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+        }
+        const bool finite = ss <= FLT_MAX;   // false for inf and NaN
+        if (__builtin_amdgcn_ballot_w64(!finite)) {   // (rare: a scalar branch around it)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                if (!finite) xs[s] = qu4_t{0u, 0u, 0u, 0u};
+        }
+        const float tscale = (finite && ss > 0.f) ? kscale * __frsqrt_rn(ss) : 0.f;
+
+        uint32_t pk[BITS];
+#pragma unroll
+        for (int w = 0; w < BITS; ++w) pk[w] = 0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            // (the k-steps start at s = t >> 1, so no two tiles share a partial sum:
+            // shared partials would keep more accumulators live at once)
+            qf4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int s = ((t >> 1) + k) & 3;
+                acc = mfma_16x16x32(hop[t & 1][__popc((t >> 1) & s) & 1], xs[s], acc);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float tv = acc[jj] * tscale;
+                const LutEntry e = lut0[cvt_floor(tv)];
+                const uint32_t code = (uint32_t)e.base + (tv > e.thr ? 1u : 0u);
+                const int bit = BITS * (4 * t + jj);   // compile-time
+                const int wd = bit >> 5, off = bit & 31;
+                pk[wd] |= code << off;
+                if (off + BITS > 32) pk[wd + 1] |= code >> (32 - off);
+            }
+            // pack each tile's codes now: left to the store, the compiler sinks every
+            // table entry and scaled value into it and holds all 32 at once
+#pragma unroll
+            for (int w = 0; w < BITS; ++w) asm volatile("" : "+v"(pk[w]));
+        }
+
+        const int64_t slot = tl.slot;
+        if (vt + n < p.n_vec && slot >= 0 && slot < p.cap) {
+            const uint32_t blk_id = fdiv((uint32_t)slot, bsdiv);
+            const uint32_t off = (uint32_t)slot - blk_id * (uint32_t)p.block_size;
+            const int64_t row = ((int64_t)blk_id * p.n_kv + head) * p.block_size + off;
+            uint8_t *dst = p.codes + row * (16 * BITS) + 4 * BITS * g;
+            if constexpr (BITS == 4) {
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            } else if constexpr (BITS == 2) {
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(pk[0], pk[1]);
+            } else {   // 12 bytes at byte 12 g (4-byte aligned)
+                uint32_t *d = reinterpret_cast<uint32_t *>(dst);
+                d[0] = pk[0];
+                d[1] = pk[1];
+                d[2] = pk[2];
+            }
+            if (g == 0) p.norms[row] = __fsqrt_rn(ss);
+        }
+    };
+
+    // One tile in flight: a tile's loads are issued when the previous tile has been
+    // encoded.  Every wave of the call is resident at once (4 per SIMD), so the
+    // memory system sees the first tiles of all waves before any second tile, and
+    // the waves whose first data lands early compute while the rest still load
+    // (measured 2-5% faster than issuing both tiles' loads at the start).
+    Tile tl;
+    load(tl, tok0);
+    build_lut(p, lut);
+    __syncthreads();
+    for (int i = 0; i < n_tiles; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        encode(tl, first + i * 16);
+        if (i + 1 < n_tiles) load(tl, tok0 + (i + 1) * tok_step);
+    }
+}
+
 __global__ __launch_bounds__(256) void tq_quantize_kernel(QuantArgs a) {
     __shared__ LutEntry lut[kLutMax];   // built inside quant_side, once its first loads are out
     const bool second = (int)blockIdx.x >= a.blocks_k;
     const QuantSide &p = second ? a.side[1] : a.side[0];
     const int blk = second ? (int)blockIdx.x - a.blocks_k : (int)blockIdx.x;
     const int nblk = second ? (int)gridDim.x - a.blocks_k : a.blocks_k;
+#ifndef TQ_QUANT_NO_MFMA
+    if (p.n_out == 0 && p.gpw > 0 && p.bits != 16) {   // n_kv | 8: tiles of 16 vectors on the matrix cores
+        switch (p.bits) {
+            case 2: quant_side_mx<2>(p, a.slots, lut, blk); break;
+            case 3: quant_side_mx<3>(p, a.slots, lut, blk); break;
+            default: quant_side_mx<4>(p, a.slots, lut, blk); break;
+        }
+        return;
+    }
+#endif
     if (p.n_out > 0) {   // kept channels (compressed sides only)
         switch (p.bits) {
             case 2: quant_side<2, true>(p, a.slots, lut, blk, nblk); break;

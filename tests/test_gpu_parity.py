@@ -108,8 +108,10 @@ def quantize_and_compare(x16, signs, bits, block_size=16, slot_perm=None, token_
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("n_kv,n_tok", [(1, 1), (3, 7), (8, 300), (5, 33)])
+@pytest.mark.parametrize("n_kv,n_tok", [(1, 1), (3, 7), (8, 300), (5, 33), (4, 13), (2, 77), (8, 6)])
 def test_quantize_random(bits, n_kv, n_tok):
+    """n_kv dividing 8 takes the matrix-core transform (tiles of 16 vectors: 52, 154
+    and 48 vectors leave partial tiles and waves), the others the vector path."""
     rng = np.random.default_rng(100 * bits + n_tok)
     x = (rng.standard_normal((n_tok, n_kv, 128)) * rng.lognormal(0, 1, (1, n_kv, 128))).astype(np.float16)
     signs = W.random_sign_words(rng, n_kv)
