@@ -714,14 +714,16 @@ def _skip_valu_for_wide_heads(kernel):
         pytest.skip("heads of several blocks run on the matrix-core pass only (the vector-ALU pass rejects them)")
 
 
+@pytest.mark.parametrize("n_kv", [3, 2])
 @pytest.mark.parametrize("head_dim", [256, 512])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_quantize_wide_heads(bits, head_dim):
+def test_quantize_wide_heads(bits, head_dim, n_kv):
     """Every 128-slice of every head is quantized with its own sign words (R12),
-    from a padded token stride and into shuffled slots."""
+    from a padded token stride and into shuffled slots.  (2 KV heads make 4 or 8
+    sub-heads: the matrix-core transform; 3 make 6 or 12: the vector path.)"""
     torch = _t()
-    rng = np.random.default_rng(7 * bits + head_dim)
-    nb, n_kv, n_tok, bs, pad = head_dim // 128, 3, 90, 16, 24
+    rng = np.random.default_rng(7 * bits + head_dim + 1000 * (3 - n_kv))
+    nb, n_tok, bs, pad = head_dim // 128, 90, 16, 24
     x = (rng.standard_normal((n_tok, n_kv, head_dim)) * rng.lognormal(0, 1, (1, n_kv, head_dim))).astype(np.float16)
     signs = W.random_sign_words(rng, n_kv * nb)
     n_blocks = -(-n_tok // bs) + 1
@@ -756,7 +758,7 @@ def test_quantize_wide_heads(bits, head_dim):
         want = O.cache_read(oc, slots[ok], h)
         err = U.row_rel_err(got[:, h], want)
         assert np.max(err) < 1e-4, f"dequantize head {h}: {np.max(err)} (near-boundary codes {near})"
-    log(f"quantize head_dim={head_dim} bits={bits}: near-boundary {near}")
+    log(f"quantize head_dim={head_dim} n_kv={n_kv} bits={bits}: near-boundary {near}")
 
 
 @pytest.mark.parametrize("case", [
