@@ -94,9 +94,15 @@ tq_status check_cache(const tq_cache *c) {
     return check_codebook(c->cb, c->bits);
 }
 
-// Groups of 8 vectors each quantize wave takes in a row (when n_kv divides 8).
+// Groups of 8 vectors each quantize wave takes in a row: when n_kv divides 8 (the
+// vector path's groups of 8 then hold whole tokens), or, for a side the matrix-core
+// transform quantizes (compressed, no kept channels), when n_kv divides its tiles
+// of 16 vectors.
 constexpr int kQuantGroups = 4;
-int quant_gpw(int n_kv) { return (n_kv > 0 && 8 % n_kv == 0) ? kQuantGroups : 0; }
+int quant_gpw(int n_kv, bool mfma_side) {
+    if (n_kv <= 0) return 0;
+    return (8 % n_kv == 0 || (mfma_side && 16 % n_kv == 0)) ? kQuantGroups : 0;
+}
 
 // Encode grid for one codebook: cells of width 1/grid in y, at most one boundary
 // per (slightly widened) cell; the table covers y in [-1, 1] (|y| <= 1 because y
@@ -111,7 +117,7 @@ tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, in
         q.n_vec = (int64_t)n_tokens * sub_heads(c);
         q.n_tokens = n_tokens;
         q.cap = c->n_blocks * c->block_size;
-        q.gpw = quant_gpw(sub_heads(c));
+        q.gpw = quant_gpw(sub_heads(c), false);
         q.n_kv = sub_heads(c);
         q.block_size = c->block_size;
         q.bits = c->bits;
@@ -136,7 +142,7 @@ tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, in
     q.n_vec = (int64_t)n_tokens * sub_heads(c);
     q.n_tokens = n_tokens;
     q.cap = c->n_blocks * c->block_size;
-    q.gpw = quant_gpw(sub_heads(c));
+    q.gpw = quant_gpw(sub_heads(c), c->n_outliers == 0);
     q.n_kv = sub_heads(c);
     q.block_size = c->block_size;
     q.bits = c->bits;
@@ -154,13 +160,13 @@ tq_status fill_quant_side(const tq_cache *c, const void *src, int64_t stride, in
 
 int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 
-// Blocks for one quantize side (4 waves per block).  When n_kv divides 8, every
+// Blocks for one quantize side (4 waves per block).  With gpw > 0 (quant_gpw) every
 // wave takes kQuantGroups consecutive groups of 8 vectors; otherwise at most 512
 // blocks (with both sides, about 4 waves per SIMD, each pipelining several
 // groups), rounded so the grid stride is a multiple of n_kv.
-int quant_blocks(int64_t n_vec, int n_kv) {
+int quant_blocks(int64_t n_vec, int n_kv, int gpw) {
     if (n_vec == 0) return 0;
-    if (quant_gpw(n_kv) > 0) return (int)((n_vec + 32 * kQuantGroups - 1) / (32 * kQuantGroups));
+    if (gpw > 0) return (int)((n_vec + 32 * kQuantGroups - 1) / (32 * kQuantGroups));
     const int64_t need = (n_vec + 31) / 32;
     int blocks = (int)std::min<int64_t>(need, 512);
     const int m = n_kv / gcd_int(n_kv, 32);
@@ -434,8 +440,8 @@ tq_status tq_quantize_kv(const tq_cache *k, const void *k_src, const tq_cache *v
     if (n_tokens == 0 || n_kv < 0) return TQ_OK;
     if (!slot_mapping) return TQ_ERR_INVALID_ARG;
     if ((int64_t)n_tokens * n_kv * (head_dim / kD) > (1LL << 31) - (1LL << 20)) return TQ_ERR_UNSUPPORTED;
-    const int bk = quant_blocks(a.side[0].n_vec, std::max(1, a.side[0].n_kv));
-    const int bv = quant_blocks(a.side[1].n_vec, std::max(1, a.side[1].n_kv));
+    const int bk = quant_blocks(a.side[0].n_vec, std::max(1, a.side[0].n_kv), a.side[0].gpw);
+    const int bv = quant_blocks(a.side[1].n_vec, std::max(1, a.side[1].n_kv), a.side[1].gpw);
     a.slots = slot_mapping;
     a.blocks_k = bk;
     if (launch_quantize(a, bk + bv, static_cast<hipStream_t>(stream)) != hipSuccess) return TQ_ERR_HIP;

@@ -66,6 +66,8 @@ struct QuantSide {
     int32_t n_tokens;
     int64_t cap;              // slots of the cache (n_blocks * block_size): larger slots are skipped
     int32_t gpw;              // groups of 8 vectors per wave (consecutive), or 0: grid stride
+                              // (> 0 only where each lane's head stays fixed: n_kv | 8, or
+                              // n_kv | 16 on a side for the matrix-core transform)
     int32_t n_kv;
     int32_t block_size;
     int32_t bits;

@@ -5,10 +5,10 @@
 //   domain, sum of squares with v_dot2_f32_f16, 8-lane DPP reduction -> norm,
 //   Walsh-Hadamard transform (4 in-register stages + 3 DPP stages), scale to
 //   the encode grid, encode with a small LDS table, bit-pack, store.
-// When the KV heads divide 8 (every cache without kept channels of the usual
-// head counts) the transform runs on the matrix cores instead, 16 vectors per
-// tile (quant_side_mx below): same encode table and cache layout, about 45%
-// fewer vector instructions.
+// When the KV heads (sub-heads of wide heads) divide 16 and no channels are kept
+// the transform runs on the matrix cores instead, 16 vectors per tile
+// (quant_side_mx below): same encode table and cache layout, about 45% fewer
+// vector instructions.
 // Sources: [TQ blog] 3.2 (signs then Hadamard, fast transform), [TQ blog] 3.3
 // (Lloyd-Max codebook), [TQ+ README] quantization-types note (128-element
 // blocks) and backend table (SET_ROWS quantize-on-append).
@@ -297,8 +297,9 @@ __device__ __forceinline__ qu4_t hadamard_operand(int lane, int odd, int neg) {
     return qu4_t{w[0], w[1], w[2], w[3]};
 }
 
-// Requires n_kv | 8 (p.gpw > 0): a tile of 16 consecutive vectors then holds
-// whole tokens, so the KV head of each lane's vector is fixed for the wave.
+// Requires n_kv | 16 (the host sets p.gpw > 0 for such a side): a tile of 16
+// consecutive vectors then holds whole tokens, so the KV head of each lane's vector
+// is fixed for the wave.
 template <int BITS>
 __device__ __forceinline__ void quant_side_mx(const QuantSide &p, const int64_t *__restrict__ slots, LutEntry *lut,
                                               int blk) {
@@ -441,8 +442,7 @@ __global__ __launch_bounds__(256) void tq_quantize_kernel(QuantArgs a) {
     const QuantSide &p = second ? a.side[1] : a.side[0];
     const int blk = second ? (int)blockIdx.x - a.blocks_k : (int)blockIdx.x;
     const int nblk = second ? (int)gridDim.x - a.blocks_k : a.blocks_k;
-#ifndef TQ_QUANT_NO_MFMA
-    if (p.n_out == 0 && p.gpw > 0 && p.bits != 16) {   // n_kv | 8: tiles of 16 vectors on the matrix cores
+    if (p.n_out == 0 && p.gpw > 0 && p.bits != 16) {   // n_kv | 16: tiles of 16 vectors on the matrix cores
         switch (p.bits) {
             case 2: quant_side_mx<2>(p, a.slots, lut, blk); break;
             case 3: quant_side_mx<3>(p, a.slots, lut, blk); break;
@@ -450,7 +450,6 @@ __global__ __launch_bounds__(256) void tq_quantize_kernel(QuantArgs a) {
         }
         return;
     }
-#endif
     if (p.n_out > 0) {   // kept channels (compressed sides only)
         switch (p.bits) {
             case 2: quant_side<2, true>(p, a.slots, lut, blk, nblk); break;

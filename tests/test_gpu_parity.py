@@ -108,10 +108,11 @@ def quantize_and_compare(x16, signs, bits, block_size=16, slot_perm=None, token_
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("n_kv,n_tok", [(1, 1), (3, 7), (8, 300), (5, 33), (4, 13), (2, 77), (8, 6)])
+@pytest.mark.parametrize("n_kv,n_tok", [(1, 1), (3, 7), (8, 300), (5, 33), (4, 13), (2, 77), (8, 6), (16, 21),
+                                        (12, 9)])
 def test_quantize_random(bits, n_kv, n_tok):
-    """n_kv dividing 8 takes the matrix-core transform (tiles of 16 vectors: 52, 154
-    and 48 vectors leave partial tiles and waves), the others the vector path."""
+    """n_kv dividing 16 takes the matrix-core transform (tiles of 16 vectors: 52, 154,
+    48 and 336 vectors leave partial tiles and waves), the others the vector path."""
     rng = np.random.default_rng(100 * bits + n_tok)
     x = (rng.standard_normal((n_tok, n_kv, 128)) * rng.lognormal(0, 1, (1, n_kv, 128))).astype(np.float16)
     signs = W.random_sign_words(rng, n_kv)
@@ -714,15 +715,16 @@ def _skip_valu_for_wide_heads(kernel):
         pytest.skip("heads of several blocks run on the matrix-core pass only (the vector-ALU pass rejects them)")
 
 
-@pytest.mark.parametrize("n_kv", [3, 2])
+@pytest.mark.parametrize("n_kv", [3, 2, 8])
 @pytest.mark.parametrize("head_dim", [256, 512])
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_quantize_wide_heads(bits, head_dim, n_kv):
     """Every 128-slice of every head is quantized with its own sign words (R12),
-    from a padded token stride and into shuffled slots.  (2 KV heads make 4 or 8
-    sub-heads: the matrix-core transform; 3 make 6 or 12: the vector path.)"""
+    from a padded token stride and into shuffled slots.  (Sub-heads dividing 16 take
+    the matrix-core transform: 2 KV heads, and 8 of 256 elements; 3 KV heads and 8
+    of 512 elements the vector path.)"""
     torch = _t()
-    rng = np.random.default_rng(7 * bits + head_dim + 1000 * (3 - n_kv))
+    rng = np.random.default_rng(7 * bits + head_dim + (0 if n_kv == 3 else 1000 * n_kv))
     nb, n_tok, bs, pad = head_dim // 128, 90, 16, 24
     x = (rng.standard_normal((n_tok, n_kv, head_dim)) * rng.lognormal(0, 1, (1, n_kv, head_dim))).astype(np.float16)
     signs = W.random_sign_words(rng, n_kv * nb)
