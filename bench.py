@@ -102,24 +102,33 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 def record_traffic(kernel_key, fetch_csv, write_csv):
     """Write the HBM bytes per launch of one kernel into the traffic record, from two
     rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; counter_collection.csv, KiB
-    per dispatch): the mean over that kernel's dispatches, scaled as above."""
+    per dispatch): the mean over that kernel's dispatches, scaled as above.  Of the
+    instantiations of the kernel in the run (the scoring and the gated pass of a
+    sparse decode are both the matrix-core kernel) the one that fetches the most is
+    taken: the dominant kernel the bench's roofline is about."""
     import csv
     kernel = kernel_key.split(":")[0]
 
-    def per_dispatch(path, counter):
-        tot = {}
+    def per_name(path, counter):
+        tot = {}   # kernel name -> dispatch -> KiB
         with open(path) as f:
             for row in csv.DictReader(f):
-                if row.get("Counter_Name") != counter or kernel not in row.get("Kernel_Name", ""):
+                name = row.get("Kernel_Name", "")
+                if row.get("Counter_Name") != counter or kernel not in name:
                     continue
                 d = row.get("Dispatch_Id") or row.get("Correlation_Id")
-                tot[d] = tot.get(d, 0.0) + float(row["Counter_Value"])
+                tot.setdefault(name, {})
+                tot[name][d] = tot[name].get(d, 0.0) + float(row["Counter_Value"])
         if not tot:
             raise SystemExit(f"no {counter} rows for {kernel} in {path}")
-        return sum(tot.values()) / len(tot), len(tot)
+        return {n: (sum(v.values()) / len(v), len(v)) for n, v in tot.items()}
 
-    fetch_kib, nf = per_dispatch(fetch_csv, "FETCH_SIZE")
-    write_kib, nw = per_dispatch(write_csv, "WRITE_SIZE")
+    fetch = per_name(fetch_csv, "FETCH_SIZE")
+    name = max(fetch, key=lambda n: fetch[n][0])
+    write = per_name(write_csv, "WRITE_SIZE")
+    if name not in write:
+        raise SystemExit(f"{name} has no WRITE_SIZE rows in {write_csv}")
+    (fetch_kib, nf), (write_kib, nw) = fetch[name], write[name]
     fetch_b = FETCH_SCALE * fetch_kib * 1024
     write_b = WRITE_SCALE * write_kib * 1024
     rec = {}
@@ -128,6 +137,7 @@ def record_traffic(kernel_key, fetch_csv, write_csv):
             rec = json.load(f)
     rec[kernel_key] = {"bytes_per_launch": int(round(fetch_b + write_b)), "fetch_bytes": int(round(fetch_b)),
                        "write_bytes": int(round(write_b)), "source_hash": source_hash(kernel),
+                       "kernel_name": name[:160],
                        "dispatches": [nf, nw], "fetch_kib_per_dispatch": round(fetch_kib, 1),
                        "write_kib_per_dispatch": round(write_kib, 1)}
     with open(PMC_RECORD, "w") as f:
