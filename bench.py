@@ -135,8 +135,9 @@ def record_traffic(kernel_key, fetch_csv, write_csv):
     if os.path.exists(PMC_RECORD):
         with open(PMC_RECORD) as f:
             rec = json.load(f)
-    rec[kernel_key] = {"bytes_per_launch": int(round(fetch_b + write_b)), "fetch_bytes": int(round(fetch_b)),
-                       "write_bytes": int(round(write_b)), "source_hash": source_hash(kernel),
+    fetch_i, write_i = int(round(fetch_b)), int(round(write_b))
+    rec[kernel_key] = {"bytes_per_launch": fetch_i + write_i, "fetch_bytes": fetch_i,
+                       "write_bytes": write_i, "source_hash": source_hash(kernel),
                        "kernel_name": name[:160],
                        "dispatches": [nf, nw], "fetch_kib_per_dispatch": round(fetch_kib, 1),
                        "write_kib_per_dispatch": round(write_kib, 1)}
